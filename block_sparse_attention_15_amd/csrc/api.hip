@@ -1,0 +1,322 @@
+// C ABI entry points: host-side validation, derived sizes, workspace
+// carving and kernel launches.  No entry point allocates, frees or
+// synchronizes; all work goes onto the caller's stream.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "common.h"
+
+namespace pbsa {
+namespace {
+
+thread_local std::string g_err;
+
+pbsa_status fail(pbsa_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+pbsa_status fail(pbsa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct Plan {
+  Geo g;
+  pbsa_plan_info info;
+};
+
+// Derive the geometry of a configuration (block tiling of the project page's
+// sparse_kv_block_size, cache sizes of its constructor) and check it.
+pbsa_status make_plan(const pbsa_config* c, Plan* p) {
+  if (!c) return fail(PBSA_ERR_INVALID_ARG, "config is NULL");
+  if (c->batch <= 0 || c->heads <= 0 || c->head_dim <= 0)
+    return fail(PBSA_ERR_INVALID_ARG, "batch, heads and head_dim must be positive");
+  if (c->frame_h <= 0 || c->frame_w <= 0 || c->block_t <= 0 || c->block_h <= 0 || c->block_w <= 0 ||
+      c->chunk_frames <= 0)
+    return fail(PBSA_ERR_INVALID_ARG, "frame, block and chunk sizes must be positive");
+  if (c->local_cache_size <= 0 || c->persistent_cache_size < 0)
+    return fail(PBSA_ERR_INVALID_ARG, "cache sizes must be positive");
+  if (c->total_cache_size != c->local_cache_size + c->persistent_cache_size)
+    return fail(PBSA_ERR_INVALID_ARG, "total_cache_size (%lld) != local (%lld) + persistent (%lld)",
+                (long long)c->total_cache_size, (long long)c->local_cache_size,
+                (long long)c->persistent_cache_size);
+  if (c->chunk_frames % c->block_t)
+    return fail(PBSA_ERR_INVALID_ARG, "chunk_frames (%d) must be a multiple of block_t (%d)", c->chunk_frames,
+                c->block_t);
+  if (c->dtype != PBSA_BF16 && c->dtype != PBSA_FP32) return fail(PBSA_ERR_INVALID_ARG, "unknown dtype %d", c->dtype);
+  if (c->use_local_block_sparse_attn && !(c->topk_ratio > 0.f && c->topk_ratio <= 1.f))
+    return fail(PBSA_ERR_INVALID_ARG, "topk_ratio (%g) must be in (0, 1]", (double)c->topk_ratio);
+  if (!(c->softmax_scale >= 0.f) || isinf(c->softmax_scale))
+    return fail(PBSA_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
+  const int64_t ft = (int64_t)c->frame_h * c->frame_w;
+  const int64_t ct = ft * c->chunk_frames;
+  if (c->local_cache_size % ct)
+    return fail(PBSA_ERR_INVALID_ARG, "local_cache_size (%lld) is not a whole number of %lld-token chunks",
+                (long long)c->local_cache_size, (long long)ct);
+  if (c->persistent_cache_size % (ft * c->block_t))
+    return fail(PBSA_ERR_INVALID_ARG, "persistent_cache_size (%lld) is not a whole number of %lld-token frame groups",
+                (long long)c->persistent_cache_size, (long long)(ft * c->block_t));
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(PBSA_ERR_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", c->head_dim);
+  const int C = c->block_t * c->block_h * c->block_w;
+  if (C > 64) return fail(PBSA_ERR_UNSUPPORTED, "blocks of %d tokens unsupported (at most 64)", C);
+  if (ct > (1 << 24) || c->local_cache_size > (1 << 26))
+    return fail(PBSA_ERR_UNSUPPORTED, "chunk or cache too large");
+
+  Geo& g = p->g;
+  g.B = c->batch;
+  g.H = c->heads;
+  g.D = c->head_dim;
+  g.fh = c->frame_h;
+  g.fw = c->frame_w;
+  g.bt = c->block_t;
+  g.bh = c->block_h;
+  g.bw = c->block_w;
+  g.cf = c->chunk_frames;
+  g.ft = (int)ft;
+  g.ct = (int)ct;
+  g.nbr = (g.fh + g.bh - 1) / g.bh;
+  g.nbc = (g.fw + g.bw - 1) / g.bw;
+  g.bpg = g.nbr * g.nbc;
+  g.nq = g.bpg * (g.cf / g.bt);
+  g.R = (int)(c->local_cache_size / ct);
+  g.nl = g.R * g.nq;
+  g.NL = (int)c->local_cache_size;
+  g.S = (int)(c->persistent_cache_size / (ft * g.bt)) * g.bpg;
+  g.C = C;
+  if (c->use_local_block_sparse_attn) {
+    // k = ceil(ratio * n) with a 1e-6 allowance so that products that are
+    // integers in decimal (0.1 * 10) do not round up.
+    double k = ceil((double)c->topk_ratio * g.nl - 1e-6);
+    g.K = (int)fmin(fmax(k, 1.0), (double)g.nl);
+  } else {
+    g.K = g.nl;
+  }
+  g.scale = c->softmax_scale > 0.f ? c->softmax_scale : (float)(1.0 / sqrt((double)g.D));
+  g.dtype = c->dtype;
+  if (g.S > 4096 || g.nl > 4096 || g.nq > 4096)
+    return fail(PBSA_ERR_UNSUPPORTED, "more than 4096 blocks per cache");
+
+  pbsa_plan_info& in = p->info;
+  memset(&in, 0, sizeof in);
+  in.blocks_per_chunk = g.nq;
+  in.local_blocks = g.nl;
+  in.ring_chunks = g.R;
+  in.persistent_slots = g.S;
+  in.slot_rows = g.C;
+  in.topk = g.K;
+  in.chunk_tokens = g.ct;
+  int mx = 0;
+  for (int j = 0; j < g.nq; ++j) mx = mx > block_ext(g, j).len ? mx : block_ext(g, j).len;
+  in.max_block_tokens = mx;
+  const size_t BH = (size_t)g.B * g.H;
+  in.ws_score_select = align256(BH * g.nq * g.D * 4) + align256(BH * g.nq * (g.S + g.nl) * 4);
+  in.ws_fwd = 0;
+  in.ws_bwd = align256(BH * g.ct * 4) + align256(BH * g.nl * 4) + align256(BH * g.nl * g.nq * 4);
+  in.ws_persist_update = align256(BH * g.S * 4);
+  return PBSA_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+#define REQUIRE_PTR(p)                                                         \
+  do {                                                                         \
+    if (!(p)) return fail(PBSA_ERR_INVALID_ARG, "%s is NULL", #p);             \
+  } while (0)
+#define REQUIRE_ALIGNED(p)                                                                   \
+  do {                                                                                       \
+    REQUIRE_PTR(p);                                                                          \
+    if (!aligned16(p)) return fail(PBSA_ERR_ALIGNMENT, "%s is not 16-byte aligned", #p);     \
+  } while (0)
+
+pbsa_status check_ws(void* ws, size_t have, size_t need) {
+  if (need == 0) return PBSA_OK;
+  if (!ws) return fail(PBSA_ERR_WORKSPACE, "workspace is NULL but %zu bytes are needed", need);
+  if (!aligned16(ws)) return fail(PBSA_ERR_ALIGNMENT, "workspace is not 16-byte aligned");
+  if (have < need) return fail(PBSA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", have, need);
+  return PBSA_OK;
+}
+
+pbsa_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) {
+    g_err.clear();
+    return PBSA_OK;
+  }
+  return fail(PBSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+}  // namespace pbsa
+
+using namespace pbsa;
+
+extern "C" {
+
+pbsa_status pbsa_plan(const pbsa_config* cfg, pbsa_plan_info* out) {
+  if (!out) return fail(PBSA_ERR_INVALID_ARG, "out is NULL");
+  Plan p;
+  pbsa_status st = make_plan(cfg, &p);
+  if (st != PBSA_OK) return st;
+  *out = p.info;
+  g_err.clear();
+  return PBSA_OK;
+}
+
+pbsa_status pbsa_pool_slots(const pbsa_config* cfg, const void* k_pers, const int32_t* persist_len,
+                            float* persist_kbar, void* stream) {
+  Plan p;
+  pbsa_status st = make_plan(cfg, &p);
+  if (st != PBSA_OK) return st;
+  REQUIRE_ALIGNED(k_pers);
+  REQUIRE_PTR(persist_len);
+  REQUIRE_ALIGNED(persist_kbar);
+  if (p.g.S == 0) return PBSA_OK;
+  return hip_status(launch_pool_slots(p.g, k_pers, persist_len, persist_kbar, (hipStream_t)stream),
+                    "pbsa_pool_slots");
+}
+
+pbsa_status pbsa_score_select(const pbsa_config* cfg, const void* q, const void* k_local,
+                              const int32_t* ring_head, const float* persist_kbar,
+                              const int32_t* persist_len, int32_t* topk_idx, float* mass,
+                              float* kbar_local, void* ws, size_t ws_bytes, void* stream) {
+  Plan p;
+  pbsa_status st = make_plan(cfg, &p);
+  if (st != PBSA_OK) return st;
+  REQUIRE_ALIGNED(q);
+  REQUIRE_ALIGNED(k_local);
+  REQUIRE_PTR(ring_head);
+  REQUIRE_PTR(topk_idx);
+  REQUIRE_PTR(mass);
+  REQUIRE_ALIGNED(kbar_local);
+  if (p.g.S > 0) {
+    REQUIRE_ALIGNED(persist_kbar);
+    REQUIRE_PTR(persist_len);
+  }
+  if ((st = check_ws(ws, ws_bytes, p.info.ws_score_select)) != PBSA_OK) return st;
+  const size_t BH = (size_t)p.g.B * p.g.H;
+  WsScore w;
+  w.qbar = (float*)ws;
+  w.prow = (float*)((char*)ws + align256(BH * p.g.nq * p.g.D * 4));
+  return hip_status(launch_score_select(p.g, q, k_local, ring_head, persist_kbar, persist_len, topk_idx, mass,
+                                        kbar_local, w, (hipStream_t)stream),
+                    "pbsa_score_select");
+}
+
+pbsa_status pbsa_fwd(const pbsa_config* cfg, const void* q, const void* k_pers, const void* v_pers,
+                     const int32_t* persist_len, const void* k_local, const void* v_local,
+                     const int32_t* topk_idx, void* o, float* lse, void* ws, size_t ws_bytes,
+                     void* stream) {
+  Plan p;
+  pbsa_status st = make_plan(cfg, &p);
+  if (st != PBSA_OK) return st;
+  REQUIRE_ALIGNED(q);
+  REQUIRE_ALIGNED(k_local);
+  REQUIRE_ALIGNED(v_local);
+  REQUIRE_PTR(topk_idx);
+  REQUIRE_ALIGNED(o);
+  REQUIRE_PTR(lse);
+  if (p.g.S > 0) {
+    REQUIRE_ALIGNED(k_pers);
+    REQUIRE_ALIGNED(v_pers);
+    REQUIRE_PTR(persist_len);
+  }
+  if ((st = check_ws(ws, ws_bytes, p.info.ws_fwd)) != PBSA_OK) return st;
+  return hip_status(launch_fwd(p.g, q, k_pers, v_pers, persist_len, k_local, v_local, topk_idx, o, lse,
+                               (hipStream_t)stream),
+                    "pbsa_fwd");
+}
+
+pbsa_status pbsa_bwd(const pbsa_config* cfg, const void* q, const void* k_pers, const void* v_pers,
+                     const int32_t* persist_len, const void* k_local, const void* v_local,
+                     const int32_t* topk_idx, const void* o, const float* lse, const void* dout,
+                     float* dq, float* dk_pers, float* dv_pers, float* dk_local, float* dv_local,
+                     void* ws, size_t ws_bytes, void* stream) {
+  Plan p;
+  pbsa_status st = make_plan(cfg, &p);
+  if (st != PBSA_OK) return st;
+  REQUIRE_ALIGNED(q);
+  REQUIRE_ALIGNED(k_local);
+  REQUIRE_ALIGNED(v_local);
+  REQUIRE_PTR(topk_idx);
+  REQUIRE_ALIGNED(o);
+  REQUIRE_PTR(lse);
+  REQUIRE_ALIGNED(dout);
+  REQUIRE_ALIGNED(dq);
+  REQUIRE_ALIGNED(dk_local);
+  REQUIRE_ALIGNED(dv_local);
+  if (p.g.S > 0) {
+    REQUIRE_ALIGNED(k_pers);
+    REQUIRE_ALIGNED(v_pers);
+    REQUIRE_PTR(persist_len);
+    REQUIRE_ALIGNED(dk_pers);
+    REQUIRE_ALIGNED(dv_pers);
+  }
+  if ((st = check_ws(ws, ws_bytes, p.info.ws_bwd)) != PBSA_OK) return st;
+  const size_t BH = (size_t)p.g.B * p.g.H;
+  WsBwd w;
+  char* base = (char*)ws;
+  w.delta = (float*)base;
+  base += align256(BH * p.g.ct * 4);
+  w.tcount = (int32_t*)base;
+  base += align256(BH * p.g.nl * 4);
+  w.tlist = (int32_t*)base;
+  return hip_status(launch_bwd(p.g, q, k_pers, v_pers, persist_len, k_local, v_local, topk_idx, o, lse, dout, dq,
+                               dk_pers, dv_pers, dk_local, dv_local, w, (hipStream_t)stream),
+                    "pbsa_bwd");
+}
+
+pbsa_status pbsa_persist_update(const pbsa_config* cfg, const float* mass, const void* k_local,
+                                const void* v_local, const float* kbar_local, int32_t* ring_head,
+                                int32_t step_id, void* k_pers, void* v_pers, int32_t* persist_len,
+                                int32_t* persist_src, float* persist_kbar, int32_t* n_replaced,
+                                void* ws, size_t ws_bytes, void* stream) {
+  Plan p;
+  pbsa_status st = make_plan(cfg, &p);
+  if (st != PBSA_OK) return st;
+  REQUIRE_PTR(mass);
+  REQUIRE_ALIGNED(k_local);
+  REQUIRE_ALIGNED(v_local);
+  REQUIRE_ALIGNED(kbar_local);
+  REQUIRE_PTR(ring_head);
+  REQUIRE_PTR(n_replaced);
+  if (step_id < 0 || (int64_t)step_id * p.g.nq + p.g.nq > INT32_MAX)
+    return fail(PBSA_ERR_INVALID_ARG, "step_id %d out of range", step_id);
+  if (p.g.S > 0) {
+    REQUIRE_ALIGNED(k_pers);
+    REQUIRE_ALIGNED(v_pers);
+    REQUIRE_PTR(persist_len);
+    REQUIRE_PTR(persist_src);
+    REQUIRE_ALIGNED(persist_kbar);
+  }
+  if ((st = check_ws(ws, ws_bytes, p.info.ws_persist_update)) != PBSA_OK) return st;
+  return hip_status(launch_persist_update(p.g, mass, k_local, v_local, kbar_local, ring_head, step_id, k_pers,
+                                          v_pers, persist_len, persist_src, persist_kbar, n_replaced,
+                                          (int32_t*)ws, (hipStream_t)stream),
+                    "pbsa_persist_update");
+}
+
+pbsa_status pbsa_ring_append(const pbsa_config* cfg, const void* k_new, const void* v_new,
+                             const int32_t* ring_head, void* k_local, void* v_local, void* stream) {
+  Plan p;
+  pbsa_status st = make_plan(cfg, &p);
+  if (st != PBSA_OK) return st;
+  REQUIRE_ALIGNED(k_new);
+  REQUIRE_ALIGNED(v_new);
+  REQUIRE_PTR(ring_head);
+  REQUIRE_ALIGNED(k_local);
+  REQUIRE_ALIGNED(v_local);
+  return hip_status(launch_ring_append(p.g, k_new, v_new, ring_head, k_local, v_local, (hipStream_t)stream),
+                    "pbsa_ring_append");
+}
+
+const char* pbsa_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,264 @@
+// Sparse attention backward, plain VALU version (fp32 inputs, and any shape
+// the matrix-core kernels do not cover) plus the shared preparation kernels.
+//
+// The project page lists full gradient support for training.  For a fixed
+// block mask (persistent slots plus the selected local blocks), the gradients
+// are those of softmax attention: P = exp(scale*q.k - lse), dV = P^T dO,
+// dP = dO V^T, D = rowsum(dO * O), dS = P * (dP - D), dQ = scale * dS K,
+// dK = scale * dS^T Q.  Deterministic: dQ is computed query-outer and dK/dV
+// key-outer, each with a fixed loop order; no floating-point atomics.
+#include "common.h"
+
+namespace pbsa {
+
+namespace {
+
+// grid (ceil(ct/4), H, B), 256 threads: one wave per query token.
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_delta_kernel(Geo g, const T* __restrict__ o, const T* __restrict__ dout,
+                                                        float* __restrict__ delta) {
+  const int t = blockIdx.x * 4 + threadIdx.x / 64, lane = threadIdx.x & 63;
+  const size_t bh = (size_t)blockIdx.z * g.H + blockIdx.y;
+  if (t >= g.ct) return;
+  const size_t row = (bh * g.ct + t) * g.D;
+  float a = 0.f;
+  for (int d = lane; d < g.D; d += 64) a = fmaf(to_f<T>(o[row + d]), to_f<T>(dout[row + d]), a);
+  for (int k = 32; k > 0; k >>= 1) a += __shfl_xor(a, k, 64);
+  if (lane == 0) delta[bh * g.ct + t] = a;
+}
+
+// grid (H, B): for each local block, the query blocks that selected it, ascending.
+__global__ __launch_bounds__(256) void bwd_tindex_kernel(Geo g, const int32_t* __restrict__ topk,
+                                                         int32_t* __restrict__ tcount, int32_t* __restrict__ tlist) {
+  const size_t bh = (size_t)blockIdx.y * g.H + blockIdx.x;
+  const int32_t* tk = topk + bh * g.nq * g.K;
+  for (int p = threadIdx.x; p < g.nl; p += 256) {
+    int n = 0;
+    int32_t* out = tlist + (bh * g.nl + p) * g.nq;
+    for (int i = 0; i < g.nq; ++i) {
+      bool hit = false;
+      for (int k = 0; k < g.K; ++k) hit |= tk[i * g.K + k] == p;
+      if (hit) out[n++] = i;
+    }
+    tcount[bh * g.nl + p] = n;
+  }
+}
+
+// dQ, query-outer.  grid (nq, H, B), 64 lanes = query tokens of one block.
+template <typename T, int D>
+__global__ __launch_bounds__(64) void bwd_dq_simple_kernel(Geo g, const T* __restrict__ q, const T* __restrict__ kp,
+                                                           const T* __restrict__ vp, const int32_t* __restrict__ plen,
+                                                           const T* __restrict__ kl, const T* __restrict__ vl,
+                                                           const int32_t* __restrict__ topk,
+                                                           const float* __restrict__ lse,
+                                                           const float* __restrict__ delta, const T* __restrict__ dout,
+                                                           float* __restrict__ dq) {
+  constexpr int kRows = 32;
+  __shared__ float ks[kRows][D];
+  __shared__ float vs[kRows][D];
+  const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const size_t bh = (size_t)b * g.H + h;
+  const int lane = threadIdx.x;
+  const BlockExt e = block_ext(g, i);
+  const bool active = lane < e.len;
+  const int tok = active ? block_token(g, e, lane) : 0;
+  float qr[D], dor[D], acc[D];
+  for (int d = 0; d < D; ++d) {
+    qr[d] = active ? to_f<T>(q[(bh * g.ct + tok) * D + d]) : 0.f;
+    dor[d] = active ? to_f<T>(dout[(bh * g.ct + tok) * D + d]) : 0.f;
+    acc[d] = 0.f;
+  }
+  const float L = active ? lse[bh * g.ct + tok] : 0.f;
+  const float Dl = active ? delta[bh * g.ct + tok] : 0.f;
+  for (int t = 0; t < g.S + g.K; ++t) {
+    int n;
+    const T *kb, *vb;
+    BlockExt le;
+    int loff = 0;
+    const bool pers = t < g.S;
+    if (pers) {
+      n = min(plen[bh * g.S + t], g.C);
+      kb = kp + (bh * g.S + t) * g.C * D;
+      vb = vp + (bh * g.S + t) * g.C * D;
+    } else {
+      const int p = topk[(bh * g.nq + i) * g.K + (t - g.S)];
+      if ((unsigned)p >= (unsigned)g.nl) continue;  // ids outside the cache are ignored
+      le = block_ext(g, p % g.nq);
+      loff = (p / g.nq) * g.ct;
+      n = le.len;
+      kb = kl + bh * (size_t)g.NL * D;
+      vb = vl + bh * (size_t)g.NL * D;
+    }
+    for (int r0 = 0; r0 < n; r0 += kRows) {
+      const int nr = min(kRows, n - r0);
+      __syncthreads();
+      for (int r = 0; r < nr; ++r) {
+        const size_t row = pers ? (size_t)(r0 + r) : (size_t)(loff + block_token(g, le, r0 + r));
+        for (int d = lane; d < D; d += 64) {
+          ks[r][d] = to_f<T>(kb[row * D + d]);
+          vs[r][d] = to_f<T>(vb[row * D + d]);
+        }
+      }
+      __syncthreads();
+      for (int r = 0; r < nr; ++r) {
+        float s = 0.f, dp = 0.f;
+        for (int d = 0; d < D; ++d) {
+          s = fmaf(qr[d], ks[r][d], s);
+          dp = fmaf(dor[d], vs[r][d], dp);
+        }
+        const float p = expf(s * g.scale - L);
+        const float ds = p * (dp - Dl);
+        for (int d = 0; d < D; ++d) acc[d] = fmaf(ds, ks[r][d], acc[d]);
+      }
+    }
+  }
+  if (!active) return;
+  for (int d = 0; d < D; ++d) dq[(bh * g.ct + tok) * D + d] = acc[d] * g.scale;
+}
+
+// dK, dV, key-outer.  grid (S + nl, H, B), 256 threads = 64 key rows x 4
+// column quarters.  Persistent slots see every query token (ascending);
+// local blocks see the tokens of the query blocks that selected them.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_dkv_simple_kernel(Geo g, const T* __restrict__ q, const T* __restrict__ kp,
+                                                             const T* __restrict__ vp, const int32_t* __restrict__ plen,
+                                                             const T* __restrict__ kl, const T* __restrict__ vl,
+                                                             const int32_t* __restrict__ tcount,
+                                                             const int32_t* __restrict__ tlist,
+                                                             const float* __restrict__ lse,
+                                                             const float* __restrict__ delta,
+                                                             const T* __restrict__ dout, float* __restrict__ dkp,
+                                                             float* __restrict__ dvp, float* __restrict__ dkl,
+                                                             float* __restrict__ dvl) {
+  constexpr int Q4 = D / 4;
+  constexpr int kTq = 32;  // query tokens staged per tile
+  __shared__ float qs[kTq][D];
+  __shared__ float ds_[kTq][D];
+  __shared__ float ls[kTq], dls[kTq];
+  const int h = blockIdx.y, b = blockIdx.z;
+  const size_t bh = (size_t)b * g.H + h;
+  const int r = threadIdx.x / 4, c = threadIdx.x & 3;
+  const bool pers = (int)blockIdx.x < g.S;
+  const int s_or_p = pers ? blockIdx.x : blockIdx.x - g.S;
+  int n, loff = 0;
+  BlockExt le;
+  const T *kb, *vb;
+  if (pers) {
+    n = min(plen[bh * g.S + s_or_p], g.C);
+    kb = kp + (bh * g.S + s_or_p) * g.C * D;
+    vb = vp + (bh * g.S + s_or_p) * g.C * D;
+  } else {
+    le = block_ext(g, s_or_p % g.nq);
+    loff = (s_or_p / g.nq) * g.ct;
+    n = le.len;
+    kb = kl + bh * (size_t)g.NL * D;
+    vb = vl + bh * (size_t)g.NL * D;
+  }
+  const bool act = r < n;
+  const size_t krow = act ? (pers ? (size_t)r : (size_t)(loff + block_token(g, le, r))) : 0;
+  float kr[Q4], vr[Q4], dk[Q4], dv[Q4];
+  for (int d = 0; d < Q4; ++d) {
+    kr[d] = act ? to_f<T>(kb[krow * D + c * Q4 + d]) : 0.f;
+    vr[d] = act ? to_f<T>(vb[krow * D + c * Q4 + d]) : 0.f;
+    dk[d] = 0.f;
+    dv[d] = 0.f;
+  }
+  // query token list: all tokens (persistent) or the selecting query blocks' tokens
+  const int nsel = pers ? 1 : tcount[bh * g.nl + s_or_p];
+  const int32_t* sel = pers ? nullptr : tlist + (bh * g.nl + s_or_p) * g.nq;
+  for (int si = 0; si < nsel; ++si) {
+    BlockExt qe;
+    int ntok;
+    if (pers) {
+      ntok = g.ct;
+    } else {
+      qe = block_ext(g, sel[si]);
+      ntok = qe.len;
+    }
+    for (int t0 = 0; t0 < ntok; t0 += kTq) {
+      const int nt = min(kTq, ntok - t0);
+      __syncthreads();
+      for (int x = threadIdx.x; x < nt * D; x += 256) {
+        const int tt = x / D, d = x - tt * D;
+        const int tok = pers ? t0 + tt : block_token(g, qe, t0 + tt);
+        qs[tt][d] = to_f<T>(q[(bh * g.ct + tok) * D + d]);
+        ds_[tt][d] = to_f<T>(dout[(bh * g.ct + tok) * D + d]);
+        if (d == 0) {
+          ls[tt] = lse[bh * g.ct + tok];
+          dls[tt] = delta[bh * g.ct + tok];
+        }
+      }
+      __syncthreads();
+      for (int tt = 0; tt < nt; ++tt) {
+        float s = 0.f, dp = 0.f;
+        for (int d = 0; d < Q4; ++d) {
+          s = fmaf(qs[tt][c * Q4 + d], kr[d], s);
+          dp = fmaf(ds_[tt][c * Q4 + d], vr[d], dp);
+        }
+        s += __shfl_xor(s, 1, 64);
+        s += __shfl_xor(s, 2, 64);
+        dp += __shfl_xor(dp, 1, 64);
+        dp += __shfl_xor(dp, 2, 64);
+        const float p = act ? expf(s * g.scale - ls[tt]) : 0.f;
+        const float dsv = p * (dp - dls[tt]);
+        for (int d = 0; d < Q4; ++d) {
+          dv[d] = fmaf(p, ds_[tt][c * Q4 + d], dv[d]);
+          dk[d] = fmaf(dsv, qs[tt][c * Q4 + d], dk[d]);
+        }
+      }
+    }
+  }
+  if (pers) {
+    if (r >= g.C) return;
+    const size_t o = ((bh * g.S + s_or_p) * g.C + r) * D + c * Q4;
+    for (int d = 0; d < Q4; ++d) {
+      dkp[o + d] = act ? dk[d] * g.scale : 0.f;
+      dvp[o + d] = act ? dv[d] : 0.f;
+    }
+  } else if (act) {
+    const size_t o = (bh * g.NL + krow) * D + c * Q4;
+    for (int d = 0; d < Q4; ++d) {
+      dkl[o + d] = dk[d] * g.scale;
+      dvl[o + d] = dv[d];
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_bwd_prep(const Geo& g, const void* o, const void* dout, const int32_t* topk, WsBwd ws,
+                           hipStream_t s) {
+  dim3 g1((g.ct + 3) / 4, g.H, g.B);
+  if (g.dtype == PBSA_BF16)
+    bwd_delta_kernel<bf16_t><<<g1, 256, 0, s>>>(g, (const bf16_t*)o, (const bf16_t*)dout, ws.delta);
+  else
+    bwd_delta_kernel<float><<<g1, 256, 0, s>>>(g, (const float*)o, (const float*)dout, ws.delta);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  bwd_tindex_kernel<<<dim3(g.H, g.B), 256, 0, s>>>(g, topk, ws.tcount, ws.tlist);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_simple(const Geo& g, const void* q, const void* k_p, const void* v_p, const int32_t* plen,
+                             const void* k_l, const void* v_l, const int32_t* topk, const float* lse,
+                             const void* dout, float* dq, float* dk_p, float* dv_p, float* dk_l, float* dv_l,
+                             WsBwd ws, hipStream_t s) {
+#define PBSA_LAUNCH(T, D)                                                                                       \
+  do {                                                                                                          \
+    bwd_dq_simple_kernel<T, D><<<dim3(g.nq, g.H, g.B), 64, 0, s>>>(g, (const T*)q, (const T*)k_p, (const T*)v_p, \
+                                                                  plen, (const T*)k_l, (const T*)v_l, topk, lse,  \
+                                                                  ws.delta, (const T*)dout, dq);                  \
+    bwd_dkv_simple_kernel<T, D><<<dim3(g.S + g.nl, g.H, g.B), 256, 0, s>>>(                                      \
+        g, (const T*)q, (const T*)k_p, (const T*)v_p, plen, (const T*)k_l, (const T*)v_l, ws.tcount, ws.tlist,   \
+        lse, ws.delta, (const T*)dout, dk_p, dv_p, dk_l, dv_l);                                                   \
+  } while (0)
+  if (g.dtype == PBSA_BF16) {
+    if (g.D == 64) PBSA_LAUNCH(bf16_t, 64); else PBSA_LAUNCH(bf16_t, 128);
+  } else {
+    if (g.D == 64) PBSA_LAUNCH(float, 64); else PBSA_LAUNCH(float, 128);
+  }
+#undef PBSA_LAUNCH
+  return hipGetLastError();
+}
+
+}  // namespace pbsa

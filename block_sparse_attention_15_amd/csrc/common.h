@@ -1,0 +1,115 @@
+// Shared host/device definitions of the PBSA HIP library (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pbsa.h"
+
+namespace pbsa {
+
+// Derived geometry, passed by value to every kernel.
+struct Geo {
+  int B, H, D;
+  int fh, fw, bt, bh, bw, cf;
+  int ft;      // tokens per frame
+  int ct;      // tokens per chunk (= query tokens)
+  int nbr;     // block rows per frame
+  int nbc;     // block columns per frame
+  int bpg;     // blocks per block_t-frame group
+  int nq;      // blocks per chunk = query blocks
+  int R;       // local ring chunk slots
+  int nl;      // local blocks
+  int NL;      // local tokens
+  int S;       // persistent slots
+  int C;       // rows per persistent slot
+  int K;       // top-k
+  float scale; // softmax scale
+  int dtype;   // pbsa_dtype
+};
+
+// Extent of chunk block j: base token offset inside the chunk, frames, rows,
+// columns and the total token count.  Block-row-major within a frame group.
+struct BlockExt {
+  int f0, r0, c0, nt, nh, nw, len;
+};
+
+__host__ __device__ inline BlockExt block_ext(const Geo& g, int j) {
+  BlockExt e;
+  int grp = j / g.bpg, rem = j - grp * g.bpg;
+  int br = rem / g.nbc, bc = rem - br * g.nbc;
+  e.f0 = grp * g.bt;
+  e.r0 = br * g.bh;
+  e.c0 = bc * g.bw;
+  e.nt = g.bt;
+  e.nh = min(g.bh, g.fh - e.r0);
+  e.nw = min(g.bw, g.fw - e.c0);
+  e.len = e.nt * e.nh * e.nw;
+  return e;
+}
+
+// Token offset (inside the chunk) of the i-th token of a block, raster order.
+__host__ __device__ inline int block_token(const Geo& g, const BlockExt& e, int i) {
+  int hw = e.nh * e.nw;
+  int f = i / hw, rem = i - f * hw;
+  int r = rem / e.nw, c = rem - r * e.nw;
+  return (e.f0 + f) * g.ft + (e.r0 + r) * g.fw + e.c0 + c;
+}
+
+// ---------------------------------------------------------------------------
+// Element conversion
+// ---------------------------------------------------------------------------
+typedef uint16_t bf16_t;  // raw bfloat16 bits
+
+__device__ __forceinline__ float bf2f(bf16_t x) { return __uint_as_float(((uint32_t)x) << 16); }
+
+// float -> bfloat16, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ bf16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+template <typename T> __device__ __forceinline__ float to_f(T x);
+template <> __device__ __forceinline__ float to_f<float>(float x) { return x; }
+template <> __device__ __forceinline__ float to_f<bf16_t>(bf16_t x) { return bf2f(x); }
+
+template <typename T> __device__ __forceinline__ T from_f(float x);
+template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16_t from_f<bf16_t>(float x) { return f2bf(x); }
+
+constexpr int32_t kEmptySrc = INT32_MIN;
+
+// ---------------------------------------------------------------------------
+// Launchers implemented in the kernel translation units.  Each returns the
+// hipError_t of its launches.
+// ---------------------------------------------------------------------------
+struct WsScore {
+  float* qbar;   // [B,H,nq,D]
+  float* prow;   // [B,H,nq,S+nl]  pooled softmax rows
+};
+hipError_t launch_pool_slots(const Geo& g, const void* k_p, const int32_t* plen, float* kbar, hipStream_t s);
+hipError_t launch_score_select(const Geo& g, const void* q, const void* k_l, const int32_t* ring_head,
+                               const float* kbar_p, const int32_t* plen, int32_t* topk, float* mass,
+                               float* kbar_l, WsScore ws, hipStream_t s);
+hipError_t launch_fwd(const Geo& g, const void* q, const void* k_p, const void* v_p, const int32_t* plen,
+                      const void* k_l, const void* v_l, const int32_t* topk, void* o, float* lse,
+                      hipStream_t s);
+struct WsBwd {
+  float* delta;     // [B,H,Nq]      rowsum(dO * O)
+  int32_t* tcount;  // [B,H,nl]      query blocks that selected each local block
+  int32_t* tlist;   // [B,H,nl,nq]   their ids, ascending
+};
+hipError_t launch_bwd(const Geo& g, const void* q, const void* k_p, const void* v_p, const int32_t* plen,
+                      const void* k_l, const void* v_l, const int32_t* topk, const void* o,
+                      const float* lse, const void* dout, float* dq, float* dk_p, float* dv_p,
+                      float* dk_l, float* dv_l, WsBwd ws, hipStream_t s);
+hipError_t launch_persist_update(const Geo& g, const float* mass, const void* k_l, const void* v_l,
+                                 const float* kbar_l, int32_t* ring_head, int32_t step_id, void* k_p,
+                                 void* v_p, int32_t* plen, int32_t* psrc, float* pkbar, int32_t* n_rep,
+                                 int32_t* plan, hipStream_t s);
+hipError_t launch_ring_append(const Geo& g, const void* k_new, const void* v_new, const int32_t* ring_head,
+                              void* k_l, void* v_l, hipStream_t s);
+
+}  // namespace pbsa

@@ -1,0 +1,195 @@
+/*
+ * pbsa.h -- C ABI of the Persistent Block-Sparse Attention (PBSA) library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * PBSA is the attention kernel of "Sparse Forcing: Native Trainable Sparse
+ * Attention for Real-time Autoregressive Diffusion Video Generation".  The
+ * abstract describes it as sparse attention of a query chunk over a persistent
+ * set of salient blocks plus a dynamically selected neighbourhood of a sliding
+ * local window, together with the update of that persistent memory.  The
+ * project page ("Sparse Forcing") gives the module interface this ABI mirrors:
+ * SparseForcingAttention(total_cache_size, local_cache_size,
+ * persistent_cache_size, sparse_kv_block_size, local_block_sparse_topk_ratio,
+ * use_local_block_sparse_attn, ...) called with (query, key_persistent,
+ * value_persistent, key_local, value_local), and lists full gradient support.
+ * The fragment of the paper's training algorithm on the review page fixes when
+ * the update runs: the t=0 cache pass applies PBSA with top-K and updates the
+ * persistent (P) and local (L) caches.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Ownership: the caller owns every buffer.  Device pointers point to device
+ *    memory the caller allocated; the library never allocates, frees or
+ *    synchronizes.  Host pointers (the config, the plan) are read during the
+ *    call only.
+ *  - Streams: every kernel is enqueued on `stream` (a hipStream_t; NULL means
+ *    the default stream).  No entry point reads device data back to the host,
+ *    so each call is asynchronous and may be captured into a hipGraph.
+ *  - Errors: arguments are checked on the host before any launch.  On failure
+ *    nothing is launched, a non-zero pbsa_status is returned and
+ *    pbsa_last_error() describes the problem.  A failed kernel launch returns
+ *    PBSA_ERR_HIP.
+ *  - Layouts (all row-major, contiguous):
+ *      q, o, dout, dq        [B, H, Nq, D]   Nq = chunk tokens, raster order
+ *                                            (frame, row, column)
+ *      k_local, v_local,     [B, H, NL, D]   NL = local_cache_size; physical
+ *      dk_local, dv_local                    chunk slot c holds tokens
+ *                                            [c*Nq, (c+1)*Nq), raster order
+ *      k_pers, v_pers,       [B, H, S, C, D] S persistent slots of C rows
+ *      dk_pers, dv_pers                      (C = block_t*block_h*block_w);
+ *                                            rows >= persist_len are zero
+ *      persist_len, persist_src  [B, H, S] int32
+ *      persist_kbar          [B, H, S, D] float32 (mean of the slot's rows)
+ *      kbar_local            [B, H, NL_blocks, D] float32, physical order
+ *      topk_idx              [B, H, NQ_blocks, K] int32 physical local block
+ *                                            ids, ascending
+ *      mass                  [B, H, S + NL_blocks] float32 (slot s at s,
+ *                                            physical local block p at S+p)
+ *      lse                   [B, H, Nq] float32 (natural log)
+ *      ring_head             one int32 on the device: physical chunk slot of
+ *                                            the oldest local chunk
+ *    Element type of q/k/v/o/dout is bf16 (PBSA_BF16) or fp32 (PBSA_FP32);
+ *    gradients are always fp32.
+ *  - Blocks: a frame of frame_h x frame_w tokens is tiled into
+ *    ceil(h/block_h) x ceil(w/block_w) blocks in block-row-major order (edge
+ *    blocks are smaller); with block_t > 1 a block spans block_t frames.  The
+ *    chunk's blocks are the query blocks; local physical block p is block
+ *    (p mod NQ_blocks) of chunk slot (p div NQ_blocks).
+ */
+#ifndef PBSA_H
+#define PBSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PBSA_OK = 0,
+  PBSA_ERR_INVALID_ARG = -1,  /* inconsistent sizes, null pointer, bad value */
+  PBSA_ERR_UNSUPPORTED = -2,  /* valid but not implemented (e.g. head_dim 96) */
+  PBSA_ERR_ALIGNMENT = -3,    /* a tensor pointer is not 16-byte aligned */
+  PBSA_ERR_WORKSPACE = -4,    /* workspace missing or smaller than planned */
+  PBSA_ERR_HIP = -5           /* the HIP runtime reported an error */
+} pbsa_status;
+
+typedef enum { PBSA_BF16 = 0, PBSA_FP32 = 1 } pbsa_dtype;
+
+/* Mirrors the SparseForcingAttention constructor of the project page's usage
+ * example, plus the latent frame grid and batch geometry it leaves implicit. */
+typedef struct {
+  int32_t batch, heads, head_dim;      /* head_dim in {64, 128} */
+  int32_t frame_h, frame_w;            /* latent tokens per frame (e.g. 30 x 52) */
+  int32_t block_t, block_h, block_w;   /* sparse_kv_block_size, e.g. [1, 8, 8] */
+  int32_t chunk_frames;                /* frames per generated chunk (multiple of block_t) */
+  int64_t total_cache_size;            /* tokens; must equal local + persistent */
+  int64_t local_cache_size;            /* tokens; a whole number of chunks (the ring) */
+  int64_t persistent_cache_size;       /* tokens; a whole number of block_t-frame groups */
+  int32_t use_local_block_sparse_attn; /* 0: attend every local block (k = all) */
+  float topk_ratio;                    /* local_block_sparse_topk_ratio, in (0, 1] */
+  float softmax_scale;                 /* 0 means 1/sqrt(head_dim) */
+  int32_t dtype;                       /* pbsa_dtype of q/k/v/o/dout */
+} pbsa_config;
+
+/* Derived sizes and workspace requirements (bytes). */
+typedef struct {
+  int32_t blocks_per_chunk;   /* NQ_blocks: query blocks = blocks per chunk */
+  int32_t local_blocks;       /* NL_blocks */
+  int32_t ring_chunks;        /* R = local_cache_size / chunk tokens */
+  int32_t persistent_slots;   /* S */
+  int32_t slot_rows;          /* C = block_t*block_h*block_w */
+  int32_t topk;               /* K = clamp(ceil(ratio*NL_blocks - 1e-6), 1, NL_blocks) */
+  int32_t chunk_tokens;       /* Nq */
+  int32_t max_block_tokens;   /* largest block */
+  size_t ws_score_select;
+  size_t ws_fwd;
+  size_t ws_bwd;
+  size_t ws_persist_update;
+} pbsa_plan_info;
+
+/* Validate a configuration and derive its sizes.  Host only; touches no GPU.
+ * Returns PBSA_ERR_INVALID_ARG for inconsistent sizes (total != local +
+ * persistent, a local cache that is not whole chunks, a persistent cache that
+ * is not whole frame groups, ratio outside (0,1]) and PBSA_ERR_UNSUPPORTED for
+ * head_dim outside {64,128} or blocks of more than 64 tokens. */
+pbsa_status pbsa_plan(const pbsa_config* cfg, pbsa_plan_info* out);
+
+/* Mean of each persistent slot's first persist_len rows -> persist_kbar (zero
+ * for empty slots).  Used to initialise the pooled-key metadata of a
+ * persistent cache that was filled from outside the library (reading: block
+ * scores use mean-pooled keys). */
+pbsa_status pbsa_pool_slots(const pbsa_config* cfg, const void* k_pers, const int32_t* persist_len,
+                            float* persist_kbar, void* stream);
+
+/* Block scoring and top-k selection ("learned top-k selection" on the project
+ * page; "dynamically selected local neighborhood" in the abstract), plus the
+ * pooled attention masses that drive the persistent update.
+ *   q, k_local      inputs (dtype)
+ *   ring_head       device int32, oldest chunk slot; ties in the top-k go to
+ *                   the lower logical index (oldest chunk first)
+ *   persist_kbar, persist_len   persistent slot metadata
+ *   topk_idx        out [B,H,NQ_blocks,K] physical ids, ascending
+ *   mass            out [B,H,S+NL_blocks]: for every query block a softmax of
+ *                   scale*qbar.kbar over valid slots and all local blocks,
+ *                   summed over query blocks (empty slots get 0)
+ *   kbar_local      out [B,H,NL_blocks,D] pooled local keys
+ *   ws, ws_bytes    workspace of at least plan.ws_score_select bytes */
+pbsa_status pbsa_score_select(const pbsa_config* cfg, const void* q, const void* k_local,
+                              const int32_t* ring_head, const float* persist_kbar,
+                              const int32_t* persist_len, int32_t* topk_idx, float* mass,
+                              float* kbar_local, void* ws, size_t ws_bytes, void* stream);
+
+/* Sparse attention forward.  Every query token of query block i attends all
+ * valid rows of all persistent slots and every token of the K local blocks
+ * topk_idx[b,h,i,:], with one softmax over that union.  Writes o (dtype) and
+ * lse (float32, natural log).  ws may be NULL when plan.ws_fwd is 0. */
+pbsa_status pbsa_fwd(const pbsa_config* cfg, const void* q, const void* k_pers, const void* v_pers,
+                     const int32_t* persist_len, const void* k_local, const void* v_local,
+                     const int32_t* topk_idx, void* o, float* lse, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/* Backward of pbsa_fwd for a fixed block mask ("full gradient support for
+ * training" on the project page).  Inputs as in pbsa_fwd plus o, lse (from
+ * pbsa_fwd) and dout.  Writes float32 dq, dk_pers, dv_pers, dk_local,
+ * dv_local, overwriting them entirely (rows that receive no gradient are set
+ * to zero).  Deterministic: no floating-point atomics.  ws of at least
+ * plan.ws_bwd bytes. */
+pbsa_status pbsa_bwd(const pbsa_config* cfg, const void* q, const void* k_pers, const void* v_pers,
+                     const int32_t* persist_len, const void* k_local, const void* v_local,
+                     const int32_t* topk_idx, const void* o, const float* lse, const void* dout,
+                     float* dq, float* dk_pers, float* dv_pers, float* dk_local, float* dv_local,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* Persistent-cache update of the cache pass ("update P and L" in the paper's
+ * algorithm; "compress, preserve, and update these persistent blocks" in the
+ * abstract).  Candidates are the valid slots and the NQ_blocks blocks of the
+ * oldest local chunk (physical slot *ring_head).  The S candidates of largest
+ * mass are kept (ties: incumbents first, then lower slot / block index).
+ * Vacated slots, ascending, receive the admitted blocks, ascending: their rows
+ * are copied (zero padding), len = block size, src = step_id*NQ_blocks + e,
+ * kbar = kbar_local of the block.  Vacated slots left over are emptied (len 0,
+ * rows 0, src INT32_MIN, kbar 0).  n_replaced[b,h] receives the admitted
+ * count.  Finally *ring_head advances to (ring_head+1) mod R, so the evicted
+ * chunk slot becomes the newest and is free for the next chunk.  ws of at
+ * least plan.ws_persist_update bytes. */
+pbsa_status pbsa_persist_update(const pbsa_config* cfg, const float* mass, const void* k_local,
+                                const void* v_local, const float* kbar_local, int32_t* ring_head,
+                                int32_t step_id, void* k_pers, void* v_pers, int32_t* persist_len,
+                                int32_t* persist_src, float* persist_kbar, int32_t* n_replaced,
+                                void* ws, size_t ws_bytes, void* stream);
+
+/* Write a new chunk's keys and values ([B,H,Nq,D] each) into the newest local
+ * ring slot, physical slot (ring_head + R - 1) mod R, reading ring_head on the
+ * device (so one captured graph serves every step of a rollout). */
+pbsa_status pbsa_ring_append(const pbsa_config* cfg, const void* k_new, const void* v_new,
+                             const int32_t* ring_head, void* k_local, void* v_local, void* stream);
+
+/* Text of the last error on the calling thread ("" if none). */
+const char* pbsa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PBSA_H */

@@ -1,0 +1,101 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every symbol include/pbsa.h declares, derives the same sizes as the oracle's
+geometry, and rejects bad arguments before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_attention_15_amd as pb
+from block_sparse_attention_15_amd import _lib
+import oracle
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "pbsa.h")).read()
+    return sorted(set(re.findall(r"\b(pbsa_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = pb.load_library()
+    decl = declared_symbols()
+    assert "pbsa_fwd" in decl and "pbsa_bwd" in decl
+    for name in decl:
+        assert hasattr(lib, name), name
+    assert sorted(_lib.exported_symbols()) == decl
+
+
+@pytest.mark.parametrize("cfg", [
+    synth.workload("decode_c1"),
+    synth.workload("tiny_fp32"),
+    dict(synth.workload("decode_c1"), frame_h=14, frame_w=22, total_cache_size=7 * 308, local_cache_size=4 * 308,
+         persistent_cache_size=3 * 308, chunk_frames=2, topk_ratio=0.3),
+    dict(synth.workload("decode_c1"), block_t=3, block_h=4, block_w=4),
+    dict(synth.workload("decode_c1"), use_local_block_sparse_attn=0),
+])
+def test_plan_matches_oracle_geometry(cfg):
+    p = pb.pbsa_plan(cfg)
+    g = oracle.geometry(cfg)
+    assert (p.blocks_per_chunk, p.local_blocks, p.ring_chunks, p.persistent_slots, p.slot_rows, p.topk,
+            p.chunk_tokens) == (g.n_qblk, g.n_lblk, g.R, g.S, g.cap, g.topk, g.chunk_tokens)
+    assert p.max_block_tokens == int(g.block_len.max())
+
+
+def test_plan_footprint_c1():
+    p = pb.pbsa_plan(synth.workload("decode_c1"))
+    assert (p.blocks_per_chunk, p.local_blocks, p.persistent_slots, p.topk) == (84, 168, 168, 21)
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(total_cache_size=1), _lib.PBSA_ERR_INVALID_ARG),
+    (dict(local_cache_size=9000, total_cache_size=18360), _lib.PBSA_ERR_INVALID_ARG),
+    (dict(persistent_cache_size=9000, total_cache_size=18360), _lib.PBSA_ERR_INVALID_ARG),
+    (dict(topk_ratio=0.0), _lib.PBSA_ERR_INVALID_ARG),
+    (dict(topk_ratio=1.5), _lib.PBSA_ERR_INVALID_ARG),
+    (dict(chunk_frames=2, block_t=3), _lib.PBSA_ERR_INVALID_ARG),
+    (dict(head_dim=96), _lib.PBSA_ERR_UNSUPPORTED),
+    (dict(block_h=16), _lib.PBSA_ERR_UNSUPPORTED),
+    (dict(heads=0), _lib.PBSA_ERR_INVALID_ARG),
+    (dict(dtype=7), _lib.PBSA_ERR_INVALID_ARG),
+])
+def test_plan_rejects(bad, status):
+    cfg = dict(synth.workload("decode_c1"), **bad)
+    with pytest.raises(pb.PbsaError) as ei:
+        pb.pbsa_plan(cfg)
+    assert ei.value.status == status
+    assert pb.load_library().pbsa_last_error().decode()
+
+
+def _raw_fwd(cfg, **ptrs):
+    lib = pb.load_library()
+    c = pb.make_config(cfg)
+    a = dict(q=0x1000, kp=0x2000, vp=0x3000, plen=0x4000, kl=0x5000, vl=0x6000, topk=0x7000, o=0x8000,
+             lse=0x9000)
+    a.update(ptrs)
+    return lib.pbsa_fwd(ctypes.byref(c), *(ctypes.c_void_p(a[k]) for k in
+                                          ("q", "kp", "vp", "plen", "kl", "vl", "topk", "o", "lse")),
+                        None, 0, None)
+
+
+def test_pointer_checks_before_launch():
+    cfg = synth.workload("decode_c1")
+    # these fake addresses are rejected on the host; nothing is launched
+    assert _raw_fwd(cfg, q=0) == _lib.PBSA_ERR_INVALID_ARG
+    assert _raw_fwd(cfg, o=0x8004) == _lib.PBSA_ERR_ALIGNMENT
+    lib = pb.load_library()
+    c = pb.make_config(cfg)
+    st = lib.pbsa_score_select(ctypes.byref(c), *(ctypes.c_void_p(0x1000 * (i + 1)) for i in range(8)),
+                               None, 0, None)
+    assert st == _lib.PBSA_ERR_WORKSPACE
+    p = pb.pbsa_plan(cfg)
+    st = lib.pbsa_score_select(ctypes.byref(c), *(ctypes.c_void_p(0x1000 * (i + 1)) for i in range(8)),
+                               ctypes.c_void_p(0x10000), p.ws_score_select - 1, None)
+    assert st == _lib.PBSA_ERR_WORKSPACE
+    st = lib.pbsa_persist_update(ctypes.byref(c), *(ctypes.c_void_p(0x1000 * (i + 1)) for i in range(5)),
+                                 ctypes.c_int32(-1), *(ctypes.c_void_p(0x1000 * (i + 1)) for i in range(6)),
+                                 ctypes.c_void_p(0x10000), p.ws_persist_update, None)
+    assert st == _lib.PBSA_ERR_INVALID_ARG
