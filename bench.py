@@ -84,6 +84,7 @@ class Bench:
         self.ws_s = pb.workspace(p, "score_select")
         self.ws_b = pb.workspace(p, "bwd")
         self.ws_u = pb.workspace(p, "persist_update")
+        self.ws_f = pb.workspace(p, "fwd")
         self.step_id = 0
 
     def reset(self):
@@ -107,7 +108,8 @@ class Bench:
         pb.pbsa_score_select(p, self.q, L["k_l"], L["ring_head"], self.pkbar, L["plen"], self.topk, self.mass,
                              self.kbar_l, self.ws_s)
         mark(2)
-        pb.pbsa_fwd(p, self.q, L["k_p"], L["v_p"], L["plen"], L["k_l"], L["v_l"], self.topk, self.o, self.lse)
+        pb.pbsa_fwd(p, self.q, L["k_p"], L["v_p"], L["plen"], L["k_l"], L["v_l"], self.topk, self.o, self.lse,
+                    self.ws_f)
         mark(3)
         pb.pbsa_bwd(p, self.q, L["k_p"], L["v_p"], L["plen"], L["k_l"], L["v_l"], self.topk, self.o, self.lse,
                     self.dout, self.dq, self.dk_p, self.dv_p, self.dk_l, self.dv_l, self.ws_b)

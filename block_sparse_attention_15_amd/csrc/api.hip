@@ -119,7 +119,7 @@ pbsa_status make_plan(const pbsa_config* c, Plan* p) {
   in.max_block_tokens = mx;
   const size_t BH = (size_t)g.B * g.H;
   in.ws_score_select = align256(BH * g.nq * g.D * 4) + align256(BH * g.nq * (g.S + g.nl) * 4);
-  in.ws_fwd = 0;
+  in.ws_fwd = fwd_workspace(g);
   in.ws_bwd = align256(BH * g.ct * 4) + align256(BH * g.nl * 4) + align256(BH * g.nl * g.nq * 4);
   in.ws_persist_update = align256(BH * g.S * 4);
   return PBSA_OK;
@@ -229,7 +229,7 @@ pbsa_status pbsa_fwd(const pbsa_config* cfg, const void* q, const void* k_pers, 
     REQUIRE_PTR(persist_len);
   }
   if ((st = check_ws(ws, ws_bytes, p.info.ws_fwd)) != PBSA_OK) return st;
-  return hip_status(launch_fwd(p.g, q, k_pers, v_pers, persist_len, k_local, v_local, topk_idx, o, lse,
+  return hip_status(launch_fwd(p.g, q, k_pers, v_pers, persist_len, k_local, v_local, topk_idx, o, lse, ws,
                                (hipStream_t)stream),
                     "pbsa_fwd");
 }

@@ -94,8 +94,9 @@ hipError_t launch_score_select(const Geo& g, const void* q, const void* k_l, con
                                const float* kbar_p, const int32_t* plen, int32_t* topk, float* mass,
                                float* kbar_l, WsScore ws, hipStream_t s);
 hipError_t launch_fwd(const Geo& g, const void* q, const void* k_p, const void* v_p, const int32_t* plen,
-                      const void* k_l, const void* v_l, const int32_t* topk, void* o, float* lse,
+                      const void* k_l, const void* v_l, const int32_t* topk, void* o, float* lse, void* ws,
                       hipStream_t s);
+size_t fwd_workspace(const Geo& g);
 struct WsBwd {
   float* delta;     // [B,H,Nq]      rowsum(dO * O)
   int32_t* tcount;  // [B,H,nl]      query blocks that selected each local block

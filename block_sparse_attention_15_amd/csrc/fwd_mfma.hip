@@ -1,0 +1,495 @@
+// Sparse attention forward on the gfx950 matrix cores (bf16 inputs, head_dim
+// 64 or 128).
+//
+// What is computed (abstract and project page of Sparse Forcing): every query
+// token of query block i attends all valid rows of every persistent slot and
+// every token of its K selected local blocks, with one softmax over that union.
+//
+// Mapping to CDNA4
+// ----------------
+//  * Two kernels.  The persistent slots are the same for every query of a
+//    head, so the first kernel is a dense attention of all of a head's
+//    queries (contiguous 256-row tiles, 4 waves x 64 rows) against the
+//    compact persistent memory, each slot staged once in LDS for the four
+//    waves; it writes a normalised fp32 partial output and its log-sum-exp.
+//    The second kernel handles the selected local blocks, which differ per
+//    query block: 8 waves = 4 query blocks x 2 tiles of 32 queries, one LDS
+//    region per query block per step; it merges its result with the
+//    persistent partial by log-sum-exp and writes O (bf16) and LSE.
+//  * The products are computed transposed with v_mfma_f32_32x32x16_bf16:
+//    S^T = K Q^T (keys x queries) and O^T += V^T P^T.  In the result layout a
+//    lane holds one query and 16 of the tile's 32 keys, so the online softmax
+//    is lane-local plus one exchange with lane^32 (v_permlane32_swap), the
+//    P^T operand of the second product is already in the right registers
+//    (keys reordered consistently on both operands), and the O rescale is a
+//    per-lane scalar multiply.
+//  * K is read from LDS as the A operand with 16-byte reads; V is read
+//    transposed with ds_read_b64_tr_b16 (two per 8-key operand).  Both LDS
+//    tiles are XOR-swizzled at 16-byte granularity to spread banks.
+//  * LDS is double-buffered (2 x 64 KB); the next step's rows are prefetched
+//    into registers while the current step computes, so there is one barrier
+//    per step.
+//  * exp2 with softmax_scale*log2(e) folded into one FMA; the running max is
+//    only raised when a tile's max exceeds it by more than 2^8 (P values stay
+//    below 256, safe in bf16 and fp32), which makes O rescales rare.
+//  * Workgroup ids are remapped so that each XCD (ids i, i+8, ...) works on a
+//    contiguous range of (head, query tile): a head's persistent K/V is then
+//    read by one or two XCDs instead of all eight.
+#include "common.h"
+
+namespace pbsa {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kBufBytes = 64 * 1024;
+
+template <int D> struct Shape {
+  static constexpr int CPR = D / 8;    // 16-byte chunks per row
+  static constexpr int KS = D / 16;    // k-steps of S^T = K Q^T
+  static constexpr int DT = D / 32;    // 32-wide d tiles of O^T
+  static constexpr int ROWB = D * 2;   // bytes per bf16 row
+};
+
+__device__ __forceinline__ int swz_k(int r, int c, int cpr) { return c ^ (r & (cpr - 1)); }
+__device__ __forceinline__ int swz_v(int r, int c, int cpr) { return c ^ (((r & 3) << 2) & (cpr - 1)); }
+
+__device__ __forceinline__ float half_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ void st16(char* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+
+struct FwdArgs {
+  Geo g;
+  const bf16_t* q;
+  const bf16_t* kp;
+  const bf16_t* vp;
+  const int32_t* plen;
+  const bf16_t* kl;
+  const bf16_t* vl;
+  const int32_t* topk;
+  bf16_t* o;
+  float* lse;
+  float* o_part;    // [B,H,ct,D] persistent-part output (normalised), fp32
+  float* lse_part;  // [B,H,ct]   its log-sum-exp (-inf when no slot is valid)
+  int ntiles;       // work items per (batch, head)
+};
+
+// Per-wave online-softmax state for NT tiles of 32 queries.
+template <int D, int NT> struct WaveState {
+  bf16x8_t qf[NT][Shape<D>::KS];
+  f32x16_t o[NT][Shape<D>::DT];
+  float m[NT];  // running max in log2 units (scores times scale*log2e)
+  float l[NT];  // partial row sum over this lane's keys
+};
+
+// One 32-key tile in LDS: K rows kbase[row0 .. row0+31], V rows likewise,
+// the first nvalid (1..32) keys valid.  ntq (<= NT) query tiles are active.
+template <int D, int NT>
+__device__ __forceinline__ void tile(const char* kbase, const char* vbase, int row0, int nvalid, int ntq, float c2,
+                                     WaveState<D, NT>& st) {
+  using Sh = Shape<D>;
+  const int lane = threadIdx.x & 63, h = lane >> 5, l32 = lane & 31;
+  f32x16_t s[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) s[n] = f32x16_t{};
+  {
+    const int r = row0 + l32;
+    const char* krow = kbase + r * Sh::ROWB;
+#pragma unroll
+    for (int ks = 0; ks < Sh::KS; ++ks) {
+      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(krow + swz_k(r, 2 * ks + h, Sh::CPR) * 16);
+#pragma unroll
+      for (int n = 0; n < NT; ++n)
+        if (n < ntq) s[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.qf[n][ks], s[n], 0, 0, 0);
+    }
+  }
+  if (nvalid < 32) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int kk = 8 * (j >> 2) + 4 * h + (j & 3);
+      if (kk >= nvalid) {
+#pragma unroll
+        for (int n = 0; n < NT; ++n) s[n][j] = -INFINITY;
+      }
+    }
+  }
+  bf16x8_t pk[NT][2];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    if (n < ntq) {
+      float tm = s[n][0];
+#pragma unroll
+      for (int j = 1; j < 16; ++j) tm = fmaxf(tm, s[n][j]);
+      tm = half_max(tm) * c2;
+      // raise the running max only when the tile exceeds it by more than 2^8
+      if (__builtin_amdgcn_ballot_w64(tm > st.m[n] + 8.0f)) {
+        const float mn = fmaxf(st.m[n], tm);
+        const float f = __builtin_amdgcn_exp2f(st.m[n] - mn);
+        st.l[n] *= f;
+#pragma unroll
+        for (int dt = 0; dt < Sh::DT; ++dt) st.o[n][dt] *= f;
+        st.m[n] = mn;
+      }
+      const float mneg = -st.m[n];
+      float ls = 0.f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[n][j], c2, mneg));
+        ls += p;
+        pk[n][j >> 3][j & 7] = (__bf16)p;
+      }
+      st.l[n] += ls;
+    }
+  }
+  // O^T += V^T P^T; A = V^T (d x keys) read transposed from LDS
+  const int G = lane >> 4, s16 = lane & 15;
+#pragma unroll
+  for (int dt = 0; dt < Sh::DT; ++dt) {
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2) {
+      s16x4_t part[2];
+#pragma unroll
+      for (int h8 = 0; h8 < 2; ++h8) {
+        const int r = row0 + 16 * ks2 + 8 * h8 + 4 * (G >> 1) + (s16 >> 2);
+        const int col = 32 * dt + 16 * (G & 1) + 4 * (s16 & 3);
+        const char* p = vbase + r * Sh::ROWB + swz_v(r, col >> 3, Sh::CPR) * 16 + (col & 7) * 2;
+        part[h8] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(p));
+      }
+      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, (__attribute__((ext_vector_type(8))) short){
+          part[0][0], part[0][1], part[0][2], part[0][3], part[1][0], part[1][1], part[1][2], part[1][3]});
+#pragma unroll
+      for (int n = 0; n < NT; ++n)
+        if (n < ntq) st.o[n][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[n][ks2], st.o[n][dt], 0, 0, 0);
+    }
+  }
+}
+
+template <int D, int NT>
+__device__ __forceinline__ void init_state(WaveState<D, NT>& st) {
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+#pragma unroll
+    for (int dt = 0; dt < Shape<D>::DT; ++dt) st.o[n][dt] = f32x16_t{};
+    st.m[n] = -INFINITY;
+    st.l[n] = 0.f;
+  }
+}
+
+template <int D, int NT>
+__device__ __forceinline__ void load_q(const bf16_t* qrow, bool ok, int n, WaveState<D, NT>& st) {
+  const int h = (threadIdx.x & 63) >> 5;
+#pragma unroll
+  for (int ks = 0; ks < Shape<D>::KS; ++ks) {
+    const uint4 v = ok ? ld16(qrow + 16 * ks + 8 * h) : make_uint4(0, 0, 0, 0);
+    st.qf[n][ks] = __builtin_bit_cast(bf16x8_t, v);
+  }
+}
+
+// XCD-aware remap of a 1-D grid: hardware places workgroup i on XCD i % 8,
+// so give each XCD a contiguous range of the linear work index.
+__device__ __forceinline__ int xcd_remap(int total) {
+  const int per_xcd = (total + 7) / 8;
+  return (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+}
+
+// ---------------------------------------------------------------------------
+// Kernel 1: every query of a head against all persistent slots (dense over
+// the compact memory).  4 waves x 64 contiguous query rows; slot K/V staged
+// in LDS once per workgroup.  Writes the normalised partial output and its
+// log-sum-exp.
+// ---------------------------------------------------------------------------
+constexpr int kPersWaves = 4;
+constexpr int kPersThreads = 64 * kPersWaves;
+constexpr int kPersRows = 64 * kPersWaves;
+
+template <int D> struct PersPrefetch {
+  static constexpr int N = 64 * Shape<D>::CPR / kPersThreads;  // chunks per thread per tensor
+  uint4 k[N], v[N];
+};
+
+template <int D>
+__device__ __forceinline__ void pers_load(const FwdArgs& a, size_t bh, int s, PersPrefetch<D>& pf) {
+  using Sh = Shape<D>;
+  const Geo& g = a.g;
+  const int n = min(a.plen[bh * g.S + s], g.C);
+  const bf16_t* kb = a.kp + (bh * g.S + s) * (size_t)g.C * D;
+  const bf16_t* vb = a.vp + (bh * g.S + s) * (size_t)g.C * D;
+#pragma unroll
+  for (int u = 0; u < PersPrefetch<D>::N; ++u) {
+    const int id = threadIdx.x + kPersThreads * u, r = id / Sh::CPR, c = id % Sh::CPR;
+    const bool ok = r < n;
+    pf.k[u] = ok ? ld16(kb + (size_t)r * D + c * 8) : make_uint4(0, 0, 0, 0);
+    pf.v[u] = ok ? ld16(vb + (size_t)r * D + c * 8) : make_uint4(0, 0, 0, 0);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void pers_store(const PersPrefetch<D>& pf, char* buf) {
+  using Sh = Shape<D>;
+#pragma unroll
+  for (int u = 0; u < PersPrefetch<D>::N; ++u) {
+    const int id = threadIdx.x + kPersThreads * u, r = id / Sh::CPR, c = id % Sh::CPR;
+    st16(buf + r * Sh::ROWB + swz_k(r, c, Sh::CPR) * 16, pf.k[u]);
+    st16(buf + 64 * Sh::ROWB + r * Sh::ROWB + swz_v(r, c, Sh::CPR) * 16, pf.v[u]);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kPersThreads, 1) void fwd_pers_kernel(FwdArgs a) {
+  using Sh = Shape<D>;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const Geo& g = a.g;
+  const int total = g.B * g.H * a.ntiles;
+  const int lin = xcd_remap(total);
+  if (lin >= total) return;
+  const int qt = lin % a.ntiles;
+  const size_t bh = lin / a.ntiles;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, h = lane >> 5, l32 = lane & 31;
+  const int row_w = qt * kPersRows + 64 * wave;  // first query row of this wave
+  const int ntq = max(0, min(2, (g.ct - row_w + 31) / 32));
+
+  WaveState<D, 2> st;
+  init_state(st);
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    const int r = row_w + 32 * n + l32;
+    load_q(a.q + (bh * g.ct + min(r, g.ct - 1)) * D, r < g.ct, n, st);
+  }
+  const float c2 = g.scale * 1.4426950408889634f;
+
+  if (g.S > 0) {
+    PersPrefetch<D> pf;
+    pers_load<D>(a, bh, 0, pf);
+    pers_store<D>(pf, smem);
+    __syncthreads();
+    for (int s = 0; s < g.S; ++s) {
+      char* buf = smem + (s & 1) * kBufBytes;
+      const int n = min(a.plen[bh * g.S + s], g.C);
+      if (s + 1 < g.S) pers_load<D>(a, bh, s + 1, pf);
+      if (ntq > 0) {
+        if (n > 0) tile<D, 2>(buf, buf + 64 * Sh::ROWB, 0, min(n, 32), ntq, c2, st);
+        if (n > 32) tile<D, 2>(buf, buf + 64 * Sh::ROWB, 32, n - 32, ntq, c2, st);
+      }
+      if (s + 1 < g.S) pers_store<D>(pf, smem + ((s + 1) & 1) * kBufBytes);
+      __syncthreads();
+    }
+  }
+
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    if (n < ntq) {
+      const int r = row_w + 32 * n + l32;
+      const float lt = half_sum(st.l[n]);
+      if (r < g.ct) {
+        float* orow = a.o_part + (bh * g.ct + r) * D;
+        const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+#pragma unroll
+        for (int dt = 0; dt < Sh::DT; ++dt) {
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) {
+            const int d0 = 32 * dt + 8 * i4 + 4 * h;
+            *reinterpret_cast<float4*>(orow + d0) =
+                make_float4(st.o[n][dt][4 * i4] * inv, st.o[n][dt][4 * i4 + 1] * inv, st.o[n][dt][4 * i4 + 2] * inv,
+                            st.o[n][dt][4 * i4 + 3] * inv);
+          }
+        }
+        if (h == 0) a.lse_part[bh * g.ct + r] = lt > 0.f ? st.m[n] * 0.6931471805599453f + logf(lt) : -INFINITY;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Kernel 2: each query block against its K selected local blocks, merged with
+// the persistent partial by log-sum-exp.  8 waves = 4 query blocks x 2 query
+// tiles; per step the workgroup stages 32 rows of each block's current
+// selected block (one LDS region per query block).
+// ---------------------------------------------------------------------------
+constexpr int kLocBlocks = 4;
+constexpr int kLocWaves = 2 * kLocBlocks;
+constexpr int kLocThreads = 64 * kLocWaves;
+
+template <int D> struct LocPrefetch {
+  static constexpr int N = kLocBlocks * 32 * Shape<D>::CPR / kLocThreads;
+  uint4 k[N], v[N];
+};
+
+template <int D>
+__device__ __forceinline__ void loc_load(const FwdArgs& a, size_t bh, int qg, int j, LocPrefetch<D>& pf) {
+  using Sh = Shape<D>;
+  const Geo& g = a.g;
+  const int t = j >> 1, half = j & 1;
+  const bf16_t* kb = a.kl + bh * (size_t)g.NL * D;
+  const bf16_t* vb = a.vl + bh * (size_t)g.NL * D;
+#pragma unroll
+  for (int u = 0; u < LocPrefetch<D>::N; ++u) {
+    const int id = threadIdx.x + kLocThreads * u;
+    const int w = id / (32 * Sh::CPR), rem = id % (32 * Sh::CPR);
+    const int r = 32 * half + rem / Sh::CPR, c = rem % Sh::CPR;
+    const int qb = qg * kLocBlocks + w;
+    bool ok = false;
+    size_t off = 0;
+    if (qb < g.nq) {
+      const int p = a.topk[(bh * g.nq + qb) * g.K + t];
+      if ((unsigned)p < (unsigned)g.nl) {
+        const BlockExt e = block_ext(g, p % g.nq);
+        if (r < e.len) {
+          ok = true;
+          off = ((size_t)(p / g.nq) * g.ct + block_token(g, e, r)) * D + c * 8;
+        }
+      }
+    }
+    pf.k[u] = ok ? ld16(kb + off) : make_uint4(0, 0, 0, 0);
+    pf.v[u] = ok ? ld16(vb + off) : make_uint4(0, 0, 0, 0);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void loc_store(const LocPrefetch<D>& pf, char* buf) {
+  using Sh = Shape<D>;
+#pragma unroll
+  for (int u = 0; u < LocPrefetch<D>::N; ++u) {
+    const int id = threadIdx.x + kLocThreads * u;
+    const int w = id / (32 * Sh::CPR), rem = id % (32 * Sh::CPR);
+    const int r = rem / Sh::CPR, c = rem % Sh::CPR;
+    char* region = buf + w * (64 * Sh::ROWB);
+    st16(region + r * Sh::ROWB + swz_k(r, c, Sh::CPR) * 16, pf.k[u]);
+    st16(region + 32 * Sh::ROWB + r * Sh::ROWB + swz_v(r, c, Sh::CPR) * 16, pf.v[u]);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kLocThreads, 1) void fwd_local_kernel(FwdArgs a) {
+  using Sh = Shape<D>;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const Geo& g = a.g;
+  const int total = g.B * g.H * a.ntiles;
+  const int lin = xcd_remap(total);
+  if (lin >= total) return;
+  const int qg = lin % a.ntiles;
+  const size_t bh = lin / a.ntiles;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, h = lane >> 5, l32 = lane & 31;
+  const int qb = qg * kLocBlocks + (wave >> 1), nt = wave & 1;
+  const bool has_q = qb < g.nq;
+  const BlockExt qe = block_ext(g, has_q ? qb : 0);
+  const int ntq = has_q && 32 * nt < qe.len ? 1 : 0;
+  const int r = 32 * nt + l32;
+  const bool row_ok = ntq && r < qe.len;
+  const int tok = row_ok ? block_token(g, qe, r) : 0;
+
+  WaveState<D, 1> st;
+  init_state(st);
+  load_q(a.q + (bh * g.ct + tok) * D, row_ok, 0, st);
+  const float c2 = g.scale * 1.4426950408889634f;
+
+  const int nsteps = 2 * g.K;
+  LocPrefetch<D> pf;
+  loc_load<D>(a, bh, qg, 0, pf);
+  loc_store<D>(pf, smem);
+  __syncthreads();
+  for (int j = 0; j < nsteps; ++j) {
+    char* buf = smem + (j & 1) * kBufBytes;
+    int nv = 0;
+    if (ntq) {
+      const int p = a.topk[(bh * g.nq + qb) * g.K + (j >> 1)];
+      if ((unsigned)p < (unsigned)g.nl) nv = min(block_ext(g, p % g.nq).len - 32 * (j & 1), 32);
+    }
+    if (j + 1 < nsteps) loc_load<D>(a, bh, qg, j + 1, pf);
+    if (nv > 0) {
+      const char* region = buf + (wave >> 1) * (64 * Sh::ROWB);
+      tile<D, 1>(region, region + 32 * Sh::ROWB, 0, nv, 1, c2, st);
+    }
+    if (j + 1 < nsteps) loc_store<D>(pf, smem + ((j + 1) & 1) * kBufBytes);
+    __syncthreads();
+  }
+
+  // merge with the persistent partial and write O (bf16) and LSE
+  const float lt = half_sum(st.l[0]);
+  if (!row_ok) return;
+  const size_t row = bh * g.ct + tok;
+  const float lse_l = lt > 0.f ? st.m[0] * 0.6931471805599453f + logf(lt) : -INFINITY;
+  const float lse_p = a.lse_part[row];
+  const float mx = fmaxf(lse_l, lse_p);
+  const float wl = lse_l == -INFINITY ? 0.f : expf(lse_l - mx);
+  const float wp = lse_p == -INFINITY ? 0.f : expf(lse_p - mx);
+  const float den = wl + wp;
+  const float fl = lt > 0.f ? wl / (den * lt) : 0.f;  // local accumulators are unnormalised
+  const float fp = wp / den;
+  const float* op = a.o_part + row * D;
+  bf16_t* orow = a.o + row * D;
+#pragma unroll
+  for (int dt = 0; dt < Sh::DT; ++dt) {
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int d0 = 32 * dt + 8 * i4 + 4 * h;
+      const float4 pv = *reinterpret_cast<const float4*>(op + d0);
+      uint2 w;
+      w.x = (uint32_t)f2bf(fmaf(st.o[0][dt][4 * i4 + 0], fl, pv.x * fp)) |
+            ((uint32_t)f2bf(fmaf(st.o[0][dt][4 * i4 + 1], fl, pv.y * fp)) << 16);
+      w.y = (uint32_t)f2bf(fmaf(st.o[0][dt][4 * i4 + 2], fl, pv.z * fp)) |
+            ((uint32_t)f2bf(fmaf(st.o[0][dt][4 * i4 + 3], fl, pv.w * fp)) << 16);
+      *reinterpret_cast<uint2*>(orow + d0) = w;
+    }
+  }
+  if (h == 0) a.lse[row] = mx + logf(den);
+}
+
+template <typename K>
+hipError_t set_lds(K kernel, size_t bytes) {
+  return hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+template <int D>
+hipError_t launch_d(const FwdArgs& base, hipStream_t s) {
+  static bool attr = false;
+  const size_t shm = 2 * kBufBytes;
+  if (!attr) {
+    hipError_t e = set_lds(fwd_pers_kernel<D>, shm);
+    if (e == hipSuccess) e = set_lds(fwd_local_kernel<D>, shm);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  const Geo& g = base.g;
+  FwdArgs a = base;
+  a.ntiles = (g.ct + kPersRows - 1) / kPersRows;
+  int total = g.B * g.H * a.ntiles;
+  fwd_pers_kernel<D><<<((total + 7) / 8) * 8, kPersThreads, shm, s>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  a.ntiles = (g.nq + kLocBlocks - 1) / kLocBlocks;
+  total = g.B * g.H * a.ntiles;
+  fwd_local_kernel<D><<<((total + 7) / 8) * 8, kLocThreads, shm, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool fwd_mfma_supported(const Geo& g) {
+  return g.dtype == PBSA_BF16 && (g.D == 64 || g.D == 128) && g.C <= 64;
+}
+
+size_t fwd_mfma_workspace(const Geo& g) {
+  return ((size_t)g.B * g.H * g.ct * g.D * 4 + 255) / 256 * 256 + ((size_t)g.B * g.H * g.ct * 4 + 255) / 256 * 256;
+}
+
+hipError_t launch_fwd_mfma(const Geo& g, const void* q, const void* k_p, const void* v_p, const int32_t* plen,
+                           const void* k_l, const void* v_l, const int32_t* topk, void* o, float* lse, void* ws,
+                           hipStream_t s) {
+  float* o_part = (float*)ws;
+  float* lse_part = (float*)((char*)ws + ((size_t)g.B * g.H * g.ct * g.D * 4 + 255) / 256 * 256);
+  FwdArgs a{g, (const bf16_t*)q, (const bf16_t*)k_p, (const bf16_t*)v_p, plen, (const bf16_t*)k_l,
+            (const bf16_t*)v_l, topk, (bf16_t*)o, lse, o_part, lse_part, 0};
+  return g.D == 128 ? launch_d<128>(a, s) : launch_d<64>(a, s);
+}
+
+}  // namespace pbsa

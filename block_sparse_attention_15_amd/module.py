@@ -58,6 +58,7 @@ class SparseForcingAttention:
         self.ws_score = api.workspace(p, "score_select", device)
         self.ws_bwd = None
         self.ws_update = api.workspace(p, "persist_update", device)
+        self.ws_fwd = api.workspace(p, "fwd", device)
         self.topk_idx = torch.empty(s["topk_idx"], dtype=torch.int32, device=device)
         self.mass = torch.empty(s["mass"], dtype=torch.float32, device=device)
         self.kbar_local = torch.empty(s["kbar_local"], dtype=torch.float32, device=device)
@@ -93,7 +94,7 @@ class SparseForcingAttention:
         api.pbsa_score_select(p, query, cache.k_local, cache.ring_head, cache.persist_kbar, cache.persist_len,
                               self.topk_idx, self.mass, self.kbar_local, self.ws_score, stream)
         api.pbsa_fwd(p, query, cache.k_pers, cache.v_pers, cache.persist_len, cache.k_local, cache.v_local,
-                     self.topk_idx, o, lse, None, stream)
+                     self.topk_idx, o, lse, self.ws_fwd, stream)
         if update:
             api.pbsa_persist_update(p, self.mass, cache.k_local, cache.v_local, self.kbar_local, cache.ring_head,
                                     cache.step, cache.k_pers, cache.v_pers, cache.persist_len, cache.persist_src,

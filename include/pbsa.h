@@ -144,7 +144,9 @@ pbsa_status pbsa_score_select(const pbsa_config* cfg, const void* q, const void*
 /* Sparse attention forward.  Every query token of query block i attends all
  * valid rows of all persistent slots and every token of the K local blocks
  * topk_idx[b,h,i,:], with one softmax over that union.  Writes o (dtype) and
- * lse (float32, natural log).  ws may be NULL when plan.ws_fwd is 0. */
+ * lse (float32, natural log).  ws: at least plan.ws_fwd bytes (it holds the
+ * persistent-part partial output of the bf16 path; 0 bytes and NULL allowed for
+ * fp32). */
 pbsa_status pbsa_fwd(const pbsa_config* cfg, const void* q, const void* k_pers, const void* v_pers,
                      const int32_t* persist_len, const void* k_local, const void* v_local,
                      const int32_t* topk_idx, void* o, float* lse, void* ws, size_t ws_bytes,

@@ -49,6 +49,7 @@ class GpuStep:
         self.ws_score = pb.workspace(p, "score_select")
         self.ws_bwd = pb.workspace(p, "bwd")
         self.ws_update = pb.workspace(p, "persist_update")
+        self.ws_fwd = pb.workspace(p, "fwd")
         pb.pbsa_pool_slots(p, self.k_p, self.plen, self.pkbar)
 
     def score_select(self):
@@ -57,7 +58,7 @@ class GpuStep:
 
     def fwd(self, topk=None):
         pb.pbsa_fwd(self.p, self.q, self.k_p, self.v_p, self.plen, self.k_l, self.v_l,
-                    self.topk if topk is None else topk, self.o, self.lse)
+                    self.topk if topk is None else topk, self.o, self.lse, self.ws_fwd)
 
     def bwd(self, dout, topk=None):
         s = pb.shapes(self.p)
