@@ -1,0 +1,673 @@
+// Sparse attention backward on the gfx950 matrix cores (bf16 inputs, head_dim
+// 64 or 128).
+//
+// For the fixed block mask of the forward (all persistent slots plus each
+// query block's selected local blocks) the gradients are those of softmax
+// attention ("full gradient support for training" on the Sparse Forcing
+// project page):
+//   P = exp(scale q.k - lse),  dP = dO.v,  dS = P (dP - D),  D = rowsum(dO*O)
+//   dV = P^T dO,  dK = scale dS^T Q,  dQ = scale dS K.
+//
+// Four kernels, all deterministic (every output element is accumulated by one
+// lane in a fixed order; no atomics):
+//   dq_pers   query-outer over the persistent slots: 8 waves x 32 contiguous
+//             query rows; S^T = K Q^T and dP^T = V dO^T put one query per
+//             lane (lane-local P and dS), dQ^T += K^T dS^T reads K transposed
+//             from LDS (ds_read_b64_tr_b16).  Writes dq.
+//   dq_local  the same over each query block's selected local blocks (8 waves
+//             = 4 query blocks x 2 query tiles); adds into dq.
+//   dkv_pers  key-outer: 4 waves x 32 keys (two slots) stream every query of
+//             the head through LDS in 32-row tiles; S = Q K^T and dP = dO V^T
+//             put one key per lane, dV += P^T dO and dK += dS^T Q read dO and
+//             Q transposed from LDS.
+//   dkv_local key-outer over a local block (2 waves x 32 keys), streaming only
+//             the query blocks that selected it (a key-block -> query-block
+//             index built from the top-k lists).
+// LDS tiles hold 32 rows of 16-byte chunks XOR-swizzled so that both the
+// natural 16-byte reads (rows of one chunk column) and the transposed
+// ds_read_b64_tr_b16 reads (4 rows x 4 chunks per 16 lanes) avoid bank
+// conflicts.
+#include "common.h"
+
+namespace pbsa {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <int D> struct Sh {
+  static constexpr int CPR = D / 8;       // 16-byte chunks per row
+  static constexpr int KS = D / 16;       // k-steps over the head dimension
+  static constexpr int DT = D / 32;       // 32-wide tiles of the head dimension
+  static constexpr int ROWB = D * 2;      // bytes per bf16 row
+  static constexpr int TILEB = 32 * ROWB; // bytes per 32-row tile
+};
+
+__device__ __forceinline__ int swz(int r, int c, int cpr) {
+  return c ^ ((((r & 3) << 2) | ((r >> 2) & 3)) & (cpr - 1));
+}
+
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+__device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// 16-byte chunk c of row r of a 32-row LDS tile.
+template <int D>
+__device__ __forceinline__ bf16x8_t rd_nat(const char* t, int r, int c) {
+  return *reinterpret_cast<const bf16x8_t*>(t + r * Sh<D>::ROWB + swz(r, c, Sh<D>::CPR) * 16);
+}
+
+// Transposed operand from a 32-row tile: lane l receives column 32*dt + l%32
+// at rows 16*ks2 + 4*(l/32) + {0,1,2,3} and the same +8 (the row order that
+// matches the packing of a 32x32 MFMA result into the next product).
+template <int D>
+__device__ __forceinline__ bf16x8_t rd_tr(const char* t, int ks2, int dt) {
+  const int lane = threadIdx.x & 63, G = lane >> 4, s16 = lane & 15;
+  s16x4_t part[2];
+#pragma unroll
+  for (int h8 = 0; h8 < 2; ++h8) {
+    const int r = 16 * ks2 + 8 * h8 + 4 * (G >> 1) + (s16 >> 2);
+    const int col = 32 * dt + 16 * (G & 1) + 4 * (s16 & 3);
+    const char* p = t + r * Sh<D>::ROWB + swz(r, col >> 3, Sh<D>::CPR) * 16 + (col & 7) * 2;
+    part[h8] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(p));
+  }
+  return __builtin_bit_cast(bf16x8_t, s16x8_t{part[0][0], part[0][1], part[0][2], part[0][3], part[1][0],
+                                              part[1][1], part[1][2], part[1][3]});
+}
+
+__device__ __forceinline__ void st_chunk(char* tile, int rowb, int cpr, int r, int c, uint4 v) {
+  *reinterpret_cast<uint4*>(tile + r * rowb + swz(r, c, cpr) * 16) = v;
+}
+
+__device__ __forceinline__ bf16x8_t pack8(const f32x16_t& x, int ks2) {
+  bf16x8_t r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (__bf16)x[8 * ks2 + i];
+  return r;
+}
+
+__device__ __forceinline__ int xcd_remap(int total) {
+  const int per_xcd = (total + 7) / 8;
+  return (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+}
+
+struct BwdArgs {
+  Geo g;
+  const bf16_t* q;
+  const bf16_t* kp;
+  const bf16_t* vp;
+  const int32_t* plen;
+  const bf16_t* kl;
+  const bf16_t* vl;
+  const int32_t* topk;
+  const float* lse;
+  const float* delta;
+  const bf16_t* dout;
+  const int32_t* tcount;
+  const int32_t* tlist;
+  float* dq;
+  float* dkp;
+  float* dvp;
+  float* dkl;
+  float* dvl;
+  int ntiles;
+};
+
+// ===========================================================================
+// dQ, query-outer
+// ===========================================================================
+template <int D> struct QState {
+  bf16x8_t qf[Sh<D>::KS];
+  bf16x8_t df[Sh<D>::KS];
+  f32x16_t acc[Sh<D>::DT];
+  float lse2;   // lse * log2(e) of this lane's query
+  float dl;     // rowsum(dO * O) of this lane's query
+};
+
+template <int D>
+__device__ __forceinline__ void q_init(const BwdArgs& a, size_t bh, int tok, bool ok, QState<D>& st) {
+  const int h = (threadIdx.x & 63) >> 5;
+  const size_t row = bh * a.g.ct + tok;
+#pragma unroll
+  for (int ks = 0; ks < Sh<D>::KS; ++ks) {
+    st.qf[ks] = __builtin_bit_cast(bf16x8_t, ok ? ld16(a.q + row * D + 16 * ks + 8 * h) : make_uint4(0, 0, 0, 0));
+    st.df[ks] = __builtin_bit_cast(bf16x8_t, ok ? ld16(a.dout + row * D + 16 * ks + 8 * h) : make_uint4(0, 0, 0, 0));
+  }
+#pragma unroll
+  for (int dt = 0; dt < Sh<D>::DT; ++dt) st.acc[dt] = f32x16_t{};
+  st.lse2 = ok ? a.lse[row] * kLog2e : INFINITY;
+  st.dl = ok ? a.delta[row] : 0.f;
+}
+
+// One 32-key tile: K tile tk, V tile tv (32 rows each), nvalid leading keys.
+template <int D>
+__device__ __forceinline__ void q_tile(const char* tk, const char* tv, int nvalid, float c2, QState<D>& st) {
+  const int lane = threadIdx.x & 63, h = lane >> 5, l32 = lane & 31;
+  f32x16_t s = {}, dp = {};
+#pragma unroll
+  for (int ks = 0; ks < Sh<D>::KS; ++ks) {
+    s = mfma(rd_nat<D>(tk, l32, 2 * ks + h), st.qf[ks], s);
+    dp = mfma(rd_nat<D>(tv, l32, 2 * ks + h), st.df[ks], dp);
+  }
+  f32x16_t ds;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int kk = 8 * (j >> 2) + 4 * h + (j & 3);
+    const float p = kk < nvalid ? __builtin_amdgcn_exp2f(fmaf(s[j], c2, -st.lse2)) : 0.f;
+    ds[j] = p * (dp[j] - st.dl);
+  }
+  const bf16x8_t d0 = pack8(ds, 0), d1 = pack8(ds, 1);
+#pragma unroll
+  for (int dt = 0; dt < Sh<D>::DT; ++dt) {
+    st.acc[dt] = mfma(rd_tr<D>(tk, 0, dt), d0, st.acc[dt]);
+    st.acc[dt] = mfma(rd_tr<D>(tk, 1, dt), d1, st.acc[dt]);
+  }
+}
+
+// Persistent part: 8 waves x 32 contiguous query rows; every slot staged once.
+constexpr int kDqWaves = 8;
+constexpr int kDqThreads = 64 * kDqWaves;
+constexpr int kDqRows = 32 * kDqWaves;
+
+template <int D> struct SlotPf {
+  static constexpr int N = 64 * Sh<D>::CPR / kDqThreads;  // chunks per thread per tensor
+  uint4 k[N], v[N];
+};
+
+template <int D>
+__device__ __forceinline__ void slot_load(const BwdArgs& a, size_t bh, int s, SlotPf<D>& pf) {
+  const Geo& g = a.g;
+  const int n = min(a.plen[bh * g.S + s], g.C);
+  const bf16_t* kb = a.kp + (bh * g.S + s) * (size_t)g.C * D;
+  const bf16_t* vb = a.vp + (bh * g.S + s) * (size_t)g.C * D;
+#pragma unroll
+  for (int u = 0; u < SlotPf<D>::N; ++u) {
+    const int id = threadIdx.x + kDqThreads * u, r = id / Sh<D>::CPR, c = id % Sh<D>::CPR;
+    const bool ok = r < n;
+    pf.k[u] = ok ? ld16(kb + (size_t)r * D + c * 8) : make_uint4(0, 0, 0, 0);
+    pf.v[u] = ok ? ld16(vb + (size_t)r * D + c * 8) : make_uint4(0, 0, 0, 0);
+  }
+}
+
+// LDS: K rows 0-31, K rows 32-63, V rows 0-31, V rows 32-63 (four tiles)
+template <int D>
+__device__ __forceinline__ void slot_store(const SlotPf<D>& pf, char* buf) {
+#pragma unroll
+  for (int u = 0; u < SlotPf<D>::N; ++u) {
+    const int id = threadIdx.x + kDqThreads * u, r = id / Sh<D>::CPR, c = id % Sh<D>::CPR;
+    st_chunk(buf + (r >> 5) * Sh<D>::TILEB, Sh<D>::ROWB, Sh<D>::CPR, r & 31, c, pf.k[u]);
+    st_chunk(buf + (2 + (r >> 5)) * Sh<D>::TILEB, Sh<D>::ROWB, Sh<D>::CPR, r & 31, c, pf.v[u]);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kDqThreads, 1) void dq_pers_kernel(BwdArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  constexpr int BUF = 4 * Sh<D>::TILEB;
+  const Geo& g = a.g;
+  const int total = g.B * g.H * a.ntiles;
+  const int lin = xcd_remap(total);
+  if (lin >= total) return;
+  const int qt = lin % a.ntiles;
+  const size_t bh = lin / a.ntiles;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, h = lane >> 5, l32 = lane & 31;
+  const int r = qt * kDqRows + 32 * wave + l32;
+  const bool ok = r < g.ct;
+  const bool active = qt * kDqRows + 32 * wave < g.ct;
+  QState<D> st;
+  q_init<D>(a, bh, ok ? r : 0, ok, st);
+  const float c2 = g.scale * kLog2e;
+  if (g.S > 0) {
+    SlotPf<D> pf;
+    slot_load<D>(a, bh, 0, pf);
+    slot_store<D>(pf, smem);
+    __syncthreads();
+    for (int s = 0; s < g.S; ++s) {
+      char* buf = smem + (s & 1) * BUF;
+      const int n = min(a.plen[bh * g.S + s], g.C);
+      if (s + 1 < g.S) slot_load<D>(a, bh, s + 1, pf);
+      if (active) {
+        if (n > 0) q_tile<D>(buf, buf + 2 * Sh<D>::TILEB, min(n, 32), c2, st);
+        if (n > 32) q_tile<D>(buf + Sh<D>::TILEB, buf + 3 * Sh<D>::TILEB, n - 32, c2, st);
+      }
+      if (s + 1 < g.S) slot_store<D>(pf, smem + ((s + 1) & 1) * BUF);
+      __syncthreads();
+    }
+  }
+  if (!ok) return;
+  float* out = a.dq + (bh * g.ct + r) * D;
+#pragma unroll
+  for (int dt = 0; dt < Sh<D>::DT; ++dt)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4)
+      *reinterpret_cast<float4*>(out + 32 * dt + 8 * i4 + 4 * h) =
+          make_float4(st.acc[dt][4 * i4] * g.scale, st.acc[dt][4 * i4 + 1] * g.scale,
+                      st.acc[dt][4 * i4 + 2] * g.scale, st.acc[dt][4 * i4 + 3] * g.scale);
+}
+
+// Local part: 8 waves = 4 query blocks x 2 query tiles; per step the 32-row
+// half of each query block's current selected block (K and V) is staged.
+constexpr int kLocBlocks = 4;
+
+template <int D> struct LocPf {
+  static constexpr int N = kLocBlocks * 32 * Sh<D>::CPR / kDqThreads;
+  uint4 k[N], v[N];
+};
+
+template <int D>
+__device__ __forceinline__ void loc_load(const BwdArgs& a, size_t bh, int qg, int j, LocPf<D>& pf) {
+  const Geo& g = a.g;
+  const int t = j >> 1, half = j & 1;
+  const bf16_t* kb = a.kl + bh * (size_t)g.NL * D;
+  const bf16_t* vb = a.vl + bh * (size_t)g.NL * D;
+#pragma unroll
+  for (int u = 0; u < LocPf<D>::N; ++u) {
+    const int id = threadIdx.x + kDqThreads * u;
+    const int w = id / (32 * Sh<D>::CPR), rem = id % (32 * Sh<D>::CPR);
+    const int r = 32 * half + rem / Sh<D>::CPR, c = rem % Sh<D>::CPR;
+    const int qb = qg * kLocBlocks + w;
+    bool ok = false;
+    size_t off = 0;
+    if (qb < g.nq) {
+      const int p = a.topk[(bh * g.nq + qb) * g.K + t];
+      if ((unsigned)p < (unsigned)g.nl) {
+        const BlockExt e = block_ext(g, p % g.nq);
+        if (r < e.len) {
+          ok = true;
+          off = ((size_t)(p / g.nq) * g.ct + block_token(g, e, r)) * D + c * 8;
+        }
+      }
+    }
+    pf.k[u] = ok ? ld16(kb + off) : make_uint4(0, 0, 0, 0);
+    pf.v[u] = ok ? ld16(vb + off) : make_uint4(0, 0, 0, 0);
+  }
+}
+
+// LDS: region w = [K tile, V tile]
+template <int D>
+__device__ __forceinline__ void loc_store(const LocPf<D>& pf, char* buf) {
+#pragma unroll
+  for (int u = 0; u < LocPf<D>::N; ++u) {
+    const int id = threadIdx.x + kDqThreads * u;
+    const int w = id / (32 * Sh<D>::CPR), rem = id % (32 * Sh<D>::CPR);
+    const int r = rem / Sh<D>::CPR, c = rem % Sh<D>::CPR;
+    char* region = buf + w * 2 * Sh<D>::TILEB;
+    st_chunk(region, Sh<D>::ROWB, Sh<D>::CPR, r, c, pf.k[u]);
+    st_chunk(region + Sh<D>::TILEB, Sh<D>::ROWB, Sh<D>::CPR, r, c, pf.v[u]);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kDqThreads, 1) void dq_local_kernel(BwdArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  constexpr int BUF = kLocBlocks * 2 * Sh<D>::TILEB;
+  const Geo& g = a.g;
+  const int total = g.B * g.H * a.ntiles;
+  const int lin = xcd_remap(total);
+  if (lin >= total) return;
+  const int qg = lin % a.ntiles;
+  const size_t bh = lin / a.ntiles;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, h = lane >> 5, l32 = lane & 31;
+  const int qb = qg * kLocBlocks + (wave >> 1), nt = wave & 1;
+  const bool has_q = qb < g.nq;
+  const BlockExt qe = block_ext(g, has_q ? qb : 0);
+  const bool active = has_q && 32 * nt < qe.len;
+  const int r = 32 * nt + l32;
+  const bool ok = active && r < qe.len;
+  const int tok = ok ? block_token(g, qe, r) : 0;
+  QState<D> st;
+  q_init<D>(a, bh, tok, ok, st);
+  const float c2 = g.scale * kLog2e;
+  const int nsteps = 2 * g.K;
+  LocPf<D> pf;
+  loc_load<D>(a, bh, qg, 0, pf);
+  loc_store<D>(pf, smem);
+  __syncthreads();
+  for (int j = 0; j < nsteps; ++j) {
+    char* buf = smem + (j & 1) * BUF;
+    int nv = 0;
+    if (active) {
+      const int p = a.topk[(bh * g.nq + qb) * g.K + (j >> 1)];
+      if ((unsigned)p < (unsigned)g.nl) nv = min(block_ext(g, p % g.nq).len - 32 * (j & 1), 32);
+    }
+    if (j + 1 < nsteps) loc_load<D>(a, bh, qg, j + 1, pf);
+    if (nv > 0) {
+      const char* region = buf + (wave >> 1) * 2 * Sh<D>::TILEB;
+      q_tile<D>(region, region + Sh<D>::TILEB, nv, c2, st);
+    }
+    if (j + 1 < nsteps) loc_store<D>(pf, smem + ((j + 1) & 1) * BUF);
+    __syncthreads();
+  }
+  if (!ok) return;
+  float* out = a.dq + (bh * g.ct + tok) * D;
+#pragma unroll
+  for (int dt = 0; dt < Sh<D>::DT; ++dt)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      float4* o4 = reinterpret_cast<float4*>(out + 32 * dt + 8 * i4 + 4 * h);
+      float4 v = *o4;
+      v.x += st.acc[dt][4 * i4] * g.scale;
+      v.y += st.acc[dt][4 * i4 + 1] * g.scale;
+      v.z += st.acc[dt][4 * i4 + 2] * g.scale;
+      v.w += st.acc[dt][4 * i4 + 3] * g.scale;
+      *o4 = v;
+    }
+}
+
+// ===========================================================================
+// dK, dV, key-outer
+// ===========================================================================
+template <int D> struct KState {
+  bf16x8_t kf[Sh<D>::KS];
+  bf16x8_t vf[Sh<D>::KS];
+  f32x16_t dk[Sh<D>::DT];
+  f32x16_t dv[Sh<D>::DT];
+};
+
+// row pointer (or null) for this lane's key
+template <int D>
+__device__ __forceinline__ void k_init(const bf16_t* krow, const bf16_t* vrow, bool ok, KState<D>& st) {
+  const int h = (threadIdx.x & 63) >> 5;
+#pragma unroll
+  for (int ks = 0; ks < Sh<D>::KS; ++ks) {
+    st.kf[ks] = __builtin_bit_cast(bf16x8_t, ok ? ld16(krow + 16 * ks + 8 * h) : make_uint4(0, 0, 0, 0));
+    st.vf[ks] = __builtin_bit_cast(bf16x8_t, ok ? ld16(vrow + 16 * ks + 8 * h) : make_uint4(0, 0, 0, 0));
+  }
+#pragma unroll
+  for (int dt = 0; dt < Sh<D>::DT; ++dt) {
+    st.dk[dt] = f32x16_t{};
+    st.dv[dt] = f32x16_t{};
+  }
+}
+
+// One 32-query tile in LDS: Q tile tq, dO tile td, per-row lse*log2e and D.
+template <int D>
+__device__ __forceinline__ void k_tile(const char* tq, const char* td, const float* lse2, const float* dl, float c2,
+                                       KState<D>& st) {
+  const int lane = threadIdx.x & 63, h = lane >> 5, l32 = lane & 31;
+  f32x16_t s = {}, dp = {};
+#pragma unroll
+  for (int ks = 0; ks < Sh<D>::KS; ++ks) {
+    s = mfma(rd_nat<D>(tq, l32, 2 * ks + h), st.kf[ks], s);
+    dp = mfma(rd_nat<D>(td, l32, 2 * ks + h), st.vf[ks], dp);
+  }
+  f32x16_t p, ds;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float4 L = *reinterpret_cast<const float4*>(lse2 + 8 * i + 4 * h);
+    const float4 Dv = *reinterpret_cast<const float4*>(dl + 8 * i + 4 * h);
+    const float Ls[4] = {L.x, L.y, L.z, L.w}, Ds[4] = {Dv.x, Dv.y, Dv.z, Dv.w};
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int j = 4 * i + jj;
+      p[j] = __builtin_amdgcn_exp2f(fmaf(s[j], c2, -Ls[jj]));
+      ds[j] = p[j] * (dp[j] - Ds[jj]);
+    }
+  }
+  const bf16x8_t p0 = pack8(p, 0), p1 = pack8(p, 1), d0 = pack8(ds, 0), d1 = pack8(ds, 1);
+#pragma unroll
+  for (int dt = 0; dt < Sh<D>::DT; ++dt) {
+    st.dv[dt] = mfma(p0, rd_tr<D>(td, 0, dt), st.dv[dt]);
+    st.dv[dt] = mfma(p1, rd_tr<D>(td, 1, dt), st.dv[dt]);
+    st.dk[dt] = mfma(d0, rd_tr<D>(tq, 0, dt), st.dk[dt]);
+    st.dk[dt] = mfma(d1, rd_tr<D>(tq, 1, dt), st.dk[dt]);
+  }
+}
+
+// Write this wave's 32 key rows: row kr of the tile goes to dst(kr) if kr < n, else zero.
+template <int D, typename RowPtr>
+__device__ __forceinline__ void k_write(const KState<D>& st, int n, float scale, RowPtr rows) {
+  const int lane = threadIdx.x & 63, h = lane >> 5, l32 = lane & 31;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int kr = 8 * (j >> 2) + 4 * h + (j & 3);
+    float* dk;
+    float* dv;
+    if (!rows(kr, dk, dv)) continue;
+    const bool ok = kr < n;
+#pragma unroll
+    for (int dt = 0; dt < Sh<D>::DT; ++dt) {
+      dk[32 * dt + l32] = ok ? st.dk[dt][j] * scale : 0.f;
+      dv[32 * dt + l32] = ok ? st.dv[dt][j] : 0.f;
+    }
+  }
+}
+
+constexpr int kKvThreads = 256;   // dkv_pers: 4 waves = 2 slots x 2 key tiles
+
+template <int D> struct QPf {
+  static constexpr int N = 32 * Sh<D>::CPR / 64;  // chunks per lane per tensor when one wave loads
+};
+
+// Stage 32 query rows (Q, dO, lse*log2e, D) into LDS with `nthr` threads.
+// row(i) returns the token of tile row i, or -1 for an empty row.
+template <int D, int NTHR, typename RowFn>
+struct QTileLoader {
+  static constexpr int N = 32 * Sh<D>::CPR / NTHR;
+  uint4 q[N], d[N];
+  float l, dd;
+  __device__ __forceinline__ void load(const BwdArgs& a, size_t bh, RowFn row) {
+    const Geo& g = a.g;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int u = 0; u < N; ++u) {
+      const int id = tid + NTHR * u, r = id / Sh<D>::CPR, c = id % Sh<D>::CPR;
+      const int tok = row(r);
+      const size_t off = (bh * g.ct + (tok < 0 ? 0 : tok)) * (size_t)D + c * 8;
+      q[u] = tok >= 0 ? ld16(a.q + off) : make_uint4(0, 0, 0, 0);
+      d[u] = tok >= 0 ? ld16(a.dout + off) : make_uint4(0, 0, 0, 0);
+    }
+    if (tid < 32) {
+      const int tok = row(tid);
+      l = tok >= 0 ? a.lse[bh * g.ct + tok] * kLog2e : INFINITY;
+      dd = tok >= 0 ? a.delta[bh * g.ct + tok] : 0.f;
+    }
+  }
+  // LDS: Q tile, dO tile, lse2[32], D[32]
+  __device__ __forceinline__ void store(char* buf) const {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int u = 0; u < N; ++u) {
+      const int id = tid + NTHR * u, r = id / Sh<D>::CPR, c = id % Sh<D>::CPR;
+      st_chunk(buf, Sh<D>::ROWB, Sh<D>::CPR, r, c, q[u]);
+      st_chunk(buf + Sh<D>::TILEB, Sh<D>::ROWB, Sh<D>::CPR, r, c, d[u]);
+    }
+    if (tid < 32) {
+      float* f = reinterpret_cast<float*>(buf + 2 * Sh<D>::TILEB);
+      f[tid] = l;
+      f[32 + tid] = dd;
+    }
+  }
+};
+
+template <int D>
+__global__ __launch_bounds__(kKvThreads, 1) void dkv_pers_kernel(BwdArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  constexpr int BUF = 2 * Sh<D>::TILEB + 256;
+  const Geo& g = a.g;
+  const int total = g.B * g.H * a.ntiles;
+  const int lin = xcd_remap(total);
+  if (lin >= total) return;
+  const int sp = lin % a.ntiles;  // slot pair
+  const size_t bh = lin / a.ntiles;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31;
+  const int slot = 2 * sp + (wave >> 1), kh = wave & 1;
+  const bool has_slot = slot < g.S;
+  const int n = has_slot ? min(a.plen[bh * g.S + slot], g.C) : 0;
+  const int nk = min(max(n - 32 * kh, 0), 32);  // valid keys of this wave's tile
+  const size_t sbase = (bh * g.S + (has_slot ? slot : 0)) * (size_t)g.C * D;
+  const int kr = 32 * kh + l32;
+  KState<D> st;
+  k_init<D>(a.kp + sbase + (size_t)kr * D, a.vp + sbase + (size_t)kr * D, kr < n, st);
+  const float c2 = g.scale * kLog2e;
+
+  const int nsteps = (g.ct + 31) / 32;
+  struct Contig {
+    int base, ct;
+    __device__ int operator()(int i) const { return base + i < ct ? base + i : -1; }
+  };
+  QTileLoader<D, kKvThreads, Contig> pf;
+  pf.load(a, bh, Contig{0, g.ct});
+  pf.store(smem);
+  __syncthreads();
+  for (int i = 0; i < nsteps; ++i) {
+    char* buf = smem + (i & 1) * BUF;
+    if (i + 1 < nsteps) pf.load(a, bh, Contig{32 * (i + 1), g.ct});
+    if (nk > 0) {
+      const float* f = reinterpret_cast<const float*>(buf + 2 * Sh<D>::TILEB);
+      k_tile<D>(buf, buf + Sh<D>::TILEB, f, f + 32, c2, st);
+    }
+    if (i + 1 < nsteps) pf.store(smem + ((i + 1) & 1) * BUF);
+    __syncthreads();
+  }
+  if (!has_slot || 32 * kh >= g.C) return;
+  float* dkb = a.dkp + sbase;
+  float* dvb = a.dvp + sbase;
+  k_write<D>(st, nk, g.scale, [&](int r, float*& dk, float*& dv) {
+    const int row = 32 * kh + r;
+    if (row >= g.C) return false;
+    dk = dkb + (size_t)row * D;
+    dv = dvb + (size_t)row * D;
+    return true;
+  });
+}
+
+constexpr int kKvlThreads = 128;  // dkv_local: 2 waves = one local block
+
+template <int D>
+__global__ __launch_bounds__(kKvlThreads, 1) void dkv_local_kernel(BwdArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  constexpr int BUF = 2 * Sh<D>::TILEB + 256;
+  const Geo& g = a.g;
+  const int total = g.B * g.H * g.nl;
+  const int lin = xcd_remap(total);
+  if (lin >= total) return;
+  const int p = lin % g.nl;
+  const size_t bh = lin / g.nl;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31;
+  const BlockExt ke = block_ext(g, p % g.nq);
+  const int koff = (p / g.nq) * g.ct;
+  const int nk = min(max(ke.len - 32 * wave, 0), 32);
+  const int kr = 32 * wave + l32;
+  const bool kok = kr < ke.len;
+  const size_t krow = (bh * g.NL + koff + (kok ? block_token(g, ke, kr) : 0)) * (size_t)D;
+  KState<D> st;
+  k_init<D>(a.kl + krow, a.vl + krow, kok, st);
+  const float c2 = g.scale * kLog2e;
+
+  const int ncount = a.tcount[bh * g.nl + p];
+  const int32_t* lst = a.tlist + (bh * g.nl + p) * g.nq;
+  struct Gather {
+    Geo g;
+    BlockExt e;
+    int half;
+    __device__ int operator()(int i) const {
+      const int r = 32 * half + i;
+      return r < e.len ? block_token(g, e, r) : -1;
+    }
+  };
+  // steps: (selecting query block, half) pairs, in list order
+  int nsteps = 0;
+  for (int s = 0; s < ncount; ++s) nsteps += (block_ext(g, lst[s]).len + 31) / 32;
+  if (nsteps > 0) {
+    int cur = 0, half = 0;  // next step to load: list entry and half
+    BlockExt ce = block_ext(g, lst[0]);
+    QTileLoader<D, kKvlThreads, Gather> pf;
+    pf.load(a, bh, Gather{g, ce, half});
+    pf.store(smem);
+    __syncthreads();
+    for (int i = 0; i < nsteps; ++i) {
+      char* buf = smem + (i & 1) * BUF;
+      if (i + 1 < nsteps) {
+        if (32 * (half + 1) < ce.len) {
+          ++half;
+        } else {
+          ce = block_ext(g, lst[++cur]);
+          half = 0;
+        }
+        pf.load(a, bh, Gather{g, ce, half});
+      }
+      if (nk > 0) {
+        const float* f = reinterpret_cast<const float*>(buf + 2 * Sh<D>::TILEB);
+        k_tile<D>(buf, buf + Sh<D>::TILEB, f, f + 32, c2, st);
+      }
+      if (i + 1 < nsteps) pf.store(smem + ((i + 1) & 1) * BUF);
+      __syncthreads();
+    }
+  }
+  if (nk <= 0) return;
+  float* dkb = a.dkl + (bh * g.NL + koff) * (size_t)D;
+  float* dvb = a.dvl + (bh * g.NL + koff) * (size_t)D;
+  k_write<D>(st, nk, g.scale, [&](int r, float*& dk, float*& dv) {
+    const int row = 32 * wave + r;
+    if (row >= ke.len) return false;
+    const size_t t = (size_t)block_token(g, ke, row) * D;
+    dk = dkb + t;
+    dv = dvb + t;
+    return true;
+  });
+}
+
+template <typename K>
+hipError_t set_lds(K kernel, size_t bytes) {
+  return hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+template <int D>
+hipError_t launch_d(const BwdArgs& base, hipStream_t s) {
+  const Geo& g = base.g;
+  const size_t shm_dq = 2 * 4 * Sh<D>::TILEB;                 // persistent: 2 x (K,K,V,V)
+  const size_t shm_dql = 2 * kLocBlocks * 2 * Sh<D>::TILEB;   // local: 2 x 4 x (K,V)
+  const size_t shm_kv = 2 * (2 * Sh<D>::TILEB + 256);
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = set_lds(dq_pers_kernel<D>, shm_dq);
+    if (e == hipSuccess) e = set_lds(dq_local_kernel<D>, shm_dql);
+    if (e == hipSuccess) e = set_lds(dkv_pers_kernel<D>, shm_kv);
+    if (e == hipSuccess) e = set_lds(dkv_local_kernel<D>, shm_kv);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  BwdArgs a = base;
+  hipError_t e;
+  // dq: persistent part writes, local part adds
+  a.ntiles = (g.ct + kDqRows - 1) / kDqRows;
+  int total = g.B * g.H * a.ntiles;
+  dq_pers_kernel<D><<<((total + 7) / 8) * 8, kDqThreads, shm_dq, s>>>(a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  a.ntiles = (g.nq + kLocBlocks - 1) / kLocBlocks;
+  total = g.B * g.H * a.ntiles;
+  dq_local_kernel<D><<<((total + 7) / 8) * 8, kDqThreads, shm_dql, s>>>(a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (g.S > 0) {
+    a.ntiles = (g.S + 1) / 2;
+    total = g.B * g.H * a.ntiles;
+    dkv_pers_kernel<D><<<((total + 7) / 8) * 8, kKvThreads, shm_kv, s>>>(a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  total = g.B * g.H * g.nl;
+  dkv_local_kernel<D><<<((total + 7) / 8) * 8, kKvlThreads, shm_kv, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool bwd_mfma_supported(const Geo& g) { return g.dtype == PBSA_BF16 && (g.D == 64 || g.D == 128) && g.C <= 64; }
+
+hipError_t launch_bwd_mfma(const Geo& g, const void* q, const void* k_p, const void* v_p, const int32_t* plen,
+                           const void* k_l, const void* v_l, const int32_t* topk, const float* lse,
+                           const void* dout, float* dq, float* dk_p, float* dv_p, float* dk_l, float* dv_l,
+                           WsBwd ws, hipStream_t s) {
+  BwdArgs a{g, (const bf16_t*)q, (const bf16_t*)k_p, (const bf16_t*)v_p, plen, (const bf16_t*)k_l,
+            (const bf16_t*)v_l, topk, lse, ws.delta, (const bf16_t*)dout, ws.tcount, ws.tlist,
+            dq, dk_p, dv_p, dk_l, dv_l, 0};
+  return g.D == 128 ? launch_d<128>(a, s) : launch_d<64>(a, s);
+}
+
+}  // namespace pbsa
