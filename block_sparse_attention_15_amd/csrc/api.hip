@@ -102,8 +102,8 @@ pbsa_status make_plan(const pbsa_config* c, Plan* p) {
   }
   g.scale = c->softmax_scale > 0.f ? c->softmax_scale : (float)(1.0 / sqrt((double)g.D));
   g.dtype = c->dtype;
-  if (g.S > 4096 || g.nl > 4096 || g.nq > 4096)
-    return fail(PBSA_ERR_UNSUPPORTED, "more than 4096 blocks per cache");
+  if (g.S > 2048 || g.nl > 2048 || g.nq > 2048)
+    return fail(PBSA_ERR_UNSUPPORTED, "more than 2048 blocks per cache or chunk");
 
   pbsa_plan_info& in = p->info;
   memset(&in, 0, sizeof in);

@@ -28,10 +28,32 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(Geo g, const T* __restri
 }
 
 // grid (H, B): for each local block, the query blocks that selected it, ascending.
+// When the (local block x query block) incidence fits in LDS it is built there
+// as a byte matrix from the top-k lists, then each thread scans one row.
+constexpr int kTindexLds = 48 * 1024;
+
 __global__ __launch_bounds__(256) void bwd_tindex_kernel(Geo g, const int32_t* __restrict__ topk,
                                                          int32_t* __restrict__ tcount, int32_t* __restrict__ tlist) {
+  extern __shared__ unsigned char mark[];
   const size_t bh = (size_t)blockIdx.y * g.H + blockIdx.x;
   const int32_t* tk = topk + bh * g.nq * g.K;
+  if (g.nl * g.nq <= kTindexLds) {
+    for (int x = threadIdx.x; x < g.nl * g.nq; x += 256) mark[x] = 0;
+    __syncthreads();
+    for (int x = threadIdx.x; x < g.nq * g.K; x += 256) {
+      const int p = tk[x];
+      if ((unsigned)p < (unsigned)g.nl) mark[p * g.nq + x / g.K] = 1;
+    }
+    __syncthreads();
+    for (int p = threadIdx.x; p < g.nl; p += 256) {
+      int n = 0;
+      int32_t* out = tlist + (bh * g.nl + p) * g.nq;
+      for (int i = 0; i < g.nq; ++i)
+        if (mark[p * g.nq + i]) out[n++] = i;
+      tcount[bh * g.nl + p] = n;
+    }
+    return;
+  }
   for (int p = threadIdx.x; p < g.nl; p += 256) {
     int n = 0;
     int32_t* out = tlist + (bh * g.nl + p) * g.nq;
@@ -235,7 +257,8 @@ hipError_t launch_bwd_prep(const Geo& g, const void* o, const void* dout, const 
     bwd_delta_kernel<float><<<g1, 256, 0, s>>>(g, (const float*)o, (const float*)dout, ws.delta);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  bwd_tindex_kernel<<<dim3(g.H, g.B), 256, 0, s>>>(g, topk, ws.tcount, ws.tlist);
+  const size_t shm = (size_t)g.nl * g.nq <= (size_t)kTindexLds ? (size_t)g.nl * g.nq : 0;
+  bwd_tindex_kernel<<<dim3(g.H, g.B), 256, shm, s>>>(g, topk, ws.tcount, ws.tlist);
   return hipGetLastError();
 }
 

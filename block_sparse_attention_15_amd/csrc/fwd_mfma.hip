@@ -9,7 +9,8 @@
 // ----------------
 //  * Two kernels.  The persistent slots are the same for every query of a
 //    head, so the first kernel is a dense attention of all of a head's
-//    queries (contiguous 256-row tiles, 4 waves x 64 rows) against the
+//    queries (contiguous 256-row tiles, 8 waves x 32 rows, two waves per
+//    SIMD so one wave's softmax overlaps the other's MFMAs) against the
 //    compact persistent memory, each slot staged once in LDS for the four
 //    waves; it writes a normalised fp32 partial output and its log-sum-exp.
 //    The second kernel handles the selected local blocks, which differ per
@@ -204,13 +205,14 @@ __device__ __forceinline__ int xcd_remap(int total) {
 
 // ---------------------------------------------------------------------------
 // Kernel 1: every query of a head against all persistent slots (dense over
-// the compact memory).  4 waves x 64 contiguous query rows; slot K/V staged
+// the compact memory).  8 waves x 32 contiguous query rows; slot K/V staged
 // in LDS once per workgroup.  Writes the normalised partial output and its
 // log-sum-exp.
 // ---------------------------------------------------------------------------
-constexpr int kPersWaves = 4;
+constexpr int kPersWaves = 8;   // 2 waves per SIMD: one's softmax overlaps the other's MFMAs
+constexpr int kPersNT = 1;      // 32-query tiles per wave
 constexpr int kPersThreads = 64 * kPersWaves;
-constexpr int kPersRows = 64 * kPersWaves;
+constexpr int kPersRows = 32 * kPersNT * kPersWaves;
 
 template <int D> struct PersPrefetch {
   static constexpr int N = 64 * Shape<D>::CPR / kPersThreads;  // chunks per thread per tensor
@@ -255,13 +257,13 @@ __global__ __launch_bounds__(kPersThreads, 1) void fwd_pers_kernel(FwdArgs a) {
   const int qt = lin % a.ntiles;
   const size_t bh = lin / a.ntiles;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, h = lane >> 5, l32 = lane & 31;
-  const int row_w = qt * kPersRows + 64 * wave;  // first query row of this wave
-  const int ntq = max(0, min(2, (g.ct - row_w + 31) / 32));
+  const int row_w = qt * kPersRows + 32 * kPersNT * wave;  // first query row of this wave
+  const int ntq = max(0, min(kPersNT, (g.ct - row_w + 31) / 32));
 
-  WaveState<D, 2> st;
+  WaveState<D, kPersNT> st;
   init_state(st);
 #pragma unroll
-  for (int n = 0; n < 2; ++n) {
+  for (int n = 0; n < kPersNT; ++n) {
     const int r = row_w + 32 * n + l32;
     load_q(a.q + (bh * g.ct + min(r, g.ct - 1)) * D, r < g.ct, n, st);
   }
@@ -277,8 +279,8 @@ __global__ __launch_bounds__(kPersThreads, 1) void fwd_pers_kernel(FwdArgs a) {
       const int n = min(a.plen[bh * g.S + s], g.C);
       if (s + 1 < g.S) pers_load<D>(a, bh, s + 1, pf);
       if (ntq > 0) {
-        if (n > 0) tile<D, 2>(buf, buf + 64 * Sh::ROWB, 0, min(n, 32), ntq, c2, st);
-        if (n > 32) tile<D, 2>(buf, buf + 64 * Sh::ROWB, 32, n - 32, ntq, c2, st);
+        if (n > 0) tile<D, kPersNT>(buf, buf + 64 * Sh::ROWB, 0, min(n, 32), ntq, c2, st);
+        if (n > 32) tile<D, kPersNT>(buf, buf + 64 * Sh::ROWB, 32, n - 32, ntq, c2, st);
       }
       if (s + 1 < g.S) pers_store<D>(pf, smem + ((s + 1) & 1) * kBufBytes);
       __syncthreads();
@@ -286,7 +288,7 @@ __global__ __launch_bounds__(kPersThreads, 1) void fwd_pers_kernel(FwdArgs a) {
   }
 
 #pragma unroll
-  for (int n = 0; n < 2; ++n) {
+  for (int n = 0; n < kPersNT; ++n) {
     if (n < ntq) {
       const int r = row_w + 32 * n + l32;
       const float lt = half_sum(st.l[n]);

@@ -90,28 +90,21 @@ __global__ __launch_bounds__(kThreads) void pool_slots_kernel(Geo g, const T* __
   pool_rows<T>(kp + bhs * g.C * g.D, g.D, len, [](int i) { return i; }, red, kbar + bhs * g.D);
 }
 
+__device__ __forceinline__ float wave_max(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
 __device__ __forceinline__ float wave_sum(float v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
 }
 
-__device__ float block_reduce(float v, float* sh, bool is_max) {
-  // fixed-order tree within each wave, then waves 0..3 in order
-  for (int o = 32; o > 0; o >>= 1) {
-    float w = __shfl_xor(v, o, 64);
-    v = is_max ? fmaxf(v, w) : v + w;
-  }
-  const int wid = threadIdx.x / 64;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) sh[wid] = v;
-  __syncthreads();
-  float r = sh[0];
-  for (int k = 1; k < kThreads / 64; ++k) r = is_max ? fmaxf(r, sh[k]) : r + sh[k];
-  return r;
-}
+constexpr int kQPerWg = 4;  // query blocks scored per workgroup (one wave each for top-k)
 
-// grid (nq, H, B): scores of one query block against every local block and
-// every valid persistent slot; top-k selection; one pooled softmax row.
+// grid (ceil(nq/4), H, B): pooled scores of 4 query blocks against every local
+// block and every valid persistent slot (each candidate's pooled key is read
+// once for the 4 query blocks), then per query block (one wave) the top-k by
+// rank and one pooled softmax row.
 __global__ __launch_bounds__(kThreads) void score_topk_kernel(Geo g, const int32_t* __restrict__ ring_head,
                                                               const float* __restrict__ qbar,
                                                               const float* __restrict__ kbar_l,
@@ -120,85 +113,113 @@ __global__ __launch_bounds__(kThreads) void score_topk_kernel(Geo g, const int32
                                                               int32_t* __restrict__ topk,
                                                               float* __restrict__ prow) {
   extern __shared__ float smem[];
-  float* qb = smem;                 // [D]
-  float* sl = qb + g.D;             // [nl]   local scores
-  float* sp = sl + g.nl;            // [S]    persistent scores (-inf if empty)
-  int* sel = (int*)(sp + g.S);      // [nl]   selected flags
-  __shared__ float red[kThreads / 64];
-  const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int W = g.nl + g.S;        // candidates: local blocks, then slots
+  float* qb = smem;                // [4][D]
+  float* sc = qb + kQPerWg * g.D;  // [4][W] scores (-inf for empty slots)
+  int* sel = (int*)(sc + kQPerWg * W);  // [4][nl] 64-bit sort keys, then [4][nl] flags
+  const int i0 = blockIdx.x * kQPerWg, h = blockIdx.y, b = blockIdx.z;
   const size_t bh = (size_t)b * g.H + h;
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = kThreads / 64;
-  for (int d = threadIdx.x; d < g.D; d += kThreads) qb[d] = qbar[(bh * g.nq + i) * g.D + d];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int x = threadIdx.x; x < kQPerWg * g.D; x += kThreads) {
+    const int qi = i0 + x / g.D;
+    qb[x] = qi < g.nq ? qbar[(bh * g.nq + qi) * g.D + x % g.D] : 0.f;
+  }
   __syncthreads();
-  const int rh = *ring_head;
-  // dot products: one wave per candidate, lanes split the head dimension
-  for (int c = wid; c < g.nl + g.S; c += nw) {
+  for (int c = threadIdx.x; c < W; c += kThreads) {
     const bool loc = c < g.nl;
     const int idx = loc ? c : c - g.nl;
     if (!loc && plen[bh * g.S + idx] <= 0) {
-      if (lane == 0) sp[idx] = -INFINITY;
+      for (int k = 0; k < kQPerWg; ++k) sc[k * W + c] = -INFINITY;
       continue;
     }
-    const float* kv = loc ? kbar_l + (bh * g.nl + idx) * g.D : kbar_p + (bh * g.S + idx) * g.D;
-    float part = 0.f;
-    for (int d = lane; d < g.D; d += 64) part = fmaf(qb[d], kv[d], part);
-    part = wave_sum(part) * g.scale;
-    if (lane == 0) (loc ? sl : sp)[idx] = part;
-  }
-  __syncthreads();
-  // top-k by rank: rank(p) = #candidates strictly better (higher score, or
-  // equal score and lower logical index)
-  for (int p = threadIdx.x; p < g.nl; p += kThreads) {
-    const float mine = sl[p];
-    const int cp = p / g.nq;
-    const int lp = ((cp - rh) % g.R + g.R) % g.R * g.nq + (p - cp * g.nq);
-    int rank = 0;
-    for (int o = 0; o < g.nl; ++o) {
-      const float x = sl[o];
-      const int co = o / g.nq;
-      const int lo = ((co - rh) % g.R + g.R) % g.R * g.nq + (o - co * g.nq);
-      rank += (x > mine) || (x == mine && lo < lp);
+    const float4* kv = reinterpret_cast<const float4*>(loc ? kbar_l + (bh * g.nl + idx) * g.D
+                                                           : kbar_p + (bh * g.S + idx) * g.D);
+    float acc[kQPerWg] = {};
+    for (int d4 = 0; d4 < g.D / 4; ++d4) {
+      const float4 k4 = kv[d4];
+#pragma unroll
+      for (int k = 0; k < kQPerWg; ++k) {
+        const float4 q4 = reinterpret_cast<const float4*>(qb + k * g.D)[d4];
+        acc[k] = fmaf(q4.x, k4.x, acc[k]);
+        acc[k] = fmaf(q4.y, k4.y, acc[k]);
+        acc[k] = fmaf(q4.z, k4.z, acc[k]);
+        acc[k] = fmaf(q4.w, k4.w, acc[k]);
+      }
     }
-    sel[p] = rank < g.K;
+#pragma unroll
+    for (int k = 0; k < kQPerWg; ++k) sc[k * W + c] = acc[k] * g.scale;
   }
   __syncthreads();
+  const int i = i0 + w;
+  const bool has = i < g.nq;
+  const float* row = sc + w * W;
+  unsigned long long* key = reinterpret_cast<unsigned long long*>(sel) + w * g.nl;
+  const int rh = *ring_head;
+  // composite key: descending score, then ascending logical index (oldest
+  // chunk first); rank(p) = #local blocks with a larger key
+  if (has) {
+    for (int p = lane; p < g.nl; p += 64) {
+      const int cp = p / g.nq;
+      const unsigned lg = (unsigned)(((cp - rh) % g.R + g.R) % g.R * g.nq + (p - cp * g.nq));
+      unsigned u = row[p] == 0.f ? 0u : __float_as_uint(row[p]);  // -0 ties +0
+      u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);  // order-preserving map to unsigned
+      key[p] = ((unsigned long long)u << 32) | (0xffffffffu - lg);
+    }
+  }
+  __syncthreads();
+  if (!has) return;
   int32_t* out = topk + (bh * g.nq + i) * g.K;
-  for (int p = threadIdx.x; p < g.nl; p += kThreads) {
-    if (!sel[p]) continue;
-    int pos = 0;
-    for (int o = 0; o < p; ++o) pos += sel[o];
-    out[pos] = p;
+  // every lane ranks its own candidates against all keys (LDS broadcast reads)
+  for (int p = lane; p < g.nl; p += 64) {
+    const unsigned long long kp = key[p];
+    int rank = 0;
+    for (int o = 0; o < g.nl; ++o) rank += key[o] > kp;
+    sel[g.nl * 2 * kQPerWg + w * g.nl + p] = rank < g.K;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const int* sl = sel + g.nl * 2 * kQPerWg + w * g.nl;
+  // ascending physical ids: position = selected count below p (ballot prefix)
+  int running = 0;
+  for (int p0 = 0; p0 < g.nl; p0 += 64) {
+    const int p = p0 + lane;
+    const bool on = p < g.nl && sl[p];
+    const unsigned long long m = __builtin_amdgcn_ballot_w64(on);
+    if (on) out[running + __builtin_popcountll(m & ((1ull << lane) - 1))] = p;
+    running += __builtin_popcountll(m);
   }
   // pooled softmax over valid slots and all local blocks
   float mx = -INFINITY;
-  for (int c = threadIdx.x; c < g.nl + g.S; c += kThreads) mx = fmaxf(mx, c < g.nl ? sl[c] : sp[c - g.nl]);
-  mx = block_reduce(mx, red, true);
+  for (int c = lane; c < W; c += 64) mx = fmaxf(mx, row[c]);
+  mx = wave_max(mx);
   float sum = 0.f;
-  for (int c = threadIdx.x; c < g.nl + g.S; c += kThreads) {
-    const float x = c < g.nl ? sl[c] : sp[c - g.nl];
-    sum += x == -INFINITY ? 0.f : expf(x - mx);
-  }
-  sum = block_reduce(sum, red, false);
-  float* row = prow + (bh * g.nq + i) * (size_t)(g.S + g.nl);
-  for (int c = threadIdx.x; c < g.nl + g.S; c += kThreads) {
-    const float x = c < g.nl ? sl[c] : sp[c - g.nl];
-    const float pv = x == -INFINITY ? 0.f : expf(x - mx) / sum;
-    row[c < g.nl ? g.S + c : c - g.nl] = pv;
+  for (int c = lane; c < W; c += 64) sum += row[c] == -INFINITY ? 0.f : expf(row[c] - mx);
+  sum = wave_sum(sum);
+  float* pr = prow + (bh * g.nq + i) * (size_t)W;
+  for (int c = lane; c < W; c += 64) {
+    const float x = row[c];
+    pr[c < g.nl ? g.S + c : c - g.nl] = x == -INFINITY ? 0.f : expf(x - mx) / sum;
   }
 }
 
-// grid (ceil((S+nl)/256), H, B): mass[j] = sum over query blocks, in order.
+// grid (ceil((S+nl)/64), H, B), 256 threads = 64 columns x 4 row groups:
+// mass[j] = sum over query blocks; partial sums over rows rg, rg+4, ... are
+// added in row-group order (fixed, deterministic).
 __global__ __launch_bounds__(kThreads) void mass_kernel(Geo g, const float* __restrict__ prow,
                                                         float* __restrict__ mass) {
-  const int j = blockIdx.x * kThreads + threadIdx.x;
-  const int h = blockIdx.y, b = blockIdx.z;
+  __shared__ float red[4][64];
   const int W = g.S + g.nl;
-  if (j >= W) return;
-  const size_t bh = (size_t)b * g.H + h;
-  const float* r = prow + bh * g.nq * (size_t)W + j;
+  const int col = blockIdx.x * 64 + (threadIdx.x & 63), rg = threadIdx.x >> 6;
+  const size_t bh = (size_t)blockIdx.z * g.H + blockIdx.y;
   float s = 0.f;
-  for (int i = 0; i < g.nq; ++i) s += r[(size_t)i * W];
-  mass[bh * W + j] = s;
+  if (col < W) {
+    const float* r = prow + bh * g.nq * (size_t)W + col;
+    for (int i = rg; i < g.nq; i += 4) s += r[(size_t)i * W];
+  }
+  red[rg][threadIdx.x & 63] = s;
+  __syncthreads();
+  if (rg == 0 && col < W) mass[bh * W + col] = ((red[0][col & 63] + red[1][col & 63]) + red[2][col & 63]) + red[3][col & 63];
 }
 
 }  // namespace
@@ -222,11 +243,17 @@ hipError_t launch_score_select(const Geo& g, const void* q, const void* k_l, con
     pool_blocks_kernel<float><<<g1, kThreads, 0, s>>>(g, (const float*)q, (const float*)k_l, ws.qbar, kbar_l);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  size_t shm = (size_t)(g.D + g.nl + g.S) * 4 + (size_t)g.nl * 4;
-  score_topk_kernel<<<dim3(g.nq, g.H, g.B), kThreads, shm, s>>>(g, ring_head, ws.qbar, kbar_l, kbar_p, plen, topk,
-                                                               ws.prow);
+  const size_t shm = (size_t)kQPerWg * (g.D + g.nl + g.S + 3 * g.nl) * 4;
+  static bool attr = false;
+  if (!attr) {
+    e = hipFuncSetAttribute((const void*)score_topk_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  score_topk_kernel<<<dim3((g.nq + kQPerWg - 1) / kQPerWg, g.H, g.B), kThreads, shm, s>>>(
+      g, ring_head, ws.qbar, kbar_l, kbar_p, plen, topk, ws.prow);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  mass_kernel<<<dim3((g.S + g.nl + kThreads - 1) / kThreads, g.H, g.B), kThreads, 0, s>>>(g, ws.prow, mass);
+  mass_kernel<<<dim3((g.S + g.nl + 63) / 64, g.H, g.B), kThreads, 0, s>>>(g, ws.prow, mass);
   return hipGetLastError();
 }
 

@@ -21,90 +21,91 @@ namespace {
 constexpr int kThreads = 256;
 
 // plan[b,h,s]: -2 keep, -1 empty the slot, p >= 0 fill from physical local block p.
+// Candidates carry a 64-bit key (mass, then the tie order: slots before
+// entrants, lower index first); a candidate is kept when fewer than S valid
+// candidates have a larger key.  Wave 0 then pairs vacated slots with admitted
+// entrants by ballot prefix counts.
 __global__ __launch_bounds__(kThreads) void update_decide_kernel(Geo g, const float* __restrict__ mass,
-                                                                 const float* __restrict__ kbar_l,
                                                                  const int32_t* __restrict__ ring_head,
                                                                  int32_t step_id, int32_t* __restrict__ plen,
                                                                  int32_t* __restrict__ psrc,
-                                                                 float* __restrict__ pkbar,
                                                                  int32_t* __restrict__ n_rep,
                                                                  int32_t* __restrict__ plan) {
-  extern __shared__ int sm[];
+  extern __shared__ unsigned long long sk[];
   const int NC = g.S + g.nq;
-  float* cm = (float*)sm;        // [NC] candidate mass
-  int* valid = sm + NC;          // [NC]
-  int* kept = valid + NC;        // [NC]
-  int* alist = kept + NC;        // [nq] admitted entrants in order
-  __shared__ int n_adm;
+  unsigned long long* key = sk;            // [NC], 0 for empty slots
+  int* kept = (int*)(sk + NC);             // [NC]
+  int* alist = kept + NC;                  // [nq] admitted entrants in order
   const int h = blockIdx.x, b = blockIdx.y;
   const size_t bh = (size_t)b * g.H + h;
   const int old = *ring_head;
   const float* mrow = mass + bh * (g.S + g.nl);
   for (int c = threadIdx.x; c < NC; c += kThreads) {
-    if (c < g.S) {
-      valid[c] = plen[bh * g.S + c] > 0;
-      cm[c] = mrow[c];
-    } else {
-      valid[c] = 1;
-      cm[c] = mrow[g.S + old * g.nq + (c - g.S)];
-    }
+    const bool valid = c >= g.S || plen[bh * g.S + c] > 0;
+    const float m = c < g.S ? mrow[c] : mrow[g.S + old * g.nq + (c - g.S)];
+    unsigned u = m == 0.f ? 0u : __float_as_uint(m);
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    key[c] = valid ? ((unsigned long long)u << 32) | (0xffffffffu - (unsigned)c) : 0ull;
   }
   __syncthreads();
-  // rank among valid candidates; candidate order (slots, then entrants, each
-  // by index) is the tie-break order
   for (int c = threadIdx.x; c < NC; c += kThreads) {
-    int k = 0;
-    if (valid[c]) {
-      const float mc = cm[c];
-      int rank = 0;
-      for (int o = 0; o < NC; ++o) rank += valid[o] && (cm[o] > mc || (cm[o] == mc && o < c));
-      k = rank < g.S;
-    }
-    kept[c] = k;
+    const unsigned long long kc = key[c];
+    int rank = 0;
+    for (int o = 0; o < NC; ++o) rank += key[o] > kc;
+    kept[c] = kc != 0ull && rank < g.S;
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < g.nq; e += kThreads) {
-    if (!kept[g.S + e]) continue;
-    int pos = 0;
-    for (int o = 0; o < e; ++o) pos += kept[g.S + o];
-    alist[pos] = e;
+  if (threadIdx.x >= 64) return;
+  const int lane = threadIdx.x;
+  const unsigned long long below = (1ull << lane) - 1;
+  int n_adm = 0;
+  for (int e0 = 0; e0 < g.nq; e0 += 64) {
+    const int e = e0 + lane;
+    const bool on = e < g.nq && kept[g.S + e];
+    const unsigned long long m = __builtin_amdgcn_ballot_w64(on);
+    if (on) alist[n_adm + __builtin_popcountll(m & below)] = e;
+    n_adm += __builtin_popcountll(m);
   }
-  if (threadIdx.x == 0) {
-    int n = 0;
-    for (int e = 0; e < g.nq; ++e) n += kept[g.S + e];
-    n_adm = n;
-    n_rep[bh] = n;
-  }
-  __syncthreads();
-  for (int s = threadIdx.x; s < g.S; s += kThreads) {
-    const size_t bs = bh * g.S + s;
-    if (valid[s] && kept[s]) {
-      plan[bs] = -2;
-      continue;
+  if (lane == 0) n_rep[bh] = n_adm;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  int nvac = 0;
+  for (int s0 = 0; s0 < g.S; s0 += 64) {
+    const int s = s0 + lane;
+    const bool in = s < g.S;
+    const bool vac = in && !(key[s] != 0ull && kept[s]);
+    const unsigned long long m = __builtin_amdgcn_ballot_w64(vac);
+    if (in) {
+      const size_t bs = bh * g.S + s;
+      if (!vac) {
+        plan[bs] = -2;
+      } else {
+        const int j = nvac + __builtin_popcountll(m & below);  // rank among vacated slots
+        if (j < n_adm) {
+          const int e = alist[j];
+          plan[bs] = old * g.nq + e;
+          plen[bs] = block_ext(g, e).len;
+          psrc[bs] = step_id * g.nq + e;
+        } else {
+          plan[bs] = -1;
+          plen[bs] = 0;
+          psrc[bs] = kEmptySrc;
+        }
+      }
     }
-    int j = 0;  // rank of this slot among vacated slots
-    for (int o = 0; o < s; ++o) j += !(valid[o] && kept[o]);
-    if (j < n_adm) {
-      const int e = alist[j];
-      const int p = old * g.nq + e;
-      plan[bs] = p;
-      plen[bs] = block_ext(g, e).len;
-      psrc[bs] = step_id * g.nq + e;
-      for (int d = 0; d < g.D; ++d) pkbar[bs * g.D + d] = kbar_l[(bh * g.nl + p) * g.D + d];
-    } else {
-      plan[bs] = -1;
-      plen[bs] = 0;
-      psrc[bs] = kEmptySrc;
-      for (int d = 0; d < g.D; ++d) pkbar[bs * g.D + d] = 0.f;
-    }
+    nvac += __builtin_popcountll(m);
   }
 }
 
-// grid (S, H, B): move rows according to the plan; block (0,0,0) advances the ring head.
+// grid (S, H, B): move rows and pooled keys according to the plan; block
+// (0,0,0) advances the ring head.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void update_copy_kernel(Geo g, const int32_t* __restrict__ plan,
                                                                const T* __restrict__ kl, const T* __restrict__ vl,
+                                                               const float* __restrict__ kbar_l,
                                                                T* __restrict__ kp, T* __restrict__ vp,
+                                                               float* __restrict__ pkbar,
                                                                int32_t* __restrict__ ring_head) {
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const size_t bh = (size_t)b * g.H + h;
@@ -121,6 +122,8 @@ __global__ __launch_bounds__(kThreads) void update_copy_kernel(Geo g, const int3
     off = (p / g.nq) * g.ct;
   }
   const size_t dst = (bh * g.S + s) * (size_t)g.C * g.D;
+  for (int d = threadIdx.x; d < g.D; d += kThreads)
+    pkbar[(bh * g.S + s) * g.D + d] = p >= 0 ? kbar_l[(bh * g.nl + p) * g.D + d] : 0.f;
   for (int c = threadIdx.x; c < g.C * cpr; c += kThreads) {
     const int r = c / cpr, k = c - r * cpr;
     uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
@@ -161,9 +164,8 @@ hipError_t launch_persist_update(const Geo& g, const float* mass, const void* k_
                                  void* v_p, int32_t* plen, int32_t* psrc, float* pkbar, int32_t* n_rep,
                                  int32_t* plan, hipStream_t s) {
   const int NC = g.S + g.nq;
-  const size_t shm = (size_t)NC * 3 * 4 + (size_t)g.nq * 4;
-  update_decide_kernel<<<dim3(g.H, g.B), kThreads, shm, s>>>(g, mass, kbar_l, ring_head, step_id, plen, psrc, pkbar,
-                                                              n_rep, plan);
+  const size_t shm = (size_t)NC * 8 + (size_t)NC * 4 + (size_t)g.nq * 4;
+  update_decide_kernel<<<dim3(g.H, g.B), kThreads, shm, s>>>(g, mass, ring_head, step_id, plen, psrc, n_rep, plan);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (g.S == 0) {
@@ -172,11 +174,11 @@ hipError_t launch_persist_update(const Geo& g, const float* mass, const void* k_
   }
   dim3 grid(g.S, g.H, g.B);
   if (g.dtype == PBSA_BF16)
-    update_copy_kernel<bf16_t><<<grid, kThreads, 0, s>>>(g, plan, (const bf16_t*)k_l, (const bf16_t*)v_l,
-                                                        (bf16_t*)k_p, (bf16_t*)v_p, ring_head);
+    update_copy_kernel<bf16_t><<<grid, kThreads, 0, s>>>(g, plan, (const bf16_t*)k_l, (const bf16_t*)v_l, kbar_l,
+                                                        (bf16_t*)k_p, (bf16_t*)v_p, pkbar, ring_head);
   else
-    update_copy_kernel<float><<<grid, kThreads, 0, s>>>(g, plan, (const float*)k_l, (const float*)v_l,
-                                                       (float*)k_p, (float*)v_p, ring_head);
+    update_copy_kernel<float><<<grid, kThreads, 0, s>>>(g, plan, (const float*)k_l, (const float*)v_l, kbar_l,
+                                                       (float*)k_p, (float*)v_p, pkbar, ring_head);
   return hipGetLastError();
 }
 
