@@ -25,6 +25,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-fno-honor-nans",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable", "-Wno-unused-result",
     "-I", INCLUDE, "-I", CSRC,
 ]

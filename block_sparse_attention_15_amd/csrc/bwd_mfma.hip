@@ -253,10 +253,11 @@ __global__ __launch_bounds__(kDqThreads, 1) void dq_pers_kernel(BwdArgs a) {
 
 // Local part: 8 waves = 4 query blocks x 2 query tiles; per step the 32-row
 // half of each query block's current selected block (K and V) is staged.
-constexpr int kLocBlocks = 4;
+constexpr int kLocBlocks = 4;  // query blocks per workgroup (2 waves each)
+constexpr int kDqlThreads = 64 * 2 * kLocBlocks;
 
 template <int D> struct LocPf {
-  static constexpr int N = kLocBlocks * 32 * Sh<D>::CPR / kDqThreads;
+  static constexpr int N = kLocBlocks * 32 * Sh<D>::CPR / kDqlThreads;
   uint4 k[N], v[N];
 };
 
@@ -268,7 +269,7 @@ __device__ __forceinline__ void loc_load(const BwdArgs& a, size_t bh, int qg, in
   const bf16_t* vb = a.vl + bh * (size_t)g.NL * D;
 #pragma unroll
   for (int u = 0; u < LocPf<D>::N; ++u) {
-    const int id = threadIdx.x + kDqThreads * u;
+    const int id = threadIdx.x + kDqlThreads * u;
     const int w = id / (32 * Sh<D>::CPR), rem = id % (32 * Sh<D>::CPR);
     const int r = 32 * half + rem / Sh<D>::CPR, c = rem % Sh<D>::CPR;
     const int qb = qg * kLocBlocks + w;
@@ -294,7 +295,7 @@ template <int D>
 __device__ __forceinline__ void loc_store(const LocPf<D>& pf, char* buf) {
 #pragma unroll
   for (int u = 0; u < LocPf<D>::N; ++u) {
-    const int id = threadIdx.x + kDqThreads * u;
+    const int id = threadIdx.x + kDqlThreads * u;
     const int w = id / (32 * Sh<D>::CPR), rem = id % (32 * Sh<D>::CPR);
     const int r = rem / Sh<D>::CPR, c = rem % Sh<D>::CPR;
     char* region = buf + w * 2 * Sh<D>::TILEB;
@@ -304,7 +305,7 @@ __device__ __forceinline__ void loc_store(const LocPf<D>& pf, char* buf) {
 }
 
 template <int D>
-__global__ __launch_bounds__(kDqThreads, 1) void dq_local_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kDqlThreads, 1) void dq_local_kernel(BwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int BUF = kLocBlocks * 2 * Sh<D>::TILEB;
   const Geo& g = a.g;
@@ -363,79 +364,81 @@ __global__ __launch_bounds__(kDqThreads, 1) void dq_local_kernel(BwdArgs a) {
 // ===========================================================================
 // dK, dV, key-outer
 // ===========================================================================
-template <int D> struct KState {
+// Key-outer state of one wave (32 keys).  The dV pass needs K only
+// (S = Q K^T, dV += P^T dO); the dK pass needs K and V (dP = dO V^T,
+// dK += dS^T Q).  Splitting the two keeps each under 256 registers so two
+// waves share a SIMD.
+template <int D, bool DV> struct KState {
   bf16x8_t kf[Sh<D>::KS];
-  bf16x8_t vf[Sh<D>::KS];
-  f32x16_t dk[Sh<D>::DT];
-  f32x16_t dv[Sh<D>::DT];
+  bf16x8_t vf[DV ? 1 : Sh<D>::KS];
+  f32x16_t acc[Sh<D>::DT];
 };
 
-// row pointer (or null) for this lane's key
-template <int D>
-__device__ __forceinline__ void k_init(const bf16_t* krow, const bf16_t* vrow, bool ok, KState<D>& st) {
+template <int D, bool DV>
+__device__ __forceinline__ void k_init(const bf16_t* krow, const bf16_t* vrow, bool ok, KState<D, DV>& st) {
   const int h = (threadIdx.x & 63) >> 5;
 #pragma unroll
   for (int ks = 0; ks < Sh<D>::KS; ++ks) {
     st.kf[ks] = __builtin_bit_cast(bf16x8_t, ok ? ld16(krow + 16 * ks + 8 * h) : make_uint4(0, 0, 0, 0));
-    st.vf[ks] = __builtin_bit_cast(bf16x8_t, ok ? ld16(vrow + 16 * ks + 8 * h) : make_uint4(0, 0, 0, 0));
+    if (!DV)
+      st.vf[DV ? 0 : ks] = __builtin_bit_cast(bf16x8_t, ok ? ld16(vrow + 16 * ks + 8 * h) : make_uint4(0, 0, 0, 0));
   }
 #pragma unroll
-  for (int dt = 0; dt < Sh<D>::DT; ++dt) {
-    st.dk[dt] = f32x16_t{};
-    st.dv[dt] = f32x16_t{};
-  }
+  for (int dt = 0; dt < Sh<D>::DT; ++dt) st.acc[dt] = f32x16_t{};
 }
 
 // One 32-query tile in LDS: Q tile tq, dO tile td, per-row lse*log2e and D.
-template <int D>
+template <int D, bool DV>
 __device__ __forceinline__ void k_tile(const char* tq, const char* td, const float* lse2, const float* dl, float c2,
-                                       KState<D>& st) {
+                                       KState<D, DV>& st) {
   const int lane = threadIdx.x & 63, h = lane >> 5, l32 = lane & 31;
   f32x16_t s = {}, dp = {};
 #pragma unroll
   for (int ks = 0; ks < Sh<D>::KS; ++ks) {
     s = mfma(rd_nat<D>(tq, l32, 2 * ks + h), st.kf[ks], s);
-    dp = mfma(rd_nat<D>(td, l32, 2 * ks + h), st.vf[ks], dp);
+    if (!DV) dp = mfma(rd_nat<D>(td, l32, 2 * ks + h), st.vf[DV ? 0 : ks], dp);
   }
-  f32x16_t p, ds;
+  f32x16_t x;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const float4 L = *reinterpret_cast<const float4*>(lse2 + 8 * i + 4 * h);
-    const float4 Dv = *reinterpret_cast<const float4*>(dl + 8 * i + 4 * h);
-    const float Ls[4] = {L.x, L.y, L.z, L.w}, Ds[4] = {Dv.x, Dv.y, Dv.z, Dv.w};
+    const float Ls[4] = {L.x, L.y, L.z, L.w};
+    float Ds[4] = {0.f, 0.f, 0.f, 0.f};
+    if (!DV) {
+      const float4 Dv = *reinterpret_cast<const float4*>(dl + 8 * i + 4 * h);
+      Ds[0] = Dv.x;
+      Ds[1] = Dv.y;
+      Ds[2] = Dv.z;
+      Ds[3] = Dv.w;
+    }
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const int j = 4 * i + jj;
-      p[j] = __builtin_amdgcn_exp2f(fmaf(s[j], c2, -Ls[jj]));
-      ds[j] = p[j] * (dp[j] - Ds[jj]);
+      const float p = __builtin_amdgcn_exp2f(fmaf(s[j], c2, -Ls[jj]));
+      x[j] = DV ? p : p * (dp[j] - Ds[jj]);
     }
   }
-  const bf16x8_t p0 = pack8(p, 0), p1 = pack8(p, 1), d0 = pack8(ds, 0), d1 = pack8(ds, 1);
+  const bf16x8_t x0 = pack8(x, 0), x1 = pack8(x, 1);
+  const char* tb = DV ? td : tq;  // dV += P^T dO ; dK += dS^T Q
 #pragma unroll
   for (int dt = 0; dt < Sh<D>::DT; ++dt) {
-    st.dv[dt] = mfma(p0, rd_tr<D>(td, 0, dt), st.dv[dt]);
-    st.dv[dt] = mfma(p1, rd_tr<D>(td, 1, dt), st.dv[dt]);
-    st.dk[dt] = mfma(d0, rd_tr<D>(tq, 0, dt), st.dk[dt]);
-    st.dk[dt] = mfma(d1, rd_tr<D>(tq, 1, dt), st.dk[dt]);
+    st.acc[dt] = mfma(x0, rd_tr<D>(tb, 0, dt), st.acc[dt]);
+    st.acc[dt] = mfma(x1, rd_tr<D>(tb, 1, dt), st.acc[dt]);
   }
 }
 
 // Write this wave's 32 key rows: row kr of the tile goes to dst(kr) if kr < n, else zero.
-template <int D, typename RowPtr>
-__device__ __forceinline__ void k_write(const KState<D>& st, int n, float scale, RowPtr rows) {
+template <int D, bool DV, typename RowPtr>
+__device__ __forceinline__ void k_write(const KState<D, DV>& st, int n, float scale, RowPtr rows) {
   const int lane = threadIdx.x & 63, h = lane >> 5, l32 = lane & 31;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     const int kr = 8 * (j >> 2) + 4 * h + (j & 3);
-    float* dk;
-    float* dv;
-    if (!rows(kr, dk, dv)) continue;
+    float* dst;
+    if (!rows(kr, dst)) continue;
     const bool ok = kr < n;
 #pragma unroll
-    for (int dt = 0; dt < Sh<D>::DT; ++dt) {
-      dk[32 * dt + l32] = ok ? st.dk[dt][j] * scale : 0.f;
-      dv[32 * dt + l32] = ok ? st.dv[dt][j] : 0.f;
-    }
+    for (int dt = 0; dt < Sh<D>::DT; ++dt) dst[32 * dt + l32] = ok ? st.acc[dt][j] * scale : 0.f;
   }
 }
 
@@ -486,8 +489,8 @@ struct QTileLoader {
   }
 };
 
-template <int D>
-__global__ __launch_bounds__(kKvThreads, 1) void dkv_pers_kernel(BwdArgs a) {
+template <int D, bool DV>
+__global__ __launch_bounds__(kKvThreads, 2) void dkv_pers_kernel(BwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int BUF = 2 * Sh<D>::TILEB + 256;
   const Geo& g = a.g;
@@ -503,8 +506,8 @@ __global__ __launch_bounds__(kKvThreads, 1) void dkv_pers_kernel(BwdArgs a) {
   const int nk = min(max(n - 32 * kh, 0), 32);  // valid keys of this wave's tile
   const size_t sbase = (bh * g.S + (has_slot ? slot : 0)) * (size_t)g.C * D;
   const int kr = 32 * kh + l32;
-  KState<D> st;
-  k_init<D>(a.kp + sbase + (size_t)kr * D, a.vp + sbase + (size_t)kr * D, kr < n, st);
+  KState<D, DV> st;
+  k_init<D, DV>(a.kp + sbase + (size_t)kr * D, a.vp + sbase + (size_t)kr * D, kr < n, st);
   const float c2 = g.scale * kLog2e;
 
   const int nsteps = (g.ct + 31) / 32;
@@ -521,27 +524,25 @@ __global__ __launch_bounds__(kKvThreads, 1) void dkv_pers_kernel(BwdArgs a) {
     if (i + 1 < nsteps) pf.load(a, bh, Contig{32 * (i + 1), g.ct});
     if (nk > 0) {
       const float* f = reinterpret_cast<const float*>(buf + 2 * Sh<D>::TILEB);
-      k_tile<D>(buf, buf + Sh<D>::TILEB, f, f + 32, c2, st);
+      k_tile<D, DV>(buf, buf + Sh<D>::TILEB, f, f + 32, c2, st);
     }
     if (i + 1 < nsteps) pf.store(smem + ((i + 1) & 1) * BUF);
     __syncthreads();
   }
   if (!has_slot || 32 * kh >= g.C) return;
-  float* dkb = a.dkp + sbase;
-  float* dvb = a.dvp + sbase;
-  k_write<D>(st, nk, g.scale, [&](int r, float*& dk, float*& dv) {
+  float* ob = (DV ? a.dvp : a.dkp) + sbase;
+  k_write<D, DV>(st, nk, DV ? 1.0f : g.scale, [&](int r, float*& dst) {
     const int row = 32 * kh + r;
     if (row >= g.C) return false;
-    dk = dkb + (size_t)row * D;
-    dv = dvb + (size_t)row * D;
+    dst = ob + (size_t)row * D;
     return true;
   });
 }
 
 constexpr int kKvlThreads = 128;  // dkv_local: 2 waves = one local block
 
-template <int D>
-__global__ __launch_bounds__(kKvlThreads, 1) void dkv_local_kernel(BwdArgs a) {
+template <int D, bool DV>
+__global__ __launch_bounds__(kKvlThreads, 2) void dkv_local_kernel(BwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int BUF = 2 * Sh<D>::TILEB + 256;
   const Geo& g = a.g;
@@ -557,8 +558,8 @@ __global__ __launch_bounds__(kKvlThreads, 1) void dkv_local_kernel(BwdArgs a) {
   const int kr = 32 * wave + l32;
   const bool kok = kr < ke.len;
   const size_t krow = (bh * g.NL + koff + (kok ? block_token(g, ke, kr) : 0)) * (size_t)D;
-  KState<D> st;
-  k_init<D>(a.kl + krow, a.vl + krow, kok, st);
+  KState<D, DV> st;
+  k_init<D, DV>(a.kl + krow, a.vl + krow, kok, st);
   const float c2 = g.scale * kLog2e;
 
   const int ncount = a.tcount[bh * g.nl + p];
@@ -595,21 +596,18 @@ __global__ __launch_bounds__(kKvlThreads, 1) void dkv_local_kernel(BwdArgs a) {
       }
       if (nk > 0) {
         const float* f = reinterpret_cast<const float*>(buf + 2 * Sh<D>::TILEB);
-        k_tile<D>(buf, buf + Sh<D>::TILEB, f, f + 32, c2, st);
+        k_tile<D, DV>(buf, buf + Sh<D>::TILEB, f, f + 32, c2, st);
       }
       if (i + 1 < nsteps) pf.store(smem + ((i + 1) & 1) * BUF);
       __syncthreads();
     }
   }
   if (nk <= 0) return;
-  float* dkb = a.dkl + (bh * g.NL + koff) * (size_t)D;
-  float* dvb = a.dvl + (bh * g.NL + koff) * (size_t)D;
-  k_write<D>(st, nk, g.scale, [&](int r, float*& dk, float*& dv) {
+  float* ob = (DV ? a.dvl : a.dkl) + (bh * g.NL + koff) * (size_t)D;
+  k_write<D, DV>(st, nk, DV ? 1.0f : g.scale, [&](int r, float*& dst) {
     const int row = 32 * wave + r;
     if (row >= ke.len) return false;
-    const size_t t = (size_t)block_token(g, ke, row) * D;
-    dk = dkb + t;
-    dv = dvb + t;
+    dst = ob + (size_t)block_token(g, ke, row) * D;
     return true;
   });
 }
@@ -629,8 +627,10 @@ hipError_t launch_d(const BwdArgs& base, hipStream_t s) {
   if (!attr) {
     hipError_t e = set_lds(dq_pers_kernel<D>, shm_dq);
     if (e == hipSuccess) e = set_lds(dq_local_kernel<D>, shm_dql);
-    if (e == hipSuccess) e = set_lds(dkv_pers_kernel<D>, shm_kv);
-    if (e == hipSuccess) e = set_lds(dkv_local_kernel<D>, shm_kv);
+    if (e == hipSuccess) e = set_lds(dkv_pers_kernel<D, true>, shm_kv);
+    if (e == hipSuccess) e = set_lds(dkv_pers_kernel<D, false>, shm_kv);
+    if (e == hipSuccess) e = set_lds(dkv_local_kernel<D, true>, shm_kv);
+    if (e == hipSuccess) e = set_lds(dkv_local_kernel<D, false>, shm_kv);
     if (e != hipSuccess) return e;
     attr = true;
   }
@@ -643,16 +643,20 @@ hipError_t launch_d(const BwdArgs& base, hipStream_t s) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   a.ntiles = (g.nq + kLocBlocks - 1) / kLocBlocks;
   total = g.B * g.H * a.ntiles;
-  dq_local_kernel<D><<<((total + 7) / 8) * 8, kDqThreads, shm_dql, s>>>(a);
+  dq_local_kernel<D><<<((total + 7) / 8) * 8, kDqlThreads, shm_dql, s>>>(a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (g.S > 0) {
     a.ntiles = (g.S + 1) / 2;
     total = g.B * g.H * a.ntiles;
-    dkv_pers_kernel<D><<<((total + 7) / 8) * 8, kKvThreads, shm_kv, s>>>(a);
+    dkv_pers_kernel<D, true><<<((total + 7) / 8) * 8, kKvThreads, shm_kv, s>>>(a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    dkv_pers_kernel<D, false><<<((total + 7) / 8) * 8, kKvThreads, shm_kv, s>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   total = g.B * g.H * g.nl;
-  dkv_local_kernel<D><<<((total + 7) / 8) * 8, kKvlThreads, shm_kv, s>>>(a);
+  dkv_local_kernel<D, true><<<((total + 7) / 8) * 8, kKvlThreads, shm_kv, s>>>(a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  dkv_local_kernel<D, false><<<((total + 7) / 8) * 8, kKvlThreads, shm_kv, s>>>(a);
   return hipGetLastError();
 }
 
