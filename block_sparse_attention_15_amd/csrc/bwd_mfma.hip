@@ -116,6 +116,7 @@ struct BwdArgs {
   float* dvp;
   float* dkl;
   float* dvl;
+  GeoTab tab;
   int ntiles;
 };
 
@@ -261,8 +262,32 @@ template <int D> struct LocPf {
   uint4 k[N], v[N];
 };
 
+// Row tokens of every step of this workgroup, built once in LDS (see the
+// forward's local kernel): rowtab[(w*K + t)*64 + r], lentab[w*K + t].
+constexpr int kRowTabMax = 24 * 1024;
+
+__device__ __forceinline__ void build_rowtab(const BwdArgs& a, size_t bh, int qg, int nthreads, int* rowtab,
+                                             int* lentab) {
+  const Geo& g = a.g;
+  for (int x = threadIdx.x; x < kLocBlocks * g.K * 64; x += nthreads) {
+    const int w = x / (g.K * 64), t = (x / 64) % g.K, r = x & 63;
+    const int qb = qg * kLocBlocks + w;
+    int tok = -1, len = 0;
+    if (qb < g.nq) {
+      const int p = a.topk[(bh * g.nq + qb) * g.K + t];
+      if ((unsigned)p < (unsigned)g.nl) {
+        len = a.tab.blen[a.tab.pblk[p]];
+        if (r < len) tok = a.tab.pbase[p] + a.tab.btok[a.tab.pblk[p] * g.C + r];
+      }
+    }
+    rowtab[x] = tok;
+    if (r == 0) lentab[w * g.K + t] = len;
+  }
+}
+
 template <int D>
-__device__ __forceinline__ void loc_load(const BwdArgs& a, size_t bh, int qg, int j, LocPf<D>& pf) {
+__device__ __forceinline__ void loc_load(const BwdArgs& a, size_t bh, int qg, int j, LocPf<D>& pf,
+                                         const int* rowtab) {
   const Geo& g = a.g;
   const int t = j >> 1, half = j & 1;
   const bf16_t* kb = a.kl + bh * (size_t)g.NL * D;
@@ -275,13 +300,17 @@ __device__ __forceinline__ void loc_load(const BwdArgs& a, size_t bh, int qg, in
     const int qb = qg * kLocBlocks + w;
     bool ok = false;
     size_t off = 0;
-    if (qb < g.nq) {
+    if (rowtab) {
+      const int tok = rowtab[(w * g.K + t) * 64 + r];
+      ok = tok >= 0;
+      off = (size_t)(ok ? tok : 0) * D + c * 8;
+    } else if (qb < g.nq) {
       const int p = a.topk[(bh * g.nq + qb) * g.K + t];
-      if ((unsigned)p < (unsigned)g.nl) {
-        const BlockExt e = block_ext(g, p % g.nq);
-        if (r < e.len) {
+      if ((unsigned)p < (unsigned)g.nl && r < g.C) {
+        const int tok = a.tab.btok[a.tab.pblk[p] * g.C + r];
+        if (tok >= 0) {
           ok = true;
-          off = ((size_t)(p / g.nq) * g.ct + block_token(g, e, r)) * D + c * 8;
+          off = (size_t)(a.tab.pbase[p] + tok) * D + c * 8;
         }
       }
     }
@@ -326,18 +355,31 @@ __global__ __launch_bounds__(kDqlThreads, 1) void dq_local_kernel(BwdArgs a) {
   q_init<D>(a, bh, tok, ok, st);
   const float c2 = g.scale * kLog2e;
   const int nsteps = 2 * g.K;
+  const bool use_tab = kLocBlocks * g.K * 64 * 4 <= kRowTabMax;
+  int* rowtab = use_tab ? reinterpret_cast<int*>(smem + 2 * BUF) : nullptr;
+  int* lentab = rowtab + kLocBlocks * g.K * 64;
+  if (use_tab) {
+    build_rowtab(a, bh, qg, kDqlThreads, rowtab, lentab);
+    __syncthreads();
+  }
   LocPf<D> pf;
-  loc_load<D>(a, bh, qg, 0, pf);
+  loc_load<D>(a, bh, qg, 0, pf, rowtab);
   loc_store<D>(pf, smem);
   __syncthreads();
   for (int j = 0; j < nsteps; ++j) {
     char* buf = smem + (j & 1) * BUF;
     int nv = 0;
     if (active) {
-      const int p = a.topk[(bh * g.nq + qb) * g.K + (j >> 1)];
-      if ((unsigned)p < (unsigned)g.nl) nv = min(block_ext(g, p % g.nq).len - 32 * (j & 1), 32);
+      int len = 0;
+      if (use_tab) {
+        len = lentab[(wave >> 1) * g.K + (j >> 1)];
+      } else {
+        const int p = a.topk[(bh * g.nq + qb) * g.K + (j >> 1)];
+        if ((unsigned)p < (unsigned)g.nl) len = a.tab.blen[a.tab.pblk[p]];
+      }
+      nv = min(len - 32 * (j & 1), 32);
     }
-    if (j + 1 < nsteps) loc_load<D>(a, bh, qg, j + 1, pf);
+    if (j + 1 < nsteps) loc_load<D>(a, bh, qg, j + 1, pf, rowtab);
     if (nv > 0) {
       const char* region = buf + (wave >> 1) * 2 * Sh<D>::TILEB;
       q_tile<D>(region, region + Sh<D>::TILEB, nv, c2, st);
@@ -564,35 +606,50 @@ __global__ __launch_bounds__(kKvlThreads, 2) void dkv_local_kernel(BwdArgs a) {
 
   const int ncount = a.tcount[bh * g.nl + p];
   const int32_t* lst = a.tlist + (bh * g.nl + p) * g.nq;
-  struct Gather {
-    Geo g;
-    BlockExt e;
-    int half;
+  struct Gather {  // rows 32*half .. of one selecting query block (token row table)
+    const int* rows;
+    int C, half;
     __device__ int operator()(int i) const {
       const int r = 32 * half + i;
-      return r < e.len ? block_token(g, e, r) : -1;
+      return r < C ? rows[r] : -1;
     }
   };
+  // The selecting query blocks' row tokens can be copied once into LDS, but
+  // the extra LDS halves the resident workgroups of this 2-wave kernel and
+  // measured slower; the rows are read from the (L2-resident) global table.
+  constexpr bool use_tab = false;
+  int* qtab = reinterpret_cast<int*>(smem + 2 * BUF);
+  int* qlen = qtab + g.nq * 64;
+  if (use_tab) {
+    for (int x = threadIdx.x; x < ncount * 64; x += kKvlThreads) {
+      const int sidx = x >> 6, r = x & 63, blk = lst[sidx];
+      qtab[x] = r < g.C ? a.tab.btok[blk * g.C + r] : -1;
+      if (r == 0) qlen[sidx] = a.tab.blen[blk];
+    }
+    __syncthreads();
+  }
+  auto len_of = [&](int sidx) { return use_tab ? qlen[sidx] : a.tab.blen[lst[sidx]]; };
+  auto rows_of = [&](int sidx) -> const int* { return use_tab ? qtab + sidx * 64 : a.tab.btok + lst[sidx] * g.C; };
   // steps: (selecting query block, half) pairs, in list order
   int nsteps = 0;
-  for (int s = 0; s < ncount; ++s) nsteps += (block_ext(g, lst[s]).len + 31) / 32;
+  for (int sidx = 0; sidx < ncount; ++sidx) nsteps += (len_of(sidx) + 31) / 32;
   if (nsteps > 0) {
     int cur = 0, half = 0;  // next step to load: list entry and half
-    BlockExt ce = block_ext(g, lst[0]);
+    int clen = len_of(0);
     QTileLoader<D, kKvlThreads, Gather> pf;
-    pf.load(a, bh, Gather{g, ce, half});
+    pf.load(a, bh, Gather{rows_of(0), g.C, half});
     pf.store(smem);
     __syncthreads();
     for (int i = 0; i < nsteps; ++i) {
       char* buf = smem + (i & 1) * BUF;
       if (i + 1 < nsteps) {
-        if (32 * (half + 1) < ce.len) {
+        if (32 * (half + 1) < clen) {
           ++half;
         } else {
-          ce = block_ext(g, lst[++cur]);
+          clen = len_of(++cur);
           half = 0;
         }
-        pf.load(a, bh, Gather{g, ce, half});
+        pf.load(a, bh, Gather{rows_of(cur), g.C, half});
       }
       if (nk > 0) {
         const float* f = reinterpret_cast<const float*>(buf + 2 * Sh<D>::TILEB);
@@ -621,12 +678,16 @@ template <int D>
 hipError_t launch_d(const BwdArgs& base, hipStream_t s) {
   const Geo& g = base.g;
   const size_t shm_dq = 2 * 4 * Sh<D>::TILEB;                 // persistent: 2 x (K,K,V,V)
-  const size_t shm_dql = 2 * kLocBlocks * 2 * Sh<D>::TILEB;   // local: 2 x 4 x (K,V)
+  const size_t tabb = (size_t)kLocBlocks * g.K * 64 * 4;
+  const size_t shm_dql = 2 * kLocBlocks * 2 * Sh<D>::TILEB +   // local: 2 x 4 x (K,V)
+                         (tabb <= (size_t)kRowTabMax ? tabb + kLocBlocks * g.K * 4 : 0);
   const size_t shm_kv = 2 * (2 * Sh<D>::TILEB + 256);
+  const size_t shm_kvl = shm_kv;
   static bool attr = false;
   if (!attr) {
     hipError_t e = set_lds(dq_pers_kernel<D>, shm_dq);
-    if (e == hipSuccess) e = set_lds(dq_local_kernel<D>, shm_dql);
+    if (e == hipSuccess)
+      e = set_lds(dq_local_kernel<D>, 2 * kLocBlocks * 2 * Sh<D>::TILEB + kRowTabMax + 4096);
     if (e == hipSuccess) e = set_lds(dkv_pers_kernel<D, true>, shm_kv);
     if (e == hipSuccess) e = set_lds(dkv_pers_kernel<D, false>, shm_kv);
     if (e == hipSuccess) e = set_lds(dkv_local_kernel<D, true>, shm_kv);
@@ -654,9 +715,9 @@ hipError_t launch_d(const BwdArgs& base, hipStream_t s) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   total = g.B * g.H * g.nl;
-  dkv_local_kernel<D, true><<<((total + 7) / 8) * 8, kKvlThreads, shm_kv, s>>>(a);
+  dkv_local_kernel<D, true><<<((total + 7) / 8) * 8, kKvlThreads, shm_kvl, s>>>(a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  dkv_local_kernel<D, false><<<((total + 7) / 8) * 8, kKvlThreads, shm_kv, s>>>(a);
+  dkv_local_kernel<D, false><<<((total + 7) / 8) * 8, kKvlThreads, shm_kvl, s>>>(a);
   return hipGetLastError();
 }
 
@@ -668,9 +729,12 @@ hipError_t launch_bwd_mfma(const Geo& g, const void* q, const void* k_p, const v
                            const void* k_l, const void* v_l, const int32_t* topk, const float* lse,
                            const void* dout, float* dq, float* dk_p, float* dv_p, float* dk_l, float* dv_l,
                            WsBwd ws, hipStream_t s) {
+  GeoTab tab;
+  hipError_t e = launch_geo_table(g, ws.geo, &tab, s);
+  if (e != hipSuccess) return e;
   BwdArgs a{g, (const bf16_t*)q, (const bf16_t*)k_p, (const bf16_t*)v_p, plen, (const bf16_t*)k_l,
             (const bf16_t*)v_l, topk, lse, ws.delta, (const bf16_t*)dout, ws.tcount, ws.tlist,
-            dq, dk_p, dv_p, dk_l, dv_l, 0};
+            dq, dk_p, dv_p, dk_l, dv_l, tab, 0};
   return g.D == 128 ? launch_d<128>(a, s) : launch_d<64>(a, s);
 }
 

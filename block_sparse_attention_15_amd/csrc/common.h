@@ -85,6 +85,20 @@ constexpr int32_t kEmptySrc = INT32_MIN;
 // Launchers implemented in the kernel translation units.  Each returns the
 // hipError_t of its launches.
 // ---------------------------------------------------------------------------
+// Geometry lookup tables (filled on the device by launch_geo_table at the
+// start of the attention entry points, in the caller's workspace): token
+// offset inside the chunk of row r of chunk block j (-1 past its length),
+// block lengths, and for every physical local block its chunk's first token
+// and its block index inside the chunk.
+struct GeoTab {
+  const int32_t* btok;   // [nq][C]
+  const int32_t* blen;   // [nq]
+  const int32_t* pbase;  // [nl]
+  const int32_t* pblk;   // [nl]
+};
+size_t geo_table_bytes(const Geo& g);
+hipError_t launch_geo_table(const Geo& g, void* ws, GeoTab* tab, hipStream_t s);
+
 struct WsScore {
   float* qbar;   // [B,H,nq,D]
   float* prow;   // [B,H,nq,S+nl]  pooled softmax rows
@@ -101,6 +115,7 @@ struct WsBwd {
   float* delta;     // [B,H,Nq]      rowsum(dO * O)
   int32_t* tcount;  // [B,H,nl]      query blocks that selected each local block
   int32_t* tlist;   // [B,H,nl,nq]   their ids, ascending
+  void* geo;        // geometry tables (geo_table_bytes)
 };
 hipError_t launch_bwd(const Geo& g, const void* q, const void* k_p, const void* v_p, const int32_t* plen,
                       const void* k_l, const void* v_l, const int32_t* topk, const void* o,

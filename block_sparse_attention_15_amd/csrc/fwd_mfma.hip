@@ -82,6 +82,7 @@ struct FwdArgs {
   float* lse;
   float* o_part;    // [B,H,ct,D] persistent-part output (normalised), fp32
   float* lse_part;  // [B,H,ct]   its log-sum-exp (-inf when no slot is valid)
+  GeoTab tab;       // geometry lookup tables
   int ntiles;       // work items per (batch, head)
 };
 
@@ -326,8 +327,33 @@ template <int D> struct LocPrefetch {
   uint4 k[N], v[N];
 };
 
+// Row tokens of every step of this workgroup, built once in LDS:
+// rowtab[(w*K + t)*64 + r] = ring row of row r of query block w's t-th
+// selected block, or -1.  Used when it fits (4*K*64 ints <= kRowTabMax).
+constexpr int kRowTabMax = 24 * 1024;
+
+__device__ __forceinline__ void build_rowtab(const FwdArgs& a, size_t bh, int qg, int nthreads, int* rowtab,
+                                             int* lentab) {
+  const Geo& g = a.g;
+  for (int x = threadIdx.x; x < kLocBlocks * g.K * 64; x += nthreads) {
+    const int w = x / (g.K * 64), t = (x / 64) % g.K, r = x & 63;
+    const int qb = qg * kLocBlocks + w;
+    int tok = -1, len = 0;
+    if (qb < g.nq) {
+      const int p = a.topk[(bh * g.nq + qb) * g.K + t];
+      if ((unsigned)p < (unsigned)g.nl) {
+        len = a.tab.blen[a.tab.pblk[p]];
+        if (r < len) tok = a.tab.pbase[p] + a.tab.btok[a.tab.pblk[p] * g.C + r];
+      }
+    }
+    rowtab[x] = tok;
+    if (r == 0) lentab[w * g.K + t] = len;
+  }
+}
+
 template <int D>
-__device__ __forceinline__ void loc_load(const FwdArgs& a, size_t bh, int qg, int j, LocPrefetch<D>& pf) {
+__device__ __forceinline__ void loc_load(const FwdArgs& a, size_t bh, int qg, int j, LocPrefetch<D>& pf,
+                                         const int* rowtab) {
   using Sh = Shape<D>;
   const Geo& g = a.g;
   const int t = j >> 1, half = j & 1;
@@ -341,13 +367,17 @@ __device__ __forceinline__ void loc_load(const FwdArgs& a, size_t bh, int qg, in
     const int qb = qg * kLocBlocks + w;
     bool ok = false;
     size_t off = 0;
-    if (qb < g.nq) {
+    if (rowtab) {
+      const int tok = rowtab[(w * g.K + t) * 64 + r];
+      ok = tok >= 0;
+      off = (size_t)(ok ? tok : 0) * D + c * 8;
+    } else if (qb < g.nq) {
       const int p = a.topk[(bh * g.nq + qb) * g.K + t];
-      if ((unsigned)p < (unsigned)g.nl) {
-        const BlockExt e = block_ext(g, p % g.nq);
-        if (r < e.len) {
+      if ((unsigned)p < (unsigned)g.nl && r < g.C) {
+        const int tok = a.tab.btok[a.tab.pblk[p] * g.C + r];
+        if (tok >= 0) {
           ok = true;
-          off = ((size_t)(p / g.nq) * g.ct + block_token(g, e, r)) * D + c * 8;
+          off = (size_t)(a.tab.pbase[p] + tok) * D + c * 8;
         }
       }
     }
@@ -395,18 +425,31 @@ __global__ __launch_bounds__(kLocThreads, 1) void fwd_local_kernel(FwdArgs a) {
   const float c2 = g.scale * 1.4426950408889634f;
 
   const int nsteps = 2 * g.K;
+  const bool use_tab = kLocBlocks * g.K * 64 * 4 <= kRowTabMax;
+  int* rowtab = use_tab ? reinterpret_cast<int*>(smem + 2 * kBufBytes) : nullptr;
+  int* lentab = rowtab + kLocBlocks * g.K * 64;
+  if (use_tab) {
+    build_rowtab(a, bh, qg, kLocThreads, rowtab, lentab);
+    __syncthreads();
+  }
   LocPrefetch<D> pf;
-  loc_load<D>(a, bh, qg, 0, pf);
+  loc_load<D>(a, bh, qg, 0, pf, rowtab);
   loc_store<D>(pf, smem);
   __syncthreads();
   for (int j = 0; j < nsteps; ++j) {
     char* buf = smem + (j & 1) * kBufBytes;
     int nv = 0;
     if (ntq) {
-      const int p = a.topk[(bh * g.nq + qb) * g.K + (j >> 1)];
-      if ((unsigned)p < (unsigned)g.nl) nv = min(block_ext(g, p % g.nq).len - 32 * (j & 1), 32);
+      int len = 0;
+      if (use_tab) {
+        len = lentab[(wave >> 1) * g.K + (j >> 1)];
+      } else {
+        const int p = a.topk[(bh * g.nq + qb) * g.K + (j >> 1)];
+        if ((unsigned)p < (unsigned)g.nl) len = a.tab.blen[a.tab.pblk[p]];
+      }
+      nv = min(len - 32 * (j & 1), 32);
     }
-    if (j + 1 < nsteps) loc_load<D>(a, bh, qg, j + 1, pf);
+    if (j + 1 < nsteps) loc_load<D>(a, bh, qg, j + 1, pf, rowtab);
     if (nv > 0) {
       const char* region = buf + (wave >> 1) * (64 * Sh::ROWB);
       tile<D, 1>(region, region + 32 * Sh::ROWB, 0, nv, 1, c2, st);
@@ -455,9 +498,12 @@ template <int D>
 hipError_t launch_d(const FwdArgs& base, hipStream_t s) {
   static bool attr = false;
   const size_t shm = 2 * kBufBytes;
+  const Geo& g0 = base.g;
+  const size_t tabb = (size_t)kLocBlocks * g0.K * 64 * 4;
+  const size_t shm_loc = shm + (tabb <= (size_t)kRowTabMax ? tabb + kLocBlocks * g0.K * 4 : 0);
   if (!attr) {
     hipError_t e = set_lds(fwd_pers_kernel<D>, shm);
-    if (e == hipSuccess) e = set_lds(fwd_local_kernel<D>, shm);
+    if (e == hipSuccess) e = set_lds(fwd_local_kernel<D>, shm + kRowTabMax + 4096);
     if (e != hipSuccess) return e;
     attr = true;
   }
@@ -470,7 +516,7 @@ hipError_t launch_d(const FwdArgs& base, hipStream_t s) {
   if (e != hipSuccess) return e;
   a.ntiles = (g.nq + kLocBlocks - 1) / kLocBlocks;
   total = g.B * g.H * a.ntiles;
-  fwd_local_kernel<D><<<((total + 7) / 8) * 8, kLocThreads, shm, s>>>(a);
+  fwd_local_kernel<D><<<((total + 7) / 8) * 8, kLocThreads, shm_loc, s>>>(a);
   return hipGetLastError();
 }
 
@@ -481,16 +527,20 @@ bool fwd_mfma_supported(const Geo& g) {
 }
 
 size_t fwd_mfma_workspace(const Geo& g) {
-  return ((size_t)g.B * g.H * g.ct * g.D * 4 + 255) / 256 * 256 + ((size_t)g.B * g.H * g.ct * 4 + 255) / 256 * 256;
+  return geo_table_bytes(g) + ((size_t)g.B * g.H * g.ct * g.D * 4 + 255) / 256 * 256 +
+         ((size_t)g.B * g.H * g.ct * 4 + 255) / 256 * 256;
 }
 
 hipError_t launch_fwd_mfma(const Geo& g, const void* q, const void* k_p, const void* v_p, const int32_t* plen,
                            const void* k_l, const void* v_l, const int32_t* topk, void* o, float* lse, void* ws,
                            hipStream_t s) {
-  float* o_part = (float*)ws;
-  float* lse_part = (float*)((char*)ws + ((size_t)g.B * g.H * g.ct * g.D * 4 + 255) / 256 * 256);
+  GeoTab tab;
+  hipError_t e = launch_geo_table(g, ws, &tab, s);
+  if (e != hipSuccess) return e;
+  float* o_part = (float*)((char*)ws + geo_table_bytes(g));
+  float* lse_part = (float*)((char*)o_part + ((size_t)g.B * g.H * g.ct * g.D * 4 + 255) / 256 * 256);
   FwdArgs a{g, (const bf16_t*)q, (const bf16_t*)k_p, (const bf16_t*)v_p, plen, (const bf16_t*)k_l,
-            (const bf16_t*)v_l, topk, (bf16_t*)o, lse, o_part, lse_part, 0};
+            (const bf16_t*)v_l, topk, (bf16_t*)o, lse, o_part, lse_part, tab, 0};
   return g.D == 128 ? launch_d<128>(a, s) : launch_d<64>(a, s);
 }
 
