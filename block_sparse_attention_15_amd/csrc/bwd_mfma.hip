@@ -484,7 +484,9 @@ __device__ __forceinline__ void k_write(const KState<D, DV>& st, int n, float sc
   }
 }
 
-constexpr int kKvThreads = 256;   // dkv_pers: 4 waves = 2 slots x 2 key tiles
+constexpr int kKvWaves = 4;       // dkv_pers: 4 waves = 2 slots x 2 key tiles
+constexpr int kKvThreads = 64 * kKvWaves;
+constexpr int kKvSlots = kKvWaves / 2;
 
 template <int D> struct QPf {
   static constexpr int N = 32 * Sh<D>::CPR / 64;  // chunks per lane per tensor when one wave loads
@@ -494,7 +496,8 @@ template <int D> struct QPf {
 // row(i) returns the token of tile row i, or -1 for an empty row.
 template <int D, int NTHR, typename RowFn>
 struct QTileLoader {
-  static constexpr int N = 32 * Sh<D>::CPR / NTHR;
+  static constexpr int NCH = 32 * Sh<D>::CPR;         // 16-byte chunks per tensor tile
+  static constexpr int N = (NCH + NTHR - 1) / NTHR;   // per thread
   uint4 q[N], d[N];
   float l, dd;
   __device__ __forceinline__ void load(const BwdArgs& a, size_t bh, RowFn row) {
@@ -503,7 +506,7 @@ struct QTileLoader {
 #pragma unroll
     for (int u = 0; u < N; ++u) {
       const int id = tid + NTHR * u, r = id / Sh<D>::CPR, c = id % Sh<D>::CPR;
-      const int tok = row(r);
+      const int tok = id < NCH ? row(r) : -1;
       const size_t off = (bh * g.ct + (tok < 0 ? 0 : tok)) * (size_t)D + c * 8;
       q[u] = tok >= 0 ? ld16(a.q + off) : make_uint4(0, 0, 0, 0);
       d[u] = tok >= 0 ? ld16(a.dout + off) : make_uint4(0, 0, 0, 0);
@@ -520,6 +523,7 @@ struct QTileLoader {
 #pragma unroll
     for (int u = 0; u < N; ++u) {
       const int id = tid + NTHR * u, r = id / Sh<D>::CPR, c = id % Sh<D>::CPR;
+      if (id >= NCH) break;
       st_chunk(buf, Sh<D>::ROWB, Sh<D>::CPR, r, c, q[u]);
       st_chunk(buf + Sh<D>::TILEB, Sh<D>::ROWB, Sh<D>::CPR, r, c, d[u]);
     }
@@ -539,10 +543,10 @@ __global__ __launch_bounds__(kKvThreads, 2) void dkv_pers_kernel(BwdArgs a) {
   const int total = g.B * g.H * a.ntiles;
   const int lin = xcd_remap(total);
   if (lin >= total) return;
-  const int sp = lin % a.ntiles;  // slot pair
+  const int sp = lin % a.ntiles;  // slot group
   const size_t bh = lin / a.ntiles;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31;
-  const int slot = 2 * sp + (wave >> 1), kh = wave & 1;
+  const int slot = kKvSlots * sp + (wave >> 1), kh = wave & 1;
   const bool has_slot = slot < g.S;
   const int n = has_slot ? min(a.plen[bh * g.S + slot], g.C) : 0;
   const int nk = min(max(n - 32 * kh, 0), 32);  // valid keys of this wave's tile
@@ -707,7 +711,7 @@ hipError_t launch_d(const BwdArgs& base, hipStream_t s) {
   dq_local_kernel<D><<<((total + 7) / 8) * 8, kDqlThreads, shm_dql, s>>>(a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (g.S > 0) {
-    a.ntiles = (g.S + 1) / 2;
+    a.ntiles = (g.S + kKvSlots - 1) / kKvSlots;
     total = g.B * g.H * a.ntiles;
     dkv_pers_kernel<D, true><<<((total + 7) / 8) * 8, kKvThreads, shm_kv, s>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
