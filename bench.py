@@ -37,6 +37,10 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-accounting", action="store_true", help="skip the exact per-step FLOP replay")
     ap.add_argument("--cpu-heads", type=int, default=12, help="heads in the CPU oracle sample")
+    ap.add_argument("--rollout-steps", type=int, default=80,
+                    help="chunks of the graph-replayed rollout (0 skips it)")
+    ap.add_argument("--denoise-passes", type=int, default=4,
+                    help="denoising passes per chunk in the full-schedule timing (not given by the pages)")
     return ap.parse_args()
 
 
@@ -58,7 +62,7 @@ class Bench:
                                  torch.from_numpy(np.ascontiguousarray(a))).cuda()
         self.pristine = dict(k_p=dev(x["k_p"], dt), v_p=dev(x["v_p"], dt), plen=dev(x["persist_len"]),
                              psrc=dev(x["persist_src"]), ring_head=dev(x["ring_head"]), k_l=dev(x["k_l"], dt),
-                             v_l=dev(x["v_l"], dt))
+                             v_l=dev(x["v_l"], dt), step=torch.zeros(1, dtype=torch.int32, device="cuda"))
         self.live = {k: v.clone() for k, v in self.pristine.items()}
         self.pkbar0 = torch.empty(s["persist_kbar"], dtype=torch.float32, device="cuda")
         pb.pbsa_pool_slots(p, self.pristine["k_p"], self.pristine["plen"], self.pkbar0)
@@ -117,7 +121,7 @@ class Bench:
         if record is not None:
             record.append(self.account())
             plen_before = L["plen"].cpu().numpy()
-        pb.pbsa_persist_update(p, self.mass, L["k_l"], L["v_l"], self.kbar_l, L["ring_head"], self.step_id,
+        pb.pbsa_persist_update(p, self.mass, L["k_l"], L["v_l"], self.kbar_l, L["ring_head"], L["step"],
                                L["k_p"], L["v_p"], L["plen"], L["psrc"], self.pkbar, self.n_rep, self.ws_u)
         mark(5)
         if record is not None:
@@ -197,6 +201,71 @@ def run_gpu(args, cfg):
         torch.cuda.synchronize()
         acc = rec
     return b, total_ms, wall, per_op, acc
+
+
+def run_rollout(cfg, steps: int, denoise: int):
+    """Long rollout: chunk s's q/k/v (seeded, drifting planted blocks) are staged
+    into the loop's buffers (device-to-device) and one captured graph runs the
+    cache pass (ring append, score/select, fwd, persistent update).  Also times
+    the per-chunk schedule with `denoise` denoising passes before the cache pass."""
+    import torch
+    import block_sparse_attention_15_amd as pb
+    from block_sparse_attention_15_amd.rollout import DecodeLoop
+    import synth
+    rcfg = synth.workload("rollout_c4", steps=steps)
+    stream = synth.RolloutStream(rcfg)
+    x = synth.make_step_inputs(rcfg)
+    p = pb.pbsa_plan(rcfg)
+    dt = p.torch_dtype
+    dev = lambda a: torch.from_numpy(a).to(dt).cuda()
+    chunks = [stream.chunk(s) for s in range(-1, steps)]
+    dq = torch.stack([dev(c["q"]) for c in chunks[1:]])
+    dk = torch.stack([dev(c["k"]) for c in chunks[1:]])
+    dv = torch.stack([dev(c["v"]) for c in chunks[1:]])
+
+    def fresh():
+        cache = pb.PBSACache(p)
+        cache.k_pers.copy_(dev(x["k_p"]))
+        cache.v_pers.copy_(dev(x["v_p"]))
+        cache.persist_len.copy_(torch.from_numpy(x["persist_len"]).cuda())
+        cache.persist_src.copy_(torch.from_numpy(x["persist_src"]).cuda())
+        ct = p.chunk_tokens
+        cache.k_local[:, :, :ct].copy_(dev(chunks[0]["k"]))
+        cache.v_local[:, :, :ct].copy_(dev(chunks[0]["v"]))
+        cache.refresh_pooled_keys()
+        return cache, DecodeLoop(p, cache)
+
+    out = {"steps": steps, "denoise_passes": denoise}
+    for mode in ("eager", "graph", "schedule"):
+        cache, loop = fresh()
+        nd = denoise if mode == "schedule" else 0
+        loop.load_chunk(dq[0], dk[0], dv[0])
+        if mode != "eager":
+            _, warm = fresh()
+            warm.load_chunk(dq[0], dk[0], dv[0])
+            warm.step(nd)
+            torch.cuda.synchronize()
+            loop.capture(nd)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for s in range(steps):
+            loop.load_chunk(dq[s], dk[s], dv[s])
+            if mode == "eager":
+                loop.step(0)
+            else:
+                loop.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        if mode == "eager":
+            out["eager_ms_per_step"] = round(ms, 4)
+        elif mode == "graph":
+            out["graph_ms_per_step"] = round(ms, 4)
+            out["final_valid_persistent_tokens_per_head"] = float(cache.persist_len.sum(-1).float().mean())
+        else:
+            out["schedule_ms_per_chunk"] = round(ms, 4)
+    return out
 
 
 def cpu_baseline(cfg, heads: int):
@@ -281,6 +350,8 @@ def main():
                    "parallelism": "single GPU"},
         "kernels": kern, "roofline": roof, "wall_s": round(wall, 3), **extra,
     })
+    if args.rollout_steps > 0:
+        out["rollout"] = run_rollout(cfg, args.rollout_steps, args.denoise_passes)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_heads)
     print(json.dumps(out))

@@ -53,8 +53,7 @@ SIGNATURES = {
     "pbsa_score_select": [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "pbsa_fwd": [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "pbsa_bwd": [_CFG] + [_P] * 15 + [_P, ctypes.c_size_t, _P],
-    "pbsa_persist_update": [_CFG, _P, _P, _P, _P, _P, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P,
-                            ctypes.c_size_t, _P],
+    "pbsa_persist_update": [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "pbsa_ring_append": [_CFG, _P, _P, _P, _P, _P, _P],
 }
 

@@ -183,15 +183,18 @@ def pbsa_bwd(p: Plan, q, k_pers, v_pers, persist_len, k_local, v_local, topk_idx
           w, nb, _stream(stream))
 
 
-def pbsa_persist_update(p: Plan, mass, k_local, v_local, kbar_local, ring_head, step_id: int, k_pers, v_pers,
+def pbsa_persist_update(p: Plan, mass, k_local, v_local, kbar_local, ring_head, step_counter, k_pers, v_pers,
                         persist_len, persist_src, persist_kbar, n_replaced, ws, stream=None):
+    """``ring_head`` and ``step_counter`` are int32 device tensors of shape (1,),
+    both advanced by the call (the step id tags the admitted blocks' src)."""
     s = shapes(p)
     dt = p.torch_dtype
     w, nb = _ws(ws, p.ws_persist_update)
     _call("pbsa_persist_update", ctypes.byref(p.cfg), _ptr(mass, s["mass"], torch.float32, "mass"),
           _ptr(k_local, s["k_local"], dt, "k_local"), _ptr(v_local, s["k_local"], dt, "v_local"),
           _ptr(kbar_local, s["kbar_local"], torch.float32, "kbar_local"),
-          _ptr(ring_head, s["ring_head"], torch.int32, "ring_head"), ctypes.c_int32(step_id),
+          _ptr(ring_head, s["ring_head"], torch.int32, "ring_head"),
+          _ptr(step_counter, s["ring_head"], torch.int32, "step_counter"),
           _ptr(k_pers, s["k_pers"], dt, "k_pers"), _ptr(v_pers, s["k_pers"], dt, "v_pers"),
           _ptr(persist_len, s["persist_len"], torch.int32, "persist_len"),
           _ptr(persist_src, s["persist_len"], torch.int32, "persist_src"),

@@ -278,7 +278,7 @@ pbsa_status pbsa_bwd(const pbsa_config* cfg, const void* q, const void* k_pers, 
 
 pbsa_status pbsa_persist_update(const pbsa_config* cfg, const float* mass, const void* k_local,
                                 const void* v_local, const float* kbar_local, int32_t* ring_head,
-                                int32_t step_id, void* k_pers, void* v_pers, int32_t* persist_len,
+                                int32_t* step_counter, void* k_pers, void* v_pers, int32_t* persist_len,
                                 int32_t* persist_src, float* persist_kbar, int32_t* n_replaced,
                                 void* ws, size_t ws_bytes, void* stream) {
   Plan p;
@@ -290,8 +290,7 @@ pbsa_status pbsa_persist_update(const pbsa_config* cfg, const float* mass, const
   REQUIRE_ALIGNED(kbar_local);
   REQUIRE_PTR(ring_head);
   REQUIRE_PTR(n_replaced);
-  if (step_id < 0 || (int64_t)step_id * p.g.nq + p.g.nq > INT32_MAX)
-    return fail(PBSA_ERR_INVALID_ARG, "step_id %d out of range", step_id);
+  REQUIRE_PTR(step_counter);
   if (p.g.S > 0) {
     REQUIRE_ALIGNED(k_pers);
     REQUIRE_ALIGNED(v_pers);
@@ -300,7 +299,7 @@ pbsa_status pbsa_persist_update(const pbsa_config* cfg, const float* mass, const
     REQUIRE_ALIGNED(persist_kbar);
   }
   if ((st = check_ws(ws, ws_bytes, p.info.ws_persist_update)) != PBSA_OK) return st;
-  return hip_status(launch_persist_update(p.g, mass, k_local, v_local, kbar_local, ring_head, step_id, k_pers,
+  return hip_status(launch_persist_update(p.g, mass, k_local, v_local, kbar_local, ring_head, step_counter, k_pers,
                                           v_pers, persist_len, persist_src, persist_kbar, n_replaced,
                                           (int32_t*)ws, (hipStream_t)stream),
                     "pbsa_persist_update");

@@ -122,7 +122,7 @@ hipError_t launch_bwd(const Geo& g, const void* q, const void* k_p, const void* 
                       const float* lse, const void* dout, float* dq, float* dk_p, float* dv_p,
                       float* dk_l, float* dv_l, WsBwd ws, hipStream_t s);
 hipError_t launch_persist_update(const Geo& g, const float* mass, const void* k_l, const void* v_l,
-                                 const float* kbar_l, int32_t* ring_head, int32_t step_id, void* k_p,
+                                 const float* kbar_l, int32_t* ring_head, int32_t* step_counter, void* k_p,
                                  void* v_p, int32_t* plen, int32_t* psrc, float* pkbar, int32_t* n_rep,
                                  int32_t* plan, hipStream_t s);
 hipError_t launch_ring_append(const Geo& g, const void* k_new, const void* v_new, const int32_t* ring_head,

@@ -27,7 +27,8 @@ constexpr int kThreads = 256;
 // entrants by ballot prefix counts.
 __global__ __launch_bounds__(kThreads) void update_decide_kernel(Geo g, const float* __restrict__ mass,
                                                                  const int32_t* __restrict__ ring_head,
-                                                                 int32_t step_id, int32_t* __restrict__ plen,
+                                                                 const int32_t* __restrict__ step_counter,
+                                                                 int32_t* __restrict__ plen,
                                                                  int32_t* __restrict__ psrc,
                                                                  int32_t* __restrict__ n_rep,
                                                                  int32_t* __restrict__ plan) {
@@ -39,6 +40,7 @@ __global__ __launch_bounds__(kThreads) void update_decide_kernel(Geo g, const fl
   const int h = blockIdx.x, b = blockIdx.y;
   const size_t bh = (size_t)b * g.H + h;
   const int old = *ring_head;
+  const int step_id = *step_counter;
   const float* mrow = mass + bh * (g.S + g.nl);
   for (int c = threadIdx.x; c < NC; c += kThreads) {
     const bool valid = c >= g.S || plen[bh * g.S + c] > 0;
@@ -99,17 +101,21 @@ __global__ __launch_bounds__(kThreads) void update_decide_kernel(Geo g, const fl
 }
 
 // grid (S, H, B): move rows and pooled keys according to the plan; block
-// (0,0,0) advances the ring head.
+// (0,0,0) advances the ring head and the step counter.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void update_copy_kernel(Geo g, const int32_t* __restrict__ plan,
                                                                const T* __restrict__ kl, const T* __restrict__ vl,
                                                                const float* __restrict__ kbar_l,
                                                                T* __restrict__ kp, T* __restrict__ vp,
                                                                float* __restrict__ pkbar,
-                                                               int32_t* __restrict__ ring_head) {
+                                                               int32_t* __restrict__ ring_head,
+                                                               int32_t* __restrict__ step_counter) {
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const size_t bh = (size_t)b * g.H + h;
-  if (s == 0 && h == 0 && b == 0 && threadIdx.x == 0) *ring_head = (*ring_head + 1) % g.R;
+  if (s == 0 && h == 0 && b == 0 && threadIdx.x == 0) {
+    *ring_head = (*ring_head + 1) % g.R;
+    *step_counter += 1;
+  }
   const int p = plan[bh * g.S + s];
   if (p == -2) return;
   constexpr int kVec = 16 / sizeof(T);           // elements per 16-byte chunk
@@ -137,7 +143,10 @@ __global__ __launch_bounds__(kThreads) void update_copy_kernel(Geo g, const int3
   }
 }
 
-__global__ void ring_advance_kernel(int32_t* ring_head, int R) { *ring_head = (*ring_head + 1) % R; }
+__global__ void ring_advance_kernel(int32_t* ring_head, int32_t* step_counter, int R) {
+  *ring_head = (*ring_head + 1) % R;
+  *step_counter += 1;
+}
 
 // grid-stride copy of a [B,H,Nq,D] chunk into the newest ring slot.
 template <typename T>
@@ -160,25 +169,28 @@ __global__ __launch_bounds__(kThreads) void ring_append_kernel(Geo g, const T* _
 }  // namespace
 
 hipError_t launch_persist_update(const Geo& g, const float* mass, const void* k_l, const void* v_l,
-                                 const float* kbar_l, int32_t* ring_head, int32_t step_id, void* k_p,
+                                 const float* kbar_l, int32_t* ring_head, int32_t* step_counter, void* k_p,
                                  void* v_p, int32_t* plen, int32_t* psrc, float* pkbar, int32_t* n_rep,
                                  int32_t* plan, hipStream_t s) {
   const int NC = g.S + g.nq;
   const size_t shm = (size_t)NC * 8 + (size_t)NC * 4 + (size_t)g.nq * 4;
-  update_decide_kernel<<<dim3(g.H, g.B), kThreads, shm, s>>>(g, mass, ring_head, step_id, plen, psrc, n_rep, plan);
+  update_decide_kernel<<<dim3(g.H, g.B), kThreads, shm, s>>>(g, mass, ring_head, step_counter, plen, psrc, n_rep,
+                                                              plan);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (g.S == 0) {
-    ring_advance_kernel<<<1, 1, 0, s>>>(ring_head, g.R);
+    ring_advance_kernel<<<1, 1, 0, s>>>(ring_head, step_counter, g.R);
     return hipGetLastError();
   }
   dim3 grid(g.S, g.H, g.B);
   if (g.dtype == PBSA_BF16)
     update_copy_kernel<bf16_t><<<grid, kThreads, 0, s>>>(g, plan, (const bf16_t*)k_l, (const bf16_t*)v_l, kbar_l,
-                                                        (bf16_t*)k_p, (bf16_t*)v_p, pkbar, ring_head);
+                                                        (bf16_t*)k_p, (bf16_t*)v_p, pkbar, ring_head,
+                                                        step_counter);
   else
     update_copy_kernel<float><<<grid, kThreads, 0, s>>>(g, plan, (const float*)k_l, (const float*)v_l, kbar_l,
-                                                       (float*)k_p, (float*)v_p, pkbar, ring_head);
+                                                       (float*)k_p, (float*)v_p, pkbar, ring_head,
+                                                       step_counter);
   return hipGetLastError();
 }
 

@@ -30,7 +30,7 @@ class PBSACache:
         self.k_local = torch.zeros(s["k_local"], dtype=dt, device=device)
         self.v_local = torch.zeros(s["k_local"], dtype=dt, device=device)
         self.ring_head = torch.zeros(1, dtype=torch.int32, device=device)
-        self.step = 0
+        self.step_counter = torch.zeros(1, dtype=torch.int32, device=device)
 
     def refresh_pooled_keys(self, stream=None):
         api.pbsa_pool_slots(self.plan, self.k_pers, self.persist_len, self.persist_kbar, stream)
@@ -87,7 +87,7 @@ class SparseForcingAttention:
                                              device=query.device).expand(shp["persist_len"]).contiguous()
             cache.persist_kbar = torch.empty(shp["persist_kbar"], dtype=torch.float32, device=query.device)
             cache.ring_head = torch.zeros(1, dtype=torch.int32, device=query.device)
-            cache.step = 0
+            cache.step_counter = torch.zeros(1, dtype=torch.int32, device=query.device)
             cache.refresh_pooled_keys(stream)
         o = torch.empty_like(query)
         lse = torch.empty(api.shapes(p)["lse"], dtype=torch.float32, device=query.device)
@@ -97,8 +97,7 @@ class SparseForcingAttention:
                      self.topk_idx, o, lse, self.ws_fwd, stream)
         if update:
             api.pbsa_persist_update(p, self.mass, cache.k_local, cache.v_local, self.kbar_local, cache.ring_head,
-                                    cache.step, cache.k_pers, cache.v_pers, cache.persist_len, cache.persist_src,
-                                    cache.persist_kbar, self.n_replaced, self.ws_update, stream)
-            cache.step += 1
+                                    cache.step_counter, cache.k_pers, cache.v_pers, cache.persist_len,
+                                    cache.persist_src, cache.persist_kbar, self.n_replaced, self.ws_update, stream)
         self.last_lse = lse
         return o

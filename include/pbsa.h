@@ -170,15 +170,18 @@ pbsa_status pbsa_bwd(const pbsa_config* cfg, const void* q, const void* k_pers, 
  * oldest local chunk (physical slot *ring_head).  The S candidates of largest
  * mass are kept (ties: incumbents first, then lower slot / block index).
  * Vacated slots, ascending, receive the admitted blocks, ascending: their rows
- * are copied (zero padding), len = block size, src = step_id*NQ_blocks + e,
- * kbar = kbar_local of the block.  Vacated slots left over are emptied (len 0,
- * rows 0, src INT32_MIN, kbar 0).  n_replaced[b,h] receives the admitted
- * count.  Finally *ring_head advances to (ring_head+1) mod R, so the evicted
- * chunk slot becomes the newest and is free for the next chunk.  ws of at
- * least plan.ws_persist_update bytes. */
+ * are copied (zero padding), len = block size, src = step*NQ_blocks + e where
+ * step = *step_counter, kbar = kbar_local of the block.  Vacated slots left
+ * over are emptied (len 0, rows 0, src INT32_MIN, kbar 0).  n_replaced[b,h]
+ * receives the admitted count.  Finally *ring_head advances to
+ * (ring_head+1) mod R, so the evicted chunk slot becomes the newest and is
+ * free for the next chunk, and *step_counter advances by one.  Both are
+ * device int32 values, so one captured graph serves every step of a rollout
+ * (src ids are int32: step*NQ_blocks must stay below 2^31).  ws of at least
+ * plan.ws_persist_update bytes. */
 pbsa_status pbsa_persist_update(const pbsa_config* cfg, const float* mass, const void* k_local,
                                 const void* v_local, const float* kbar_local, int32_t* ring_head,
-                                int32_t step_id, void* k_pers, void* v_pers, int32_t* persist_len,
+                                int32_t* step_counter, void* k_pers, void* v_pers, int32_t* persist_len,
                                 int32_t* persist_src, float* persist_kbar, int32_t* n_replaced,
                                 void* ws, size_t ws_bytes, void* stream);
 

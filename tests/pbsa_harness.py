@@ -39,6 +39,7 @@ class GpuStep:
         self.plen = dev(x["persist_len"])
         self.psrc = dev(x["persist_src"])
         self.ring_head = dev(x["ring_head"])
+        self.step_counter = torch.zeros(1, dtype=torch.int32, device="cuda")
         self.pkbar = torch.empty(s["persist_kbar"], dtype=torch.float32, device="cuda")
         self.topk = torch.full(s["topk_idx"], -7, dtype=torch.int32, device="cuda")
         self.mass = torch.full(s["mass"], float("nan"), dtype=torch.float32, device="cuda")
@@ -72,9 +73,10 @@ class GpuStep:
         return g
 
     def update(self, step_id: int, mass=None):
+        self.step_counter.fill_(step_id)
         pb.pbsa_persist_update(self.p, self.mass if mass is None else mass, self.k_l, self.v_l, self.kbar_l,
-                               self.ring_head, step_id, self.k_p, self.v_p, self.plen, self.psrc, self.pkbar,
-                               self.n_rep, self.ws_update)
+                               self.ring_head, self.step_counter, self.k_p, self.v_p, self.plen, self.psrc,
+                               self.pkbar, self.n_rep, self.ws_update)
 
     def state(self) -> dict:
         return dict(k_p=host(self.k_p), v_p=host(self.v_p), persist_len=host(self.plen),

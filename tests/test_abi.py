@@ -96,6 +96,6 @@ def test_pointer_checks_before_launch():
                                ctypes.c_void_p(0x10000), p.ws_score_select - 1, None)
     assert st == _lib.PBSA_ERR_WORKSPACE
     st = lib.pbsa_persist_update(ctypes.byref(c), *(ctypes.c_void_p(0x1000 * (i + 1)) for i in range(5)),
-                                 ctypes.c_int32(-1), *(ctypes.c_void_p(0x1000 * (i + 1)) for i in range(6)),
+                                 None, *(ctypes.c_void_p(0x1000 * (i + 1)) for i in range(6)),
                                  ctypes.c_void_p(0x10000), p.ws_persist_update, None)
-    assert st == _lib.PBSA_ERR_INVALID_ARG
+    assert st == _lib.PBSA_ERR_INVALID_ARG   # NULL step counter
