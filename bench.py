@@ -344,8 +344,10 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg["dtype"],
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: B{cfg['batch']} H{cfg['heads']} d{cfg['head_dim']} "
-                               f"grid {cfg['frame_h']}x{cfg['frame_w']} [1,8,8] blocks, 4680 queries, "
-                               f"9360 local + 9360 persistent tokens, top-k ratio {cfg['topk_ratio']}",
+                               f"grid {cfg['frame_h']}x{cfg['frame_w']} "
+                               f"[{cfg['block_t']},{cfg['block_h']},{cfg['block_w']}] blocks, "
+                               f"{p.chunk_tokens} queries, {cfg['local_cache_size']} local + "
+                               f"{cfg['persistent_cache_size']} persistent tokens, top-k ratio {cfg['topk_ratio']}",
                    "step": "ring_append + score_select + fwd + bwd + persist_update",
                    "parallelism": "single GPU"},
         "kernels": kern, "roofline": roof, "wall_s": round(wall, 3), **extra,

@@ -75,6 +75,9 @@ WORKLOADS["update_c2"] = dict(WORKLOADS["decode_c1"])
 WORKLOADS["backward_c3"] = dict(WORKLOADS["decode_c1"], dout_seed=3)
 WORKLOADS["rollout_c4"] = dict(WORKLOADS["decode_c1"], seed=4, steps=80,
                                plant_blocks=8, drift_p=0.25, redraw_every=20)
+# the decode step with [3,4,4] blocks (the project page's faster block size):
+# 104 blocks of 48/24 tokens per 3-frame chunk, 208 local blocks, 208 slots, k = 26
+WORKLOADS["decode_344"] = dict(WORKLOADS["decode_c1"], block_t=3, block_h=4, block_w=4, seed=6)
 
 
 def workload(name: str, **overrides) -> dict:

@@ -74,6 +74,24 @@ def test_geometry_closed_forms():
     assert sorted(toks.tolist()) == list(range(1560))
 
 
+def test_geometry_block_344():
+    # [3,4,4] blocks (the project page's faster configuration) on the 30x52
+    # grid: 8 block rows (7 of 4 rows + 1 of 2) x 13 block columns per
+    # 3-frame group = 104 blocks of 48 (91) and 24 (13) tokens.
+    g = oracle.geometry(synth.workload("decode_c1", block_t=3, block_h=4, block_w=4))
+    assert (g.n_qblk, g.n_lblk, g.S, g.cap, g.topk) == (104, 208, 208, 48, 26)
+    hist = {}
+    for n in g.block_len:
+        hist[int(n)] = hist.get(int(n), 0) + 1
+    assert hist == {48: 91, 24: 13}
+    assert int(g.block_len.sum()) == g.chunk_tokens == 4680
+    toks = np.concatenate(g.block_tok)
+    assert sorted(toks.tolist()) == list(range(4680))
+    # a block spans the three frames of the chunk at the same 4x4 window
+    t0 = g.block_tok[0]
+    assert sorted(set((t0 // 1560).tolist())) == [0, 1, 2]
+
+
 def test_geometry_tiny_config():
     g = oracle.geometry(synth.workload("tiny_fp32"))
     assert (g.n_qblk, g.R, g.n_lblk, g.S, g.topk, g.cap) == (4, 4, 16, 8, 4, 64)
