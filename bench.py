@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--cpu-heads", type=int, default=12, help="heads in the CPU oracle sample")
     ap.add_argument("--rollout-steps", type=int, default=80,
                     help="chunks of the graph-replayed rollout (0 skips it)")
+    ap.add_argument("--cold-steps", type=int, default=5,
+                    help="extra steps with a cache-evicting fill before every op (0 skips them)")
     ap.add_argument("--denoise-passes", type=int, default=4,
                     help="denoising passes per chunk in the full-schedule timing (not given by the pages)")
     return ap.parse_args()
@@ -97,33 +99,36 @@ class Bench:
         self.pkbar.copy_(self.pkbar0)
         self.step_id = 0
 
-    def step(self, ev=None, record=None):
+    def step(self, ev=None, record=None, flush=None):
+        """One step.  ``ev``: per-op (start, end) event pairs to record;
+        ``flush``: callable run before each op (outside its events) to evict
+        the caches for cold-HBM timing."""
         pb, L, p = self.pb, self.live, self.p
 
-        def mark(i):
+        def op(i, fn):
+            if flush is not None:
+                flush()
             if ev is not None:
-                ev[i].record()
+                ev[i][0].record()
+            fn()
+            if ev is not None:
+                ev[i][1].record()
 
         # ring append writes into the slot the previous update freed (the
         # first step overwrites the current chunk with itself)
-        mark(0)
-        pb.pbsa_ring_append(p, self.k_new, self.v_new, L["ring_head"], L["k_l"], L["v_l"])
-        mark(1)
-        pb.pbsa_score_select(p, self.q, L["k_l"], L["ring_head"], self.pkbar, L["plen"], self.topk, self.mass,
-                             self.kbar_l, self.ws_s)
-        mark(2)
-        pb.pbsa_fwd(p, self.q, L["k_p"], L["v_p"], L["plen"], L["k_l"], L["v_l"], self.topk, self.o, self.lse,
-                    self.ws_f)
-        mark(3)
-        pb.pbsa_bwd(p, self.q, L["k_p"], L["v_p"], L["plen"], L["k_l"], L["v_l"], self.topk, self.o, self.lse,
-                    self.dout, self.dq, self.dk_p, self.dv_p, self.dk_l, self.dv_l, self.ws_b)
-        mark(4)
+        op(0, lambda: pb.pbsa_ring_append(p, self.k_new, self.v_new, L["ring_head"], L["k_l"], L["v_l"]))
+        op(1, lambda: pb.pbsa_score_select(p, self.q, L["k_l"], L["ring_head"], self.pkbar, L["plen"], self.topk,
+                                           self.mass, self.kbar_l, self.ws_s))
+        op(2, lambda: pb.pbsa_fwd(p, self.q, L["k_p"], L["v_p"], L["plen"], L["k_l"], L["v_l"], self.topk, self.o,
+                                  self.lse, self.ws_f))
+        op(3, lambda: pb.pbsa_bwd(p, self.q, L["k_p"], L["v_p"], L["plen"], L["k_l"], L["v_l"], self.topk, self.o,
+                                  self.lse, self.dout, self.dq, self.dk_p, self.dv_p, self.dk_l, self.dv_l, self.ws_b))
         if record is not None:
             record.append(self.account())
             plen_before = L["plen"].cpu().numpy()
-        pb.pbsa_persist_update(p, self.mass, L["k_l"], L["v_l"], self.kbar_l, L["ring_head"], L["step"],
-                               L["k_p"], L["v_p"], L["plen"], L["psrc"], self.pkbar, self.n_rep, self.ws_u)
-        mark(5)
+        op(4, lambda: pb.pbsa_persist_update(p, self.mass, L["k_l"], L["v_l"], self.kbar_l, L["ring_head"], L["step"],
+                                             L["k_p"], L["v_p"], L["plen"], L["psrc"], self.pkbar, self.n_rep,
+                                             self.ws_u))
         if record is not None:
             record[-1]["update_bytes"] = self.update_bytes(plen_before)
         self.step_id += 1
@@ -168,15 +173,29 @@ class Bench:
         return float(2 * row * (lens.sum() + p.slot_rows * (ent.sum() + emptied.sum())))
 
 
+def _events(n):
+    import torch
+    return [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(len(Bench.OPS))] for _ in range(n)]
+
+
+def _op_stats(evs):
+    """Per-op mean, median and p99 (ms) over the recorded steps."""
+    out = {}
+    for i, op in enumerate(Bench.OPS):
+        t = np.array([e[i][0].elapsed_time(e[i][1]) for e in evs])
+        out[op] = dict(mean=float(t.mean()), p50=float(np.median(t)), p99=float(np.percentile(t, 99)))
+    return out
+
+
 def run_gpu(args, cfg):
     import torch
     b = Bench(cfg)
     b._bl = b.block_lens().astype(np.int64)
-    nev = 6
     torch.cuda.synchronize()
     for _ in range(args.warmup):
         b.step()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+    evs = _events(args.steps)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -187,8 +206,17 @@ def run_gpu(args, cfg):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     total_ms = start.elapsed_time(end)
-    per_op = {op: float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps)]))
-              for i, op in enumerate(Bench.OPS)}
+    per_op = _op_stats(evs)
+    # cold-cache pass: a 1 GiB fill before every op evicts L2 and the MALL
+    cold = None
+    if args.cold_steps > 0:
+        junk = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        cevs = _events(args.cold_steps)
+        for k in range(args.cold_steps):
+            b.step(cevs[k], flush=lambda: junk.fill_(k & 0xFF))
+        torch.cuda.synchronize()
+        cold = _op_stats(cevs)
+        del junk
     # exact accounting by deterministic replay
     acc = None
     if not args.no_accounting:
@@ -200,7 +228,25 @@ def run_gpu(args, cfg):
             b.step(record=rec)
         torch.cuda.synchronize()
         acc = rec
-    return b, total_ms, wall, per_op, acc
+    return b, total_ms, wall, per_op, cold, acc
+
+
+def traffic_record(workload: str):
+    """HBM bytes per launch of each op, from the committed FETCH_SIZE /
+    WRITE_SIZE summary of this workload.  Returns {} when there is none or
+    when the kernel sources changed since the counters were taken."""
+    from block_sparse_attention_15_amd.build import source_digest
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return {}
+    digest, out = None, {}
+    for line in open(path):
+        f = line.split()
+        if len(f) >= 2 and f[0] == "source_digest:":
+            digest = f[1]
+        elif len(f) >= 3 and f[0] == "traffic":
+            out[f[1]] = float(f[2])
+    return out if digest == source_digest() else {}
 
 
 def run_rollout(cfg, steps: int, denoise: int):
@@ -308,11 +354,14 @@ def main():
         sys.exit(2)
     import synth
     cfg = synth.workload(args.workload)
-    b, total_ms, wall, per_op, acc = run_gpu(args, cfg)
+    b, total_ms, wall, stats, cold, acc = run_gpu(args, cfg)
     p = b.p
     ms_step = total_ms / args.steps
     out = {"metric": "PBSA decode-step ms + effective TFLOP/s (fraction of bf16 MFMA peak)"}
-    kern = {op: {"ms": round(v, 4)} for op, v in per_op.items()}
+    per_op = {op: v["mean"] for op, v in stats.items()}
+    kern = {op: {"ms": round(v["mean"], 4), "p50_ms": round(v["p50"], 4), "p99_ms": round(v["p99"], 4)}
+            for op, v in stats.items()}
+    kern_cold = {}
     if acc:
         pairs = float(np.mean([a["pairs"] for a in acc]))
         fwd_flops = 4 * p.D * pairs
@@ -328,19 +377,31 @@ def main():
         kern["update"].update(gbs=round(ub / (per_op["update"] * 1e-3) / 1e9, 1), mb=round(ub / 1e6, 2))
         app = 2 * 2 * B * H * p.chunk_tokens * D * esz
         kern["append"].update(gbs=round(app / (per_op["append"] * 1e-3) / 1e9, 1), mb=round(app / 1e6, 2))
+        if cold:
+            hbm = dict(append=app, score_select=score_bytes, update=ub)
+            for op in Bench.OPS:
+                c = {"ms": round(cold[op]["mean"], 4), "p50_ms": round(cold[op]["p50"], 4)}
+                if op in hbm:
+                    c["gbs"] = round(hbm[op] / (cold[op]["mean"] * 1e-3) / 1e9, 1)
+                    c["frac_hbm"] = round(c["gbs"] / MI355X_HBM_GBS, 4)
+                kern_cold[op] = c
         dom = max(("fwd", "bwd"), key=lambda k: per_op[k])
         achieved = kern[dom]["tflops"]
+        traffic = traffic_record(args.workload).get(f"pbsa_{dom}")
         roof = {"kernel": f"pbsa_{dom}", "bound": "mfma", "achieved": achieved, "peak": MI355X_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / MI355X_BF16_TFLOPS, 4), "traffic": None}
+                "unit": "TFLOP/s", "frac": round(achieved / MI355X_BF16_TFLOPS, 4),
+                "traffic": round(traffic) if traffic else None}
         value = step_tflops
         extra = dict(pairs_per_step=pairs, mean_valid_persistent_tokens=float(np.mean([a["pers_tokens"] for a in acc])),
                      mean_selected_local_tokens=float(np.mean([a["local_tokens"] for a in acc])))
     else:
         value, roof, extra = None, None, {}
     decode_ms = per_op["append"] + per_op["score_select"] + per_op["fwd"] + per_op["update"]
+    decode_p50 = sum(stats[op]["p50"] for op in ("append", "score_select", "fwd", "update"))
     out.update({
         "value": round(value, 3) if value else None, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "decode_step_ms": round(decode_ms, 4),
+        "decode_step_p50_ms": round(decode_p50, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg["dtype"],
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: B{cfg['batch']} H{cfg['heads']} d{cfg['head_dim']} "
@@ -350,7 +411,7 @@ def main():
                                f"{cfg['persistent_cache_size']} persistent tokens, top-k ratio {cfg['topk_ratio']}",
                    "step": "ring_append + score_select + fwd + bwd + persist_update",
                    "parallelism": "single GPU"},
-        "kernels": kern, "roofline": roof, "wall_s": round(wall, 3), **extra,
+        "kernels": kern, "kernels_cold": kern_cold or None, "roofline": roof, "wall_s": round(wall, 3), **extra,
     })
     if args.rollout_steps > 0:
         out["rollout"] = run_rollout(cfg, args.rollout_steps, args.denoise_passes)

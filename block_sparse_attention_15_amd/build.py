@@ -8,6 +8,7 @@ header changed, unless force=True.
 from __future__ import annotations
 
 import glob
+import hashlib
 import os
 import subprocess
 import sys
@@ -46,6 +47,19 @@ def _compile(src: str, force: bool) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
     return obj
+
+
+def source_digest() -> str:
+    """SHA-256 over the kernel sources, headers and code-generation flags (not
+    paths), identifying the compiled kernels that a profile was taken on."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + _headers(), key=os.path.basename)
+    for f in files:
+        h.update(os.path.basename(f).encode() + b"\0")
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    h.update(" ".join(x for x in FLAGS if x not in (INCLUDE, CSRC)).encode())
+    return h.hexdigest()[:16]
 
 
 def build(force: bool = True, verbose: bool = False) -> str:
