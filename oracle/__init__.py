@@ -17,7 +17,8 @@ and restated in each function's docstring.
 Precision: attention outputs and gradients are computed in float64.  The
 quantities that decide integers (pooled block scores for top-k selection and
 pooled masses for the update) are computed in float32, the precision in which
-the HIP kernels take the same decisions.
+the HIP kernels take the same decisions; token-exact masses are accumulated
+in float64 and rounded to float32 before the update ranks them.
 
 Parity pins: every function here is pinned by ``tests/test_oracle_*.py``
 (brute force, dense-attention reduction, invariants, closed forms, finite
@@ -37,6 +38,7 @@ from .pbsa import (  # noqa: F401
     score_select,
     attend,
     attend_bwd,
+    token_mass,
     persist_update,
     update_decisions,
     apply_update,

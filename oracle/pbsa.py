@@ -46,6 +46,9 @@ READINGS = {
     "R15": "near-tie: boundary gap < 1e-4 * (max - min) of the row's (or head's) oracle scores",
     "R16": "inputs are bf16-rounded (or fp32); attention and gradients in float64; decisions in float32",
     "R17": "gradients flow to q, k_p, v_p, k_l, v_l only; the block mask is fixed",
+    "R19": "token-exact mass (the other reading of R11, chosen by the caller): block mass = sum over the chunk's "
+           "query tokens of the probability their PBSA softmax puts on the block's rows; 0 for empty slots and for "
+           "local blocks no query block selected",
 }
 
 
@@ -278,6 +281,35 @@ def attend(q, k_p, v_p, plen, k_l, v_l, topk_idx, g: Geometry, qblocks=None):
                 O[b, h, tok] = (P @ V) / l
                 L[b, h, tok] = (m + np.log(l))[:, 0]
     return O, L
+
+
+def token_mass(q, k_p, plen, k_l, topk_idx, g: Geometry) -> np.ndarray:
+    """Token-exact attention mass per candidate block (reading R19).
+
+    For every query token t of query block i, P_t is the softmax of
+    scale * q_t . k over t's PBSA key set (valid persistent rows plus the
+    rows of block i's selected local blocks, as in ``attend``); the mass of a
+    block is the sum over all query tokens of the probability P_t puts on
+    that block's rows.  Accumulated in float64 and returned as float32 (the
+    precision in which the update ranks masses), in the layout of
+    ``pooled_mass``: slot s at index s, physical local block p at S+p.
+    """
+    out = np.zeros((g.B, g.H, g.S + g.n_lblk))
+    for b in range(g.B):
+        for h in range(g.H):
+            for i in range(g.n_qblk):
+                K, _, where = _key_rows(k_p, k_p, plen, k_l, k_l, topk_idx[b, h, i], b, h, g)
+                Q = q[b, h, g.block_tok[i]].astype(np.float64)
+                S = g.scale * (Q @ K.T)
+                P = np.exp(S - S.max(axis=1, keepdims=True))
+                P /= P.sum(axis=1, keepdims=True)
+                col = P.sum(axis=0)                       # probability received by each key row
+                r = 0
+                for kind, idx, ext in where:
+                    n = ext if kind == "p" else len(ext)
+                    out[b, h, idx if kind == "p" else g.S + idx] += col[r:r + n].sum()
+                    r += n
+    return out.astype(np.float32)
 
 
 def attend_bwd(q, k_p, v_p, plen, k_l, v_l, topk_idx, dout, g: Geometry):

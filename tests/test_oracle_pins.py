@@ -493,3 +493,75 @@ def test_near_tie_band():
     assert nt and band == pytest.approx(3e-4)
     nt, _, _ = oracle.near_tie_rows(s, 2)
     assert not nt
+
+
+# ---------------------------------------------------------------------------
+# Token-exact masses (reading R19)
+# ---------------------------------------------------------------------------
+
+
+def _sel_for(cfg, x, ring_head=0):
+    g = oracle.geometry(cfg)
+    sel = oracle.score_select(x["q"], x["k_l"], ring_head, oracle.pool_slots(x["k_p"], x["persist_len"]),
+                              x["persist_len"], g)
+    return g, sel
+
+
+@pytest.mark.parametrize("ring_head", [0, 1])
+def test_token_mass_totals_and_zeros(ring_head):
+    cfg = tiny_cfg()
+    x = synth.make_step_inputs(cfg)
+    x["persist_len"][0, 1, 0] = 0          # one empty slot
+    g, sel = _sel_for(cfg, x, ring_head)
+    m = oracle.token_mass(x["q"], x["k_p"], x["persist_len"], x["k_l"], sel["topk_idx"], g)
+    # every query token's probabilities sum to one
+    np.testing.assert_allclose(m.sum(axis=-1, dtype=np.float64), g.chunk_tokens, rtol=1e-6)
+    assert m[0, 1, 0] == 0
+    for b in range(g.B):
+        for h in range(g.H):
+            chosen = set(np.unique(sel["topk_idx"][b, h]).tolist())
+            for p in range(g.n_lblk):
+                assert (m[b, h, g.S + p] > 0) == (p in chosen), (b, h, p)
+
+
+def test_token_mass_equals_value_gradient_of_unit_upstream():
+    """With dO = 1 the value gradient of a key row is the probability mass it
+    receives (dV = P^T dO), so per-block sums of the (finite-difference
+    pinned) backward equal the token-exact masses."""
+    cfg = tiny_cfg(heads=2)
+    x = synth.make_step_inputs(cfg)
+    g, sel = _sel_for(cfg, x)
+    idx = sel["topk_idx"]
+    ones = np.ones((g.B, g.H, g.chunk_tokens, g.D))
+    gr = oracle.attend_bwd(x["q"], x["k_p"], x["v_p"], x["persist_len"], x["k_l"], x["v_l"], idx, ones, g)
+    m = oracle.token_mass(x["q"], x["k_p"], x["persist_len"], x["k_l"], idx, g)
+    ref = np.zeros_like(m, dtype=np.float64)
+    ref[..., :g.S] = gr["dv_p"][..., 3].sum(axis=-1)
+    for p in range(g.n_lblk):
+        ref[..., g.S + p] = gr["dv_l"][:, :, g.local_tokens_of(p), 3].sum(axis=-1)
+    np.testing.assert_allclose(m, ref, rtol=1e-6, atol=1e-9)
+
+
+def test_token_mass_uniform_keys_closed_form():
+    """All key rows identical -> each query spreads its mass uniformly over its
+    N_t keys: slot s gets sum_t len_s / N_t, local block p gets
+    sum over query tokens whose block selected p of len_p / N_t."""
+    cfg = tiny_cfg(plant_frac=0.0)
+    x = synth.make_step_inputs(cfg)
+    g, sel = _sel_for(cfg, x)
+    idx = sel["topk_idx"]
+    kp = np.ones_like(x["k_p"]) * 0.5
+    kl = np.ones_like(x["k_l"]) * 0.5
+    m = oracle.token_mass(x["q"], kp, x["persist_len"], kl, idx, g)
+    blen = g.block_len
+    for b in range(g.B):
+        for h in range(g.H):
+            plen = x["persist_len"][b, h].astype(np.float64)
+            exp = np.zeros(g.S + g.n_lblk)
+            for i in range(g.n_qblk):
+                n_t = plen.sum() + sum(blen[p % g.n_qblk] for p in idx[b, h, i])
+                nq = blen[i]
+                exp[:g.S] += nq * plen / n_t
+                for p in idx[b, h, i]:
+                    exp[g.S + p] += nq * blen[p % g.n_qblk] / n_t
+            np.testing.assert_allclose(m[b, h], exp, rtol=1e-6)
