@@ -13,6 +13,7 @@ from .api import (  # noqa: F401
     pbsa_pool_slots,
     pbsa_score_select,
     pbsa_fwd,
+    pbsa_fwd_mass,
     pbsa_bwd,
     pbsa_persist_update,
     pbsa_ring_append,

@@ -42,6 +42,7 @@ class PbsaPlanInfo(ctypes.Structure):
         ("chunk_tokens", ctypes.c_int32), ("max_block_tokens", ctypes.c_int32),
         ("ws_score_select", ctypes.c_size_t), ("ws_fwd", ctypes.c_size_t),
         ("ws_bwd", ctypes.c_size_t), ("ws_persist_update", ctypes.c_size_t),
+        ("ws_fwd_mass", ctypes.c_size_t),
     ]
 
 
@@ -52,6 +53,7 @@ SIGNATURES = {
     "pbsa_pool_slots": [_CFG, _P, _P, _P, _P],
     "pbsa_score_select": [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "pbsa_fwd": [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "pbsa_fwd_mass": [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "pbsa_bwd": [_CFG] + [_P] * 15 + [_P, ctypes.c_size_t, _P],
     "pbsa_persist_update": [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "pbsa_ring_append": [_CFG, _P, _P, _P, _P, _P, _P],

@@ -40,6 +40,7 @@ class Plan:
     ws_fwd: int
     ws_bwd: int
     ws_persist_update: int
+    ws_fwd_mass: int
 
     @property
     def B(self):
@@ -165,6 +166,20 @@ def pbsa_fwd(p: Plan, q, k_pers, v_pers, persist_len, k_local, v_local, topk_idx
           _ptr(k_local, s["k_local"], dt, "k_local"), _ptr(v_local, s["k_local"], dt, "v_local"),
           _ptr(topk_idx, s["topk_idx"], torch.int32, "topk_idx"), _ptr(o, s["q"], dt, "o"),
           _ptr(lse, s["lse"], torch.float32, "lse"), w, nb, _stream(stream))
+
+
+def pbsa_fwd_mass(p: Plan, q, k_pers, v_pers, persist_len, k_local, v_local, topk_idx, o, lse, mass, ws,
+                  stream=None):
+    """pbsa_fwd plus the token-exact mass of every candidate block into ``mass``."""
+    s = shapes(p)
+    dt = p.torch_dtype
+    w, nb = _ws(ws, p.ws_fwd_mass)
+    _call("pbsa_fwd_mass", ctypes.byref(p.cfg), _ptr(q, s["q"], dt, "q"), _ptr(k_pers, s["k_pers"], dt, "k_pers"),
+          _ptr(v_pers, s["k_pers"], dt, "v_pers"), _ptr(persist_len, s["persist_len"], torch.int32, "persist_len"),
+          _ptr(k_local, s["k_local"], dt, "k_local"), _ptr(v_local, s["k_local"], dt, "v_local"),
+          _ptr(topk_idx, s["topk_idx"], torch.int32, "topk_idx"), _ptr(o, s["q"], dt, "o"),
+          _ptr(lse, s["lse"], torch.float32, "lse"), _ptr(mass, s["mass"], torch.float32, "mass"), w, nb,
+          _stream(stream))
 
 
 def pbsa_bwd(p: Plan, q, k_pers, v_pers, persist_len, k_local, v_local, topk_idx, o, lse, dout,

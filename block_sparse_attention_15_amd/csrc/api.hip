@@ -123,6 +123,8 @@ pbsa_status make_plan(const pbsa_config* c, Plan* p) {
   in.ws_bwd = align256(BH * g.ct * 4) + align256(BH * g.nl * 4) + align256(BH * g.nl * g.nq * 4) +
               geo_table_bytes(g);
   in.ws_persist_update = align256(BH * g.S * 4);
+  in.ws_fwd_mass = align256(in.ws_fwd) + align256(BH * g.S * g.ct * 4) + align256(BH * g.K * g.ct * 4) +
+                   align256(BH * g.nq * g.nl * 4);
   return PBSA_OK;
 }
 
@@ -231,8 +233,45 @@ pbsa_status pbsa_fwd(const pbsa_config* cfg, const void* q, const void* k_pers, 
   }
   if ((st = check_ws(ws, ws_bytes, p.info.ws_fwd)) != PBSA_OK) return st;
   return hip_status(launch_fwd(p.g, q, k_pers, v_pers, persist_len, k_local, v_local, topk_idx, o, lse, ws,
-                               (hipStream_t)stream),
+                               nullptr, nullptr, (hipStream_t)stream),
                     "pbsa_fwd");
+}
+
+pbsa_status pbsa_fwd_mass(const pbsa_config* cfg, const void* q, const void* k_pers, const void* v_pers,
+                          const int32_t* persist_len, const void* k_local, const void* v_local,
+                          const int32_t* topk_idx, void* o, float* lse, float* mass, void* ws, size_t ws_bytes,
+                          void* stream) {
+  Plan p;
+  pbsa_status st = make_plan(cfg, &p);
+  if (st != PBSA_OK) return st;
+  REQUIRE_ALIGNED(q);
+  REQUIRE_ALIGNED(k_local);
+  REQUIRE_ALIGNED(v_local);
+  REQUIRE_PTR(topk_idx);
+  REQUIRE_ALIGNED(o);
+  REQUIRE_PTR(lse);
+  REQUIRE_PTR(mass);
+  if (p.g.S > 0) {
+    REQUIRE_ALIGNED(k_pers);
+    REQUIRE_ALIGNED(v_pers);
+    REQUIRE_PTR(persist_len);
+  }
+  if ((st = check_ws(ws, ws_bytes, p.info.ws_fwd_mass)) != PBSA_OK) return st;
+  const Geo& g = p.g;
+  const size_t BH = (size_t)g.B * g.H;
+  char* base = (char*)ws;
+  void* ws_f = p.info.ws_fwd ? base : nullptr;
+  base += align256(p.info.ws_fwd);
+  float* blse_p = (float*)base;
+  base += align256(BH * g.S * g.ct * 4);
+  float* blse_l = (float*)base;
+  base += align256(BH * g.K * g.ct * 4);
+  float* part = (float*)base;
+  hipError_t e = launch_fwd(g, q, k_pers, v_pers, persist_len, k_local, v_local, topk_idx, o, lse, ws_f, blse_p,
+                            blse_l, (hipStream_t)stream);
+  if (e == hipSuccess)
+    e = launch_token_mass(g, persist_len, topk_idx, lse, blse_p, blse_l, part, mass, (hipStream_t)stream);
+  return hip_status(e, "pbsa_fwd_mass");
 }
 
 pbsa_status pbsa_bwd(const pbsa_config* cfg, const void* q, const void* k_pers, const void* v_pers,

@@ -5,12 +5,12 @@ namespace pbsa {
 
 hipError_t launch_fwd_simple(const Geo& g, const void* q, const void* k_p, const void* v_p, const int32_t* plen,
                              const void* k_l, const void* v_l, const int32_t* topk, void* o, float* lse,
-                             hipStream_t s);
+                             float* blse_p, float* blse_l, hipStream_t s);
 bool fwd_mfma_supported(const Geo& g);
 size_t fwd_mfma_workspace(const Geo& g);
 hipError_t launch_fwd_mfma(const Geo& g, const void* q, const void* k_p, const void* v_p, const int32_t* plen,
                            const void* k_l, const void* v_l, const int32_t* topk, void* o, float* lse, void* ws,
-                           hipStream_t s);
+                           float* blse_p, float* blse_l, hipStream_t s);
 hipError_t launch_bwd_prep(const Geo& g, const void* o, const void* dout, const int32_t* topk, WsBwd ws,
                            hipStream_t s);
 hipError_t launch_bwd_simple(const Geo& g, const void* q, const void* k_p, const void* v_p, const int32_t* plen,
@@ -28,9 +28,10 @@ hipError_t launch_bwd_mfma(const Geo& g, const void* q, const void* k_p, const v
 
 hipError_t launch_fwd(const Geo& g, const void* q, const void* k_p, const void* v_p, const int32_t* plen,
                       const void* k_l, const void* v_l, const int32_t* topk, void* o, float* lse, void* ws,
-                      hipStream_t s) {
-  if (fwd_mfma_supported(g)) return launch_fwd_mfma(g, q, k_p, v_p, plen, k_l, v_l, topk, o, lse, ws, s);
-  return launch_fwd_simple(g, q, k_p, v_p, plen, k_l, v_l, topk, o, lse, s);
+                      float* blse_p, float* blse_l, hipStream_t s) {
+  if (fwd_mfma_supported(g))
+    return launch_fwd_mfma(g, q, k_p, v_p, plen, k_l, v_l, topk, o, lse, ws, blse_p, blse_l, s);
+  return launch_fwd_simple(g, q, k_p, v_p, plen, k_l, v_l, topk, o, lse, blse_p, blse_l, s);
 }
 
 hipError_t launch_bwd(const Geo& g, const void* q, const void* k_p, const void* v_p, const int32_t* plen,

@@ -36,6 +36,11 @@
 //  * Workgroup ids are remapped so that each XCD (ids i, i+8, ...) works on a
 //    contiguous range of (head, query tile): a head's persistent K/V is then
 //    read by one or two XCDs instead of all eight.
+//  * Optional (MASS): for the token-exact attention mass, each query also
+//    writes the log-sum-exp of its scores over every persistent slot and
+//    every selected local block.  The tile already forms the row sum of its
+//    probabilities (relative to the running max) for the online softmax, so
+//    this costs one lane exchange and one log per (query, block).
 #include "common.h"
 
 namespace pbsa {
@@ -82,6 +87,8 @@ struct FwdArgs {
   float* lse;
   float* o_part;    // [B,H,ct,D] persistent-part output (normalised), fp32
   float* lse_part;  // [B,H,ct]   its log-sum-exp (-inf when no slot is valid)
+  float* blse_p;    // MASS: [B,H,S,ct] log-sum-exp of each query over each slot's rows
+  float* blse_l;    // MASS: [B,H,K,ct] ... over each of its selected local blocks
   GeoTab tab;       // geometry lookup tables
   int ntiles;       // work items per (batch, head)
 };
@@ -94,10 +101,14 @@ template <int D, int NT> struct WaveState {
   float l[NT];  // partial row sum over this lane's keys
 };
 
+constexpr float kLn2 = 0.6931471805599453f;
+
 // One 32-key tile in LDS: K rows kbase[row0 .. row0+31], V rows likewise,
 // the first nvalid (1..32) keys valid.  ntq (<= NT) query tiles are active.
+// Returns this lane's part of the tile's probability sum for query tile 0,
+// relative to the running max after the tile.
 template <int D, int NT>
-__device__ __forceinline__ void tile(const char* kbase, const char* vbase, int row0, int nvalid, int ntq, float c2,
+__device__ __forceinline__ float tile(const char* kbase, const char* vbase, int row0, int nvalid, int ntq, float c2,
                                      WaveState<D, NT>& st) {
   using Sh = Shape<D>;
   const int lane = threadIdx.x & 63, h = lane >> 5, l32 = lane & 31;
@@ -126,6 +137,7 @@ __device__ __forceinline__ void tile(const char* kbase, const char* vbase, int r
     }
   }
   bf16x8_t pk[NT][2];
+  float ret = 0.f;
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
     if (n < ntq) {
@@ -151,6 +163,7 @@ __device__ __forceinline__ void tile(const char* kbase, const char* vbase, int r
         pk[n][j >> 3][j & 7] = (__bf16)p;
       }
       st.l[n] += ls;
+      if (n == 0) ret = ls;
     }
   }
   // O^T += V^T P^T; A = V^T (d x keys) read transposed from LDS
@@ -174,6 +187,7 @@ __device__ __forceinline__ void tile(const char* kbase, const char* vbase, int r
         if (n < ntq) st.o[n][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[n][ks2], st.o[n][dt], 0, 0, 0);
     }
   }
+  return ret;
 }
 
 template <int D, int NT>
@@ -247,7 +261,7 @@ __device__ __forceinline__ void pers_store(const PersPrefetch<D>& pf, char* buf)
   }
 }
 
-template <int D>
+template <int D, bool MASS>
 __global__ __launch_bounds__(kPersThreads, 1) void fwd_pers_kernel(FwdArgs a) {
   using Sh = Shape<D>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -280,8 +294,19 @@ __global__ __launch_bounds__(kPersThreads, 1) void fwd_pers_kernel(FwdArgs a) {
       const int n = min(a.plen[bh * g.S + s], g.C);
       if (s + 1 < g.S) pers_load<D>(a, bh, s + 1, pf);
       if (ntq > 0) {
-        if (n > 0) tile<D, kPersNT>(buf, buf + 64 * Sh::ROWB, 0, min(n, 32), ntq, c2, st);
-        if (n > 32) tile<D, kPersNT>(buf, buf + 64 * Sh::ROWB, 32, n - 32, ntq, c2, st);
+        float bs = 0.f;  // this lane's probability sum over the slot (MASS)
+        if (n > 0) bs = tile<D, kPersNT>(buf, buf + 64 * Sh::ROWB, 0, min(n, 32), ntq, c2, st);
+        if (n > 32) {
+          const float m0 = st.m[0];
+          const float t2 = tile<D, kPersNT>(buf, buf + 64 * Sh::ROWB, 32, n - 32, ntq, c2, st);
+          bs = bs * __builtin_amdgcn_exp2f(m0 - st.m[0]) + t2;
+        }
+        if (MASS) {
+          const float tot = half_sum(bs);
+          const int r = row_w + l32;
+          if (h == 0 && r < g.ct)
+            a.blse_p[(bh * g.S + s) * g.ct + r] = tot > 0.f ? st.m[0] * kLn2 + logf(tot) : -INFINITY;
+        }
       }
       if (s + 1 < g.S) pers_store<D>(pf, smem + ((s + 1) & 1) * kBufBytes);
       __syncthreads();
@@ -306,7 +331,7 @@ __global__ __launch_bounds__(kPersThreads, 1) void fwd_pers_kernel(FwdArgs a) {
                             st.o[n][dt][4 * i4 + 3] * inv);
           }
         }
-        if (h == 0) a.lse_part[bh * g.ct + r] = lt > 0.f ? st.m[n] * 0.6931471805599453f + logf(lt) : -INFINITY;
+        if (h == 0) a.lse_part[bh * g.ct + r] = lt > 0.f ? st.m[n] * kLn2 + logf(lt) : -INFINITY;
       }
     }
   }
@@ -400,7 +425,7 @@ __device__ __forceinline__ void loc_store(const LocPrefetch<D>& pf, char* buf) {
   }
 }
 
-template <int D>
+template <int D, bool MASS>
 __global__ __launch_bounds__(kLocThreads, 1) void fwd_local_kernel(FwdArgs a) {
   using Sh = Shape<D>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -436,6 +461,7 @@ __global__ __launch_bounds__(kLocThreads, 1) void fwd_local_kernel(FwdArgs a) {
   loc_load<D>(a, bh, qg, 0, pf, rowtab);
   loc_store<D>(pf, smem);
   __syncthreads();
+  float bs = 0.f;  // this lane's probability sum over the current selected block (MASS)
   for (int j = 0; j < nsteps; ++j) {
     char* buf = smem + (j & 1) * kBufBytes;
     int nv = 0;
@@ -452,7 +478,16 @@ __global__ __launch_bounds__(kLocThreads, 1) void fwd_local_kernel(FwdArgs a) {
     if (j + 1 < nsteps) loc_load<D>(a, bh, qg, j + 1, pf, rowtab);
     if (nv > 0) {
       const char* region = buf + (wave >> 1) * (64 * Sh::ROWB);
-      tile<D, 1>(region, region + 32 * Sh::ROWB, 0, nv, 1, c2, st);
+      const float m0 = st.m[0];
+      const float ts = tile<D, 1>(region, region + 32 * Sh::ROWB, 0, nv, 1, c2, st);
+      if (MASS) bs = (j & 1) ? bs * __builtin_amdgcn_exp2f(m0 - st.m[0]) + ts : ts;
+    } else if (MASS && !(j & 1)) {
+      bs = 0.f;
+    }
+    if (MASS && (j & 1) && ntq) {
+      const float tot = half_sum(bs);
+      if (h == 0 && row_ok)
+        a.blse_l[(bh * g.K + (j >> 1)) * g.ct + tok] = tot > 0.f ? st.m[0] * kLn2 + logf(tot) : -INFINITY;
     }
     if (j + 1 < nsteps) loc_store<D>(pf, smem + ((j + 1) & 1) * kBufBytes);
     __syncthreads();
@@ -462,7 +497,7 @@ __global__ __launch_bounds__(kLocThreads, 1) void fwd_local_kernel(FwdArgs a) {
   const float lt = half_sum(st.l[0]);
   if (!row_ok) return;
   const size_t row = bh * g.ct + tok;
-  const float lse_l = lt > 0.f ? st.m[0] * 0.6931471805599453f + logf(lt) : -INFINITY;
+  const float lse_l = lt > 0.f ? st.m[0] * kLn2 + logf(lt) : -INFINITY;
   const float lse_p = a.lse_part[row];
   const float mx = fmaxf(lse_l, lse_p);
   const float wl = lse_l == -INFINITY ? 0.f : expf(lse_l - mx);
@@ -494,7 +529,7 @@ hipError_t set_lds(K kernel, size_t bytes) {
   return hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
-template <int D>
+template <int D, bool MASS>
 hipError_t launch_d(const FwdArgs& base, hipStream_t s) {
   static bool attr = false;
   const size_t shm = 2 * kBufBytes;
@@ -502,8 +537,8 @@ hipError_t launch_d(const FwdArgs& base, hipStream_t s) {
   const size_t tabb = (size_t)kLocBlocks * g0.K * 64 * 4;
   const size_t shm_loc = shm + (tabb <= (size_t)kRowTabMax ? tabb + kLocBlocks * g0.K * 4 : 0);
   if (!attr) {
-    hipError_t e = set_lds(fwd_pers_kernel<D>, shm);
-    if (e == hipSuccess) e = set_lds(fwd_local_kernel<D>, shm + kRowTabMax + 4096);
+    hipError_t e = set_lds(fwd_pers_kernel<D, MASS>, shm);
+    if (e == hipSuccess) e = set_lds(fwd_local_kernel<D, MASS>, shm + kRowTabMax + 4096);
     if (e != hipSuccess) return e;
     attr = true;
   }
@@ -511,12 +546,12 @@ hipError_t launch_d(const FwdArgs& base, hipStream_t s) {
   FwdArgs a = base;
   a.ntiles = (g.ct + kPersRows - 1) / kPersRows;
   int total = g.B * g.H * a.ntiles;
-  fwd_pers_kernel<D><<<((total + 7) / 8) * 8, kPersThreads, shm, s>>>(a);
+  fwd_pers_kernel<D, MASS><<<((total + 7) / 8) * 8, kPersThreads, shm, s>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   a.ntiles = (g.nq + kLocBlocks - 1) / kLocBlocks;
   total = g.B * g.H * a.ntiles;
-  fwd_local_kernel<D><<<((total + 7) / 8) * 8, kLocThreads, shm_loc, s>>>(a);
+  fwd_local_kernel<D, MASS><<<((total + 7) / 8) * 8, kLocThreads, shm_loc, s>>>(a);
   return hipGetLastError();
 }
 
@@ -533,15 +568,16 @@ size_t fwd_mfma_workspace(const Geo& g) {
 
 hipError_t launch_fwd_mfma(const Geo& g, const void* q, const void* k_p, const void* v_p, const int32_t* plen,
                            const void* k_l, const void* v_l, const int32_t* topk, void* o, float* lse, void* ws,
-                           hipStream_t s) {
+                           float* blse_p, float* blse_l, hipStream_t s) {
   GeoTab tab;
   hipError_t e = launch_geo_table(g, ws, &tab, s);
   if (e != hipSuccess) return e;
   float* o_part = (float*)((char*)ws + geo_table_bytes(g));
   float* lse_part = (float*)((char*)o_part + ((size_t)g.B * g.H * g.ct * g.D * 4 + 255) / 256 * 256);
   FwdArgs a{g, (const bf16_t*)q, (const bf16_t*)k_p, (const bf16_t*)v_p, plen, (const bf16_t*)k_l,
-            (const bf16_t*)v_l, topk, (bf16_t*)o, lse, o_part, lse_part, tab, 0};
-  return g.D == 128 ? launch_d<128>(a, s) : launch_d<64>(a, s);
+            (const bf16_t*)v_l, topk, (bf16_t*)o, lse, o_part, lse_part, blse_p, blse_l, tab, 0};
+  if (blse_p) return g.D == 128 ? launch_d<128, true>(a, s) : launch_d<64, true>(a, s);
+  return g.D == 128 ? launch_d<128, false>(a, s) : launch_d<64, false>(a, s);
 }
 
 }  // namespace pbsa

@@ -7,7 +7,9 @@
 // neighbourhood; project page: local block-sparse attention with persistent
 // blocks).  One workgroup per (query block, head, batch); one lane per query
 // token; key/value tiles of up to 64 rows are staged through LDS and read as
-// broadcasts.  Online softmax in fp32.
+// broadcasts.  Online softmax in fp32.  Optionally (blse_p non-null) writes
+// each query's log-sum-exp over every slot and selected block, the input of
+// the token-exact attention mass.
 #include "common.h"
 
 namespace pbsa {
@@ -19,7 +21,8 @@ __global__ __launch_bounds__(64) void fwd_simple_kernel(Geo g, const T* __restri
                                                         const T* __restrict__ vp, const int32_t* __restrict__ plen,
                                                         const T* __restrict__ kl, const T* __restrict__ vl,
                                                         const int32_t* __restrict__ topk, T* __restrict__ o,
-                                                        float* __restrict__ lse) {
+                                                        float* __restrict__ lse, float* __restrict__ blse_p,
+                                                        float* __restrict__ blse_l) {
   constexpr int kRows = 32;  // rows staged per sub-tile (all lanes read the same row: broadcast)
   __shared__ float ks[kRows][D];
   __shared__ float vs[kRows][D];
@@ -44,19 +47,26 @@ __global__ __launch_bounds__(64) void fwd_simple_kernel(Geo g, const T* __restri
     BlockExt le;
     int loff = 0;
     bool pers = t < g.S;
+    float* blse = nullptr;  // where this query's log-sum-exp over the tile's rows goes
+    if (blse_p && active)
+      blse = pers ? blse_p + (bh * g.S + t) * g.ct + tok : blse_l + (bh * g.K + (t - g.S)) * g.ct + tok;
     if (pers) {
       n = min(plen[bh * g.S + t], g.C);
       kb = kp + (bh * g.S + t) * g.C * D;
       vb = vp + (bh * g.S + t) * g.C * D;
     } else {
       const int p = topk[(bh * g.nq + i) * g.K + (t - g.S)];
-      if ((unsigned)p >= (unsigned)g.nl) continue;  // ids outside the cache are ignored
+      if ((unsigned)p >= (unsigned)g.nl) {  // ids outside the cache are ignored
+        if (blse) *blse = -INFINITY;
+        continue;
+      }
       le = block_ext(g, p % g.nq);
       loff = (p / g.nq) * g.ct;
       n = le.len;
       kb = kl + bh * (size_t)g.NL * D;
       vb = vl + bh * (size_t)g.NL * D;
     }
+    float bsum = 0.f;  // probability sum over this tile's rows, relative to m
     for (int r0 = 0; r0 < n; r0 += kRows) {
       const int nr = min(kRows, n - r0);
       __syncthreads();
@@ -82,17 +92,20 @@ __global__ __launch_bounds__(64) void fwd_simple_kernel(Geo g, const T* __restri
       const float mn = fmaxf(m, tmax);
       const float corr = expf(m - mn);
       l *= corr;
+      bsum *= corr;
       for (int d = 0; d < D; ++d) acc[d] *= corr;
 #pragma unroll
       for (int r = 0; r < kRows; ++r) {
         if (r < nr) {
           const float p = expf(s[r] - mn);
           l += p;
+          bsum += p;
           for (int d = 0; d < D; ++d) acc[d] = fmaf(p, vs[r][d], acc[d]);
         }
       }
       m = mn;
     }
+    if (blse) *blse = bsum > 0.f ? m + logf(bsum) : -INFINITY;
   }
   if (!active) return;
   const float inv = 1.0f / l;
@@ -105,11 +118,11 @@ __global__ __launch_bounds__(64) void fwd_simple_kernel(Geo g, const T* __restri
 
 hipError_t launch_fwd_simple(const Geo& g, const void* q, const void* k_p, const void* v_p, const int32_t* plen,
                              const void* k_l, const void* v_l, const int32_t* topk, void* o, float* lse,
-                             hipStream_t s) {
+                             float* blse_p, float* blse_l, hipStream_t s) {
   dim3 grid(g.nq, g.H, g.B);
 #define PBSA_LAUNCH(T, D)                                                                                   \
   fwd_simple_kernel<T, D><<<grid, 64, 0, s>>>(g, (const T*)q, (const T*)k_p, (const T*)v_p, plen, (const T*)k_l, \
-                                              (const T*)v_l, topk, (T*)o, lse)
+                                              (const T*)v_l, topk, (T*)o, lse, blse_p, blse_l)
   if (g.dtype == PBSA_BF16) {
     if (g.D == 64) PBSA_LAUNCH(bf16_t, 64); else PBSA_LAUNCH(bf16_t, 128);
   } else {

@@ -107,6 +107,7 @@ typedef struct {
   size_t ws_fwd;
   size_t ws_bwd;
   size_t ws_persist_update;
+  size_t ws_fwd_mass;
 } pbsa_plan_info;
 
 /* Validate a configuration and derive its sizes.  Host only; touches no GPU.
@@ -151,6 +152,23 @@ pbsa_status pbsa_fwd(const pbsa_config* cfg, const void* q, const void* k_pers, 
                      const int32_t* persist_len, const void* k_local, const void* v_local,
                      const int32_t* topk_idx, void* o, float* lse, void* ws, size_t ws_bytes,
                      void* stream);
+
+/* pbsa_fwd plus the token-exact attention mass of every candidate block: the
+ * alternative to the pooled mass of pbsa_score_select as input of
+ * pbsa_persist_update (the abstract only says the persistent memory keeps the
+ * blocks most relevant to the queries; this reading takes relevance from the
+ * attention itself).  mass[b,h,j] = sum over the chunk's query tokens t of the
+ * softmax probability that t's attention puts on the rows of block j (slot s
+ * at index s, physical local block p at S+p).  Every entry is written: empty
+ * slots and local blocks that no query block selected get 0, and the entries
+ * of a head sum to Nq.  o and lse are as from pbsa_fwd.  Deterministic (fixed
+ * summation order, no atomics).  ws: at least plan.ws_fwd_mass bytes
+ * (per-query log-sum-exps over every slot and selected block, about
+ * 4*B*H*(S+K)*Nq bytes, plus 4*B*H*NQ_blocks*NL_blocks). */
+pbsa_status pbsa_fwd_mass(const pbsa_config* cfg, const void* q, const void* k_pers, const void* v_pers,
+                          const int32_t* persist_len, const void* k_local, const void* v_local,
+                          const int32_t* topk_idx, void* o, float* lse, float* mass, void* ws, size_t ws_bytes,
+                          void* stream);
 
 /* Backward of pbsa_fwd for a fixed block mask ("full gradient support for
  * training" on the project page).  Inputs as in pbsa_fwd plus o, lse (from

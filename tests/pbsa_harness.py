@@ -61,6 +61,13 @@ class GpuStep:
         pb.pbsa_fwd(self.p, self.q, self.k_p, self.v_p, self.plen, self.k_l, self.v_l,
                     self.topk if topk is None else topk, self.o, self.lse, self.ws_fwd)
 
+    def fwd_mass(self, topk=None):
+        """Forward plus token-exact masses (into self.mass)."""
+        if not hasattr(self, "ws_fwd_mass"):
+            self.ws_fwd_mass = pb.workspace(self.p, "fwd_mass")
+        pb.pbsa_fwd_mass(self.p, self.q, self.k_p, self.v_p, self.plen, self.k_l, self.v_l,
+                         self.topk if topk is None else topk, self.o, self.lse, self.mass, self.ws_fwd_mass)
+
     def bwd(self, dout, topk=None):
         s = pb.shapes(self.p)
         f = dict(dtype=torch.float32, device="cuda")
