@@ -122,17 +122,22 @@ def step(cfg, q, k_l, v_l, k_p, v_p, plen, ring_head, step_id):
             for j, x in cand:
                 mass[j] += math.exp(x - m) / z
         res["mass"].append(mass)
-        # update: exhaustive ranking of all candidates
+        # update: exhaustive ranking of all candidates; pinned sink slots
+        # (the first `sink` slots) stay, or take the evicted block of their index
         old = ring_head % R
-        cands = [(-mass[s], 0, s) for s in range(S) if lens[s]]
-        cands += [(-mass[S + old * nq + e], 1, e) for e in range(nq)]
+        sink = cfg.get("sink_slots", 0)
+        pinned = {s for s in range(sink) if lens[s]}
+        sink_fill = {s: s for s in range(sink) if not lens[s]}
+        cands = [(-mass[s], 0, s) for s in range(S) if lens[s] and s not in pinned]
+        cands += [(-mass[S + old * nq + e], 1, e) for e in range(nq) if e not in sink_fill]
         cands.sort()
-        kept = cands[:S]
-        keep = {c[2] for c in kept if c[1] == 0}
+        kept = cands[:S - sink]
+        keep = {c[2] for c in kept if c[1] == 0} | pinned
         admit = sorted(c[2] for c in kept if c[1] == 1)
-        vac = [s for s in range(S) if s not in keep]
+        vac = [s for s in range(S) if s not in keep and s not in sink_fill]
         slots = []
         ent_for = dict(zip(vac, admit))
+        ent_for.update(sink_fill)
         for s in range(S):
             if s in keep:
                 slots.append((lens[s], None, [r[:] for r in KP[s]], [r[:] for r in VP[s]]))
@@ -145,5 +150,5 @@ def step(cfg, q, k_l, v_l, k_p, v_p, plen, ring_head, step_id):
             else:
                 slots.append((0, "empty", [[0.0] * D] * len(KP[s]), [[0.0] * D] * len(KP[s])))
         res["slots"].append(slots)
-        res["n_replaced"].append(len(admit))
+        res["n_replaced"].append(len(admit) + len(sink_fill))
     return res

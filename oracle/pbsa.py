@@ -46,6 +46,9 @@ READINGS = {
     "R15": "near-tie: boundary gap < 1e-4 * (max - min) of the row's (or head's) oracle scores",
     "R16": "inputs are bf16-rounded (or fp32); attention and gradients in float64; decisions in float32",
     "R17": "gradients flow to q, k_p, v_p, k_l, v_l only; the block mask is fixed",
+    "R20": "sink pattern (project page feature list): the first sink_slots persistent slots are pinned: never "
+           "candidates for eviction; an empty sink slot j takes block j of the chunk leaving the local window, so "
+           "a rollout that starts from an empty persistent cache pins the first frame's blocks",
     "R19": "token-exact mass (the other reading of R11, chosen by the caller): block mass = sum over the chunk's "
            "query tokens of the probability their PBSA softmax puts on the block's rows; 0 for empty slots and for "
            "local blocks no query block selected",
@@ -79,6 +82,7 @@ class Geometry:
     scale: float
     block_tok: list      # per chunk block: token offsets inside the chunk (raster order)
     block_len: np.ndarray
+    n_sink: int = 0      # pinned leading persistent slots (reading R20)
 
     def local_tokens_of(self, p: int) -> np.ndarray:
         c, blk = divmod(p, self.n_qblk)
@@ -129,9 +133,12 @@ def geometry(cfg: dict) -> Geometry:
     else:
         k = n_lblk
     scale = cfg.get("softmax_scale", 0.0) or 1.0 / math.sqrt(cfg["head_dim"])
+    n_sink = int(cfg.get("sink_slots", 0))
+    if not 0 <= n_sink <= min(S, n_qblk):
+        raise ValueError("sink_slots must be in [0, min(persistent slots, blocks per chunk)]")
     return Geometry(cfg["batch"], cfg["heads"], cfg["head_dim"], fh, fw, bt, bh, bw, cf, ft, ct,
                     n_qblk, R, n_lblk, S, bt * bh * bw, k, float(scale), block_tok,
-                    np.array([len(t) for t in block_tok], dtype=np.int32))
+                    np.array([len(t) for t in block_tok], dtype=np.int32), n_sink)
 
 
 # ----------------------------------------------------------------------------
@@ -371,16 +378,27 @@ def update_decisions(mass, plen, ring_head: int, g: Geometry):
     incumbents before entrants, then the lower slot / block index.  The first
     min(S, #candidates) are kept.  Returns keep[B,H,S] (bool) and
     admit[B,H,n_qblk] (bool).
+
+    Sink slots (reading R20), s < n_sink, are not candidates: a valid one is
+    always kept, an empty one always admits evicted block e = s; the other
+    candidates compete for the remaining S - n_sink places.
     """
     keep = np.zeros((g.B, g.H, g.S), dtype=bool)
     admit = np.zeros((g.B, g.H, g.n_qblk), dtype=bool)
     old = ring_head % g.R
+    Z = g.n_sink
     for b in range(g.B):
         for h in range(g.H):
-            cands = [(-float(mass[b, h, s]), 0, s) for s in range(g.S) if plen[b, h, s] > 0]
-            cands += [(-float(mass[b, h, g.S + old * g.n_qblk + e]), 1, e) for e in range(g.n_qblk)]
+            for s in range(Z):
+                if plen[b, h, s] > 0:
+                    keep[b, h, s] = True
+                else:
+                    admit[b, h, s] = True
+            cands = [(-float(mass[b, h, s]), 0, s) for s in range(Z, g.S) if plen[b, h, s] > 0]
+            cands += [(-float(mass[b, h, g.S + old * g.n_qblk + e]), 1, e) for e in range(g.n_qblk)
+                      if not (e < Z and plen[b, h, e] == 0)]
             cands.sort()
-            for _, kind, idx in cands[: g.S]:
+            for _, kind, idx in cands[: g.S - Z]:
                 if kind == 0:
                     keep[b, h, idx] = True
                 else:
@@ -393,7 +411,9 @@ def apply_update(state: dict, keep, admit, k_l, v_l, kbar_l, ring_head: int, ste
     """Move admitted blocks into vacated slots (reading R13) and return the new state.
 
     Vacated slots = empty or dropped slots, ascending; admitted blocks in
-    ascending order fill them pairwise.  A filled slot gets the block's rows
+    ascending order fill them pairwise.  With sink slots (R20) an empty sink
+    slot s takes admitted block s, and pairing uses the other slots and
+    blocks only.  A filled slot gets the block's rows
     (raster order within the block), zero padding, len = block size,
     src = step_id * n_qblk + e and kbar = the block's pooled key.  Vacated
     slots left over are emptied (rows zero, len 0, src EMPTY_SRC, kbar 0).
@@ -405,17 +425,20 @@ def apply_update(state: dict, keep, admit, k_l, v_l, kbar_l, ring_head: int, ste
     kbar = state["persist_kbar"].copy()
     n_rep = np.zeros((g.B, g.H), dtype=np.int32)
     old = ring_head % g.R
+    Z = g.n_sink
     for b in range(g.B):
         for h in range(g.H):
-            vac = [s for s in range(g.S) if not (plen[b, h, s] > 0 and keep[b, h, s])]
-            ent = [e for e in range(g.n_qblk) if admit[b, h, e]]
+            fills = [s for s in range(Z) if plen[b, h, s] == 0]
+            assert all(admit[b, h, s] for s in fills) and all(keep[b, h, s] for s in range(Z) if s not in fills)
+            vac = [s for s in range(Z, g.S) if not (plen[b, h, s] > 0 and keep[b, h, s])]
+            ent = [e for e in range(g.n_qblk) if admit[b, h, e] and e not in fills]
             assert len(ent) <= len(vac)
-            n_rep[b, h] = len(ent)
-            for j, s in enumerate(vac):
+            n_rep[b, h] = len(ent) + len(fills)
+            pairs = list(zip(fills, fills)) + [(s, ent[j] if j < len(ent) else None) for j, s in enumerate(vac)]
+            for s, e in pairs:
                 k_p[b, h, s] = 0
                 v_p[b, h, s] = 0
-                if j < len(ent):
-                    e = ent[j]
+                if e is not None:
                     tok = old * g.chunk_tokens + g.block_tok[e]
                     n = len(tok)
                     k_p[b, h, s, :n] = k_l[b, h, tok]

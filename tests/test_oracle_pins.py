@@ -119,10 +119,14 @@ def test_topk_rounding():
 # ---------------------------------------------------------------------------
 
 
-@pytest.mark.parametrize("ring_head", [0, 2])
-def test_brute_force_matches(ring_head):
-    cfg = tiny_cfg()
+@pytest.mark.parametrize("ring_head,sink", [(0, 0), (2, 0), (1, 2), (2, 4)])
+def test_brute_force_matches(ring_head, sink):
+    cfg = tiny_cfg(sink_slots=sink)
     x = synth.make_step_inputs(cfg)
+    if sink:
+        x["persist_len"][..., 1] = 0        # an empty sink slot is filled from the evicted chunk
+        x["k_p"][..., 1, :, :] = 0
+        x["v_p"][..., 1, :, :] = 0
     g, sel, O, L, up = run_oracle(cfg, x, ring_head=ring_head, step_id=7)
     br = brute.step(cfg, x["q"], x["k_l"], x["v_l"], x["k_p"], x["v_p"], x["persist_len"],
                     ring_head, 7)
@@ -485,6 +489,58 @@ def test_update_valid_count_and_src_multiset():
                              for c in top])
             got = sorted(int(v) for v in up["persist_src"][b, h] if v != oracle.EMPTY_SRC)
             assert got == expect
+
+
+def test_sink_slots_stay_under_lowest_mass():
+    cfg = dict(synth.workload("tiny_fp32"), sink_slots=2)
+    x = synth.make_step_inputs(cfg)
+    g = oracle.geometry(cfg)
+    assert g.n_sink == 2
+    rng = np.random.default_rng(12)
+    mass = rng.uniform(1.0, 2.0, (g.B, g.H, g.S + g.n_lblk)).astype(np.float32)
+    n = min(g.n_qblk, g.S - 2)
+    mass[..., :2] = 0.0                       # sinks receive nothing
+    mass[..., 2:2 + n] = 0.01                 # the n weakest other incumbents
+    old = 0
+    mass[..., g.S + old * g.n_qblk:g.S + (old + 1) * g.n_qblk] = 50.0
+    st = _state(x, g)
+    up = oracle.persist_update(st, mass, x["k_l"], x["v_l"], oracle.pool_local_blocks(x["k_l"], g), old, 1, g)
+    for k in ("k_p", "v_p", "persist_len", "persist_src", "persist_kbar"):
+        np.testing.assert_array_equal(up[k][:, :, :2], st[k][:, :, :2])
+    # the evicted blocks all win, against the weakest non-sink incumbents
+    assert (up["n_replaced"] == n).all()
+    assert (~up["keep"][..., 2:2 + n]).all() and up["keep"][..., 2 + n:].all()
+    # without sinks the two zero-mass slots are the first to go
+    up0 = oracle.persist_update(st, mass, x["k_l"], x["v_l"], oracle.pool_local_blocks(x["k_l"], g), old, 1,
+                                oracle.geometry(dict(cfg, sink_slots=0)))
+    assert (~up0["keep"][..., :2]).all()
+
+
+def test_sink_fill_from_empty_cache():
+    cfg = dict(synth.workload("tiny_fp32"), sink_slots=3)
+    x = synth.make_step_inputs(cfg)
+    g = oracle.geometry(cfg)
+    st = _state(x, g)
+    for k in ("persist_len", "k_p", "v_p", "persist_kbar"):
+        st[k] = np.zeros_like(st[k])
+    st["persist_src"] = np.full_like(st["persist_src"], oracle.EMPTY_SRC)
+    mass = np.zeros((g.B, g.H, g.S + g.n_lblk), np.float32)
+    rh = 1
+    mass[..., g.S + rh * g.n_qblk + 0] = 9.0   # block 0 would win anyway; blocks 1, 2 have no mass
+    kbl = oracle.pool_local_blocks(x["k_l"], g)
+    up = oracle.persist_update(st, mass, x["k_l"], x["v_l"], kbl, rh, 4, g)
+    for b in range(g.B):
+        for h in range(g.H):
+            for s in range(3):                     # sink slot s holds evicted block s
+                tok = rh * g.chunk_tokens + g.block_tok[s]
+                np.testing.assert_array_equal(up["k_p"][b, h, s, :len(tok)], x["k_l"][b, h, tok])
+                assert up["persist_src"][b, h, s] == 4 * g.n_qblk + s
+                np.testing.assert_array_equal(up["persist_kbar"][b, h, s], kbl[b, h, rh * g.n_qblk + s])
+            # the remaining blocks fill slots 3.. in ascending order
+            rest = list(range(3, g.n_qblk))
+            for j, e in enumerate(rest):
+                assert up["persist_src"][b, h, 3 + j] == 4 * g.n_qblk + e
+    assert (up["n_replaced"] == g.n_qblk).all()
 
 
 def test_near_tie_band():
