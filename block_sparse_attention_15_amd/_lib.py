@@ -30,7 +30,7 @@ class PbsaConfig(ctypes.Structure):
         ("persistent_cache_size", ctypes.c_int64),
         ("use_local_block_sparse_attn", ctypes.c_int32),
         ("topk_ratio", ctypes.c_float), ("softmax_scale", ctypes.c_float),
-        ("dtype", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("sink_slots", ctypes.c_int32),
     ]
 
 

@@ -104,6 +104,10 @@ pbsa_status make_plan(const pbsa_config* c, Plan* p) {
   g.dtype = c->dtype;
   if (g.S > 2048 || g.nl > 2048 || g.nq > 2048)
     return fail(PBSA_ERR_UNSUPPORTED, "more than 2048 blocks per cache or chunk");
+  if (c->sink_slots < 0 || c->sink_slots > g.S || c->sink_slots > g.nq)
+    return fail(PBSA_ERR_INVALID_ARG, "sink_slots (%d) must be in [0, min(%d slots, %d blocks per chunk)]",
+                c->sink_slots, g.S, g.nq);
+  g.Z = c->sink_slots;
 
   pbsa_plan_info& in = p->info;
   memset(&in, 0, sizeof in);

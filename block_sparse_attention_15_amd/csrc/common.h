@@ -26,6 +26,7 @@ struct Geo {
   int K;       // top-k
   float scale; // softmax scale
   int dtype;   // pbsa_dtype
+  int Z;       // pinned sink slots (leading persistent slots)
 };
 
 // Extent of chunk block j: base token offset inside the chunk, frames, rows,

@@ -7,7 +7,10 @@
 // local chunk (the ones leaving the sliding window); the S candidates with the
 // largest pooled attention mass stay (ties: incumbents first, then lower slot
 // or block index); vacated slots, ascending, receive the admitted blocks,
-// ascending, and slots left over are emptied.
+// ascending, and slots left over are emptied.  With Z pinned sink slots
+// (the project page's "sink" pattern) the first Z slots are not candidates: a
+// valid one stays, an empty one takes the evicted block of its own index, and
+// the other candidates compete for the remaining S - Z slots.
 //
 // Two launches: a per-(batch, head) decision kernel that ranks candidates and
 // rewrites slot metadata, then a data-movement kernel with one workgroup per
@@ -22,9 +25,9 @@ constexpr int kThreads = 256;
 
 // plan[b,h,s]: -2 keep, -1 empty the slot, p >= 0 fill from physical local block p.
 // Candidates carry a 64-bit key (mass, then the tie order: slots before
-// entrants, lower index first); a candidate is kept when fewer than S valid
-// candidates have a larger key.  Wave 0 then pairs vacated slots with admitted
-// entrants by ballot prefix counts.
+// entrants, lower index first); a candidate is kept when fewer than S - Z
+// valid candidates have a larger key.  Wave 0 then pairs vacated slots with
+// admitted entrants by ballot prefix counts.
 __global__ __launch_bounds__(kThreads) void update_decide_kernel(Geo g, const float* __restrict__ mass,
                                                                  const int32_t* __restrict__ ring_head,
                                                                  const int32_t* __restrict__ step_counter,
@@ -43,7 +46,9 @@ __global__ __launch_bounds__(kThreads) void update_decide_kernel(Geo g, const fl
   const int step_id = *step_counter;
   const float* mrow = mass + bh * (g.S + g.nl);
   for (int c = threadIdx.x; c < NC; c += kThreads) {
-    const bool valid = c >= g.S || plen[bh * g.S + c] > 0;
+    // sink slots, and evicted blocks reserved for an empty sink slot, are not candidates
+    const bool valid = c < g.S ? (c >= g.Z && plen[bh * g.S + c] > 0)
+                               : !(c - g.S < g.Z && plen[bh * g.S + (c - g.S)] == 0);
     const float m = c < g.S ? mrow[c] : mrow[g.S + old * g.nq + (c - g.S)];
     unsigned u = m == 0.f ? 0u : __float_as_uint(m);
     u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
@@ -54,11 +59,27 @@ __global__ __launch_bounds__(kThreads) void update_decide_kernel(Geo g, const fl
     const unsigned long long kc = key[c];
     int rank = 0;
     for (int o = 0; o < NC; ++o) rank += key[o] > kc;
-    kept[c] = kc != 0ull && rank < g.S;
+    kept[c] = kc != 0ull && rank < g.S - g.Z;
   }
   __syncthreads();
   if (threadIdx.x >= 64) return;
   const int lane = threadIdx.x;
+  int n_sink_fill = 0;  // empty sink slots, each filled with the evicted block of its index
+  for (int s0 = 0; s0 < g.Z; s0 += 64) {
+    const int s = s0 + lane;
+    const bool fill = s < g.Z && plen[bh * g.S + s] == 0;
+    n_sink_fill += __builtin_popcountll(__builtin_amdgcn_ballot_w64(fill));
+    if (s < g.Z) {
+      const size_t bs = bh * g.S + s;
+      if (fill) {
+        plan[bs] = old * g.nq + s;
+        plen[bs] = block_ext(g, s).len;
+        psrc[bs] = step_id * g.nq + s;
+      } else {
+        plan[bs] = -2;
+      }
+    }
+  }
   const unsigned long long below = (1ull << lane) - 1;
   int n_adm = 0;
   for (int e0 = 0; e0 < g.nq; e0 += 64) {
@@ -68,12 +89,12 @@ __global__ __launch_bounds__(kThreads) void update_decide_kernel(Geo g, const fl
     if (on) alist[n_adm + __builtin_popcountll(m & below)] = e;
     n_adm += __builtin_popcountll(m);
   }
-  if (lane == 0) n_rep[bh] = n_adm;
+  if (lane == 0) n_rep[bh] = n_adm + n_sink_fill;
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   int nvac = 0;
-  for (int s0 = 0; s0 < g.S; s0 += 64) {
+  for (int s0 = g.Z; s0 < g.S; s0 += 64) {
     const int s = s0 + lane;
     const bool in = s < g.S;
     const bool vac = in && !(key[s] != 0ull && kept[s]);

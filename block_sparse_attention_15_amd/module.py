@@ -41,7 +41,8 @@ class SparseForcingAttention:
                  kv_cache_mode: str = "sparse_forcing", sparse_kv_block_size=(1, 8, 8), max_seq_len: int = 32760,
                  use_local_block_sparse_attn: bool = True, local_block_sparse_topk_ratio: float = 0.125, *,
                  batch: int = 1, heads: int = 12, head_dim: int = 128, frame_h: int = 30, frame_w: int = 52,
-                 chunk_frames: int = 3, softmax_scale: float = 0.0, dtype: str = "bf16", device="cuda"):
+                 chunk_frames: int = 3, softmax_scale: float = 0.0, dtype: str = "bf16", sink_slots: int = 0,
+                 mass: str = "pooled", device="cuda"):
         if kv_cache_mode != "sparse_forcing":
             raise ValueError("only kv_cache_mode='sparse_forcing' is implemented")
         bt, bh, bw = sparse_kv_block_size
@@ -52,13 +53,18 @@ class SparseForcingAttention:
             total_cache_size=total_cache_size, local_cache_size=local_cache_size,
             persistent_cache_size=persistent_cache_size,
             use_local_block_sparse_attn=int(bool(use_local_block_sparse_attn)),
-            topk_ratio=local_block_sparse_topk_ratio, softmax_scale=softmax_scale, dtype=dtype))
+            topk_ratio=local_block_sparse_topk_ratio, softmax_scale=softmax_scale, dtype=dtype,
+            sink_slots=sink_slots))
+        if mass not in ("pooled", "token"):
+            raise ValueError("mass must be 'pooled' or 'token'")
+        self.mass_mode = mass
         p, s = self.plan, api.shapes(self.plan)
         self.device = device
         self.ws_score = api.workspace(p, "score_select", device)
         self.ws_bwd = None
         self.ws_update = api.workspace(p, "persist_update", device)
         self.ws_fwd = api.workspace(p, "fwd", device)
+        self.ws_fwd_mass = api.workspace(p, "fwd_mass", device) if mass == "token" else None
         self.topk_idx = torch.empty(s["topk_idx"], dtype=torch.int32, device=device)
         self.mass = torch.empty(s["mass"], dtype=torch.float32, device=device)
         self.kbar_local = torch.empty(s["kbar_local"], dtype=torch.float32, device=device)
@@ -93,8 +99,12 @@ class SparseForcingAttention:
         lse = torch.empty(api.shapes(p)["lse"], dtype=torch.float32, device=query.device)
         api.pbsa_score_select(p, query, cache.k_local, cache.ring_head, cache.persist_kbar, cache.persist_len,
                               self.topk_idx, self.mass, self.kbar_local, self.ws_score, stream)
-        api.pbsa_fwd(p, query, cache.k_pers, cache.v_pers, cache.persist_len, cache.k_local, cache.v_local,
-                     self.topk_idx, o, lse, self.ws_fwd, stream)
+        if update and self.mass_mode == "token":
+            api.pbsa_fwd_mass(p, query, cache.k_pers, cache.v_pers, cache.persist_len, cache.k_local, cache.v_local,
+                              self.topk_idx, o, lse, self.mass, self.ws_fwd_mass, stream)
+        else:
+            api.pbsa_fwd(p, query, cache.k_pers, cache.v_pers, cache.persist_len, cache.k_local, cache.v_local,
+                         self.topk_idx, o, lse, self.ws_fwd, stream)
         if update:
             api.pbsa_persist_update(p, self.mass, cache.k_local, cache.v_local, self.kbar_local, cache.ring_head,
                                     cache.step_counter, cache.k_pers, cache.v_pers, cache.persist_len,

@@ -8,6 +8,9 @@ local (L) caches.  ``DecodeLoop`` issues exactly those library calls:
 * ``denoise_pass()``: score_select + fwd on the current chunk (no update);
 * ``cache_pass()``:   ring_append of the chunk's K/V into the free ring slot,
   score_select, fwd, persist_update (which advances ring head and step).
+  With ``mass="token"`` the forward of the cache pass is ``pbsa_fwd_mass``
+  and the update ranks blocks by their token-exact attention mass instead of
+  the pooled mass of score_select.
 
 All per-step state (ring head, step counter, slot metadata) lives on the
 device, so ``capture()`` records one step into a HIP graph (via
@@ -24,9 +27,12 @@ from .module import PBSACache
 
 
 class DecodeLoop:
-    def __init__(self, plan: api.Plan, cache: PBSACache, device="cuda"):
+    def __init__(self, plan: api.Plan, cache: PBSACache, device="cuda", mass: str = "pooled"):
+        if mass not in ("pooled", "token"):
+            raise ValueError("mass must be 'pooled' or 'token'")
         self.plan = plan
         self.cache = cache
+        self.mass_mode = mass
         s = api.shapes(plan)
         dt = plan.torch_dtype
         self.q = torch.zeros(s["q"], dtype=dt, device=device)       # staging: current chunk queries
@@ -41,6 +47,7 @@ class DecodeLoop:
         self.ws_score = api.workspace(plan, "score_select", device)
         self.ws_fwd = api.workspace(plan, "fwd", device)
         self.ws_update = api.workspace(plan, "persist_update", device)
+        self.ws_fwd_mass = api.workspace(plan, "fwd_mass", device) if mass == "token" else None
         self.graph = None
 
     def load_chunk(self, q, k, v):
@@ -64,7 +71,13 @@ class DecodeLoop:
         """Append the chunk's K/V to the ring, attend, then update the persistent cache."""
         c, p = self.cache, self.plan
         api.pbsa_ring_append(p, self.k_new, self.v_new, c.ring_head, c.k_local, c.v_local, stream)
-        self._attend(stream)
+        if self.mass_mode == "token":
+            api.pbsa_score_select(p, self.q, c.k_local, c.ring_head, c.persist_kbar, c.persist_len, self.topk,
+                                  self.mass, self.kbar_local, self.ws_score, stream)
+            api.pbsa_fwd_mass(p, self.q, c.k_pers, c.v_pers, c.persist_len, c.k_local, c.v_local, self.topk, self.o,
+                              self.lse, self.mass, self.ws_fwd_mass, stream)
+        else:
+            self._attend(stream)
         api.pbsa_persist_update(p, self.mass, c.k_local, c.v_local, self.kbar_local, c.ring_head, c.step_counter,
                                 c.k_pers, c.v_pers, c.persist_len, c.persist_src, c.persist_kbar, self.n_replaced,
                                 self.ws_update, stream)

@@ -91,6 +91,9 @@ typedef struct {
   float topk_ratio;                    /* local_block_sparse_topk_ratio, in (0, 1] */
   float softmax_scale;                 /* 0 means 1/sqrt(head_dim) */
   int32_t dtype;                       /* pbsa_dtype of q/k/v/o/dout */
+  int32_t sink_slots;                  /* "sink" pattern: the first sink_slots persistent slots
+                                          are pinned (see pbsa_persist_update); 0 = none;
+                                          at most min(S, NQ_blocks) */
 } pbsa_config;
 
 /* Derived sizes and workspace requirements (bytes). */
@@ -196,7 +199,14 @@ pbsa_status pbsa_bwd(const pbsa_config* cfg, const void* q, const void* k_pers, 
  * free for the next chunk, and *step_counter advances by one.  Both are
  * device int32 values, so one captured graph serves every step of a rollout
  * (src ids are int32: step*NQ_blocks must stay below 2^31).  ws of at least
- * plan.ws_persist_update bytes. */
+ * plan.ws_persist_update bytes.
+ *
+ * Sink slots (cfg.sink_slots = Z > 0; the project page lists "sink" among the
+ * sparsity patterns): slots s < Z are not candidates.  A valid sink slot is
+ * always kept; an empty one receives block s of the evicted chunk (so a
+ * rollout that starts from an empty persistent cache pins the blocks of the
+ * first frame to leave the local window).  The other candidates compete for
+ * the remaining S - Z slots as above. */
 pbsa_status pbsa_persist_update(const pbsa_config* cfg, const float* mass, const void* k_local,
                                 const void* v_local, const float* kbar_local, int32_t* ring_head,
                                 int32_t* step_counter, void* k_pers, void* v_pers, int32_t* persist_len,

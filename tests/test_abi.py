@@ -48,6 +48,9 @@ def test_plan_matches_oracle_geometry(cfg):
 def test_plan_footprint_c1():
     p = pb.pbsa_plan(synth.workload("decode_c1"))
     assert (p.blocks_per_chunk, p.local_blocks, p.persistent_slots, p.topk) == (84, 168, 168, 21)
+    # the token-mass forward needs the forward's workspace plus per-query block log-sum-exps
+    assert p.ws_fwd_mass >= p.ws_fwd + 4 * 12 * (168 + 21) * 4680 + 4 * 12 * 84 * 168
+    assert pb.pbsa_plan(dict(synth.workload("decode_c1"), sink_slots=84)).persistent_slots == 168
 
 
 @pytest.mark.parametrize("bad,status", [
@@ -61,6 +64,8 @@ def test_plan_footprint_c1():
     (dict(block_h=16), _lib.PBSA_ERR_UNSUPPORTED),
     (dict(heads=0), _lib.PBSA_ERR_INVALID_ARG),
     (dict(dtype=7), _lib.PBSA_ERR_INVALID_ARG),
+    (dict(sink_slots=-1), _lib.PBSA_ERR_INVALID_ARG),
+    (dict(sink_slots=85), _lib.PBSA_ERR_INVALID_ARG),     # more than the 84 blocks per chunk
 ])
 def test_plan_rejects(bad, status):
     cfg = dict(synth.workload("decode_c1"), **bad)
