@@ -285,7 +285,10 @@ __device__ __forceinline__ void build_rowtab(const BwdArgs& a, size_t bh, int qg
   }
 }
 
-template <int D>
+// TAB (row addresses from the LDS table) is a compile-time choice so that the
+// global-memory address path does not share the loop: joining the two makes
+// the compiler wait for every outstanding load, the K/V prefetch included.
+template <int D, bool TAB>
 __device__ __forceinline__ void loc_load(const BwdArgs& a, size_t bh, int qg, int j, LocPf<D>& pf,
                                          const int* rowtab) {
   const Geo& g = a.g;
@@ -300,7 +303,7 @@ __device__ __forceinline__ void loc_load(const BwdArgs& a, size_t bh, int qg, in
     const int qb = qg * kLocBlocks + w;
     bool ok = false;
     size_t off = 0;
-    if (rowtab) {
+    if (TAB) {
       const int tok = rowtab[(w * g.K + t) * 64 + r];
       ok = tok >= 0;
       off = (size_t)(ok ? tok : 0) * D + c * 8;
@@ -333,7 +336,7 @@ __device__ __forceinline__ void loc_store(const LocPf<D>& pf, char* buf) {
   }
 }
 
-template <int D>
+template <int D, bool TAB>
 __global__ __launch_bounds__(kDqlThreads, 1) void dq_local_kernel(BwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int BUF = kLocBlocks * 2 * Sh<D>::TILEB;
@@ -355,15 +358,14 @@ __global__ __launch_bounds__(kDqlThreads, 1) void dq_local_kernel(BwdArgs a) {
   q_init<D>(a, bh, tok, ok, st);
   const float c2 = g.scale * kLog2e;
   const int nsteps = 2 * g.K;
-  const bool use_tab = kLocBlocks * g.K * 64 * 4 <= kRowTabMax;
-  int* rowtab = use_tab ? reinterpret_cast<int*>(smem + 2 * BUF) : nullptr;
+  int* rowtab = reinterpret_cast<int*>(smem + 2 * BUF);
   int* lentab = rowtab + kLocBlocks * g.K * 64;
-  if (use_tab) {
+  if (TAB) {
     build_rowtab(a, bh, qg, kDqlThreads, rowtab, lentab);
     __syncthreads();
   }
   LocPf<D> pf;
-  loc_load<D>(a, bh, qg, 0, pf, rowtab);
+  loc_load<D, TAB>(a, bh, qg, 0, pf, rowtab);
   loc_store<D>(pf, smem);
   __syncthreads();
   for (int j = 0; j < nsteps; ++j) {
@@ -371,7 +373,7 @@ __global__ __launch_bounds__(kDqlThreads, 1) void dq_local_kernel(BwdArgs a) {
     int nv = 0;
     if (active) {
       int len = 0;
-      if (use_tab) {
+      if (TAB) {
         len = lentab[(wave >> 1) * g.K + (j >> 1)];
       } else {
         const int p = a.topk[(bh * g.nq + qb) * g.K + (j >> 1)];
@@ -379,7 +381,7 @@ __global__ __launch_bounds__(kDqlThreads, 1) void dq_local_kernel(BwdArgs a) {
       }
       nv = min(len - 32 * (j & 1), 32);
     }
-    if (j + 1 < nsteps) loc_load<D>(a, bh, qg, j + 1, pf, rowtab);
+    if (j + 1 < nsteps) loc_load<D, TAB>(a, bh, qg, j + 1, pf, rowtab);
     if (nv > 0) {
       const char* region = buf + (wave >> 1) * 2 * Sh<D>::TILEB;
       q_tile<D>(region, region + Sh<D>::TILEB, nv, c2, st);
@@ -389,12 +391,17 @@ __global__ __launch_bounds__(kDqlThreads, 1) void dq_local_kernel(BwdArgs a) {
   }
   if (!ok) return;
   float* out = a.dq + (bh * g.ct + tok) * D;
+  float4 prev[Sh<D>::DT][4];  // the persistent part, all loads issued before the first use
+#pragma unroll
+  for (int dt = 0; dt < Sh<D>::DT; ++dt)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) prev[dt][i4] = *reinterpret_cast<const float4*>(out + 32 * dt + 8 * i4 + 4 * h);
 #pragma unroll
   for (int dt = 0; dt < Sh<D>::DT; ++dt)
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
       float4* o4 = reinterpret_cast<float4*>(out + 32 * dt + 8 * i4 + 4 * h);
-      float4 v = *o4;
+      float4 v = prev[dt][i4];
       v.x += st.acc[dt][4 * i4] * g.scale;
       v.y += st.acc[dt][4 * i4 + 1] * g.scale;
       v.z += st.acc[dt][4 * i4 + 2] * g.scale;
@@ -587,6 +594,76 @@ __global__ __launch_bounds__(kKvThreads, 2) void dkv_pers_kernel(BwdArgs a) {
 
 constexpr int kKvlThreads = 128;  // dkv_local: 2 waves = one local block
 
+// Query-tile gather of dkv_local, software-pipelined two steps deep.  A step
+// is one 32-row half of one query block that selected this local block; the
+// selecting blocks and their lengths sit in LDS (copied once).  Row tokens of
+// step i+2 are loaded while step i computes, so the Q / dO loads of step i+1
+// issue with ready addresses; rows past a block's end load token 0 and are
+// zeroed when staged into LDS.
+template <int D> struct GatherPipe {
+  static constexpr int NCH = 32 * Sh<D>::CPR;              // 16-byte chunks per tensor tile
+  static constexpr int N = (NCH + kKvlThreads - 1) / kKvlThreads;
+  int tok[N], tokl;            // raw row tokens of the next step to load
+  unsigned okm;                // bit u: chunk u is a valid row; bit N: row tid (lse / D) valid
+  int tok2[N], tokl2;          // ... of the step after
+  unsigned okm2;
+  uint4 q[N], d[N];            // Q / dO chunks of the next step
+  float l, dd;
+  unsigned okq;                // validity of q/d/l/dd
+
+  __device__ __forceinline__ static void tokens(const BwdArgs& a, const int* sel, const int* slen, int sidx,
+                                                int half, int* t, int& tl, unsigned& ok) {
+    const Geo& g = a.g;
+    const int tid = threadIdx.x;
+    const int len = slen[sidx];
+    const int32_t* rows = a.tab.btok + sel[sidx] * g.C;
+    ok = 0;
+#pragma unroll
+    for (int u = 0; u < N; ++u) {
+      const int id = tid + kKvlThreads * u, r = 32 * half + id / Sh<D>::CPR;
+      t[u] = rows[min(r, g.C - 1)];
+      if (id < NCH && r < len) ok |= 1u << u;
+    }
+    const int rl = 32 * half + (tid & 31);
+    tl = rows[min(rl, g.C - 1)];
+    if (tid < 32 && rl < len) ok |= 1u << N;
+  }
+  __device__ __forceinline__ void load(const BwdArgs& a, size_t bh) {
+    const Geo& g = a.g;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int u = 0; u < N; ++u) {
+      const int c = (tid + kKvlThreads * u) % Sh<D>::CPR;
+      const size_t off = (bh * g.ct + ((okm >> u) & 1 ? tok[u] : 0)) * (size_t)D + c * 8;
+      q[u] = ld16(a.q + off);
+      d[u] = ld16(a.dout + off);
+    }
+    const size_t ro = bh * g.ct + ((okm >> N) & 1 ? tokl : 0);
+    l = a.lse[ro];
+    dd = a.delta[ro];
+    okq = okm;
+  }
+  // LDS: Q tile, dO tile, lse2[32], D[32]
+  __device__ __forceinline__ void store(char* buf) const {
+    const int tid = threadIdx.x;
+    const uint4 z = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < N; ++u) {
+      const int id = tid + kKvlThreads * u, r = id / Sh<D>::CPR, c = id % Sh<D>::CPR;
+      if (id >= NCH) break;
+      const bool ok = (okq >> u) & 1;
+      st_chunk(buf, Sh<D>::ROWB, Sh<D>::CPR, r, c, ok ? q[u] : z);
+      st_chunk(buf + Sh<D>::TILEB, Sh<D>::ROWB, Sh<D>::CPR, r, c, ok ? d[u] : z);
+    }
+    if (tid < 32) {
+      const bool ok = (okq >> N) & 1;
+      float* f = reinterpret_cast<float*>(buf + 2 * Sh<D>::TILEB);
+      f[tid] = ok ? l * kLog2e : INFINITY;
+      f[32 + tid] = ok ? dd : 0.f;
+    }
+  }
+};
+
 template <int D, bool DV>
 __global__ __launch_bounds__(kKvlThreads, 2) void dkv_local_kernel(BwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -608,52 +685,58 @@ __global__ __launch_bounds__(kKvlThreads, 2) void dkv_local_kernel(BwdArgs a) {
   k_init<D, DV>(a.kl + krow, a.vl + krow, kok, st);
   const float c2 = g.scale * kLog2e;
 
+  // selecting query blocks (ascending) and their lengths, into LDS
   const int ncount = a.tcount[bh * g.nl + p];
   const int32_t* lst = a.tlist + (bh * g.nl + p) * g.nq;
-  struct Gather {  // rows 32*half .. of one selecting query block (token row table)
-    const int* rows;
-    int C, half;
-    __device__ int operator()(int i) const {
-      const int r = 32 * half + i;
-      return r < C ? rows[r] : -1;
-    }
-  };
-  // The selecting query blocks' row tokens can be copied once into LDS, but
-  // the extra LDS halves the resident workgroups of this 2-wave kernel and
-  // measured slower; the rows are read from the (L2-resident) global table.
-  constexpr bool use_tab = false;
-  int* qtab = reinterpret_cast<int*>(smem + 2 * BUF);
-  int* qlen = qtab + g.nq * 64;
-  if (use_tab) {
-    for (int x = threadIdx.x; x < ncount * 64; x += kKvlThreads) {
-      const int sidx = x >> 6, r = x & 63, blk = lst[sidx];
-      qtab[x] = r < g.C ? a.tab.btok[blk * g.C + r] : -1;
-      if (r == 0) qlen[sidx] = a.tab.blen[blk];
-    }
-    __syncthreads();
+  int* sel = reinterpret_cast<int*>(smem + 2 * BUF);
+  int* slen = sel + g.nq;
+  for (int x = threadIdx.x; x < ncount; x += kKvlThreads) {
+    const int blk = lst[x];
+    sel[x] = blk;
+    slen[x] = a.tab.blen[blk];
   }
-  auto len_of = [&](int sidx) { return use_tab ? qlen[sidx] : a.tab.blen[lst[sidx]]; };
-  auto rows_of = [&](int sidx) -> const int* { return use_tab ? qtab + sidx * 64 : a.tab.btok + lst[sidx] * g.C; };
-  // steps: (selecting query block, half) pairs, in list order
+  __syncthreads();
   int nsteps = 0;
-  for (int sidx = 0; sidx < ncount; ++sidx) nsteps += (len_of(sidx) + 31) / 32;
+  for (int x = 0; x < ncount; ++x) nsteps += (slen[x] + 31) / 32;
   if (nsteps > 0) {
-    int cur = 0, half = 0;  // next step to load: list entry and half
-    int clen = len_of(0);
-    QTileLoader<D, kKvlThreads, Gather> pf;
-    pf.load(a, bh, Gather{rows_of(0), g.C, half});
+    // cursors of the steps whose tokens are held (next) and loading (after)
+    int c1 = 0, h1 = 0;
+    auto advance = [&](int& c, int& hh) {
+      if (32 * (hh + 1) < slen[c]) {
+        ++hh;
+      } else {
+        ++c;
+        hh = 0;
+      }
+    };
+    GatherPipe<D> pf;
+    GatherPipe<D>::tokens(a, sel, slen, 0, 0, pf.tok, pf.tokl, pf.okm);
+    pf.load(a, bh);
     pf.store(smem);
+    int c2i = c1, h2 = h1;
+    if (nsteps > 1) {
+      advance(c1, h1);
+      GatherPipe<D>::tokens(a, sel, slen, c1, h1, pf.tok, pf.tokl, pf.okm);
+      c2i = c1;
+      h2 = h1;
+    }
+    if (nsteps > 2) {
+      advance(c2i, h2);
+      GatherPipe<D>::tokens(a, sel, slen, c2i, h2, pf.tok2, pf.tokl2, pf.okm2);
+    }
     __syncthreads();
     for (int i = 0; i < nsteps; ++i) {
       char* buf = smem + (i & 1) * BUF;
-      if (i + 1 < nsteps) {
-        if (32 * (half + 1) < clen) {
-          ++half;
-        } else {
-          clen = len_of(++cur);
-          half = 0;
+      if (i + 1 < nsteps) pf.load(a, bh);  // step i+1, tokens ready
+      if (i + 2 < nsteps) {
+#pragma unroll
+        for (int u = 0; u < GatherPipe<D>::N; ++u) pf.tok[u] = pf.tok2[u];
+        pf.tokl = pf.tokl2;
+        pf.okm = pf.okm2;
+        if (i + 3 < nsteps) {
+          advance(c2i, h2);
+          GatherPipe<D>::tokens(a, sel, slen, c2i, h2, pf.tok2, pf.tokl2, pf.okm2);
         }
-        pf.load(a, bh, Gather{rows_of(cur), g.C, half});
       }
       if (nk > 0) {
         const float* f = reinterpret_cast<const float*>(buf + 2 * Sh<D>::TILEB);
@@ -683,19 +766,21 @@ hipError_t launch_d(const BwdArgs& base, hipStream_t s) {
   const Geo& g = base.g;
   const size_t shm_dq = 2 * 4 * Sh<D>::TILEB;                 // persistent: 2 x (K,K,V,V)
   const size_t tabb = (size_t)kLocBlocks * g.K * 64 * 4;
+  const bool tab = tabb <= (size_t)kRowTabMax;
   const size_t shm_dql = 2 * kLocBlocks * 2 * Sh<D>::TILEB +   // local: 2 x 4 x (K,V)
-                         (tabb <= (size_t)kRowTabMax ? tabb + kLocBlocks * g.K * 4 : 0);
+                         (tab ? tabb + kLocBlocks * g.K * 4 : 0);
   const size_t shm_kv = 2 * (2 * Sh<D>::TILEB + 256);
-  const size_t shm_kvl = shm_kv;
+  const size_t shm_kvl = shm_kv + 2 * (size_t)g.nq * 4;     // + selecting blocks and their lengths
   static bool attr = false;
   if (!attr) {
     hipError_t e = set_lds(dq_pers_kernel<D>, shm_dq);
     if (e == hipSuccess)
-      e = set_lds(dq_local_kernel<D>, 2 * kLocBlocks * 2 * Sh<D>::TILEB + kRowTabMax + 4096);
+      e = set_lds(dq_local_kernel<D, true>, 2 * kLocBlocks * 2 * Sh<D>::TILEB + kRowTabMax + 4096);
+    if (e == hipSuccess) e = set_lds(dq_local_kernel<D, false>, 2 * kLocBlocks * 2 * Sh<D>::TILEB);
     if (e == hipSuccess) e = set_lds(dkv_pers_kernel<D, true>, shm_kv);
     if (e == hipSuccess) e = set_lds(dkv_pers_kernel<D, false>, shm_kv);
-    if (e == hipSuccess) e = set_lds(dkv_local_kernel<D, true>, shm_kv);
-    if (e == hipSuccess) e = set_lds(dkv_local_kernel<D, false>, shm_kv);
+    if (e == hipSuccess) e = set_lds(dkv_local_kernel<D, true>, shm_kv + 2 * 2048 * 4);
+    if (e == hipSuccess) e = set_lds(dkv_local_kernel<D, false>, shm_kv + 2 * 2048 * 4);
     if (e != hipSuccess) return e;
     attr = true;
   }
@@ -708,7 +793,10 @@ hipError_t launch_d(const BwdArgs& base, hipStream_t s) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   a.ntiles = (g.nq + kLocBlocks - 1) / kLocBlocks;
   total = g.B * g.H * a.ntiles;
-  dq_local_kernel<D><<<((total + 7) / 8) * 8, kDqlThreads, shm_dql, s>>>(a);
+  if (tab)
+    dq_local_kernel<D, true><<<((total + 7) / 8) * 8, kDqlThreads, shm_dql, s>>>(a);
+  else
+    dq_local_kernel<D, false><<<((total + 7) / 8) * 8, kDqlThreads, shm_dql, s>>>(a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (g.S > 0) {
     a.ntiles = (g.S + kKvSlots - 1) / kKvSlots;

@@ -109,16 +109,17 @@ hipError_t launch_score_select(const Geo& g, const void* q, const void* k_l, con
                                const float* kbar_p, const int32_t* plen, int32_t* topk, float* mass,
                                float* kbar_l, WsScore ws, hipStream_t s);
 // blse_p / blse_l: NULL, or [B,H,S,ct] / [B,H,K,ct] outputs of each query's
-// log-sum-exp over each persistent slot / each of its selected local blocks
-// (-inf where the slot or block holds no valid row).
+// log-sum-exp over each persistent slot / each of its selected local blocks,
+// in base 2 (log2 of the sum of exp of the scaled scores; -inf where the slot
+// or block holds no valid row).
 hipError_t launch_fwd(const Geo& g, const void* q, const void* k_p, const void* v_p, const int32_t* plen,
                       const void* k_l, const void* v_l, const int32_t* topk, void* o, float* lse, void* ws,
                       float* blse_p, float* blse_l, hipStream_t s);
 size_t fwd_workspace(const Geo& g);
-// Token-exact mass from the block log-sum-exps and the final LSE:
-// mass[s] = sum_t exp(blse_p[s][t] - lse[t]); mass[S+p] = sum over query
-// blocks i and their selections k with topk[i][k] = p of sum_{t in i}
-// exp(blse_l[k][t] - lse[t]).  part: [B,H,nq,nl] float scratch.
+// Token-exact mass from the block log-sum-exps and the final LSE (natural
+// log): mass[s] = sum_t 2^(blse_p[s][t] - lse[t]*log2e); mass[S+p] = sum over
+// query blocks i and their selections k with topk[i][k] = p of
+// sum_{t in i} 2^(blse_l[k][t] - lse[t]*log2e).  part: [B,H,nq,nl] scratch.
 hipError_t launch_token_mass(const Geo& g, const int32_t* plen, const int32_t* topk, const float* lse,
                              const float* blse_p, const float* blse_l, float* part, float* mass, hipStream_t s);
 struct WsBwd {

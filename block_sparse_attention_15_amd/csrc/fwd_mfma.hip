@@ -38,9 +38,10 @@
 //    read by one or two XCDs instead of all eight.
 //  * Optional (MASS): for the token-exact attention mass, each query also
 //    writes the log-sum-exp of its scores over every persistent slot and
-//    every selected local block.  The tile already forms the row sum of its
-//    probabilities (relative to the running max) for the online softmax, so
-//    this costs one lane exchange and one log per (query, block).
+//    every selected local block (base 2, in the units of the running max).
+//    The tile already forms the row sum of its probabilities (relative to the
+//    running max) for the online softmax, so this costs one lane exchange and
+//    one native log2 per (query, block).
 #include "common.h"
 
 namespace pbsa {
@@ -87,7 +88,7 @@ struct FwdArgs {
   float* lse;
   float* o_part;    // [B,H,ct,D] persistent-part output (normalised), fp32
   float* lse_part;  // [B,H,ct]   its log-sum-exp (-inf when no slot is valid)
-  float* blse_p;    // MASS: [B,H,S,ct] log-sum-exp of each query over each slot's rows
+  float* blse_p;    // MASS: [B,H,S,ct] log2-sum-exp2 of each query's scaled scores (log2 units) over each slot's rows
   float* blse_l;    // MASS: [B,H,K,ct] ... over each of its selected local blocks
   GeoTab tab;       // geometry lookup tables
   int ntiles;       // work items per (batch, head)
@@ -293,8 +294,9 @@ __global__ __launch_bounds__(kPersThreads, 1) void fwd_pers_kernel(FwdArgs a) {
       char* buf = smem + (s & 1) * kBufBytes;
       const int n = min(a.plen[bh * g.S + s], g.C);
       if (s + 1 < g.S) pers_load<D>(a, bh, s + 1, pf);
+      float bl = 0.f;  // MASS: log2-sum-exp2 over the slot
       if (ntq > 0) {
-        float bs = 0.f;  // this lane's probability sum over the slot (MASS)
+        float bs = 0.f;  // this lane's probability sum over the slot
         if (n > 0) bs = tile<D, kPersNT>(buf, buf + 64 * Sh::ROWB, 0, min(n, 32), ntq, c2, st);
         if (n > 32) {
           const float m0 = st.m[0];
@@ -303,12 +305,12 @@ __global__ __launch_bounds__(kPersThreads, 1) void fwd_pers_kernel(FwdArgs a) {
         }
         if (MASS) {
           const float tot = half_sum(bs);
-          const int r = row_w + l32;
-          if (h == 0 && r < g.ct)
-            a.blse_p[(bh * g.S + s) * g.ct + r] = tot > 0.f ? st.m[0] * kLn2 + logf(tot) : -INFINITY;
+          bl = tot > 0.f ? st.m[0] + __builtin_amdgcn_logf(tot) : -INFINITY;
         }
       }
       if (s + 1 < g.S) pers_store<D>(pf, smem + ((s + 1) & 1) * kBufBytes);
+      // stored after the LDS fill so that its wait for the prefetch does not also wait for this store
+      if (MASS && ntq > 0 && h == 0 && row_w + l32 < g.ct) a.blse_p[(bh * g.S + s) * g.ct + row_w + l32] = bl;
       __syncthreads();
     }
   }
@@ -376,7 +378,10 @@ __device__ __forceinline__ void build_rowtab(const FwdArgs& a, size_t bh, int qg
   }
 }
 
-template <int D>
+// TAB: row addresses come from the LDS row table.  Kept a compile-time
+// choice: if the global-memory address path shares the loop, the compiler
+// joins the two with a full vmcnt wait that also drains the K/V prefetch.
+template <int D, bool TAB>
 __device__ __forceinline__ void loc_load(const FwdArgs& a, size_t bh, int qg, int j, LocPrefetch<D>& pf,
                                          const int* rowtab) {
   using Sh = Shape<D>;
@@ -392,7 +397,7 @@ __device__ __forceinline__ void loc_load(const FwdArgs& a, size_t bh, int qg, in
     const int qb = qg * kLocBlocks + w;
     bool ok = false;
     size_t off = 0;
-    if (rowtab) {
+    if (TAB) {
       const int tok = rowtab[(w * g.K + t) * 64 + r];
       ok = tok >= 0;
       off = (size_t)(ok ? tok : 0) * D + c * 8;
@@ -425,7 +430,7 @@ __device__ __forceinline__ void loc_store(const LocPrefetch<D>& pf, char* buf) {
   }
 }
 
-template <int D, bool MASS>
+template <int D, bool MASS, bool TAB>
 __global__ __launch_bounds__(kLocThreads, 1) void fwd_local_kernel(FwdArgs a) {
   using Sh = Shape<D>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -450,15 +455,14 @@ __global__ __launch_bounds__(kLocThreads, 1) void fwd_local_kernel(FwdArgs a) {
   const float c2 = g.scale * 1.4426950408889634f;
 
   const int nsteps = 2 * g.K;
-  const bool use_tab = kLocBlocks * g.K * 64 * 4 <= kRowTabMax;
-  int* rowtab = use_tab ? reinterpret_cast<int*>(smem + 2 * kBufBytes) : nullptr;
+  int* rowtab = reinterpret_cast<int*>(smem + 2 * kBufBytes);
   int* lentab = rowtab + kLocBlocks * g.K * 64;
-  if (use_tab) {
+  if (TAB) {
     build_rowtab(a, bh, qg, kLocThreads, rowtab, lentab);
     __syncthreads();
   }
   LocPrefetch<D> pf;
-  loc_load<D>(a, bh, qg, 0, pf, rowtab);
+  loc_load<D, TAB>(a, bh, qg, 0, pf, rowtab);
   loc_store<D>(pf, smem);
   __syncthreads();
   float bs = 0.f;  // this lane's probability sum over the current selected block (MASS)
@@ -467,7 +471,7 @@ __global__ __launch_bounds__(kLocThreads, 1) void fwd_local_kernel(FwdArgs a) {
     int nv = 0;
     if (ntq) {
       int len = 0;
-      if (use_tab) {
+      if (TAB) {
         len = lentab[(wave >> 1) * g.K + (j >> 1)];
       } else {
         const int p = a.topk[(bh * g.nq + qb) * g.K + (j >> 1)];
@@ -475,7 +479,7 @@ __global__ __launch_bounds__(kLocThreads, 1) void fwd_local_kernel(FwdArgs a) {
       }
       nv = min(len - 32 * (j & 1), 32);
     }
-    if (j + 1 < nsteps) loc_load<D>(a, bh, qg, j + 1, pf, rowtab);
+    if (j + 1 < nsteps) loc_load<D, TAB>(a, bh, qg, j + 1, pf, rowtab);
     if (nv > 0) {
       const char* region = buf + (wave >> 1) * (64 * Sh::ROWB);
       const float m0 = st.m[0];
@@ -484,12 +488,14 @@ __global__ __launch_bounds__(kLocThreads, 1) void fwd_local_kernel(FwdArgs a) {
     } else if (MASS && !(j & 1)) {
       bs = 0.f;
     }
+    float bl = 0.f;
     if (MASS && (j & 1) && ntq) {
       const float tot = half_sum(bs);
-      if (h == 0 && row_ok)
-        a.blse_l[(bh * g.K + (j >> 1)) * g.ct + tok] = tot > 0.f ? st.m[0] * kLn2 + logf(tot) : -INFINITY;
+      bl = tot > 0.f ? st.m[0] + __builtin_amdgcn_logf(tot) : -INFINITY;
     }
     if (j + 1 < nsteps) loc_store<D>(pf, smem + ((j + 1) & 1) * kBufBytes);
+    // stored after the LDS fill (its wait for the prefetch must not wait for this store)
+    if (MASS && (j & 1) && ntq && h == 0 && row_ok) a.blse_l[(bh * g.K + (j >> 1)) * g.ct + tok] = bl;
     __syncthreads();
   }
 
@@ -507,12 +513,18 @@ __global__ __launch_bounds__(kLocThreads, 1) void fwd_local_kernel(FwdArgs a) {
   const float fp = wp / den;
   const float* op = a.o_part + row * D;
   bf16_t* orow = a.o + row * D;
+  float4 pvs[Sh::DT][4];  // all loads issued before the first use
+#pragma unroll
+  for (int dt = 0; dt < Sh::DT; ++dt) {
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) pvs[dt][i4] = *reinterpret_cast<const float4*>(op + 32 * dt + 8 * i4 + 4 * h);
+  }
 #pragma unroll
   for (int dt = 0; dt < Sh::DT; ++dt) {
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
       const int d0 = 32 * dt + 8 * i4 + 4 * h;
-      const float4 pv = *reinterpret_cast<const float4*>(op + d0);
+      const float4 pv = pvs[dt][i4];
       uint2 w;
       w.x = (uint32_t)f2bf(fmaf(st.o[0][dt][4 * i4 + 0], fl, pv.x * fp)) |
             ((uint32_t)f2bf(fmaf(st.o[0][dt][4 * i4 + 1], fl, pv.y * fp)) << 16);
@@ -535,10 +547,12 @@ hipError_t launch_d(const FwdArgs& base, hipStream_t s) {
   const size_t shm = 2 * kBufBytes;
   const Geo& g0 = base.g;
   const size_t tabb = (size_t)kLocBlocks * g0.K * 64 * 4;
-  const size_t shm_loc = shm + (tabb <= (size_t)kRowTabMax ? tabb + kLocBlocks * g0.K * 4 : 0);
+  const bool tab = tabb <= (size_t)kRowTabMax;
+  const size_t shm_loc = shm + (tab ? tabb + kLocBlocks * g0.K * 4 : 0);
   if (!attr) {
     hipError_t e = set_lds(fwd_pers_kernel<D, MASS>, shm);
-    if (e == hipSuccess) e = set_lds(fwd_local_kernel<D, MASS>, shm + kRowTabMax + 4096);
+    if (e == hipSuccess) e = set_lds(fwd_local_kernel<D, MASS, true>, shm + kRowTabMax + 4096);
+    if (e == hipSuccess) e = set_lds(fwd_local_kernel<D, MASS, false>, shm);
     if (e != hipSuccess) return e;
     attr = true;
   }
@@ -551,7 +565,10 @@ hipError_t launch_d(const FwdArgs& base, hipStream_t s) {
   if (e != hipSuccess) return e;
   a.ntiles = (g.nq + kLocBlocks - 1) / kLocBlocks;
   total = g.B * g.H * a.ntiles;
-  fwd_local_kernel<D, MASS><<<((total + 7) / 8) * 8, kLocThreads, shm_loc, s>>>(a);
+  if (tab)
+    fwd_local_kernel<D, MASS, true><<<((total + 7) / 8) * 8, kLocThreads, shm_loc, s>>>(a);
+  else
+    fwd_local_kernel<D, MASS, false><<<((total + 7) / 8) * 8, kLocThreads, shm_loc, s>>>(a);
   return hipGetLastError();
 }
 

@@ -8,8 +8,8 @@
 // blocks).  One workgroup per (query block, head, batch); one lane per query
 // token; key/value tiles of up to 64 rows are staged through LDS and read as
 // broadcasts.  Online softmax in fp32.  Optionally (blse_p non-null) writes
-// each query's log-sum-exp over every slot and selected block, the input of
-// the token-exact attention mass.
+// each query's log-sum-exp over every slot and selected block, in base 2, the
+// input of the token-exact attention mass.
 #include "common.h"
 
 namespace pbsa {
@@ -105,7 +105,7 @@ __global__ __launch_bounds__(64) void fwd_simple_kernel(Geo g, const T* __restri
       }
       m = mn;
     }
-    if (blse) *blse = bsum > 0.f ? m + logf(bsum) : -INFINITY;
+    if (blse) *blse = bsum > 0.f ? (m + logf(bsum)) * 1.4426950408889634f : -INFINITY;  // log2 units
   }
   if (!active) return;
   const float inv = 1.0f / l;

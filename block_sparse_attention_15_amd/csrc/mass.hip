@@ -8,22 +8,24 @@
 // selected local blocks) puts on j's rows.
 //
 // The forward leaves, for every query t and every block j it attends, the
-// log-sum-exp of t's scores over j's rows (blse); with t's full log-sum-exp
-// (lse) that probability is exp(blse - lse).  Three small HBM-bound kernels
-// reduce it, in a fixed order (no atomics, so the result is deterministic):
+// log-sum-exp of t's scores over j's rows (blse, base 2); with t's full
+// log-sum-exp (lse, natural log) that probability is 2^(blse - lse*log2 e).
+// Three small HBM-bound kernels reduce it, in a fixed order (no atomics, so
+// the result is deterministic):
 //   * tmass_pers: one workgroup per (slot, head, batch) sums over the chunk's
 //     queries;
 //   * tmass_part: one workgroup per (query block, head, batch) sums over the
 //     block's queries for each of its K selections, then scatters the K sums
 //     to a dense row part[i][p] (zeros elsewhere);
 //   * tmass_local: one thread per (local block, head, batch) adds its column
-//     of part over the query blocks, ascending.
+//     of part over the query blocks, ascending (loads issued eight at a time).
 #include "common.h"
 
 namespace pbsa {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -42,7 +44,7 @@ __global__ __launch_bounds__(kThreads) void tmass_pers_kernel(Geo g, const int32
   const float* ls = lse + bh * g.ct;
   float acc = 0.f;
   if (plen[bh * g.S + s] > 0)
-    for (int t = threadIdx.x; t < g.ct; t += kThreads) acc += expf(bl[t] - ls[t]);
+    for (int t = threadIdx.x; t < g.ct; t += kThreads) acc += exp2f(bl[t] - ls[t] * kLog2e);
   acc = wave_sum(acc);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
   __syncthreads();
@@ -72,7 +74,7 @@ __global__ __launch_bounds__(kThreads) void tmass_part_kernel(Geo g, const int32
     float acc = 0.f;
     for (int r = lane; r < e.len; r += 64) {
       const int t = block_token(g, e, r);
-      acc += expf(bl[t] - ls[t]);
+      acc += exp2f(bl[t] - ls[t] * kLog2e);
     }
     acc = wave_sum(acc);
     if (lane == 0) sums[k] = acc;
@@ -90,14 +92,24 @@ __global__ __launch_bounds__(kThreads) void tmass_part_kernel(Geo g, const int32
   for (int x = threadIdx.x; x < g.nl; x += kThreads) out[x] = row[x];
 }
 
-__global__ __launch_bounds__(kThreads) void tmass_local_kernel(Geo g, const float* __restrict__ part,
-                                                               float* __restrict__ mass) {
-  const int p = blockIdx.x * kThreads + threadIdx.x;
+constexpr int kLocalThreads = 64;
+
+__global__ __launch_bounds__(kLocalThreads) void tmass_local_kernel(Geo g, const float* __restrict__ part,
+                                                                    float* __restrict__ mass) {
+  const int p = blockIdx.x * kLocalThreads + threadIdx.x;
   const size_t bh = blockIdx.y;
   if (p >= g.nl) return;
   const float* col = part + bh * g.nq * (size_t)g.nl + p;
   float acc = 0.f;
-  for (int i = 0; i < g.nq; ++i) acc += col[(size_t)i * g.nl];
+  int i = 0;
+  for (; i + 8 <= g.nq; i += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = col[(size_t)(i + u) * g.nl];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc += v[u];
+  }
+  for (; i < g.nq; ++i) acc += col[(size_t)i * g.nl];
   mass[bh * (g.S + g.nl) + g.S + p] = acc;
 }
 
@@ -114,7 +126,8 @@ hipError_t launch_token_mass(const Geo& g, const int32_t* plen, const int32_t* t
   tmass_part_kernel<<<dim3(g.nq, g.H, g.B), kThreads, 0, s>>>(g, topk, lse, blse_l, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  tmass_local_kernel<<<dim3((g.nl + kThreads - 1) / kThreads, g.B * g.H), kThreads, 0, s>>>(g, part, mass);
+  tmass_local_kernel<<<dim3((g.nl + kLocalThreads - 1) / kLocalThreads, g.B * g.H), kLocalThreads, 0, s>>>(g, part,
+                                                                                                         mass);
   return hipGetLastError();
 }
 
