@@ -592,35 +592,42 @@ __global__ __launch_bounds__(kKvThreads, 2) void dkv_pers_kernel(BwdArgs a) {
   });
 }
 
-constexpr int kKvlThreads = 128;  // dkv_local: 2 waves = one local block
+// dkv_local: one local block (64 keys = 2 key tiles) per workgroup and two
+// query streams that take the steps alternately, 4 waves in all; the two
+// partial accumulators are added in a fixed order at the end.  Splitting the
+// steps halves the longest workgroups: a block chosen by many query blocks
+// would otherwise set the end of the launch.
+constexpr int kKvlStreamThreads = 128;
+constexpr int kKvlThreads = 2 * kKvlStreamThreads;
 
-// Query-tile gather of dkv_local, software-pipelined two steps deep.  A step
+// Query-tile gather of one stream, software-pipelined two steps deep.  A step
 // is one 32-row half of one query block that selected this local block; the
-// selecting blocks and their lengths sit in LDS (copied once).  Row tokens of
-// step i+2 are loaded while step i computes, so the Q / dO loads of step i+1
-// issue with ready addresses; rows past a block's end load token 0 and are
-// zeroed when staged into LDS.
+// step list and the selecting blocks' lengths sit in LDS.  Row tokens of the
+// stream's step after next are loaded while it computes, so the Q / dO loads
+// of its next step issue with ready addresses; rows past a block's end load
+// token 0 and are zeroed when staged into LDS.
 template <int D> struct GatherPipe {
   static constexpr int NCH = 32 * Sh<D>::CPR;              // 16-byte chunks per tensor tile
-  static constexpr int N = (NCH + kKvlThreads - 1) / kKvlThreads;
+  static constexpr int N = (NCH + kKvlStreamThreads - 1) / kKvlStreamThreads;
   int tok[N], tokl;            // raw row tokens of the next step to load
-  unsigned okm;                // bit u: chunk u is a valid row; bit N: row tid (lse / D) valid
+  unsigned okm;                // bit u: chunk u is a valid row; bit N: row (lse / D) valid
   int tok2[N], tokl2;          // ... of the step after
   unsigned okm2;
   uint4 q[N], d[N];            // Q / dO chunks of the next step
   float l, dd;
   unsigned okq;                // validity of q/d/l/dd
 
-  __device__ __forceinline__ static void tokens(const BwdArgs& a, const int* sel, const int* slen, int sidx,
-                                                int half, int* t, int& tl, unsigned& ok) {
+  // step = (selecting-list index << 1) | half
+  __device__ __forceinline__ static void tokens(const BwdArgs& a, const int* sel, const int* slen, int step,
+                                                int tid, int* t, int& tl, unsigned& ok) {
     const Geo& g = a.g;
-    const int tid = threadIdx.x;
+    const int sidx = step >> 1, half = step & 1;
     const int len = slen[sidx];
     const int32_t* rows = a.tab.btok + sel[sidx] * g.C;
     ok = 0;
 #pragma unroll
     for (int u = 0; u < N; ++u) {
-      const int id = tid + kKvlThreads * u, r = 32 * half + id / Sh<D>::CPR;
+      const int id = tid + kKvlStreamThreads * u, r = 32 * half + id / Sh<D>::CPR;
       t[u] = rows[min(r, g.C - 1)];
       if (id < NCH && r < len) ok |= 1u << u;
     }
@@ -628,12 +635,11 @@ template <int D> struct GatherPipe {
     tl = rows[min(rl, g.C - 1)];
     if (tid < 32 && rl < len) ok |= 1u << N;
   }
-  __device__ __forceinline__ void load(const BwdArgs& a, size_t bh) {
+  __device__ __forceinline__ void load(const BwdArgs& a, size_t bh, int tid) {
     const Geo& g = a.g;
-    const int tid = threadIdx.x;
 #pragma unroll
     for (int u = 0; u < N; ++u) {
-      const int c = (tid + kKvlThreads * u) % Sh<D>::CPR;
+      const int c = (tid + kKvlStreamThreads * u) % Sh<D>::CPR;
       const size_t off = (bh * g.ct + ((okm >> u) & 1 ? tok[u] : 0)) * (size_t)D + c * 8;
       q[u] = ld16(a.q + off);
       d[u] = ld16(a.dout + off);
@@ -643,13 +649,18 @@ template <int D> struct GatherPipe {
     dd = a.delta[ro];
     okq = okm;
   }
+  __device__ __forceinline__ void shift() {
+#pragma unroll
+    for (int u = 0; u < N; ++u) tok[u] = tok2[u];
+    tokl = tokl2;
+    okm = okm2;
+  }
   // LDS: Q tile, dO tile, lse2[32], D[32]
-  __device__ __forceinline__ void store(char* buf) const {
-    const int tid = threadIdx.x;
+  __device__ __forceinline__ void store(char* buf, int tid) const {
     const uint4 z = make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int u = 0; u < N; ++u) {
-      const int id = tid + kKvlThreads * u, r = id / Sh<D>::CPR, c = id % Sh<D>::CPR;
+      const int id = tid + kKvlStreamThreads * u, r = id / Sh<D>::CPR, c = id % Sh<D>::CPR;
       if (id >= NCH) break;
       const bool ok = (okq >> u) & 1;
       st_chunk(buf, Sh<D>::ROWB, Sh<D>::CPR, r, c, ok ? q[u] : z);
@@ -664,6 +675,10 @@ template <int D> struct GatherPipe {
   }
 };
 
+template <int D> constexpr size_t kvl_lds(int nq) {
+  return 4 * (2 * (size_t)Sh<D>::TILEB + 256) + 4 * (size_t)nq * 4;
+}
+
 template <int D, bool DV>
 __global__ __launch_bounds__(kKvlThreads, 2) void dkv_local_kernel(BwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -675,21 +690,24 @@ __global__ __launch_bounds__(kKvlThreads, 2) void dkv_local_kernel(BwdArgs a) {
   const int p = lin % g.nl;
   const size_t bh = lin / g.nl;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31;
+  const int kt = wave & 1, stream = wave >> 1;          // key tile, query stream
+  const int stid = threadIdx.x & (kKvlStreamThreads - 1);
   const BlockExt ke = block_ext(g, p % g.nq);
   const int koff = (p / g.nq) * g.ct;
-  const int nk = min(max(ke.len - 32 * wave, 0), 32);
-  const int kr = 32 * wave + l32;
+  const int nk = min(max(ke.len - 32 * kt, 0), 32);
+  const int kr = 32 * kt + l32;
   const bool kok = kr < ke.len;
   const size_t krow = (bh * g.NL + koff + (kok ? block_token(g, ke, kr) : 0)) * (size_t)D;
   KState<D, DV> st;
   k_init<D, DV>(a.kl + krow, a.vl + krow, kok, st);
   const float c2 = g.scale * kLog2e;
 
-  // selecting query blocks (ascending) and their lengths, into LDS
+  // selecting query blocks (ascending), their lengths and the step list, in LDS
   const int ncount = a.tcount[bh * g.nl + p];
   const int32_t* lst = a.tlist + (bh * g.nl + p) * g.nq;
-  int* sel = reinterpret_cast<int*>(smem + 2 * BUF);
+  int* sel = reinterpret_cast<int*>(smem + 4 * BUF);
   int* slen = sel + g.nq;
+  int* steps = slen + g.nq;
   for (int x = threadIdx.x; x < ncount; x += kKvlThreads) {
     const int blk = lst[x];
     sel[x] = blk;
@@ -697,59 +715,56 @@ __global__ __launch_bounds__(kKvlThreads, 2) void dkv_local_kernel(BwdArgs a) {
   }
   __syncthreads();
   int nsteps = 0;
-  for (int x = 0; x < ncount; ++x) nsteps += (slen[x] + 31) / 32;
-  if (nsteps > 0) {
-    // cursors of the steps whose tokens are held (next) and loading (after)
-    int c1 = 0, h1 = 0;
-    auto advance = [&](int& c, int& hh) {
-      if (32 * (hh + 1) < slen[c]) {
-        ++hh;
-      } else {
-        ++c;
-        hh = 0;
-      }
-    };
-    GatherPipe<D> pf;
-    GatherPipe<D>::tokens(a, sel, slen, 0, 0, pf.tok, pf.tokl, pf.okm);
-    pf.load(a, bh);
-    pf.store(smem);
-    int c2i = c1, h2 = h1;
-    if (nsteps > 1) {
-      advance(c1, h1);
-      GatherPipe<D>::tokens(a, sel, slen, c1, h1, pf.tok, pf.tokl, pf.okm);
-      c2i = c1;
-      h2 = h1;
-    }
-    if (nsteps > 2) {
-      advance(c2i, h2);
-      GatherPipe<D>::tokens(a, sel, slen, c2i, h2, pf.tok2, pf.tokl2, pf.okm2);
-    }
-    __syncthreads();
-    for (int i = 0; i < nsteps; ++i) {
-      char* buf = smem + (i & 1) * BUF;
-      if (i + 1 < nsteps) pf.load(a, bh);  // step i+1, tokens ready
-      if (i + 2 < nsteps) {
-#pragma unroll
-        for (int u = 0; u < GatherPipe<D>::N; ++u) pf.tok[u] = pf.tok2[u];
-        pf.tokl = pf.tokl2;
-        pf.okm = pf.okm2;
-        if (i + 3 < nsteps) {
-          advance(c2i, h2);
-          GatherPipe<D>::tokens(a, sel, slen, c2i, h2, pf.tok2, pf.tokl2, pf.okm2);
-        }
-      }
-      if (nk > 0) {
-        const float* f = reinterpret_cast<const float*>(buf + 2 * Sh<D>::TILEB);
-        k_tile<D, DV>(buf, buf + Sh<D>::TILEB, f, f + 32, c2, st);
-      }
-      if (i + 1 < nsteps) pf.store(smem + ((i + 1) & 1) * BUF);
-      __syncthreads();
-    }
+  for (int x = 0; x < ncount; ++x) {
+    const int nh = (slen[x] + 31) / 32;
+    if (threadIdx.x < nh) steps[nsteps + threadIdx.x] = (x << 1) | threadIdx.x;
+    nsteps += nh;
   }
-  if (nk <= 0) return;
+  __syncthreads();
+  // this stream's steps: stream, stream + 2, ...
+  const int mine = nsteps > stream ? (nsteps - stream + 1) / 2 : 0;
+  const int iters = (nsteps + 1) / 2;
+  char* sbuf = smem + stream * 2 * BUF;
+  GatherPipe<D> pf;
+  if (mine > 0) {
+    GatherPipe<D>::tokens(a, sel, slen, steps[stream], stid, pf.tok, pf.tokl, pf.okm);
+    pf.load(a, bh, stid);
+    pf.store(sbuf, stid);
+    if (mine > 1) GatherPipe<D>::tokens(a, sel, slen, steps[stream + 2], stid, pf.tok, pf.tokl, pf.okm);
+    if (mine > 2) GatherPipe<D>::tokens(a, sel, slen, steps[stream + 4], stid, pf.tok2, pf.tokl2, pf.okm2);
+  }
+  __syncthreads();
+  for (int i = 0; i < iters; ++i) {
+    char* buf = sbuf + (i & 1) * BUF;
+    if (i + 1 < mine) pf.load(a, bh, stid);  // this stream's step i+1, tokens ready
+    if (i + 2 < mine) {
+      pf.shift();
+      if (i + 3 < mine) GatherPipe<D>::tokens(a, sel, slen, steps[stream + 2 * (i + 3)], stid, pf.tok2, pf.tokl2, pf.okm2);
+    }
+    if (i < mine && nk > 0) {
+      const float* f = reinterpret_cast<const float*>(buf + 2 * Sh<D>::TILEB);
+      k_tile<D, DV>(buf, buf + Sh<D>::TILEB, f, f + 32, c2, st);
+    }
+    if (i + 1 < mine) pf.store(sbuf + ((i + 1) & 1) * BUF, stid);
+    __syncthreads();
+  }
+  // stream 1 hands its partial accumulator to stream 0 through LDS
+  float* xch = reinterpret_cast<float*>(smem) + kt * (32 * D);
+  if (stream == 1) {
+#pragma unroll
+    for (int dt = 0; dt < Sh<D>::DT; ++dt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) xch[(dt * 16 + j) * 64 + lane] = st.acc[dt][j];
+  }
+  __syncthreads();
+  if (stream == 1 || nk <= 0) return;
+#pragma unroll
+  for (int dt = 0; dt < Sh<D>::DT; ++dt)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) st.acc[dt][j] += xch[(dt * 16 + j) * 64 + lane];
   float* ob = (DV ? a.dvl : a.dkl) + (bh * g.NL + koff) * (size_t)D;
   k_write<D, DV>(st, nk, DV ? 1.0f : g.scale, [&](int r, float*& dst) {
-    const int row = 32 * wave + r;
+    const int row = 32 * kt + r;
     if (row >= ke.len) return false;
     dst = ob + (size_t)block_token(g, ke, row) * D;
     return true;
@@ -770,7 +785,7 @@ hipError_t launch_d(const BwdArgs& base, hipStream_t s) {
   const size_t shm_dql = 2 * kLocBlocks * 2 * Sh<D>::TILEB +   // local: 2 x 4 x (K,V)
                          (tab ? tabb + kLocBlocks * g.K * 4 : 0);
   const size_t shm_kv = 2 * (2 * Sh<D>::TILEB + 256);
-  const size_t shm_kvl = shm_kv + 2 * (size_t)g.nq * 4;     // + selecting blocks and their lengths
+  const size_t shm_kvl = kvl_lds<D>(g.nq);
   static bool attr = false;
   if (!attr) {
     hipError_t e = set_lds(dq_pers_kernel<D>, shm_dq);
@@ -779,8 +794,8 @@ hipError_t launch_d(const BwdArgs& base, hipStream_t s) {
     if (e == hipSuccess) e = set_lds(dq_local_kernel<D, false>, 2 * kLocBlocks * 2 * Sh<D>::TILEB);
     if (e == hipSuccess) e = set_lds(dkv_pers_kernel<D, true>, shm_kv);
     if (e == hipSuccess) e = set_lds(dkv_pers_kernel<D, false>, shm_kv);
-    if (e == hipSuccess) e = set_lds(dkv_local_kernel<D, true>, shm_kv + 2 * 2048 * 4);
-    if (e == hipSuccess) e = set_lds(dkv_local_kernel<D, false>, shm_kv + 2 * 2048 * 4);
+    if (e == hipSuccess) e = set_lds(dkv_local_kernel<D, true>, kvl_lds<D>(2048));
+    if (e == hipSuccess) e = set_lds(dkv_local_kernel<D, false>, kvl_lds<D>(2048));
     if (e != hipSuccess) return e;
     attr = true;
   }
