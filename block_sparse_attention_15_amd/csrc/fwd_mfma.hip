@@ -119,12 +119,35 @@ __device__ __forceinline__ float tile(const char* kbase, const char* vbase, int 
   {
     const int r = row0 + l32;
     const char* krow = kbase + r * Sh::ROWB;
+    bf16x8_t ka[Sh::KS];  // all K operands issued before the first product
+#pragma unroll
+    for (int ks = 0; ks < Sh::KS; ++ks)
+      ka[ks] = *reinterpret_cast<const bf16x8_t*>(krow + swz_k(r, 2 * ks + h, Sh::CPR) * 16);
 #pragma unroll
     for (int ks = 0; ks < Sh::KS; ++ks) {
-      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(krow + swz_k(r, 2 * ks + h, Sh::CPR) * 16);
 #pragma unroll
       for (int n = 0; n < NT; ++n)
-        if (n < ntq) s[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.qf[n][ks], s[n], 0, 0, 0);
+        if (n < ntq) s[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], st.qf[n][ks], s[n], 0, 0, 0);
+    }
+  }
+  // V^T operands of O^T += V^T P^T, read transposed from LDS now: they do
+  // not depend on P, so their latency is covered by the softmax below
+  const int G = lane >> 4, s16 = lane & 15;
+  bf16x8_t va[Sh::DT][2];
+#pragma unroll
+  for (int dt = 0; dt < Sh::DT; ++dt) {
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2) {
+      s16x4_t part[2];
+#pragma unroll
+      for (int h8 = 0; h8 < 2; ++h8) {
+        const int r = row0 + 16 * ks2 + 8 * h8 + 4 * (G >> 1) + (s16 >> 2);
+        const int col = 32 * dt + 16 * (G & 1) + 4 * (s16 & 3);
+        const char* p = vbase + r * Sh::ROWB + swz_v(r, col >> 3, Sh::CPR) * 16 + (col & 7) * 2;
+        part[h8] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(p));
+      }
+      va[dt][ks2] = __builtin_bit_cast(bf16x8_t, (__attribute__((ext_vector_type(8))) short){
+          part[0][0], part[0][1], part[0][2], part[0][3], part[1][0], part[1][1], part[1][2], part[1][3]});
     }
   }
   if (nvalid < 32) {
@@ -167,25 +190,14 @@ __device__ __forceinline__ float tile(const char* kbase, const char* vbase, int 
       if (n == 0) ret = ls;
     }
   }
-  // O^T += V^T P^T; A = V^T (d x keys) read transposed from LDS
-  const int G = lane >> 4, s16 = lane & 15;
+  // O^T += V^T P^T
 #pragma unroll
   for (int dt = 0; dt < Sh::DT; ++dt) {
 #pragma unroll
     for (int ks2 = 0; ks2 < 2; ++ks2) {
-      s16x4_t part[2];
-#pragma unroll
-      for (int h8 = 0; h8 < 2; ++h8) {
-        const int r = row0 + 16 * ks2 + 8 * h8 + 4 * (G >> 1) + (s16 >> 2);
-        const int col = 32 * dt + 16 * (G & 1) + 4 * (s16 & 3);
-        const char* p = vbase + r * Sh::ROWB + swz_v(r, col >> 3, Sh::CPR) * 16 + (col & 7) * 2;
-        part[h8] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(p));
-      }
-      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, (__attribute__((ext_vector_type(8))) short){
-          part[0][0], part[0][1], part[0][2], part[0][3], part[1][0], part[1][1], part[1][2], part[1][3]});
 #pragma unroll
       for (int n = 0; n < NT; ++n)
-        if (n < ntq) st.o[n][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[n][ks2], st.o[n][dt], 0, 0, 0);
+        if (n < ntq) st.o[n][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[dt][ks2], pk[n][ks2], st.o[n][dt], 0, 0, 0);
     }
   }
   return ret;
