@@ -120,6 +120,13 @@ struct BwdArgs {
   int ntiles;
 };
 
+// Which tiles read their transposed operands ahead of the VALU work (only
+// where the registers allow it without spilling).
+constexpr bool kHoistDqPers = true;
+constexpr bool kHoistDqLocal = false;
+template <bool DV> constexpr bool kHoistKvPers = true;
+template <bool DV> constexpr bool kHoistKvLocal = DV;
+
 // ===========================================================================
 // dQ, query-outer
 // ===========================================================================
@@ -147,7 +154,9 @@ __device__ __forceinline__ void q_init(const BwdArgs& a, size_t bh, int tok, boo
 }
 
 // One 32-key tile: K tile tk, V tile tv (32 rows each), nvalid leading keys.
-template <int D>
+// HOIST: read the transposed K operands of dQ before the VALU work (their
+// LDS latency is then covered), at the cost of 2*DT more live registers.
+template <int D, bool HOIST>
 __device__ __forceinline__ void q_tile(const char* tk, const char* tv, int nvalid, float c2, QState<D>& st) {
   const int lane = threadIdx.x & 63, h = lane >> 5, l32 = lane & 31;
   f32x16_t s = {}, dp = {};
@@ -155,6 +164,14 @@ __device__ __forceinline__ void q_tile(const char* tk, const char* tv, int nvali
   for (int ks = 0; ks < Sh<D>::KS; ++ks) {
     s = mfma(rd_nat<D>(tk, l32, 2 * ks + h), st.qf[ks], s);
     dp = mfma(rd_nat<D>(tv, l32, 2 * ks + h), st.df[ks], dp);
+  }
+  bf16x8_t kt[HOIST ? Sh<D>::DT : 1][2];
+  if (HOIST) {
+#pragma unroll
+    for (int dt = 0; dt < Sh<D>::DT; ++dt) {
+      kt[HOIST ? dt : 0][0] = rd_tr<D>(tk, 0, dt);
+      kt[HOIST ? dt : 0][1] = rd_tr<D>(tk, 1, dt);
+    }
   }
   f32x16_t ds;
 #pragma unroll
@@ -166,8 +183,8 @@ __device__ __forceinline__ void q_tile(const char* tk, const char* tv, int nvali
   const bf16x8_t d0 = pack8(ds, 0), d1 = pack8(ds, 1);
 #pragma unroll
   for (int dt = 0; dt < Sh<D>::DT; ++dt) {
-    st.acc[dt] = mfma(rd_tr<D>(tk, 0, dt), d0, st.acc[dt]);
-    st.acc[dt] = mfma(rd_tr<D>(tk, 1, dt), d1, st.acc[dt]);
+    st.acc[dt] = mfma(HOIST ? kt[HOIST ? dt : 0][0] : rd_tr<D>(tk, 0, dt), d0, st.acc[dt]);
+    st.acc[dt] = mfma(HOIST ? kt[HOIST ? dt : 0][1] : rd_tr<D>(tk, 1, dt), d1, st.acc[dt]);
   }
 }
 
@@ -234,8 +251,8 @@ __global__ __launch_bounds__(kDqThreads, 1) void dq_pers_kernel(BwdArgs a) {
       const int n = min(a.plen[bh * g.S + s], g.C);
       if (s + 1 < g.S) slot_load<D>(a, bh, s + 1, pf);
       if (active) {
-        if (n > 0) q_tile<D>(buf, buf + 2 * Sh<D>::TILEB, min(n, 32), c2, st);
-        if (n > 32) q_tile<D>(buf + Sh<D>::TILEB, buf + 3 * Sh<D>::TILEB, n - 32, c2, st);
+        if (n > 0) q_tile<D, kHoistDqPers>(buf, buf + 2 * Sh<D>::TILEB, min(n, 32), c2, st);
+        if (n > 32) q_tile<D, kHoistDqPers>(buf + Sh<D>::TILEB, buf + 3 * Sh<D>::TILEB, n - 32, c2, st);
       }
       if (s + 1 < g.S) slot_store<D>(pf, smem + ((s + 1) & 1) * BUF);
       __syncthreads();
@@ -384,7 +401,7 @@ __global__ __launch_bounds__(kDqlThreads, 1) void dq_local_kernel(BwdArgs a) {
     if (j + 1 < nsteps) loc_load<D, TAB>(a, bh, qg, j + 1, pf, rowtab);
     if (nv > 0) {
       const char* region = buf + (wave >> 1) * 2 * Sh<D>::TILEB;
-      q_tile<D>(region, region + Sh<D>::TILEB, nv, c2, st);
+      q_tile<D, kHoistDqLocal>(region, region + Sh<D>::TILEB, nv, c2, st);
     }
     if (j + 1 < nsteps) loc_store<D>(pf, smem + ((j + 1) & 1) * BUF);
     __syncthreads();
@@ -437,7 +454,7 @@ __device__ __forceinline__ void k_init(const bf16_t* krow, const bf16_t* vrow, b
 }
 
 // One 32-query tile in LDS: Q tile tq, dO tile td, per-row lse*log2e and D.
-template <int D, bool DV>
+template <int D, bool DV, bool HOIST>
 __device__ __forceinline__ void k_tile(const char* tq, const char* td, const float* lse2, const float* dl, float c2,
                                        KState<D, DV>& st) {
   const int lane = threadIdx.x & 63, h = lane >> 5, l32 = lane & 31;
@@ -446,6 +463,15 @@ __device__ __forceinline__ void k_tile(const char* tq, const char* td, const flo
   for (int ks = 0; ks < Sh<D>::KS; ++ks) {
     s = mfma(rd_nat<D>(tq, l32, 2 * ks + h), st.kf[ks], s);
     if (!DV) dp = mfma(rd_nat<D>(td, l32, 2 * ks + h), st.vf[DV ? 0 : ks], dp);
+  }
+  const char* tb = DV ? td : tq;  // dV += P^T dO ; dK += dS^T Q
+  bf16x8_t bt[HOIST ? Sh<D>::DT : 1][2];  // transposed B operands, read before the VALU work
+  if (HOIST) {
+#pragma unroll
+    for (int dt = 0; dt < Sh<D>::DT; ++dt) {
+      bt[HOIST ? dt : 0][0] = rd_tr<D>(tb, 0, dt);
+      bt[HOIST ? dt : 0][1] = rd_tr<D>(tb, 1, dt);
+    }
   }
   f32x16_t x;
 #pragma unroll
@@ -468,11 +494,10 @@ __device__ __forceinline__ void k_tile(const char* tq, const char* td, const flo
     }
   }
   const bf16x8_t x0 = pack8(x, 0), x1 = pack8(x, 1);
-  const char* tb = DV ? td : tq;  // dV += P^T dO ; dK += dS^T Q
 #pragma unroll
   for (int dt = 0; dt < Sh<D>::DT; ++dt) {
-    st.acc[dt] = mfma(x0, rd_tr<D>(tb, 0, dt), st.acc[dt]);
-    st.acc[dt] = mfma(x1, rd_tr<D>(tb, 1, dt), st.acc[dt]);
+    st.acc[dt] = mfma(x0, HOIST ? bt[HOIST ? dt : 0][0] : rd_tr<D>(tb, 0, dt), st.acc[dt]);
+    st.acc[dt] = mfma(x1, HOIST ? bt[HOIST ? dt : 0][1] : rd_tr<D>(tb, 1, dt), st.acc[dt]);
   }
 }
 
@@ -577,7 +602,7 @@ __global__ __launch_bounds__(kKvThreads, 2) void dkv_pers_kernel(BwdArgs a) {
     if (i + 1 < nsteps) pf.load(a, bh, Contig{32 * (i + 1), g.ct});
     if (nk > 0) {
       const float* f = reinterpret_cast<const float*>(buf + 2 * Sh<D>::TILEB);
-      k_tile<D, DV>(buf, buf + Sh<D>::TILEB, f, f + 32, c2, st);
+      k_tile<D, DV, kHoistKvPers<DV>>(buf, buf + Sh<D>::TILEB, f, f + 32, c2, st);
     }
     if (i + 1 < nsteps) pf.store(smem + ((i + 1) & 1) * BUF);
     __syncthreads();
@@ -743,7 +768,7 @@ __global__ __launch_bounds__(kKvlThreads, 2) void dkv_local_kernel(BwdArgs a) {
     }
     if (i < mine && nk > 0) {
       const float* f = reinterpret_cast<const float*>(buf + 2 * Sh<D>::TILEB);
-      k_tile<D, DV>(buf, buf + Sh<D>::TILEB, f, f + 32, c2, st);
+      k_tile<D, DV, kHoistKvLocal<DV>>(buf, buf + Sh<D>::TILEB, f, f + 32, c2, st);
     }
     if (i + 1 < mine) pf.store(sbuf + ((i + 1) & 1) * BUF, stid);
     __syncthreads();
