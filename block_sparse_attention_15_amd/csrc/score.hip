@@ -30,23 +30,32 @@ template <> struct Vec4<bf16_t> {
   }
 };
 
-// Mean of `len` rows (row(i) gives the row index) of a [*, D] tensor, written
-// to out[D].  Fixed summation order: each thread sums rows rg, rg+nrg, ...;
-// the row groups are then added in order 0..nrg-1; the sum is divided by len
-// (0 rows give 0).
-template <typename T, typename RowFn>
-__device__ void pool_rows(const T* base, int D, int len, RowFn row, float* red /* [nrg][D] */,
-                          float* out) {
-  const int ncg = D / 4;              // column groups of 4 elements
-  const int nrg = kThreads / ncg;     // row groups
+// Mean of `len` (<= 64) rows (row(i) gives the row index) of a [*, D]
+// tensor, written to out[D].  Fixed summation order: each thread sums rows
+// rg, rg+nrg, ...; the row groups are then added in order 0..nrg-1; the sum
+// is divided by len (0 rows give 0).  All of a thread's row loads are issued
+// before the first add.
+template <int D, typename T, typename RowFn>
+__device__ void pool_rows(const T* base, int len, RowFn row, float* red /* [nrg][D] */, float* out) {
+  constexpr int ncg = D / 4;              // column groups of 4 elements
+  constexpr int nrg = kThreads / ncg;     // row groups
+  constexpr int kIt = 64 / nrg;           // rows per thread at most
   const int cg = threadIdx.x % ncg, rg = threadIdx.x / ncg;
+  float4 v[kIt];
+#pragma unroll
+  for (int u = 0; u < kIt; ++u) {
+    const int i = rg + nrg * u;
+    v[u] = i < len ? Vec4<T>::load(base + (size_t)row(i) * D + cg * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int i = rg; i < len; i += nrg) {
-    float4 v = Vec4<T>::load(base + (size_t)row(i) * D + cg * 4);
-    acc.x += v.x;
-    acc.y += v.y;
-    acc.z += v.z;
-    acc.w += v.w;
+#pragma unroll
+  for (int u = 0; u < kIt; ++u) {
+    if (rg + nrg * u < len) {
+      acc.x += v[u].x;
+      acc.y += v[u].y;
+      acc.z += v[u].z;
+      acc.w += v[u].w;
+    }
   }
   float* r = red + rg * D + cg * 4;
   r[0] = acc.x;
@@ -62,7 +71,7 @@ __device__ void pool_rows(const T* base, int D, int len, RowFn row, float* red /
 }
 
 // grid (nq + nl, H, B): query block means -> qbar, local block means -> kbar_l.
-template <typename T>
+template <int D, typename T>
 __global__ __launch_bounds__(kThreads) void pool_blocks_kernel(Geo g, const T* __restrict__ q,
                                                                const T* __restrict__ kl, float* __restrict__ qbar,
                                                                float* __restrict__ kbar_l) {
@@ -75,11 +84,11 @@ __global__ __launch_bounds__(kThreads) void pool_blocks_kernel(Geo g, const T* _
   const BlockExt e = block_ext(g, p % g.nq);
   const T* base = is_q ? q + bh * g.ct * g.D : kl + bh * (size_t)g.NL * g.D;
   float* out = is_q ? qbar + (bh * g.nq + p) * g.D : kbar_l + (bh * g.nl + p) * g.D;
-  pool_rows<T>(base, g.D, e.len, [&](int i) { return off + block_token(g, e, i); }, red, out);
+  pool_rows<D, T>(base, e.len, [&](int i) { return off + block_token(g, e, i); }, red, out);
 }
 
 // grid (S, H, B): mean of each slot's first len rows (0 for empty slots).
-template <typename T>
+template <int D, typename T>
 __global__ __launch_bounds__(kThreads) void pool_slots_kernel(Geo g, const T* __restrict__ kp,
                                                               const int32_t* __restrict__ plen,
                                                               float* __restrict__ kbar) {
@@ -87,7 +96,7 @@ __global__ __launch_bounds__(kThreads) void pool_slots_kernel(Geo g, const T* __
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const size_t bhs = ((size_t)b * g.H + h) * g.S + s;
   const int len = min(max(plen[bhs], 0), g.C);
-  pool_rows<T>(kp + bhs * g.C * g.D, g.D, len, [](int i) { return i; }, red, kbar + bhs * g.D);
+  pool_rows<D, T>(kp + bhs * g.C * D, len, [](int i) { return i; }, red, kbar + bhs * D);
 }
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -105,6 +114,7 @@ constexpr int kQPerWg = 4;  // query blocks scored per workgroup (one wave each 
 // block and every valid persistent slot (each candidate's pooled key is read
 // once for the 4 query blocks), then per query block (one wave) the top-k by
 // rank and one pooled softmax row.
+template <int D>
 __global__ __launch_bounds__(kThreads) void score_topk_kernel(Geo g, const int32_t* __restrict__ ring_head,
                                                               const float* __restrict__ qbar,
                                                               const float* __restrict__ kbar_l,
@@ -132,14 +142,18 @@ __global__ __launch_bounds__(kThreads) void score_topk_kernel(Geo g, const int32
       for (int k = 0; k < kQPerWg; ++k) sc[k * W + c] = -INFINITY;
       continue;
     }
-    const float4* kv = reinterpret_cast<const float4*>(loc ? kbar_l + (bh * g.nl + idx) * g.D
-                                                           : kbar_p + (bh * g.S + idx) * g.D);
+    const float4* kv = reinterpret_cast<const float4*>(loc ? kbar_l + (bh * g.nl + idx) * D
+                                                           : kbar_p + (bh * g.S + idx) * D);
+    float4 kr[D / 4];  // the candidate's pooled key, all loads in flight together
+#pragma unroll
+    for (int d4 = 0; d4 < D / 4; ++d4) kr[d4] = kv[d4];
     float acc[kQPerWg] = {};
-    for (int d4 = 0; d4 < g.D / 4; ++d4) {
-      const float4 k4 = kv[d4];
+#pragma unroll
+    for (int d4 = 0; d4 < D / 4; ++d4) {
+      const float4 k4 = kr[d4];
 #pragma unroll
       for (int k = 0; k < kQPerWg; ++k) {
-        const float4 q4 = reinterpret_cast<const float4*>(qb + k * g.D)[d4];
+        const float4 q4 = reinterpret_cast<const float4*>(qb + k * D)[d4];
         acc[k] = fmaf(q4.x, k4.x, acc[k]);
         acc[k] = fmaf(q4.y, k4.y, acc[k]);
         acc[k] = fmaf(q4.z, k4.z, acc[k]);
@@ -224,37 +238,54 @@ __global__ __launch_bounds__(kThreads) void mass_kernel(Geo g, const float* __re
 
 }  // namespace
 
-hipError_t launch_pool_slots(const Geo& g, const void* k_p, const int32_t* plen, float* kbar, hipStream_t s) {
+template <int D>
+void pool_slots_d(const Geo& g, const void* k_p, const int32_t* plen, float* kbar, hipStream_t s) {
   dim3 grid(g.S, g.H, g.B);
   if (g.dtype == PBSA_BF16)
-    pool_slots_kernel<bf16_t><<<grid, kThreads, 0, s>>>(g, (const bf16_t*)k_p, plen, kbar);
+    pool_slots_kernel<D, bf16_t><<<grid, kThreads, 0, s>>>(g, (const bf16_t*)k_p, plen, kbar);
   else
-    pool_slots_kernel<float><<<grid, kThreads, 0, s>>>(g, (const float*)k_p, plen, kbar);
+    pool_slots_kernel<D, float><<<grid, kThreads, 0, s>>>(g, (const float*)k_p, plen, kbar);
+}
+
+hipError_t launch_pool_slots(const Geo& g, const void* k_p, const int32_t* plen, float* kbar, hipStream_t s) {
+  if (g.D == 128)
+    pool_slots_d<128>(g, k_p, plen, kbar, s);
+  else
+    pool_slots_d<64>(g, k_p, plen, kbar, s);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t score_select_d(const Geo& g, const void* q, const void* k_l, const int32_t* ring_head,
+                          const float* kbar_p, const int32_t* plen, int32_t* topk, float* mass, float* kbar_l,
+                          WsScore ws, hipStream_t s) {
+  dim3 g1(g.nq + g.nl, g.H, g.B);
+  if (g.dtype == PBSA_BF16)
+    pool_blocks_kernel<D, bf16_t><<<g1, kThreads, 0, s>>>(g, (const bf16_t*)q, (const bf16_t*)k_l, ws.qbar, kbar_l);
+  else
+    pool_blocks_kernel<D, float><<<g1, kThreads, 0, s>>>(g, (const float*)q, (const float*)k_l, ws.qbar, kbar_l);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t shm = (size_t)kQPerWg * (g.D + g.nl + g.S + 3 * g.nl) * 4;
+  static bool attr = false;
+  if (!attr) {
+    e = hipFuncSetAttribute((const void*)score_topk_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            160 * 1024);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  score_topk_kernel<D><<<dim3((g.nq + kQPerWg - 1) / kQPerWg, g.H, g.B), kThreads, shm, s>>>(
+      g, ring_head, ws.qbar, kbar_l, kbar_p, plen, topk, ws.prow);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  mass_kernel<<<dim3((g.S + g.nl + 63) / 64, g.H, g.B), kThreads, 0, s>>>(g, ws.prow, mass);
   return hipGetLastError();
 }
 
 hipError_t launch_score_select(const Geo& g, const void* q, const void* k_l, const int32_t* ring_head,
                                const float* kbar_p, const int32_t* plen, int32_t* topk, float* mass,
                                float* kbar_l, WsScore ws, hipStream_t s) {
-  dim3 g1(g.nq + g.nl, g.H, g.B);
-  if (g.dtype == PBSA_BF16)
-    pool_blocks_kernel<bf16_t><<<g1, kThreads, 0, s>>>(g, (const bf16_t*)q, (const bf16_t*)k_l, ws.qbar, kbar_l);
-  else
-    pool_blocks_kernel<float><<<g1, kThreads, 0, s>>>(g, (const float*)q, (const float*)k_l, ws.qbar, kbar_l);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const size_t shm = (size_t)kQPerWg * (g.D + g.nl + g.S + 3 * g.nl) * 4;
-  static bool attr = false;
-  if (!attr) {
-    e = hipFuncSetAttribute((const void*)score_topk_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
-  score_topk_kernel<<<dim3((g.nq + kQPerWg - 1) / kQPerWg, g.H, g.B), kThreads, shm, s>>>(
-      g, ring_head, ws.qbar, kbar_l, kbar_p, plen, topk, ws.prow);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  mass_kernel<<<dim3((g.S + g.nl + 63) / 64, g.H, g.B), kThreads, 0, s>>>(g, ws.prow, mass);
-  return hipGetLastError();
+  return g.D == 128 ? score_select_d<128>(g, q, k_l, ring_head, kbar_p, plen, topk, mass, kbar_l, ws, s)
+                    : score_select_d<64>(g, q, k_l, ring_head, kbar_p, plen, topk, mass, kbar_l, ws, s);
 }
 
 }  // namespace pbsa
