@@ -34,35 +34,41 @@ constexpr int kTindexLds = 48 * 1024;
 
 __global__ __launch_bounds__(256) void bwd_tindex_kernel(Geo g, const int32_t* __restrict__ topk,
                                                          int32_t* __restrict__ tcount, int32_t* __restrict__ tlist) {
+  // Incidence of (local block, query block) marked in LDS for as many query
+  // blocks at a time as fit, then appended to each local block's list in
+  // ascending query-block order; thread t owns local blocks t, t+256, ...
   extern __shared__ unsigned char mark[];
+  constexpr int kOwn = 2048 / 256;  // local blocks per thread at most (plan limit)
   const size_t bh = (size_t)blockIdx.y * g.H + blockIdx.x;
   const int32_t* tk = topk + bh * g.nq * g.K;
-  if (g.nl * g.nq <= kTindexLds) {
-    for (int x = threadIdx.x; x < g.nl * g.nq; x += 256) mark[x] = 0;
+  const int chunk = max(1, min(g.nq, kTindexLds / g.nl));
+  int n[kOwn];
+#pragma unroll
+  for (int u = 0; u < kOwn; ++u) n[u] = 0;
+  for (int i0 = 0; i0 < g.nq; i0 += chunk) {
+    const int ni = min(chunk, g.nq - i0);
     __syncthreads();
-    for (int x = threadIdx.x; x < g.nq * g.K; x += 256) {
-      const int p = tk[x];
-      if ((unsigned)p < (unsigned)g.nl) mark[p * g.nq + x / g.K] = 1;
+    for (int x = threadIdx.x; x < g.nl * ni; x += 256) mark[x] = 0;
+    __syncthreads();
+    for (int x = threadIdx.x; x < ni * g.K; x += 256) {
+      const int p = tk[(size_t)i0 * g.K + x];
+      if ((unsigned)p < (unsigned)g.nl) mark[p * ni + x / g.K] = 1;
     }
     __syncthreads();
-    for (int p = threadIdx.x; p < g.nl; p += 256) {
-      int n = 0;
-      int32_t* out = tlist + (bh * g.nl + p) * g.nq;
-      for (int i = 0; i < g.nq; ++i)
-        if (mark[p * g.nq + i]) out[n++] = i;
-      tcount[bh * g.nl + p] = n;
+#pragma unroll
+    for (int u = 0; u < kOwn; ++u) {
+      const int p = threadIdx.x + 256 * u;
+      if (p < g.nl) {
+        int32_t* out = tlist + (bh * g.nl + p) * g.nq;
+        for (int i = 0; i < ni; ++i)
+          if (mark[p * ni + i]) out[n[u]++] = i0 + i;
+      }
     }
-    return;
   }
-  for (int p = threadIdx.x; p < g.nl; p += 256) {
-    int n = 0;
-    int32_t* out = tlist + (bh * g.nl + p) * g.nq;
-    for (int i = 0; i < g.nq; ++i) {
-      bool hit = false;
-      for (int k = 0; k < g.K; ++k) hit |= tk[i * g.K + k] == p;
-      if (hit) out[n++] = i;
-    }
-    tcount[bh * g.nl + p] = n;
+#pragma unroll
+  for (int u = 0; u < kOwn; ++u) {
+    const int p = threadIdx.x + 256 * u;
+    if (p < g.nl) tcount[bh * g.nl + p] = n[u];
   }
 }
 
@@ -257,7 +263,7 @@ hipError_t launch_bwd_prep(const Geo& g, const void* o, const void* dout, const 
     bwd_delta_kernel<float><<<g1, 256, 0, s>>>(g, (const float*)o, (const float*)dout, ws.delta);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const size_t shm = (size_t)g.nl * g.nq <= (size_t)kTindexLds ? (size_t)g.nl * g.nq : 0;
+  const size_t shm = (size_t)g.nl * max(1, min(g.nq, kTindexLds / g.nl));
   bwd_tindex_kernel<<<dim3(g.H, g.B), 256, shm, s>>>(g, topk, ws.tcount, ws.tlist);
   return hipGetLastError();
 }

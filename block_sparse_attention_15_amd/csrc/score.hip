@@ -108,13 +108,12 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-constexpr int kQPerWg = 4;  // query blocks scored per workgroup (one wave each for top-k)
-
-// grid (ceil(nq/4), H, B): pooled scores of 4 query blocks against every local
-// block and every valid persistent slot (each candidate's pooled key is read
-// once for the 4 query blocks), then per query block (one wave) the top-k by
-// rank and one pooled softmax row.
-template <int D>
+// grid (ceil(nq/QPW), H, B): pooled scores of QPW (<= 4) query blocks against
+// every local block and every valid persistent slot (each candidate's pooled
+// key is read once for the QPW query blocks), then per query block (one wave)
+// the top-k by rank and one pooled softmax row.  QPW is the largest of 4, 2,
+// 1 whose LDS (scores, sort keys and flags of every candidate) fits.
+template <int D, int kQPerWg>
 __global__ __launch_bounds__(kThreads) void score_topk_kernel(Geo g, const int32_t* __restrict__ ring_head,
                                                               const float* __restrict__ qbar,
                                                               const float* __restrict__ kbar_l,
@@ -165,7 +164,7 @@ __global__ __launch_bounds__(kThreads) void score_topk_kernel(Geo g, const int32
   }
   __syncthreads();
   const int i = i0 + w;
-  const bool has = i < g.nq;
+  const bool has = w < kQPerWg && i < g.nq;
   const float* row = sc + w * W;
   unsigned long long* key = reinterpret_cast<unsigned long long*>(sel) + w * g.nl;
   const int rh = *ring_head;
@@ -238,6 +237,16 @@ __global__ __launch_bounds__(kThreads) void mass_kernel(Geo g, const float* __re
 
 }  // namespace
 
+constexpr int kScoreLdsMax = 160 * 1024;
+
+size_t score_lds(const Geo& g, int qpw) { return (size_t)qpw * (g.D + g.nl + g.S + 3 * g.nl) * 4; }
+
+int score_qpw(const Geo& g) {
+  for (int q = 4; q > 1; q /= 2)
+    if (score_lds(g, q) <= (size_t)kScoreLdsMax) return q;
+  return 1;
+}
+
 template <int D>
 void pool_slots_d(const Geo& g, const void* k_p, const int32_t* plen, float* kbar, hipStream_t s) {
   dim3 grid(g.S, g.H, g.B);
@@ -266,16 +275,24 @@ hipError_t score_select_d(const Geo& g, const void* q, const void* k_l, const in
     pool_blocks_kernel<D, float><<<g1, kThreads, 0, s>>>(g, (const float*)q, (const float*)k_l, ws.qbar, kbar_l);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const size_t shm = (size_t)kQPerWg * (g.D + g.nl + g.S + 3 * g.nl) * 4;
   static bool attr = false;
   if (!attr) {
-    e = hipFuncSetAttribute((const void*)score_topk_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            160 * 1024);
-    if (e != hipSuccess) return e;
+    for (const void* f : {(const void*)score_topk_kernel<D, 4>, (const void*)score_topk_kernel<D, 2>,
+                          (const void*)score_topk_kernel<D, 1>}) {
+      e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kScoreLdsMax);
+      if (e != hipSuccess) return e;
+    }
     attr = true;
   }
-  score_topk_kernel<D><<<dim3((g.nq + kQPerWg - 1) / kQPerWg, g.H, g.B), kThreads, shm, s>>>(
-      g, ring_head, ws.qbar, kbar_l, kbar_p, plen, topk, ws.prow);
+  const int qpw = score_qpw(g);
+  const size_t shm = score_lds(g, qpw);
+  const dim3 grid((g.nq + qpw - 1) / qpw, g.H, g.B);
+  if (qpw == 4)
+    score_topk_kernel<D, 4><<<grid, kThreads, shm, s>>>(g, ring_head, ws.qbar, kbar_l, kbar_p, plen, topk, ws.prow);
+  else if (qpw == 2)
+    score_topk_kernel<D, 2><<<grid, kThreads, shm, s>>>(g, ring_head, ws.qbar, kbar_l, kbar_p, plen, topk, ws.prow);
+  else
+    score_topk_kernel<D, 1><<<grid, kThreads, shm, s>>>(g, ring_head, ws.qbar, kbar_l, kbar_p, plen, topk, ws.prow);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   mass_kernel<<<dim3((g.S + g.nl + 63) / 64, g.H, g.B), kThreads, 0, s>>>(g, ws.prow, mass);
   return hipGetLastError();

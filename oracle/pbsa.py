@@ -319,22 +319,25 @@ def token_mass(q, k_p, plen, k_l, topk_idx, g: Geometry) -> np.ndarray:
     return out.astype(np.float32)
 
 
-def attend_bwd(q, k_p, v_p, plen, k_l, v_l, topk_idx, dout, g: Geometry):
+def attend_bwd(q, k_p, v_p, plen, k_l, v_l, topk_idx, dout, g: Geometry, qblocks=None):
     """Gradients of sum(dout * O) w.r.t. q, k_p, v_p, k_l, v_l (float64), fixed mask (R17).
 
     Standard softmax-attention calculus on each query block's key set:
     P = softmax(scale Q K^T), dV = P^T dO, dP = dO V^T, D = rowsum(dO * O),
     dS = P * (dP - D), dQ = scale dS K, dK = scale dS^T Q.  Padding rows and
-    unselected blocks get zero gradient.
+    unselected blocks get zero gradient.  ``qblocks`` restricts the sum to
+    those query blocks: their dQ rows are exact, other dQ rows stay zero and
+    dK / dV hold only those blocks' contributions.
     """
     dq = np.zeros((g.B, g.H, g.chunk_tokens, g.D))
     dk_p = np.zeros(k_p.shape)
     dv_p = np.zeros(v_p.shape)
     dk_l = np.zeros(k_l.shape)
     dv_l = np.zeros(v_l.shape)
+    blocks = range(g.n_qblk) if qblocks is None else qblocks
     for b in range(g.B):
         for h in range(g.H):
-            for i in range(g.n_qblk):
+            for i in blocks:
                 K, V, where = _key_rows(k_p, v_p, plen, k_l, v_l, topk_idx[b, h, i], b, h, g)
                 tok = g.block_tok[i]
                 Q = q[b, h, tok].astype(np.float64)
