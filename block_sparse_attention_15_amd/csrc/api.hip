@@ -182,10 +182,13 @@ pbsa_status pbsa_pool_slots(const pbsa_config* cfg, const void* k_pers, const in
   Plan p;
   pbsa_status st = make_plan(cfg, &p);
   if (st != PBSA_OK) return st;
+  if (p.g.S == 0) {  // no persistent memory: nothing to pool
+    g_err.clear();
+    return PBSA_OK;
+  }
   REQUIRE_ALIGNED(k_pers);
   REQUIRE_PTR(persist_len);
   REQUIRE_ALIGNED(persist_kbar);
-  if (p.g.S == 0) return PBSA_OK;
   return hip_status(launch_pool_slots(p.g, k_pers, persist_len, persist_kbar, (hipStream_t)stream),
                     "pbsa_pool_slots");
 }
