@@ -532,37 +532,48 @@ struct QTileLoader {
   static constexpr int N = (NCH + NTHR - 1) / NTHR;   // per thread
   uint4 q[N], d[N];
   float l, dd;
+  unsigned ok;  // bit u: chunk u is a valid row; bit N: row tid (lse / D) is valid
+  // Loads are unconditional (invalid rows read row 0 of the head) with one
+  // 32-bit offset per chunk shared by Q and dO against per-head base
+  // pointers; invalid rows are zeroed when staged.
   __device__ __forceinline__ void load(const BwdArgs& a, size_t bh, RowFn row) {
     const Geo& g = a.g;
     const int tid = threadIdx.x;
+    const bf16_t* qb = a.q + bh * g.ct * (size_t)D;
+    const bf16_t* db = a.dout + bh * g.ct * (size_t)D;
+    ok = 0;
 #pragma unroll
     for (int u = 0; u < N; ++u) {
       const int id = tid + NTHR * u, r = id / Sh<D>::CPR, c = id % Sh<D>::CPR;
       const int tok = id < NCH ? row(r) : -1;
-      const size_t off = (bh * g.ct + (tok < 0 ? 0 : tok)) * (size_t)D + c * 8;
-      q[u] = tok >= 0 ? ld16(a.q + off) : make_uint4(0, 0, 0, 0);
-      d[u] = tok >= 0 ? ld16(a.dout + off) : make_uint4(0, 0, 0, 0);
+      if (tok >= 0) ok |= 1u << u;
+      const unsigned off = (unsigned)(max(tok, 0) * D + c * 8);
+      q[u] = ld16(qb + off);
+      d[u] = ld16(db + off);
     }
-    if (tid < 32) {
-      const int tok = row(tid);
-      l = tok >= 0 ? a.lse[bh * g.ct + tok] * kLog2e : INFINITY;
-      dd = tok >= 0 ? a.delta[bh * g.ct + tok] : 0.f;
-    }
+    const int tl = tid < 32 ? row(tid) : -1;
+    if (tl >= 0) ok |= 1u << N;
+    const size_t ro = bh * g.ct + max(tl, 0);
+    l = a.lse[ro];
+    dd = a.delta[ro];
   }
   // LDS: Q tile, dO tile, lse2[32], D[32]
   __device__ __forceinline__ void store(char* buf) const {
     const int tid = threadIdx.x;
+    const uint4 z = make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int u = 0; u < N; ++u) {
       const int id = tid + NTHR * u, r = id / Sh<D>::CPR, c = id % Sh<D>::CPR;
       if (id >= NCH) break;
-      st_chunk(buf, Sh<D>::ROWB, Sh<D>::CPR, r, c, q[u]);
-      st_chunk(buf + Sh<D>::TILEB, Sh<D>::ROWB, Sh<D>::CPR, r, c, d[u]);
+      const bool v = (ok >> u) & 1;
+      st_chunk(buf, Sh<D>::ROWB, Sh<D>::CPR, r, c, v ? q[u] : z);
+      st_chunk(buf + Sh<D>::TILEB, Sh<D>::ROWB, Sh<D>::CPR, r, c, v ? d[u] : z);
     }
     if (tid < 32) {
+      const bool v = (ok >> N) & 1;
       float* f = reinterpret_cast<float*>(buf + 2 * Sh<D>::TILEB);
-      f[tid] = l;
-      f[32 + tid] = dd;
+      f[tid] = v ? l * kLog2e : INFINITY;
+      f[32 + tid] = v ? dd : 0.f;
     }
   }
 };
