@@ -608,15 +608,19 @@ __global__ __launch_bounds__(kKvThreads, 2) void dkv_pers_kernel(BwdArgs a) {
   pf.load(a, bh, Contig{0, g.ct});
   pf.store(smem);
   __syncthreads();
-  for (int i = 0; i < nsteps; ++i) {
-    char* buf = smem + (i & 1) * BUF;
+  // unrolled by two so that each half's LDS buffer is a compile-time offset
+  auto step = [&](int i, char* buf, char* nxt) {
     if (i + 1 < nsteps) pf.load(a, bh, Contig{32 * (i + 1), g.ct});
     if (nk > 0) {
       const float* f = reinterpret_cast<const float*>(buf + 2 * Sh<D>::TILEB);
       k_tile<D, DV, kHoistKvPers<DV>>(buf, buf + Sh<D>::TILEB, f, f + 32, c2, st);
     }
-    if (i + 1 < nsteps) pf.store(smem + ((i + 1) & 1) * BUF);
+    if (i + 1 < nsteps) pf.store(nxt);
     __syncthreads();
+  };
+  for (int i = 0; i < nsteps; i += 2) {
+    step(i, smem, smem + BUF);
+    if (i + 1 < nsteps) step(i + 1, smem + BUF, smem);
   }
   if (!has_slot || 32 * kh >= g.C) return;
   float* ob = (DV ? a.dvp : a.dkp) + sbase;

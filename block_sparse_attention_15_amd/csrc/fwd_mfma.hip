@@ -302,8 +302,8 @@ __global__ __launch_bounds__(kPersThreads, 1) void fwd_pers_kernel(FwdArgs a) {
     pers_load<D>(a, bh, 0, pf);
     pers_store<D>(pf, smem);
     __syncthreads();
-    for (int s = 0; s < g.S; ++s) {
-      char* buf = smem + (s & 1) * kBufBytes;
+    // unrolled by two so that each half's LDS buffer is a compile-time offset
+    auto step = [&](int s, char* buf, char* nxt) {
       const int n = min(a.plen[bh * g.S + s], g.C);
       if (s + 1 < g.S) pers_load<D>(a, bh, s + 1, pf);
       float bl = 0.f;  // MASS: log2-sum-exp2 over the slot
@@ -320,10 +320,14 @@ __global__ __launch_bounds__(kPersThreads, 1) void fwd_pers_kernel(FwdArgs a) {
           bl = tot > 0.f ? st.m[0] + __builtin_amdgcn_logf(tot) : -INFINITY;
         }
       }
-      if (s + 1 < g.S) pers_store<D>(pf, smem + ((s + 1) & 1) * kBufBytes);
+      if (s + 1 < g.S) pers_store<D>(pf, nxt);
       // stored after the LDS fill so that its wait for the prefetch does not also wait for this store
       if (MASS && ntq > 0 && h == 0 && row_w + l32 < g.ct) a.blse_p[(bh * g.S + s) * g.ct + row_w + l32] = bl;
       __syncthreads();
+    };
+    for (int s = 0; s < g.S; s += 2) {
+      step(s, smem, smem + kBufBytes);
+      if (s + 1 < g.S) step(s + 1, smem + kBufBytes, smem);
     }
   }
 
