@@ -632,23 +632,21 @@ __global__ __launch_bounds__(kKvThreads, 2) void dkv_pers_kernel(BwdArgs a) {
   });
 }
 
-// dkv_local: one local block (64 keys = 2 key tiles) per workgroup and two
-// query streams that take the steps alternately, 4 waves in all; the two
-// partial accumulators are added in a fixed order at the end.  Splitting the
-// steps halves the longest workgroups: a block chosen by many query blocks
-// would otherwise set the end of the launch.
-constexpr int kKvlStreamThreads = 128;
-constexpr int kKvlThreads = 2 * kKvlStreamThreads;
+// dkv_local: one local block (64 keys = 2 key tiles) per workgroup, 4 waves:
+// waves 0-1 accumulate dV and waves 2-3 dK of the two key tiles, over the
+// same gathered query tiles, which are staged into LDS once for both passes.
+// A step is one 32-row half of one query block that selected this local
+// block (key-block -> query-block lists from bwd_tindex_kernel, copied to LDS
+// with the step list).
+constexpr int kKvlThreads = 256;
 
-// Query-tile gather of one stream, software-pipelined two steps deep.  A step
-// is one 32-row half of one query block that selected this local block; the
-// step list and the selecting blocks' lengths sit in LDS.  Row tokens of the
-// stream's step after next are loaded while it computes, so the Q / dO loads
-// of its next step issue with ready addresses; rows past a block's end load
-// token 0 and are zeroed when staged into LDS.
+// Query-tile gather, software-pipelined two steps deep: row tokens of step
+// i+2 are loaded while step i computes, so the Q / dO loads of step i+1 issue
+// with ready addresses; rows past a block's end load token 0 and are zeroed
+// when staged into LDS.
 template <int D> struct GatherPipe {
   static constexpr int NCH = 32 * Sh<D>::CPR;              // 16-byte chunks per tensor tile
-  static constexpr int N = (NCH + kKvlStreamThreads - 1) / kKvlStreamThreads;
+  static constexpr int N = (NCH + kKvlThreads - 1) / kKvlThreads;
   int tok[N], tokl;            // raw row tokens of the next step to load
   unsigned okm;                // bit u: chunk u is a valid row; bit N: row (lse / D) valid
   int tok2[N], tokl2;          // ... of the step after
@@ -659,15 +657,16 @@ template <int D> struct GatherPipe {
 
   // step = (selecting-list index << 1) | half
   __device__ __forceinline__ static void tokens(const BwdArgs& a, const int* sel, const int* slen, int step,
-                                                int tid, int* t, int& tl, unsigned& ok) {
+                                                int* t, int& tl, unsigned& ok) {
     const Geo& g = a.g;
+    const int tid = threadIdx.x;
     const int sidx = step >> 1, half = step & 1;
     const int len = slen[sidx];
     const int32_t* rows = a.tab.btok + sel[sidx] * g.C;
     ok = 0;
 #pragma unroll
     for (int u = 0; u < N; ++u) {
-      const int id = tid + kKvlStreamThreads * u, r = 32 * half + id / Sh<D>::CPR;
+      const int id = tid + kKvlThreads * u, r = 32 * half + id / Sh<D>::CPR;
       t[u] = rows[min(r, g.C - 1)];
       if (id < NCH && r < len) ok |= 1u << u;
     }
@@ -675,14 +674,17 @@ template <int D> struct GatherPipe {
     tl = rows[min(rl, g.C - 1)];
     if (tid < 32 && rl < len) ok |= 1u << N;
   }
-  __device__ __forceinline__ void load(const BwdArgs& a, size_t bh, int tid) {
+  __device__ __forceinline__ void load(const BwdArgs& a, size_t bh) {
     const Geo& g = a.g;
+    const int tid = threadIdx.x;
+    const bf16_t* qb = a.q + bh * g.ct * (size_t)D;
+    const bf16_t* db = a.dout + bh * g.ct * (size_t)D;
 #pragma unroll
     for (int u = 0; u < N; ++u) {
-      const int c = (tid + kKvlStreamThreads * u) % Sh<D>::CPR;
-      const size_t off = (bh * g.ct + ((okm >> u) & 1 ? tok[u] : 0)) * (size_t)D + c * 8;
-      q[u] = ld16(a.q + off);
-      d[u] = ld16(a.dout + off);
+      const int c = (tid + kKvlThreads * u) % Sh<D>::CPR;
+      const unsigned off = (unsigned)(((okm >> u) & 1 ? tok[u] : 0) * D + c * 8);
+      q[u] = ld16(qb + off);
+      d[u] = ld16(db + off);
     }
     const size_t ro = bh * g.ct + ((okm >> N) & 1 ? tokl : 0);
     l = a.lse[ro];
@@ -696,11 +698,12 @@ template <int D> struct GatherPipe {
     okm = okm2;
   }
   // LDS: Q tile, dO tile, lse2[32], D[32]
-  __device__ __forceinline__ void store(char* buf, int tid) const {
+  __device__ __forceinline__ void store(char* buf) const {
+    const int tid = threadIdx.x;
     const uint4 z = make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int u = 0; u < N; ++u) {
-      const int id = tid + kKvlStreamThreads * u, r = id / Sh<D>::CPR, c = id % Sh<D>::CPR;
+      const int id = tid + kKvlThreads * u, r = id / Sh<D>::CPR, c = id % Sh<D>::CPR;
       if (id >= NCH) break;
       const bool ok = (okq >> u) & 1;
       st_chunk(buf, Sh<D>::ROWB, Sh<D>::CPR, r, c, ok ? q[u] : z);
@@ -716,22 +719,17 @@ template <int D> struct GatherPipe {
 };
 
 template <int D> constexpr size_t kvl_lds(int nq) {
-  return 4 * (2 * (size_t)Sh<D>::TILEB + 256) + 4 * (size_t)nq * 4;
+  return 2 * (2 * (size_t)Sh<D>::TILEB + 256) + 4 * (size_t)nq * 4;
 }
 
+// The key-outer pass of one role (dV or dK) over the workgroup's step list;
+// every wave runs the same number of barriers whatever its role.
 template <int D, bool DV>
-__global__ __launch_bounds__(kKvlThreads, 2) void dkv_local_kernel(BwdArgs a) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
+__device__ __forceinline__ void kvl_pass(const BwdArgs& a, size_t bh, int p, int kt, const int* sel,
+                                         const int* slen, const int* steps, int nsteps, char* smem) {
   constexpr int BUF = 2 * Sh<D>::TILEB + 256;
   const Geo& g = a.g;
-  const int total = g.B * g.H * g.nl;
-  const int lin = xcd_remap(total);
-  if (lin >= total) return;
-  const int p = lin % g.nl;
-  const size_t bh = lin / g.nl;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31;
-  const int kt = wave & 1, stream = wave >> 1;          // key tile, query stream
-  const int stid = threadIdx.x & (kKvlStreamThreads - 1);
+  const int l32 = threadIdx.x & 31;
   const BlockExt ke = block_ext(g, p % g.nq);
   const int koff = (p / g.nq) * g.ct;
   const int nk = min(max(ke.len - 32 * kt, 0), 32);
@@ -741,11 +739,56 @@ __global__ __launch_bounds__(kKvlThreads, 2) void dkv_local_kernel(BwdArgs a) {
   KState<D, DV> st;
   k_init<D, DV>(a.kl + krow, a.vl + krow, kok, st);
   const float c2 = g.scale * kLog2e;
+  GatherPipe<D> pf;
+  if (nsteps > 0) {
+    GatherPipe<D>::tokens(a, sel, slen, steps[0], pf.tok, pf.tokl, pf.okm);
+    pf.load(a, bh);
+    pf.store(smem);
+    if (nsteps > 1) GatherPipe<D>::tokens(a, sel, slen, steps[1], pf.tok, pf.tokl, pf.okm);
+    if (nsteps > 2) GatherPipe<D>::tokens(a, sel, slen, steps[2], pf.tok2, pf.tokl2, pf.okm2);
+  }
+  __syncthreads();
+  for (int i = 0; i < nsteps; ++i) {
+    char* buf = smem + (i & 1) * BUF;
+    if (i + 1 < nsteps) pf.load(a, bh);  // step i+1, tokens ready
+    if (i + 2 < nsteps) {
+      pf.shift();
+      if (i + 3 < nsteps) GatherPipe<D>::tokens(a, sel, slen, steps[i + 3], pf.tok2, pf.tokl2, pf.okm2);
+    }
+    if (nk > 0) {
+      const float* f = reinterpret_cast<const float*>(buf + 2 * Sh<D>::TILEB);
+      k_tile<D, DV, kHoistKvLocal<DV>>(buf, buf + Sh<D>::TILEB, f, f + 32, c2, st);
+    }
+    if (i + 1 < nsteps) pf.store(smem + ((i + 1) & 1) * BUF);
+    __syncthreads();
+  }
+  if (nk <= 0) return;
+  float* ob = (DV ? a.dvl : a.dkl) + (bh * g.NL + koff) * (size_t)D;
+  k_write<D, DV>(st, nk, DV ? 1.0f : g.scale, [&](int r, float*& dst) {
+    const int row = 32 * kt + r;
+    if (row >= ke.len) return false;
+    dst = ob + (size_t)block_token(g, ke, row) * D;
+    return true;
+  });
+}
+
+template <int D>
+__global__ __launch_bounds__(kKvlThreads, 2) void dkv_local_kernel(BwdArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  constexpr int BUF = 2 * Sh<D>::TILEB + 256;
+  const Geo& g = a.g;
+  const int total = g.B * g.H * g.nl;
+  const int lin = xcd_remap(total);
+  if (lin >= total) return;
+  const int p = lin % g.nl;
+  const size_t bh = lin / g.nl;
+  const int wave = threadIdx.x >> 6;
+  const int kt = wave & 1, role = wave >> 1;  // role 0: dV, role 1: dK
 
   // selecting query blocks (ascending), their lengths and the step list, in LDS
   const int ncount = a.tcount[bh * g.nl + p];
   const int32_t* lst = a.tlist + (bh * g.nl + p) * g.nq;
-  int* sel = reinterpret_cast<int*>(smem + 4 * BUF);
+  int* sel = reinterpret_cast<int*>(smem + 2 * BUF);
   int* slen = sel + g.nq;
   int* steps = slen + g.nq;
   for (int x = threadIdx.x; x < ncount; x += kKvlThreads) {
@@ -761,54 +804,10 @@ __global__ __launch_bounds__(kKvlThreads, 2) void dkv_local_kernel(BwdArgs a) {
     nsteps += nh;
   }
   __syncthreads();
-  // this stream's steps: stream, stream + 2, ...
-  const int mine = nsteps > stream ? (nsteps - stream + 1) / 2 : 0;
-  const int iters = (nsteps + 1) / 2;
-  char* sbuf = smem + stream * 2 * BUF;
-  GatherPipe<D> pf;
-  if (mine > 0) {
-    GatherPipe<D>::tokens(a, sel, slen, steps[stream], stid, pf.tok, pf.tokl, pf.okm);
-    pf.load(a, bh, stid);
-    pf.store(sbuf, stid);
-    if (mine > 1) GatherPipe<D>::tokens(a, sel, slen, steps[stream + 2], stid, pf.tok, pf.tokl, pf.okm);
-    if (mine > 2) GatherPipe<D>::tokens(a, sel, slen, steps[stream + 4], stid, pf.tok2, pf.tokl2, pf.okm2);
-  }
-  __syncthreads();
-  for (int i = 0; i < iters; ++i) {
-    char* buf = sbuf + (i & 1) * BUF;
-    if (i + 1 < mine) pf.load(a, bh, stid);  // this stream's step i+1, tokens ready
-    if (i + 2 < mine) {
-      pf.shift();
-      if (i + 3 < mine) GatherPipe<D>::tokens(a, sel, slen, steps[stream + 2 * (i + 3)], stid, pf.tok2, pf.tokl2, pf.okm2);
-    }
-    if (i < mine && nk > 0) {
-      const float* f = reinterpret_cast<const float*>(buf + 2 * Sh<D>::TILEB);
-      k_tile<D, DV, kHoistKvLocal<DV>>(buf, buf + Sh<D>::TILEB, f, f + 32, c2, st);
-    }
-    if (i + 1 < mine) pf.store(sbuf + ((i + 1) & 1) * BUF, stid);
-    __syncthreads();
-  }
-  // stream 1 hands its partial accumulator to stream 0 through LDS
-  float* xch = reinterpret_cast<float*>(smem) + kt * (32 * D);
-  if (stream == 1) {
-#pragma unroll
-    for (int dt = 0; dt < Sh<D>::DT; ++dt)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) xch[(dt * 16 + j) * 64 + lane] = st.acc[dt][j];
-  }
-  __syncthreads();
-  if (stream == 1 || nk <= 0) return;
-#pragma unroll
-  for (int dt = 0; dt < Sh<D>::DT; ++dt)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) st.acc[dt][j] += xch[(dt * 16 + j) * 64 + lane];
-  float* ob = (DV ? a.dvl : a.dkl) + (bh * g.NL + koff) * (size_t)D;
-  k_write<D, DV>(st, nk, DV ? 1.0f : g.scale, [&](int r, float*& dst) {
-    const int row = 32 * kt + r;
-    if (row >= ke.len) return false;
-    dst = ob + (size_t)block_token(g, ke, row) * D;
-    return true;
-  });
+  if (role == 0)
+    kvl_pass<D, true>(a, bh, p, kt, sel, slen, steps, nsteps, smem);
+  else
+    kvl_pass<D, false>(a, bh, p, kt, sel, slen, steps, nsteps, smem);
 }
 
 template <typename K>
@@ -834,8 +833,7 @@ hipError_t launch_d(const BwdArgs& base, hipStream_t s) {
     if (e == hipSuccess) e = set_lds(dq_local_kernel<D, false>, 2 * kLocBlocks * 2 * Sh<D>::TILEB);
     if (e == hipSuccess) e = set_lds(dkv_pers_kernel<D, true>, shm_kv);
     if (e == hipSuccess) e = set_lds(dkv_pers_kernel<D, false>, shm_kv);
-    if (e == hipSuccess) e = set_lds(dkv_local_kernel<D, true>, kvl_lds<D>(2048));
-    if (e == hipSuccess) e = set_lds(dkv_local_kernel<D, false>, kvl_lds<D>(2048));
+    if (e == hipSuccess) e = set_lds(dkv_local_kernel<D>, kvl_lds<D>(2048));
     if (e != hipSuccess) return e;
     attr = true;
   }
@@ -862,9 +860,7 @@ hipError_t launch_d(const BwdArgs& base, hipStream_t s) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   total = g.B * g.H * g.nl;
-  dkv_local_kernel<D, true><<<((total + 7) / 8) * 8, kKvlThreads, shm_kvl, s>>>(a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  dkv_local_kernel<D, false><<<((total + 7) / 8) * 8, kKvlThreads, shm_kvl, s>>>(a);
+  dkv_local_kernel<D><<<((total + 7) / 8) * 8, kKvlThreads, shm_kvl, s>>>(a);
   return hipGetLastError();
 }
 
