@@ -91,6 +91,8 @@ class Bench:
         self.ws_b = pb.workspace(p, "bwd")
         self.ws_u = pb.workspace(p, "persist_update")
         self.ws_f = pb.workspace(p, "fwd")
+        self.ws_fm = pb.workspace(p, "fwd_mass")
+        self.tmass = torch.empty(s["mass"], **f32)
         self.step_id = 0
 
     def reset(self):
@@ -207,6 +209,19 @@ def run_gpu(args, cfg):
     wall = time.perf_counter() - t0
     total_ms = start.elapsed_time(end)
     per_op = _op_stats(evs)
+    # the forward with token-exact masses (the cache pass's alternative mass)
+    L = b.live
+    fm = []
+    for k in range(args.steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.pb.pbsa_fwd_mass(b.p, b.q, L["k_p"], L["v_p"], L["plen"], L["k_l"], L["v_l"], b.topk, b.o, b.lse,
+                           b.tmass, b.ws_fm)
+        e1.record()
+        fm.append((e0, e1))
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(c) for a, c in fm])
+    per_op["fwd_mass"] = dict(mean=float(t.mean()), p50=float(np.median(t)), p99=float(np.percentile(t, 99)))
     # cold-cache pass: a 1 GiB fill before every op evicts L2 and the MALL
     cold = None
     if args.cold_steps > 0:
@@ -269,7 +284,7 @@ def run_rollout(cfg, steps: int, denoise: int):
     dk = torch.stack([dev(c["k"]) for c in chunks[1:]])
     dv = torch.stack([dev(c["v"]) for c in chunks[1:]])
 
-    def fresh():
+    def fresh(mass="pooled"):
         cache = pb.PBSACache(p)
         cache.k_pers.copy_(dev(x["k_p"]))
         cache.v_pers.copy_(dev(x["v_p"]))
@@ -279,15 +294,16 @@ def run_rollout(cfg, steps: int, denoise: int):
         cache.k_local[:, :, :ct].copy_(dev(chunks[0]["k"]))
         cache.v_local[:, :, :ct].copy_(dev(chunks[0]["v"]))
         cache.refresh_pooled_keys()
-        return cache, DecodeLoop(p, cache)
+        return cache, DecodeLoop(p, cache, mass=mass)
 
     out = {"steps": steps, "denoise_passes": denoise}
-    for mode in ("eager", "graph", "schedule"):
-        cache, loop = fresh()
+    for mode in ("eager", "graph", "schedule", "token_graph"):
+        mass = "token" if mode == "token_graph" else "pooled"
+        cache, loop = fresh(mass)
         nd = denoise if mode == "schedule" else 0
         loop.load_chunk(dq[0], dk[0], dv[0])
         if mode != "eager":
-            _, warm = fresh()
+            _, warm = fresh(mass)
             warm.load_chunk(dq[0], dk[0], dv[0])
             warm.step(nd)
             torch.cuda.synchronize()
@@ -309,8 +325,10 @@ def run_rollout(cfg, steps: int, denoise: int):
         elif mode == "graph":
             out["graph_ms_per_step"] = round(ms, 4)
             out["final_valid_persistent_tokens_per_head"] = float(cache.persist_len.sum(-1).float().mean())
-        else:
+        elif mode == "schedule":
             out["schedule_ms_per_chunk"] = round(ms, 4)
+        else:
+            out["token_mass_graph_ms_per_step"] = round(ms, 4)
     return out
 
 
@@ -361,6 +379,7 @@ def main():
     per_op = {op: v["mean"] for op, v in stats.items()}
     kern = {op: {"ms": round(v["mean"], 4), "p50_ms": round(v["p50"], 4), "p99_ms": round(v["p99"], 4)}
             for op, v in stats.items()}
+    kern["fwd_mass"]["extra_ms_over_fwd"] = round(per_op["fwd_mass"] - per_op["fwd"], 4)
     kern_cold = {}
     if acc:
         pairs = float(np.mean([a["pairs"] for a in acc]))
