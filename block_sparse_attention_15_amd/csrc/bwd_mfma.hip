@@ -16,7 +16,7 @@
 //             from LDS (ds_read_b64_tr_b16).  Writes dq.
 //   dq_local  the same over each query block's selected local blocks (8 waves
 //             = 4 query blocks x 2 query tiles); adds into dq.
-//   dkv_pers  key-outer: 4 waves x 32 keys (two slots) stream every query of
+//   dkv_pers  key-outer: 8 waves x 32 keys (four slots) stream every query of
 //             the head through LDS in 32-row tiles; S = Q K^T and dP = dO V^T
 //             put one key per lane, dV += P^T dO and dK += dS^T Q read dO and
 //             Q transposed from LDS.
@@ -516,7 +516,7 @@ __device__ __forceinline__ void k_write(const KState<D, DV>& st, int n, float sc
   }
 }
 
-constexpr int kKvWaves = 4;       // dkv_pers: 4 waves = 2 slots x 2 key tiles
+constexpr int kKvWaves = 8;       // dkv_pers: 8 waves = 4 slots x 2 key tiles
 constexpr int kKvThreads = 64 * kKvWaves;
 constexpr int kKvSlots = kKvWaves / 2;
 
@@ -579,7 +579,7 @@ struct QTileLoader {
 };
 
 template <int D, bool DV>
-__global__ __launch_bounds__(kKvThreads, 2) void dkv_pers_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kKvThreads, 1) void dkv_pers_kernel(BwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int BUF = 2 * Sh<D>::TILEB + 256;
   const Geo& g = a.g;
@@ -604,23 +604,30 @@ __global__ __launch_bounds__(kKvThreads, 2) void dkv_pers_kernel(BwdArgs a) {
     int base, ct;
     __device__ int operator()(int i) const { return base + i < ct ? base + i : -1; }
   };
-  QTileLoader<D, kKvThreads, Contig> pf;
-  pf.load(a, bh, Contig{0, g.ct});
-  pf.store(smem);
+  // Query tiles are prefetched two steps ahead into two register sets that
+  // alternate by step (tile i+1 is stored into LDS at the end of step i while
+  // tile i+2 is in flight); LDS holds two tiles.
+  using Loader = QTileLoader<D, kKvThreads, Contig>;
+  Loader pa, pb;
+  pa.load(a, bh, Contig{0, g.ct});
+  pa.store(smem);
+  if (nsteps > 1) pa.load(a, bh, Contig{32, g.ct});
+  if (nsteps > 2) pb.load(a, bh, Contig{64, g.ct});
   __syncthreads();
-  // unrolled by two so that each half's LDS buffer is a compile-time offset
-  auto step = [&](int i, char* buf, char* nxt) {
-    if (i + 1 < nsteps) pf.load(a, bh, Contig{32 * (i + 1), g.ct});
+  // cur holds tile i+1 and nx tile i+2; unrolled by two so that the LDS
+  // buffers and the register sets are fixed at compile time
+  auto step = [&](int i, char* buf, char* nxt, Loader& cur) {
     if (nk > 0) {
       const float* f = reinterpret_cast<const float*>(buf + 2 * Sh<D>::TILEB);
       k_tile<D, DV, kHoistKvPers<DV>>(buf, buf + Sh<D>::TILEB, f, f + 32, c2, st);
     }
-    if (i + 1 < nsteps) pf.store(nxt);
+    if (i + 1 < nsteps) cur.store(nxt);
+    if (i + 3 < nsteps) cur.load(a, bh, Contig{32 * (i + 3), g.ct});
     __syncthreads();
   };
   for (int i = 0; i < nsteps; i += 2) {
-    step(i, smem, smem + BUF);
-    if (i + 1 < nsteps) step(i + 1, smem + BUF, smem);
+    step(i, smem, smem + BUF, pa);
+    if (i + 1 < nsteps) step(i + 1, smem + BUF, smem, pb);
   }
   if (!has_slot || 32 * kh >= g.C) return;
   float* ob = (DV ? a.dvp : a.dkp) + sbase;
