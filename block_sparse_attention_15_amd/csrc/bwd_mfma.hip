@@ -63,6 +63,24 @@ __device__ __forceinline__ bf16x8_t rd_nat(const char* t, int r, int c) {
   return *reinterpret_cast<const bf16x8_t*>(t + r * Sh<D>::ROWB + swz(r, c, Sh<D>::CPR) * 16);
 }
 
+// Natural-layout operands by k-step, addressed from the LDS array `arr` that
+// holds the tile (tile offset `rel` in it a multiple of 256 bytes): with the
+// XOR swizzle the byte offset of chunk 2*ks+h of row r inside its row is
+// (32*ks) ^ (16*h ^ 16*swizzle(r)), so one XOR with the lane's base offset
+// per read stands in for a live offset register per k-step.  The empty asm
+// keeps the base opaque so the per-k-step offsets are not hoisted out of the
+// caller's loop.
+template <int D>
+__device__ __forceinline__ int nat_base(int rel, int r, int h) {
+  int off = rel + r * Sh<D>::ROWB + ((16 * h) ^ (16 * swz(r, 0, Sh<D>::CPR)));
+  asm volatile("" : "+v"(off));
+  return off;
+}
+template <int D>
+__device__ __forceinline__ bf16x8_t rd_nat_at(const char* arr, int base, int ks) {
+  return *reinterpret_cast<const bf16x8_t*>(arr + (base ^ (32 * ks)));
+}
+
 // Transposed operand from a 32-row tile: lane l receives column 32*dt + l%32
 // at rows 16*ks2 + 4*(l/32) + {0,1,2,3} and the same +8 (the row order that
 // matches the packing of a 32x32 MFMA result into the next product).
@@ -123,7 +141,6 @@ struct BwdArgs {
 // Which tiles read their transposed operands ahead of the VALU work (only
 // where the registers allow it without spilling).
 constexpr bool kHoistDqPers = true;
-constexpr bool kHoistDqLocal = false;
 template <bool DV> constexpr bool kHoistKvPers = true;
 template <bool DV> constexpr bool kHoistKvLocal = DV;
 
@@ -153,26 +170,53 @@ __device__ __forceinline__ void q_init(const BwdArgs& a, size_t bh, int tok, boo
   st.dl = ok ? a.delta[row] : 0.f;
 }
 
-// One 32-key tile: K tile tk, V tile tv (32 rows each), nvalid leading keys.
-// HOIST: read the transposed K operands of dQ before the VALU work (their
-// LDS latency is then covered), at the cost of 2*DT more live registers.
-template <int D, bool HOIST>
-__device__ __forceinline__ void q_tile(const char* tk, const char* tv, int nvalid, float c2, QState<D>& st) {
+// One 32-key tile: K tile at arr + tk_rel, V tile at arr + tv_rel (32 rows
+// each), nvalid leading keys.  HOIST: read the transposed K operands of dQ
+// ahead of the VALU work (their LDS latency is then covered), at the cost of
+// 2*DT more live registers; EARLY: read them first of all, then call mid()
+// (the local kernel issues its next gather there: the compiler cannot tell
+// transposed LDS reads from an LDS-bound load in flight and would wait for
+// it).  XADDR: natural reads through per-read XOR offsets (nat_base) rather
+// than one live offset register per k-step (fewer registers, more VALU).
+struct NoMid {
+  __device__ void operator()() const {}
+};
+template <int D, bool HOIST, bool EARLY = false, bool XADDR = false, typename Mid = NoMid>
+__device__ __forceinline__ void q_tile(const char* arr, int tk_rel, int tv_rel, int nvalid, float c2,
+                                       QState<D>& st, Mid mid = Mid{}) {
+  static_assert(HOIST || !EARLY, "EARLY reads are hoisted reads");
   const int lane = threadIdx.x & 63, h = lane >> 5, l32 = lane & 31;
-  f32x16_t s = {}, dp = {};
-#pragma unroll
-  for (int ks = 0; ks < Sh<D>::KS; ++ks) {
-    s = mfma(rd_nat<D>(tk, l32, 2 * ks + h), st.qf[ks], s);
-    dp = mfma(rd_nat<D>(tv, l32, 2 * ks + h), st.df[ks], dp);
-  }
+  const char* tk = arr + tk_rel;
   bf16x8_t kt[HOIST ? Sh<D>::DT : 1][2];
-  if (HOIST) {
+  auto read_kt = [&]() {
 #pragma unroll
     for (int dt = 0; dt < Sh<D>::DT; ++dt) {
       kt[HOIST ? dt : 0][0] = rd_tr<D>(tk, 0, dt);
       kt[HOIST ? dt : 0][1] = rd_tr<D>(tk, 1, dt);
     }
+  };
+  if (EARLY) {
+    read_kt();
+    __builtin_amdgcn_sched_barrier(0);  // keep mid() after the reads
   }
+  mid();
+  f32x16_t s = {}, dp = {};
+  if (XADDR) {
+    const int bk = nat_base<D>(tk_rel, l32, h), bv = nat_base<D>(tv_rel, l32, h);
+#pragma unroll
+    for (int ks = 0; ks < Sh<D>::KS; ++ks) {
+      s = mfma(rd_nat_at<D>(arr, bk, ks), st.qf[ks], s);
+      dp = mfma(rd_nat_at<D>(arr, bv, ks), st.df[ks], dp);
+    }
+  } else {
+    const char* tv = arr + tv_rel;
+#pragma unroll
+    for (int ks = 0; ks < Sh<D>::KS; ++ks) {
+      s = mfma(rd_nat<D>(tk, l32, 2 * ks + h), st.qf[ks], s);
+      dp = mfma(rd_nat<D>(tv, l32, 2 * ks + h), st.df[ks], dp);
+    }
+  }
+  if (HOIST && !EARLY) read_kt();
   f32x16_t ds;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
@@ -251,8 +295,9 @@ __global__ __launch_bounds__(kDqThreads, 1) void dq_pers_kernel(BwdArgs a) {
       const int n = min(a.plen[bh * g.S + s], g.C);
       if (s + 1 < g.S) slot_load<D>(a, bh, s + 1, pf);
       if (active) {
-        if (n > 0) q_tile<D, kHoistDqPers>(buf, buf + 2 * Sh<D>::TILEB, min(n, 32), c2, st);
-        if (n > 32) q_tile<D, kHoistDqPers>(buf + Sh<D>::TILEB, buf + 3 * Sh<D>::TILEB, n - 32, c2, st);
+        const int rb = (s & 1) * BUF;
+        if (n > 0) q_tile<D, kHoistDqPers>(smem, rb, rb + 2 * Sh<D>::TILEB, min(n, 32), c2, st);
+        if (n > 32) q_tile<D, kHoistDqPers>(smem, rb + Sh<D>::TILEB, rb + 3 * Sh<D>::TILEB, n - 32, c2, st);
       }
       if (s + 1 < g.S) slot_store<D>(pf, smem + ((s + 1) & 1) * BUF);
       __syncthreads();
@@ -273,11 +318,6 @@ __global__ __launch_bounds__(kDqThreads, 1) void dq_pers_kernel(BwdArgs a) {
 // half of each query block's current selected block (K and V) is staged.
 constexpr int kLocBlocks = 4;  // query blocks per workgroup (2 waves each)
 constexpr int kDqlThreads = 64 * 2 * kLocBlocks;
-
-template <int D> struct LocPf {
-  static constexpr int N = kLocBlocks * 32 * Sh<D>::CPR / kDqlThreads;
-  uint4 k[N], v[N];
-};
 
 // Row tokens of every step of this workgroup, built once in LDS (see the
 // forward's local kernel): rowtab[(w*K + t)*64 + r], lentab[w*K + t].
@@ -302,61 +342,59 @@ __device__ __forceinline__ void build_rowtab(const BwdArgs& a, size_t bh, int qg
   }
 }
 
-// TAB (row addresses from the LDS table) is a compile-time choice so that the
-// global-memory address path does not share the loop: joining the two makes
-// the compiler wait for every outstanding load, the K/V prefetch included.
+// One local step gathered straight into LDS (global_load_lds_dwordx4): no
+// staging registers and no LDS store instructions.  An instruction fills 1 KB
+// of the buffer (lane l at byte 16*l); lane l fetches the global chunk whose
+// swizzled position is l's, so the tile lands in the swizzled layout.  Rows
+// past a selected block's end (and absent selections) load row 0 of the
+// head's queries instead: finite values whose keys the tile masks.  TAB:
+// row tokens from the LDS table (compile-time, see the forward's local
+// kernel).
 template <int D, bool TAB>
-__device__ __forceinline__ void loc_load(const BwdArgs& a, size_t bh, int qg, int j, LocPf<D>& pf,
-                                         const int* rowtab) {
+__device__ __forceinline__ void loc_gather(const BwdArgs& a, size_t bh, int qg, int j, char* buf,
+                                           const int* rowtab) {
+  constexpr int RPK = 1024 / Sh<D>::ROWB;                // rows per KB unit
+  constexpr int UPT = Sh<D>::TILEB / 1024;               // KB units per 32-row tile
+  constexpr int PER_WAVE = kLocBlocks * 2 * UPT / (kDqlThreads / 64);
   const Geo& g = a.g;
   const int t = j >> 1, half = j & 1;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int rr = lane / Sh<D>::CPR, pos = lane % Sh<D>::CPR;
   const bf16_t* kb = a.kl + bh * (size_t)g.NL * D;
   const bf16_t* vb = a.vl + bh * (size_t)g.NL * D;
+  const bf16_t* fill = a.q + bh * (size_t)g.ct * D;
 #pragma unroll
-  for (int u = 0; u < LocPf<D>::N; ++u) {
-    const int id = threadIdx.x + kDqlThreads * u;
-    const int w = id / (32 * Sh<D>::CPR), rem = id % (32 * Sh<D>::CPR);
-    const int r = 32 * half + rem / Sh<D>::CPR, c = rem % Sh<D>::CPR;
-    const int qb = qg * kLocBlocks + w;
-    bool ok = false;
-    size_t off = 0;
+  for (int i = 0; i < PER_WAVE; ++i) {
+    const int u = wave * PER_WAVE + i;
+    const int w = u / (2 * UPT), tensor = (u / UPT) & 1;
+    const int r = RPK * (u % UPT) + rr;  // row in the 32-row tile
+    const int c = swz(r, pos, Sh<D>::CPR);
+    int tok = -1;
     if (TAB) {
-      const int tok = rowtab[(w * g.K + t) * 64 + r];
-      ok = tok >= 0;
-      off = (size_t)(ok ? tok : 0) * D + c * 8;
-    } else if (qb < g.nq) {
-      const int p = a.topk[(bh * g.nq + qb) * g.K + t];
-      if ((unsigned)p < (unsigned)g.nl && r < g.C) {
-        const int tok = a.tab.btok[a.tab.pblk[p] * g.C + r];
-        if (tok >= 0) {
-          ok = true;
-          off = (size_t)(a.tab.pbase[p] + tok) * D + c * 8;
+      tok = rowtab[(w * g.K + t) * 64 + 32 * half + r];
+    } else {
+      const int qb = qg * kLocBlocks + w;
+      if (qb < g.nq) {
+        const int p = a.topk[(bh * g.nq + qb) * g.K + t];
+        if ((unsigned)p < (unsigned)g.nl && 32 * half + r < g.C) {
+          const int bt = a.tab.btok[a.tab.pblk[p] * g.C + 32 * half + r];
+          if (bt >= 0) tok = a.tab.pbase[p] + bt;
         }
       }
     }
-    pf.k[u] = ok ? ld16(kb + off) : make_uint4(0, 0, 0, 0);
-    pf.v[u] = ok ? ld16(vb + off) : make_uint4(0, 0, 0, 0);
-  }
-}
-
-// LDS: region w = [K tile, V tile]
-template <int D>
-__device__ __forceinline__ void loc_store(const LocPf<D>& pf, char* buf) {
-#pragma unroll
-  for (int u = 0; u < LocPf<D>::N; ++u) {
-    const int id = threadIdx.x + kDqlThreads * u;
-    const int w = id / (32 * Sh<D>::CPR), rem = id % (32 * Sh<D>::CPR);
-    const int r = rem / Sh<D>::CPR, c = rem % Sh<D>::CPR;
-    char* region = buf + w * 2 * Sh<D>::TILEB;
-    st_chunk(region, Sh<D>::ROWB, Sh<D>::CPR, r, c, pf.k[u]);
-    st_chunk(region + Sh<D>::TILEB, Sh<D>::ROWB, Sh<D>::CPR, r, c, pf.v[u]);
+    const bf16_t* src = (tok >= 0 ? (tensor ? vb : kb) + (size_t)tok * D : fill) + c * 8;
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(buf + u * 1024), 16, 0, 0);
   }
 }
 
 template <int D, bool TAB>
 __global__ __launch_bounds__(kDqlThreads, 1) void dq_local_kernel(BwdArgs a) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
+  extern __shared__ __attribute__((aligned(16))) char smem[];  // row tables
   constexpr int BUF = kLocBlocks * 2 * Sh<D>::TILEB;
+  // the two step buffers are separate arrays so that the compiler can tell the
+  // gather into one from the reads of the other
+  __shared__ __attribute__((aligned(1024))) char kv0[BUF];
+  __shared__ __attribute__((aligned(1024))) char kv1[BUF];
   const Geo& g = a.g;
   const int total = g.B * g.H * a.ntiles;
   const int lin = xcd_remap(total);
@@ -375,18 +413,16 @@ __global__ __launch_bounds__(kDqlThreads, 1) void dq_local_kernel(BwdArgs a) {
   q_init<D>(a, bh, tok, ok, st);
   const float c2 = g.scale * kLog2e;
   const int nsteps = 2 * g.K;
-  int* rowtab = reinterpret_cast<int*>(smem + 2 * BUF);
+  int* rowtab = reinterpret_cast<int*>(smem);
   int* lentab = rowtab + kLocBlocks * g.K * 64;
   if (TAB) {
     build_rowtab(a, bh, qg, kDqlThreads, rowtab, lentab);
     __syncthreads();
   }
-  LocPf<D> pf;
-  loc_load<D, TAB>(a, bh, qg, 0, pf, rowtab);
-  loc_store<D>(pf, smem);
-  __syncthreads();
-  for (int j = 0; j < nsteps; ++j) {
-    char* buf = smem + (j & 1) * BUF;
+  loc_gather<D, TAB>(a, bh, qg, 0, kv0, rowtab);
+  __syncthreads();  // its fence waits for the gather
+  // unrolled by two so that each step's buffers are compile-time arrays
+  auto step = [&](int j, char* cur, char* nxt) {
     int nv = 0;
     if (active) {
       int len = 0;
@@ -398,13 +434,21 @@ __global__ __launch_bounds__(kDqlThreads, 1) void dq_local_kernel(BwdArgs a) {
       }
       nv = min(len - 32 * (j & 1), 32);
     }
-    if (j + 1 < nsteps) loc_load<D, TAB>(a, bh, qg, j + 1, pf, rowtab);
+    nv = __builtin_amdgcn_readfirstlane(nv);  // uniform per wave: a scalar branch
+    auto gather = [&]() {
+      if (j + 1 < nsteps) loc_gather<D, TAB>(a, bh, qg, j + 1, nxt, rowtab);
+    };
     if (nv > 0) {
-      const char* region = buf + (wave >> 1) * 2 * Sh<D>::TILEB;
-      q_tile<D, kHoistDqLocal>(region, region + Sh<D>::TILEB, nv, c2, st);
+      const int rel = (wave >> 1) * 2 * Sh<D>::TILEB;
+      q_tile<D, true, true, true>(cur, rel, rel + Sh<D>::TILEB, nv, c2, st, gather);
+    } else {
+      gather();
     }
-    if (j + 1 < nsteps) loc_store<D>(pf, smem + ((j + 1) & 1) * BUF);
     __syncthreads();
+  };
+  for (int j = 0; j < nsteps; j += 2) {
+    step(j, kv0, kv1);
+    if (j + 1 < nsteps) step(j + 1, kv1, kv0);
   }
   if (!ok) return;
   float* out = a.dq + (bh * g.ct + tok) * D;
@@ -828,16 +872,14 @@ hipError_t launch_d(const BwdArgs& base, hipStream_t s) {
   const size_t shm_dq = 2 * 4 * Sh<D>::TILEB;                 // persistent: 2 x (K,K,V,V)
   const size_t tabb = (size_t)kLocBlocks * g.K * 64 * 4;
   const bool tab = tabb <= (size_t)kRowTabMax;
-  const size_t shm_dql = 2 * kLocBlocks * 2 * Sh<D>::TILEB +   // local: 2 x 4 x (K,V)
-                         (tab ? tabb + kLocBlocks * g.K * 4 : 0);
+  const size_t shm_dql = tab ? tabb + kLocBlocks * g.K * 4 : 0;  // local: row tables (step buffers are static)
   const size_t shm_kv = 2 * (2 * Sh<D>::TILEB + 256);
   const size_t shm_kvl = kvl_lds<D>(g.nq);
   static bool attr = false;
   if (!attr) {
     hipError_t e = set_lds(dq_pers_kernel<D>, shm_dq);
     if (e == hipSuccess)
-      e = set_lds(dq_local_kernel<D, true>, 2 * kLocBlocks * 2 * Sh<D>::TILEB + kRowTabMax + 4096);
-    if (e == hipSuccess) e = set_lds(dq_local_kernel<D, false>, 2 * kLocBlocks * 2 * Sh<D>::TILEB);
+      e = set_lds(dq_local_kernel<D, true>, kRowTabMax + 4096);
     if (e == hipSuccess) e = set_lds(dkv_pers_kernel<D, true>, shm_kv);
     if (e == hipSuccess) e = set_lds(dkv_pers_kernel<D, false>, shm_kv);
     if (e == hipSuccess) e = set_lds(dkv_local_kernel<D>, kvl_lds<D>(2048));
