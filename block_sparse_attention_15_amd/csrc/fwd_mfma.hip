@@ -104,15 +104,52 @@ template <int D, int NT> struct WaveState {
 
 constexpr float kLn2 = 0.6931471805599453f;
 
+struct NoMid {
+  __device__ void operator()() const {}
+};
+
+// V^T operands of O^T += V^T P^T for keys row0 .. row0+31, read transposed
+// from LDS (two ds_read_b64_tr_b16 per 8-key operand).
+template <int D>
+__device__ __forceinline__ void read_vt(const char* vbase, int row0, bf16x8_t (&va)[Shape<D>::DT][2]) {
+  using Sh = Shape<D>;
+  const int lane = threadIdx.x & 63, G = lane >> 4, s16 = lane & 15;
+#pragma unroll
+  for (int dt = 0; dt < Sh::DT; ++dt) {
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2) {
+      s16x4_t part[2];
+#pragma unroll
+      for (int h8 = 0; h8 < 2; ++h8) {
+        const int r = row0 + 16 * ks2 + 8 * h8 + 4 * (G >> 1) + (s16 >> 2);
+        const int col = 32 * dt + 16 * (G & 1) + 4 * (s16 & 3);
+        const char* p = vbase + r * Sh::ROWB + swz_v(r, col >> 3, Sh::CPR) * 16 + (col & 7) * 2;
+        part[h8] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(p));
+      }
+      va[dt][ks2] = __builtin_bit_cast(bf16x8_t, (__attribute__((ext_vector_type(8))) short){
+          part[0][0], part[0][1], part[0][2], part[0][3], part[1][0], part[1][1], part[1][2], part[1][3]});
+    }
+  }
+}
+
 // One 32-key tile in LDS: K rows kbase[row0 .. row0+31], V rows likewise,
 // the first nvalid (1..32) keys valid.  ntq (<= NT) query tiles are active.
 // Returns this lane's part of the tile's probability sum for query tile 0,
-// relative to the running max after the tile.
-template <int D, int NT>
+// relative to the running max after the tile.  EARLY: read the V^T operands
+// first and then call mid() (the local kernel issues its next LDS-bound
+// gather there: the compiler cannot tell transposed LDS reads from such a
+// load in flight and would wait for it).
+template <int D, int NT, bool EARLY = false, typename Mid = NoMid>
 __device__ __forceinline__ float tile(const char* kbase, const char* vbase, int row0, int nvalid, int ntq, float c2,
-                                     WaveState<D, NT>& st) {
+                                     WaveState<D, NT>& st, Mid mid = Mid{}) {
   using Sh = Shape<D>;
   const int lane = threadIdx.x & 63, h = lane >> 5, l32 = lane & 31;
+  bf16x8_t va[Sh::DT][2];
+  if (EARLY) {
+    read_vt<D>(vbase, row0, va);
+    __builtin_amdgcn_sched_barrier(0);  // keep mid() after the reads
+  }
+  mid();
   f32x16_t s[NT];
 #pragma unroll
   for (int n = 0; n < NT; ++n) s[n] = f32x16_t{};
@@ -130,26 +167,9 @@ __device__ __forceinline__ float tile(const char* kbase, const char* vbase, int 
         if (n < ntq) s[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], st.qf[n][ks], s[n], 0, 0, 0);
     }
   }
-  // V^T operands of O^T += V^T P^T, read transposed from LDS now: they do
-  // not depend on P, so their latency is covered by the softmax below
-  const int G = lane >> 4, s16 = lane & 15;
-  bf16x8_t va[Sh::DT][2];
-#pragma unroll
-  for (int dt = 0; dt < Sh::DT; ++dt) {
-#pragma unroll
-    for (int ks2 = 0; ks2 < 2; ++ks2) {
-      s16x4_t part[2];
-#pragma unroll
-      for (int h8 = 0; h8 < 2; ++h8) {
-        const int r = row0 + 16 * ks2 + 8 * h8 + 4 * (G >> 1) + (s16 >> 2);
-        const int col = 32 * dt + 16 * (G & 1) + 4 * (s16 & 3);
-        const char* p = vbase + r * Sh::ROWB + swz_v(r, col >> 3, Sh::CPR) * 16 + (col & 7) * 2;
-        part[h8] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(p));
-      }
-      va[dt][ks2] = __builtin_bit_cast(bf16x8_t, (__attribute__((ext_vector_type(8))) short){
-          part[0][0], part[0][1], part[0][2], part[0][3], part[1][0], part[1][1], part[1][2], part[1][3]});
-    }
-  }
+  // V^T operands read now if not yet: they do not depend on P, so their
+  // latency is covered by the softmax below
+  if (!EARLY) read_vt<D>(vbase, row0, va);
   if (nvalid < 32) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
@@ -365,11 +385,6 @@ constexpr int kLocBlocks = 4;
 constexpr int kLocWaves = 2 * kLocBlocks;
 constexpr int kLocThreads = 64 * kLocWaves;
 
-template <int D> struct LocPrefetch {
-  static constexpr int N = kLocBlocks * 32 * Shape<D>::CPR / kLocThreads;
-  uint4 k[N], v[N];
-};
-
 // Row tokens of every step of this workgroup, built once in LDS:
 // rowtab[(w*K + t)*64 + r] = ring row of row r of query block w's t-th
 // selected block, or -1.  Used when it fits (4*K*64 ints <= kRowTabMax).
@@ -394,62 +409,61 @@ __device__ __forceinline__ void build_rowtab(const FwdArgs& a, size_t bh, int qg
   }
 }
 
-// TAB: row addresses come from the LDS row table.  Kept a compile-time
-// choice: if the global-memory address path shares the loop, the compiler
-// joins the two with a full vmcnt wait that also drains the K/V prefetch.
+// One local step gathered straight into LDS (global_load_lds_dwordx4): no
+// staging registers and no LDS store instructions.  An instruction fills 1 KB
+// of the buffer (lane l at byte 16*l); lane l fetches the global chunk whose
+// swizzled position is l's, so K and V land in their swizzled layouts.  Rows
+// past a selected block's end (and absent selections) load row 0 of the
+// head's queries instead: finite values whose keys the tile masks.  TAB: row
+// tokens from the LDS row table (a compile-time choice: if the global-memory
+// address path shares the loop, the compiler joins the two with a full wait).
 template <int D, bool TAB>
-__device__ __forceinline__ void loc_load(const FwdArgs& a, size_t bh, int qg, int j, LocPrefetch<D>& pf,
-                                         const int* rowtab) {
+__device__ __forceinline__ void loc_gather(const FwdArgs& a, size_t bh, int qg, int j, char* buf,
+                                           const int* rowtab) {
   using Sh = Shape<D>;
+  constexpr int RPK = 1024 / Sh::ROWB;                 // rows per KB unit
+  constexpr int UPT = 32 * Sh::ROWB / 1024;            // KB units per 32-row tile
+  constexpr int PER_WAVE = kLocBlocks * 2 * UPT / kLocWaves;
   const Geo& g = a.g;
   const int t = j >> 1, half = j & 1;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int rr = lane / Sh::CPR, pos = lane % Sh::CPR;
   const bf16_t* kb = a.kl + bh * (size_t)g.NL * D;
   const bf16_t* vb = a.vl + bh * (size_t)g.NL * D;
+  const bf16_t* fill = a.q + bh * (size_t)g.ct * D;
 #pragma unroll
-  for (int u = 0; u < LocPrefetch<D>::N; ++u) {
-    const int id = threadIdx.x + kLocThreads * u;
-    const int w = id / (32 * Sh::CPR), rem = id % (32 * Sh::CPR);
-    const int r = 32 * half + rem / Sh::CPR, c = rem % Sh::CPR;
-    const int qb = qg * kLocBlocks + w;
-    bool ok = false;
-    size_t off = 0;
+  for (int i = 0; i < PER_WAVE; ++i) {
+    const int u = wave * PER_WAVE + i;
+    const int w = u / (2 * UPT), tensor = (u / UPT) & 1;
+    const int r = RPK * (u % UPT) + rr;  // row in the 32-row tile
+    const int c = tensor ? swz_v(r, pos, Sh::CPR) : swz_k(r, pos, Sh::CPR);
+    int tok = -1;
     if (TAB) {
-      const int tok = rowtab[(w * g.K + t) * 64 + r];
-      ok = tok >= 0;
-      off = (size_t)(ok ? tok : 0) * D + c * 8;
-    } else if (qb < g.nq) {
-      const int p = a.topk[(bh * g.nq + qb) * g.K + t];
-      if ((unsigned)p < (unsigned)g.nl && r < g.C) {
-        const int tok = a.tab.btok[a.tab.pblk[p] * g.C + r];
-        if (tok >= 0) {
-          ok = true;
-          off = (size_t)(a.tab.pbase[p] + tok) * D + c * 8;
+      tok = rowtab[(w * g.K + t) * 64 + 32 * half + r];
+    } else {
+      const int qb = qg * kLocBlocks + w;
+      if (qb < g.nq) {
+        const int p = a.topk[(bh * g.nq + qb) * g.K + t];
+        if ((unsigned)p < (unsigned)g.nl && 32 * half + r < g.C) {
+          const int bt = a.tab.btok[a.tab.pblk[p] * g.C + 32 * half + r];
+          if (bt >= 0) tok = a.tab.pbase[p] + bt;
         }
       }
     }
-    pf.k[u] = ok ? ld16(kb + off) : make_uint4(0, 0, 0, 0);
-    pf.v[u] = ok ? ld16(vb + off) : make_uint4(0, 0, 0, 0);
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void loc_store(const LocPrefetch<D>& pf, char* buf) {
-  using Sh = Shape<D>;
-#pragma unroll
-  for (int u = 0; u < LocPrefetch<D>::N; ++u) {
-    const int id = threadIdx.x + kLocThreads * u;
-    const int w = id / (32 * Sh::CPR), rem = id % (32 * Sh::CPR);
-    const int r = rem / Sh::CPR, c = rem % Sh::CPR;
-    char* region = buf + w * (64 * Sh::ROWB);
-    st16(region + r * Sh::ROWB + swz_k(r, c, Sh::CPR) * 16, pf.k[u]);
-    st16(region + 32 * Sh::ROWB + r * Sh::ROWB + swz_v(r, c, Sh::CPR) * 16, pf.v[u]);
+    const bf16_t* src = (tok >= 0 ? (tensor ? vb : kb) + (size_t)tok * D : fill) + c * 8;
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(buf + u * 1024), 16, 0, 0);
   }
 }
 
 template <int D, bool MASS, bool TAB>
 __global__ __launch_bounds__(kLocThreads, 1) void fwd_local_kernel(FwdArgs a) {
   using Sh = Shape<D>;
-  extern __shared__ __attribute__((aligned(16))) char smem[];
+  extern __shared__ __attribute__((aligned(16))) char smem[];  // row tables
+  constexpr int BUF = kLocBlocks * 64 * Sh::ROWB;            // per block: 32 K rows, 32 V rows
+  // the two step buffers are separate arrays so that the compiler can tell the
+  // gather into one from the reads of the other
+  __shared__ __attribute__((aligned(1024))) char kv0[BUF];
+  __shared__ __attribute__((aligned(1024))) char kv1[BUF];
   const Geo& g = a.g;
   const int total = g.B * g.H * a.ntiles;
   const int lin = xcd_remap(total);
@@ -471,19 +485,17 @@ __global__ __launch_bounds__(kLocThreads, 1) void fwd_local_kernel(FwdArgs a) {
   const float c2 = g.scale * 1.4426950408889634f;
 
   const int nsteps = 2 * g.K;
-  int* rowtab = reinterpret_cast<int*>(smem + 2 * kBufBytes);
+  int* rowtab = reinterpret_cast<int*>(smem);
   int* lentab = rowtab + kLocBlocks * g.K * 64;
   if (TAB) {
     build_rowtab(a, bh, qg, kLocThreads, rowtab, lentab);
     __syncthreads();
   }
-  LocPrefetch<D> pf;
-  loc_load<D, TAB>(a, bh, qg, 0, pf, rowtab);
-  loc_store<D>(pf, smem);
-  __syncthreads();
-  float bs = 0.f;  // this lane's probability sum over the current selected block (MASS)
-  for (int j = 0; j < nsteps; ++j) {
-    char* buf = smem + (j & 1) * kBufBytes;
+  loc_gather<D, TAB>(a, bh, qg, 0, kv0, rowtab);
+  __syncthreads();  // its fence waits for the gather
+  float bs = 0.f;   // this lane's probability sum over the current selected block (MASS)
+  // unrolled by two so that each step's buffers are compile-time arrays
+  auto step = [&](int j, char* cur, char* nxt) {
     int nv = 0;
     if (ntq) {
       int len = 0;
@@ -495,24 +507,29 @@ __global__ __launch_bounds__(kLocThreads, 1) void fwd_local_kernel(FwdArgs a) {
       }
       nv = min(len - 32 * (j & 1), 32);
     }
-    if (j + 1 < nsteps) loc_load<D, TAB>(a, bh, qg, j + 1, pf, rowtab);
+    nv = __builtin_amdgcn_readfirstlane(nv);  // uniform per wave: a scalar branch
+    auto gather = [&]() {
+      if (j + 1 < nsteps) loc_gather<D, TAB>(a, bh, qg, j + 1, nxt, rowtab);
+    };
     if (nv > 0) {
-      const char* region = buf + (wave >> 1) * (64 * Sh::ROWB);
+      const char* region = cur + (wave >> 1) * (64 * Sh::ROWB);
       const float m0 = st.m[0];
-      const float ts = tile<D, 1>(region, region + 32 * Sh::ROWB, 0, nv, 1, c2, st);
+      const float ts = tile<D, 1, true>(region, region + 32 * Sh::ROWB, 0, nv, 1, c2, st, gather);
       if (MASS) bs = (j & 1) ? bs * __builtin_amdgcn_exp2f(m0 - st.m[0]) + ts : ts;
-    } else if (MASS && !(j & 1)) {
-      bs = 0.f;
+    } else {
+      gather();
+      if (MASS && !(j & 1)) bs = 0.f;
     }
-    float bl = 0.f;
     if (MASS && (j & 1) && ntq) {
-      const float tot = half_sum(bs);
-      bl = tot > 0.f ? st.m[0] + __builtin_amdgcn_logf(tot) : -INFINITY;
+      const float tot = half_sum(bs);  // lane exchange: both halves of the wave take part
+      if (h == 0 && row_ok)
+        a.blse_l[(bh * g.K + (j >> 1)) * g.ct + tok] = tot > 0.f ? st.m[0] + __builtin_amdgcn_logf(tot) : -INFINITY;
     }
-    if (j + 1 < nsteps) loc_store<D>(pf, smem + ((j + 1) & 1) * kBufBytes);
-    // stored after the LDS fill (its wait for the prefetch must not wait for this store)
-    if (MASS && (j & 1) && ntq && h == 0 && row_ok) a.blse_l[(bh * g.K + (j >> 1)) * g.ct + tok] = bl;
     __syncthreads();
+  };
+  for (int j = 0; j < nsteps; j += 2) {
+    step(j, kv0, kv1);
+    if (j + 1 < nsteps) step(j + 1, kv1, kv0);
   }
 
   // merge with the persistent partial and write O (bf16) and LSE
@@ -564,11 +581,10 @@ hipError_t launch_d(const FwdArgs& base, hipStream_t s) {
   const Geo& g0 = base.g;
   const size_t tabb = (size_t)kLocBlocks * g0.K * 64 * 4;
   const bool tab = tabb <= (size_t)kRowTabMax;
-  const size_t shm_loc = shm + (tab ? tabb + kLocBlocks * g0.K * 4 : 0);
+  const size_t shm_loc = tab ? tabb + kLocBlocks * g0.K * 4 : 0;  // row tables (step buffers are static)
   if (!attr) {
     hipError_t e = set_lds(fwd_pers_kernel<D, MASS>, shm);
-    if (e == hipSuccess) e = set_lds(fwd_local_kernel<D, MASS, true>, shm + kRowTabMax + 4096);
-    if (e == hipSuccess) e = set_lds(fwd_local_kernel<D, MASS, false>, shm);
+    if (e == hipSuccess) e = set_lds(fwd_local_kernel<D, MASS, true>, kRowTabMax + 4096);
     if (e != hipSuccess) return e;
     attr = true;
   }
