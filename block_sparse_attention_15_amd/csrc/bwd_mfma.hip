@@ -126,6 +126,7 @@ struct BwdArgs {
   const int32_t* topk;
   const float* lse;
   const float* delta;
+  const float* lse2;  // lse * log2(e)
   const bf16_t* dout;
   const int32_t* tcount;
   const int32_t* tlist;
@@ -142,7 +143,6 @@ struct BwdArgs {
 // where the registers allow it without spilling).
 constexpr bool kHoistDqPers = true;
 template <bool DV> constexpr bool kHoistKvPers = true;
-template <bool DV> constexpr bool kHoistKvLocal = DV;
 
 // ===========================================================================
 // dQ, query-outer
@@ -498,25 +498,46 @@ __device__ __forceinline__ void k_init(const bf16_t* krow, const bf16_t* vrow, b
 }
 
 // One 32-query tile in LDS: Q tile tq, dO tile td, per-row lse*log2e and D.
-template <int D, bool DV, bool HOIST>
+// HOIST: read the transposed B operands ahead of the VALU work; EARLY: read
+// them first of all, then call mid(); XADDR: natural reads through per-read
+// XOR offsets from the array arr holding the tiles (see q_tile).
+template <int D, bool DV, bool HOIST, bool EARLY = false, bool XADDR = false, typename Mid = NoMid>
 __device__ __forceinline__ void k_tile(const char* tq, const char* td, const float* lse2, const float* dl, float c2,
-                                       KState<D, DV>& st) {
+                                       KState<D, DV>& st, Mid mid = Mid{}, const char* arr = nullptr,
+                                       int nrow = 32) {
+  static_assert(HOIST || !EARLY, "EARLY reads are hoisted reads");
   const int lane = threadIdx.x & 63, h = lane >> 5, l32 = lane & 31;
-  f32x16_t s = {}, dp = {};
-#pragma unroll
-  for (int ks = 0; ks < Sh<D>::KS; ++ks) {
-    s = mfma(rd_nat<D>(tq, l32, 2 * ks + h), st.kf[ks], s);
-    if (!DV) dp = mfma(rd_nat<D>(td, l32, 2 * ks + h), st.vf[DV ? 0 : ks], dp);
-  }
   const char* tb = DV ? td : tq;  // dV += P^T dO ; dK += dS^T Q
-  bf16x8_t bt[HOIST ? Sh<D>::DT : 1][2];  // transposed B operands, read before the VALU work
-  if (HOIST) {
+  bf16x8_t bt[HOIST ? Sh<D>::DT : 1][2];  // transposed B operands
+  auto read_bt = [&]() {
 #pragma unroll
     for (int dt = 0; dt < Sh<D>::DT; ++dt) {
       bt[HOIST ? dt : 0][0] = rd_tr<D>(tb, 0, dt);
       bt[HOIST ? dt : 0][1] = rd_tr<D>(tb, 1, dt);
     }
+  };
+  if (EARLY) {
+    read_bt();
+    __builtin_amdgcn_sched_barrier(0);  // keep mid() after the reads
   }
+  mid();
+  f32x16_t s = {}, dp = {};
+  if (XADDR) {
+    const int bq = nat_base<D>((int)(tq - arr), l32, h);
+    const int bd = DV ? 0 : nat_base<D>((int)(td - arr), l32, h);
+#pragma unroll
+    for (int ks = 0; ks < Sh<D>::KS; ++ks) {
+      s = mfma(rd_nat_at<D>(arr, bq, ks), st.kf[ks], s);
+      if (!DV) dp = mfma(rd_nat_at<D>(arr, bd, ks), st.vf[DV ? 0 : ks], dp);
+    }
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < Sh<D>::KS; ++ks) {
+      s = mfma(rd_nat<D>(tq, l32, 2 * ks + h), st.kf[ks], s);
+      if (!DV) dp = mfma(rd_nat<D>(td, l32, 2 * ks + h), st.vf[DV ? 0 : ks], dp);
+    }
+  }
+  if (HOIST && !EARLY) read_bt();
   f32x16_t x;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -536,6 +557,11 @@ __device__ __forceinline__ void k_tile(const char* tq, const char* td, const flo
       const float p = __builtin_amdgcn_exp2f(fmaf(s[j], c2, -Ls[jj]));
       x[j] = DV ? p : p * (dp[j] - Ds[jj]);
     }
+  }
+  if (nrow < 32) {  // query rows past nrow hold filler data
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (8 * (j >> 2) + 4 * h + (j & 3) >= nrow) x[j] = 0.f;
   }
   const bf16x8_t x0 = pack8(x, 0), x1 = pack8(x, 1);
 #pragma unroll
@@ -688,130 +714,111 @@ __global__ __launch_bounds__(kKvThreads, 1) void dkv_pers_kernel(BwdArgs a) {
 // same gathered query tiles, which are staged into LDS once for both passes.
 // A step is one 32-row half of one query block that selected this local
 // block (key-block -> query-block lists from bwd_tindex_kernel, copied to LDS
-// with the step list).
+// with the step list).  Q and dO rows are gathered straight into LDS
+// (global_load_lds_dwordx4) into two static buffers; the row tokens of the
+// next gather are loaded one step ahead, and each row's lse / D go through
+// registers.
 constexpr int kKvlThreads = 256;
+constexpr int kKvlWaves = kKvlThreads / 64;
 
-// Query-tile gather, software-pipelined two steps deep: row tokens of step
-// i+2 are loaded while step i computes, so the Q / dO loads of step i+1 issue
-// with ready addresses; rows past a block's end load token 0 and are zeroed
-// when staged into LDS.
-template <int D> struct GatherPipe {
-  static constexpr int NCH = 32 * Sh<D>::CPR;              // 16-byte chunks per tensor tile
-  static constexpr int N = (NCH + kKvlThreads - 1) / kKvlThreads;
-  int tok[N], tokl;            // raw row tokens of the next step to load
-  unsigned okm;                // bit u: chunk u is a valid row; bit N: row (lse / D) valid
-  int tok2[N], tokl2;          // ... of the step after
-  unsigned okm2;
-  uint4 q[N], d[N];            // Q / dO chunks of the next step
-  float l, dd;
-  unsigned okq;                // validity of q/d/l/dd
+template <int D> struct KvlGather {
+  static constexpr int RPK = 1024 / Sh<D>::ROWB;   // rows per KB unit
+  static constexpr int UPT = Sh<D>::TILEB / 1024;  // KB units per 32-row tile
+  static constexpr int UPW = UPT / kKvlWaves;      // units of each tensor per wave
+  static constexpr int BUF = 2 * Sh<D>::TILEB + 256;  // Q tile, dO tile, lse2[32], D[32]
+  int tok[UPW];  // row tokens of this lane's units in the next step (-1: no row)
+  int tokl;      // row token of row lane%32 (lse2 / D, gathered by wave 0)
 
   // step = (selecting-list index << 1) | half
-  __device__ __forceinline__ static void tokens(const BwdArgs& a, const int* sel, const int* slen, int step,
-                                                int* t, int& tl, unsigned& ok) {
+  __device__ __forceinline__ void tokens(const BwdArgs& a, const int* sel, const int* slen, int step) {
     const Geo& g = a.g;
-    const int tid = threadIdx.x;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int sidx = step >> 1, half = step & 1;
     const int len = slen[sidx];
     const int32_t* rows = a.tab.btok + sel[sidx] * g.C;
-    ok = 0;
 #pragma unroll
-    for (int u = 0; u < N; ++u) {
-      const int id = tid + kKvlThreads * u, r = 32 * half + id / Sh<D>::CPR;
-      t[u] = rows[min(r, g.C - 1)];
-      if (id < NCH && r < len) ok |= 1u << u;
+    for (int i = 0; i < UPW; ++i) {
+      const int r = 32 * half + RPK * (wave * UPW + i) + lane / Sh<D>::CPR;
+      tok[i] = r < len ? rows[r] : -1;
     }
-    const int rl = 32 * half + (tid & 31);
-    tl = rows[min(rl, g.C - 1)];
-    if (tid < 32 && rl < len) ok |= 1u << N;
+    const int rl = 32 * half + (threadIdx.x & 31);
+    tokl = rl < len ? rows[rl] : -1;
   }
-  __device__ __forceinline__ void load(const BwdArgs& a, size_t bh) {
+  // Issue the gather of the step whose tokens are held into buf: Q and dO
+  // rows, and (wave 0) the rows' lse2 and D, lanes 0-31 and 32-63.  Rows
+  // without a token load row 0 of the head: finite filler that the tile masks.
+  __device__ __forceinline__ void gather(const BwdArgs& a, size_t bh, char* buf) {
     const Geo& g = a.g;
-    const int tid = threadIdx.x;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int rr = lane / Sh<D>::CPR, pos = lane % Sh<D>::CPR;
     const bf16_t* qb = a.q + bh * g.ct * (size_t)D;
     const bf16_t* db = a.dout + bh * g.ct * (size_t)D;
 #pragma unroll
-    for (int u = 0; u < N; ++u) {
-      const int c = (tid + kKvlThreads * u) % Sh<D>::CPR;
-      const unsigned off = (unsigned)(((okm >> u) & 1 ? tok[u] : 0) * D + c * 8);
-      q[u] = ld16(qb + off);
-      d[u] = ld16(db + off);
+    for (int i = 0; i < UPW; ++i) {
+      const int u = wave * UPW + i;
+      const int r = RPK * u + rr;
+      const int off = max(tok[i], 0) * D + swz(r, pos, Sh<D>::CPR) * 8;
+      __builtin_amdgcn_global_load_lds(qb + off, (__attribute__((address_space(3))) void*)(buf + u * 1024), 16, 0,
+                                       0);
+      __builtin_amdgcn_global_load_lds(db + off,
+                                       (__attribute__((address_space(3))) void*)(buf + Sh<D>::TILEB + u * 1024),
+                                       16, 0, 0);
     }
-    const size_t ro = bh * g.ct + ((okm >> N) & 1 ? tokl : 0);
-    l = a.lse[ro];
-    dd = a.delta[ro];
-    okq = okm;
-  }
-  __device__ __forceinline__ void shift() {
-#pragma unroll
-    for (int u = 0; u < N; ++u) tok[u] = tok2[u];
-    tokl = tokl2;
-    okm = okm2;
-  }
-  // LDS: Q tile, dO tile, lse2[32], D[32]
-  __device__ __forceinline__ void store(char* buf) const {
-    const int tid = threadIdx.x;
-    const uint4 z = make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int u = 0; u < N; ++u) {
-      const int id = tid + kKvlThreads * u, r = id / Sh<D>::CPR, c = id % Sh<D>::CPR;
-      if (id >= NCH) break;
-      const bool ok = (okq >> u) & 1;
-      st_chunk(buf, Sh<D>::ROWB, Sh<D>::CPR, r, c, ok ? q[u] : z);
-      st_chunk(buf + Sh<D>::TILEB, Sh<D>::ROWB, Sh<D>::CPR, r, c, ok ? d[u] : z);
-    }
-    if (tid < 32) {
-      const bool ok = (okq >> N) & 1;
-      float* f = reinterpret_cast<float*>(buf + 2 * Sh<D>::TILEB);
-      f[tid] = ok ? l * kLog2e : INFINITY;
-      f[32 + tid] = ok ? dd : 0.f;
+    if (wave == 0) {
+      const size_t ro = bh * g.ct + max(tokl, 0);
+      __builtin_amdgcn_global_load_lds(lane < 32 ? a.lse2 + ro : a.delta + ro,
+                                       (__attribute__((address_space(3))) void*)(buf + 2 * Sh<D>::TILEB), 4, 0, 0);
     }
   }
 };
 
-template <int D> constexpr size_t kvl_lds(int nq) {
-  return 2 * (2 * (size_t)Sh<D>::TILEB + 256) + 4 * (size_t)nq * 4;
-}
+// LDS beyond the two static step buffers: the selecting list, lengths and steps.
+constexpr size_t kvl_lds(int nq) { return 4 * (size_t)nq * 4; }
 
 // The key-outer pass of one role (dV or dK) over the workgroup's step list;
-// every wave runs the same number of barriers whatever its role.
+// every wave runs the same number of barriers and gathers whatever its role.
 template <int D, bool DV>
 __device__ __forceinline__ void kvl_pass(const BwdArgs& a, size_t bh, int p, int kt, const int* sel,
-                                         const int* slen, const int* steps, int nsteps, char* smem) {
-  constexpr int BUF = 2 * Sh<D>::TILEB + 256;
+                                         const int* slen, const int* steps, int nsteps, char* kv0, char* kv1) {
   const Geo& g = a.g;
   const int l32 = threadIdx.x & 31;
   const BlockExt ke = block_ext(g, p % g.nq);
   const int koff = (p / g.nq) * g.ct;
-  const int nk = min(max(ke.len - 32 * kt, 0), 32);
+  const int nk = __builtin_amdgcn_readfirstlane(min(max(ke.len - 32 * kt, 0), 32));  // uniform per wave
   const int kr = 32 * kt + l32;
   const bool kok = kr < ke.len;
   const size_t krow = (bh * g.NL + koff + (kok ? block_token(g, ke, kr) : 0)) * (size_t)D;
   KState<D, DV> st;
   k_init<D, DV>(a.kl + krow, a.vl + krow, kok, st);
   const float c2 = g.scale * kLog2e;
-  GatherPipe<D> pf;
+  KvlGather<D> ga;
   if (nsteps > 0) {
-    GatherPipe<D>::tokens(a, sel, slen, steps[0], pf.tok, pf.tokl, pf.okm);
-    pf.load(a, bh);
-    pf.store(smem);
-    if (nsteps > 1) GatherPipe<D>::tokens(a, sel, slen, steps[1], pf.tok, pf.tokl, pf.okm);
-    if (nsteps > 2) GatherPipe<D>::tokens(a, sel, slen, steps[2], pf.tok2, pf.tokl2, pf.okm2);
+    ga.tokens(a, sel, slen, steps[0]);
+    ga.gather(a, bh, kv0);
+    if (nsteps > 1) ga.tokens(a, sel, slen, steps[1]);
   }
-  __syncthreads();
-  for (int i = 0; i < nsteps; ++i) {
-    char* buf = smem + (i & 1) * BUF;
-    if (i + 1 < nsteps) pf.load(a, bh);  // step i+1, tokens ready
-    if (i + 2 < nsteps) {
-      pf.shift();
-      if (i + 3 < nsteps) GatherPipe<D>::tokens(a, sel, slen, steps[i + 3], pf.tok2, pf.tokl2, pf.okm2);
-    }
+  __syncthreads();  // its fence waits for the gather
+  // unrolled by two so that each step's buffers are compile-time arrays
+  auto step = [&](int i, char* cur, char* nxt) {
+    auto mid = [&]() {
+      if (i + 1 < nsteps) {
+        ga.gather(a, bh, nxt);
+        if (i + 2 < nsteps) ga.tokens(a, sel, slen, steps[i + 2]);
+      }
+    };
     if (nk > 0) {
-      const float* f = reinterpret_cast<const float*>(buf + 2 * Sh<D>::TILEB);
-      k_tile<D, DV, kHoistKvLocal<DV>>(buf, buf + Sh<D>::TILEB, f, f + 32, c2, st);
+      const int sx = steps[i];
+      const int nrow = __builtin_amdgcn_readfirstlane(min(slen[sx >> 1] - 32 * (sx & 1), 32));
+      const float* f = reinterpret_cast<const float*>(cur + 2 * Sh<D>::TILEB);
+      k_tile<D, DV, true, true, true>(cur, cur + Sh<D>::TILEB, f, f + 32, c2, st, mid, cur, nrow);
+    } else {
+      mid();
     }
-    if (i + 1 < nsteps) pf.store(smem + ((i + 1) & 1) * BUF);
     __syncthreads();
+  };
+  for (int i = 0; i < nsteps; i += 2) {
+    step(i, kv0, kv1);
+    if (i + 1 < nsteps) step(i + 1, kv1, kv0);
   }
   if (nk <= 0) return;
   float* ob = (DV ? a.dvl : a.dkl) + (bh * g.NL + koff) * (size_t)D;
@@ -825,8 +832,11 @@ __device__ __forceinline__ void kvl_pass(const BwdArgs& a, size_t bh, int p, int
 
 template <int D>
 __global__ __launch_bounds__(kKvlThreads, 2) void dkv_local_kernel(BwdArgs a) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-  constexpr int BUF = 2 * Sh<D>::TILEB + 256;
+  extern __shared__ __attribute__((aligned(16))) char smem[];  // step lists
+  // the two step buffers are separate arrays so that the compiler can tell the
+  // gather into one from the reads of the other
+  __shared__ __attribute__((aligned(1024))) char kv0[KvlGather<D>::BUF];
+  __shared__ __attribute__((aligned(1024))) char kv1[KvlGather<D>::BUF];
   const Geo& g = a.g;
   const int total = g.B * g.H * g.nl;
   const int lin = xcd_remap(total);
@@ -839,7 +849,7 @@ __global__ __launch_bounds__(kKvlThreads, 2) void dkv_local_kernel(BwdArgs a) {
   // selecting query blocks (ascending), their lengths and the step list, in LDS
   const int ncount = a.tcount[bh * g.nl + p];
   const int32_t* lst = a.tlist + (bh * g.nl + p) * g.nq;
-  int* sel = reinterpret_cast<int*>(smem + 2 * BUF);
+  int* sel = reinterpret_cast<int*>(smem);
   int* slen = sel + g.nq;
   int* steps = slen + g.nq;
   for (int x = threadIdx.x; x < ncount; x += kKvlThreads) {
@@ -856,9 +866,9 @@ __global__ __launch_bounds__(kKvlThreads, 2) void dkv_local_kernel(BwdArgs a) {
   }
   __syncthreads();
   if (role == 0)
-    kvl_pass<D, true>(a, bh, p, kt, sel, slen, steps, nsteps, smem);
+    kvl_pass<D, true>(a, bh, p, kt, sel, slen, steps, nsteps, kv0, kv1);
   else
-    kvl_pass<D, false>(a, bh, p, kt, sel, slen, steps, nsteps, smem);
+    kvl_pass<D, false>(a, bh, p, kt, sel, slen, steps, nsteps, kv0, kv1);
 }
 
 template <typename K>
@@ -874,7 +884,7 @@ hipError_t launch_d(const BwdArgs& base, hipStream_t s) {
   const bool tab = tabb <= (size_t)kRowTabMax;
   const size_t shm_dql = tab ? tabb + kLocBlocks * g.K * 4 : 0;  // local: row tables (step buffers are static)
   const size_t shm_kv = 2 * (2 * Sh<D>::TILEB + 256);
-  const size_t shm_kvl = kvl_lds<D>(g.nq);
+  const size_t shm_kvl = kvl_lds(g.nq);
   static bool attr = false;
   if (!attr) {
     hipError_t e = set_lds(dq_pers_kernel<D>, shm_dq);
@@ -882,7 +892,7 @@ hipError_t launch_d(const BwdArgs& base, hipStream_t s) {
       e = set_lds(dq_local_kernel<D, true>, kRowTabMax + 4096);
     if (e == hipSuccess) e = set_lds(dkv_pers_kernel<D, true>, shm_kv);
     if (e == hipSuccess) e = set_lds(dkv_pers_kernel<D, false>, shm_kv);
-    if (e == hipSuccess) e = set_lds(dkv_local_kernel<D>, kvl_lds<D>(2048));
+    if (e == hipSuccess) e = set_lds(dkv_local_kernel<D>, kvl_lds(2048));
     if (e != hipSuccess) return e;
     attr = true;
   }
@@ -925,7 +935,7 @@ hipError_t launch_bwd_mfma(const Geo& g, const void* q, const void* k_p, const v
   hipError_t e = launch_geo_table(g, ws.geo, &tab, s);
   if (e != hipSuccess) return e;
   BwdArgs a{g, (const bf16_t*)q, (const bf16_t*)k_p, (const bf16_t*)v_p, plen, (const bf16_t*)k_l,
-            (const bf16_t*)v_l, topk, lse, ws.delta, (const bf16_t*)dout, ws.tcount, ws.tlist,
+            (const bf16_t*)v_l, topk, lse, ws.delta, ws.lse2, (const bf16_t*)dout, ws.tcount, ws.tlist,
             dq, dk_p, dv_p, dk_l, dv_l, tab, 0};
   return g.D == 128 ? launch_d<128>(a, s) : launch_d<64>(a, s);
 }

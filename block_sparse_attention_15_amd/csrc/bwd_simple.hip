@@ -16,7 +16,8 @@ namespace {
 // grid (ceil(ct/4), H, B), 256 threads: one wave per query token.
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(Geo g, const T* __restrict__ o, const T* __restrict__ dout,
-                                                        float* __restrict__ delta) {
+                                                        const float* __restrict__ lse, float* __restrict__ delta,
+                                                        float* __restrict__ lse2) {
   const int t = blockIdx.x * 4 + threadIdx.x / 64, lane = threadIdx.x & 63;
   const size_t bh = (size_t)blockIdx.z * g.H + blockIdx.y;
   if (t >= g.ct) return;
@@ -24,7 +25,10 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(Geo g, const T* __restri
   float a = 0.f;
   for (int d = lane; d < g.D; d += 64) a = fmaf(to_f<T>(o[row + d]), to_f<T>(dout[row + d]), a);
   for (int k = 32; k > 0; k >>= 1) a += __shfl_xor(a, k, 64);
-  if (lane == 0) delta[bh * g.ct + t] = a;
+  if (lane == 0) {
+    delta[bh * g.ct + t] = a;
+    lse2[bh * g.ct + t] = lse[bh * g.ct + t] * 1.4426950408889634f;
+  }
 }
 
 // grid (H, B): for each local block, the query blocks that selected it, ascending.
@@ -254,13 +258,13 @@ __global__ __launch_bounds__(256) void bwd_dkv_simple_kernel(Geo g, const T* __r
 
 }  // namespace
 
-hipError_t launch_bwd_prep(const Geo& g, const void* o, const void* dout, const int32_t* topk, WsBwd ws,
-                           hipStream_t s) {
+hipError_t launch_bwd_prep(const Geo& g, const void* o, const void* dout, const float* lse, const int32_t* topk,
+                           WsBwd ws, hipStream_t s) {
   dim3 g1((g.ct + 3) / 4, g.H, g.B);
   if (g.dtype == PBSA_BF16)
-    bwd_delta_kernel<bf16_t><<<g1, 256, 0, s>>>(g, (const bf16_t*)o, (const bf16_t*)dout, ws.delta);
+    bwd_delta_kernel<bf16_t><<<g1, 256, 0, s>>>(g, (const bf16_t*)o, (const bf16_t*)dout, lse, ws.delta, ws.lse2);
   else
-    bwd_delta_kernel<float><<<g1, 256, 0, s>>>(g, (const float*)o, (const float*)dout, ws.delta);
+    bwd_delta_kernel<float><<<g1, 256, 0, s>>>(g, (const float*)o, (const float*)dout, lse, ws.delta, ws.lse2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t shm = (size_t)g.nl * max(1, min(g.nq, kTindexLds / g.nl));

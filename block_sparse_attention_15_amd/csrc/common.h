@@ -124,6 +124,7 @@ hipError_t launch_token_mass(const Geo& g, const int32_t* plen, const int32_t* t
                              const float* blse_p, const float* blse_l, float* part, float* mass, hipStream_t s);
 struct WsBwd {
   float* delta;     // [B,H,Nq]      rowsum(dO * O)
+  float* lse2;      // [B,H,Nq]      lse * log2(e)
   int32_t* tcount;  // [B,H,nl]      query blocks that selected each local block
   int32_t* tlist;   // [B,H,nl,nq]   their ids, ascending
   void* geo;        // geometry tables (geo_table_bytes)
