@@ -15,14 +15,16 @@
 //             lane (lane-local P and dS), dQ^T += K^T dS^T reads K transposed
 //             from LDS (ds_read_b64_tr_b16).  Writes dq.
 //   dq_local  the same over each query block's selected local blocks (8 waves
-//             = 4 query blocks x 2 query tiles); adds into dq.
+//             = 4 query blocks x 2 query tiles), rows gathered straight into
+//             LDS; adds into dq.
 //   dkv_pers  key-outer: 8 waves x 32 keys (four slots) stream every query of
 //             the head through LDS in 32-row tiles; S = Q K^T and dP = dO V^T
 //             put one key per lane, dV += P^T dO and dK += dS^T Q read dO and
 //             Q transposed from LDS.
-//   dkv_local key-outer over a local block (2 waves x 32 keys), streaming only
-//             the query blocks that selected it (a key-block -> query-block
-//             index built from the top-k lists).
+//   dkv_local key-outer over a local block (4 waves: dV and dK for 2 x 32
+//             keys), streaming only the query blocks that selected it (a
+//             key-block -> query-block index built from the top-k lists),
+//             rows gathered straight into LDS.
 // LDS tiles hold 32 rows of 16-byte chunks XOR-swizzled so that both the
 // natural 16-byte reads (rows of one chunk column) and the transposed
 // ds_read_b64_tr_b16 reads (4 rows x 4 chunks per 16 lanes) avoid bank

@@ -27,9 +27,10 @@
 //  * K is read from LDS as the A operand with 16-byte reads; V is read
 //    transposed with ds_read_b64_tr_b16 (two per 8-key operand).  Both LDS
 //    tiles are XOR-swizzled at 16-byte granularity to spread banks.
-//  * LDS is double-buffered (2 x 64 KB); the next step's rows are prefetched
-//    into registers while the current step computes, so there is one barrier
-//    per step.
+//  * LDS is double-buffered, with one barrier per step.  The persistent
+//    kernel prefetches the next slot into registers while the current one
+//    computes; the local kernel gathers the next step's rows straight into
+//    LDS (global_load_lds_dwordx4), with no staging registers.
 //  * exp2 with softmax_scale*log2(e) folded into one FMA; the running max is
 //    only raised when a tile's max exceeds it by more than 2^8 (P values stay
 //    below 256, safe in bf16 and fp32), which makes O rescales rare.
