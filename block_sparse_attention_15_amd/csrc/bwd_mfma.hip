@@ -716,10 +716,10 @@ __global__ __launch_bounds__(kKvThreads, 1) void dkv_pers_kernel(BwdArgs a) {
 // same gathered query tiles, which are staged into LDS once for both passes.
 // A step is one 32-row half of one query block that selected this local
 // block (key-block -> query-block lists from bwd_tindex_kernel, copied to LDS
-// with the step list).  Q and dO rows are gathered straight into LDS
-// (global_load_lds_dwordx4) into two static buffers; the row tokens of the
-// next gather are loaded one step ahead, and each row's lse / D go through
-// registers.
+// with the step list).  Q and dO rows and their lse*log2(e) / D are
+// gathered straight into LDS (global_load_lds_dwordx4 / _dword) into two
+// static buffers; the row tokens of the next gather are loaded one step
+// ahead.
 constexpr int kKvlThreads = 256;
 constexpr int kKvlWaves = kKvlThreads / 64;
 
