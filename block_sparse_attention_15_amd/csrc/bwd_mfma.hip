@@ -29,6 +29,8 @@
 // natural 16-byte reads (rows of one chunk column) and the transposed
 // ds_read_b64_tr_b16 reads (4 rows x 4 chunks per 16 lanes) avoid bank
 // conflicts.
+#include <mutex>
+
 #include "common.h"
 
 namespace pbsa {
@@ -873,6 +875,37 @@ __global__ __launch_bounds__(kKvlThreads, 2) void dkv_local_kernel(BwdArgs a) {
     kvl_pass<D, false>(a, bh, p, kt, sel, slen, steps, nsteps, kv0, kv1);
 }
 
+// The dK/dV kernels run on a second stream of the device, forked from and
+// joined back into the caller's stream by events, so that they fill the CUs
+// the dQ kernels leave idle (the persistent dQ kernel has fewer workgroups
+// than CUs) and each chain's tail.  One side stream and event pair per
+// device, default priority; the enqueue is serialised per device because
+// the events are shared.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  std::mutex mu;
+};
+constexpr int kMaxDevices = 64;
+
+hipError_t side_stream(SideStream** out) {
+  static SideStream per_dev[kMaxDevices];
+  static std::mutex init_mu;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  SideStream& ss = per_dev[dev];
+  std::lock_guard<std::mutex> lock(init_mu);
+  if (!ss.s) {
+    if ((e = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&ss.join, hipEventDisableTiming)) != hipSuccess) return e;
+  }
+  *out = &ss;
+  return hipSuccess;
+}
+
 template <typename K>
 hipError_t set_lds(K kernel, size_t bytes) {
   return hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
@@ -898,11 +931,29 @@ hipError_t launch_d(const BwdArgs& base, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr = true;
   }
+  SideStream* ss = nullptr;
+  hipError_t e = side_stream(&ss);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(ss->mu);
+  const hipStream_t s2 = ss->s;
+  if ((e = hipEventRecord(ss->fork, s)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(s2, ss->fork, 0)) != hipSuccess) return e;
   BwdArgs a = base;
-  hipError_t e;
-  // dq: persistent part writes, local part adds
+  // side stream: dK, dV (local blocks, then the persistent slots)
+  int total = g.B * g.H * g.nl;
+  dkv_local_kernel<D><<<((total + 7) / 8) * 8, kKvlThreads, shm_kvl, s2>>>(a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (g.S > 0) {
+    a.ntiles = (g.S + kKvSlots - 1) / kKvSlots;
+    total = g.B * g.H * a.ntiles;
+    dkv_pers_kernel<D, true><<<((total + 7) / 8) * 8, kKvThreads, shm_kv, s2>>>(a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    dkv_pers_kernel<D, false><<<((total + 7) / 8) * 8, kKvThreads, shm_kv, s2>>>(a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  // caller's stream: dq (persistent part writes, local part adds)
   a.ntiles = (g.ct + kDqRows - 1) / kDqRows;
-  int total = g.B * g.H * a.ntiles;
+  total = g.B * g.H * a.ntiles;
   dq_pers_kernel<D><<<((total + 7) / 8) * 8, kDqThreads, shm_dq, s>>>(a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   a.ntiles = (g.nq + kLocBlocks - 1) / kLocBlocks;
@@ -912,17 +963,8 @@ hipError_t launch_d(const BwdArgs& base, hipStream_t s) {
   else
     dq_local_kernel<D, false><<<((total + 7) / 8) * 8, kDqlThreads, shm_dql, s>>>(a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (g.S > 0) {
-    a.ntiles = (g.S + kKvSlots - 1) / kKvSlots;
-    total = g.B * g.H * a.ntiles;
-    dkv_pers_kernel<D, true><<<((total + 7) / 8) * 8, kKvThreads, shm_kv, s>>>(a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    dkv_pers_kernel<D, false><<<((total + 7) / 8) * 8, kKvThreads, shm_kv, s>>>(a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
-  total = g.B * g.H * g.nl;
-  dkv_local_kernel<D><<<((total + 7) / 8) * 8, kKvlThreads, shm_kvl, s>>>(a);
-  return hipGetLastError();
+  if ((e = hipEventRecord(ss->join, s2)) != hipSuccess) return e;
+  return hipStreamWaitEvent(s, ss->join, 0);
 }
 
 }  // namespace
