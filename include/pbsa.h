@@ -23,8 +23,13 @@
  *    synchronizes.  Host pointers (the config, the plan) are read during the
  *    call only.
  *  - Streams: every kernel is enqueued on `stream` (a hipStream_t; NULL means
- *    the default stream).  No entry point reads device data back to the host,
- *    so each call is asynchronous and may be captured into a hipGraph.
+ *    the default stream), except that pbsa_bwd forks part of its kernels onto
+ *    a second stream of the device (created by the library on first use,
+ *    default priority) after an event recorded on `stream`, and makes
+ *    `stream` wait for them with an event before it returns, so work enqueued
+ *    on `stream` afterwards sees all of its results.  No entry point reads
+ *    device data back to the host, so each call is asynchronous and may be
+ *    captured into a hipGraph (the fork and join become graph dependencies).
  *  - Errors: arguments are checked on the host before any launch.  On failure
  *    nothing is launched, a non-zero pbsa_status is returned and
  *    pbsa_last_error() describes the problem.  A failed kernel launch returns
@@ -178,7 +183,9 @@ pbsa_status pbsa_fwd_mass(const pbsa_config* cfg, const void* q, const void* k_p
  * pbsa_fwd) and dout.  Writes float32 dq, dk_pers, dv_pers, dk_local,
  * dv_local, overwriting them entirely (rows that receive no gradient are set
  * to zero).  Deterministic: no floating-point atomics.  ws of at least
- * plan.ws_bwd bytes. */
+ * plan.ws_bwd bytes.  The dk / dv kernels run on the library's second stream
+ * of the device (see Streams above); calls on one device are serialised
+ * while they are enqueued. */
 pbsa_status pbsa_bwd(const pbsa_config* cfg, const void* q, const void* k_pers, const void* v_pers,
                      const int32_t* persist_len, const void* k_local, const void* v_local,
                      const int32_t* topk_idx, const void* o, const float* lse, const void* dout,
