@@ -108,10 +108,13 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+constexpr int kRadixSlots = 4;  // keys per lane for the radix select (local blocks <= 256)
+
 // grid (ceil(nq/QPW), H, B): pooled scores of QPW (<= 4) query blocks against
 // every local block and every valid persistent slot (each candidate's pooled
 // key is read once for the QPW query blocks), then per query block (one wave)
-// the top-k by rank and one pooled softmax row.  QPW is the largest of 4, 2,
+// the top-k (a wavefront radix select up to 256 local blocks, ranks by
+// counting beyond) and one pooled softmax row.  QPW is the largest of 4, 2,
 // 1 whose LDS (scores, sort keys and flags of every candidate) fits.
 template <int D, int kQPerWg>
 __global__ __launch_bounds__(kThreads) void score_topk_kernel(Geo g, const int32_t* __restrict__ ring_head,
@@ -182,12 +185,38 @@ __global__ __launch_bounds__(kThreads) void score_topk_kernel(Geo g, const int32
   __syncthreads();
   if (!has) return;
   int32_t* out = topk + (bh * g.nq + i) * g.K;
-  // every lane ranks its own candidates against all keys (LDS broadcast reads)
-  for (int p = lane; p < g.nl; p += 64) {
-    const unsigned long long kp = key[p];
-    int rank = 0;
-    for (int o = 0; o < g.nl; ++o) rank += key[o] > kp;
-    sel[g.nl * 2 * kQPerWg + w * g.nl + p] = rank < g.K;
+  if (g.nl <= 64 * kRadixSlots) {
+    // wavefront radix select: the K-th largest key T, one bit at a time from
+    // the top (keep the bit when at least K keys are >= the candidate), with
+    // the keys in registers and the counts by ballot; the keys are distinct,
+    // so exactly K are >= T
+    unsigned long long kr[kRadixSlots];
+#pragma unroll
+    for (int u = 0; u < kRadixSlots; ++u) {
+      const int p = lane + 64 * u;
+      kr[u] = p < g.nl ? key[p] : 0ull;  // 0 is below every key
+    }
+    unsigned long long thr = 0ull;
+    for (int b = 63; b >= 0; --b) {
+      const unsigned long long cand = thr | (1ull << b);
+      int cnt = 0;
+#pragma unroll
+      for (int u = 0; u < kRadixSlots; ++u) cnt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(kr[u] >= cand));
+      if (cnt >= g.K) thr = cand;
+    }
+#pragma unroll
+    for (int u = 0; u < kRadixSlots; ++u) {
+      const int p = lane + 64 * u;
+      if (p < g.nl) sel[g.nl * 2 * kQPerWg + w * g.nl + p] = kr[u] >= thr;
+    }
+  } else {
+    // every lane ranks its own candidates against all keys (LDS broadcast reads)
+    for (int p = lane; p < g.nl; p += 64) {
+      const unsigned long long kp = key[p];
+      int rank = 0;
+      for (int o = 0; o < g.nl; ++o) rank += key[o] > kp;
+      sel[g.nl * 2 * kQPerWg + w * g.nl + p] = rank < g.K;
+    }
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
