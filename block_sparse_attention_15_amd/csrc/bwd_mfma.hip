@@ -134,6 +134,7 @@ struct BwdArgs {
   const bf16_t* dout;
   const int32_t* tcount;
   const int32_t* tlist;
+  const int32_t* korder;
   float* dq;
   float* dkp;
   float* dvp;
@@ -721,7 +722,10 @@ __global__ __launch_bounds__(kKvThreads, 1) void dkv_pers_kernel(BwdArgs a) {
 // with the step list).  Q and dO rows and their lse*log2(e) / D are
 // gathered straight into LDS (global_load_lds_dwordx4 / _dword) into two
 // static buffers; the row tokens of the next gather are loaded one step
-// ahead.
+// ahead.  Step counts per local block are heavy-tailed (a few blocks are
+// selected by most query blocks), so workgroups take their blocks in the
+// order of korder: within each XCD's range, most selecting query blocks
+// first, which keeps the longest workgroups off the end of the launch.
 constexpr int kKvlThreads = 256;
 constexpr int kKvlWaves = kKvlThreads / 64;
 
@@ -843,8 +847,9 @@ __global__ __launch_bounds__(kKvlThreads, 2) void dkv_local_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char kv1[KvlGather<D>::BUF];
   const Geo& g = a.g;
   const int total = g.B * g.H * g.nl;
-  const int lin = xcd_remap(total);
-  if (lin >= total) return;
+  const int slot = xcd_remap(total);
+  if (slot >= total) return;
+  const int lin = a.korder[slot];
   const int p = lin % g.nl;
   const size_t bh = lin / g.nl;
   const int wave = threadIdx.x >> 6;
@@ -980,7 +985,7 @@ hipError_t launch_bwd_mfma(const Geo& g, const void* q, const void* k_p, const v
   if (e != hipSuccess) return e;
   BwdArgs a{g, (const bf16_t*)q, (const bf16_t*)k_p, (const bf16_t*)v_p, plen, (const bf16_t*)k_l,
             (const bf16_t*)v_l, topk, lse, ws.delta, ws.lse2, (const bf16_t*)dout, ws.tcount, ws.tlist,
-            dq, dk_p, dv_p, dk_l, dv_l, tab, 0};
+            ws.korder, dq, dk_p, dv_p, dk_l, dv_l, tab, 0};
   return g.D == 128 ? launch_d<128>(a, s) : launch_d<64>(a, s);
 }
 

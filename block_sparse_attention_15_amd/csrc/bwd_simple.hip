@@ -76,6 +76,44 @@ __global__ __launch_bounds__(256) void bwd_tindex_kernel(Geo g, const int32_t* _
   }
 }
 
+// grid 8: the launch order of the key-outer local workgroups.  Workgroup
+// b of that kernel runs on XCD b%8 and takes index (b%8)*per + b/8 of the
+// (B,H,local block) list (per = ceil(total/8)), so each XCD works through one
+// contiguous range of it; here each range is ordered by descending number of
+// selecting query blocks (a counting sort over that number, ties in any
+// order), so that the longest workgroups start first and the short ones fill
+// in behind them.  korder[lo + i] = the list index the i-th workgroup of the
+// range takes.
+__global__ __launch_bounds__(256) void bwd_korder_kernel(Geo g, const int32_t* __restrict__ tcount,
+                                                         int32_t* __restrict__ korder) {
+  extern __shared__ int hist[];  // [nq + 1] buckets (bucket nq - count), then [256] partial sums
+  int* part = hist + g.nq + 1;
+  const int total = g.B * g.H * g.nl, per = (total + 7) / 8;
+  const int lo = blockIdx.x * per, hi = min(total, lo + per);
+  const int nb = g.nq + 1, cb = (nb + 255) / 256, t = threadIdx.x;
+  for (int k = t; k < nb; k += 256) hist[k] = 0;
+  __syncthreads();
+  for (int e = lo + t; e < hi; e += 256) atomicAdd(&hist[g.nq - min(max(tcount[e], 0), g.nq)], 1);
+  __syncthreads();
+  // exclusive scan over the buckets: thread t owns buckets [t*cb, t*cb + cb)
+  int sum = 0;
+  for (int k = t * cb; k < min(nb, t * cb + cb); ++k) sum += hist[k];
+  part[t] = sum;
+  __syncthreads();
+  int base = 0;
+  for (int j = 0; j < t; ++j) base += part[j];
+  for (int k = t * cb; k < min(nb, t * cb + cb); ++k) {
+    const int v = hist[k];
+    hist[k] = base;
+    base += v;
+  }
+  __syncthreads();
+  for (int e = lo + t; e < hi; e += 256) {
+    const int pos = atomicAdd(&hist[g.nq - min(max(tcount[e], 0), g.nq)], 1);
+    korder[lo + pos] = e;
+  }
+}
+
 // dQ, query-outer.  grid (nq, H, B), 64 lanes = query tokens of one block.
 template <typename T, int D>
 __global__ __launch_bounds__(64) void bwd_dq_simple_kernel(Geo g, const T* __restrict__ q, const T* __restrict__ kp,
@@ -269,6 +307,8 @@ hipError_t launch_bwd_prep(const Geo& g, const void* o, const void* dout, const 
   if (e != hipSuccess) return e;
   const size_t shm = (size_t)g.nl * max(1, min(g.nq, kTindexLds / g.nl));
   bwd_tindex_kernel<<<dim3(g.H, g.B), 256, shm, s>>>(g, topk, ws.tcount, ws.tlist);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  bwd_korder_kernel<<<8, 256, (size_t)(g.nq + 1 + 256) * 4, s>>>(g, ws.tcount, ws.korder);
   return hipGetLastError();
 }
 

@@ -127,6 +127,7 @@ struct WsBwd {
   float* lse2;      // [B,H,Nq]      lse * log2(e)
   int32_t* tcount;  // [B,H,nl]      query blocks that selected each local block
   int32_t* tlist;   // [B,H,nl,nq]   their ids, ascending
+  int32_t* korder;  // [B,H,nl]      local blocks in key-outer launch order (see launch_bwd_prep)
   void* geo;        // geometry tables (geo_table_bytes)
 };
 hipError_t launch_bwd(const Geo& g, const void* q, const void* k_p, const void* v_p, const int32_t* plen,
