@@ -103,6 +103,102 @@ __device__ __forceinline__ bf16x8_t rd_tr(const char* t, int ks2, int dt) {
                                               part[1][1], part[1][2], part[1][3]});
 }
 
+// All transposed operands of a 32-row tile, out[dt][ks2] = rd_tr(t, ks2, dt),
+// read in one asm block that waits for its own reads.  The compiler cannot
+// tell which LDS array a ds_read_tr builtin reads, so it waits for every
+// LDS-bound global load in flight before one; reads it does not see let
+// loads into the other step buffers stay in flight.  Rows 16*ks2 + r share
+// the swizzle of row r, so ks2 = 1 is the offset 16 rows further.
+#define PBSA_TR(o, i, off) "ds_read_b64_tr_b16 %" #o ", %" #i " offset:" #off "\n\t"
+template <int D>
+__device__ __forceinline__ void rd_tr_all(const char* t, bf16x8_t (&out)[Sh<D>::DT][2]) {
+  static_assert(D == 64 || D == 128, "head dimension");
+  const int lane = threadIdx.x & 63, G = lane >> 4, s16 = lane & 15;
+  unsigned ad[Sh<D>::DT][2];
+#pragma unroll
+  for (int dt = 0; dt < Sh<D>::DT; ++dt)
+#pragma unroll
+    for (int h8 = 0; h8 < 2; ++h8) {
+      const int r = 8 * h8 + 4 * (G >> 1) + (s16 >> 2);
+      const int col = 32 * dt + 16 * (G & 1) + 4 * (s16 & 3);
+      const char* p = t + r * Sh<D>::ROWB + swz(r, col >> 3, Sh<D>::CPR) * 16 + (col & 7) * 2;
+      ad[dt][h8] = (unsigned)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
+    }
+  s16x4_t v[Sh<D>::DT][2][2];  // [dt][ks2][h8]
+  if constexpr (D == 128) {
+    asm volatile(PBSA_TR(0, 16, 0) PBSA_TR(1, 17, 0) PBSA_TR(2, 16, 4096) PBSA_TR(3, 17, 4096)
+                 PBSA_TR(4, 18, 0) PBSA_TR(5, 19, 0) PBSA_TR(6, 18, 4096) PBSA_TR(7, 19, 4096)
+                 PBSA_TR(8, 20, 0) PBSA_TR(9, 21, 0) PBSA_TR(10, 20, 4096) PBSA_TR(11, 21, 4096)
+                 PBSA_TR(12, 22, 0) PBSA_TR(13, 23, 0) PBSA_TR(14, 22, 4096) PBSA_TR(15, 23, 4096)
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(v[0][0][0]), "=&v"(v[0][0][1]), "=&v"(v[0][1][0]), "=&v"(v[0][1][1]),
+                   "=&v"(v[1][0][0]), "=&v"(v[1][0][1]), "=&v"(v[1][1][0]), "=&v"(v[1][1][1]),
+                   "=&v"(v[2][0][0]), "=&v"(v[2][0][1]), "=&v"(v[2][1][0]), "=&v"(v[2][1][1]),
+                   "=&v"(v[3][0][0]), "=&v"(v[3][0][1]), "=&v"(v[3][1][0]), "=&v"(v[3][1][1])
+                 : "v"(ad[0][0]), "v"(ad[0][1]), "v"(ad[1][0]), "v"(ad[1][1]), "v"(ad[2][0]), "v"(ad[2][1]),
+                   "v"(ad[3][0]), "v"(ad[3][1]));
+  } else {
+    asm volatile(PBSA_TR(0, 8, 0) PBSA_TR(1, 9, 0) PBSA_TR(2, 8, 2048) PBSA_TR(3, 9, 2048)
+                 PBSA_TR(4, 10, 0) PBSA_TR(5, 11, 0) PBSA_TR(6, 10, 2048) PBSA_TR(7, 11, 2048)
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(v[0][0][0]), "=&v"(v[0][0][1]), "=&v"(v[0][1][0]), "=&v"(v[0][1][1]),
+                   "=&v"(v[1][0][0]), "=&v"(v[1][0][1]), "=&v"(v[1][1][0]), "=&v"(v[1][1][1])
+                 : "v"(ad[0][0]), "v"(ad[0][1]), "v"(ad[1][0]), "v"(ad[1][1]));
+  }
+#pragma unroll
+  for (int dt = 0; dt < Sh<D>::DT; ++dt)
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      const s16x4_t a = v[dt][k2][0], b = v[dt][k2][1];
+      out[dt][k2] = __builtin_bit_cast(bf16x8_t, s16x8_t{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]});
+    }
+}
+
+// The two transposed operands of column tile dt, out[ks2] = rd_tr(t, ks2, dt),
+// in one asm block that waits for its own reads (fewer live registers than
+// rd_tr_all, one LDS round trip per column tile).
+template <int D>
+__device__ __forceinline__ void rd_tr_dt(const char* t, int dt, bf16x8_t (&out)[2]) {
+  const int lane = threadIdx.x & 63, G = lane >> 4, s16 = lane & 15;
+  unsigned ad[2];
+#pragma unroll
+  for (int h8 = 0; h8 < 2; ++h8) {
+    const int r = 8 * h8 + 4 * (G >> 1) + (s16 >> 2);
+    const int col = 32 * dt + 16 * (G & 1) + 4 * (s16 & 3);
+    const char* p = t + r * Sh<D>::ROWB + swz(r, col >> 3, Sh<D>::CPR) * 16 + (col & 7) * 2;
+    ad[h8] = (unsigned)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
+  }
+  s16x4_t v[2][2];  // [ks2][h8]
+  if constexpr (D == 128)
+    asm volatile(PBSA_TR(0, 4, 0) PBSA_TR(1, 5, 0) PBSA_TR(2, 4, 4096) PBSA_TR(3, 5, 4096) "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(v[0][0]), "=&v"(v[0][1]), "=&v"(v[1][0]), "=&v"(v[1][1])
+                 : "v"(ad[0]), "v"(ad[1]));
+  else
+    asm volatile(PBSA_TR(0, 4, 0) PBSA_TR(1, 5, 0) PBSA_TR(2, 4, 2048) PBSA_TR(3, 5, 2048) "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(v[0][0]), "=&v"(v[0][1]), "=&v"(v[1][0]), "=&v"(v[1][1])
+                 : "v"(ad[0]), "v"(ad[1]));
+#pragma unroll
+  for (int k2 = 0; k2 < 2; ++k2) {
+    const s16x4_t x = v[k2][0], y = v[k2][1];
+    out[k2] = __builtin_bit_cast(bf16x8_t, s16x8_t{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]});
+  }
+}
+#undef PBSA_TR
+
+// Wait until at most N of this wave's global loads are in flight, then the
+// workgroup barrier.  Unlike __syncthreads this leaves the newest LDS-bound
+// loads running.  The wait is the s_waitcnt builtin, which the compiler's own
+// wait placement takes into account (it then knows every older load has
+// landed); the empty asm statements keep memory accesses from moving across.
+template <int N>
+__device__ __forceinline__ void vm_barrier() {
+  static_assert(N >= 0 && N < 16, "vmcnt");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xF70 | N);  // vmcnt(N), expcnt and lgkmcnt not waited for
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ void st_chunk(char* tile, int rowb, int cpr, int r, int c, uint4 v) {
   *reinterpret_cast<uint4*>(tile + r * rowb + swz(r, c, cpr) * 16) = v;
 }
@@ -147,7 +243,6 @@ struct BwdArgs {
 // Which tiles read their transposed operands ahead of the VALU work (only
 // where the registers allow it without spilling).
 constexpr bool kHoistDqPers = true;
-template <bool DV> constexpr bool kHoistKvPers = true;
 
 // ===========================================================================
 // dQ, query-outer
@@ -506,7 +601,8 @@ __device__ __forceinline__ void k_init(const bf16_t* krow, const bf16_t* vrow, b
 // HOIST: read the transposed B operands ahead of the VALU work; EARLY: read
 // them first of all, then call mid(); XADDR: natural reads through per-read
 // XOR offsets from the array arr holding the tiles (see q_tile).
-template <int D, bool DV, bool HOIST, bool EARLY = false, bool XADDR = false, typename Mid = NoMid>
+template <int D, bool DV, bool HOIST, bool EARLY = false, bool XADDR = false, bool ASMTR = false,
+          typename Mid = NoMid>
 __device__ __forceinline__ void k_tile(const char* tq, const char* td, const float* lse2, const float* dl, float c2,
                                        KState<D, DV>& st, Mid mid = Mid{}, const char* arr = nullptr,
                                        int nrow = 32) {
@@ -515,6 +611,10 @@ __device__ __forceinline__ void k_tile(const char* tq, const char* td, const flo
   const char* tb = DV ? td : tq;  // dV += P^T dO ; dK += dS^T Q
   bf16x8_t bt[HOIST ? Sh<D>::DT : 1][2];  // transposed B operands
   auto read_bt = [&]() {
+    if constexpr (ASMTR && HOIST) {
+      rd_tr_all<D>(tb, bt);
+      return;
+    }
 #pragma unroll
     for (int dt = 0; dt < Sh<D>::DT; ++dt) {
       bt[HOIST ? dt : 0][0] = rd_tr<D>(tb, 0, dt);
@@ -571,8 +671,10 @@ __device__ __forceinline__ void k_tile(const char* tq, const char* td, const flo
   const bf16x8_t x0 = pack8(x, 0), x1 = pack8(x, 1);
 #pragma unroll
   for (int dt = 0; dt < Sh<D>::DT; ++dt) {
-    st.acc[dt] = mfma(x0, HOIST ? bt[HOIST ? dt : 0][0] : rd_tr<D>(tb, 0, dt), st.acc[dt]);
-    st.acc[dt] = mfma(x1, HOIST ? bt[HOIST ? dt : 0][1] : rd_tr<D>(tb, 1, dt), st.acc[dt]);
+    if constexpr (ASMTR && !HOIST) rd_tr_dt<D>(tb, dt, bt[0]);
+    const bool direct = HOIST || ASMTR;
+    st.acc[dt] = mfma(x0, direct ? bt[HOIST ? dt : 0][0] : rd_tr<D>(tb, 0, dt), st.acc[dt]);
+    st.acc[dt] = mfma(x1, direct ? bt[HOIST ? dt : 0][1] : rd_tr<D>(tb, 1, dt), st.acc[dt]);
   }
 }
 
@@ -595,68 +697,46 @@ constexpr int kKvWaves = 8;       // dkv_pers: 8 waves = 4 slots x 2 key tiles
 constexpr int kKvThreads = 64 * kKvWaves;
 constexpr int kKvSlots = kKvWaves / 2;
 
-template <int D> struct QPf {
-  static constexpr int N = 32 * Sh<D>::CPR / 64;  // chunks per lane per tensor when one wave loads
-};
-
-// Stage 32 query rows (Q, dO, lse*log2e, D) into LDS with `nthr` threads.
-// row(i) returns the token of tile row i, or -1 for an empty row.
-template <int D, int NTHR, typename RowFn>
-struct QTileLoader {
-  static constexpr int NCH = 32 * Sh<D>::CPR;         // 16-byte chunks per tensor tile
-  static constexpr int N = (NCH + NTHR - 1) / NTHR;   // per thread
-  uint4 q[N], d[N];
-  float l, dd;
-  unsigned ok;  // bit u: chunk u is a valid row; bit N: row tid (lse / D) is valid
-  // Loads are unconditional (invalid rows read row 0 of the head) with one
-  // 32-bit offset per chunk shared by Q and dO against per-head base
-  // pointers; invalid rows are zeroed when staged.
-  __device__ __forceinline__ void load(const BwdArgs& a, size_t bh, RowFn row) {
+// LDS-bound loads of one contiguous 32-row query tile of a head (Q and dO
+// rows XOR-swizzled as the tiles expect, then lse*log2(e) in lanes 0-31 and
+// D in lanes 32-63).  Every wave issues the same NLD loads (the lse2 / D row
+// by all waves, to the same place), and rows past the head's last query
+// repeat it (the tile masks them), so a wait for "all but the last NLD"
+// means exactly "all but this tile".
+template <int D> struct PersDma {
+  static constexpr int RPK = 1024 / Sh<D>::ROWB;   // rows per 1 KB unit
+  static constexpr int UPT = Sh<D>::TILEB / 1024;  // units per tensor tile
+  static constexpr int NU = 2 * UPT / kKvWaves;    // Q / dO units per wave
+  static constexpr int NLD = NU + 1;
+  static constexpr int BUF = 2 * Sh<D>::TILEB + 256;
+  static_assert(NU * kKvWaves == 2 * UPT, "whole units per wave");
+  static __device__ __forceinline__ void issue(const BwdArgs& a, size_t bh, int row0, char* buf) {
     const Geo& g = a.g;
-    const int tid = threadIdx.x;
-    const bf16_t* qb = a.q + bh * g.ct * (size_t)D;
-    const bf16_t* db = a.dout + bh * g.ct * (size_t)D;
-    ok = 0;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int rr = lane / Sh<D>::CPR, pos = lane % Sh<D>::CPR;
+    const size_t hb = bh * g.ct;
 #pragma unroll
-    for (int u = 0; u < N; ++u) {
-      const int id = tid + NTHR * u, r = id / Sh<D>::CPR, c = id % Sh<D>::CPR;
-      const int tok = id < NCH ? row(r) : -1;
-      if (tok >= 0) ok |= 1u << u;
-      const unsigned off = (unsigned)(max(tok, 0) * D + c * 8);
-      q[u] = ld16(qb + off);
-      d[u] = ld16(db + off);
+    for (int i = 0; i < NU; ++i) {
+      const int u = wave * NU + i, t = u / UPT, uu = u % UPT;  // t: 0 Q, 1 dO
+      const int r = RPK * uu + rr;
+      const bf16_t* src = (t ? a.dout : a.q) + (hb + min(row0 + r, g.ct - 1)) * D + swz(r, pos, Sh<D>::CPR) * 8;
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(buf + t * Sh<D>::TILEB + uu * 1024),
+                                       16, 0, 0);
     }
-    const int tl = tid < 32 ? row(tid) : -1;
-    if (tl >= 0) ok |= 1u << N;
-    const size_t ro = bh * g.ct + max(tl, 0);
-    l = a.lse[ro];
-    dd = a.delta[ro];
-  }
-  // LDS: Q tile, dO tile, lse2[32], D[32]
-  __device__ __forceinline__ void store(char* buf) const {
-    const int tid = threadIdx.x;
-    const uint4 z = make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int u = 0; u < N; ++u) {
-      const int id = tid + NTHR * u, r = id / Sh<D>::CPR, c = id % Sh<D>::CPR;
-      if (id >= NCH) break;
-      const bool v = (ok >> u) & 1;
-      st_chunk(buf, Sh<D>::ROWB, Sh<D>::CPR, r, c, v ? q[u] : z);
-      st_chunk(buf + Sh<D>::TILEB, Sh<D>::ROWB, Sh<D>::CPR, r, c, v ? d[u] : z);
-    }
-    if (tid < 32) {
-      const bool v = (ok >> N) & 1;
-      float* f = reinterpret_cast<float*>(buf + 2 * Sh<D>::TILEB);
-      f[tid] = v ? l * kLog2e : INFINITY;
-      f[32 + tid] = v ? dd : 0.f;
-    }
+    const size_t ro = hb + min(row0 + (lane & 31), g.ct - 1);
+    __builtin_amdgcn_global_load_lds(lane < 32 ? a.lse2 + ro : a.delta + ro,
+                                     (__attribute__((address_space(3))) void*)(buf + 2 * Sh<D>::TILEB), 4, 0, 0);
   }
 };
 
 template <int D, bool DV>
 __global__ __launch_bounds__(kKvThreads, 1) void dkv_pers_kernel(BwdArgs a) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-  constexpr int BUF = 2 * Sh<D>::TILEB + 256;
+  using Dm = PersDma<D>;
+  // three step buffers, separate arrays so that the compiler can tell the
+  // loads into one from the reads of another
+  __shared__ __attribute__((aligned(1024))) char kb0[Dm::BUF];
+  __shared__ __attribute__((aligned(1024))) char kb1[Dm::BUF];
+  __shared__ __attribute__((aligned(1024))) char kb2[Dm::BUF];
   const Geo& g = a.g;
   const int total = g.B * g.H * a.ntiles;
   const int lin = xcd_remap(total);
@@ -667,43 +747,40 @@ __global__ __launch_bounds__(kKvThreads, 1) void dkv_pers_kernel(BwdArgs a) {
   const int slot = kKvSlots * sp + (wave >> 1), kh = wave & 1;
   const bool has_slot = slot < g.S;
   const int n = has_slot ? min(a.plen[bh * g.S + slot], g.C) : 0;
-  const int nk = min(max(n - 32 * kh, 0), 32);  // valid keys of this wave's tile
+  const int nk = __builtin_amdgcn_readfirstlane(min(max(n - 32 * kh, 0), 32));  // valid keys of this wave's tile
   const size_t sbase = (bh * g.S + (has_slot ? slot : 0)) * (size_t)g.C * D;
   const int kr = 32 * kh + l32;
   KState<D, DV> st;
   k_init<D, DV>(a.kp + sbase + (size_t)kr * D, a.vp + sbase + (size_t)kr * D, kr < n, st);
   const float c2 = g.scale * kLog2e;
 
-  const int nsteps = (g.ct + 31) / 32;
-  struct Contig {
-    int base, ct;
-    __device__ int operator()(int i) const { return base + i < ct ? base + i : -1; }
-  };
-  // Query tiles are prefetched two steps ahead into two register sets that
-  // alternate by step (tile i+1 is stored into LDS at the end of step i while
-  // tile i+2 is in flight); LDS holds two tiles.
-  using Loader = QTileLoader<D, kKvThreads, Contig>;
-  Loader pa, pb;
-  pa.load(a, bh, Contig{0, g.ct});
-  pa.store(smem);
-  if (nsteps > 1) pa.load(a, bh, Contig{32, g.ct});
-  if (nsteps > 2) pb.load(a, bh, Contig{64, g.ct});
-  __syncthreads();
-  // cur holds tile i+1 and nx tile i+2; unrolled by two so that the LDS
-  // buffers and the register sets are fixed at compile time
-  auto step = [&](int i, char* buf, char* nxt, Loader& cur) {
-    if (nk > 0) {
-      const float* f = reinterpret_cast<const float*>(buf + 2 * Sh<D>::TILEB);
-      k_tile<D, DV, kHoistKvPers<DV>>(buf, buf + Sh<D>::TILEB, f, f + 32, c2, st);
+  // Every query tile of the head streams through LDS, loaded two steps
+  // ahead: step i computes on buffer i%3 while the tiles of steps i+1 and
+  // i+2 land.  The barrier that ends a step waits for all but the loads it
+  // issued; the transposed operands are read by asm that the compiler's own
+  // waits do not cover, so they do not drain the loads in flight either.
+  // Every step issues its loads (steps past the end repeat the last tile),
+  // so the counts hold on every path.
+  const int nsteps = (g.ct + 31) / 32, last = nsteps - 1;
+  Dm::issue(a, bh, 0, kb0);
+  Dm::issue(a, bh, 32 * min(1, last), kb1);
+  vm_barrier<Dm::NLD>();
+  auto step = [&](int i, char* cur, char* nx2) {
+    Dm::issue(a, bh, 32 * min(i + 2, last), nx2);
+    if (nk > 0 && i <= last) {
+      const float* f = reinterpret_cast<const float*>(cur + 2 * Sh<D>::TILEB);
+      // the dK pass holds V too: its transposed operands are read per column tile
+      k_tile<D, DV, DV, false, false, true>(cur, cur + Sh<D>::TILEB, f, f + 32, c2, st, NoMid{}, nullptr,
+                                            min(g.ct - 32 * i, 32));
     }
-    if (i + 1 < nsteps) cur.store(nxt);
-    if (i + 3 < nsteps) cur.load(a, bh, Contig{32 * (i + 3), g.ct});
-    __syncthreads();
+    vm_barrier<Dm::NLD>();
   };
-  for (int i = 0; i < nsteps; i += 2) {
-    step(i, smem, smem + BUF, pa);
-    if (i + 1 < nsteps) step(i + 1, smem + BUF, smem, pb);
+  for (int i = 0; i < nsteps; i += 3) {
+    step(i, kb0, kb2);
+    step(i + 1, kb1, kb0);
+    step(i + 2, kb2, kb1);
   }
+  __builtin_amdgcn_s_waitcnt(0xF70);  // the last loads land before the workgroup can end
   if (!has_slot || 32 * kh >= g.C) return;
   float* ob = (DV ? a.dvp : a.dkp) + sbase;
   k_write<D, DV>(st, nk, DV ? 1.0f : g.scale, [&](int r, float*& dst) {
@@ -923,15 +1000,12 @@ hipError_t launch_d(const BwdArgs& base, hipStream_t s) {
   const size_t tabb = (size_t)kLocBlocks * g.K * 64 * 4;
   const bool tab = tabb <= (size_t)kRowTabMax;
   const size_t shm_dql = tab ? tabb + kLocBlocks * g.K * 4 : 0;  // local: row tables (step buffers are static)
-  const size_t shm_kv = 2 * (2 * Sh<D>::TILEB + 256);
   const size_t shm_kvl = kvl_lds(g.nq);
   static bool attr = false;
   if (!attr) {
     hipError_t e = set_lds(dq_pers_kernel<D>, shm_dq);
     if (e == hipSuccess)
       e = set_lds(dq_local_kernel<D, true>, kRowTabMax + 4096);
-    if (e == hipSuccess) e = set_lds(dkv_pers_kernel<D, true>, shm_kv);
-    if (e == hipSuccess) e = set_lds(dkv_pers_kernel<D, false>, shm_kv);
     if (e == hipSuccess) e = set_lds(dkv_local_kernel<D>, kvl_lds(2048));
     if (e != hipSuccess) return e;
     attr = true;
@@ -951,9 +1025,9 @@ hipError_t launch_d(const BwdArgs& base, hipStream_t s) {
   if (g.S > 0) {
     a.ntiles = (g.S + kKvSlots - 1) / kKvSlots;
     total = g.B * g.H * a.ntiles;
-    dkv_pers_kernel<D, true><<<((total + 7) / 8) * 8, kKvThreads, shm_kv, s2>>>(a);
+    dkv_pers_kernel<D, true><<<((total + 7) / 8) * 8, kKvThreads, 0, s2>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    dkv_pers_kernel<D, false><<<((total + 7) / 8) * 8, kKvThreads, shm_kv, s2>>>(a);
+    dkv_pers_kernel<D, false><<<((total + 7) / 8) * 8, kKvThreads, 0, s2>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   // caller's stream: dq (persistent part writes, local part adds)
