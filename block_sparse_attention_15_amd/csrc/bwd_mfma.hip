@@ -185,20 +185,6 @@ __device__ __forceinline__ void rd_tr_dt(const char* t, int dt, bf16x8_t (&out)[
 }
 #undef PBSA_TR
 
-// Wait until at most N of this wave's global loads are in flight, then the
-// workgroup barrier.  Unlike __syncthreads this leaves the newest LDS-bound
-// loads running.  The wait is the s_waitcnt builtin, which the compiler's own
-// wait placement takes into account (it then knows every older load has
-// landed); the empty asm statements keep memory accesses from moving across.
-template <int N>
-__device__ __forceinline__ void vm_barrier() {
-  static_assert(N >= 0 && N < 16, "vmcnt");
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xF70 | N);  // vmcnt(N), expcnt and lgkmcnt not waited for
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 __device__ __forceinline__ void st_chunk(char* tile, int rowb, int cpr, int r, int c, uint4 v) {
   *reinterpret_cast<uint4*>(tile + r * rowb + swz(r, c, cpr) * 16) = v;
 }

@@ -57,6 +57,20 @@ __host__ __device__ inline int block_token(const Geo& g, const BlockExt& e, int 
   return (e.f0 + f) * g.ft + (e.r0 + r) * g.fw + e.c0 + c;
 }
 
+// Wait until at most N of this wave's global loads are in flight, then the
+// workgroup barrier.  Unlike __syncthreads this leaves the newest LDS-bound
+// loads running.  The wait is the s_waitcnt builtin, which the compiler's own
+// wait placement takes into account (it then knows every older load has
+// landed); the empty asm statements keep memory accesses from moving across.
+template <int N>
+__device__ __forceinline__ void vm_barrier() {
+  static_assert(N >= 0 && N < 16, "vmcnt");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xF70 | N);  // vmcnt(N), expcnt and lgkmcnt not waited for
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // ---------------------------------------------------------------------------
 // Element conversion
 // ---------------------------------------------------------------------------

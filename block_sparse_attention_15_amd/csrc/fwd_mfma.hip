@@ -133,6 +133,56 @@ __device__ __forceinline__ void read_vt(const char* vbase, int row0, bf16x8_t (&
   }
 }
 
+// The same operands read by one asm block that waits for its own reads: the
+// compiler cannot tell a ds_read_tr builtin's LDS array and waits for every
+// LDS-bound load in flight before one, which would drain the loads of the
+// slots after this one.  The V swizzle depends on the row mod 4 only, so the
+// four reads of column tile dt share one address, 8 and 16 rows apart.
+#define PBSA_TRV(o, i, off) "ds_read_b64_tr_b16 %" #o ", %" #i " offset:" #off "\n\t"
+template <int D>
+__device__ __forceinline__ void read_vt_asm(const char* vbase, int row0, bf16x8_t (&va)[Shape<D>::DT][2]) {
+  using Sh = Shape<D>;
+  static_assert(D == 64 || D == 128, "head dimension");
+  const int lane = threadIdx.x & 63, G = lane >> 4, s16 = lane & 15;
+  const int r = row0 + 4 * (G >> 1) + (s16 >> 2);
+  unsigned ad[Sh::DT];
+#pragma unroll
+  for (int dt = 0; dt < Sh::DT; ++dt) {
+    const int col = 32 * dt + 16 * (G & 1) + 4 * (s16 & 3);
+    const char* p = vbase + r * Sh::ROWB + swz_v(r, col >> 3, Sh::CPR) * 16 + (col & 7) * 2;
+    ad[dt] = (unsigned)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
+  }
+  s16x4_t v[Sh::DT][2][2];  // [dt][ks2][h8]: rows +16*ks2 +8*h8
+  if constexpr (D == 128) {
+    asm volatile(PBSA_TRV(0, 16, 0) PBSA_TRV(1, 16, 2048) PBSA_TRV(2, 16, 4096) PBSA_TRV(3, 16, 6144)
+                 PBSA_TRV(4, 17, 0) PBSA_TRV(5, 17, 2048) PBSA_TRV(6, 17, 4096) PBSA_TRV(7, 17, 6144)
+                 PBSA_TRV(8, 18, 0) PBSA_TRV(9, 18, 2048) PBSA_TRV(10, 18, 4096) PBSA_TRV(11, 18, 6144)
+                 PBSA_TRV(12, 19, 0) PBSA_TRV(13, 19, 2048) PBSA_TRV(14, 19, 4096) PBSA_TRV(15, 19, 6144)
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(v[0][0][0]), "=&v"(v[0][0][1]), "=&v"(v[0][1][0]), "=&v"(v[0][1][1]),
+                   "=&v"(v[1][0][0]), "=&v"(v[1][0][1]), "=&v"(v[1][1][0]), "=&v"(v[1][1][1]),
+                   "=&v"(v[2][0][0]), "=&v"(v[2][0][1]), "=&v"(v[2][1][0]), "=&v"(v[2][1][1]),
+                   "=&v"(v[3][0][0]), "=&v"(v[3][0][1]), "=&v"(v[3][1][0]), "=&v"(v[3][1][1])
+                 : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]));
+  } else {
+    asm volatile(PBSA_TRV(0, 8, 0) PBSA_TRV(1, 8, 1024) PBSA_TRV(2, 8, 2048) PBSA_TRV(3, 8, 3072)
+                 PBSA_TRV(4, 9, 0) PBSA_TRV(5, 9, 1024) PBSA_TRV(6, 9, 2048) PBSA_TRV(7, 9, 3072)
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(v[0][0][0]), "=&v"(v[0][0][1]), "=&v"(v[0][1][0]), "=&v"(v[0][1][1]),
+                   "=&v"(v[1][0][0]), "=&v"(v[1][0][1]), "=&v"(v[1][1][0]), "=&v"(v[1][1][1])
+                 : "v"(ad[0]), "v"(ad[1]));
+  }
+#pragma unroll
+  for (int dt = 0; dt < Sh::DT; ++dt)
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      const s16x4_t x = v[dt][k2][0], y = v[dt][k2][1];
+      va[dt][k2] = __builtin_bit_cast(bf16x8_t, (__attribute__((ext_vector_type(8))) short){
+                                                    x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]});
+    }
+}
+#undef PBSA_TRV
+
 // One 32-key tile in LDS: K rows kbase[row0 .. row0+31], V rows likewise,
 // the first nvalid (1..32) keys valid.  ntq (<= NT) query tiles are active.
 // Returns this lane's part of the tile's probability sum for query tile 0,
@@ -140,7 +190,7 @@ __device__ __forceinline__ void read_vt(const char* vbase, int row0, bf16x8_t (&
 // first and then call mid() (the local kernel issues its next LDS-bound
 // gather there: the compiler cannot tell transposed LDS reads from such a
 // load in flight and would wait for it).
-template <int D, int NT, bool EARLY = false, typename Mid = NoMid>
+template <int D, int NT, bool EARLY = false, bool ASMV = false, typename Mid = NoMid>
 __device__ __forceinline__ float tile(const char* kbase, const char* vbase, int row0, int nvalid, int ntq, float c2,
                                      WaveState<D, NT>& st, Mid mid = Mid{}) {
   using Sh = Shape<D>;
@@ -170,7 +220,12 @@ __device__ __forceinline__ float tile(const char* kbase, const char* vbase, int 
   }
   // V^T operands read now if not yet: they do not depend on P, so their
   // latency is covered by the softmax below
-  if (!EARLY) read_vt<D>(vbase, row0, va);
+  if (!EARLY) {
+    if constexpr (ASMV)
+      read_vt_asm<D>(vbase, row0, va);
+    else
+      read_vt<D>(vbase, row0, va);
+  }
   if (nvalid < 32) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
@@ -295,6 +350,35 @@ __device__ __forceinline__ void pers_store(const PersPrefetch<D>& pf, char* buf)
   }
 }
 
+// LDS-bound loads of one persistent slot: K rows 0-63 (swz_k) then V rows
+// 0-63 (swz_v).  Every wave issues NU loads; rows past the slot's length take
+// its last row (finite; the tile gives those keys no probability), so the
+// count is the same on every path.
+template <int D> struct PersSlotDma {
+  using Sh = Shape<D>;
+  static constexpr int RPK = 1024 / Sh::ROWB;    // rows per 1 KB unit
+  static constexpr int UPT = 64 * Sh::ROWB / 1024;  // units per 64-row tensor
+  static constexpr int NU = 2 * UPT / kPersWaves;   // units per wave
+  static constexpr int BUF = 2 * 64 * Sh::ROWB;
+  static_assert(NU * kPersWaves == 2 * UPT, "whole units per wave");
+  static __device__ __forceinline__ void issue(const FwdArgs& a, size_t bh, int s, int n, char* buf) {
+    const Geo& g = a.g;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int rr = lane / Sh::CPR, pos = lane % Sh::CPR;
+    const int nl = max(n, 1) - 1;
+    const size_t sb = (bh * g.S + s) * (size_t)g.C * D;
+#pragma unroll
+    for (int i = 0; i < NU; ++i) {
+      const int u = wave * NU + i, t = u / UPT, tu = u % UPT;  // t: 0 K, 1 V
+      const int r = RPK * tu + rr;                             // slot row 0-63
+      const int c = t ? swz_v(r, pos, Sh::CPR) : swz_k(r, pos, Sh::CPR);
+      const bf16_t* src = (t ? a.vp : a.kp) + sb + (size_t)min(r, nl) * D + c * 8;
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(buf + t * 64 * Sh::ROWB + tu * 1024),
+                                       16, 0, 0);
+    }
+  }
+};
+
 template <int D, bool MASS>
 __global__ __launch_bounds__(kPersThreads, 1) void fwd_pers_kernel(FwdArgs a) {
   using Sh = Shape<D>;
@@ -319,36 +403,74 @@ __global__ __launch_bounds__(kPersThreads, 1) void fwd_pers_kernel(FwdArgs a) {
   const float c2 = g.scale * 1.4426950408889634f;
 
   if (g.S > 0) {
-    PersPrefetch<D> pf;
-    pers_load<D>(a, bh, 0, pf);
-    pers_store<D>(pf, smem);
-    __syncthreads();
-    // unrolled by two so that each half's LDS buffer is a compile-time offset
-    auto step = [&](int s, char* buf, char* nxt) {
-      const int n = min(a.plen[bh * g.S + s], g.C);
-      if (s + 1 < g.S) pers_load<D>(a, bh, s + 1, pf);
-      float bl = 0.f;  // MASS: log2-sum-exp2 over the slot
-      if (ntq > 0) {
-        float bs = 0.f;  // this lane's probability sum over the slot
-        if (n > 0) bs = tile<D, kPersNT>(buf, buf + 64 * Sh::ROWB, 0, min(n, 32), ntq, c2, st);
-        if (n > 32) {
-          const float m0 = st.m[0];
-          const float t2 = tile<D, kPersNT>(buf, buf + 64 * Sh::ROWB, 32, n - 32, ntq, c2, st);
-          bs = bs * __builtin_amdgcn_exp2f(m0 - st.m[0]) + t2;
-        }
-        if (MASS) {
-          const float tot = half_sum(bs);
-          bl = tot > 0.f ? st.m[0] + __builtin_amdgcn_logf(tot) : -INFINITY;
-        }
-      }
-      if (s + 1 < g.S) pers_store<D>(pf, nxt);
-      // stored after the LDS fill so that its wait for the prefetch does not also wait for this store
-      if (MASS && ntq > 0 && h == 0 && row_w + l32 < g.ct) a.blse_p[(bh * g.S + s) * g.ct + row_w + l32] = bl;
+    if constexpr (MASS) {
+      // register prefetch (this variant stores per-slot values inside the
+      // loop, which the counted waits of the other variant do not allow)
+      PersPrefetch<D> pf;
+      pers_load<D>(a, bh, 0, pf);
+      pers_store<D>(pf, smem);
       __syncthreads();
-    };
-    for (int s = 0; s < g.S; s += 2) {
-      step(s, smem, smem + kBufBytes);
-      if (s + 1 < g.S) step(s + 1, smem + kBufBytes, smem);
+      // unrolled by two so that each half's LDS buffer is a compile-time offset
+      auto step = [&](int s, char* buf, char* nxt) {
+        const int n = min(a.plen[bh * g.S + s], g.C);
+        if (s + 1 < g.S) pers_load<D>(a, bh, s + 1, pf);
+        float bl = 0.f;  // MASS: log2-sum-exp2 over the slot
+        if (ntq > 0) {
+          float bs = 0.f;  // this lane's probability sum over the slot
+          if (n > 0) bs = tile<D, kPersNT>(buf, buf + 64 * Sh::ROWB, 0, min(n, 32), ntq, c2, st);
+          if (n > 32) {
+            const float m0 = st.m[0];
+            const float t2 = tile<D, kPersNT>(buf, buf + 64 * Sh::ROWB, 32, n - 32, ntq, c2, st);
+            bs = bs * __builtin_amdgcn_exp2f(m0 - st.m[0]) + t2;
+          }
+          if (MASS) {
+            const float tot = half_sum(bs);
+            bl = tot > 0.f ? st.m[0] + __builtin_amdgcn_logf(tot) : -INFINITY;
+          }
+        }
+        if (s + 1 < g.S) pers_store<D>(pf, nxt);
+        // stored after the LDS fill so that its wait for the prefetch does not also wait for this store
+        if (MASS && ntq > 0 && h == 0 && row_w + l32 < g.ct) a.blse_p[(bh * g.S + s) * g.ct + row_w + l32] = bl;
+        __syncthreads();
+      };
+      for (int s = 0; s < g.S; s += 2) {
+        step(s, smem, smem + kBufBytes);
+        if (s + 1 < g.S) step(s + 1, smem + kBufBytes, smem);
+      }
+    } else {
+      // Every slot streams through LDS, loaded two steps ahead: step s
+      // computes on buffer s%3 while slots s+1 and s+2 land.  The barrier
+      // that ends a step waits for all but the loads it issued; V is read
+      // transposed by asm that the compiler's own waits do not cover.  Every
+      // step issues its loads (steps past the end repeat the last slot), so
+      // the counts hold on every path.
+      using Dm = PersSlotDma<D>;
+      __shared__ __attribute__((aligned(1024))) char pb0[Dm::BUF];
+      __shared__ __attribute__((aligned(1024))) char pb1[Dm::BUF];
+      __shared__ __attribute__((aligned(1024))) char pb2[Dm::BUF];
+      int* plen_s = reinterpret_cast<int*>(smem);  // [S] this head's slot lengths
+      for (int x = threadIdx.x; x < g.S; x += kPersThreads) plen_s[x] = min(a.plen[bh * g.S + x], g.C);
+      __syncthreads();
+      const int last = g.S - 1;
+      Dm::issue(a, bh, 0, plen_s[0], pb0);
+      Dm::issue(a, bh, min(1, last), plen_s[min(1, last)], pb1);
+      vm_barrier<Dm::NU>();
+      auto step = [&](int s, char* cur, char* nx2) {
+        const int s2 = min(s + 2, last);
+        Dm::issue(a, bh, s2, plen_s[s2], nx2);
+        if (ntq > 0 && s <= last) {
+          const int n = plen_s[s];
+          if (n > 0) tile<D, kPersNT, false, true>(cur, cur + 64 * Sh::ROWB, 0, min(n, 32), ntq, c2, st);
+          if (n > 32) tile<D, kPersNT, false, true>(cur, cur + 64 * Sh::ROWB, 32, n - 32, ntq, c2, st);
+        }
+        vm_barrier<Dm::NU>();
+      };
+      for (int s = 0; s < g.S; s += 3) {
+        step(s, pb0, pb2);
+        step(s + 1, pb1, pb0);
+        step(s + 2, pb2, pb1);
+      }
+      __builtin_amdgcn_s_waitcnt(0xF70);  // the last loads land before the workgroup can end
     }
   }
 
@@ -578,13 +700,15 @@ hipError_t set_lds(K kernel, size_t bytes) {
 template <int D, bool MASS>
 hipError_t launch_d(const FwdArgs& base, hipStream_t s) {
   static bool attr = false;
-  const size_t shm = 2 * kBufBytes;
+  // persistent kernel: the mass variant stages through dynamic LDS, the other
+  // keeps only the slot lengths there (at most 2048 slots)
+  const size_t shm = MASS ? 2 * kBufBytes : (size_t)base.g.S * 4;
   const Geo& g0 = base.g;
   const size_t tabb = (size_t)kLocBlocks * g0.K * 64 * 4;
   const bool tab = tabb <= (size_t)kRowTabMax;
   const size_t shm_loc = tab ? tabb + kLocBlocks * g0.K * 4 : 0;  // row tables (step buffers are static)
   if (!attr) {
-    hipError_t e = set_lds(fwd_pers_kernel<D, MASS>, shm);
+    hipError_t e = set_lds(fwd_pers_kernel<D, MASS>, MASS ? 2 * kBufBytes : 2048 * 4);
     if (e == hipSuccess) e = set_lds(fwd_local_kernel<D, MASS, true>, kRowTabMax + 4096);
     if (e != hipSuccess) return e;
     attr = true;
