@@ -584,14 +584,14 @@ __device__ __forceinline__ void k_init(const bf16_t* krow, const bf16_t* vrow, b
 }
 
 // One 32-query tile in LDS: Q tile tq, dO tile td, per-row lse*log2e and D.
+// Rows that do not exist carry lse*log2e = +inf (their probability is 0).
 // HOIST: read the transposed B operands ahead of the VALU work; EARLY: read
 // them first of all, then call mid(); XADDR: natural reads through per-read
 // XOR offsets from the array arr holding the tiles (see q_tile).
 template <int D, bool DV, bool HOIST, bool EARLY = false, bool XADDR = false, bool ASMTR = false,
           typename Mid = NoMid>
 __device__ __forceinline__ void k_tile(const char* tq, const char* td, const float* lse2, const float* dl, float c2,
-                                       KState<D, DV>& st, Mid mid = Mid{}, const char* arr = nullptr,
-                                       int nrow = 32) {
+                                       KState<D, DV>& st, Mid mid = Mid{}, const char* arr = nullptr) {
   static_assert(HOIST || !EARLY, "EARLY reads are hoisted reads");
   const int lane = threadIdx.x & 63, h = lane >> 5, l32 = lane & 31;
   const char* tb = DV ? td : tq;  // dV += P^T dO ; dK += dS^T Q
@@ -649,11 +649,6 @@ __device__ __forceinline__ void k_tile(const char* tq, const char* td, const flo
       x[j] = DV ? p : p * (dp[j] - Ds[jj]);
     }
   }
-  if (nrow < 32) {  // query rows past nrow hold filler data
-#pragma unroll
-    for (int j = 0; j < 16; ++j)
-      if (8 * (j >> 2) + 4 * h + (j & 3) >= nrow) x[j] = 0.f;
-  }
   const bf16x8_t x0 = pack8(x, 0), x1 = pack8(x, 1);
 #pragma unroll
   for (int dt = 0; dt < Sh<D>::DT; ++dt) {
@@ -686,9 +681,10 @@ constexpr int kKvSlots = kKvWaves / 2;
 // LDS-bound loads of one contiguous 32-row query tile of a head (Q and dO
 // rows XOR-swizzled as the tiles expect, then lse*log2(e) in lanes 0-31 and
 // D in lanes 32-63).  Every wave issues the same NLD loads (the lse2 / D row
-// by all waves, to the same place), and rows past the head's last query
-// repeat it (the tile masks them), so a wait for "all but the last NLD"
-// means exactly "all but this tile".
+// by all waves, to the same place), so a wait for "all but the last NLD"
+// means exactly "all but this tile".  Rows past the head's last query repeat
+// its Q / dO (finite) and read the lse2 / D sentinel after the last head
+// (lse2 = +inf: no probability, so they add nothing).
 template <int D> struct PersDma {
   static constexpr int RPK = 1024 / Sh<D>::ROWB;   // rows per 1 KB unit
   static constexpr int UPT = Sh<D>::TILEB / 1024;  // units per tensor tile
@@ -709,7 +705,8 @@ template <int D> struct PersDma {
       __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(buf + t * Sh<D>::TILEB + uu * 1024),
                                        16, 0, 0);
     }
-    const size_t ro = hb + min(row0 + (lane & 31), g.ct - 1);
+    const int rl = row0 + (lane & 31);
+    const size_t ro = rl < g.ct ? hb + rl : (size_t)g.B * g.H * g.ct;
     __builtin_amdgcn_global_load_lds(lane < 32 ? a.lse2 + ro : a.delta + ro,
                                      (__attribute__((address_space(3))) void*)(buf + 2 * Sh<D>::TILEB), 4, 0, 0);
   }
@@ -756,8 +753,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void dkv_pers_kernel(BwdArgs a) {
     if (nk > 0 && i <= last) {
       const float* f = reinterpret_cast<const float*>(cur + 2 * Sh<D>::TILEB);
       // the dK pass holds V too: its transposed operands are read per column tile
-      k_tile<D, DV, DV, false, false, true>(cur, cur + Sh<D>::TILEB, f, f + 32, c2, st, NoMid{}, nullptr,
-                                            min(g.ct - 32 * i, 32));
+      k_tile<D, DV, DV, false, false, true>(cur, cur + Sh<D>::TILEB, f, f + 32, c2, st);
     }
     vm_barrier<Dm::NLD>();
   };
@@ -817,7 +813,8 @@ template <int D> struct KvlGather {
   }
   // Issue the gather of the step whose tokens are held into buf: Q and dO
   // rows, and (wave 0) the rows' lse2 and D, lanes 0-31 and 32-63.  Rows
-  // without a token load row 0 of the head: finite filler that the tile masks.
+  // without a token load Q / dO row 0 of the head (finite filler) and the
+  // lse2 / D sentinel, which gives them no probability.
   __device__ __forceinline__ void gather(const BwdArgs& a, size_t bh, char* buf) {
     const Geo& g = a.g;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -836,7 +833,9 @@ template <int D> struct KvlGather {
                                        16, 0, 0);
     }
     if (wave == 0) {
-      const size_t ro = bh * g.ct + max(tokl, 0);
+      // rows without a token read the sentinel after the last head: lse2 = +inf
+      // (probability 0, so their dV and dS terms vanish) and D = 0
+      const size_t ro = tokl >= 0 ? bh * g.ct + tokl : (size_t)g.B * g.H * g.ct;
       __builtin_amdgcn_global_load_lds(lane < 32 ? a.lse2 + ro : a.delta + ro,
                                        (__attribute__((address_space(3))) void*)(buf + 2 * Sh<D>::TILEB), 4, 0, 0);
     }
@@ -878,10 +877,8 @@ __device__ __forceinline__ void kvl_pass(const BwdArgs& a, size_t bh, int p, int
       }
     };
     if (nk > 0) {
-      const int sx = steps[i];
-      const int nrow = __builtin_amdgcn_readfirstlane(min(slen[sx >> 1] - 32 * (sx & 1), 32));
       const float* f = reinterpret_cast<const float*>(cur + 2 * Sh<D>::TILEB);
-      k_tile<D, DV, true, true, true>(cur, cur + Sh<D>::TILEB, f, f + 32, c2, st, mid, cur, nrow);
+      k_tile<D, DV, true, true, true>(cur, cur + Sh<D>::TILEB, f, f + 32, c2, st, mid, cur);
     } else {
       mid();
     }

@@ -20,6 +20,13 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(Geo g, const T* __restri
                                                         float* __restrict__ lse2) {
   const int t = blockIdx.x * 4 + threadIdx.x / 64, lane = threadIdx.x & 63;
   const size_t bh = (size_t)blockIdx.z * g.H + blockIdx.y;
+  // sentinel row after the last head: rows that do not exist read lse2 = +inf
+  // (probability 0) and D = 0
+  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) {
+    const size_t end = (size_t)g.B * g.H * g.ct;
+    lse2[end] = INFINITY;
+    delta[end] = 0.f;
+  }
   if (t >= g.ct) return;
   const size_t row = (bh * g.ct + t) * g.D;
   float a = 0.f;

@@ -57,16 +57,17 @@ __host__ __device__ inline int block_token(const Geo& g, const BlockExt& e, int 
   return (e.f0 + f) * g.ft + (e.r0 + r) * g.fw + e.c0 + c;
 }
 
-// Wait until at most N of this wave's global loads are in flight, then the
-// workgroup barrier.  Unlike __syncthreads this leaves the newest LDS-bound
-// loads running.  The wait is the s_waitcnt builtin, which the compiler's own
-// wait placement takes into account (it then knows every older load has
-// landed); the empty asm statements keep memory accesses from moving across.
+// Wait until at most N of this wave's global loads are in flight and all of
+// its LDS reads have returned, then the workgroup barrier.  Unlike
+// __syncthreads this leaves the newest LDS-bound loads running.  The wait is
+// the s_waitcnt builtin, which the compiler's own wait placement takes into
+// account (it then knows every older load has landed); the empty asm
+// statements keep memory accesses from moving across.
 template <int N>
 __device__ __forceinline__ void vm_barrier() {
   static_assert(N >= 0 && N < 16, "vmcnt");
   asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xF70 | N);  // vmcnt(N), expcnt and lgkmcnt not waited for
+  __builtin_amdgcn_s_waitcnt(0x070 | N);  // vmcnt(N), lgkmcnt(0), expcnt not waited for
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
@@ -137,8 +138,8 @@ size_t fwd_workspace(const Geo& g);
 hipError_t launch_token_mass(const Geo& g, const int32_t* plen, const int32_t* topk, const float* lse,
                              const float* blse_p, const float* blse_l, float* part, float* mass, hipStream_t s);
 struct WsBwd {
-  float* delta;     // [B,H,Nq]      rowsum(dO * O)
-  float* lse2;      // [B,H,Nq]      lse * log2(e)
+  float* delta;     // [B,H,Nq] + 1  rowsum(dO * O); the extra entry is 0
+  float* lse2;      // [B,H,Nq] + 1  lse * log2(e); the extra entry is +inf (rows that do not exist)
   int32_t* tcount;  // [B,H,nl]      query blocks that selected each local block
   int32_t* tlist;   // [B,H,nl,nq]   their ids, ascending
   int32_t* korder;  // [B,H,nl]      local blocks in key-outer launch order (see launch_bwd_prep)
