@@ -42,6 +42,9 @@ SMALL = {
                             seed=25),
     # no persistent memory: plain local block-sparse attention; the update only advances the ring
     "no_persistent_bf16": ragged(persistent_cache_size=0, total_cache_size=4 * 308, seed=51),
+    # 16x16 grid, head_dim 64, 8 slots: a slot count that is not a multiple of the persistent
+    # kernels' three-deep load rotation
+    "tiny_bf16": {**synth.workload("tiny_fp32"), "dtype": "bf16", "seed": 61},
 }
 
 
@@ -114,6 +117,43 @@ def test_bwd(name):
         r = rel_l2(a, ref[k])
         print(f"{name}: {k} max-abs {err:.3g} rel-L2 {r:.3g}")
         assert err <= t["g_abs"] and r <= t["g_rel"], k
+
+
+@pytest.mark.parametrize("name", ["ragged_bf16", "block344_bf16", "tiny_bf16"])
+def test_fwd_bwd_empty_slots(name):
+    """Empty persistent slots (length 0) beside full and partial ones.  The
+    emptied slots keep their K/V rows, which must be ignored; their gradient
+    rows must come back zero."""
+    cfg = SMALL[name]
+    x = synth.make_step_inputs(cfg)
+    S = x["persist_len"].shape[-1]
+    empty = [s for s in (1, 4, 9) if s < S]
+    x["persist_len"][..., empty] = 0
+    g, _, sel = oracle_select(cfg, x, 0)
+    O, L = oracle.attend(x["q"], x["k_p"], x["v_p"], x["persist_len"], x["k_l"], x["v_l"], sel["topk_idx"], g)
+    dout = synth.make_dout(cfg, seed=cfg["seed"] + 100)
+    ref = oracle.attend_bwd(x["q"], x["k_p"], x["v_p"], x["persist_len"], x["k_l"], x["v_l"], sel["topk_idx"],
+                            dout, g)
+    st = GpuStep(cfg, x)
+    idx = dev(sel["topk_idx"])
+    st.fwd(idx)
+    gr = st.bwd(dev(dout, st.p.torch_dtype), idx)
+    torch.cuda.synchronize()
+    t = tol(cfg)
+    o = host(st.o)
+    err = np.abs(o - O).max()
+    print(f"{name}: empty slots {empty}: O max-abs {err:.3g} rel-L2 {rel_l2(o, O):.3g}")
+    assert err <= t["o_abs"] and rel_l2(o, O) <= t["o_rel"]
+    np.testing.assert_allclose(host(st.lse), L, rtol=0, atol=t["lse"])
+    for k in ("dq", "dk_p", "dv_p", "dk_l", "dv_l"):
+        a = host(gr[k])
+        assert np.isfinite(a).all(), k
+        err = np.abs(a - ref[k]).max()
+        r = rel_l2(a, ref[k])
+        print(f"{name}: {k} max-abs {err:.3g} rel-L2 {r:.3g}")
+        assert err <= t["g_abs"] and r <= t["g_rel"], k
+    for k in ("dk_p", "dv_p"):
+        assert not host(gr[k])[..., empty, :, :].any(), f"{k}: empty slots must get zero gradient"
 
 
 @pytest.mark.parametrize("name", list(SMALL))
