@@ -27,10 +27,12 @@
 //  * K is read from LDS as the A operand with 16-byte reads; V is read
 //    transposed with ds_read_b64_tr_b16 (two per 8-key operand).  Both LDS
 //    tiles are XOR-swizzled at 16-byte granularity to spread banks.
-//  * LDS is double-buffered, with one barrier per step.  The persistent
-//    kernel prefetches the next slot into registers while the current one
-//    computes; the local kernel gathers the next step's rows straight into
-//    LDS (global_load_lds_dwordx4), with no staging registers.
+//  * Rows reach LDS by LDS-bound loads (global_load_lds_dwordx4), with no
+//    staging registers.  The persistent kernel loads slots two steps ahead
+//    into three buffers and ends each step with a barrier that waits for all
+//    but the newest loads (its token-mass variant, which stores inside the
+//    loop, prefetches the next slot into registers instead); the local
+//    kernel gathers the next step's rows into two buffers.
 //  * exp2 with softmax_scale*log2(e) folded into one FMA; the running max is
 //    only raised when a tile's max exceeds it by more than 2^8 (P values stay
 //    below 256, safe in bf16 and fp32), which makes O rescales rare.
