@@ -943,12 +943,12 @@ __global__ __launch_bounds__(kKvlThreads, 2) void dkv_local_kernel(BwdArgs a) {
 // The dK/dV kernels run on a second stream of the device, forked from and
 // joined back into the caller's stream by events, so that they fill the CUs
 // the dQ kernels leave idle (the persistent dQ kernel has fewer workgroups
-// than CUs) and each chain's tail.  One side stream and event pair per
+// than CUs) and each chain's tail.  One side stream and its events per
 // device, default priority; the enqueue is serialised per device because
 // the events are shared.
 struct SideStream {
   hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
+  hipEvent_t fork = nullptr, prep = nullptr, join = nullptr;
   std::mutex mu;
 };
 constexpr int kMaxDevices = 64;
@@ -965,6 +965,7 @@ hipError_t side_stream(SideStream** out) {
   if (!ss.s) {
     if ((e = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking)) != hipSuccess) return e;
     if ((e = hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&ss.prep, hipEventDisableTiming)) != hipSuccess) return e;
     if ((e = hipEventCreateWithFlags(&ss.join, hipEventDisableTiming)) != hipSuccess) return e;
   }
   *out = &ss;
@@ -976,8 +977,10 @@ hipError_t set_lds(K kernel, size_t bytes) {
   return hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
+// The MFMA kernels: dK/dV on the side stream s2, dQ on the caller's stream s
+// (both already past the preparation).
 template <int D>
-hipError_t launch_d(const BwdArgs& base, hipStream_t s) {
+hipError_t launch_d(const BwdArgs& base, hipStream_t s, hipStream_t s2) {
   const Geo& g = base.g;
   const size_t shm_dq = 2 * 4 * Sh<D>::TILEB;                 // persistent: 2 x (K,K,V,V)
   const size_t tabb = (size_t)kLocBlocks * g.K * 64 * 4;
@@ -993,13 +996,7 @@ hipError_t launch_d(const BwdArgs& base, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr = true;
   }
-  SideStream* ss = nullptr;
-  hipError_t e = side_stream(&ss);
-  if (e != hipSuccess) return e;
-  std::lock_guard<std::mutex> lock(ss->mu);
-  const hipStream_t s2 = ss->s;
-  if ((e = hipEventRecord(ss->fork, s)) != hipSuccess) return e;
-  if ((e = hipStreamWaitEvent(s2, ss->fork, 0)) != hipSuccess) return e;
+  hipError_t e;
   BwdArgs a = base;
   // side stream: dK, dV (local blocks, then the persistent slots)
   int total = g.B * g.H * g.nl;
@@ -1024,26 +1021,41 @@ hipError_t launch_d(const BwdArgs& base, hipStream_t s) {
     dq_local_kernel<D, true><<<((total + 7) / 8) * 8, kDqlThreads, shm_dql, s>>>(a);
   else
     dq_local_kernel<D, false><<<((total + 7) / 8) * 8, kDqlThreads, shm_dql, s>>>(a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  if ((e = hipEventRecord(ss->join, s2)) != hipSuccess) return e;
-  return hipStreamWaitEvent(s, ss->join, 0);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 bool bwd_mfma_supported(const Geo& g) { return g.dtype == PBSA_BF16 && (g.D == 64 || g.D == 128) && g.C <= 64; }
 
+// Fork onto the side stream first: the key-block index and its launch order
+// (read only by the key-outer local kernel) are built there while D, lse2
+// and the geometry table are computed on the caller's stream; the side
+// stream waits for those before its kernels, and the caller's stream waits
+// for the side stream at the end.
 hipError_t launch_bwd_mfma(const Geo& g, const void* q, const void* k_p, const void* v_p, const int32_t* plen,
-                           const void* k_l, const void* v_l, const int32_t* topk, const float* lse,
+                           const void* k_l, const void* v_l, const int32_t* topk, const void* o, const float* lse,
                            const void* dout, float* dq, float* dk_p, float* dv_p, float* dk_l, float* dv_l,
                            WsBwd ws, hipStream_t s) {
-  GeoTab tab;
-  hipError_t e = launch_geo_table(g, ws.geo, &tab, s);
+  SideStream* ss = nullptr;
+  hipError_t e = side_stream(&ss);
   if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(ss->mu);
+  const hipStream_t s2 = ss->s;
+  if ((e = hipEventRecord(ss->fork, s)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(s2, ss->fork, 0)) != hipSuccess) return e;
+  if ((e = launch_bwd_index(g, topk, ws, s2)) != hipSuccess) return e;
+  if ((e = launch_bwd_delta(g, o, dout, lse, ws, s)) != hipSuccess) return e;
+  GeoTab tab;
+  if ((e = launch_geo_table(g, ws.geo, &tab, s)) != hipSuccess) return e;
+  if ((e = hipEventRecord(ss->prep, s)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(s2, ss->prep, 0)) != hipSuccess) return e;
   BwdArgs a{g, (const bf16_t*)q, (const bf16_t*)k_p, (const bf16_t*)v_p, plen, (const bf16_t*)k_l,
             (const bf16_t*)v_l, topk, lse, ws.delta, ws.lse2, (const bf16_t*)dout, ws.tcount, ws.tlist,
             ws.korder, dq, dk_p, dv_p, dk_l, dv_l, tab, 0};
-  return g.D == 128 ? launch_d<128>(a, s) : launch_d<64>(a, s);
+  if ((e = g.D == 128 ? launch_d<128>(a, s, s2) : launch_d<64>(a, s, s2)) != hipSuccess) return e;
+  if ((e = hipEventRecord(ss->join, s2)) != hipSuccess) return e;
+  return hipStreamWaitEvent(s, ss->join, 0);
 }
 
 }  // namespace pbsa

@@ -13,12 +13,17 @@ namespace pbsa {
 
 namespace {
 
-// grid (ceil(ct/4), H, B), 256 threads: one wave per query token.
-template <typename T>
+// grid (ceil(ct/RPW), H, B), 256 threads: each lane loads 16 bytes of a
+// query row of O and of dO (EPT elements), TPR = D/EPT lanes share a row
+// (RPW = 256/TPR rows per workgroup).  D = rowsum(dO * O): every lane sums
+// its EPT products in order, then the row's lanes are combined by a fixed
+// xor tree, so the result is the same on every run.
+template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(Geo g, const T* __restrict__ o, const T* __restrict__ dout,
                                                         const float* __restrict__ lse, float* __restrict__ delta,
                                                         float* __restrict__ lse2) {
-  const int t = blockIdx.x * 4 + threadIdx.x / 64, lane = threadIdx.x & 63;
+  constexpr int EPT = 16 / sizeof(T), TPR = D / EPT, RPW = 256 / TPR;
+  static_assert(TPR <= 64 && (TPR & (TPR - 1)) == 0, "row lanes");
   const size_t bh = (size_t)blockIdx.z * g.H + blockIdx.y;
   // sentinel row after the last head: rows that do not exist read lse2 = +inf
   // (probability 0) and D = 0
@@ -27,14 +32,21 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(Geo g, const T* __restri
     lse2[end] = INFINITY;
     delta[end] = 0.f;
   }
-  if (t >= g.ct) return;
-  const size_t row = (bh * g.ct + t) * g.D;
+  const int t = blockIdx.x * RPW + threadIdx.x / TPR, c = threadIdx.x % TPR;
+  const bool ok = t < g.ct;
+  const size_t row = bh * g.ct + (ok ? t : 0);
+  const uint4 ov = *reinterpret_cast<const uint4*>(o + row * D + c * EPT);
+  const uint4 dv = *reinterpret_cast<const uint4*>(dout + row * D + c * EPT);
+  const T* op = reinterpret_cast<const T*>(&ov);
+  const T* dp = reinterpret_cast<const T*>(&dv);
   float a = 0.f;
-  for (int d = lane; d < g.D; d += 64) a = fmaf(to_f<T>(o[row + d]), to_f<T>(dout[row + d]), a);
-  for (int k = 32; k > 0; k >>= 1) a += __shfl_xor(a, k, 64);
-  if (lane == 0) {
-    delta[bh * g.ct + t] = a;
-    lse2[bh * g.ct + t] = lse[bh * g.ct + t] * 1.4426950408889634f;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) a = fmaf(to_f<T>(op[e]), to_f<T>(dp[e]), a);
+#pragma unroll
+  for (int k = TPR / 2; k > 0; k >>= 1) a += __shfl_xor(a, k, TPR);
+  if (ok && c == 0) {
+    delta[row] = a;
+    lse2[row] = lse[row] * 1.4426950408889634f;
   }
 }
 
@@ -303,20 +315,33 @@ __global__ __launch_bounds__(256) void bwd_dkv_simple_kernel(Geo g, const T* __r
 
 }  // namespace
 
-hipError_t launch_bwd_prep(const Geo& g, const void* o, const void* dout, const float* lse, const int32_t* topk,
-                           WsBwd ws, hipStream_t s) {
-  dim3 g1((g.ct + 3) / 4, g.H, g.B);
-  if (g.dtype == PBSA_BF16)
-    bwd_delta_kernel<bf16_t><<<g1, 256, 0, s>>>(g, (const bf16_t*)o, (const bf16_t*)dout, lse, ws.delta, ws.lse2);
-  else
-    bwd_delta_kernel<float><<<g1, 256, 0, s>>>(g, (const float*)o, (const float*)dout, lse, ws.delta, ws.lse2);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+hipError_t launch_bwd_delta(const Geo& g, const void* o, const void* dout, const float* lse, WsBwd ws,
+                            hipStream_t s) {
+#define PBSA_DELTA(T, DD)                                                                              \
+  bwd_delta_kernel<T, DD><<<dim3((g.ct + 256 / (DD * sizeof(T) / 16) - 1) / (256 / (DD * sizeof(T) / 16)), g.H, g.B), \
+                           256, 0, s>>>(g, (const T*)o, (const T*)dout, lse, ws.delta, ws.lse2)
+  if (g.dtype == PBSA_BF16) {
+    if (g.D == 128) PBSA_DELTA(bf16_t, 128); else PBSA_DELTA(bf16_t, 64);
+  } else {
+    if (g.D == 128) PBSA_DELTA(float, 128); else PBSA_DELTA(float, 64);
+  }
+#undef PBSA_DELTA
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_index(const Geo& g, const int32_t* topk, WsBwd ws, hipStream_t s) {
   const size_t shm = (size_t)g.nl * max(1, min(g.nq, kTindexLds / g.nl));
   bwd_tindex_kernel<<<dim3(g.H, g.B), 256, shm, s>>>(g, topk, ws.tcount, ws.tlist);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   bwd_korder_kernel<<<8, 256, (size_t)(g.nq + 1 + 256) * 4, s>>>(g, ws.tcount, ws.korder);
   return hipGetLastError();
+}
+
+hipError_t launch_bwd_prep(const Geo& g, const void* o, const void* dout, const float* lse, const int32_t* topk,
+                           WsBwd ws, hipStream_t s) {
+  hipError_t e = launch_bwd_delta(g, o, dout, lse, ws, s);
+  return e != hipSuccess ? e : launch_bwd_index(g, topk, ws, s);
 }
 
 hipError_t launch_bwd_simple(const Geo& g, const void* q, const void* k_p, const void* v_p, const int32_t* plen,

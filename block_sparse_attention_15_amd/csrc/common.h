@@ -142,9 +142,15 @@ struct WsBwd {
   float* lse2;      // [B,H,Nq] + 1  lse * log2(e); the extra entry is +inf (rows that do not exist)
   int32_t* tcount;  // [B,H,nl]      query blocks that selected each local block
   int32_t* tlist;   // [B,H,nl,nq]   their ids, ascending
-  int32_t* korder;  // [B,H,nl]      local blocks in key-outer launch order (see launch_bwd_prep)
+  int32_t* korder;  // [B,H,nl]      local blocks in key-outer launch order (see bwd_korder_kernel)
   void* geo;        // geometry tables (geo_table_bytes)
 };
+// Backward preparation: D = rowsum(dO * O) and lse * log2(e) (with the
+// sentinel entries), and the key-block -> query-block index with its launch
+// order.
+hipError_t launch_bwd_delta(const Geo& g, const void* o, const void* dout, const float* lse, WsBwd ws,
+                            hipStream_t s);
+hipError_t launch_bwd_index(const Geo& g, const int32_t* topk, WsBwd ws, hipStream_t s);
 hipError_t launch_bwd(const Geo& g, const void* q, const void* k_p, const void* v_p, const int32_t* plen,
                       const void* k_l, const void* v_l, const int32_t* topk, const void* o,
                       const float* lse, const void* dout, float* dq, float* dk_p, float* dv_p,

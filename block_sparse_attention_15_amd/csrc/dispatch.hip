@@ -22,7 +22,7 @@ size_t fwd_workspace(const Geo& g) { return fwd_mfma_supported(g) ? fwd_mfma_wor
 
 bool bwd_mfma_supported(const Geo& g);
 hipError_t launch_bwd_mfma(const Geo& g, const void* q, const void* k_p, const void* v_p, const int32_t* plen,
-                           const void* k_l, const void* v_l, const int32_t* topk, const float* lse,
+                           const void* k_l, const void* v_l, const int32_t* topk, const void* o, const float* lse,
                            const void* dout, float* dq, float* dk_p, float* dv_p, float* dk_l, float* dv_l,
                            WsBwd ws, hipStream_t s);
 
@@ -38,10 +38,10 @@ hipError_t launch_bwd(const Geo& g, const void* q, const void* k_p, const void* 
                       const void* k_l, const void* v_l, const int32_t* topk, const void* o,
                       const float* lse, const void* dout, float* dq, float* dk_p, float* dv_p,
                       float* dk_l, float* dv_l, WsBwd ws, hipStream_t s) {
+  if (bwd_mfma_supported(g))  // runs its own preparation, partly on its second stream
+    return launch_bwd_mfma(g, q, k_p, v_p, plen, k_l, v_l, topk, o, lse, dout, dq, dk_p, dv_p, dk_l, dv_l, ws, s);
   hipError_t e = launch_bwd_prep(g, o, dout, lse, topk, ws, s);
   if (e != hipSuccess) return e;
-  if (bwd_mfma_supported(g))
-    return launch_bwd_mfma(g, q, k_p, v_p, plen, k_l, v_l, topk, lse, dout, dq, dk_p, dv_p, dk_l, dv_l, ws, s);
   return launch_bwd_simple(g, q, k_p, v_p, plen, k_l, v_l, topk, lse, dout, dq, dk_p, dv_p, dk_l, dv_l, ws, s);
 }
 
