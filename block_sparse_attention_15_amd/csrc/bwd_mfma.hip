@@ -987,16 +987,14 @@ hipError_t launch_d(const BwdArgs& base, hipStream_t s, hipStream_t s2) {
   const bool tab = tabb <= (size_t)kRowTabMax;
   const size_t shm_dql = tab ? tabb + kLocBlocks * g.K * 4 : 0;  // local: row tables (step buffers are static)
   const size_t shm_kvl = kvl_lds(g.nq);
-  static bool attr = false;
-  if (!attr) {
-    hipError_t e = set_lds(dq_pers_kernel<D>, shm_dq);
-    if (e == hipSuccess)
-      e = set_lds(dq_local_kernel<D, true>, kRowTabMax + 4096);
-    if (e == hipSuccess) e = set_lds(dkv_local_kernel<D>, kvl_lds(2048));
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
-  hipError_t e;
+  static PerDeviceOnce attr;
+  hipError_t e = attr.run([] {
+    hipError_t r = set_lds(dq_pers_kernel<D>, 2 * 4 * Sh<D>::TILEB);
+    if (r == hipSuccess) r = set_lds(dq_local_kernel<D, true>, kRowTabMax + 4096);
+    if (r == hipSuccess) r = set_lds(dkv_local_kernel<D>, kvl_lds(2048));
+    return r;
+  });
+  if (e != hipSuccess) return e;
   BwdArgs a = base;
   // side stream: dK, dV (local blocks, then the persistent slots)
   int total = g.B * g.H * g.nl;

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "pbsa.h"
 
 namespace pbsa {
@@ -71,6 +73,28 @@ __device__ __forceinline__ void vm_barrier() {
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
+
+// Runs a set-up step (kernel attributes) once per device: run(f) calls f
+// with the caller's device current the first time that device is seen and
+// returns its status; later calls on that device return hipSuccess.  A failed
+// f is tried again on the next call.  Thread-safe.
+struct PerDeviceOnce {
+  static constexpr int kMaxDevices = 64;
+  std::mutex mu;
+  bool done[kMaxDevices] = {};
+  template <typename F>
+  hipError_t run(F f) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (done[dev]) return hipSuccess;
+    if ((e = f()) != hipSuccess) return e;
+    done[dev] = true;
+    return hipSuccess;
+  }
+};
 
 // ---------------------------------------------------------------------------
 // Element conversion

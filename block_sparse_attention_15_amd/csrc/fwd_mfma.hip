@@ -701,7 +701,7 @@ hipError_t set_lds(K kernel, size_t bytes) {
 
 template <int D, bool MASS>
 hipError_t launch_d(const FwdArgs& base, hipStream_t s) {
-  static bool attr = false;
+  static PerDeviceOnce attr;
   // persistent kernel: the mass variant stages through dynamic LDS, the other
   // keeps only the slot lengths there (at most 2048 slots)
   const size_t shm = MASS ? 2 * kBufBytes : (size_t)base.g.S * 4;
@@ -709,11 +709,13 @@ hipError_t launch_d(const FwdArgs& base, hipStream_t s) {
   const size_t tabb = (size_t)kLocBlocks * g0.K * 64 * 4;
   const bool tab = tabb <= (size_t)kRowTabMax;
   const size_t shm_loc = tab ? tabb + kLocBlocks * g0.K * 4 : 0;  // row tables (step buffers are static)
-  if (!attr) {
-    hipError_t e = set_lds(fwd_pers_kernel<D, MASS>, MASS ? 2 * kBufBytes : 2048 * 4);
-    if (e == hipSuccess) e = set_lds(fwd_local_kernel<D, MASS, true>, kRowTabMax + 4096);
+  {
+    const hipError_t e = attr.run([] {
+      hipError_t r = set_lds(fwd_pers_kernel<D, MASS>, MASS ? 2 * kBufBytes : 2048 * 4);
+      if (r == hipSuccess) r = set_lds(fwd_local_kernel<D, MASS, true>, kRowTabMax + 4096);
+      return r;
+    });
     if (e != hipSuccess) return e;
-    attr = true;
   }
   const Geo& g = base.g;
   FwdArgs a = base;

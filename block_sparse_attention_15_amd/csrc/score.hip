@@ -304,15 +304,16 @@ hipError_t score_select_d(const Geo& g, const void* q, const void* k_l, const in
     pool_blocks_kernel<D, float><<<g1, kThreads, 0, s>>>(g, (const float*)q, (const float*)k_l, ws.qbar, kbar_l);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  static bool attr = false;
-  if (!attr) {
+  static PerDeviceOnce attr;
+  e = attr.run([] {
     for (const void* f : {(const void*)score_topk_kernel<D, 4>, (const void*)score_topk_kernel<D, 2>,
                           (const void*)score_topk_kernel<D, 1>}) {
-      e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kScoreLdsMax);
-      if (e != hipSuccess) return e;
+      const hipError_t r = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kScoreLdsMax);
+      if (r != hipSuccess) return r;
     }
-    attr = true;
-  }
+    return hipSuccess;
+  });
+  if (e != hipSuccess) return e;
   const int qpw = score_qpw(g);
   const size_t shm = score_lds(g, qpw);
   const dim3 grid((g.nq + qpw - 1) / qpw, g.H, g.B);
