@@ -377,7 +377,6 @@ __global__ __launch_bounds__(kDqThreads, 1) void dq_pers_kernel(BwdArgs a) {
     slot_store<D>(pf, smem);
     __syncthreads();
     for (int s = 0; s < g.S; ++s) {
-      char* buf = smem + (s & 1) * BUF;
       const int n = min(a.plen[bh * g.S + s], g.C);
       if (s + 1 < g.S) slot_load<D>(a, bh, s + 1, pf);
       if (active) {
@@ -930,7 +929,7 @@ __global__ __launch_bounds__(kKvlThreads, 2) void dkv_local_kernel(BwdArgs a) {
   int nsteps = 0;
   for (int x = 0; x < ncount; ++x) {
     const int nh = (slen[x] + 31) / 32;
-    if (threadIdx.x < nh) steps[nsteps + threadIdx.x] = (x << 1) | threadIdx.x;
+    if ((int)threadIdx.x < nh) steps[nsteps + threadIdx.x] = (x << 1) | threadIdx.x;
     nsteps += nh;
   }
   __syncthreads();
