@@ -552,7 +552,10 @@ __global__ __launch_bounds__(kDqlThreads, 1) void dq_local_kernel(BwdArgs a) {
       v.y += st.acc[dt][4 * i4 + 1] * g.scale;
       v.z += st.acc[dt][4 * i4 + 2] * g.scale;
       v.w += st.acc[dt][4 * i4 + 3] * g.scale;
-      *o4 = v;
+      // gradients are written once and not read again here: non-temporal
+      // stores keep them from evicting the gathered rows from L2
+      typedef float nf4 __attribute__((ext_vector_type(4)));
+      __builtin_nontemporal_store(nf4{v.x, v.y, v.z, v.w}, reinterpret_cast<nf4*>(o4));
     }
 }
 
@@ -659,6 +662,8 @@ __device__ __forceinline__ void k_tile(const char* tq, const char* td, const flo
 }
 
 // Write this wave's 32 key rows: row kr of the tile goes to dst(kr) if kr < n, else zero.
+// Non-temporal stores: the gradients are not read again by these kernels, and
+// cached they would evict the query rows the other workgroups gather.
 template <int D, bool DV, typename RowPtr>
 __device__ __forceinline__ void k_write(const KState<D, DV>& st, int n, float scale, RowPtr rows) {
   const int lane = threadIdx.x & 63, h = lane >> 5, l32 = lane & 31;
@@ -669,7 +674,8 @@ __device__ __forceinline__ void k_write(const KState<D, DV>& st, int n, float sc
     if (!rows(kr, dst)) continue;
     const bool ok = kr < n;
 #pragma unroll
-    for (int dt = 0; dt < Sh<D>::DT; ++dt) dst[32 * dt + l32] = ok ? st.acc[dt][j] * scale : 0.f;
+    for (int dt = 0; dt < Sh<D>::DT; ++dt)
+      __builtin_nontemporal_store(ok ? st.acc[dt][j] * scale : 0.f, dst + 32 * dt + l32);
   }
 }
 
