@@ -27,6 +27,9 @@ pbsa_status fail(pbsa_status st, const char* fmt, ...) {
 }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+// float index of the zero row in the delta region: after the n entries and the
+// sentinel, rounded up to 16 bytes
+size_t zrow_offset(size_t n) { return (n + 1 + 3) & ~size_t(3); }
 
 struct Plan {
   Geo g;
@@ -124,7 +127,7 @@ pbsa_status make_plan(const pbsa_config* c, Plan* p) {
   const size_t BH = (size_t)g.B * g.H;
   in.ws_score_select = align256(BH * g.nq * g.D * 4) + align256(BH * g.nq * (g.S + g.nl) * 4);
   in.ws_fwd = fwd_workspace(g);
-  in.ws_bwd = 2 * align256(BH * g.ct * 4 + 4) + 2 * align256(BH * g.nl * 4) + align256(BH * g.nl * g.nq * 4) +
+  in.ws_bwd = align256(zrow_offset(BH * g.ct) * 4 + 256) + align256(BH * g.ct * 4 + 4) + 2 * align256(BH * g.nl * 4) + align256(BH * g.nl * g.nq * 4) +
               geo_table_bytes(g);
   in.ws_persist_update = align256(BH * g.S * 4);
   in.ws_fwd_mass = align256(in.ws_fwd) + align256(BH * g.S * g.ct * 4) + align256(BH * g.K * g.ct * 4) +
@@ -311,7 +314,8 @@ pbsa_status pbsa_bwd(const pbsa_config* cfg, const void* q, const void* k_pers, 
   WsBwd w;
   char* base = (char*)ws;
   w.delta = (float*)base;
-  base += align256(BH * p.g.ct * 4 + 4);  // + a sentinel entry
+  w.zrow = w.delta + zrow_offset(BH * p.g.ct);  // after the sentinel entry, 16-byte aligned
+  base += align256(zrow_offset(BH * p.g.ct) * 4 + 256);
   w.lse2 = (float*)base;
   base += align256(BH * p.g.ct * 4 + 4);
   w.tcount = (int32_t*)base;

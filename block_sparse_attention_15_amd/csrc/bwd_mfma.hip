@@ -217,6 +217,7 @@ struct BwdArgs {
   const int32_t* tcount;
   const int32_t* tlist;
   const int32_t* korder;
+  const bf16_t* zrow;  // a zero row: the gathers' filler for key rows that do not exist
   float* dq;
   float* dkp;
   float* dvp;
@@ -264,10 +265,15 @@ __device__ __forceinline__ void q_init(const BwdArgs& a, size_t bh, int tok, boo
 // transposed LDS reads from an LDS-bound load in flight and would wait for
 // it).  XADDR: natural reads through per-read XOR offsets (nat_base) rather
 // than one live offset register per k-step (fewer registers, more VALU).
+// MASK: zero the probabilities of keys at or past nvalid.  Without it those
+// keys must have zero K rows: their dS then meets a zero row in dQ += dS K,
+// and the probability is clamped to [0, 1] (free, a modifier of the exp) so
+// that it stays finite for any log-sum-exp; that saves a compare and a
+// select per score.
 struct NoMid {
   __device__ void operator()() const {}
 };
-template <int D, bool HOIST, bool EARLY = false, bool XADDR = false, typename Mid = NoMid>
+template <int D, bool HOIST, bool EARLY = false, bool XADDR = false, bool MASK = true, typename Mid = NoMid>
 __device__ __forceinline__ void q_tile(const char* arr, int tk_rel, int tv_rel, int nvalid, float c2,
                                        QState<D>& st, Mid mid = Mid{}) {
   static_assert(HOIST || !EARLY, "EARLY reads are hoisted reads");
@@ -307,7 +313,8 @@ __device__ __forceinline__ void q_tile(const char* arr, int tk_rel, int tv_rel, 
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     const int kk = 8 * (j >> 2) + 4 * h + (j & 3);
-    const float p = kk < nvalid ? __builtin_amdgcn_exp2f(fmaf(s[j], c2, -st.lse2)) : 0.f;
+    const float e = __builtin_amdgcn_exp2f(fmaf(s[j], c2, -st.lse2));
+    const float p = MASK ? (kk < nvalid ? e : 0.f) : __builtin_amdgcn_fmed3f(e, 0.f, 1.f);
     ds[j] = p * (dp[j] - st.dl);
   }
   const bf16x8_t d0 = pack8(ds, 0), d1 = pack8(ds, 1);
@@ -381,8 +388,10 @@ __global__ __launch_bounds__(kDqThreads, 1) void dq_pers_kernel(BwdArgs a) {
       if (s + 1 < g.S) slot_load<D>(a, bh, s + 1, pf);
       if (active) {
         const int rb = (s & 1) * BUF;
-        if (n > 0) q_tile<D, kHoistDqPers>(smem, rb, rb + 2 * Sh<D>::TILEB, min(n, 32), c2, st);
-        if (n > 32) q_tile<D, kHoistDqPers>(smem, rb + Sh<D>::TILEB, rb + 3 * Sh<D>::TILEB, n - 32, c2, st);
+        // slot rows at or past n are staged as zeros: no key mask needed
+        if (n > 0) q_tile<D, kHoistDqPers, false, false, false>(smem, rb, rb + 2 * Sh<D>::TILEB, min(n, 32), c2, st);
+        if (n > 32)
+          q_tile<D, kHoistDqPers, false, false, false>(smem, rb + Sh<D>::TILEB, rb + 3 * Sh<D>::TILEB, n - 32, c2, st);
       }
       if (s + 1 < g.S) slot_store<D>(pf, smem + ((s + 1) & 1) * BUF);
       __syncthreads();
@@ -431,8 +440,8 @@ __device__ __forceinline__ void build_rowtab(const BwdArgs& a, size_t bh, int qg
 // staging registers and no LDS store instructions.  An instruction fills 1 KB
 // of the buffer (lane l at byte 16*l); lane l fetches the global chunk whose
 // swizzled position is l's, so the tile lands in the swizzled layout.  Rows
-// past a selected block's end (and absent selections) load row 0 of the
-// head's queries instead: finite values whose keys the tile masks.  TAB:
+// past a selected block's end (and absent selections) load the zero row
+// instead, so the tile needs no key mask (see q_tile).  TAB:
 // row tokens from the LDS table (compile-time, see the forward's local
 // kernel).
 template <int D, bool TAB>
@@ -447,7 +456,6 @@ __device__ __forceinline__ void loc_gather(const BwdArgs& a, size_t bh, int qg, 
   const int rr = lane / Sh<D>::CPR, pos = lane % Sh<D>::CPR;
   const bf16_t* kb = a.kl + bh * (size_t)g.NL * D;
   const bf16_t* vb = a.vl + bh * (size_t)g.NL * D;
-  const bf16_t* fill = a.q + bh * (size_t)g.ct * D;
 #pragma unroll
   for (int i = 0; i < PER_WAVE; ++i) {
     const int u = wave * PER_WAVE + i;
@@ -467,7 +475,7 @@ __device__ __forceinline__ void loc_gather(const BwdArgs& a, size_t bh, int qg, 
         }
       }
     }
-    const bf16_t* src = (tok >= 0 ? (tensor ? vb : kb) + (size_t)tok * D : fill) + c * 8;
+    const bf16_t* src = (tok >= 0 ? (tensor ? vb : kb) + (size_t)tok * D : a.zrow) + c * 8;
     __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(buf + u * 1024), 16, 0, 0);
   }
 }
@@ -525,7 +533,7 @@ __global__ __launch_bounds__(kDqlThreads, 1) void dq_local_kernel(BwdArgs a) {
     };
     if (nv > 0) {
       const int rel = (wave >> 1) * 2 * Sh<D>::TILEB;
-      q_tile<D, true, true, true>(cur, rel, rel + Sh<D>::TILEB, nv, c2, st, gather);
+      q_tile<D, true, true, true, false>(cur, rel, rel + Sh<D>::TILEB, nv, c2, st, gather);
     } else {
       gather();
     }
@@ -1055,7 +1063,7 @@ hipError_t launch_bwd_mfma(const Geo& g, const void* q, const void* k_p, const v
   if ((e = hipStreamWaitEvent(s2, ss->prep, 0)) != hipSuccess) return e;
   BwdArgs a{g, (const bf16_t*)q, (const bf16_t*)k_p, (const bf16_t*)v_p, plen, (const bf16_t*)k_l,
             (const bf16_t*)v_l, topk, lse, ws.delta, ws.lse2, (const bf16_t*)dout, ws.tcount, ws.tlist,
-            ws.korder, dq, dk_p, dv_p, dk_l, dv_l, tab, 0};
+            ws.korder, (const bf16_t*)ws.zrow, dq, dk_p, dv_p, dk_l, dv_l, tab, 0};
   if ((e = g.D == 128 ? launch_d<128>(a, s, s2) : launch_d<64>(a, s, s2)) != hipSuccess) return e;
   if ((e = hipEventRecord(ss->join, s2)) != hipSuccess) return e;
   return hipStreamWaitEvent(s, ss->join, 0);

@@ -21,16 +21,20 @@ namespace {
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(Geo g, const T* __restrict__ o, const T* __restrict__ dout,
                                                         const float* __restrict__ lse, float* __restrict__ delta,
-                                                        float* __restrict__ lse2) {
+                                                        float* __restrict__ lse2, float* __restrict__ zrow) {
   constexpr int EPT = 16 / sizeof(T), TPR = D / EPT, RPW = 256 / TPR;
   static_assert(TPR <= 64 && (TPR & (TPR - 1)) == 0, "row lanes");
   const size_t bh = (size_t)blockIdx.z * g.H + blockIdx.y;
   // sentinel row after the last head: rows that do not exist read lse2 = +inf
-  // (probability 0) and D = 0
-  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) {
-    const size_t end = (size_t)g.B * g.H * g.ct;
-    lse2[end] = INFINITY;
-    delta[end] = 0.f;
+  // (probability 0) and D = 0; and a zero row that gathers read for key rows
+  // that do not exist
+  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0) {
+    if (threadIdx.x == 0) {
+      const size_t end = (size_t)g.B * g.H * g.ct;
+      lse2[end] = INFINITY;
+      delta[end] = 0.f;
+    }
+    if (threadIdx.x < 16) reinterpret_cast<float4*>(zrow)[threadIdx.x] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
   const int t = blockIdx.x * RPW + threadIdx.x / TPR, c = threadIdx.x % TPR;
   const bool ok = t < g.ct;
@@ -319,7 +323,7 @@ hipError_t launch_bwd_delta(const Geo& g, const void* o, const void* dout, const
                             hipStream_t s) {
 #define PBSA_DELTA(T, DD)                                                                              \
   bwd_delta_kernel<T, DD><<<dim3((g.ct + 256 / (DD * sizeof(T) / 16) - 1) / (256 / (DD * sizeof(T) / 16)), g.H, g.B), \
-                           256, 0, s>>>(g, (const T*)o, (const T*)dout, lse, ws.delta, ws.lse2)
+                           256, 0, s>>>(g, (const T*)o, (const T*)dout, lse, ws.delta, ws.lse2, ws.zrow)
   if (g.dtype == PBSA_BF16) {
     if (g.D == 128) PBSA_DELTA(bf16_t, 128); else PBSA_DELTA(bf16_t, 64);
   } else {

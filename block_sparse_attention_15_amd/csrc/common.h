@@ -163,6 +163,7 @@ hipError_t launch_token_mass(const Geo& g, const int32_t* plen, const int32_t* t
                              const float* blse_p, const float* blse_l, float* part, float* mass, hipStream_t s);
 struct WsBwd {
   float* delta;     // [B,H,Nq] + 1  rowsum(dO * O); the extra entry is 0
+  float* zrow;      // 256 zero bytes after delta: a zero row (head_dim <= 128 bf16) for gathers
   float* lse2;      // [B,H,Nq] + 1  lse * log2(e); the extra entry is +inf (rows that do not exist)
   int32_t* tcount;  // [B,H,nl]      query blocks that selected each local block
   int32_t* tlist;   // [B,H,nl,nq]   their ids, ascending
