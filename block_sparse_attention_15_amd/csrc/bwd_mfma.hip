@@ -573,10 +573,13 @@ __global__ __launch_bounds__(kDqlThreads, 1) void dq_local_kernel(BwdArgs a) {
 // Key-outer state of one wave (32 keys).  The dV pass needs K only
 // (S = Q K^T, dV += P^T dO); the dK pass needs K and V (dP = dO V^T,
 // dK += dS^T Q).  Splitting the two keeps each under 256 registers so two
-// waves share a SIMD.
+// waves share a SIMD.  The dK pass holds -V: its dP product then starts from
+// D (read from LDS straight into the accumulator) and ends at D - dP, so the
+// tile forms -dS with one multiply per score, and the result is written
+// negated.
 template <int D, bool DV> struct KState {
   bf16x8_t kf[Sh<D>::KS];
-  bf16x8_t vf[DV ? 1 : Sh<D>::KS];
+  bf16x8_t vf[DV ? 1 : Sh<D>::KS];  // -V
   f32x16_t acc[Sh<D>::DT];
 };
 
@@ -586,8 +589,11 @@ __device__ __forceinline__ void k_init(const bf16_t* krow, const bf16_t* vrow, b
 #pragma unroll
   for (int ks = 0; ks < Sh<D>::KS; ++ks) {
     st.kf[ks] = __builtin_bit_cast(bf16x8_t, ok ? ld16(krow + 16 * ks + 8 * h) : make_uint4(0, 0, 0, 0));
-    if (!DV)
-      st.vf[DV ? 0 : ks] = __builtin_bit_cast(bf16x8_t, ok ? ld16(vrow + 16 * ks + 8 * h) : make_uint4(0, 0, 0, 0));
+    if (!DV) {
+      const uint4 v = ok ? ld16(vrow + 16 * ks + 8 * h) : make_uint4(0, 0, 0, 0);
+      const unsigned sg = 0x80008000u;  // bf16 sign bits
+      st.vf[DV ? 0 : ks] = __builtin_bit_cast(bf16x8_t, make_uint4(v.x ^ sg, v.y ^ sg, v.z ^ sg, v.w ^ sg));
+    }
   }
 #pragma unroll
   for (int dt = 0; dt < Sh<D>::DT; ++dt) st.acc[dt] = f32x16_t{};
@@ -623,6 +629,16 @@ __device__ __forceinline__ void k_tile(const char* tq, const char* td, const flo
   }
   mid();
   f32x16_t s = {}, dp = {};
+  if (!DV) {  // dp starts at D (rows 8i + 4h + jj of element 4i + jj)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 Dv = *reinterpret_cast<const float4*>(dl + 8 * i + 4 * h);
+      dp[4 * i] = Dv.x;
+      dp[4 * i + 1] = Dv.y;
+      dp[4 * i + 2] = Dv.z;
+      dp[4 * i + 3] = Dv.w;
+    }
+  }
   if (XADDR) {
     const int bq = nat_base<D>((int)(tq - arr), l32, h);
     const int bd = DV ? 0 : nat_base<D>((int)(td - arr), l32, h);
@@ -644,19 +660,11 @@ __device__ __forceinline__ void k_tile(const char* tq, const char* td, const flo
   for (int i = 0; i < 4; ++i) {
     const float4 L = *reinterpret_cast<const float4*>(lse2 + 8 * i + 4 * h);
     const float Ls[4] = {L.x, L.y, L.z, L.w};
-    float Ds[4] = {0.f, 0.f, 0.f, 0.f};
-    if (!DV) {
-      const float4 Dv = *reinterpret_cast<const float4*>(dl + 8 * i + 4 * h);
-      Ds[0] = Dv.x;
-      Ds[1] = Dv.y;
-      Ds[2] = Dv.z;
-      Ds[3] = Dv.w;
-    }
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const int j = 4 * i + jj;
       const float p = __builtin_amdgcn_exp2f(fmaf(s[j], c2, -Ls[jj]));
-      x[j] = DV ? p : p * (dp[j] - Ds[jj]);
+      x[j] = DV ? p : p * dp[j];  // P, or -dS = P (D - dP)
     }
   }
   const bf16x8_t x0 = pack8(x, 0), x1 = pack8(x, 1);
@@ -778,7 +786,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void dkv_pers_kernel(BwdArgs a) {
   __builtin_amdgcn_s_waitcnt(0xF70);  // the last loads land before the workgroup can end
   if (!has_slot || 32 * kh >= g.C) return;
   float* ob = (DV ? a.dvp : a.dkp) + sbase;
-  k_write<D, DV>(st, nk, DV ? 1.0f : g.scale, [&](int r, float*& dst) {
+  k_write<D, DV>(st, nk, DV ? 1.0f : -g.scale, [&](int r, float*& dst) {
     const int row = 32 * kh + r;
     if (row >= g.C) return false;
     dst = ob + (size_t)row * D;
@@ -903,7 +911,7 @@ __device__ __forceinline__ void kvl_pass(const BwdArgs& a, size_t bh, int p, int
   }
   if (nk <= 0) return;
   float* ob = (DV ? a.dvl : a.dkl) + (bh * g.NL + koff) * (size_t)D;
-  k_write<D, DV>(st, nk, DV ? 1.0f : g.scale, [&](int r, float*& dst) {
+  k_write<D, DV>(st, nk, DV ? 1.0f : -g.scale, [&](int r, float*& dst) {
     const int row = 32 * kt + r;
     if (row >= ke.len) return false;
     dst = ob + (size_t)block_token(g, ke, row) * D;
