@@ -8,19 +8,21 @@
 //   P = exp(scale q.k - lse),  dP = dO.v,  dS = P (dP - D),  D = rowsum(dO*O)
 //   dV = P^T dO,  dK = scale dS^T Q,  dQ = scale dS K.
 //
-// Four kernels, all deterministic (every output element is accumulated by one
+// Five kernels, all deterministic (every output element is accumulated by one
 // lane in a fixed order; no atomics):
 //   dq_pers   query-outer over the persistent slots: 8 waves x 32 contiguous
 //             query rows; S^T = K Q^T and dP^T = V dO^T put one query per
 //             lane (lane-local P and dS), dQ^T += K^T dS^T reads K transposed
-//             from LDS (ds_read_b64_tr_b16).  Writes dq.
+//             from LDS (ds_read_b64_tr_b16).  Writes dq, and every dS tile
+//             (bf16) for dk_ds.
 //   dq_local  the same over each query block's selected local blocks (8 waves
 //             = 4 query blocks x 2 query tiles), rows gathered straight into
 //             LDS; adds into dq.
-//   dkv_pers  key-outer: 8 waves x 32 keys (four slots) stream every query of
-//             the head through LDS in 32-row tiles; S = Q K^T and dP = dO V^T
-//             put one key per lane, dV += P^T dO and dK += dS^T Q read dO and
-//             Q transposed from LDS.
+//   dv_pers   key-outer: 8 waves x 32 keys (four slots) stream every query of
+//             the head through LDS in 32-row tiles; S = Q K^T puts one key per
+//             lane, dV += P^T dO reads dO transposed from LDS.
+//   dk_ds     key-outer like dv_pers: dK += dS^T Q from the stored dS tiles,
+//             one product where recomputing dS would take three.
 //   dkv_local key-outer over a local block (4 waves: dV and dK for 2 x 32
 //             keys), streaming only the query blocks that selected it (a
 //             key-block -> query-block index built from the top-k lists),
@@ -183,6 +185,35 @@ __device__ __forceinline__ void rd_tr_dt(const char* t, int dt, bf16x8_t (&out)[
     out[k2] = __builtin_bit_cast(bf16x8_t, s16x8_t{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]});
   }
 }
+// A dS tile (32 queries x 32 keys, bf16) as the query-outer dQ kernel stores
+// it: the 8-byte piece of query q holding keys 4m..4m+3 sits at byte
+// 1024*(m/4) + 16*(2q + m%2) + 8*((m/2)%2), i.e. each lane's two packed
+// 16-byte operands, lane-interleaved so that both the stores (1 KB per
+// instruction) and the transposed reads below (4 queries x 32 contiguous
+// bytes per 16 lanes) are dense.  out[ks2] as rd_tr(t, ks2, 0) would
+// return them from a row-major tile.
+__device__ __forceinline__ int ds_piece(int q, int m) {
+  return 1024 * (m >> 2) + 16 * (2 * q + (m & 1)) + 8 * ((m >> 1) & 1);
+}
+__device__ __forceinline__ void rd_tr_ds(const char* t, bf16x8_t (&out)[2]) {
+  const int lane = threadIdx.x & 63, G = lane >> 4, s16 = lane & 15;
+  unsigned ad[2];
+#pragma unroll
+  for (int h8 = 0; h8 < 2; ++h8) {
+    const int q = 8 * h8 + 4 * (G >> 1) + (s16 >> 2);
+    const int m = 4 * (G & 1) + (s16 & 3);
+    ad[h8] = (unsigned)(uintptr_t)(__attribute__((address_space(3))) const char*)(t + ds_piece(q, m));
+  }
+  s16x4_t v[2][2];  // [ks2][h8]; queries 16..31 are 512 bytes further
+  asm volatile(PBSA_TR(0, 4, 0) PBSA_TR(1, 5, 0) PBSA_TR(2, 4, 512) PBSA_TR(3, 5, 512) "s_waitcnt lgkmcnt(0)"
+               : "=&v"(v[0][0]), "=&v"(v[0][1]), "=&v"(v[1][0]), "=&v"(v[1][1])
+               : "v"(ad[0]), "v"(ad[1]));
+#pragma unroll
+  for (int k2 = 0; k2 < 2; ++k2) {
+    const s16x4_t x = v[k2][0], y = v[k2][1];
+    out[k2] = __builtin_bit_cast(bf16x8_t, s16x8_t{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]});
+  }
+}
 #undef PBSA_TR
 
 __device__ __forceinline__ void st_chunk(char* tile, int rowb, int cpr, int r, int c, uint4 v) {
@@ -218,6 +249,7 @@ struct BwdArgs {
   const int32_t* tlist;
   const int32_t* korder;
   const bf16_t* zrow;  // a zero row: the gathers' filler for key rows that do not exist
+  bf16_t* dsb;         // persistent dS tiles [B,H][2S key tiles][query tiles][32 x 32], bf16
   float* dq;
   float* dkp;
   float* dvp;
@@ -269,13 +301,15 @@ __device__ __forceinline__ void q_init(const BwdArgs& a, size_t bh, int tok, boo
 // keys must have zero K rows: their dS then meets a zero row in dQ += dS K,
 // and the probability is clamped to [0, 1] (free, a modifier of the exp) so
 // that it stays finite for any log-sum-exp; that saves a compare and a
-// select per score.
+// select per score.  STORE: also write the tile's dS (bf16, as rounded for
+// the dQ product) to dso, a 2 KB tile in the layout rd_tr_ds reads.
 struct NoMid {
   __device__ void operator()() const {}
 };
-template <int D, bool HOIST, bool EARLY = false, bool XADDR = false, bool MASK = true, typename Mid = NoMid>
+template <int D, bool HOIST, bool EARLY = false, bool XADDR = false, bool MASK = true, bool STORE = false,
+          typename Mid = NoMid>
 __device__ __forceinline__ void q_tile(const char* arr, int tk_rel, int tv_rel, int nvalid, float c2,
-                                       QState<D>& st, Mid mid = Mid{}) {
+                                       QState<D>& st, Mid mid = Mid{}, bf16_t* dso = nullptr) {
   static_assert(HOIST || !EARLY, "EARLY reads are hoisted reads");
   const int lane = threadIdx.x & 63, h = lane >> 5, l32 = lane & 31;
   const char* tk = arr + tk_rel;
@@ -318,6 +352,15 @@ __device__ __forceinline__ void q_tile(const char* arr, int tk_rel, int tv_rel, 
     ds[j] = p * (dp[j] - st.dl);
   }
   const bf16x8_t d0 = pack8(ds, 0), d1 = pack8(ds, 1);
+  if constexpr (STORE) {
+    // d0 holds keys 4h..4h+3 and 8+4h..8+4h+3 of this lane's query (pieces
+    // m = h and 2+h), d1 the same +16 (m = 4+h, 6+h); non-temporal: read
+    // back only by the dK kernel, much later
+    typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+    u32x4_t* t = reinterpret_cast<u32x4_t*>(dso) + 2 * l32 + h;
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, d0), t);
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, d1), t + 64);
+  }
 #pragma unroll
   for (int dt = 0; dt < Sh<D>::DT; ++dt) {
     st.acc[dt] = mfma(HOIST ? kt[HOIST ? dt : 0][0] : rd_tr<D>(tk, 0, dt), d0, st.acc[dt]);
@@ -378,6 +421,8 @@ __global__ __launch_bounds__(kDqThreads, 1) void dq_pers_kernel(BwdArgs a) {
   QState<D> st;
   q_init<D>(a, bh, ok ? r : 0, ok, st);
   const float c2 = g.scale * kLog2e;
+  const int nqt = (g.ct + 31) / 32;  // query tiles of the head; this wave's is qt * kDqWaves + wave
+  bf16_t* dsw = a.dsb + ((size_t)bh * 2 * g.S * nqt + qt * kDqWaves + wave) * 1024;
   if (g.S > 0) {
     SlotPf<D> pf;
     slot_load<D>(a, bh, 0, pf);
@@ -388,10 +433,15 @@ __global__ __launch_bounds__(kDqThreads, 1) void dq_pers_kernel(BwdArgs a) {
       if (s + 1 < g.S) slot_load<D>(a, bh, s + 1, pf);
       if (active) {
         const int rb = (s & 1) * BUF;
-        // slot rows at or past n are staged as zeros: no key mask needed
-        if (n > 0) q_tile<D, kHoistDqPers, false, false, false>(smem, rb, rb + 2 * Sh<D>::TILEB, min(n, 32), c2, st);
+        // slot rows at or past n are staged as zeros: no key mask needed;
+        // dS goes to the tiles of key tiles 2s and 2s+1
+        bf16_t* dso = dsw + (size_t)(2 * s) * nqt * 1024;
+        if (n > 0)
+          q_tile<D, kHoistDqPers, false, false, false, true>(smem, rb, rb + 2 * Sh<D>::TILEB, min(n, 32), c2, st,
+                                                             NoMid{}, dso);
         if (n > 32)
-          q_tile<D, kHoistDqPers, false, false, false>(smem, rb + Sh<D>::TILEB, rb + 3 * Sh<D>::TILEB, n - 32, c2, st);
+          q_tile<D, kHoistDqPers, false, false, false, true>(smem, rb + Sh<D>::TILEB, rb + 3 * Sh<D>::TILEB, n - 32,
+                                                             c2, st, NoMid{}, dso + (size_t)nqt * 1024);
       }
       if (s + 1 < g.S) slot_store<D>(pf, smem + ((s + 1) & 1) * BUF);
       __syncthreads();
@@ -570,10 +620,10 @@ __global__ __launch_bounds__(kDqlThreads, 1) void dq_local_kernel(BwdArgs a) {
 // ===========================================================================
 // dK, dV, key-outer
 // ===========================================================================
-// Key-outer state of one wave (32 keys).  The dV pass needs K only
-// (S = Q K^T, dV += P^T dO); the dK pass needs K and V (dP = dO V^T,
-// dK += dS^T Q).  Splitting the two keeps each under 256 registers so two
-// waves share a SIMD.  The dK pass holds -V: its dP product then starts from
+// Key-outer state of one wave (32 keys).  A dV role needs K only
+// (S = Q K^T, dV += P^T dO); a dK role needs K and V (dP = dO V^T,
+// dK += dS^T Q).  Separate waves keep each under 256 registers so two
+// waves share a SIMD.  The dK role holds -V: its dP product then starts from
 // D (read from LDS straight into the accumulator) and ends at D - dP, so the
 // tile forms -dS with one multiply per score, and the result is written
 // negated.
@@ -601,26 +651,25 @@ __device__ __forceinline__ void k_init(const bf16_t* krow, const bf16_t* vrow, b
 
 // One 32-query tile in LDS: Q tile tq, dO tile td, per-row lse*log2e and D.
 // Rows that do not exist carry lse*log2e = +inf (their probability is 0).
-// HOIST: read the transposed B operands ahead of the VALU work; EARLY: read
-// them first of all, then call mid(); XADDR: natural reads through per-read
-// XOR offsets from the array arr holding the tiles (see q_tile).
-template <int D, bool DV, bool HOIST, bool EARLY = false, bool XADDR = false, bool ASMTR = false,
-          typename Mid = NoMid>
+// The transposed B operands are read ahead of the VALU work: after the
+// first products, or with EARLY first of all, before mid(); XADDR: natural
+// reads through per-read XOR offsets from the array arr holding the tiles
+// (see q_tile); ASMTR: transposed reads in one asm block (rd_tr_all).
+template <int D, bool DV, bool EARLY = false, bool XADDR = false, bool ASMTR = false, typename Mid = NoMid>
 __device__ __forceinline__ void k_tile(const char* tq, const char* td, const float* lse2, const float* dl, float c2,
                                        KState<D, DV>& st, Mid mid = Mid{}, const char* arr = nullptr) {
-  static_assert(HOIST || !EARLY, "EARLY reads are hoisted reads");
   const int lane = threadIdx.x & 63, h = lane >> 5, l32 = lane & 31;
   const char* tb = DV ? td : tq;  // dV += P^T dO ; dK += dS^T Q
-  bf16x8_t bt[HOIST ? Sh<D>::DT : 1][2];  // transposed B operands
+  bf16x8_t bt[Sh<D>::DT][2];      // transposed B operands
   auto read_bt = [&]() {
-    if constexpr (ASMTR && HOIST) {
+    if constexpr (ASMTR) {
       rd_tr_all<D>(tb, bt);
       return;
     }
 #pragma unroll
     for (int dt = 0; dt < Sh<D>::DT; ++dt) {
-      bt[HOIST ? dt : 0][0] = rd_tr<D>(tb, 0, dt);
-      bt[HOIST ? dt : 0][1] = rd_tr<D>(tb, 1, dt);
+      bt[dt][0] = rd_tr<D>(tb, 0, dt);
+      bt[dt][1] = rd_tr<D>(tb, 1, dt);
     }
   };
   if (EARLY) {
@@ -654,7 +703,7 @@ __device__ __forceinline__ void k_tile(const char* tq, const char* td, const flo
       if (!DV) dp = mfma(rd_nat<D>(td, l32, 2 * ks + h), st.vf[DV ? 0 : ks], dp);
     }
   }
-  if (HOIST && !EARLY) read_bt();
+  if (!EARLY) read_bt();
   f32x16_t x;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -670,10 +719,8 @@ __device__ __forceinline__ void k_tile(const char* tq, const char* td, const flo
   const bf16x8_t x0 = pack8(x, 0), x1 = pack8(x, 1);
 #pragma unroll
   for (int dt = 0; dt < Sh<D>::DT; ++dt) {
-    if constexpr (ASMTR && !HOIST) rd_tr_dt<D>(tb, dt, bt[0]);
-    const bool direct = HOIST || ASMTR;
-    st.acc[dt] = mfma(x0, direct ? bt[HOIST ? dt : 0][0] : rd_tr<D>(tb, 0, dt), st.acc[dt]);
-    st.acc[dt] = mfma(x1, direct ? bt[HOIST ? dt : 0][1] : rd_tr<D>(tb, 1, dt), st.acc[dt]);
+    st.acc[dt] = mfma(x0, bt[dt][0], st.acc[dt]);
+    st.acc[dt] = mfma(x1, bt[dt][1], st.acc[dt]);
   }
 }
 
@@ -695,7 +742,7 @@ __device__ __forceinline__ void k_write(const KState<D, DV>& st, int n, float sc
   }
 }
 
-constexpr int kKvWaves = 8;       // dkv_pers: 8 waves = 4 slots x 2 key tiles
+constexpr int kKvWaves = 8;       // dv_pers, dk_ds: 8 waves = 4 slots x 2 key tiles
 constexpr int kKvThreads = 64 * kKvWaves;
 constexpr int kKvSlots = kKvWaves / 2;
 
@@ -733,8 +780,10 @@ template <int D> struct PersDma {
   }
 };
 
-template <int D, bool DV>
-__global__ __launch_bounds__(kKvThreads, 1) void dkv_pers_kernel(BwdArgs a) {
+// dV of the persistent slots (their dK comes from dk_ds).
+template <int D>
+__global__ __launch_bounds__(kKvThreads, 1) void dv_pers_kernel(BwdArgs a) {
+  constexpr bool DV = true;
   using Dm = PersDma<D>;
   // three step buffers, separate arrays so that the compiler can tell the
   // loads into one from the reads of another
@@ -773,8 +822,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void dkv_pers_kernel(BwdArgs a) {
     Dm::issue(a, bh, 32 * min(i + 2, last), nx2);
     if (nk > 0 && i <= last) {
       const float* f = reinterpret_cast<const float*>(cur + 2 * Sh<D>::TILEB);
-      // the dK pass holds V too: its transposed operands are read per column tile
-      k_tile<D, DV, DV, false, false, true>(cur, cur + Sh<D>::TILEB, f, f + 32, c2, st);
+      k_tile<D, DV, false, false, true>(cur, cur + Sh<D>::TILEB, f, f + 32, c2, st);
     }
     vm_barrier<Dm::NLD>();
   };
@@ -785,8 +833,105 @@ __global__ __launch_bounds__(kKvThreads, 1) void dkv_pers_kernel(BwdArgs a) {
   }
   __builtin_amdgcn_s_waitcnt(0xF70);  // the last loads land before the workgroup can end
   if (!has_slot || 32 * kh >= g.C) return;
-  float* ob = (DV ? a.dvp : a.dkp) + sbase;
-  k_write<D, DV>(st, nk, DV ? 1.0f : -g.scale, [&](int r, float*& dst) {
+  float* ob = a.dvp + sbase;
+  k_write<D, DV>(st, nk, 1.0f, [&](int r, float*& dst) {
+    const int row = 32 * kh + r;
+    if (row >= g.C) return false;
+    dst = ob + (size_t)row * D;
+    return true;
+  });
+}
+
+// dK of the persistent slots from the dS tiles that dq_pers stored:
+// dK = scale dS^T Q, one product instead of the three of a recomputing pass.
+// Key-outer like dv_pers (8 waves = 4 slots x 2 key tiles, 32 keys per
+// wave): every query tile of the head streams through LDS with each wave's
+// dS tile for it, loaded two steps ahead into three buffers; both operands
+// are read transposed (dS^T with lane = key, Q with lane = column), so their
+// query orders match.  Every wave issues the same loads in every step
+// (waves whose key tile holds no keys load tile 0's and skip the product;
+// Q units beyond the tile's are loaded twice by two waves, the same bytes).
+template <int D> struct DsDma {
+  static constexpr int RPK = 1024 / Sh<D>::ROWB;   // rows per 1 KB unit
+  static constexpr int UPT = Sh<D>::TILEB / 1024;  // units per Q tile
+  static constexpr int NQ = UPT >= kKvWaves ? UPT / kKvWaves : 1;
+  static constexpr int NLD = NQ + 2;               // Q units, then the wave's 2 KB dS tile
+  static constexpr int QB = Sh<D>::TILEB;          // the dS tiles follow the Q tile
+  static constexpr int BUF = QB + kKvWaves * 2048;
+  static_assert(UPT % kKvWaves == 0 || kKvWaves % UPT == 0, "whole Q units per wave");
+  static __device__ __forceinline__ void issue(const BwdArgs& a, size_t bh, const bf16_t* dsw, int qtile,
+                                               char* buf) {
+    const Geo& g = a.g;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int rr = lane / Sh<D>::CPR, pos = lane % Sh<D>::CPR;
+    const int row0 = 32 * qtile;
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      const int u = (wave * NQ + i) % UPT, r = RPK * u + rr;
+      const bf16_t* src = a.q + (bh * g.ct + min(row0 + r, g.ct - 1)) * D + swz(r, pos, Sh<D>::CPR) * 8;
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(buf + u * 1024), 16, 0, 0);
+    }
+    // the dS tile, read once: a streaming (nt) load, so that the 2 KB tiles
+    // of the whole pass do not evict what the caches hold for later kernels
+    const bf16_t* ds = dsw + (size_t)qtile * 1024 + lane * 8;
+    constexpr int kNt = 2;  // cache-policy operand: nt
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      __builtin_amdgcn_global_load_lds(ds + u * 512,
+                                       (__attribute__((address_space(3))) void*)(buf + QB + wave * 2048 + u * 1024),
+                                       16, 0, kNt);
+  }
+};
+
+template <int D>
+__global__ __launch_bounds__(kKvThreads, 1) void dk_ds_kernel(BwdArgs a) {
+  using Dm = DsDma<D>;
+  __shared__ __attribute__((aligned(1024))) char db0[Dm::BUF];
+  __shared__ __attribute__((aligned(1024))) char db1[Dm::BUF];
+  __shared__ __attribute__((aligned(1024))) char db2[Dm::BUF];
+  const Geo& g = a.g;
+  const int total = g.B * g.H * a.ntiles;
+  const int lin = xcd_remap(total);
+  if (lin >= total) return;
+  const int sp = lin % a.ntiles;  // slot group
+  const size_t bh = lin / a.ntiles;
+  const int wave = threadIdx.x >> 6;
+  const int slot = kKvSlots * sp + (wave >> 1), kh = wave & 1;
+  const bool has_slot = slot < g.S;
+  const int n = has_slot ? min(a.plen[bh * g.S + slot], g.C) : 0;
+  const int nk = __builtin_amdgcn_readfirstlane(min(max(n - 32 * kh, 0), 32));  // valid keys of this wave's tile
+  const int nqt = (g.ct + 31) / 32, last = nqt - 1;
+  const bf16_t* dsw = a.dsb + ((size_t)bh * 2 * g.S + (has_slot ? 2 * slot + kh : 0)) * nqt * 1024;
+  KState<D, true> st;
+#pragma unroll
+  for (int dt = 0; dt < Sh<D>::DT; ++dt) st.acc[dt] = f32x16_t{};
+  Dm::issue(a, bh, dsw, 0, db0);
+  Dm::issue(a, bh, dsw, min(1, last), db1);
+  vm_barrier<Dm::NLD>();
+  auto step = [&](int i, char* cur, char* nx2) {
+    Dm::issue(a, bh, dsw, min(i + 2, last), nx2);
+    if (nk > 0 && i <= last) {
+      bf16x8_t as[2];
+      rd_tr_ds(cur + Dm::QB + wave * 2048, as);
+#pragma unroll
+      for (int dt = 0; dt < Sh<D>::DT; ++dt) {
+        bf16x8_t bt[2];
+        rd_tr_dt<D>(cur, dt, bt);
+        st.acc[dt] = mfma(as[0], bt[0], st.acc[dt]);
+        st.acc[dt] = mfma(as[1], bt[1], st.acc[dt]);
+      }
+    }
+    vm_barrier<Dm::NLD>();
+  };
+  for (int i = 0; i < nqt; i += 3) {
+    step(i, db0, db2);
+    step(i + 1, db1, db0);
+    step(i + 2, db2, db1);
+  }
+  __builtin_amdgcn_s_waitcnt(0xF70);  // the last loads land before the workgroup can end
+  if (!has_slot || 32 * kh >= g.C) return;
+  float* ob = a.dkp + (bh * g.S + slot) * (size_t)g.C * D;
+  k_write<D, true>(st, nk, g.scale, [&](int r, float*& dst) {
     const int row = 32 * kh + r;
     if (row >= g.C) return false;
     dst = ob + (size_t)row * D;
@@ -899,7 +1044,7 @@ __device__ __forceinline__ void kvl_pass(const BwdArgs& a, size_t bh, int p, int
     };
     if (nk > 0) {
       const float* f = reinterpret_cast<const float*>(cur + 2 * Sh<D>::TILEB);
-      k_tile<D, DV, true, true, true>(cur, cur + Sh<D>::TILEB, f, f + 32, c2, st, mid, cur);
+      k_tile<D, DV, true, true>(cur, cur + Sh<D>::TILEB, f, f + 32, c2, st, mid, cur);
     } else {
       mid();
     }
@@ -969,7 +1114,7 @@ __global__ __launch_bounds__(kKvlThreads, 2) void dkv_local_kernel(BwdArgs a) {
 // the events are shared.
 struct SideStream {
   hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, prep = nullptr, join = nullptr;
+  hipEvent_t fork = nullptr, prep = nullptr, dsready = nullptr, join = nullptr;
   std::mutex mu;
 };
 constexpr int kMaxDevices = 64;
@@ -987,6 +1132,7 @@ hipError_t side_stream(SideStream** out) {
     if ((e = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking)) != hipSuccess) return e;
     if ((e = hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming)) != hipSuccess) return e;
     if ((e = hipEventCreateWithFlags(&ss.prep, hipEventDisableTiming)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&ss.dsready, hipEventDisableTiming)) != hipSuccess) return e;
     if ((e = hipEventCreateWithFlags(&ss.join, hipEventDisableTiming)) != hipSuccess) return e;
   }
   *out = &ss;
@@ -999,9 +1145,12 @@ hipError_t set_lds(K kernel, size_t bytes) {
 }
 
 // The MFMA kernels: dK/dV on the side stream s2, dQ on the caller's stream s
-// (both already past the preparation).
+// (both already past the preparation).  dq_pers writes the persistent dS
+// tiles that dk_ds reads: the side stream waits for it (event dsready,
+// recorded before the wait is issued) after its dK/dV of the local blocks and
+// its dV of the slots.
 template <int D>
-hipError_t launch_d(const BwdArgs& base, hipStream_t s, hipStream_t s2) {
+hipError_t launch_d(const BwdArgs& base, hipStream_t s, hipStream_t s2, hipEvent_t dsready) {
   const Geo& g = base.g;
   const size_t shm_dq = 2 * 4 * Sh<D>::TILEB;                 // persistent: 2 x (K,K,V,V)
   const size_t tabb = (size_t)kLocBlocks * g.K * 64 * 4;
@@ -1017,23 +1166,32 @@ hipError_t launch_d(const BwdArgs& base, hipStream_t s, hipStream_t s2) {
   });
   if (e != hipSuccess) return e;
   BwdArgs a = base;
-  // side stream: dK, dV (local blocks, then the persistent slots)
+  // side stream: dK, dV of the local blocks, then dV of the persistent slots
   int total = g.B * g.H * g.nl;
   dkv_local_kernel<D><<<((total + 7) / 8) * 8, kKvlThreads, shm_kvl, s2>>>(a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int kv_tiles = (g.S + kKvSlots - 1) / kKvSlots;
   if (g.S > 0) {
-    a.ntiles = (g.S + kKvSlots - 1) / kKvSlots;
+    a.ntiles = kv_tiles;
     total = g.B * g.H * a.ntiles;
-    dkv_pers_kernel<D, true><<<((total + 7) / 8) * 8, kKvThreads, 0, s2>>>(a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    dkv_pers_kernel<D, false><<<((total + 7) / 8) * 8, kKvThreads, 0, s2>>>(a);
+    dv_pers_kernel<D><<<((total + 7) / 8) * 8, kKvThreads, 0, s2>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  // caller's stream: dq (persistent part writes, local part adds)
+  // caller's stream: dq of the persistent slots (writes dq and the dS tiles)
   a.ntiles = (g.ct + kDqRows - 1) / kDqRows;
   total = g.B * g.H * a.ntiles;
   dq_pers_kernel<D><<<((total + 7) / 8) * 8, kDqThreads, shm_dq, s>>>(a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (g.S > 0) {
+    // side stream: dK of the persistent slots from the dS tiles
+    if ((e = hipEventRecord(dsready, s)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(s2, dsready, 0)) != hipSuccess) return e;
+    a.ntiles = kv_tiles;
+    total = g.B * g.H * a.ntiles;
+    dk_ds_kernel<D><<<((total + 7) / 8) * 8, kKvThreads, 0, s2>>>(a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  // caller's stream: dq of the local blocks (adds)
   a.ntiles = (g.nq + kLocBlocks - 1) / kLocBlocks;
   total = g.B * g.H * a.ntiles;
   if (tab)
@@ -1046,6 +1204,11 @@ hipError_t launch_d(const BwdArgs& base, hipStream_t s, hipStream_t s2) {
 }  // namespace
 
 bool bwd_mfma_supported(const Geo& g) { return g.dtype == PBSA_BF16 && (g.D == 64 || g.D == 128) && g.C <= 64; }
+
+size_t bwd_ds_bytes(const Geo& g) {
+  if (!bwd_mfma_supported(g) || g.S <= 0) return 0;
+  return (size_t)g.B * g.H * 2 * g.S * ((g.ct + 31) / 32) * 32 * 32 * 2;
+}
 
 // Fork onto the side stream first: the key-block index and its launch order
 // (read only by the key-outer local kernel) are built there while D, lse2
@@ -1071,8 +1234,9 @@ hipError_t launch_bwd_mfma(const Geo& g, const void* q, const void* k_p, const v
   if ((e = hipStreamWaitEvent(s2, ss->prep, 0)) != hipSuccess) return e;
   BwdArgs a{g, (const bf16_t*)q, (const bf16_t*)k_p, (const bf16_t*)v_p, plen, (const bf16_t*)k_l,
             (const bf16_t*)v_l, topk, lse, ws.delta, ws.lse2, (const bf16_t*)dout, ws.tcount, ws.tlist,
-            ws.korder, (const bf16_t*)ws.zrow, dq, dk_p, dv_p, dk_l, dv_l, tab, 0};
-  if ((e = g.D == 128 ? launch_d<128>(a, s, s2) : launch_d<64>(a, s, s2)) != hipSuccess) return e;
+            ws.korder, (const bf16_t*)ws.zrow, (bf16_t*)ws.dsb, dq, dk_p, dv_p, dk_l, dv_l, tab, 0};
+  if ((e = g.D == 128 ? launch_d<128>(a, s, s2, ss->dsready) : launch_d<64>(a, s, s2, ss->dsready)) != hipSuccess)
+    return e;
   if ((e = hipEventRecord(ss->join, s2)) != hipSuccess) return e;
   return hipStreamWaitEvent(s, ss->join, 0);
 }

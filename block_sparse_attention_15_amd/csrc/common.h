@@ -137,6 +137,9 @@ struct GeoTab {
   const int32_t* pblk;   // [nl]
 };
 size_t geo_table_bytes(const Geo& g);
+// Bytes of the persistent dS tiles that the MFMA backward passes from its dQ
+// kernel to its dK kernel (0 where that path is not used).
+size_t bwd_ds_bytes(const Geo& g);
 hipError_t launch_geo_table(const Geo& g, void* ws, GeoTab* tab, hipStream_t s);
 
 struct WsScore {
@@ -168,6 +171,7 @@ struct WsBwd {
   int32_t* tcount;  // [B,H,nl]      query blocks that selected each local block
   int32_t* tlist;   // [B,H,nl,nq]   their ids, ascending
   int32_t* korder;  // [B,H,nl]      local blocks in key-outer launch order (see bwd_korder_kernel)
+  void* dsb;        // bwd_ds_bytes: dS of the persistent slots as bf16 32x32 tiles (MFMA path)
   void* geo;        // geometry tables (geo_table_bytes)
 };
 // Backward preparation: D = rowsum(dO * O) and lse * log2(e) (with the

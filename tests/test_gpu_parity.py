@@ -160,6 +160,48 @@ def test_fwd_bwd_empty_slots(name):
         assert not host(gr[k])[..., empty, :, :].any(), f"{k}: empty slots must get zero gradient"
 
 
+@pytest.mark.parametrize("name", ["ragged_bf16", "block344_bf16"])
+def test_bwd_very_negative_scores(name):
+    """Every score near -120 (queries and keys shifted in opposite directions),
+    beside partial persistent slots and short local blocks.  The dQ kernels
+    take no key mask: key rows that do not exist are zero, and exp(-lse) of
+    such a row (about e^120, beyond fp32) must be clamped, not overflow into
+    inf * 0 = NaN."""
+    cfg = SMALL[name]
+    x = synth.make_step_inputs(cfg)
+    C = x["k_p"].shape[-2]
+    S = x["persist_len"].shape[-1]
+    x["persist_len"][..., 0] = min(C, 17)
+    if S > 3:
+        x["persist_len"][..., 3] = min(C, 40)
+    D = x["q"].shape[-1]
+    scale = cfg.get("softmax_scale") or D ** -0.5
+    shift = np.float32(np.sqrt(120.0 / scale / D))  # scale * (-shift^2 * D) = -120
+    x["q"] = synth.bf16_round(x["q"] - shift)
+    for k in ("k_p", "k_l"):
+        x[k] = synth.bf16_round(x[k] + shift)
+    g, _, sel = oracle_select(cfg, x, 0)
+    O, L = oracle.attend(x["q"], x["k_p"], x["v_p"], x["persist_len"], x["k_l"], x["v_l"], sel["topk_idx"], g)
+    assert L.max() < -80, "scores are not as negative as intended"
+    dout = synth.make_dout(cfg, seed=cfg["seed"] + 200)
+    ref = oracle.attend_bwd(x["q"], x["k_p"], x["v_p"], x["persist_len"], x["k_l"], x["v_l"], sel["topk_idx"],
+                            dout, g)
+    st = GpuStep(cfg, x)
+    idx = dev(sel["topk_idx"])
+    st.fwd(idx)
+    gr = st.bwd(dev(dout, st.p.torch_dtype), idx)
+    torch.cuda.synchronize()
+    t = tol(cfg)
+    for k in ("dq", "dk_p", "dv_p", "dk_l", "dv_l"):
+        a = host(gr[k])
+        assert np.isfinite(a).all(), k
+        scale = max(1.0, float(np.abs(ref[k]).max()))
+        err = np.abs(a - ref[k]).max()
+        r = rel_l2(a, ref[k])
+        print(f"{name}: {k} max-abs {err:.3g} (of {scale:.3g}) rel-L2 {r:.3g}")
+        assert err <= t["g_abs"] * scale and r <= t["g_rel"], k
+
+
 @pytest.mark.parametrize("name", list(SMALL))
 @pytest.mark.parametrize("ring_head", [0, 1])
 def test_update(name, ring_head):
