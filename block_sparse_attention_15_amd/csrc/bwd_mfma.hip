@@ -379,28 +379,30 @@ template <int D> struct SlotPf {
 };
 
 template <int D>
+// Unconditional loads (rows clamped to the slot's last): the rows at or past
+// the slot's length are zeroed when staged, after the wait for the loads.
 __device__ __forceinline__ void slot_load(const BwdArgs& a, size_t bh, int s, SlotPf<D>& pf) {
   const Geo& g = a.g;
-  const int n = min(a.plen[bh * g.S + s], g.C);
   const bf16_t* kb = a.kp + (bh * g.S + s) * (size_t)g.C * D;
   const bf16_t* vb = a.vp + (bh * g.S + s) * (size_t)g.C * D;
 #pragma unroll
   for (int u = 0; u < SlotPf<D>::N; ++u) {
-    const int id = threadIdx.x + kDqThreads * u, r = id / Sh<D>::CPR, c = id % Sh<D>::CPR;
-    const bool ok = r < n;
-    pf.k[u] = ok ? ld16(kb + (size_t)r * D + c * 8) : make_uint4(0, 0, 0, 0);
-    pf.v[u] = ok ? ld16(vb + (size_t)r * D + c * 8) : make_uint4(0, 0, 0, 0);
+    const int id = threadIdx.x + kDqThreads * u, r = min(id / Sh<D>::CPR, g.C - 1), c = id % Sh<D>::CPR;
+    pf.k[u] = ld16(kb + (size_t)r * D + c * 8);
+    pf.v[u] = ld16(vb + (size_t)r * D + c * 8);
   }
 }
 
 // LDS: K rows 0-31, K rows 32-63, V rows 0-31, V rows 32-63 (four tiles)
 template <int D>
-__device__ __forceinline__ void slot_store(const SlotPf<D>& pf, char* buf) {
+__device__ __forceinline__ void slot_store(const SlotPf<D>& pf, char* buf, int n) {
 #pragma unroll
   for (int u = 0; u < SlotPf<D>::N; ++u) {
     const int id = threadIdx.x + kDqThreads * u, r = id / Sh<D>::CPR, c = id % Sh<D>::CPR;
-    st_chunk(buf + (r >> 5) * Sh<D>::TILEB, Sh<D>::ROWB, Sh<D>::CPR, r & 31, c, pf.k[u]);
-    st_chunk(buf + (2 + (r >> 5)) * Sh<D>::TILEB, Sh<D>::ROWB, Sh<D>::CPR, r & 31, c, pf.v[u]);
+    const bool ok = r < n;
+    st_chunk(buf + (r >> 5) * Sh<D>::TILEB, Sh<D>::ROWB, Sh<D>::CPR, r & 31, c, ok ? pf.k[u] : make_uint4(0, 0, 0, 0));
+    st_chunk(buf + (2 + (r >> 5)) * Sh<D>::TILEB, Sh<D>::ROWB, Sh<D>::CPR, r & 31, c,
+             ok ? pf.v[u] : make_uint4(0, 0, 0, 0));
   }
 }
 
@@ -423,27 +425,31 @@ __global__ __launch_bounds__(kDqThreads, 1) void dq_pers_kernel(BwdArgs a) {
   const float c2 = g.scale * kLog2e;
   const int nqt = (g.ct + 31) / 32;  // query tiles of the head; this wave's is qt * kDqWaves + wave
   bf16_t* dsw = a.dsb + ((size_t)bh * 2 * g.S * nqt + qt * kDqWaves + wave) * 1024;
+  // Slot lengths go to LDS before the first dS store: a length read from
+  // global memory later would wait (vmcnt) for every store in flight.
+  int* plen_s = reinterpret_cast<int*>(smem + 2 * BUF);
+  for (int i = threadIdx.x; i < g.S; i += kDqThreads) plen_s[i] = min(a.plen[bh * g.S + i], g.C);
+  __syncthreads();
   if (g.S > 0) {
     SlotPf<D> pf;
     slot_load<D>(a, bh, 0, pf);
-    slot_store<D>(pf, smem);
+    slot_store<D>(pf, smem, plen_s[0]);
     __syncthreads();
     for (int s = 0; s < g.S; ++s) {
-      const int n = min(a.plen[bh * g.S + s], g.C);
       if (s + 1 < g.S) slot_load<D>(a, bh, s + 1, pf);
       if (active) {
-        const int rb = (s & 1) * BUF;
-        // slot rows at or past n are staged as zeros: no key mask needed;
-        // dS goes to the tiles of key tiles 2s and 2s+1
+        // slot rows at or past n are staged as zeros: no key mask needed
+        // (see q_tile); dS goes to the tiles of key tiles 2s and 2s+1
+        const int n = plen_s[s], rb = (s & 1) * BUF;
         bf16_t* dso = dsw + (size_t)(2 * s) * nqt * 1024;
         if (n > 0)
-          q_tile<D, kHoistDqPers, false, false, false, true>(smem, rb, rb + 2 * Sh<D>::TILEB, min(n, 32), c2, st,
-                                                             NoMid{}, dso);
+          q_tile<D, kHoistDqPers, false, false, false, true>(smem, rb, rb + 2 * Sh<D>::TILEB, 32, c2, st, NoMid{},
+                                                             dso);
         if (n > 32)
-          q_tile<D, kHoistDqPers, false, false, false, true>(smem, rb + Sh<D>::TILEB, rb + 3 * Sh<D>::TILEB, n - 32,
+          q_tile<D, kHoistDqPers, false, false, false, true>(smem, rb + Sh<D>::TILEB, rb + 3 * Sh<D>::TILEB, 32,
                                                              c2, st, NoMid{}, dso + (size_t)nqt * 1024);
       }
-      if (s + 1 < g.S) slot_store<D>(pf, smem + ((s + 1) & 1) * BUF);
+      if (s + 1 < g.S) slot_store<D>(pf, smem + ((s + 1) & 1) * BUF, plen_s[s + 1]);
       __syncthreads();
     }
   }
@@ -1152,14 +1158,14 @@ hipError_t set_lds(K kernel, size_t bytes) {
 template <int D>
 hipError_t launch_d(const BwdArgs& base, hipStream_t s, hipStream_t s2, hipEvent_t dsready) {
   const Geo& g = base.g;
-  const size_t shm_dq = 2 * 4 * Sh<D>::TILEB;                 // persistent: 2 x (K,K,V,V)
+  const size_t shm_dq = 2 * 4 * Sh<D>::TILEB + g.S * 4;      // persistent: 2 x (K,K,V,V), slot lengths
   const size_t tabb = (size_t)kLocBlocks * g.K * 64 * 4;
   const bool tab = tabb <= (size_t)kRowTabMax;
   const size_t shm_dql = tab ? tabb + kLocBlocks * g.K * 4 : 0;  // local: row tables (step buffers are static)
   const size_t shm_kvl = kvl_lds(g.nq);
   static PerDeviceOnce attr;
   hipError_t e = attr.run([] {
-    hipError_t r = set_lds(dq_pers_kernel<D>, 2 * 4 * Sh<D>::TILEB);
+    hipError_t r = set_lds(dq_pers_kernel<D>, 2 * 4 * Sh<D>::TILEB + 2048 * 4);
     if (r == hipSuccess) r = set_lds(dq_local_kernel<D, true>, kRowTabMax + 4096);
     if (r == hipSuccess) r = set_lds(dkv_local_kernel<D>, kvl_lds(2048));
     return r;
