@@ -183,7 +183,10 @@ pbsa_status pbsa_fwd_mass(const pbsa_config* cfg, const void* q, const void* k_p
  * pbsa_fwd) and dout.  Writes float32 dq, dk_pers, dv_pers, dk_local,
  * dv_local, overwriting them entirely (rows that receive no gradient are set
  * to zero).  Deterministic: no floating-point atomics.  ws of at least
- * plan.ws_bwd bytes.  The dk / dv kernels run on the library's second stream
+ * plan.ws_bwd bytes: for bf16 inputs it holds dS of every (query, persistent
+ * key) pair as bf16 (about 2*B*H*2S*ceil(Nq/32)*1024 bytes: 1.2 GB at the
+ * 30x52 decode shape), which the dq kernel writes and the dk kernel reads
+ * instead of recomputing it.  The dk / dv kernels run on the library's second stream
  * of the device (see Streams above); calls on one device are serialised
  * while they are enqueued. */
 pbsa_status pbsa_bwd(const pbsa_config* cfg, const void* q, const void* k_pers, const void* v_pers,
