@@ -2,6 +2,7 @@
 // carving and kernel launches.  No entry point allocates, frees or
 // synchronizes; all work goes onto the caller's stream.
 #include <math.h>
+#include <stdlib.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -111,6 +112,17 @@ pbsa_status make_plan(const pbsa_config* c, Plan* p) {
     return fail(PBSA_ERR_INVALID_ARG, "sink_slots (%d) must be in [0, min(%d slots, %d blocks per chunk)]",
                 c->sink_slots, g.S, g.nq);
   g.Z = c->sink_slots;
+  // The backward stores dS of every (query, persistent key) pair in its
+  // workspace when that takes at most PBSA_BWD_DS_MAX_MB megabytes (default
+  // 8192); above it the dK pass recomputes dS instead (slower, no such
+  // workspace).
+  {
+    double cap_mb = 8192.0;
+    if (const char* env = getenv("PBSA_BWD_DS_MAX_MB")) cap_mb = atof(env);
+    g.ds = 0;
+    const size_t need = bwd_ds_tile_bytes(g);
+    g.ds = need > 0 && (double)need <= cap_mb * 1048576.0 ? 1 : 0;
+  }
 
   pbsa_plan_info& in = p->info;
   memset(&in, 0, sizeof in);

@@ -18,11 +18,13 @@
 //   dq_local  the same over each query block's selected local blocks (8 waves
 //             = 4 query blocks x 2 query tiles), rows gathered straight into
 //             LDS; adds into dq.
-//   dv_pers   key-outer: 8 waves x 32 keys (four slots) stream every query of
-//             the head through LDS in 32-row tiles; S = Q K^T puts one key per
-//             lane, dV += P^T dO reads dO transposed from LDS.
-//   dk_ds     key-outer like dv_pers: dK += dS^T Q from the stored dS tiles,
-//             one product where recomputing dS would take three.
+//   dkv_pers  key-outer: 8 waves x 32 keys (four slots) stream every query of
+//             the head through LDS in 32-row tiles; S = Q K^T (and dP =
+//             dO V^T) put one key per lane, dV += P^T dO (or dK += dS^T Q)
+//             reads dO (or Q) transposed from LDS.  The dV pass always; the
+//             dK pass only where the dS tiles would not fit their cap.
+//   dk_ds     key-outer like dkv_pers: dK += dS^T Q from the stored dS tiles,
+//             one product where recomputing dS takes three.
 //   dkv_local key-outer over a local block (4 waves: dV and dK for 2 x 32
 //             keys), streaming only the query blocks that selected it (a
 //             key-block -> query-block index built from the top-k lists),
@@ -406,8 +408,9 @@ __device__ __forceinline__ void slot_store(const SlotPf<D>& pf, char* buf, int n
   }
 }
 
-template <int D>
+template <int D, bool DS>
 __global__ __launch_bounds__(kDqThreads, 1) void dq_pers_kernel(BwdArgs a) {
+  // DS: also store every dS tile for dk_ds
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int BUF = 4 * Sh<D>::TILEB;
   const Geo& g = a.g;
@@ -443,11 +446,11 @@ __global__ __launch_bounds__(kDqThreads, 1) void dq_pers_kernel(BwdArgs a) {
         const int n = plen_s[s], rb = (s & 1) * BUF;
         bf16_t* dso = dsw + (size_t)(2 * s) * nqt * 1024;
         if (n > 0)
-          q_tile<D, kHoistDqPers, false, false, false, true>(smem, rb, rb + 2 * Sh<D>::TILEB, 32, c2, st, NoMid{},
-                                                             dso);
+          q_tile<D, kHoistDqPers, false, false, false, DS>(smem, rb, rb + 2 * Sh<D>::TILEB, 32, c2, st, NoMid{},
+                                                           dso);
         if (n > 32)
-          q_tile<D, kHoistDqPers, false, false, false, true>(smem, rb + Sh<D>::TILEB, rb + 3 * Sh<D>::TILEB, 32,
-                                                             c2, st, NoMid{}, dso + (size_t)nqt * 1024);
+          q_tile<D, kHoistDqPers, false, false, false, DS>(smem, rb + Sh<D>::TILEB, rb + 3 * Sh<D>::TILEB, 32,
+                                                           c2, st, NoMid{}, dso + (size_t)nqt * 1024);
       }
       if (s + 1 < g.S) slot_store<D>(pf, smem + ((s + 1) & 1) * BUF, plen_s[s + 1]);
       __syncthreads();
@@ -657,25 +660,30 @@ __device__ __forceinline__ void k_init(const bf16_t* krow, const bf16_t* vrow, b
 
 // One 32-query tile in LDS: Q tile tq, dO tile td, per-row lse*log2e and D.
 // Rows that do not exist carry lse*log2e = +inf (their probability is 0).
-// The transposed B operands are read ahead of the VALU work: after the
-// first products, or with EARLY first of all, before mid(); XADDR: natural
-// reads through per-read XOR offsets from the array arr holding the tiles
-// (see q_tile); ASMTR: transposed reads in one asm block (rd_tr_all).
+// The transposed B operands are read ahead of the VALU work (HOIST): after
+// the first products, or with EARLY first of all, before mid().  XADDR:
+// natural reads through per-read XOR offsets from the array arr holding the
+// tiles (see q_tile).  ASMTR: transposed reads in asm blocks that wait for
+// their own reads: all at once (rd_tr_all) in a dV role, per column tile
+// after the softmax (rd_tr_dt, fewer live registers) in a dK role, which
+// holds V as well.
 template <int D, bool DV, bool EARLY = false, bool XADDR = false, bool ASMTR = false, typename Mid = NoMid>
 __device__ __forceinline__ void k_tile(const char* tq, const char* td, const float* lse2, const float* dl, float c2,
                                        KState<D, DV>& st, Mid mid = Mid{}, const char* arr = nullptr) {
+  constexpr bool HOIST = !ASMTR || DV;
+  static_assert(HOIST || !EARLY, "EARLY reads are hoisted reads");
   const int lane = threadIdx.x & 63, h = lane >> 5, l32 = lane & 31;
   const char* tb = DV ? td : tq;  // dV += P^T dO ; dK += dS^T Q
-  bf16x8_t bt[Sh<D>::DT][2];      // transposed B operands
+  bf16x8_t bt[HOIST ? Sh<D>::DT : 1][2];  // transposed B operands
   auto read_bt = [&]() {
-    if constexpr (ASMTR) {
+    if constexpr (ASMTR && HOIST) {
       rd_tr_all<D>(tb, bt);
       return;
     }
 #pragma unroll
     for (int dt = 0; dt < Sh<D>::DT; ++dt) {
-      bt[dt][0] = rd_tr<D>(tb, 0, dt);
-      bt[dt][1] = rd_tr<D>(tb, 1, dt);
+      bt[HOIST ? dt : 0][0] = rd_tr<D>(tb, 0, dt);
+      bt[HOIST ? dt : 0][1] = rd_tr<D>(tb, 1, dt);
     }
   };
   if (EARLY) {
@@ -709,7 +717,7 @@ __device__ __forceinline__ void k_tile(const char* tq, const char* td, const flo
       if (!DV) dp = mfma(rd_nat<D>(td, l32, 2 * ks + h), st.vf[DV ? 0 : ks], dp);
     }
   }
-  if (!EARLY) read_bt();
+  if constexpr (HOIST && !EARLY) read_bt();
   f32x16_t x;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -725,8 +733,9 @@ __device__ __forceinline__ void k_tile(const char* tq, const char* td, const flo
   const bf16x8_t x0 = pack8(x, 0), x1 = pack8(x, 1);
 #pragma unroll
   for (int dt = 0; dt < Sh<D>::DT; ++dt) {
-    st.acc[dt] = mfma(x0, bt[dt][0], st.acc[dt]);
-    st.acc[dt] = mfma(x1, bt[dt][1], st.acc[dt]);
+    if constexpr (!HOIST) rd_tr_dt<D>(tb, dt, bt[0]);
+    st.acc[dt] = mfma(x0, bt[HOIST ? dt : 0][0], st.acc[dt]);
+    st.acc[dt] = mfma(x1, bt[HOIST ? dt : 0][1], st.acc[dt]);
   }
 }
 
@@ -748,7 +757,7 @@ __device__ __forceinline__ void k_write(const KState<D, DV>& st, int n, float sc
   }
 }
 
-constexpr int kKvWaves = 8;       // dv_pers, dk_ds: 8 waves = 4 slots x 2 key tiles
+constexpr int kKvWaves = 8;       // dkv_pers, dk_ds: 8 waves = 4 slots x 2 key tiles
 constexpr int kKvThreads = 64 * kKvWaves;
 constexpr int kKvSlots = kKvWaves / 2;
 
@@ -786,10 +795,10 @@ template <int D> struct PersDma {
   }
 };
 
-// dV of the persistent slots (their dK comes from dk_ds).
-template <int D>
-__global__ __launch_bounds__(kKvThreads, 1) void dv_pers_kernel(BwdArgs a) {
-  constexpr bool DV = true;
+// dV (DV) or dK of the persistent slots; dK comes from dk_ds where the dS
+// tiles are stored.
+template <int D, bool DV>
+__global__ __launch_bounds__(kKvThreads, 1) void dkv_pers_kernel(BwdArgs a) {
   using Dm = PersDma<D>;
   // three step buffers, separate arrays so that the compiler can tell the
   // loads into one from the reads of another
@@ -839,8 +848,8 @@ __global__ __launch_bounds__(kKvThreads, 1) void dv_pers_kernel(BwdArgs a) {
   }
   __builtin_amdgcn_s_waitcnt(0xF70);  // the last loads land before the workgroup can end
   if (!has_slot || 32 * kh >= g.C) return;
-  float* ob = a.dvp + sbase;
-  k_write<D, DV>(st, nk, 1.0f, [&](int r, float*& dst) {
+  float* ob = (DV ? a.dvp : a.dkp) + sbase;
+  k_write<D, DV>(st, nk, DV ? 1.0f : -g.scale, [&](int r, float*& dst) {
     const int row = 32 * kh + r;
     if (row >= g.C) return false;
     dst = ob + (size_t)row * D;
@@ -850,7 +859,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void dv_pers_kernel(BwdArgs a) {
 
 // dK of the persistent slots from the dS tiles that dq_pers stored:
 // dK = scale dS^T Q, one product instead of the three of a recomputing pass.
-// Key-outer like dv_pers (8 waves = 4 slots x 2 key tiles, 32 keys per
+// Key-outer like dkv_pers (8 waves = 4 slots x 2 key tiles, 32 keys per
 // wave): every query tile of the head streams through LDS with each wave's
 // dS tile for it, loaded two steps ahead into three buffers; both operands
 // are read transposed (dS^T with lane = key, Q with lane = column), so their
@@ -1151,10 +1160,11 @@ hipError_t set_lds(K kernel, size_t bytes) {
 }
 
 // The MFMA kernels: dK/dV on the side stream s2, dQ on the caller's stream s
-// (both already past the preparation).  dq_pers writes the persistent dS
-// tiles that dk_ds reads: the side stream waits for it (event dsready,
-// recorded before the wait is issued) after its dK/dV of the local blocks and
-// its dV of the slots.
+// (both already past the preparation).  With g.ds, dq_pers writes the
+// persistent dS tiles that dk_ds reads: the side stream waits for it (event
+// dsready, recorded before the wait is issued) after its dK/dV of the local
+// blocks and its dV of the slots.  Without, the side stream's recomputing dK
+// pass needs nothing from the caller's stream.
 template <int D>
 hipError_t launch_d(const BwdArgs& base, hipStream_t s, hipStream_t s2, hipEvent_t dsready) {
   const Geo& g = base.g;
@@ -1165,14 +1175,17 @@ hipError_t launch_d(const BwdArgs& base, hipStream_t s, hipStream_t s2, hipEvent
   const size_t shm_kvl = kvl_lds(g.nq);
   static PerDeviceOnce attr;
   hipError_t e = attr.run([] {
-    hipError_t r = set_lds(dq_pers_kernel<D>, 2 * 4 * Sh<D>::TILEB + 2048 * 4);
+    hipError_t r = set_lds(dq_pers_kernel<D, true>, 2 * 4 * Sh<D>::TILEB + 2048 * 4);
+    if (r == hipSuccess) r = set_lds(dq_pers_kernel<D, false>, 2 * 4 * Sh<D>::TILEB + 2048 * 4);
     if (r == hipSuccess) r = set_lds(dq_local_kernel<D, true>, kRowTabMax + 4096);
     if (r == hipSuccess) r = set_lds(dkv_local_kernel<D>, kvl_lds(2048));
     return r;
   });
   if (e != hipSuccess) return e;
   BwdArgs a = base;
-  // side stream: dK, dV of the local blocks, then dV of the persistent slots
+  const bool ds = g.ds && g.S > 0;
+  // side stream: dK, dV of the local blocks, then dV (and without dS tiles,
+  // dK) of the persistent slots
   int total = g.B * g.H * g.nl;
   dkv_local_kernel<D><<<((total + 7) / 8) * 8, kKvlThreads, shm_kvl, s2>>>(a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -1180,15 +1193,22 @@ hipError_t launch_d(const BwdArgs& base, hipStream_t s, hipStream_t s2, hipEvent
   if (g.S > 0) {
     a.ntiles = kv_tiles;
     total = g.B * g.H * a.ntiles;
-    dv_pers_kernel<D><<<((total + 7) / 8) * 8, kKvThreads, 0, s2>>>(a);
+    dkv_pers_kernel<D, true><<<((total + 7) / 8) * 8, kKvThreads, 0, s2>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (!ds) {
+      dkv_pers_kernel<D, false><<<((total + 7) / 8) * 8, kKvThreads, 0, s2>>>(a);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
   }
-  // caller's stream: dq of the persistent slots (writes dq and the dS tiles)
+  // caller's stream: dq of the persistent slots (writes dq, and the dS tiles)
   a.ntiles = (g.ct + kDqRows - 1) / kDqRows;
   total = g.B * g.H * a.ntiles;
-  dq_pers_kernel<D><<<((total + 7) / 8) * 8, kDqThreads, shm_dq, s>>>(a);
+  if (ds)
+    dq_pers_kernel<D, true><<<((total + 7) / 8) * 8, kDqThreads, shm_dq, s>>>(a);
+  else
+    dq_pers_kernel<D, false><<<((total + 7) / 8) * 8, kDqThreads, shm_dq, s>>>(a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (g.S > 0) {
+  if (ds) {
     // side stream: dK of the persistent slots from the dS tiles
     if ((e = hipEventRecord(dsready, s)) != hipSuccess) return e;
     if ((e = hipStreamWaitEvent(s2, dsready, 0)) != hipSuccess) return e;
@@ -1211,10 +1231,12 @@ hipError_t launch_d(const BwdArgs& base, hipStream_t s, hipStream_t s2, hipEvent
 
 bool bwd_mfma_supported(const Geo& g) { return g.dtype == PBSA_BF16 && (g.D == 64 || g.D == 128) && g.C <= 64; }
 
-size_t bwd_ds_bytes(const Geo& g) {
+size_t bwd_ds_tile_bytes(const Geo& g) {
   if (!bwd_mfma_supported(g) || g.S <= 0) return 0;
   return (size_t)g.B * g.H * 2 * g.S * ((g.ct + 31) / 32) * 32 * 32 * 2;
 }
+
+size_t bwd_ds_bytes(const Geo& g) { return g.ds ? bwd_ds_tile_bytes(g) : 0; }
 
 // Fork onto the side stream first: the key-block index and its launch order
 // (read only by the key-outer local kernel) are built there while D, lse2

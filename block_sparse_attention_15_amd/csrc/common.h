@@ -29,6 +29,7 @@ struct Geo {
   float scale; // softmax scale
   int dtype;   // pbsa_dtype
   int Z;       // pinned sink slots (leading persistent slots)
+  int ds;      // the MFMA backward stores the persistent dS tiles (else its dK pass recomputes dS)
 };
 
 // Extent of chunk block j: base token offset inside the chunk, frames, rows,
@@ -138,8 +139,11 @@ struct GeoTab {
 };
 size_t geo_table_bytes(const Geo& g);
 // Bytes of the persistent dS tiles that the MFMA backward passes from its dQ
-// kernel to its dK kernel (0 where that path is not used).
+// kernel to its dK kernel, whether or not g.ds selects that path.
+size_t bwd_ds_tile_bytes(const Geo& g);
+// The same where g.ds is set, else 0.
 size_t bwd_ds_bytes(const Geo& g);
+bool bwd_mfma_supported(const Geo& g);
 hipError_t launch_geo_table(const Geo& g, void* ws, GeoTab* tab, hipStream_t s);
 
 struct WsScore {

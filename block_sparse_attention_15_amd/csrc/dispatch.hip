@@ -20,7 +20,6 @@ hipError_t launch_bwd_simple(const Geo& g, const void* q, const void* k_p, const
 
 size_t fwd_workspace(const Geo& g) { return fwd_mfma_supported(g) ? fwd_mfma_workspace(g) : 0; }
 
-bool bwd_mfma_supported(const Geo& g);
 hipError_t launch_bwd_mfma(const Geo& g, const void* q, const void* k_p, const void* v_p, const int32_t* plen,
                            const void* k_l, const void* v_l, const int32_t* topk, const void* o, const float* lse,
                            const void* dout, float* dq, float* dk_p, float* dv_p, float* dk_l, float* dv_l,

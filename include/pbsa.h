@@ -186,7 +186,11 @@ pbsa_status pbsa_fwd_mass(const pbsa_config* cfg, const void* q, const void* k_p
  * plan.ws_bwd bytes: for bf16 inputs it holds dS of every (query, persistent
  * key) pair as bf16 (about 2*B*H*2S*ceil(Nq/32)*1024 bytes: 1.2 GB at the
  * 30x52 decode shape), which the dq kernel writes and the dk kernel reads
- * instead of recomputing it.  The dk / dv kernels run on the library's second stream
+ * instead of recomputing it, when that size is at most PBSA_BWD_DS_MAX_MB
+ * megabytes (environment, read by every call; default 8192); above it the dk
+ * kernel recomputes dS and the workspace is smaller.  Plan and call with the
+ * same setting (a call that finds ws_bytes below its plan's ws_bwd fails with
+ * PBSA_ERR_WORKSPACE).  The dk / dv kernels run on the library's second stream
  * of the device (see Streams above); calls on one device are serialised
  * while they are enqueued. */
 pbsa_status pbsa_bwd(const pbsa_config* cfg, const void* q, const void* k_pers, const void* v_pers,

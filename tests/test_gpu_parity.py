@@ -14,6 +14,7 @@ import torch
 
 import oracle
 import synth
+import block_sparse_attention_15_amd as pb
 from pbsa_harness import (GpuStep, compare_topk, compare_update_decisions, decisions_from_state, dev, host,
                           rel_l2)
 
@@ -158,6 +159,73 @@ def test_fwd_bwd_empty_slots(name):
         assert err <= t["g_abs"] and r <= t["g_rel"], k
     for k in ("dk_p", "dv_p"):
         assert not host(gr[k])[..., empty, :, :].any(), f"{k}: empty slots must get zero gradient"
+
+
+@pytest.mark.parametrize("name", ["ragged_bf16", "ragged_bf16_d64_b2", "block344_bf16", "tiny_bf16"])
+def test_bwd_recompute_path(name, monkeypatch):
+    """With the persistent dS tiles capped to 0 MB (PBSA_BWD_DS_MAX_MB) the
+    backward's dK pass recomputes dS instead of reading it from the
+    workspace: the same gradients from a smaller workspace."""
+    cfg = SMALL[name]
+    stored = pb.pbsa_plan(cfg).ws_bwd
+    monkeypatch.setenv("PBSA_BWD_DS_MAX_MB", "0")
+    assert pb.pbsa_plan(cfg).ws_bwd < stored
+    x = synth.make_step_inputs(cfg)
+    x["persist_len"][..., 1] = 0
+    x["persist_len"][..., 2] = min(x["k_p"].shape[-2], 40)
+    g, _, sel = oracle_select(cfg, x, 0)
+    dout = synth.make_dout(cfg, seed=cfg["seed"] + 300)
+    ref = oracle.attend_bwd(x["q"], x["k_p"], x["v_p"], x["persist_len"], x["k_l"], x["v_l"], sel["topk_idx"],
+                            dout, g)
+    st = GpuStep(cfg, x)
+    idx = dev(sel["topk_idx"])
+    st.fwd(idx)
+    gr = st.bwd(dev(dout, st.p.torch_dtype), idx)
+    torch.cuda.synchronize()
+    t = tol(cfg)
+    for k in ("dq", "dk_p", "dv_p", "dk_l", "dv_l"):
+        a = host(gr[k])
+        assert np.isfinite(a).all(), k
+        err = np.abs(a - ref[k]).max()
+        r = rel_l2(a, ref[k])
+        print(f"{name} (recomputed dS): {k} max-abs {err:.3g} rel-L2 {r:.3g}")
+        assert err <= t["g_abs"] and r <= t["g_rel"], k
+
+
+def test_bwd_decode_c1_sampled():
+    """The decode shape (12 heads, 168 slots, 4680 queries; dS tiles stored):
+    dQ against the oracle on sampled query blocks, dK and dV over every key
+    by identities that hold at any size (sum of dK = 0, sum of dV = sum of
+    dO)."""
+    cfg = synth.workload("decode_c1")
+    assert pb.pbsa_plan(cfg).ws_bwd > 10 ** 9, "the decode shape should take the stored-dS path"
+    x = synth.make_step_inputs(cfg)
+    g, _, sel = oracle_select(cfg, x, 0)
+    dout = synth.make_dout(cfg, seed=3)
+    st = GpuStep(cfg, x)
+    idx = dev(sel["topk_idx"])
+    st.fwd(idx)
+    gr = st.bwd(dev(dout, torch.bfloat16), idx)
+    torch.cuda.synchronize()
+    blocks = [0, 41, g.n_qblk - 1]
+    ref = oracle.attend_bwd(x["q"], x["k_p"], x["v_p"], x["persist_len"], x["k_l"], x["v_l"], sel["topk_idx"],
+                            dout, g, qblocks=blocks)
+    rows = np.concatenate([g.block_tok[i] for i in blocks])
+    dq = host(gr["dq"])
+    assert np.isfinite(dq).all()
+    err = np.abs(dq[:, :, rows] - ref["dq"][:, :, rows]).max()
+    r = rel_l2(dq[:, :, rows], ref["dq"][:, :, rows])
+    print(f"decode_c1: dq on blocks {blocks}: max-abs {err:.3g} rel-L2 {r:.3g}")
+    assert err <= 1e-2 and r <= 2e-2
+    for b in range(g.B):
+        for h in range(g.H):
+            dk = np.concatenate([host(gr["dk_p"])[b, h].reshape(-1, g.D), host(gr["dk_l"])[b, h].reshape(-1, g.D)])
+            dv = np.concatenate([host(gr["dv_p"])[b, h].reshape(-1, g.D), host(gr["dv_l"])[b, h].reshape(-1, g.D)])
+            dk, dv = dk.astype(np.float64), dv.astype(np.float64)
+            assert np.isfinite(dk).all() and np.isfinite(dv).all()
+            assert np.abs(dk.sum(0)).max() <= 1e-3 * np.abs(dk).sum(0).max(), (b, h)
+            want = dout[b, h].astype(np.float64).reshape(-1, g.D).sum(0)
+            assert np.abs(dv.sum(0) - want).max() <= 1e-2 * np.abs(want).max() + 1e-2, (b, h)
 
 
 @pytest.mark.parametrize("name", ["ragged_bf16", "block344_bf16"])
