@@ -427,7 +427,7 @@ __global__ __launch_bounds__(kDqThreads, 1) void dq_pers_kernel(BwdArgs a) {
   q_init<D>(a, bh, ok ? r : 0, ok, st);
   const float c2 = g.scale * kLog2e;
   const int nqt = (g.ct + 31) / 32;  // query tiles of the head; this wave's is qt * kDqWaves + wave
-  bf16_t* dsw = a.dsb + ((size_t)bh * 2 * g.S * nqt + qt * kDqWaves + wave) * 1024;
+  bf16_t* dsw = DS ? a.dsb + ((size_t)bh * 2 * g.S * nqt + qt * kDqWaves + wave) * 1024 : nullptr;
   // Slot lengths go to LDS before the first dS store: a length read from
   // global memory later would wait (vmcnt) for every store in flight.
   int* plen_s = reinterpret_cast<int*>(smem + 2 * BUF);
@@ -444,13 +444,13 @@ __global__ __launch_bounds__(kDqThreads, 1) void dq_pers_kernel(BwdArgs a) {
         // slot rows at or past n are staged as zeros: no key mask needed
         // (see q_tile); dS goes to the tiles of key tiles 2s and 2s+1
         const int n = plen_s[s], rb = (s & 1) * BUF;
-        bf16_t* dso = dsw + (size_t)(2 * s) * nqt * 1024;
+        bf16_t* dso = DS ? dsw + (size_t)(2 * s) * nqt * 1024 : nullptr;
         if (n > 0)
           q_tile<D, kHoistDqPers, false, false, false, DS>(smem, rb, rb + 2 * Sh<D>::TILEB, 32, c2, st, NoMid{},
                                                            dso);
         if (n > 32)
           q_tile<D, kHoistDqPers, false, false, false, DS>(smem, rb + Sh<D>::TILEB, rb + 3 * Sh<D>::TILEB, 32,
-                                                           c2, st, NoMid{}, dso + (size_t)nqt * 1024);
+                                                           c2, st, NoMid{}, DS ? dso + (size_t)nqt * 1024 : nullptr);
       }
       if (s + 1 < g.S) slot_store<D>(pf, smem + ((s + 1) & 1) * BUF, plen_s[s + 1]);
       __syncthreads();
@@ -863,9 +863,11 @@ __global__ __launch_bounds__(kKvThreads, 1) void dkv_pers_kernel(BwdArgs a) {
 // wave): every query tile of the head streams through LDS with each wave's
 // dS tile for it, loaded two steps ahead into three buffers; both operands
 // are read transposed (dS^T with lane = key, Q with lane = column), so their
-// query orders match.  Every wave issues the same loads in every step
-// (waves whose key tile holds no keys load tile 0's and skip the product;
-// Q units beyond the tile's are loaded twice by two waves, the same bytes).
+// query orders match.  Every wave issues the same loads in every step:
+// waves past the last slot load key tile 0's dS tiles, and waves whose key
+// tile holds no keys load tiles that nothing wrote; both skip the product.
+// Where a Q tile has fewer 1 KB units than there are waves (head_dim 64),
+// two waves load each unit, the same bytes to the same place.
 template <int D> struct DsDma {
   static constexpr int RPK = 1024 / Sh<D>::ROWB;   // rows per 1 KB unit
   static constexpr int UPT = Sh<D>::TILEB / 1024;  // units per Q tile
