@@ -17,6 +17,7 @@ from .api import (  # noqa: F401
     pbsa_bwd,
     pbsa_persist_update,
     pbsa_ring_append,
+    pbsa_device_status,
     shapes,
     workspace,
 )

@@ -15,6 +15,8 @@ PBSA_ERR_WORKSPACE = -4
 PBSA_ERR_HIP = -5
 PBSA_BF16 = 0
 PBSA_FP32 = 1
+PBSA_DEVICE_BAD_RING_HEAD = 1
+PBSA_DEVICE_BAD_STEP_COUNTER = 2
 
 STATUS_NAMES = {0: "PBSA_OK", -1: "PBSA_ERR_INVALID_ARG", -2: "PBSA_ERR_UNSUPPORTED",
                 -3: "PBSA_ERR_ALIGNMENT", -4: "PBSA_ERR_WORKSPACE", -5: "PBSA_ERR_HIP"}
@@ -57,6 +59,7 @@ SIGNATURES = {
     "pbsa_bwd": [_CFG] + [_P] * 15 + [_P, ctypes.c_size_t, _P],
     "pbsa_persist_update": [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "pbsa_ring_append": [_CFG, _P, _P, _P, _P, _P, _P],
+    "pbsa_device_status": [_P, ctypes.c_int32, _P],
 }
 
 _lib = None

@@ -224,3 +224,10 @@ def pbsa_ring_append(p: Plan, k_new, v_new, ring_head, k_local, v_local, stream=
     _call("pbsa_ring_append", ctypes.byref(p.cfg), _ptr(k_new, s["q"], dt, "k_new"), _ptr(v_new, s["q"], dt, "v_new"),
           _ptr(ring_head, s["ring_head"], torch.int32, "ring_head"), _ptr(k_local, s["k_local"], dt, "k_local"),
           _ptr(v_local, s["k_local"], dt, "v_local"), _stream(stream))
+
+
+def pbsa_device_status(out, clear: bool = True, stream=None):
+    """Copy the device's sticky status bits into ``out`` (int32 device tensor
+    of shape (1,)), resetting them when ``clear``; see PBSA_DEVICE_* in _lib."""
+    _call("pbsa_device_status", _ptr(out, (1,), torch.int32, "out"), ctypes.c_int32(1 if clear else 0),
+          _stream(stream))

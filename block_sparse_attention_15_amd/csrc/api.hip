@@ -7,12 +7,40 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "common.h"
 
 namespace pbsa {
+
+// Sticky error bits raised by the kernels of this device (one copy per
+// device; pbsa_device_status reads and clears it).
+__device__ uint32_t g_device_status;
+
+hipError_t device_status_word(uint32_t** out) {
+  static std::mutex mu;
+  static uint32_t* addr[PerDeviceOnce::kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= PerDeviceOnce::kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(g_device_status))) != hipSuccess) return e;
+    addr[dev] = (uint32_t*)p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
+
 namespace {
+
+__global__ void device_status_kernel(uint32_t* word, uint32_t* out, int clear) {
+  *out = *word;
+  if (clear) *word = 0u;
+}
 
 thread_local std::string g_err;
 
@@ -230,9 +258,12 @@ pbsa_status pbsa_score_select(const pbsa_config* cfg, const void* q, const void*
   WsScore w;
   w.qbar = (float*)ws;
   w.prow = (float*)((char*)ws + align256(BH * p.g.nq * p.g.D * 4));
-  return hip_status(launch_score_select(p.g, q, k_local, ring_head, persist_kbar, persist_len, topk_idx, mass,
-                                        kbar_local, w, (hipStream_t)stream),
-                    "pbsa_score_select");
+  uint32_t* status = nullptr;
+  hipError_t e = device_status_word(&status);
+  if (e == hipSuccess)
+    e = launch_score_select(p.g, q, k_local, ring_head, persist_kbar, persist_len, topk_idx, mass, kbar_local, w,
+                            status, (hipStream_t)stream);
+  return hip_status(e, "pbsa_score_select");
 }
 
 pbsa_status pbsa_fwd(const pbsa_config* cfg, const void* q, const void* k_pers, const void* v_pers,
@@ -367,10 +398,13 @@ pbsa_status pbsa_persist_update(const pbsa_config* cfg, const float* mass, const
     REQUIRE_ALIGNED(persist_kbar);
   }
   if ((st = check_ws(ws, ws_bytes, p.info.ws_persist_update)) != PBSA_OK) return st;
-  return hip_status(launch_persist_update(p.g, mass, k_local, v_local, kbar_local, ring_head, step_counter, k_pers,
-                                          v_pers, persist_len, persist_src, persist_kbar, n_replaced,
-                                          (int32_t*)ws, (hipStream_t)stream),
-                    "pbsa_persist_update");
+  uint32_t* status = nullptr;
+  hipError_t e = device_status_word(&status);
+  if (e == hipSuccess)
+    e = launch_persist_update(p.g, mass, k_local, v_local, kbar_local, ring_head, step_counter, k_pers, v_pers,
+                              persist_len, persist_src, persist_kbar, n_replaced, (int32_t*)ws, status,
+                              (hipStream_t)stream);
+  return hip_status(e, "pbsa_persist_update");
 }
 
 pbsa_status pbsa_ring_append(const pbsa_config* cfg, const void* k_new, const void* v_new,
@@ -383,8 +417,21 @@ pbsa_status pbsa_ring_append(const pbsa_config* cfg, const void* k_new, const vo
   REQUIRE_PTR(ring_head);
   REQUIRE_ALIGNED(k_local);
   REQUIRE_ALIGNED(v_local);
-  return hip_status(launch_ring_append(p.g, k_new, v_new, ring_head, k_local, v_local, (hipStream_t)stream),
-                    "pbsa_ring_append");
+  uint32_t* status = nullptr;
+  hipError_t e = device_status_word(&status);
+  if (e == hipSuccess) e = launch_ring_append(p.g, k_new, v_new, ring_head, k_local, v_local, status, (hipStream_t)stream);
+  return hip_status(e, "pbsa_ring_append");
+}
+
+pbsa_status pbsa_device_status(uint32_t* out, int32_t clear, void* stream) {
+  REQUIRE_PTR(out);
+  uint32_t* word = nullptr;
+  hipError_t e = device_status_word(&word);
+  if (e == hipSuccess) {
+    device_status_kernel<<<1, 1, 0, (hipStream_t)stream>>>(word, out, clear);
+    e = hipGetLastError();
+  }
+  return hip_status(e, "pbsa_device_status");
 }
 
 const char* pbsa_last_error(void) { return g_err.c_str(); }

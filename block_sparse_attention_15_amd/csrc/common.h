@@ -60,6 +60,41 @@ __host__ __device__ inline int block_token(const Geo& g, const BlockExt& e, int 
   return (e.f0 + f) * g.ft + (e.r0 + r) * g.fw + e.c0 + c;
 }
 
+// ---------------------------------------------------------------------------
+// Device-resident ring state
+// ---------------------------------------------------------------------------
+// Sticky error bits of the library's device status word (pbsa_device_status).
+constexpr uint32_t kStatusRingHead = 1u;     // a ring head outside [0, R) was read
+constexpr uint32_t kStatusStepCounter = 2u;  // a step counter outside [0, 2^31 / blocks per chunk) was read
+
+// A stored ring head reduced into [0, R): the non-negative remainder, so that
+// every chunk slot derived from it is in bounds whatever the stored value.
+__host__ __device__ inline int ring_wrap(int v, int R) {
+  const int r = v % R;
+  return r < 0 ? r + R : r;
+}
+
+// The ring head read on the device, reduced into [0, R); a stored value
+// outside [0, R) raises kStatusRingHead in *status.
+__device__ inline int read_ring_head(const int32_t* ring_head, int R, uint32_t* status) {
+  const int v = *ring_head;
+  if ((unsigned)v >= (unsigned)R) atomicOr(status, kStatusRingHead);
+  return ring_wrap(v, R);
+}
+
+// The step counter read on the device; a value for which step*nq would leave
+// the int32 source ids raises kStatusStepCounter (the ids it produces are
+// then not unique, nothing is out of bounds).
+__device__ inline int read_step(const int32_t* step_counter, int nq, uint32_t* status) {
+  const int v = *step_counter;
+  if (v < 0 || v > INT32_MAX / nq - 1) atomicOr(status, kStatusStepCounter);
+  return v;
+}
+
+// Address of the device status word on the current device (looked up once
+// per device).
+hipError_t device_status_word(uint32_t** out);
+
 // Wait until at most N of this wave's global loads are in flight and all of
 // its LDS reads have returned, then the workgroup barrier.  Unlike
 // __syncthreads this leaves the newest LDS-bound loads running.  The wait is
@@ -153,7 +188,7 @@ struct WsScore {
 hipError_t launch_pool_slots(const Geo& g, const void* k_p, const int32_t* plen, float* kbar, hipStream_t s);
 hipError_t launch_score_select(const Geo& g, const void* q, const void* k_l, const int32_t* ring_head,
                                const float* kbar_p, const int32_t* plen, int32_t* topk, float* mass,
-                               float* kbar_l, WsScore ws, hipStream_t s);
+                               float* kbar_l, WsScore ws, uint32_t* status, hipStream_t s);
 // blse_p / blse_l: NULL, or [B,H,S,ct] / [B,H,K,ct] outputs of each query's
 // log-sum-exp over each persistent slot / each of its selected local blocks,
 // in base 2 (log2 of the sum of exp of the scaled scores; -inf where the slot
@@ -191,8 +226,8 @@ hipError_t launch_bwd(const Geo& g, const void* q, const void* k_p, const void* 
 hipError_t launch_persist_update(const Geo& g, const float* mass, const void* k_l, const void* v_l,
                                  const float* kbar_l, int32_t* ring_head, int32_t* step_counter, void* k_p,
                                  void* v_p, int32_t* plen, int32_t* psrc, float* pkbar, int32_t* n_rep,
-                                 int32_t* plan, hipStream_t s);
+                                 int32_t* plan, uint32_t* status, hipStream_t s);
 hipError_t launch_ring_append(const Geo& g, const void* k_new, const void* v_new, const int32_t* ring_head,
-                              void* k_l, void* v_l, hipStream_t s);
+                              void* k_l, void* v_l, uint32_t* status, hipStream_t s);
 
 }  // namespace pbsa

@@ -123,7 +123,8 @@ __global__ __launch_bounds__(kThreads) void score_topk_kernel(Geo g, const int32
                                                               const float* __restrict__ kbar_p,
                                                               const int32_t* __restrict__ plen,
                                                               int32_t* __restrict__ topk,
-                                                              float* __restrict__ prow) {
+                                                              float* __restrict__ prow,
+                                                              uint32_t* __restrict__ status) {
   extern __shared__ float smem[];
   const int W = g.nl + g.S;        // candidates: local blocks, then slots
   float* qb = smem;                // [4][D]
@@ -170,7 +171,7 @@ __global__ __launch_bounds__(kThreads) void score_topk_kernel(Geo g, const int32
   const bool has = w < kQPerWg && i < g.nq;
   const float* row = sc + w * W;
   unsigned long long* key = reinterpret_cast<unsigned long long*>(sel) + w * g.nl;
-  const int rh = *ring_head;
+  const int rh = read_ring_head(ring_head, g.R, status);
   // composite key: descending score, then ascending logical index (oldest
   // chunk first); rank(p) = #local blocks with a larger key
   if (has) {
@@ -296,7 +297,7 @@ hipError_t launch_pool_slots(const Geo& g, const void* k_p, const int32_t* plen,
 template <int D>
 hipError_t score_select_d(const Geo& g, const void* q, const void* k_l, const int32_t* ring_head,
                           const float* kbar_p, const int32_t* plen, int32_t* topk, float* mass, float* kbar_l,
-                          WsScore ws, hipStream_t s) {
+                          WsScore ws, uint32_t* status, hipStream_t s) {
   dim3 g1(g.nq + g.nl, g.H, g.B);
   if (g.dtype == PBSA_BF16)
     pool_blocks_kernel<D, bf16_t><<<g1, kThreads, 0, s>>>(g, (const bf16_t*)q, (const bf16_t*)k_l, ws.qbar, kbar_l);
@@ -318,11 +319,11 @@ hipError_t score_select_d(const Geo& g, const void* q, const void* k_l, const in
   const size_t shm = score_lds(g, qpw);
   const dim3 grid((g.nq + qpw - 1) / qpw, g.H, g.B);
   if (qpw == 4)
-    score_topk_kernel<D, 4><<<grid, kThreads, shm, s>>>(g, ring_head, ws.qbar, kbar_l, kbar_p, plen, topk, ws.prow);
+    score_topk_kernel<D, 4><<<grid, kThreads, shm, s>>>(g, ring_head, ws.qbar, kbar_l, kbar_p, plen, topk, ws.prow, status);
   else if (qpw == 2)
-    score_topk_kernel<D, 2><<<grid, kThreads, shm, s>>>(g, ring_head, ws.qbar, kbar_l, kbar_p, plen, topk, ws.prow);
+    score_topk_kernel<D, 2><<<grid, kThreads, shm, s>>>(g, ring_head, ws.qbar, kbar_l, kbar_p, plen, topk, ws.prow, status);
   else
-    score_topk_kernel<D, 1><<<grid, kThreads, shm, s>>>(g, ring_head, ws.qbar, kbar_l, kbar_p, plen, topk, ws.prow);
+    score_topk_kernel<D, 1><<<grid, kThreads, shm, s>>>(g, ring_head, ws.qbar, kbar_l, kbar_p, plen, topk, ws.prow, status);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   mass_kernel<<<dim3((g.S + g.nl + 63) / 64, g.H, g.B), kThreads, 0, s>>>(g, ws.prow, mass);
   return hipGetLastError();
@@ -330,9 +331,9 @@ hipError_t score_select_d(const Geo& g, const void* q, const void* k_l, const in
 
 hipError_t launch_score_select(const Geo& g, const void* q, const void* k_l, const int32_t* ring_head,
                                const float* kbar_p, const int32_t* plen, int32_t* topk, float* mass,
-                               float* kbar_l, WsScore ws, hipStream_t s) {
-  return g.D == 128 ? score_select_d<128>(g, q, k_l, ring_head, kbar_p, plen, topk, mass, kbar_l, ws, s)
-                    : score_select_d<64>(g, q, k_l, ring_head, kbar_p, plen, topk, mass, kbar_l, ws, s);
+                               float* kbar_l, WsScore ws, uint32_t* status, hipStream_t s) {
+  return g.D == 128 ? score_select_d<128>(g, q, k_l, ring_head, kbar_p, plen, topk, mass, kbar_l, ws, status, s)
+                    : score_select_d<64>(g, q, k_l, ring_head, kbar_p, plen, topk, mass, kbar_l, ws, status, s);
 }
 
 }  // namespace pbsa

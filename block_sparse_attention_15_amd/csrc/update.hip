@@ -34,7 +34,8 @@ __global__ __launch_bounds__(kThreads) void update_decide_kernel(Geo g, const fl
                                                                  int32_t* __restrict__ plen,
                                                                  int32_t* __restrict__ psrc,
                                                                  int32_t* __restrict__ n_rep,
-                                                                 int32_t* __restrict__ plan) {
+                                                                 int32_t* __restrict__ plan,
+                                                                 uint32_t* __restrict__ status) {
   extern __shared__ unsigned long long sk[];
   const int NC = g.S + g.nq;
   unsigned long long* key = sk;            // [NC], 0 for empty slots
@@ -42,8 +43,8 @@ __global__ __launch_bounds__(kThreads) void update_decide_kernel(Geo g, const fl
   int* alist = kept + NC;                  // [nq] admitted entrants in order
   const int h = blockIdx.x, b = blockIdx.y;
   const size_t bh = (size_t)b * g.H + h;
-  const int old = *ring_head;
-  const int step_id = *step_counter;
+  const int old = read_ring_head(ring_head, g.R, status);
+  const int step_id = read_step(step_counter, g.nq, status);
   const float* mrow = mass + bh * (g.S + g.nl);
   for (int c = threadIdx.x; c < NC; c += kThreads) {
     // sink slots, and evicted blocks reserved for an empty sink slot, are not candidates
@@ -134,7 +135,7 @@ __global__ __launch_bounds__(kThreads) void update_copy_kernel(Geo g, const int3
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const size_t bh = (size_t)b * g.H + h;
   if (s == 0 && h == 0 && b == 0 && threadIdx.x == 0) {
-    *ring_head = (*ring_head + 1) % g.R;
+    *ring_head = (ring_wrap(*ring_head, g.R) + 1) % g.R;
     *step_counter += 1;
   }
   const int p = plan[bh * g.S + s];
@@ -165,7 +166,7 @@ __global__ __launch_bounds__(kThreads) void update_copy_kernel(Geo g, const int3
 }
 
 __global__ void ring_advance_kernel(int32_t* ring_head, int32_t* step_counter, int R) {
-  *ring_head = (*ring_head + 1) % R;
+  *ring_head = (ring_wrap(*ring_head, R) + 1) % R;
   *step_counter += 1;
 }
 
@@ -174,9 +175,10 @@ template <typename T>
 __global__ __launch_bounds__(kThreads) void ring_append_kernel(Geo g, const T* __restrict__ kn,
                                                                const T* __restrict__ vn,
                                                                const int32_t* __restrict__ ring_head,
-                                                               T* __restrict__ kl, T* __restrict__ vl) {
+                                                               T* __restrict__ kl, T* __restrict__ vl,
+                                                               uint32_t* __restrict__ status) {
   constexpr int kVec = 16 / sizeof(T);
-  const int slot = (*ring_head + g.R - 1) % g.R;
+  const int slot = (read_ring_head(ring_head, g.R, status) + g.R - 1) % g.R;
   const size_t per_bh = (size_t)g.ct * g.D / kVec;   // 16-byte chunks per (b,h)
   const size_t total = per_bh * g.B * g.H;
   for (size_t c = (size_t)blockIdx.x * kThreads + threadIdx.x; c < total; c += (size_t)gridDim.x * kThreads) {
@@ -192,11 +194,11 @@ __global__ __launch_bounds__(kThreads) void ring_append_kernel(Geo g, const T* _
 hipError_t launch_persist_update(const Geo& g, const float* mass, const void* k_l, const void* v_l,
                                  const float* kbar_l, int32_t* ring_head, int32_t* step_counter, void* k_p,
                                  void* v_p, int32_t* plen, int32_t* psrc, float* pkbar, int32_t* n_rep,
-                                 int32_t* plan, hipStream_t s) {
+                                 int32_t* plan, uint32_t* status, hipStream_t s) {
   const int NC = g.S + g.nq;
   const size_t shm = (size_t)NC * 8 + (size_t)NC * 4 + (size_t)g.nq * 4;
   update_decide_kernel<<<dim3(g.H, g.B), kThreads, shm, s>>>(g, mass, ring_head, step_counter, plen, psrc, n_rep,
-                                                              plan);
+                                                              plan, status);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (g.S == 0) {
@@ -216,15 +218,15 @@ hipError_t launch_persist_update(const Geo& g, const float* mass, const void* k_
 }
 
 hipError_t launch_ring_append(const Geo& g, const void* k_new, const void* v_new, const int32_t* ring_head,
-                              void* k_l, void* v_l, hipStream_t s) {
+                              void* k_l, void* v_l, uint32_t* status, hipStream_t s) {
   const size_t chunks = (size_t)g.B * g.H * g.ct * g.D * (g.dtype == PBSA_BF16 ? 2 : 4) / 16;
   const int blocks = (int)((chunks + kThreads - 1) / kThreads < 2048 ? (chunks + kThreads - 1) / kThreads : 2048);
   if (g.dtype == PBSA_BF16)
     ring_append_kernel<bf16_t><<<blocks, kThreads, 0, s>>>(g, (const bf16_t*)k_new, (const bf16_t*)v_new, ring_head,
-                                                          (bf16_t*)k_l, (bf16_t*)v_l);
+                                                          (bf16_t*)k_l, (bf16_t*)v_l, status);
   else
     ring_append_kernel<float><<<blocks, kThreads, 0, s>>>(g, (const float*)k_new, (const float*)v_new, ring_head,
-                                                         (float*)k_l, (float*)v_l);
+                                                         (float*)k_l, (float*)v_l, status);
   return hipGetLastError();
 }
 

@@ -32,8 +32,27 @@ class PBSACache:
         self.ring_head = torch.zeros(1, dtype=torch.int32, device=device)
         self.step_counter = torch.zeros(1, dtype=torch.int32, device=device)
 
+    STATE = ("k_pers", "v_pers", "persist_len", "persist_src", "persist_kbar", "k_local", "v_local", "ring_head",
+             "step_counter")
+
     def refresh_pooled_keys(self, stream=None):
         api.pbsa_pool_slots(self.plan, self.k_pers, self.persist_len, self.persist_kbar, stream)
+
+    def state_dict(self) -> dict:
+        """Host copies of every tensor of the cache state (a checkpoint).
+        Waits for the work queued on the current stream."""
+        torch.cuda.current_stream().synchronize()
+        return {k: getattr(self, k).detach().to("cpu", copy=True) for k in self.STATE}
+
+    def load_state_dict(self, state: dict):
+        """Restore a checkpoint taken by ``state_dict`` (same plan)."""
+        for k in self.STATE:
+            t = getattr(self, k)
+            src = state[k]
+            if tuple(src.shape) != tuple(t.shape) or src.dtype != t.dtype:
+                raise ValueError(f"{k}: checkpoint has {tuple(src.shape)} {src.dtype}, cache has "
+                                 f"{tuple(t.shape)} {t.dtype}")
+            t.copy_(src)
 
 
 class SparseForcingAttention:
@@ -77,12 +96,27 @@ class SparseForcingAttention:
                  cache: PBSACache | None = None, update: bool = False, stream=None):
         """Attention of ``query`` over the persistent and selected local blocks.
 
-        With ``cache`` the caches and their metadata come from it.  Without it,
-        the four key/value tensors are taken as given and every persistent slot
-        is treated as full (its pooled keys are computed on the fly).
+        With ``cache`` the caches and their metadata come from it, and
+        ``key_local`` / ``value_local`` are the current chunk's keys and values
+        (the shape of ``query``): they are written into the newest slot of the
+        cache's local ring first, so the chunk attends its own keys.  With
+        ``update=True`` the call is the cache pass: after attention the
+        persistent cache is updated from the oldest ring chunk and the ring
+        advances.  Without ``cache``, the four key/value tensors are the caches
+        themselves, and every persistent slot is treated as full (its pooled
+        keys are computed on the fly).
         """
         p = self.plan
-        if cache is None:
+        if cache is not None:
+            if key_persistent is not None or value_persistent is not None:
+                raise ValueError("with a cache, the persistent keys and values come from it")
+            if (key_local is None) != (value_local is None):
+                raise ValueError("key_local and value_local go together")
+            if key_local is not None:
+                api.pbsa_ring_append(p, key_local, value_local, cache.ring_head, cache.k_local, cache.v_local, stream)
+        else:
+            if update:
+                raise ValueError("update=True needs a cache (the persistent state it updates)")
             cache = PBSACache.__new__(PBSACache)
             cache.plan = p
             cache.k_pers, cache.v_pers = key_persistent, value_persistent

@@ -3,20 +3,28 @@
 The training algorithm fragment of Sparse Forcing (review page) runs, for each
 generated chunk, the denoising passes with "PBSA with top-K" and then a cache
 pass at t = 0 that applies PBSA with top-K and updates the persistent (P) and
-local (L) caches.  ``DecodeLoop`` issues exactly those library calls:
+local (L) caches.  ``DecodeLoop`` issues exactly those library calls, with
+``denoise_passes`` denoising passes per chunk (the pages leave their number
+to the model):
 
-* ``denoise_pass()``: score_select + fwd on the current chunk (no update);
-* ``cache_pass()``:   ring_append of the chunk's K/V into the free ring slot,
-  score_select, fwd, persist_update (which advances ring head and step).
-  With ``mass="token"`` the forward of the cache pass is ``pbsa_fwd_mass``
-  and the update ranks blocks by their token-exact attention mass instead of
-  the pooled mass of score_select.
+* denoising pass i: ``pbsa_ring_append`` of that pass's keys and values into
+  the newest ring slot (the slot the last update freed), so the local window
+  holds the previous chunk and the current one; then ``pbsa_score_select`` and
+  ``pbsa_fwd`` of that pass's queries (no update);
+* cache pass: the same with the chunk's t = 0 keys and values, then
+  ``pbsa_persist_update``, which evicts the oldest ring chunk into the
+  persistent memory and advances ring head and step counter.  With
+  ``mass="token"`` the cache pass's forward is ``pbsa_fwd_mass`` and the
+  update ranks blocks by their token-exact attention mass instead of the
+  pooled mass of score_select.
 
+Every pass has its own staging inputs (q, k, v) and outputs (o, lse, topk),
+so one replay of the captured chunk leaves every pass's result readable.
 All per-step state (ring head, step counter, slot metadata) lives on the
-device, so ``capture()`` records one step into a HIP graph (via
-``torch.cuda.CUDAGraph``) that can be replayed for every chunk after the
-caller copies the chunk's q / k / v into the staging buffers.  Nothing here
-computes any part of the method; it only sequences the C ABI calls.
+device, so ``capture()`` records one chunk into a HIP graph (via
+``torch.cuda.CUDAGraph``) that is replayed for every chunk after the caller
+writes the chunk's inputs into the staging buffers.  Nothing here computes
+any part of the method; it only sequences the C ABI calls.
 """
 from __future__ import annotations
 
@@ -27,20 +35,27 @@ from .module import PBSACache
 
 
 class DecodeLoop:
-    def __init__(self, plan: api.Plan, cache: PBSACache, device="cuda", mass: str = "pooled"):
+    def __init__(self, plan: api.Plan, cache: PBSACache, device="cuda", mass: str = "pooled",
+                 denoise_passes: int = 0):
         if mass not in ("pooled", "token"):
             raise ValueError("mass must be 'pooled' or 'token'")
+        if denoise_passes < 0:
+            raise ValueError("denoise_passes must be >= 0")
         self.plan = plan
         self.cache = cache
         self.mass_mode = mass
+        self.denoise_passes = denoise_passes
         s = api.shapes(plan)
         dt = plan.torch_dtype
-        self.q = torch.zeros(s["q"], dtype=dt, device=device)       # staging: current chunk queries
-        self.k_new = torch.zeros(s["q"], dtype=dt, device=device)   # staging: current chunk keys
-        self.v_new = torch.zeros(s["q"], dtype=dt, device=device)   # staging: current chunk values
-        self.o = torch.zeros(s["q"], dtype=dt, device=device)
-        self.lse = torch.zeros(s["lse"], dtype=torch.float32, device=device)
-        self.topk = torch.zeros(s["topk_idx"], dtype=torch.int32, device=device)
+        n = denoise_passes + 1          # the last pass is the cache pass (t = 0)
+
+        def z(shape, dtype):
+            return [torch.zeros(shape, dtype=dtype, device=device) for _ in range(n)]
+
+        # staging inputs and outputs, one set per pass
+        self.qs, self.ks, self.vs = z(s["q"], dt), z(s["q"], dt), z(s["q"], dt)
+        self.os, self.lses = z(s["q"], dt), z(s["lse"], torch.float32)
+        self.topks = z(s["topk_idx"], torch.int32)
         self.mass = torch.zeros(s["mass"], dtype=torch.float32, device=device)
         self.kbar_local = torch.zeros(s["kbar_local"], dtype=torch.float32, device=device)
         self.n_replaced = torch.zeros(s["n_replaced"], dtype=torch.int32, device=device)
@@ -50,45 +65,67 @@ class DecodeLoop:
         self.ws_fwd_mass = api.workspace(plan, "fwd_mass", device) if mass == "token" else None
         self.graph = None
 
+    # the cache pass's buffers under the names of a single-pass loop
+    @property
+    def q(self):
+        return self.qs[-1]
+
+    @property
+    def o(self):
+        return self.os[-1]
+
+    @property
+    def lse(self):
+        return self.lses[-1]
+
+    @property
+    def topk(self):
+        return self.topks[-1]
+
+    def load_pass(self, i: int, q, k, v):
+        """Copy pass i's q, k, v (device tensors of the chunk shape) into its staging buffers;
+        i = denoise_passes (or -1) is the cache pass."""
+        self.qs[i].copy_(q)
+        self.ks[i].copy_(k)
+        self.vs[i].copy_(v)
+
     def load_chunk(self, q, k, v):
-        """Copy one chunk's q, k, v (device tensors of the chunk shape) into the staging buffers."""
-        self.q.copy_(q)
-        self.k_new.copy_(k)
-        self.v_new.copy_(v)
+        """Stage the chunk's t = 0 inputs (the cache pass)."""
+        self.load_pass(-1, q, k, v)
 
-    def _attend(self, stream=None):
+    def _attend(self, i, stream, token_mass=False):
         c, p = self.cache, self.plan
-        api.pbsa_score_select(p, self.q, c.k_local, c.ring_head, c.persist_kbar, c.persist_len, self.topk,
+        api.pbsa_ring_append(p, self.ks[i], self.vs[i], c.ring_head, c.k_local, c.v_local, stream)
+        api.pbsa_score_select(p, self.qs[i], c.k_local, c.ring_head, c.persist_kbar, c.persist_len, self.topks[i],
                               self.mass, self.kbar_local, self.ws_score, stream)
-        api.pbsa_fwd(p, self.q, c.k_pers, c.v_pers, c.persist_len, c.k_local, c.v_local, self.topk, self.o,
-                     self.lse, self.ws_fwd, stream)
+        if token_mass:
+            api.pbsa_fwd_mass(p, self.qs[i], c.k_pers, c.v_pers, c.persist_len, c.k_local, c.v_local,
+                              self.topks[i], self.os[i], self.lses[i], self.mass, self.ws_fwd_mass, stream)
+        else:
+            api.pbsa_fwd(p, self.qs[i], c.k_pers, c.v_pers, c.persist_len, c.k_local, c.v_local, self.topks[i],
+                         self.os[i], self.lses[i], self.ws_fwd, stream)
 
-    def denoise_pass(self, stream=None):
-        """score_select + fwd of the current chunk against the caches (no update)."""
-        self._attend(stream)
+    def denoise_pass(self, i: int, stream=None):
+        """Denoising pass i: append its keys/values to the ring, score, select, attend (no update)."""
+        if not 0 <= i < self.denoise_passes:
+            raise IndexError(f"denoising pass {i} of {self.denoise_passes}")
+        self._attend(i, stream)
 
     def cache_pass(self, stream=None):
-        """Append the chunk's K/V to the ring, attend, then update the persistent cache."""
+        """Append the chunk's t = 0 keys/values, attend, then update the persistent cache."""
         c, p = self.cache, self.plan
-        api.pbsa_ring_append(p, self.k_new, self.v_new, c.ring_head, c.k_local, c.v_local, stream)
-        if self.mass_mode == "token":
-            api.pbsa_score_select(p, self.q, c.k_local, c.ring_head, c.persist_kbar, c.persist_len, self.topk,
-                                  self.mass, self.kbar_local, self.ws_score, stream)
-            api.pbsa_fwd_mass(p, self.q, c.k_pers, c.v_pers, c.persist_len, c.k_local, c.v_local, self.topk, self.o,
-                              self.lse, self.mass, self.ws_fwd_mass, stream)
-        else:
-            self._attend(stream)
+        self._attend(-1, stream, token_mass=self.mass_mode == "token")
         api.pbsa_persist_update(p, self.mass, c.k_local, c.v_local, self.kbar_local, c.ring_head, c.step_counter,
                                 c.k_pers, c.v_pers, c.persist_len, c.persist_src, c.persist_kbar, self.n_replaced,
                                 self.ws_update, stream)
 
-    def step(self, denoise_passes: int = 0, stream=None):
-        """One chunk: ``denoise_passes`` denoising passes, then the cache pass."""
-        for _ in range(denoise_passes):
-            self.denoise_pass(stream)
+    def step(self, stream=None):
+        """One chunk: the denoising passes, then the cache pass."""
+        for i in range(self.denoise_passes):
+            self.denoise_pass(i, stream)
         self.cache_pass(stream)
 
-    def capture(self, denoise_passes: int = 0) -> torch.cuda.CUDAGraph:
+    def capture(self) -> torch.cuda.CUDAGraph:
         """Record one ``step`` into a graph.  The library's kernels must have
         run once eagerly before (one-time kernel attribute setup)."""
         g = torch.cuda.CUDAGraph()
@@ -96,7 +133,7 @@ class DecodeLoop:
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
             with torch.cuda.graph(g, stream=side):
-                self.step(denoise_passes)
+                self.step()
         torch.cuda.current_stream().wait_stream(side)
         self.graph = g
         return g

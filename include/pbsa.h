@@ -233,6 +233,26 @@ pbsa_status pbsa_persist_update(const pbsa_config* cfg, const float* mass, const
 pbsa_status pbsa_ring_append(const pbsa_config* cfg, const void* k_new, const void* v_new,
                              const int32_t* ring_head, void* k_local, void* v_local, void* stream);
 
+/* Device status word: sticky error bits that kernels raise when they find
+ * device-resident state out of range, without faulting.  The project page
+ * lists "flexible KV-cache management"; the ring head and step counter of that
+ * cache live on the device, so a corrupt value can only be seen there.  Bits:
+ *   PBSA_DEVICE_BAD_RING_HEAD     a ring head outside [0, R) was read by
+ *                                 pbsa_score_select, pbsa_persist_update or
+ *                                 pbsa_ring_append; the call used it reduced
+ *                                 into [0, R) (non-negative remainder), so every
+ *                                 access stayed in bounds, but it is not the
+ *                                 caller's ring phase
+ *   PBSA_DEVICE_BAD_STEP_COUNTER  pbsa_persist_update read a step counter
+ *                                 outside [0, 2^31 / NQ_blocks): source ids
+ *                                 are then not unique
+ * The word is per device and shared by every call on it.  pbsa_device_status
+ * enqueues on `stream` a copy of the word into `out` (one device uint32) and,
+ * when `clear` is non-zero, resets it; asynchronous like every entry point. */
+#define PBSA_DEVICE_BAD_RING_HEAD 1u
+#define PBSA_DEVICE_BAD_STEP_COUNTER 2u
+pbsa_status pbsa_device_status(uint32_t* out, int32_t clear, void* stream);
+
 /* Text of the last error on the calling thread ("" if none). */
 const char* pbsa_last_error(void);
 

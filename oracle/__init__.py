@@ -43,4 +43,6 @@ from .pbsa import (  # noqa: F401
     update_decisions,
     apply_update,
     near_tie_rows,
+    ring_append,
+    decode_chunk,
 )

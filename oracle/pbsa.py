@@ -49,6 +49,9 @@ READINGS = {
     "R20": "sink pattern (project page feature list): the first sink_slots persistent slots are pinned: never "
            "candidates for eviction; an empty sink slot j takes block j of the chunk leaving the local window, so "
            "a rollout that starts from an empty persistent cache pins the first frame's blocks",
+    "R21": "per generated chunk, the caller's number of denoising passes (score, select and attend only) and "
+           "then the cache pass (attend, then update); each pass first writes its own keys and values into the "
+           "newest local ring slot, so every pass attends the current chunk",
     "R19": "token-exact mass (the other reading of R11, chosen by the caller): block mass = sum over the chunk's "
            "query tokens of the probability their PBSA softmax puts on the block's rows; 0 for empty slots and for "
            "local blocks no query block selected",
@@ -465,6 +468,62 @@ def persist_update(state: dict, mass, k_l, v_l, kbar_l, ring_head: int, step_id:
     out["keep"] = keep
     out["admit"] = admit
     return out
+
+
+# ----------------------------------------------------------------------------
+# The local ring and the per-chunk schedule (review page, the paper's
+# training-algorithm fragment: every denoising step applies PBSA with top-K to
+# the current chunk; the t=0 cache pass applies PBSA with top-K and updates
+# the persistent (P) and local (L) caches; readings R9, R10, R21)
+# ----------------------------------------------------------------------------
+
+
+def ring_append(k_l, v_l, k_new, v_new, ring_head: int, g: Geometry):
+    """Local ring with the current chunk's keys and values in its newest slot.
+
+    The ring holds R chunks; physical chunk slot ``ring_head`` is the oldest,
+    so the newest is slot (ring_head + R - 1) mod R -- the slot the previous
+    update evicted.  Returns new arrays; the other slots are unchanged.
+    """
+    k = k_l.copy()
+    v = v_l.copy()
+    c = (ring_head + g.R - 1) % g.R
+    rows = slice(c * g.chunk_tokens, (c + 1) * g.chunk_tokens)
+    k[:, :, rows] = k_new
+    v[:, :, rows] = v_new
+    return k, v
+
+
+def decode_chunk(state: dict, k_l, v_l, passes, ring_head: int, step_id: int, g: Geometry,
+                 mass: str = "pooled", qblocks=None) -> dict:
+    """One generated chunk: its denoising passes, then the cache pass.
+
+    ``passes`` is a list of (q, k, v) of the chunk, one per pass; the last
+    entry is the cache pass (t = 0), the ones before it the denoising passes
+    (reading R21: their number is the caller's).  Every pass writes its own
+    keys and values into the newest ring slot, so the local window it scores
+    and attends holds the previous chunks and the current chunk (R3); the
+    denoising passes only attend; the cache pass attends and then updates
+    the persistent cache with its own masses, evicting the oldest ring chunk
+    (R9, R10).  ``state`` holds k_p, v_p, persist_len, persist_src,
+    persist_kbar.  Returns per-pass selections, O and LSE (``qblocks``
+    restricts the attention rows, as in ``attend``), the ring after the
+    chunk and the updated state.
+    """
+    out = []
+    for i, (q, k, v) in enumerate(passes):
+        k_l, v_l = ring_append(k_l, v_l, k, v, ring_head, g)
+        sel = score_select(q, k_l, ring_head, state["persist_kbar"], state["persist_len"], g)
+        tm = None
+        if mass == "token" and i == len(passes) - 1:
+            tm = token_mass(q, state["k_p"], state["persist_len"], k_l, sel["topk_idx"], g)
+        O, L = attend(q, state["k_p"], state["v_p"], state["persist_len"], k_l, v_l, sel["topk_idx"], g,
+                      qblocks=qblocks)
+        out.append(dict(sel=sel, O=O, L=L, token_mass=tm))
+    last = out[-1]
+    m = last["sel"]["mass"] if mass == "pooled" else last["token_mass"]
+    up = persist_update(state, m, k_l, v_l, last["sel"]["kbar_l"], ring_head, step_id, g)
+    return dict(passes=out, k_l=k_l, v_l=v_l, update=up, mass=m)
 
 
 # ----------------------------------------------------------------------------

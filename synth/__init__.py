@@ -13,4 +13,5 @@ from .gen import (  # noqa: F401
     make_step_inputs,
     make_dout,
     RolloutStream,
+    noisy_pass,
 )

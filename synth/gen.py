@@ -294,6 +294,21 @@ class RolloutStream:
         return dict(q=_finish(q, dt), k=_finish(k, dt), v=_finish(v, dt))
 
 
+def noisy_pass(chunk: dict, cfg: dict, s: int, i: int, n: int) -> dict:
+    """Inputs of denoising pass i (0 = noisiest) of n for chunk s: the chunk's
+    q, k, v blended with seeded N(0,1) noise, a*x + sqrt(1-a^2)*eps with
+    a = (i+1)/(n+1), so every pass keeps unit variance and a fading share of
+    the planted structure.  A workload recipe only."""
+    a = (i + 1) / (n + 1)
+    b = float(np.sqrt(1.0 - a * a))
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([cfg["seed"], 7919, s + 1, i])))
+    out = {}
+    for name in ("q", "k", "v"):
+        x = chunk[name]
+        out[name] = _finish(np.float32(a) * x + np.float32(b) * _normal(rng, x.shape), cfg["dtype"])
+    return out
+
+
 def describe(cfg: dict) -> str:
     lay = _layout(cfg)
     return (f"B{cfg['batch']} H{cfg['heads']} d{cfg['head_dim']} {cfg['dtype']} grid {cfg['frame_h']}x{cfg['frame_w']} "

@@ -104,3 +104,23 @@ def test_pointer_checks_before_launch():
                                  None, *(ctypes.c_void_p(0x1000 * (i + 1)) for i in range(6)),
                                  ctypes.c_void_p(0x10000), p.ws_persist_update, None)
     assert st == _lib.PBSA_ERR_INVALID_ARG   # NULL step counter
+
+
+def test_ring_head_reduction_cpu_build(tmp_path):
+    """The kernels' ring-head reduction (common.h ring_wrap), compiled for the
+    host: the non-negative remainder for every stored value, including
+    negative and extreme ones, so no slot index derived from a corrupt head
+    leaves [0, R)."""
+    import shutil
+    import subprocess
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    if not os.path.exists(hipcc) and not shutil.which("hipcc"):
+        pytest.skip("hipcc not available")
+    exe = str(tmp_path / "ring_wrap_check")
+    src = os.path.join(ROOT, "tests", "csrc", "ring_wrap_check.cpp")
+    r = subprocess.run([hipcc, "-x", "hip", "--offload-host-only", "-std=c++17", "-I", os.path.join(ROOT, "include"),
+                        "-I", os.path.join(ROOT, "block_sparse_attention_15_amd", "csrc"), src, "-o", exe],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    out = subprocess.run([exe], capture_output=True, text=True)
+    assert out.returncode == 0 and out.stdout.strip() == "ok", out.stdout

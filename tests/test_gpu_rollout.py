@@ -24,7 +24,7 @@ from pbsa_harness import compare_topk, compare_update_decisions, decisions_from_
 pytestmark = pytest.mark.gpu
 
 
-def make_loop(cfg, x, prev):
+def make_loop(cfg, x, prev, denoise_passes=0):
     p = pb.pbsa_plan(cfg)
     cache = pb.PBSACache(p)
     dt = p.torch_dtype
@@ -36,7 +36,7 @@ def make_loop(cfg, x, prev):
     cache.k_local[:, :, :ct].copy_(dev(prev["k"], dt))   # ring slot 0: chunk -1 (oldest)
     cache.v_local[:, :, :ct].copy_(dev(prev["v"], dt))
     cache.refresh_pooled_keys()
-    return p, cache, DecodeLoop(p, cache)
+    return p, cache, DecodeLoop(p, cache, denoise_passes=denoise_passes)
 
 
 def ring_of(g, chunks, rh):
@@ -117,27 +117,86 @@ def test_rollout_80_steps_graph_teacher_forced():
 
 
 def test_graph_replay_equals_eager():
+    """The whole chunk (two denoising passes with their own noisy inputs, then
+    the cache pass) captured once and replayed: bit-identical to eager."""
     cfg = synth.workload("rollout_c4", heads=4)
     stream = synth.RolloutStream(dict(cfg, steps=6))
     x = synth.make_step_inputs(dict(cfg, plant_frac=0.0))
     prev = stream.chunk(-1)
-    p, ce, le = make_loop(cfg, x, prev)
-    _, cg, lg = make_loop(cfg, x, prev)
+    p, ce, le = make_loop(cfg, x, prev, denoise_passes=2)
+    _, cg, lg = make_loop(cfg, x, prev, denoise_passes=2)
     dt = p.torch_dtype
     for s in range(6):
         ch = stream.chunk(s)
+        passes = [synth.noisy_pass(ch, cfg, s, i, 2) for i in range(2)] + [ch]
         for loop in (le, lg):
-            loop.load_chunk(dev(ch["q"], dt), dev(ch["k"], dt), dev(ch["v"], dt))
-        le.step(denoise_passes=2)
+            for i, ps in enumerate(passes):
+                loop.load_pass(i, dev(ps["q"], dt), dev(ps["k"], dt), dev(ps["v"], dt))
+        le.step()
         if s == 0:
             torch.cuda.synchronize()
-            lg.step(denoise_passes=2)
+            lg.step()
             torch.cuda.synchronize()
-            lg.capture(denoise_passes=2)
+            lg.capture()
         else:
             lg.replay()
         torch.cuda.synchronize()
         for name in ("k_pers", "v_pers", "persist_len", "persist_src", "persist_kbar", "k_local", "v_local",
                      "ring_head", "step_counter"):
             assert torch.equal(getattr(ce, name), getattr(cg, name)), (s, name)
-        assert torch.equal(le.o, lg.o) and torch.equal(le.lse, lg.lse) and torch.equal(le.topk, lg.topk)
+        for i in range(3):
+            assert torch.equal(le.os[i], lg.os[i]) and torch.equal(le.lses[i], lg.lses[i]), (s, i)
+            assert torch.equal(le.topks[i], lg.topks[i]), (s, i)
+
+
+def test_resume_from_checkpoint_is_bit_identical():
+    """Checkpoint the rollout's cache state after 40 of 80 chunks, restore it
+    into fresh buffers with a fresh captured graph, finish the rollout there:
+    every cache tensor and the last chunk's outputs equal the uninterrupted
+    run's bit for bit."""
+    cfg = synth.workload("rollout_c4", heads=4)
+    steps, cut = 80, 40
+    stream = synth.RolloutStream(dict(cfg, steps=steps))
+    x = synth.make_step_inputs(dict(cfg, plant_frac=0.0))
+    prev = stream.chunk(-1)
+    p, cache, loop = make_loop(cfg, x, prev)
+    dt = p.torch_dtype
+    chunks = [stream.chunk(s) for s in range(steps)]
+    dq = torch.stack([dev(c["q"], dt) for c in chunks])
+    dk = torch.stack([dev(c["k"], dt) for c in chunks])
+    dv = torch.stack([dev(c["v"], dt) for c in chunks])
+    loop.load_chunk(dq[0], dk[0], dv[0])
+    loop.step()
+    torch.cuda.synchronize()
+    _, c0, l0 = make_loop(cfg, x, prev)   # graph captured on a second cache
+    l0.load_chunk(dq[0], dk[0], dv[0])
+    l0.step()
+    torch.cuda.synchronize()
+    l0.capture()
+    ckpt = None
+    # the uninterrupted run: chunk 0 ran eagerly above on `cache`; replay the rest on `c0`'s graph after copying state
+    c0.load_state_dict(cache.state_dict())
+    for s in range(1, steps):
+        if s == cut:
+            ckpt = c0.state_dict()
+        l0.load_chunk(dq[s], dk[s], dv[s])
+        l0.replay()
+    torch.cuda.synchronize()
+    final = c0.state_dict()
+    out = (l0.o.clone(), l0.lse.clone(), l0.topk.clone())
+    assert int(final["step_counter"][0]) == steps and int(ckpt["step_counter"][0]) == cut
+    # resume: fresh buffers, fresh graph, the checkpoint restored
+    _, c1, l1 = make_loop(cfg, x, prev)
+    l1.load_chunk(dq[0], dk[0], dv[0])
+    l1.step()                              # one eager step for the library's one-time setup
+    torch.cuda.synchronize()
+    l1.capture()
+    c1.load_state_dict(ckpt)
+    for s in range(cut, steps):
+        l1.load_chunk(dq[s], dk[s], dv[s])
+        l1.replay()
+    torch.cuda.synchronize()
+    resumed = c1.state_dict()
+    for k in final:
+        assert torch.equal(final[k], resumed[k]), k
+    assert torch.equal(out[0], l1.o) and torch.equal(out[1], l1.lse) and torch.equal(out[2], l1.topk)

@@ -95,14 +95,12 @@ def test_c1_token_mass_and_update():
     st.fwd_mass(dev(sel["topk_idx"]))
     torch.cuda.synchronize()
     m_gpu = host(st.mass)
-    heads = [0, 7]
+    heads = list(range(g.H))      # every head
     c2 = dict(cfg, heads=len(heads))
     g2 = oracle.geometry(c2)
     xs = {k: v[:, heads] for k, v in x.items() if k != "ring_head"}
     ref_m = oracle.token_mass(xs["q"], xs["k_p"], xs["persist_len"], xs["k_l"], sel["topk_idx"][:, heads], g2)
     check_mass(m_gpu[:, heads], ref_m, g2, sel["topk_idx"][:, heads], xs["persist_len"], "decode_c1")
-    # every head's total, all 12
-    np.testing.assert_allclose(m_gpu.sum(-1, dtype=np.float64), g.chunk_tokens, rtol=1e-4)
     # the update on those heads against the oracle's decisions from its own masses
     step_id = 4
     before = dict(k_p=x["k_p"], v_p=x["v_p"], persist_len=x["persist_len"], persist_src=x["persist_src"],

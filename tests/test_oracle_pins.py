@@ -621,3 +621,97 @@ def test_token_mass_uniform_keys_closed_form():
                 for p in idx[b, h, i]:
                     exp[g.S + p] += nq * blen[p % g.n_qblk] / n_t
             np.testing.assert_allclose(m[b, h], exp, rtol=1e-6)
+
+
+# ---------------------------------------------------------------------------
+# The local ring and the per-chunk schedule (training-algorithm fragment:
+# denoising passes attend the current chunk; the cache pass attends and
+# updates)
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("ring_head", [0, 1, 2, 3])
+def test_ring_append_writes_the_newest_logical_chunk(ring_head):
+    """The appended chunk becomes the newest logical chunk, whatever the ring
+    phase: block e of it is logical block (R-1)*n_qblk + e, whose tokens hold
+    the new rows; every other token keeps its value."""
+    cfg = synth.workload("tiny_fp32")
+    g = oracle.geometry(cfg)
+    x = synth.make_step_inputs(cfg)
+    rng = np.random.default_rng(ring_head)
+    kn = rng.standard_normal(x["q"].shape).astype(np.float32)
+    vn = rng.standard_normal(x["q"].shape).astype(np.float32)
+    k2, v2 = oracle.ring_append(x["k_l"], x["v_l"], kn, vn, ring_head, g)
+    touched = np.zeros(x["k_l"].shape[2], bool)
+    for p in range(g.n_lblk):
+        lg = g.logical_of(p, ring_head)
+        if lg >= (g.R - 1) * g.n_qblk:
+            e = lg - (g.R - 1) * g.n_qblk
+            tok = g.local_tokens_of(p)
+            np.testing.assert_array_equal(k2[:, :, tok], kn[:, :, g.block_tok[e]])
+            np.testing.assert_array_equal(v2[:, :, tok], vn[:, :, g.block_tok[e]])
+            touched[tok] = True
+    assert touched.sum() == g.chunk_tokens
+    np.testing.assert_array_equal(k2[:, :, ~touched], x["k_l"][:, :, ~touched])
+    np.testing.assert_array_equal(v2[:, :, ~touched], x["v_l"][:, :, ~touched])
+
+
+def _schedule_inputs(cfg, n_passes, seed):
+    rng = np.random.default_rng(seed)
+    shape = synth.make_step_inputs(cfg)["q"].shape
+    return [tuple(rng.standard_normal(shape).astype(np.float32) for _ in range(3)) for _ in range(n_passes)]
+
+
+def test_every_pass_attends_its_own_chunk():
+    """A block planted (large alpha along u, queries leaning on u) in the keys
+    of one pass is selected by every query block of that pass and by no
+    other pass: each pass scores the local window that holds its own keys,
+    not those of the pass before it or the chunk the last update evicted."""
+    cfg = synth.workload("tiny_fp32", plant_frac=0.0, heads=1)
+    g = oracle.geometry(cfg)
+    x = synth.make_step_inputs(cfg)
+    rng = np.random.default_rng(11)
+    u = rng.standard_normal(g.D)
+    u /= np.linalg.norm(u)
+    passes = _schedule_inputs(cfg, 3, 12)
+    ring_head = 2
+    newest = (ring_head + g.R - 1) % g.R
+    # pass i plants block i of its chunk and pushes the blocks the other
+    # passes plant far down (-alpha u), so a stale window would show
+    assert len(passes) <= g.n_qblk
+    planted = [newest * g.n_qblk + i for i in range(len(passes))]
+    for i, (q, k, v) in enumerate(passes):
+        for j in range(len(passes)):
+            k[0, 0, g.block_tok[j]] += (60 if j == i else -60) * u
+        q[0, 0] += 6 * u
+    out = oracle.decode_chunk(_state(x, g), x["k_l"], x["v_l"], passes, ring_head, 4, g)
+    for i, r in enumerate(out["passes"]):
+        idx = r["sel"]["topk_idx"][0, 0]
+        assert all(planted[i] in row for row in idx), i
+        assert all(planted[j] not in row for row in idx for j in range(len(passes)) if j != i), i
+
+
+def test_denoising_passes_do_not_touch_the_update():
+    """The persistent state after a chunk depends on the cache pass only: the
+    same chunk with zero or three denoising passes before its cache pass
+    gives the same update, and the ring ends with the cache pass's keys."""
+    cfg = synth.workload("tiny_fp32", heads=2)
+    g = oracle.geometry(cfg)
+    x = synth.make_step_inputs(cfg)
+    passes = _schedule_inputs(cfg, 4, 13)
+    a = oracle.decode_chunk(_state(x, g), x["k_l"], x["v_l"], passes, 1, 7, g)
+    b = oracle.decode_chunk(_state(x, g), x["k_l"], x["v_l"], passes[-1:], 1, 7, g)
+    for k in ("k_p", "v_p", "persist_len", "persist_src", "persist_kbar", "n_replaced"):
+        np.testing.assert_array_equal(a["update"][k], b["update"][k])
+    np.testing.assert_array_equal(a["k_l"], b["k_l"])
+    assert a["update"]["ring_head"] == 2
+    # the evicted chunk's rows went into the persistent cache, not a denoising pass's rows
+    for bb in range(g.B):
+        for h in range(g.H):
+            for s in range(g.S):
+                src = a["update"]["persist_src"][bb, h, s]
+                if src >= 7 * g.n_qblk:
+                    e = src - 7 * g.n_qblk
+                    tok = 1 * g.chunk_tokens + g.block_tok[e]
+                    n = len(tok)
+                    np.testing.assert_array_equal(a["update"]["k_p"][bb, h, s, :n], x["k_l"][bb, h, tok])
