@@ -95,6 +95,9 @@ class Bench:
         self.pkbar0 = torch.empty(s["persist_kbar"], dtype=torch.float32, device="cuda")
         pb.pbsa_pool_slots(p, self.pristine["k_p"], self.pristine["plen"], self.pkbar0)
         self.pkbar = self.pkbar0.clone()
+        self.kbar_l0 = torch.empty(s["kbar_local"], dtype=torch.float32, device="cuda")
+        pb.pbsa_pool_local(p, self.pristine["k_l"], self.kbar_l0)
+        self.kbar_l = self.kbar_l0.clone()
         self.q = dev(x["q"], dt)
         # the chunk appended each step: the current chunk of the input ring
         nq = p.chunk_tokens
@@ -104,7 +107,6 @@ class Bench:
         f32 = dict(dtype=torch.float32, device="cuda")
         self.topk = torch.empty(s["topk_idx"], dtype=torch.int32, device="cuda")
         self.mass = torch.empty(s["mass"], **f32)
-        self.kbar_l = torch.empty(s["kbar_local"], **f32)
         self.o = torch.empty(s["q"], dtype=dt, device="cuda")
         self.lse = torch.empty(s["lse"], **f32)
         self.grads = None
@@ -128,13 +130,15 @@ class Bench:
         for k, v in self.pristine.items():
             self.live[k].copy_(v)
         self.pkbar.copy_(self.pkbar0)
+        self.kbar_l.copy_(self.kbar_l0)
         self.step_id = 0
 
     def ops(self, train=False):
         pb, L, p = self.pb, self.live, self.p
-        out = [("append", lambda: pb.pbsa_ring_append(p, self.k_new, self.v_new, L["ring_head"], L["k_l"], L["v_l"])),
-               ("score_select", lambda: pb.pbsa_score_select(p, self.q, L["k_l"], L["ring_head"], self.pkbar, L["plen"],
-                                                             self.topk, self.mass, self.kbar_l, self.ws_s)),
+        out = [("append", lambda: pb.pbsa_ring_append(p, self.k_new, self.v_new, L["ring_head"], L["k_l"], L["v_l"],
+                                                     self.kbar_l)),
+               ("score_select", lambda: pb.pbsa_score_select(p, self.q, self.kbar_l, L["ring_head"], self.pkbar,
+                                                             L["plen"], self.topk, self.mass, self.ws_s)),
                ("fwd", lambda: pb.pbsa_fwd(p, self.q, L["k_p"], L["v_p"], L["plen"], L["k_l"], L["v_l"], self.topk,
                                            self.o, self.lse, self.ws_f))]
         if train:
@@ -207,12 +211,18 @@ class Bench:
         return float(2 * row * (lens.sum() + p.slot_rows * (ent.sum() + emptied.sum())))
 
     def score_bytes(self):
+        """Bytes score_select moves: the queries (pooled in the call), the pooled
+        keys of the local blocks and slots (ring and slot metadata, pooled when
+        their keys were written), the selections and the masses."""
         p, esz = self.p, (2 if self.cfg["dtype"] == "bf16" else 4)
-        return p.B * p.H * ((p.chunk_tokens + p.local_tokens) * p.D * esz + p.persistent_slots * p.D * 4)
+        nl = p.local_blocks
+        return p.B * p.H * (p.chunk_tokens * p.D * esz + (nl + p.persistent_slots) * p.D * 4 +
+                            p.blocks_per_chunk * p.topk * 4 + (nl + p.persistent_slots) * 4)
 
     def append_bytes(self):
+        """The chunk's keys and values read and written once, plus its pooled keys."""
         p, esz = self.p, (2 if self.cfg["dtype"] == "bf16" else 4)
-        return 2 * 2 * p.B * p.H * p.chunk_tokens * p.D * esz
+        return 2 * 2 * p.B * p.H * p.chunk_tokens * p.D * esz + p.B * p.H * p.blocks_per_chunk * p.D * 4
 
 
 def _stats(t):

@@ -11,6 +11,7 @@ from .api import (  # noqa: F401
     make_config,
     pbsa_plan,
     pbsa_pool_slots,
+    pbsa_pool_local,
     pbsa_score_select,
     pbsa_fwd,
     pbsa_fwd_mass,

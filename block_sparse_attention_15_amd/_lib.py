@@ -53,12 +53,13 @@ _CFG = ctypes.POINTER(PbsaConfig)
 SIGNATURES = {
     "pbsa_plan": [_CFG, ctypes.POINTER(PbsaPlanInfo)],
     "pbsa_pool_slots": [_CFG, _P, _P, _P, _P],
-    "pbsa_score_select": [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "pbsa_pool_local": [_CFG, _P, _P, _P],
+    "pbsa_score_select": [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "pbsa_fwd": [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "pbsa_fwd_mass": [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "pbsa_bwd": [_CFG] + [_P] * 15 + [_P, ctypes.c_size_t, _P],
     "pbsa_persist_update": [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
-    "pbsa_ring_append": [_CFG, _P, _P, _P, _P, _P, _P],
+    "pbsa_ring_append": [_CFG, _P, _P, _P, _P, _P, _P, _P],
     "pbsa_device_status": [_P, ctypes.c_int32, _P],
 }
 

@@ -144,18 +144,23 @@ def pbsa_pool_slots(p: Plan, k_pers, persist_len, persist_kbar, stream=None):
           _ptr(persist_kbar, s["persist_kbar"], torch.float32, "persist_kbar"), _stream(stream))
 
 
-def pbsa_score_select(p: Plan, q, k_local, ring_head, persist_kbar, persist_len, topk_idx, mass, kbar_local,
-                      ws, stream=None):
+def pbsa_pool_local(p: Plan, k_local, kbar_local, stream=None):
+    """Pooled keys of every local block of the ring (for a ring written from outside the library)."""
+    s = shapes(p)
+    _call("pbsa_pool_local", ctypes.byref(p.cfg), _ptr(k_local, s["k_local"], p.torch_dtype, "k_local"),
+          _ptr(kbar_local, s["kbar_local"], torch.float32, "kbar_local"), _stream(stream))
+
+
+def pbsa_score_select(p: Plan, q, kbar_local, ring_head, persist_kbar, persist_len, topk_idx, mass, ws, stream=None):
     s = shapes(p)
     w, nb = _ws(ws, p.ws_score_select)
     _call("pbsa_score_select", ctypes.byref(p.cfg), _ptr(q, s["q"], p.torch_dtype, "q"),
-          _ptr(k_local, s["k_local"], p.torch_dtype, "k_local"),
+          _ptr(kbar_local, s["kbar_local"], torch.float32, "kbar_local"),
           _ptr(ring_head, s["ring_head"], torch.int32, "ring_head"),
           _ptr(persist_kbar, s["persist_kbar"], torch.float32, "persist_kbar"),
           _ptr(persist_len, s["persist_len"], torch.int32, "persist_len"),
           _ptr(topk_idx, s["topk_idx"], torch.int32, "topk_idx"),
-          _ptr(mass, s["mass"], torch.float32, "mass"),
-          _ptr(kbar_local, s["kbar_local"], torch.float32, "kbar_local"), w, nb, _stream(stream))
+          _ptr(mass, s["mass"], torch.float32, "mass"), w, nb, _stream(stream))
 
 
 def pbsa_fwd(p: Plan, q, k_pers, v_pers, persist_len, k_local, v_local, topk_idx, o, lse, ws=None, stream=None):
@@ -218,12 +223,14 @@ def pbsa_persist_update(p: Plan, mass, k_local, v_local, kbar_local, ring_head, 
           _ptr(n_replaced, s["n_replaced"], torch.int32, "n_replaced"), w, nb, _stream(stream))
 
 
-def pbsa_ring_append(p: Plan, k_new, v_new, ring_head, k_local, v_local, stream=None):
+def pbsa_ring_append(p: Plan, k_new, v_new, ring_head, k_local, v_local, kbar_local, stream=None):
+    """Write a chunk's keys/values into the newest ring slot and pool its keys into ``kbar_local``."""
     s = shapes(p)
     dt = p.torch_dtype
     _call("pbsa_ring_append", ctypes.byref(p.cfg), _ptr(k_new, s["q"], dt, "k_new"), _ptr(v_new, s["q"], dt, "v_new"),
           _ptr(ring_head, s["ring_head"], torch.int32, "ring_head"), _ptr(k_local, s["k_local"], dt, "k_local"),
-          _ptr(v_local, s["k_local"], dt, "v_local"), _stream(stream))
+          _ptr(v_local, s["k_local"], dt, "v_local"), _ptr(kbar_local, s["kbar_local"], torch.float32, "kbar_local"),
+          _stream(stream))
 
 
 def pbsa_device_status(out, clear: bool = True, stream=None):

@@ -165,11 +165,11 @@ pbsa_status make_plan(const pbsa_config* c, Plan* p) {
   for (int j = 0; j < g.nq; ++j) mx = mx > block_ext(g, j).len ? mx : block_ext(g, j).len;
   in.max_block_tokens = mx;
   const size_t BH = (size_t)g.B * g.H;
-  in.ws_score_select = align256(BH * g.nq * g.D * 4) + align256(BH * g.nq * (g.S + g.nl) * 4);
+  in.ws_score_select = score_workspace(g);
   in.ws_fwd = fwd_workspace(g);
   in.ws_bwd = align256(zrow_offset(BH * g.ct) * 4 + 256) + align256(BH * g.ct * 4 + 4) + 2 * align256(BH * g.nl * 4) +
               align256(BH * g.nl * g.nq * 4) + align256(bwd_ds_bytes(g)) + geo_table_bytes(g);
-  in.ws_persist_update = align256(BH * g.S * 4);
+  in.ws_persist_update = update_workspace(g);
   in.ws_fwd_mass = align256(in.ws_fwd) + align256(BH * g.S * g.ct * 4) + align256(BH * g.K * g.ct * 4) +
                    align256(BH * g.nq * g.nl * 4);
   return PBSA_OK;
@@ -236,33 +236,38 @@ pbsa_status pbsa_pool_slots(const pbsa_config* cfg, const void* k_pers, const in
                     "pbsa_pool_slots");
 }
 
-pbsa_status pbsa_score_select(const pbsa_config* cfg, const void* q, const void* k_local,
-                              const int32_t* ring_head, const float* persist_kbar,
-                              const int32_t* persist_len, int32_t* topk_idx, float* mass,
-                              float* kbar_local, void* ws, size_t ws_bytes, void* stream) {
+pbsa_status pbsa_pool_local(const pbsa_config* cfg, const void* k_local, float* kbar_local, void* stream) {
+  Plan p;
+  pbsa_status st = make_plan(cfg, &p);
+  if (st != PBSA_OK) return st;
+  REQUIRE_ALIGNED(k_local);
+  REQUIRE_ALIGNED(kbar_local);
+  return hip_status(launch_pool_local(p.g, k_local, kbar_local, (hipStream_t)stream), "pbsa_pool_local");
+}
+
+pbsa_status pbsa_score_select(const pbsa_config* cfg, const void* q, const float* kbar_local,
+                              const int32_t* ring_head, const float* persist_kbar, const int32_t* persist_len,
+                              int32_t* topk_idx, float* mass, void* ws, size_t ws_bytes, void* stream) {
   Plan p;
   pbsa_status st = make_plan(cfg, &p);
   if (st != PBSA_OK) return st;
   REQUIRE_ALIGNED(q);
-  REQUIRE_ALIGNED(k_local);
+  REQUIRE_ALIGNED(kbar_local);
   REQUIRE_PTR(ring_head);
   REQUIRE_PTR(topk_idx);
   REQUIRE_PTR(mass);
-  REQUIRE_ALIGNED(kbar_local);
   if (p.g.S > 0) {
     REQUIRE_ALIGNED(persist_kbar);
     REQUIRE_PTR(persist_len);
   }
   if ((st = check_ws(ws, ws_bytes, p.info.ws_score_select)) != PBSA_OK) return st;
-  const size_t BH = (size_t)p.g.B * p.g.H;
   WsScore w;
-  w.qbar = (float*)ws;
-  w.prow = (float*)((char*)ws + align256(BH * p.g.nq * p.g.D * 4));
+  w.part = (float*)ws;
   uint32_t* status = nullptr;
   hipError_t e = device_status_word(&status);
   if (e == hipSuccess)
-    e = launch_score_select(p.g, q, k_local, ring_head, persist_kbar, persist_len, topk_idx, mass, kbar_local, w,
-                            status, (hipStream_t)stream);
+    e = launch_score_select(p.g, q, kbar_local, ring_head, persist_kbar, persist_len, topk_idx, mass, w, status,
+                            (hipStream_t)stream);
   return hip_status(e, "pbsa_score_select");
 }
 
@@ -402,13 +407,13 @@ pbsa_status pbsa_persist_update(const pbsa_config* cfg, const float* mass, const
   hipError_t e = device_status_word(&status);
   if (e == hipSuccess)
     e = launch_persist_update(p.g, mass, k_local, v_local, kbar_local, ring_head, step_counter, k_pers, v_pers,
-                              persist_len, persist_src, persist_kbar, n_replaced, (int32_t*)ws, status,
-                              (hipStream_t)stream);
+                              persist_len, persist_src, persist_kbar, n_replaced, ws, status, (hipStream_t)stream);
   return hip_status(e, "pbsa_persist_update");
 }
 
 pbsa_status pbsa_ring_append(const pbsa_config* cfg, const void* k_new, const void* v_new,
-                             const int32_t* ring_head, void* k_local, void* v_local, void* stream) {
+                             const int32_t* ring_head, void* k_local, void* v_local, float* kbar_local,
+                             void* stream) {
   Plan p;
   pbsa_status st = make_plan(cfg, &p);
   if (st != PBSA_OK) return st;
@@ -417,9 +422,11 @@ pbsa_status pbsa_ring_append(const pbsa_config* cfg, const void* k_new, const vo
   REQUIRE_PTR(ring_head);
   REQUIRE_ALIGNED(k_local);
   REQUIRE_ALIGNED(v_local);
+  REQUIRE_ALIGNED(kbar_local);
   uint32_t* status = nullptr;
   hipError_t e = device_status_word(&status);
-  if (e == hipSuccess) e = launch_ring_append(p.g, k_new, v_new, ring_head, k_local, v_local, status, (hipStream_t)stream);
+  if (e == hipSuccess)
+    e = launch_ring_append(p.g, k_new, v_new, ring_head, k_local, v_local, kbar_local, status, (hipStream_t)stream);
   return hip_status(e, "pbsa_ring_append");
 }
 

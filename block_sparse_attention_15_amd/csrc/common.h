@@ -181,14 +181,18 @@ size_t bwd_ds_bytes(const Geo& g);
 bool bwd_mfma_supported(const Geo& g);
 hipError_t launch_geo_table(const Geo& g, void* ws, GeoTab* tab, hipStream_t s);
 
+// Query blocks per score workgroup at a geometry (4, 2 or 1: the largest whose LDS fits).
+int score_qpw(const Geo& g);
 struct WsScore {
-  float* qbar;   // [B,H,nq,D]
-  float* prow;   // [B,H,nq,S+nl]  pooled softmax rows
+  float* part;  // [B,H,groups,S+nl]  column sums of each score workgroup's softmax rows
 };
+size_t score_workspace(const Geo& g);
 hipError_t launch_pool_slots(const Geo& g, const void* k_p, const int32_t* plen, float* kbar, hipStream_t s);
-hipError_t launch_score_select(const Geo& g, const void* q, const void* k_l, const int32_t* ring_head,
-                               const float* kbar_p, const int32_t* plen, int32_t* topk, float* mass,
-                               float* kbar_l, WsScore ws, uint32_t* status, hipStream_t s);
+// Pooled keys of every physical local block of the ring.
+hipError_t launch_pool_local(const Geo& g, const void* k_l, float* kbar_l, hipStream_t s);
+hipError_t launch_score_select(const Geo& g, const void* q, const float* kbar_l, const int32_t* ring_head,
+                               const float* kbar_p, const int32_t* plen, int32_t* topk, float* mass, WsScore ws,
+                               uint32_t* status, hipStream_t s);
 // blse_p / blse_l: NULL, or [B,H,S,ct] / [B,H,K,ct] outputs of each query's
 // log-sum-exp over each persistent slot / each of its selected local blocks,
 // in base 2 (log2 of the sum of exp of the scaled scores; -inf where the slot
@@ -223,11 +227,13 @@ hipError_t launch_bwd(const Geo& g, const void* q, const void* k_p, const void* 
                       const void* k_l, const void* v_l, const int32_t* topk, const void* o,
                       const float* lse, const void* dout, float* dq, float* dk_p, float* dv_p,
                       float* dk_l, float* dv_l, WsBwd ws, hipStream_t s);
+size_t update_workspace(const Geo& g);
 hipError_t launch_persist_update(const Geo& g, const float* mass, const void* k_l, const void* v_l,
                                  const float* kbar_l, int32_t* ring_head, int32_t* step_counter, void* k_p,
                                  void* v_p, int32_t* plen, int32_t* psrc, float* pkbar, int32_t* n_rep,
-                                 int32_t* plan, uint32_t* status, hipStream_t s);
+                                 void* ws, uint32_t* status, hipStream_t s);
+// Copy a new chunk into the newest ring slot and pool its keys into kbar_l.
 hipError_t launch_ring_append(const Geo& g, const void* k_new, const void* v_new, const int32_t* ring_head,
-                              void* k_l, void* v_l, uint32_t* status, hipStream_t s);
+                              void* k_l, void* v_l, float* kbar_l, uint32_t* status, hipStream_t s);
 
 }  // namespace pbsa

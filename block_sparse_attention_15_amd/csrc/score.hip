@@ -9,82 +9,134 @@
 // for each query block a softmax of the same pooled scores over valid
 // persistent slots and all local blocks, summed over query blocks.
 //
-// Memory-bound: pooling reads Q and the local K once (coalesced row
-// segments); scoring works on the pooled fp32 vectors, which stay in L2.
+// Pooled keys are cache metadata: a persistent slot's mean key is carried
+// with the slot, and a local block's mean key is computed when its chunk is
+// written into the ring (pbsa_ring_append pools while it copies; a ring
+// filled from outside is pooled once by pbsa_pool_local).  Scoring therefore
+// reads only the queries and the pooled keys.  Two launches, no
+// synchronisation between workgroups:
+//  1. per workgroup QPW query blocks of one head (512 threads): pool them
+//     (16-byte row loads, fixed-order reduction), score them against every
+//     candidate (each candidate's pooled key read once for the QPW blocks),
+//     per query block (one wave) a two-phase radix select of the top K and
+//     one softmax row, and the column sums of those rows (ascending rows);
+//  2. the masses: per (head, candidate) the sum of the workgroups' column
+//     sums in ascending workgroup order -- deterministic.
 #include "common.h"
 
 namespace pbsa {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kPartBatch = 16;  // partial-sum loads in flight per thread in the last workgroup
 
-template <typename T> struct Vec4;
-template <> struct Vec4<float> {
-  __device__ static float4 load(const float* p) { return *reinterpret_cast<const float4*>(p); }
-};
-template <> struct Vec4<bf16_t> {
-  __device__ static float4 load(const bf16_t* p) {
-    uint2 u = *reinterpret_cast<const uint2*>(p);
-    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
-                       __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
-  }
+template <int D, typename T> struct Rows {
+  static constexpr int VEC = 16 / sizeof(T);        // elements per 16-byte chunk
+  static constexpr int CPR = D / VEC;               // chunks per row
+  static constexpr int NRG = kThreads / CPR;        // row groups
+  static constexpr int RPT = (64 + NRG - 1) / NRG;  // rows per thread at most (blocks <= 64 rows)
 };
 
-// Mean of `len` (<= 64) rows (row(i) gives the row index) of a [*, D]
-// tensor, written to out[D].  Fixed summation order: each thread sums rows
-// rg, rg+nrg, ...; the row groups are then added in order 0..nrg-1; the sum
-// is divided by len (0 rows give 0).  All of a thread's row loads are issued
-// before the first add.
-template <int D, typename T, typename RowFn>
-__device__ void pool_rows(const T* base, int len, RowFn row, float* red /* [nrg][D] */, float* out) {
-  constexpr int ncg = D / 4;              // column groups of 4 elements
-  constexpr int nrg = kThreads / ncg;     // row groups
-  constexpr int kIt = 64 / nrg;           // rows per thread at most
-  const int cg = threadIdx.x % ncg, rg = threadIdx.x / ncg;
-  float4 v[kIt];
+__device__ __forceinline__ void add_chunk(float* acc, uint4 v, bf16_t) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-  for (int u = 0; u < kIt; ++u) {
-    const int i = rg + nrg * u;
-    v[u] = i < len ? Vec4<T>::load(base + (size_t)row(i) * D + cg * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int k = 0; k < 4; ++k) {
+    acc[2 * k] += __uint_as_float(w[k] << 16);
+    acc[2 * k + 1] += __uint_as_float(w[k] & 0xffff0000u);
   }
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+__device__ __forceinline__ void add_chunk(float* acc, uint4 v, float) {
+  acc[0] += __uint_as_float(v.x);
+  acc[1] += __uint_as_float(v.y);
+  acc[2] += __uint_as_float(v.z);
+  acc[3] += __uint_as_float(v.w);
+}
+
+// Mean of the `len` (<= 64) rows src_row(i) of a [*, D] tensor into out[D],
+// fixed summation order (each thread sums its row group's rows in order, the
+// row groups are added in order 0..NRG-1, then divided by len; 0 rows give
+// 0).  With COPY the rows are also written to dst_row(i) (the same loads).
+// All of a thread's loads are issued before the first add.
+template <int D, typename T, bool COPY, typename SrcFn, typename DstFn>
+__device__ __forceinline__ void pool_rows(const T* src, T* dst, int len, SrcFn src_row, DstFn dst_row,
+                                          float* red /* [NRG][D] */, float* out) {
+  using R = Rows<D, T>;
+  const int c = threadIdx.x % R::CPR, rg = threadIdx.x / R::CPR;
+  uint4 v[R::RPT];
 #pragma unroll
-  for (int u = 0; u < kIt; ++u) {
-    if (rg + nrg * u < len) {
-      acc.x += v[u].x;
-      acc.y += v[u].y;
-      acc.z += v[u].z;
-      acc.w += v[u].w;
+  for (int u = 0; u < R::RPT; ++u) {
+    const int i = rg + R::NRG * u;
+    v[u] = i < len ? *reinterpret_cast<const uint4*>(src + (size_t)src_row(i) * D + c * R::VEC)
+                   : make_uint4(0, 0, 0, 0);
+  }
+  if (COPY) {
+#pragma unroll
+    for (int u = 0; u < R::RPT; ++u) {
+      const int i = rg + R::NRG * u;
+      if (i < len) *reinterpret_cast<uint4*>(dst + (size_t)dst_row(i) * D + c * R::VEC) = v[u];
     }
   }
-  float* r = red + rg * D + cg * 4;
-  r[0] = acc.x;
-  r[1] = acc.y;
-  r[2] = acc.z;
-  r[3] = acc.w;
+  float acc[R::VEC] = {};
+#pragma unroll
+  for (int u = 0; u < R::RPT; ++u) add_chunk(acc, v[u], T{});  // rows past len were loaded as zero
+#pragma unroll
+  for (int k = 0; k < R::VEC; ++k) red[rg * D + c * R::VEC + k] = acc[k];
   __syncthreads();
   for (int d = threadIdx.x; d < D; d += kThreads) {
     float s = 0.f;
-    for (int k = 0; k < nrg; ++k) s += red[k * D + d];
+    for (int k = 0; k < R::NRG; ++k) s += red[k * D + d];
     out[d] = len > 0 ? s / (float)len : 0.f;
   }
 }
 
-// grid (nq + nl, H, B): query block means -> qbar, local block means -> kbar_l.
-template <int D, typename T>
-__global__ __launch_bounds__(kThreads) void pool_blocks_kernel(Geo g, const T* __restrict__ q,
-                                                               const T* __restrict__ kl, float* __restrict__ qbar,
-                                                               float* __restrict__ kbar_l) {
-  __shared__ float red[kThreads * 4];
+// Copy of a [*, D] row range without pooling (V of the appended chunk).
+template <int D, typename T, typename SrcFn, typename DstFn>
+__device__ __forceinline__ void copy_rows(const T* src, T* dst, int len, SrcFn src_row, DstFn dst_row) {
+  using R = Rows<D, T>;
+  const int c = threadIdx.x % R::CPR, rg = threadIdx.x / R::CPR;
+  uint4 v[R::RPT];
+#pragma unroll
+  for (int u = 0; u < R::RPT; ++u) {
+    const int i = rg + R::NRG * u;
+    v[u] = i < len ? *reinterpret_cast<const uint4*>(src + (size_t)src_row(i) * D + c * R::VEC)
+                   : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int u = 0; u < R::RPT; ++u) {
+    const int i = rg + R::NRG * u;
+    if (i < len) *reinterpret_cast<uint4*>(dst + (size_t)dst_row(i) * D + c * R::VEC) = v[u];
+  }
+}
+
+// grid (nq, H, B): write block j of a new chunk (k_new / v_new, [B,H,ct,D])
+// into the newest ring slot, (ring_head + R - 1) mod R, and its mean key into
+// kbar_local.  APPEND = false (pbsa_pool_local): grid (nl, H, B), only pool
+// physical local block j of the ring.
+template <int D, typename T, bool APPEND>
+__global__ __launch_bounds__(kThreads) void local_pool_kernel(Geo g, const T* __restrict__ k_new,
+                                                              const T* __restrict__ v_new,
+                                                              const int32_t* __restrict__ ring_head,
+                                                              T* __restrict__ kl, T* __restrict__ vl,
+                                                              float* __restrict__ kbar_l,
+                                                              uint32_t* __restrict__ status) {
+  __shared__ float red[Rows<D, T>::NRG * D];
   const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const size_t bh = (size_t)b * g.H + h;
-  const bool is_q = j < g.nq;
-  const int p = is_q ? j : j - g.nq;
-  const int off = is_q ? 0 : (p / g.nq) * g.ct;
-  const BlockExt e = block_ext(g, p % g.nq);
-  const T* base = is_q ? q + bh * g.ct * g.D : kl + bh * (size_t)g.NL * g.D;
-  float* out = is_q ? qbar + (bh * g.nq + p) * g.D : kbar_l + (bh * g.nl + p) * g.D;
-  pool_rows<D, T>(base, e.len, [&](int i) { return off + block_token(g, e, i); }, red, out);
+  const BlockExt e = block_ext(g, j % g.nq);
+  T* kb = kl + bh * (size_t)g.NL * D;
+  if (APPEND) {
+    const int slot = (read_ring_head(ring_head, g.R, status) + g.R - 1) % g.R;
+    const int off = slot * g.ct;
+    auto tok = [&](int i) { return block_token(g, e, i); };
+    auto dst = [&](int i) { return off + block_token(g, e, i); };
+    copy_rows<D, T>(v_new + bh * g.ct * D, vl + bh * (size_t)g.NL * D, e.len, tok, dst);
+    pool_rows<D, T, true>(k_new + bh * g.ct * D, kb, e.len, tok, dst, red,
+                          kbar_l + (bh * g.nl + slot * g.nq + j) * D);
+  } else {
+    const int off = (j / g.nq) * g.ct;
+    pool_rows<D, T, false>(kb, (T*)nullptr, e.len, [&](int i) { return off + block_token(g, e, i); },
+                           [](int i) { return i; }, red, kbar_l + (bh * g.nl + j) * D);
+  }
 }
 
 // grid (S, H, B): mean of each slot's first len rows (0 for empty slots).
@@ -92,11 +144,12 @@ template <int D, typename T>
 __global__ __launch_bounds__(kThreads) void pool_slots_kernel(Geo g, const T* __restrict__ kp,
                                                               const int32_t* __restrict__ plen,
                                                               float* __restrict__ kbar) {
-  __shared__ float red[kThreads * 4];
+  __shared__ float red[Rows<D, T>::NRG * D];
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const size_t bhs = ((size_t)b * g.H + h) * g.S + s;
   const int len = min(max(plen[bhs], 0), g.C);
-  pool_rows<D, T>(kp + bhs * g.C * D, len, [](int i) { return i; }, red, kbar + bhs * D);
+  pool_rows<D, T, false>(kp + bhs * g.C * D, (T*)nullptr, len, [](int i) { return i; }, [](int i) { return i; },
+                         red, kbar + bhs * D);
 }
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -108,41 +161,135 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-constexpr int kRadixSlots = 4;  // keys per lane for the radix select (local blocks <= 256)
+__device__ __forceinline__ int wave_count(bool p) { return __builtin_popcountll(__builtin_amdgcn_ballot_w64(p)); }
 
-// grid (ceil(nq/QPW), H, B): pooled scores of QPW (<= 4) query blocks against
-// every local block and every valid persistent slot (each candidate's pooled
-// key is read once for the QPW query blocks), then per query block (one wave)
-// the top-k (a wavefront radix select up to 256 local blocks, ranks by
-// counting beyond) and one pooled softmax row.  QPW is the largest of 4, 2,
-// 1 whose LDS (scores, sort keys and flags of every candidate) fits.
-template <int D, int kQPerWg>
-__global__ __launch_bounds__(kThreads) void score_topk_kernel(Geo g, const int32_t* __restrict__ ring_head,
-                                                              const float* __restrict__ qbar,
-                                                              const float* __restrict__ kbar_l,
-                                                              const float* __restrict__ kbar_p,
-                                                              const int32_t* __restrict__ plen,
-                                                              int32_t* __restrict__ topk,
-                                                              float* __restrict__ prow,
-                                                              uint32_t* __restrict__ status) {
+// Order-preserving map of a float to an unsigned key (-0 taken as +0).
+__device__ __forceinline__ unsigned float_key(float x) {
+  unsigned u = x == 0.f ? 0u : __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Wavefront selection of the K largest of n distinct 64-bit keys (hi, lo),
+// lane l holding keys l, l+64, ... (KPL per lane; hi = 0 marks no key).
+// Two radix passes, one bit per ballot round: the K-th largest hi value T,
+// then -- only when several keys share T and not all of them fit -- the
+// largest lo among those.  Returns, per held key, whether it is selected.
+template <int KPL>
+__device__ __forceinline__ void select_top(const unsigned (&hi)[KPL], const unsigned (&lo)[KPL], int K,
+                                           bool (&sel)[KPL]) {
+  unsigned thr = 0u;
+  for (int bit = 31; bit >= 0; --bit) {
+    const unsigned cand = thr | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int u = 0; u < KPL; ++u) cnt += wave_count(hi[u] >= cand);
+    if (cnt >= K) thr = cand;
+  }
+  int n_gt = 0, n_eq = 0;
+#pragma unroll
+  for (int u = 0; u < KPL; ++u) {
+    n_gt += wave_count(hi[u] > thr);
+    n_eq += wave_count(hi[u] == thr);
+  }
+  const int need = K - n_gt;  // >= 1 keys with hi == thr are taken
+  unsigned thr2 = 0u;
+  if (n_eq > need) {
+    for (int bit = 31; bit >= 0; --bit) {
+      const unsigned cand = thr2 | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int u = 0; u < KPL; ++u) cnt += wave_count(hi[u] == thr && lo[u] >= cand);
+      if (cnt >= need) thr2 = cand;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < KPL; ++u) sel[u] = hi[u] > thr || (hi[u] == thr && lo[u] >= thr2);
+}
+
+// XCD-aware remap of a 1-D grid: hardware places workgroup i on XCD i % 8, so
+// each XCD gets a contiguous range of the linear work index (a head's
+// workgroups then share one L2).
+__device__ __forceinline__ int xcd_remap(int total) {
+  const int per_xcd = (total + 7) / 8;
+  return (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+}
+
+constexpr int kScoreThreads = 512;
+
+// Pooling of QPW query blocks by one workgroup: kScoreThreads / QPW threads
+// per block, each summing its row group's rows in order; row groups are then
+// added in order (fixed order, deterministic).
+template <int D, typename T, int QPW> struct QPool {
+  static constexpr int VEC = 16 / sizeof(T);
+  static constexpr int CPR = D / VEC;             // 16-byte chunks per row
+  static constexpr int TPB = kScoreThreads / QPW; // threads per query block
+  static constexpr int NRG = TPB / CPR;           // row groups per block
+  static constexpr int RPT = (64 + NRG - 1) / NRG;
+  static_assert(NRG >= 1 && TPB % CPR == 0, "pooling layout");
+};
+
+// 1-D grid over (B, H, group of QPW query blocks).  qbar is pooled here; the
+// scores, top-K ids, softmax rows and the workgroup's column sums follow.
+template <int D, typename T, int QPW, int KPL>
+__global__ __launch_bounds__(kScoreThreads) void score_topk_kernel(Geo g, const T* __restrict__ q,
+                                                                   const int32_t* __restrict__ ring_head,
+                                                                   const float* __restrict__ kbar_l,
+                                                                   const float* __restrict__ kbar_p,
+                                                                   const int32_t* __restrict__ plen,
+                                                                   int32_t* __restrict__ topk,
+                                                                   float* __restrict__ part,
+                                                                   uint32_t* __restrict__ status) {
+  using P = QPool<D, T, QPW>;
   extern __shared__ float smem[];
   const int W = g.nl + g.S;        // candidates: local blocks, then slots
-  float* qb = smem;                // [4][D]
-  float* sc = qb + kQPerWg * g.D;  // [4][W] scores (-inf for empty slots)
-  int* sel = (int*)(sc + kQPerWg * W);  // [4][nl] 64-bit sort keys, then [4][nl] flags
-  const int i0 = blockIdx.x * kQPerWg, h = blockIdx.y, b = blockIdx.z;
-  const size_t bh = (size_t)b * g.H + h;
+  const int ngrp = (g.nq + QPW - 1) / QPW;
+  const int total = g.B * g.H * ngrp;
+  const int lin = xcd_remap(total);
+  if (lin >= total) return;
+  const int grp = lin % ngrp;
+  const size_t bh = lin / ngrp;
+  float* qb = smem;                         // [QPW][D]
+  float* sc = qb + QPW * D;                 // [QPW][W] scores, then softmax rows (-inf / 0 for empty slots)
+  int* flag = (int*)(sc + QPW * W);         // [QPW][nl] selected flags
+  float* red = (float*)(flag + QPW * g.nl); // [QPW][NRG][D] pooling partial sums
+  const int i0 = grp * QPW;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  for (int x = threadIdx.x; x < kQPerWg * g.D; x += kThreads) {
-    const int qi = i0 + x / g.D;
-    qb[x] = qi < g.nq ? qbar[(bh * g.nq + qi) * g.D + x % g.D] : 0.f;
+  // pool the query blocks: every row load of the thread in flight together
+  {
+    const int blk = threadIdx.x / P::TPB, t = threadIdx.x % P::TPB;
+    const int c = t % P::CPR, rg = t / P::CPR;
+    const int qi = i0 + blk;
+    const BlockExt e = block_ext(g, qi < g.nq ? qi : 0);
+    const int len = qi < g.nq ? e.len : 0;
+    const T* qh = q + bh * g.ct * D;
+    uint4 v[P::RPT];
+#pragma unroll
+    for (int u = 0; u < P::RPT; ++u) {
+      const int r = rg + P::NRG * u;
+      v[u] = r < len ? *reinterpret_cast<const uint4*>(qh + (size_t)block_token(g, e, r) * D + c * P::VEC)
+                     : make_uint4(0, 0, 0, 0);
+    }
+    float acc[P::VEC] = {};
+#pragma unroll
+    for (int u = 0; u < P::RPT; ++u) add_chunk(acc, v[u], T{});
+#pragma unroll
+    for (int k = 0; k < P::VEC; ++k) red[(blk * P::NRG + rg) * D + c * P::VEC + k] = acc[k];
+    __syncthreads();
+    for (int x = threadIdx.x; x < QPW * D; x += kScoreThreads) {
+      const int b2 = x / D, d = x % D;
+      float s = 0.f;
+      for (int k = 0; k < P::NRG; ++k) s += red[(b2 * P::NRG + k) * D + d];
+      const int l2 = i0 + b2 < g.nq ? block_ext(g, i0 + b2).len : 0;
+      qb[x] = l2 > 0 ? s / (float)l2 : 0.f;
+    }
   }
+  const int rh = read_ring_head(ring_head, g.R, status);
   __syncthreads();
-  for (int c = threadIdx.x; c < W; c += kThreads) {
+  for (int c = threadIdx.x; c < W; c += kScoreThreads) {
     const bool loc = c < g.nl;
     const int idx = loc ? c : c - g.nl;
     if (!loc && plen[bh * g.S + idx] <= 0) {
-      for (int k = 0; k < kQPerWg; ++k) sc[k * W + c] = -INFINITY;
+      for (int k = 0; k < QPW; ++k) sc[k * W + c] = -INFINITY;
       continue;
     }
     const float4* kv = reinterpret_cast<const float4*>(loc ? kbar_l + (bh * g.nl + idx) * D
@@ -150,12 +297,12 @@ __global__ __launch_bounds__(kThreads) void score_topk_kernel(Geo g, const int32
     float4 kr[D / 4];  // the candidate's pooled key, all loads in flight together
 #pragma unroll
     for (int d4 = 0; d4 < D / 4; ++d4) kr[d4] = kv[d4];
-    float acc[kQPerWg] = {};
+    float acc[QPW] = {};
 #pragma unroll
     for (int d4 = 0; d4 < D / 4; ++d4) {
       const float4 k4 = kr[d4];
 #pragma unroll
-      for (int k = 0; k < kQPerWg; ++k) {
+      for (int k = 0; k < QPW; ++k) {
         const float4 q4 = reinterpret_cast<const float4*>(qb + k * D)[d4];
         acc[k] = fmaf(q4.x, k4.x, acc[k]);
         acc[k] = fmaf(q4.y, k4.y, acc[k]);
@@ -164,112 +311,102 @@ __global__ __launch_bounds__(kThreads) void score_topk_kernel(Geo g, const int32
       }
     }
 #pragma unroll
-    for (int k = 0; k < kQPerWg; ++k) sc[k * W + c] = acc[k] * g.scale;
+    for (int k = 0; k < QPW; ++k) sc[k * W + c] = acc[k] * g.scale;
   }
   __syncthreads();
   const int i = i0 + w;
-  const bool has = w < kQPerWg && i < g.nq;
-  const float* row = sc + w * W;
-  unsigned long long* key = reinterpret_cast<unsigned long long*>(sel) + w * g.nl;
-  const int rh = read_ring_head(ring_head, g.R, status);
-  // composite key: descending score, then ascending logical index (oldest
-  // chunk first); rank(p) = #local blocks with a larger key
-  if (has) {
-    for (int p = lane; p < g.nl; p += 64) {
-      const int cp = p / g.nq;
-      const unsigned lg = (unsigned)(((cp - rh) % g.R + g.R) % g.R * g.nq + (p - cp * g.nq));
-      unsigned u = row[p] == 0.f ? 0u : __float_as_uint(row[p]);  // -0 ties +0
-      u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);  // order-preserving map to unsigned
-      key[p] = ((unsigned long long)u << 32) | (0xffffffffu - lg);
+  float* row = sc + w * W;
+  if (w < QPW && i < g.nq) {
+    // keys: descending score, then ascending logical index (oldest chunk first)
+    unsigned hi[KPL], lo[KPL];
+#pragma unroll
+    for (int u = 0; u < KPL; ++u) {
+      const int p = lane + 64 * u;
+      hi[u] = 0u;
+      lo[u] = 0u;
+      if (p < g.nl) {
+        const int cp = p / g.nq;
+        hi[u] = float_key(row[p]);
+        lo[u] = 0xffffffffu - (unsigned)(ring_wrap(cp - rh, g.R) * g.nq + (p - cp * g.nq));
+      }
+    }
+    bool on[KPL];
+    select_top<KPL>(hi, lo, g.K, on);
+    int* fl = flag + w * g.nl;
+#pragma unroll
+    for (int u = 0; u < KPL; ++u) {
+      const int p = lane + 64 * u;
+      if (p < g.nl) fl[p] = on[u];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // ascending physical ids: position = selected count below p (ballot prefix)
+    int32_t* out = topk + (bh * g.nq + i) * g.K;
+    int running = 0;
+    for (int p0 = 0; p0 < g.nl; p0 += 64) {
+      const int p = p0 + lane;
+      const bool sp = p < g.nl && fl[p];
+      const unsigned long long m = __builtin_amdgcn_ballot_w64(sp);
+      if (sp) out[running + __builtin_popcountll(m & ((1ull << lane) - 1))] = p;
+      running += __builtin_popcountll(m);
+    }
+    // pooled softmax over valid slots and all local blocks, in place of the scores
+    float mx = -INFINITY;
+    for (int c = lane; c < W; c += 64) mx = fmaxf(mx, row[c]);
+    mx = wave_max(mx);
+    float sum = 0.f;
+    for (int c = lane; c < W; c += 64) sum += row[c] == -INFINITY ? 0.f : expf(row[c] - mx);
+    sum = wave_sum(sum);
+    for (int c = lane; c < W; c += 64) {
+      const float x = row[c];
+      row[c] = x == -INFINITY ? 0.f : expf(x - mx) / sum;
     }
   }
   __syncthreads();
-  if (!has) return;
-  int32_t* out = topk + (bh * g.nq + i) * g.K;
-  if (g.nl <= 64 * kRadixSlots) {
-    // wavefront radix select: the K-th largest key T, one bit at a time from
-    // the top (keep the bit when at least K keys are >= the candidate), with
-    // the keys in registers and the counts by ballot; the keys are distinct,
-    // so exactly K are >= T
-    unsigned long long kr[kRadixSlots];
-#pragma unroll
-    for (int u = 0; u < kRadixSlots; ++u) {
-      const int p = lane + 64 * u;
-      kr[u] = p < g.nl ? key[p] : 0ull;  // 0 is below every key
-    }
-    unsigned long long thr = 0ull;
-    for (int b = 63; b >= 0; --b) {
-      const unsigned long long cand = thr | (1ull << b);
-      int cnt = 0;
-#pragma unroll
-      for (int u = 0; u < kRadixSlots; ++u) cnt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(kr[u] >= cand));
-      if (cnt >= g.K) thr = cand;
-    }
-#pragma unroll
-    for (int u = 0; u < kRadixSlots; ++u) {
-      const int p = lane + 64 * u;
-      if (p < g.nl) sel[g.nl * 2 * kQPerWg + w * g.nl + p] = kr[u] >= thr;
-    }
-  } else {
-    // every lane ranks its own candidates against all keys (LDS broadcast reads)
-    for (int p = lane; p < g.nl; p += 64) {
-      const unsigned long long kp = key[p];
-      int rank = 0;
-      for (int o = 0; o < g.nl; ++o) rank += key[o] > kp;
-      sel[g.nl * 2 * kQPerWg + w * g.nl + p] = rank < g.K;
-    }
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  const int* sl = sel + g.nl * 2 * kQPerWg + w * g.nl;
-  // ascending physical ids: position = selected count below p (ballot prefix)
-  int running = 0;
-  for (int p0 = 0; p0 < g.nl; p0 += 64) {
-    const int p = p0 + lane;
-    const bool on = p < g.nl && sl[p];
-    const unsigned long long m = __builtin_amdgcn_ballot_w64(on);
-    if (on) out[running + __builtin_popcountll(m & ((1ull << lane) - 1))] = p;
-    running += __builtin_popcountll(m);
-  }
-  // pooled softmax over valid slots and all local blocks
-  float mx = -INFINITY;
-  for (int c = lane; c < W; c += 64) mx = fmaxf(mx, row[c]);
-  mx = wave_max(mx);
-  float sum = 0.f;
-  for (int c = lane; c < W; c += 64) sum += row[c] == -INFINITY ? 0.f : expf(row[c] - mx);
-  sum = wave_sum(sum);
-  float* pr = prow + (bh * g.nq + i) * (size_t)W;
-  for (int c = lane; c < W; c += 64) {
-    const float x = row[c];
-    pr[c < g.nl ? g.S + c : c - g.nl] = x == -INFINITY ? 0.f : expf(x - mx) / sum;
+  // this workgroup's column sums (rows in ascending order), in the masses'
+  // layout (column c is local block c or slot c - nl)
+  const int nrows = min(QPW, g.nq - i0);
+  float* mypart = part + (bh * ngrp + grp) * (size_t)W;
+  for (int c = threadIdx.x; c < W; c += kScoreThreads) {
+    float v = 0.f;
+    for (int k = 0; k < nrows; ++k) v += sc[k * W + c];
+    mypart[c < g.nl ? g.S + c : c - g.nl] = v;
   }
 }
 
-// grid (ceil((S+nl)/64), H, B), 256 threads = 64 columns x 4 row groups:
-// mass[j] = sum over query blocks; partial sums over rows rg, rg+4, ... are
-// added in row-group order (fixed, deterministic).
-__global__ __launch_bounds__(kThreads) void mass_kernel(Geo g, const float* __restrict__ prow,
+// grid over (B, H, candidate): mass = the score workgroups' column sums added
+// in ascending workgroup order, kPartBatch loads in flight per thread.
+__global__ __launch_bounds__(kThreads) void mass_kernel(Geo g, int ngrp, const float* __restrict__ part,
                                                         float* __restrict__ mass) {
-  __shared__ float red[4][64];
   const int W = g.S + g.nl;
-  const int col = blockIdx.x * 64 + (threadIdx.x & 63), rg = threadIdx.x >> 6;
-  const size_t bh = (size_t)blockIdx.z * g.H + blockIdx.y;
+  const size_t x = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  if (x >= (size_t)g.B * g.H * W) return;
+  const size_t bh = x / W;
+  const int c = (int)(x - bh * W);
+  const float* hp = part + bh * ngrp * (size_t)W + c;
   float s = 0.f;
-  if (col < W) {
-    const float* r = prow + bh * g.nq * (size_t)W + col;
-    for (int i = rg; i < g.nq; i += 4) s += r[(size_t)i * W];
+  for (int g0 = 0; g0 < ngrp; g0 += kPartBatch) {
+    float v[kPartBatch];
+#pragma unroll
+    for (int u = 0; u < kPartBatch; ++u) v[u] = g0 + u < ngrp ? hp[(size_t)(g0 + u) * W] : 0.f;
+#pragma unroll
+    for (int u = 0; u < kPartBatch; ++u) s += v[u];
   }
-  red[rg][threadIdx.x & 63] = s;
-  __syncthreads();
-  if (rg == 0 && col < W) mass[bh * W + col] = ((red[0][col & 63] + red[1][col & 63]) + red[2][col & 63]) + red[3][col & 63];
+  mass[x] = s;
 }
 
 }  // namespace
 
-constexpr int kScoreLdsMax = 160 * 1024;
+constexpr int kScoreLdsMax = 159 * 1024;  // dynamic LDS
 
-size_t score_lds(const Geo& g, int qpw) { return (size_t)qpw * (g.D + g.nl + g.S + 3 * g.nl) * 4; }
+// LDS of the score kernel at QPW query blocks per workgroup (pooling scratch
+// sized for the largest layout: fp32 rows, 512 / QPW threads per block).
+size_t score_lds(const Geo& g, int qpw) {
+  const int vec = g.dtype == PBSA_BF16 ? 8 : 4;
+  const int nrg = (kScoreThreads / qpw) / (g.D / vec);
+  return ((size_t)qpw * (g.D + g.nl + g.S + g.nl) + (size_t)qpw * nrg * g.D) * 4;
+}
 
 int score_qpw(const Geo& g) {
   for (int q = 4; q > 1; q /= 2)
@@ -277,63 +414,105 @@ int score_qpw(const Geo& g) {
   return 1;
 }
 
-template <int D>
-void pool_slots_d(const Geo& g, const void* k_p, const int32_t* plen, float* kbar, hipStream_t s) {
-  dim3 grid(g.S, g.H, g.B);
-  if (g.dtype == PBSA_BF16)
-    pool_slots_kernel<D, bf16_t><<<grid, kThreads, 0, s>>>(g, (const bf16_t*)k_p, plen, kbar);
-  else
-    pool_slots_kernel<D, float><<<grid, kThreads, 0, s>>>(g, (const float*)k_p, plen, kbar);
+size_t score_workspace(const Geo& g) {
+  const size_t BH = (size_t)g.B * g.H;
+  const size_t ngrp = (g.nq + score_qpw(g) - 1) / score_qpw(g);
+  return ((BH * ngrp * (g.S + g.nl) * 4) + 255) & ~size_t(255);
+}
+
+template <int D, typename T>
+void pool_slots_t(const Geo& g, const void* k_p, const int32_t* plen, float* kbar, hipStream_t s) {
+  pool_slots_kernel<D, T><<<dim3(g.S, g.H, g.B), kThreads, 0, s>>>(g, (const T*)k_p, plen, kbar);
 }
 
 hipError_t launch_pool_slots(const Geo& g, const void* k_p, const int32_t* plen, float* kbar, hipStream_t s) {
   if (g.D == 128)
-    pool_slots_d<128>(g, k_p, plen, kbar, s);
+    g.dtype == PBSA_BF16 ? pool_slots_t<128, bf16_t>(g, k_p, plen, kbar, s) : pool_slots_t<128, float>(g, k_p, plen, kbar, s);
   else
-    pool_slots_d<64>(g, k_p, plen, kbar, s);
+    g.dtype == PBSA_BF16 ? pool_slots_t<64, bf16_t>(g, k_p, plen, kbar, s) : pool_slots_t<64, float>(g, k_p, plen, kbar, s);
   return hipGetLastError();
 }
 
-template <int D>
-hipError_t score_select_d(const Geo& g, const void* q, const void* k_l, const int32_t* ring_head,
-                          const float* kbar_p, const int32_t* plen, int32_t* topk, float* mass, float* kbar_l,
-                          WsScore ws, uint32_t* status, hipStream_t s) {
-  dim3 g1(g.nq + g.nl, g.H, g.B);
-  if (g.dtype == PBSA_BF16)
-    pool_blocks_kernel<D, bf16_t><<<g1, kThreads, 0, s>>>(g, (const bf16_t*)q, (const bf16_t*)k_l, ws.qbar, kbar_l);
+template <int D, typename T, bool APPEND>
+void local_pool_t(const Geo& g, const void* k_new, const void* v_new, const int32_t* ring_head, void* k_l, void* v_l,
+                  float* kbar_l, uint32_t* status, hipStream_t s) {
+  local_pool_kernel<D, T, APPEND><<<dim3(APPEND ? g.nq : g.nl, g.H, g.B), kThreads, 0, s>>>(
+      g, (const T*)k_new, (const T*)v_new, ring_head, (T*)k_l, (T*)v_l, kbar_l, status);
+}
+
+template <bool APPEND>
+hipError_t local_pool(const Geo& g, const void* k_new, const void* v_new, const int32_t* ring_head, void* k_l,
+                      void* v_l, float* kbar_l, uint32_t* status, hipStream_t s) {
+  const bool bf = g.dtype == PBSA_BF16;
+  if (g.D == 128)
+    bf ? local_pool_t<128, bf16_t, APPEND>(g, k_new, v_new, ring_head, k_l, v_l, kbar_l, status, s)
+       : local_pool_t<128, float, APPEND>(g, k_new, v_new, ring_head, k_l, v_l, kbar_l, status, s);
   else
-    pool_blocks_kernel<D, float><<<g1, kThreads, 0, s>>>(g, (const float*)q, (const float*)k_l, ws.qbar, kbar_l);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+    bf ? local_pool_t<64, bf16_t, APPEND>(g, k_new, v_new, ring_head, k_l, v_l, kbar_l, status, s)
+       : local_pool_t<64, float, APPEND>(g, k_new, v_new, ring_head, k_l, v_l, kbar_l, status, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_ring_append(const Geo& g, const void* k_new, const void* v_new, const int32_t* ring_head,
+                              void* k_l, void* v_l, float* kbar_l, uint32_t* status, hipStream_t s) {
+  return local_pool<true>(g, k_new, v_new, ring_head, k_l, v_l, kbar_l, status, s);
+}
+
+hipError_t launch_pool_local(const Geo& g, const void* k_l, float* kbar_l, hipStream_t s) {
+  return local_pool<false>(g, nullptr, nullptr, nullptr, const_cast<void*>(k_l), nullptr, kbar_l, nullptr, s);
+}
+
+template <int D, typename T, int QPW, int KPL>
+hipError_t score_launch(const Geo& g, const void* q, const int32_t* ring_head, const float* kbar_l,
+                        const float* kbar_p, const int32_t* plen, int32_t* topk, float* part, uint32_t* status,
+                        hipStream_t s) {
   static PerDeviceOnce attr;
-  e = attr.run([] {
-    for (const void* f : {(const void*)score_topk_kernel<D, 4>, (const void*)score_topk_kernel<D, 2>,
-                          (const void*)score_topk_kernel<D, 1>}) {
-      const hipError_t r = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kScoreLdsMax);
-      if (r != hipSuccess) return r;
-    }
-    return hipSuccess;
+  hipError_t e = attr.run([] {
+    return hipFuncSetAttribute((const void*)score_topk_kernel<D, T, QPW, KPL>,
+                               hipFuncAttributeMaxDynamicSharedMemorySize, kScoreLdsMax);
   });
   if (e != hipSuccess) return e;
-  const int qpw = score_qpw(g);
-  const size_t shm = score_lds(g, qpw);
-  const dim3 grid((g.nq + qpw - 1) / qpw, g.H, g.B);
-  if (qpw == 4)
-    score_topk_kernel<D, 4><<<grid, kThreads, shm, s>>>(g, ring_head, ws.qbar, kbar_l, kbar_p, plen, topk, ws.prow, status);
-  else if (qpw == 2)
-    score_topk_kernel<D, 2><<<grid, kThreads, shm, s>>>(g, ring_head, ws.qbar, kbar_l, kbar_p, plen, topk, ws.prow, status);
-  else
-    score_topk_kernel<D, 1><<<grid, kThreads, shm, s>>>(g, ring_head, ws.qbar, kbar_l, kbar_p, plen, topk, ws.prow, status);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  mass_kernel<<<dim3((g.S + g.nl + 63) / 64, g.H, g.B), kThreads, 0, s>>>(g, ws.prow, mass);
+  const int ngrp = (g.nq + QPW - 1) / QPW;
+  const int total = g.B * g.H * ngrp;
+  score_topk_kernel<D, T, QPW, KPL><<<(total + 7) / 8 * 8, kScoreThreads, score_lds(g, QPW), s>>>(
+      g, (const T*)q, ring_head, kbar_l, kbar_p, plen, topk, part, status);
   return hipGetLastError();
 }
 
-hipError_t launch_score_select(const Geo& g, const void* q, const void* k_l, const int32_t* ring_head,
-                               const float* kbar_p, const int32_t* plen, int32_t* topk, float* mass,
-                               float* kbar_l, WsScore ws, uint32_t* status, hipStream_t s) {
-  return g.D == 128 ? score_select_d<128>(g, q, k_l, ring_head, kbar_p, plen, topk, mass, kbar_l, ws, status, s)
-                    : score_select_d<64>(g, q, k_l, ring_head, kbar_p, plen, topk, mass, kbar_l, ws, status, s);
+template <int D, typename T, int KPL>
+hipError_t score_qpw_launch(const Geo& g, const void* q, const int32_t* ring_head, const float* kbar_l,
+                            const float* kbar_p, const int32_t* plen, int32_t* topk, float* part, uint32_t* status,
+                            hipStream_t s) {
+  switch (score_qpw(g)) {
+    case 4: return score_launch<D, T, 4, KPL>(g, q, ring_head, kbar_l, kbar_p, plen, topk, part, status, s);
+    case 2: return score_launch<D, T, 2, KPL>(g, q, ring_head, kbar_l, kbar_p, plen, topk, part, status, s);
+    default: return score_launch<D, T, 1, KPL>(g, q, ring_head, kbar_l, kbar_p, plen, topk, part, status, s);
+  }
+}
+
+template <int D, typename T>
+hipError_t score_select_t(const Geo& g, const void* q, const float* kbar_l, const int32_t* ring_head,
+                          const float* kbar_p, const int32_t* plen, int32_t* topk, float* mass, WsScore ws,
+                          uint32_t* status, hipStream_t s) {
+  hipError_t e = g.nl <= 256
+                     ? score_qpw_launch<D, T, 4>(g, q, ring_head, kbar_l, kbar_p, plen, topk, ws.part, status, s)
+                     : score_qpw_launch<D, T, 32>(g, q, ring_head, kbar_l, kbar_p, plen, topk, ws.part, status, s);
+  if (e != hipSuccess) return e;
+  const int ngrp = (g.nq + score_qpw(g) - 1) / score_qpw(g);
+  const size_t n = (size_t)g.B * g.H * (g.S + g.nl);
+  mass_kernel<<<(unsigned)((n + kThreads - 1) / kThreads), kThreads, 0, s>>>(g, ngrp, ws.part, mass);
+  return hipGetLastError();
+}
+
+hipError_t launch_score_select(const Geo& g, const void* q, const float* kbar_l, const int32_t* ring_head,
+                               const float* kbar_p, const int32_t* plen, int32_t* topk, float* mass, WsScore ws,
+                               uint32_t* status, hipStream_t s) {
+  const bool bf = g.dtype == PBSA_BF16;
+  if (g.D == 128)
+    return bf ? score_select_t<128, bf16_t>(g, q, kbar_l, ring_head, kbar_p, plen, topk, mass, ws, status, s)
+              : score_select_t<128, float>(g, q, kbar_l, ring_head, kbar_p, plen, topk, mass, ws, status, s);
+  return bf ? score_select_t<64, bf16_t>(g, q, kbar_l, ring_head, kbar_p, plen, topk, mass, ws, status, s)
+            : score_select_t<64, float>(g, q, kbar_l, ring_head, kbar_p, plen, topk, mass, ws, status, s);
 }
 
 }  // namespace pbsa

@@ -1,4 +1,4 @@
-// Persistent-cache update and local-ring maintenance.
+// Persistent-cache update.
 //
 // The abstract describes a memory that learns to "compress, preserve, and
 // update" persistent blocks; the training algorithm's cache pass updates the
@@ -12,221 +12,300 @@
 // valid one stays, an empty one takes the evicted block of its own index, and
 // the other candidates compete for the remaining S - Z slots.
 //
-// Two launches: a per-(batch, head) decision kernel that ranks candidates and
-// rewrites slot metadata, then a data-movement kernel with one workgroup per
-// slot that copies admitted rows with 16-byte coalesced loads/stores, zero-fills
-// padding and emptied slots, and advances the ring head.
+// Two launches:
+//  1. one workgroup per (batch, head, group of kSlotsPerWg slots).  Every
+//     workgroup decides its head's whole update from the masses (about 1 KB)
+//     -- a two-phase wavefront radix select of the (S - Z)-th largest
+//     candidate key, then ballot prefix counts that pair vacated slots with
+//     admitted blocks -- and then moves the rows of its own slots (16-byte
+//     coalesced copies, zero padding) and their pooled keys.  The new slot
+//     lengths and source ids go to the workspace: every workgroup reads the
+//     old lengths to decide, so none may change them yet.
+//  2. one small workgroup commits lengths and source ids and advances the
+//     ring head and the step counter.
+#include <algorithm>
+#include <type_traits>
+
 #include "common.h"
 
 namespace pbsa {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kSlotsPerWg = 2;
 
-// plan[b,h,s]: -2 keep, -1 empty the slot, p >= 0 fill from physical local block p.
-// Candidates carry a 64-bit key (mass, then the tie order: slots before
-// entrants, lower index first); a candidate is kept when fewer than S - Z
-// valid candidates have a larger key.  Wave 0 then pairs vacated slots with
-// admitted entrants by ballot prefix counts.
-__global__ __launch_bounds__(kThreads) void update_decide_kernel(Geo g, const float* __restrict__ mass,
-                                                                 const int32_t* __restrict__ ring_head,
-                                                                 const int32_t* __restrict__ step_counter,
-                                                                 int32_t* __restrict__ plen,
-                                                                 int32_t* __restrict__ psrc,
-                                                                 int32_t* __restrict__ n_rep,
-                                                                 int32_t* __restrict__ plan,
-                                                                 uint32_t* __restrict__ status) {
-  extern __shared__ unsigned long long sk[];
-  const int NC = g.S + g.nq;
-  unsigned long long* key = sk;            // [NC], 0 for empty slots
-  int* kept = (int*)(sk + NC);             // [NC]
-  int* alist = kept + NC;                  // [nq] admitted entrants in order
-  const int h = blockIdx.x, b = blockIdx.y;
-  const size_t bh = (size_t)b * g.H + h;
-  const int old = read_ring_head(ring_head, g.R, status);
-  const int step_id = read_step(step_counter, g.nq, status);
-  const float* mrow = mass + bh * (g.S + g.nl);
-  for (int c = threadIdx.x; c < NC; c += kThreads) {
-    // sink slots, and evicted blocks reserved for an empty sink slot, are not candidates
-    const bool valid = c < g.S ? (c >= g.Z && plen[bh * g.S + c] > 0)
-                               : !(c - g.S < g.Z && plen[bh * g.S + (c - g.S)] == 0);
-    const float m = c < g.S ? mrow[c] : mrow[g.S + old * g.nq + (c - g.S)];
-    unsigned u = m == 0.f ? 0u : __float_as_uint(m);
-    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    key[c] = valid ? ((unsigned long long)u << 32) | (0xffffffffu - (unsigned)c) : 0ull;
+__device__ __forceinline__ int wave_count(bool p) { return __builtin_popcountll(__builtin_amdgcn_ballot_w64(p)); }
+
+__device__ __forceinline__ unsigned mass_key(float m) {
+  unsigned u = m == 0.f ? 0u : __float_as_uint(m);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Thresholds of the K largest of the keys (hi, lo) held in registers, lane l
+// holding keys l, l+64, ... (hi = 0: not a candidate): the K-th largest hi
+// value thr and, when several keys share it and not all fit, the smallest lo
+// taken among those (thr2; 0 when every key with hi == thr is taken).  A key
+// is among the K largest iff hi > thr || (hi == thr && lo >= thr2).  Two radix
+// passes, one bit per ballot round (see select_top in score.hip).
+template <int KPL>
+__device__ __forceinline__ void radix_threshold(const unsigned (&hi)[KPL], const unsigned (&lo)[KPL], int K,
+                                                unsigned& thr, unsigned& thr2) {
+  thr = 0u;
+  for (int bit = 31; bit >= 0; --bit) {
+    const unsigned cand = thr | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int u = 0; u < KPL; ++u) cnt += wave_count(hi[u] >= cand);
+    if (cnt >= K) thr = cand;
   }
-  __syncthreads();
-  for (int c = threadIdx.x; c < NC; c += kThreads) {
-    const unsigned long long kc = key[c];
-    int rank = 0;
-    for (int o = 0; o < NC; ++o) rank += key[o] > kc;
-    kept[c] = kc != 0ull && rank < g.S - g.Z;
+  int n_gt = 0, n_eq = 0;
+#pragma unroll
+  for (int u = 0; u < KPL; ++u) {
+    n_gt += wave_count(hi[u] > thr);
+    n_eq += wave_count(hi[u] == thr);
   }
-  __syncthreads();
-  if (threadIdx.x >= 64) return;
-  const int lane = threadIdx.x;
-  int n_sink_fill = 0;  // empty sink slots, each filled with the evicted block of its index
-  for (int s0 = 0; s0 < g.Z; s0 += 64) {
-    const int s = s0 + lane;
-    const bool fill = s < g.Z && plen[bh * g.S + s] == 0;
-    n_sink_fill += __builtin_popcountll(__builtin_amdgcn_ballot_w64(fill));
-    if (s < g.Z) {
-      const size_t bs = bh * g.S + s;
-      if (fill) {
-        plan[bs] = old * g.nq + s;
-        plen[bs] = block_ext(g, s).len;
-        psrc[bs] = step_id * g.nq + s;
-      } else {
-        plan[bs] = -2;
-      }
+  const int need = K - n_gt;
+  thr2 = 0u;
+  if (n_eq > need) {
+    for (int bit = 31; bit >= 0; --bit) {
+      const unsigned cand = thr2 | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int u = 0; u < KPL; ++u) cnt += wave_count(hi[u] == thr && lo[u] >= cand);
+      if (cnt >= need) thr2 = cand;
     }
-  }
-  const unsigned long long below = (1ull << lane) - 1;
-  int n_adm = 0;
-  for (int e0 = 0; e0 < g.nq; e0 += 64) {
-    const int e = e0 + lane;
-    const bool on = e < g.nq && kept[g.S + e];
-    const unsigned long long m = __builtin_amdgcn_ballot_w64(on);
-    if (on) alist[n_adm + __builtin_popcountll(m & below)] = e;
-    n_adm += __builtin_popcountll(m);
-  }
-  if (lane == 0) n_rep[bh] = n_adm + n_sink_fill;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  int nvac = 0;
-  for (int s0 = g.Z; s0 < g.S; s0 += 64) {
-    const int s = s0 + lane;
-    const bool in = s < g.S;
-    const bool vac = in && !(key[s] != 0ull && kept[s]);
-    const unsigned long long m = __builtin_amdgcn_ballot_w64(vac);
-    if (in) {
-      const size_t bs = bh * g.S + s;
-      if (!vac) {
-        plan[bs] = -2;
-      } else {
-        const int j = nvac + __builtin_popcountll(m & below);  // rank among vacated slots
-        if (j < n_adm) {
-          const int e = alist[j];
-          plan[bs] = old * g.nq + e;
-          plen[bs] = block_ext(g, e).len;
-          psrc[bs] = step_id * g.nq + e;
-        } else {
-          plan[bs] = -1;
-          plen[bs] = 0;
-          psrc[bs] = kEmptySrc;
-        }
-      }
-    }
-    nvac += __builtin_popcountll(m);
   }
 }
 
-// grid (S, H, B): move rows and pooled keys according to the plan; block
-// (0,0,0) advances the ring head and the step counter.
-template <typename T>
-__global__ __launch_bounds__(kThreads) void update_copy_kernel(Geo g, const int32_t* __restrict__ plan,
+// 1-D grid over (B, H, slot group).  nlen / nsrc: [B,H,S] new lengths and
+// source ids (workspace), committed by update_commit_kernel.
+template <typename T, int KPL>
+__global__ __launch_bounds__(kThreads) void update_move_kernel(Geo g, const float* __restrict__ mass,
+                                                               const int32_t* __restrict__ ring_head,
+                                                               const int32_t* __restrict__ step_counter,
+                                                               const int32_t* __restrict__ plen,
                                                                const T* __restrict__ kl, const T* __restrict__ vl,
                                                                const float* __restrict__ kbar_l,
                                                                T* __restrict__ kp, T* __restrict__ vp,
                                                                float* __restrict__ pkbar,
-                                                               int32_t* __restrict__ ring_head,
-                                                               int32_t* __restrict__ step_counter) {
-  const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const size_t bh = (size_t)b * g.H + h;
-  if (s == 0 && h == 0 && b == 0 && threadIdx.x == 0) {
+                                                               int32_t* __restrict__ nlen,
+                                                               int32_t* __restrict__ nsrc,
+                                                               int32_t* __restrict__ n_rep,
+                                                               uint32_t* __restrict__ status) {
+  extern __shared__ unsigned sk[];
+  const int NC = g.S + g.nq;
+  unsigned* hi = sk;                      // [NC] candidate keys (0: not a candidate)
+  unsigned* lo = hi + NC;                 // [NC]
+  int* alist = (int*)(lo + NC);           // [nq] admitted entrants, ascending
+  __shared__ int s_plan[kSlotsPerWg];     // -2 keep, -1 empty, e >= 0 fill from evicted block e
+  __shared__ unsigned s_thr[2];
+  __shared__ int s_nadm;
+  const int ngrp = (g.S + kSlotsPerWg - 1) / kSlotsPerWg;
+  const int grp = blockIdx.x % ngrp;
+  const size_t bh = blockIdx.x / ngrp;
+  const float* mrow = mass + bh * (g.S + g.nl);
+  const int32_t* prow = plen + bh * g.S;
+  // every mass and length of the head is loaded while the ring head is: the
+  // evicted chunk's masses are picked from LDS once it is known
+  float* mall = (float*)(alist + g.nq);  // [S + nl]
+  int* lall = (int*)(mall + g.S + g.nl);  // [S]
+  for (int c = threadIdx.x; c < g.S + g.nl; c += kThreads) mall[c] = mrow[c];
+  for (int c = threadIdx.x; c < g.S; c += kThreads) lall[c] = prow[c];
+  const int old = read_ring_head(ring_head, g.R, status);
+  const int step_id = read_step(step_counter, g.nq, status);
+  __syncthreads();
+  // sink slots, and evicted blocks reserved for an empty sink slot, are not candidates
+  for (int c = threadIdx.x; c < NC; c += kThreads) {
+    const bool slot = c < g.S;
+    const bool valid = slot ? (c >= g.Z && lall[c] > 0) : !(c - g.S < g.Z && lall[c - g.S] == 0);
+    const float m = slot ? mall[c] : mall[g.S + old * g.nq + (c - g.S)];
+    hi[c] = valid ? mass_key(m) : 0u;
+    lo[c] = 0xffffffffu - (unsigned)c;  // ties: slots before entrants, lower index first
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const unsigned long long below = (1ull << lane) - 1;
+  if (threadIdx.x < 64) {
+    unsigned hr[KPL], lr[KPL];
+    int nvalid = 0;
+#pragma unroll
+    for (int u = 0; u < KPL; ++u) {
+      const int c = lane + 64 * u;
+      hr[u] = c < NC ? hi[c] : 0u;
+      lr[u] = c < NC ? lo[c] : 0u;
+      nvalid += wave_count(hr[u] != 0u);
+    }
+    unsigned thr = 1u, thr2 = 0u;  // every candidate stays when they all fit
+    if (nvalid > g.S - g.Z) radix_threshold<KPL>(hr, lr, g.S - g.Z, thr, thr2);
+    // admitted entrants (kept, and not a sink fill), ascending
+    int n_adm = 0, n_sink_fill = 0;
+    for (int e0 = 0; e0 < g.nq; e0 += 64) {
+      const int e = e0 + lane, c = g.S + e;
+      const bool on = e < g.nq && hi[c] != 0u && (hi[c] > thr || (hi[c] == thr && lo[c] >= thr2));
+      const unsigned long long m = __builtin_amdgcn_ballot_w64(on);
+      if (on) alist[n_adm + __builtin_popcountll(m & below)] = e;
+      n_adm += __builtin_popcountll(m);
+    }
+    for (int s0 = 0; s0 < g.Z; s0 += 64) n_sink_fill += wave_count(s0 + lane < g.Z && lall[s0 + lane] == 0);
+    if (lane == 0) {
+      s_thr[0] = thr;
+      s_thr[1] = thr2;
+      s_nadm = n_adm;
+      if (grp == 0) n_rep[bh] = n_adm + n_sink_fill;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    // plan of this group's slots: rank of a vacated slot among the vacated
+    // slots (ascending) picks its entrant
+    const unsigned thr = s_thr[0], thr2 = s_thr[1];
+    const int s_lo = grp * kSlotsPerWg, s_hi = min(g.S, s_lo + kSlotsPerWg);
+    int nvac = 0;
+    for (int s0 = g.Z; s0 < s_hi; s0 += 64) {
+      const int s = s0 + lane;
+      const bool kept = s < g.S && hi[s] != 0u && (hi[s] > thr || (hi[s] == thr && lo[s] >= thr2));
+      const bool vac = s < s_hi && !kept;
+      const unsigned long long m = __builtin_amdgcn_ballot_w64(vac);
+      if (s >= s_lo && s < s_hi) {
+        const int j = nvac + __builtin_popcountll(m & below);
+        s_plan[s - s_lo] = !vac ? -2 : (j < s_nadm ? alist[j] : -1);
+      }
+      nvac += __builtin_popcountll(m);
+    }
+    // sink slots: a valid one stays, an empty one takes the evicted block of its index
+    for (int s = s_lo + lane; s < min(s_hi, g.Z); s += 64) s_plan[s - s_lo] = lall[s] > 0 ? -2 : s;
+  }
+  __syncthreads();
+  // metadata and rows of this group's slots
+  constexpr int kVec = 16 / sizeof(T);
+  constexpr int kCopyIt = 64 * (128 / kVec) / kThreads;  // 16-byte chunks per thread of a 64-row, d<=128 slot
+  const int cpr = g.D / kVec;
+  for (int k = 0; k < kSlotsPerWg; ++k) {
+    const int s = grp * kSlotsPerWg + k;
+    if (s >= g.S) break;
+    const int e = s_plan[k];
+    if (e == -2) continue;
+    const size_t bs = bh * g.S + s;
+    BlockExt be;
+    int len = 0, off = 0;
+    if (e >= 0) {
+      be = block_ext(g, e);
+      len = be.len;
+      off = old * g.ct;
+    }
+    if (threadIdx.x == 0) {
+      nlen[bs] = len;
+      nsrc[bs] = e >= 0 ? step_id * g.nq + e : kEmptySrc;
+    }
+    for (int d = threadIdx.x; d < g.D; d += kThreads)
+      pkbar[bs * g.D + d] = e >= 0 ? kbar_l[(bh * g.nl + old * g.nq + e) * g.D + d] : 0.f;
+    // the slot's C rows: every load of the slot issued before the first store
+    const size_t dst = bs * (size_t)g.C * g.D;
+    uint4 kv[kCopyIt], vv[kCopyIt];
+#pragma unroll
+    for (int u = 0; u < kCopyIt; ++u) {
+      const int c = threadIdx.x + kThreads * u, r = c / cpr, q = c - r * cpr;
+      kv[u] = make_uint4(0, 0, 0, 0);
+      vv[u] = make_uint4(0, 0, 0, 0);
+      if (r < len) {
+        const size_t src = (bh * g.NL + off + block_token(g, be, r)) * (size_t)g.D + q * kVec;
+        kv[u] = *reinterpret_cast<const uint4*>(kl + src);
+        vv[u] = *reinterpret_cast<const uint4*>(vl + src);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kCopyIt; ++u) {
+      const int c = threadIdx.x + kThreads * u, r = c / cpr, q = c - r * cpr;
+      if (c < g.C * cpr) {
+        *reinterpret_cast<uint4*>(kp + dst + (size_t)r * g.D + q * kVec) = kv[u];
+        *reinterpret_cast<uint4*>(vp + dst + (size_t)r * g.D + q * kVec) = vv[u];
+      }
+    }
+  }
+  // slots this launch leaves alone keep their metadata: mark them unchanged
+  if (threadIdx.x < kSlotsPerWg) {
+    const int s = grp * kSlotsPerWg + threadIdx.x;
+    if (s < g.S && s_plan[threadIdx.x] == -2) nlen[bh * g.S + s] = -1;
+  }
+}
+
+// Grid over (B, H, S): commit new lengths / source ids (-1 length:
+// unchanged); thread 0 advances the ring head and the step counter (no other
+// thread of this launch reads them).
+__global__ __launch_bounds__(kThreads) void update_commit_kernel(Geo g, const int32_t* __restrict__ nlen,
+                                                                 const int32_t* __restrict__ nsrc,
+                                                                 int32_t* __restrict__ plen,
+                                                                 int32_t* __restrict__ psrc,
+                                                                 int32_t* __restrict__ n_rep,
+                                                                 int32_t* __restrict__ ring_head,
+                                                                 int32_t* __restrict__ step_counter) {
+  const size_t n = (size_t)g.B * g.H * g.S;
+  const size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  if (g.S == 0 && i < (size_t)g.B * g.H) n_rep[i] = 0;  // no persistent memory: nothing is admitted
+  if (i < n) {
+    const int l = nlen[i];
+    if (l >= 0) {
+      plen[i] = l;
+      psrc[i] = nsrc[i];
+    }
+  }
+  if (i == 0) {
     *ring_head = (ring_wrap(*ring_head, g.R) + 1) % g.R;
     *step_counter += 1;
-  }
-  const int p = plan[bh * g.S + s];
-  if (p == -2) return;
-  constexpr int kVec = 16 / sizeof(T);           // elements per 16-byte chunk
-  const int cpr = g.D / kVec;                      // chunks per row
-  int len = 0, off = 0;
-  BlockExt e;
-  if (p >= 0) {
-    e = block_ext(g, p % g.nq);
-    len = e.len;
-    off = (p / g.nq) * g.ct;
-  }
-  const size_t dst = (bh * g.S + s) * (size_t)g.C * g.D;
-  for (int d = threadIdx.x; d < g.D; d += kThreads)
-    pkbar[(bh * g.S + s) * g.D + d] = p >= 0 ? kbar_l[(bh * g.nl + p) * g.D + d] : 0.f;
-  for (int c = threadIdx.x; c < g.C * cpr; c += kThreads) {
-    const int r = c / cpr, k = c - r * cpr;
-    uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-    if (r < len) {
-      const size_t src = (bh * g.NL + off + block_token(g, e, r)) * (size_t)g.D + k * kVec;
-      kv = *reinterpret_cast<const uint4*>(kl + src);
-      vv = *reinterpret_cast<const uint4*>(vl + src);
-    }
-    *reinterpret_cast<uint4*>(kp + dst + (size_t)r * g.D + k * kVec) = kv;
-    *reinterpret_cast<uint4*>(vp + dst + (size_t)r * g.D + k * kVec) = vv;
-  }
-}
-
-__global__ void ring_advance_kernel(int32_t* ring_head, int32_t* step_counter, int R) {
-  *ring_head = (ring_wrap(*ring_head, R) + 1) % R;
-  *step_counter += 1;
-}
-
-// grid-stride copy of a [B,H,Nq,D] chunk into the newest ring slot.
-template <typename T>
-__global__ __launch_bounds__(kThreads) void ring_append_kernel(Geo g, const T* __restrict__ kn,
-                                                               const T* __restrict__ vn,
-                                                               const int32_t* __restrict__ ring_head,
-                                                               T* __restrict__ kl, T* __restrict__ vl,
-                                                               uint32_t* __restrict__ status) {
-  constexpr int kVec = 16 / sizeof(T);
-  const int slot = (read_ring_head(ring_head, g.R, status) + g.R - 1) % g.R;
-  const size_t per_bh = (size_t)g.ct * g.D / kVec;   // 16-byte chunks per (b,h)
-  const size_t total = per_bh * g.B * g.H;
-  for (size_t c = (size_t)blockIdx.x * kThreads + threadIdx.x; c < total; c += (size_t)gridDim.x * kThreads) {
-    const size_t bh = c / per_bh, w = c - bh * per_bh;
-    const size_t dst = (bh * g.NL + (size_t)slot * g.ct) * g.D + w * kVec;
-    *reinterpret_cast<uint4*>(kl + dst) = *reinterpret_cast<const uint4*>(kn + c * kVec);
-    *reinterpret_cast<uint4*>(vl + dst) = *reinterpret_cast<const uint4*>(vn + c * kVec);
   }
 }
 
 }  // namespace
 
+size_t update_workspace(const Geo& g) {
+  const size_t n = (size_t)g.B * g.H * g.S * 4;
+  return 2 * ((n + 255) & ~size_t(255));
+}
+
 hipError_t launch_persist_update(const Geo& g, const float* mass, const void* k_l, const void* v_l,
                                  const float* kbar_l, int32_t* ring_head, int32_t* step_counter, void* k_p,
                                  void* v_p, int32_t* plen, int32_t* psrc, float* pkbar, int32_t* n_rep,
-                                 int32_t* plan, uint32_t* status, hipStream_t s) {
+                                 void* ws, uint32_t* status, hipStream_t s) {
+  const size_t n = (size_t)g.B * g.H * g.S * 4;
+  int32_t* nlen = (int32_t*)ws;
+  int32_t* nsrc = (int32_t*)((char*)ws + ((n + 255) & ~size_t(255)));
   const int NC = g.S + g.nq;
-  const size_t shm = (size_t)NC * 8 + (size_t)NC * 4 + (size_t)g.nq * 4;
-  update_decide_kernel<<<dim3(g.H, g.B), kThreads, shm, s>>>(g, mass, ring_head, step_counter, plen, psrc, n_rep,
-                                                              plan, status);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (g.S == 0) {
-    ring_advance_kernel<<<1, 1, 0, s>>>(ring_head, step_counter, g.R);
-    return hipGetLastError();
+  if (g.S > 0) {
+    const size_t shm = (size_t)NC * 8 + (size_t)g.nq * 4 + (size_t)(g.S + g.nl) * 4 + (size_t)g.S * 4;
+    const int grid = g.B * g.H * ((g.S + kSlotsPerWg - 1) / kSlotsPerWg);
+    const bool bf = g.dtype == PBSA_BF16;
+    auto go = [&](auto kpl) {
+      constexpr int KPL = decltype(kpl)::value;
+      static PerDeviceOnce attr;
+      const hipError_t ea = attr.run([] {
+        hipError_t r = hipFuncSetAttribute((const void*)update_move_kernel<bf16_t, KPL>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
+        if (r == hipSuccess)
+          r = hipFuncSetAttribute((const void*)update_move_kernel<float, KPL>,
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
+        return r;
+      });
+      if (ea != hipSuccess) return ea;
+      if (bf)
+        update_move_kernel<bf16_t, KPL><<<grid, kThreads, shm, s>>>(g, mass, ring_head, step_counter, plen,
+                                                                   (const bf16_t*)k_l, (const bf16_t*)v_l, kbar_l,
+                                                                   (bf16_t*)k_p, (bf16_t*)v_p, pkbar, nlen, nsrc,
+                                                                   n_rep, status);
+      else
+        update_move_kernel<float, KPL><<<grid, kThreads, shm, s>>>(g, mass, ring_head, step_counter, plen,
+                                                                  (const float*)k_l, (const float*)v_l, kbar_l,
+                                                                  (float*)k_p, (float*)v_p, pkbar, nlen, nsrc,
+                                                                  n_rep, status);
+      return hipGetLastError();
+    };
+    const hipError_t e = NC <= 256    ? go(std::integral_constant<int, 4>{})
+                         : NC <= 1024 ? go(std::integral_constant<int, 16>{})
+                                      : go(std::integral_constant<int, 64>{});
+    if (e != hipSuccess) return e;
   }
-  dim3 grid(g.S, g.H, g.B);
-  if (g.dtype == PBSA_BF16)
-    update_copy_kernel<bf16_t><<<grid, kThreads, 0, s>>>(g, plan, (const bf16_t*)k_l, (const bf16_t*)v_l, kbar_l,
-                                                        (bf16_t*)k_p, (bf16_t*)v_p, pkbar, ring_head,
-                                                        step_counter);
-  else
-    update_copy_kernel<float><<<grid, kThreads, 0, s>>>(g, plan, (const float*)k_l, (const float*)v_l, kbar_l,
-                                                       (float*)k_p, (float*)v_p, pkbar, ring_head,
-                                                       step_counter);
-  return hipGetLastError();
-}
-
-hipError_t launch_ring_append(const Geo& g, const void* k_new, const void* v_new, const int32_t* ring_head,
-                              void* k_l, void* v_l, uint32_t* status, hipStream_t s) {
-  const size_t chunks = (size_t)g.B * g.H * g.ct * g.D * (g.dtype == PBSA_BF16 ? 2 : 4) / 16;
-  const int blocks = (int)((chunks + kThreads - 1) / kThreads < 2048 ? (chunks + kThreads - 1) / kThreads : 2048);
-  if (g.dtype == PBSA_BF16)
-    ring_append_kernel<bf16_t><<<blocks, kThreads, 0, s>>>(g, (const bf16_t*)k_new, (const bf16_t*)v_new, ring_head,
-                                                          (bf16_t*)k_l, (bf16_t*)v_l, status);
-  else
-    ring_append_kernel<float><<<blocks, kThreads, 0, s>>>(g, (const float*)k_new, (const float*)v_new, ring_head,
-                                                         (float*)k_l, (float*)v_l, status);
+  const size_t nc = std::max((size_t)g.B * g.H * g.S, (size_t)g.B * g.H);
+  update_commit_kernel<<<(unsigned)((nc + kThreads - 1) / kThreads), kThreads, 0, s>>>(g, nlen, nsrc, plen, psrc,
+                                                                                      n_rep, ring_head, step_counter);
   return hipGetLastError();
 }
 

@@ -29,14 +29,18 @@ class PBSACache:
         self.persist_kbar = torch.zeros(s["persist_kbar"], dtype=torch.float32, device=device)
         self.k_local = torch.zeros(s["k_local"], dtype=dt, device=device)
         self.v_local = torch.zeros(s["k_local"], dtype=dt, device=device)
+        self.kbar_local = torch.zeros(s["kbar_local"], dtype=torch.float32, device=device)  # ring metadata
         self.ring_head = torch.zeros(1, dtype=torch.int32, device=device)
         self.step_counter = torch.zeros(1, dtype=torch.int32, device=device)
 
-    STATE = ("k_pers", "v_pers", "persist_len", "persist_src", "persist_kbar", "k_local", "v_local", "ring_head",
-             "step_counter")
+    STATE = ("k_pers", "v_pers", "persist_len", "persist_src", "persist_kbar", "k_local", "v_local", "kbar_local",
+             "ring_head", "step_counter")
 
     def refresh_pooled_keys(self, stream=None):
+        """Recompute the pooled keys of the persistent slots and of the local
+        ring (after their keys were written from outside the library)."""
         api.pbsa_pool_slots(self.plan, self.k_pers, self.persist_len, self.persist_kbar, stream)
+        api.pbsa_pool_local(self.plan, self.k_local, self.kbar_local, stream)
 
     def state_dict(self) -> dict:
         """Host copies of every tensor of the cache state (a checkpoint).
@@ -86,7 +90,6 @@ class SparseForcingAttention:
         self.ws_fwd_mass = api.workspace(p, "fwd_mass", device) if mass == "token" else None
         self.topk_idx = torch.empty(s["topk_idx"], dtype=torch.int32, device=device)
         self.mass = torch.empty(s["mass"], dtype=torch.float32, device=device)
-        self.kbar_local = torch.empty(s["kbar_local"], dtype=torch.float32, device=device)
         self.n_replaced = torch.empty(s["n_replaced"], dtype=torch.int32, device=device)
 
     def new_cache(self) -> PBSACache:
@@ -113,7 +116,8 @@ class SparseForcingAttention:
             if (key_local is None) != (value_local is None):
                 raise ValueError("key_local and value_local go together")
             if key_local is not None:
-                api.pbsa_ring_append(p, key_local, value_local, cache.ring_head, cache.k_local, cache.v_local, stream)
+                api.pbsa_ring_append(p, key_local, value_local, cache.ring_head, cache.k_local, cache.v_local,
+                                     cache.kbar_local, stream)
         else:
             if update:
                 raise ValueError("update=True needs a cache (the persistent state it updates)")
@@ -126,13 +130,14 @@ class SparseForcingAttention:
             cache.persist_src = torch.arange(shp["persist_len"][-1], dtype=torch.int32,
                                              device=query.device).expand(shp["persist_len"]).contiguous()
             cache.persist_kbar = torch.empty(shp["persist_kbar"], dtype=torch.float32, device=query.device)
+            cache.kbar_local = torch.empty(shp["kbar_local"], dtype=torch.float32, device=query.device)
             cache.ring_head = torch.zeros(1, dtype=torch.int32, device=query.device)
             cache.step_counter = torch.zeros(1, dtype=torch.int32, device=query.device)
             cache.refresh_pooled_keys(stream)
         o = torch.empty_like(query)
         lse = torch.empty(api.shapes(p)["lse"], dtype=torch.float32, device=query.device)
-        api.pbsa_score_select(p, query, cache.k_local, cache.ring_head, cache.persist_kbar, cache.persist_len,
-                              self.topk_idx, self.mass, self.kbar_local, self.ws_score, stream)
+        api.pbsa_score_select(p, query, cache.kbar_local, cache.ring_head, cache.persist_kbar, cache.persist_len,
+                              self.topk_idx, self.mass, self.ws_score, stream)
         if update and self.mass_mode == "token":
             api.pbsa_fwd_mass(p, query, cache.k_pers, cache.v_pers, cache.persist_len, cache.k_local, cache.v_local,
                               self.topk_idx, o, lse, self.mass, self.ws_fwd_mass, stream)
@@ -140,7 +145,7 @@ class SparseForcingAttention:
             api.pbsa_fwd(p, query, cache.k_pers, cache.v_pers, cache.persist_len, cache.k_local, cache.v_local,
                          self.topk_idx, o, lse, self.ws_fwd, stream)
         if update:
-            api.pbsa_persist_update(p, self.mass, cache.k_local, cache.v_local, self.kbar_local, cache.ring_head,
+            api.pbsa_persist_update(p, self.mass, cache.k_local, cache.v_local, cache.kbar_local, cache.ring_head,
                                     cache.step_counter, cache.k_pers, cache.v_pers, cache.persist_len,
                                     cache.persist_src, cache.persist_kbar, self.n_replaced, self.ws_update, stream)
         self.last_lse = lse

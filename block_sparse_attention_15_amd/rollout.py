@@ -57,7 +57,6 @@ class DecodeLoop:
         self.os, self.lses = z(s["q"], dt), z(s["lse"], torch.float32)
         self.topks = z(s["topk_idx"], torch.int32)
         self.mass = torch.zeros(s["mass"], dtype=torch.float32, device=device)
-        self.kbar_local = torch.zeros(s["kbar_local"], dtype=torch.float32, device=device)
         self.n_replaced = torch.zeros(s["n_replaced"], dtype=torch.int32, device=device)
         self.ws_score = api.workspace(plan, "score_select", device)
         self.ws_fwd = api.workspace(plan, "fwd", device)
@@ -82,6 +81,10 @@ class DecodeLoop:
     def topk(self):
         return self.topks[-1]
 
+    @property
+    def kbar_local(self):
+        return self.cache.kbar_local
+
     def load_pass(self, i: int, q, k, v):
         """Copy pass i's q, k, v (device tensors of the chunk shape) into its staging buffers;
         i = denoise_passes (or -1) is the cache pass."""
@@ -95,9 +98,9 @@ class DecodeLoop:
 
     def _attend(self, i, stream, token_mass=False):
         c, p = self.cache, self.plan
-        api.pbsa_ring_append(p, self.ks[i], self.vs[i], c.ring_head, c.k_local, c.v_local, stream)
-        api.pbsa_score_select(p, self.qs[i], c.k_local, c.ring_head, c.persist_kbar, c.persist_len, self.topks[i],
-                              self.mass, self.kbar_local, self.ws_score, stream)
+        api.pbsa_ring_append(p, self.ks[i], self.vs[i], c.ring_head, c.k_local, c.v_local, c.kbar_local, stream)
+        api.pbsa_score_select(p, self.qs[i], c.kbar_local, c.ring_head, c.persist_kbar, c.persist_len, self.topks[i],
+                              self.mass, self.ws_score, stream)
         if token_mass:
             api.pbsa_fwd_mass(p, self.qs[i], c.k_pers, c.v_pers, c.persist_len, c.k_local, c.v_local,
                               self.topks[i], self.os[i], self.lses[i], self.mass, self.ws_fwd_mass, stream)
@@ -115,7 +118,7 @@ class DecodeLoop:
         """Append the chunk's t = 0 keys/values, attend, then update the persistent cache."""
         c, p = self.cache, self.plan
         self._attend(-1, stream, token_mass=self.mass_mode == "token")
-        api.pbsa_persist_update(p, self.mass, c.k_local, c.v_local, self.kbar_local, c.ring_head, c.step_counter,
+        api.pbsa_persist_update(p, self.mass, c.k_local, c.v_local, c.kbar_local, c.ring_head, c.step_counter,
                                 c.k_pers, c.v_pers, c.persist_len, c.persist_src, c.persist_kbar, self.n_replaced,
                                 self.ws_update, stream)
 

@@ -114,7 +114,7 @@ typedef struct {
   size_t ws_score_select;
   size_t ws_fwd;
   size_t ws_bwd;
-  size_t ws_persist_update;
+  size_t ws_persist_update;  /* new slot lengths and source ids, committed at the end */
   size_t ws_fwd_mass;
 } pbsa_plan_info;
 
@@ -132,23 +132,36 @@ pbsa_status pbsa_plan(const pbsa_config* cfg, pbsa_plan_info* out);
 pbsa_status pbsa_pool_slots(const pbsa_config* cfg, const void* k_pers, const int32_t* persist_len,
                             float* persist_kbar, void* stream);
 
+/* Pooled keys of every physical local block of the ring: kbar_local[b,h,p]
+ * = mean of the keys of local block p (its valid tokens), float32.  The
+ * pooled local keys are ring metadata, like persist_kbar for the slots:
+ * pbsa_ring_append keeps them for the chunk it writes, so this call is needed
+ * only for a ring whose keys were written from outside the library (or to
+ * rebuild them).  Reading: block scores use mean-pooled keys. */
+pbsa_status pbsa_pool_local(const pbsa_config* cfg, const void* k_local, float* kbar_local, void* stream);
+
 /* Block scoring and top-k selection ("learned top-k selection" on the project
  * page; "dynamically selected local neighborhood" in the abstract), plus the
  * pooled attention masses that drive the persistent update.
- *   q, k_local      inputs (dtype)
+ *   q               input (dtype)
+ *   kbar_local      pooled keys of the local blocks (kept by pbsa_ring_append,
+ *                   or pbsa_pool_local); they must describe the ring's
+ *                   current keys
  *   ring_head       device int32, oldest chunk slot; ties in the top-k go to
  *                   the lower logical index (oldest chunk first)
  *   persist_kbar, persist_len   persistent slot metadata
  *   topk_idx        out [B,H,NQ_blocks,K] physical ids, ascending
  *   mass            out [B,H,S+NL_blocks]: for every query block a softmax of
  *                   scale*qbar.kbar over valid slots and all local blocks,
- *                   summed over query blocks (empty slots get 0)
- *   kbar_local      out [B,H,NL_blocks,D] pooled local keys
- *   ws, ws_bytes    workspace of at least plan.ws_score_select bytes */
-pbsa_status pbsa_score_select(const pbsa_config* cfg, const void* q, const void* k_local,
-                              const int32_t* ring_head, const float* persist_kbar,
-                              const int32_t* persist_len, int32_t* topk_idx, float* mass,
-                              float* kbar_local, void* ws, size_t ws_bytes, void* stream);
+ *                   summed over query blocks in ascending order (empty slots
+ *                   get 0); deterministic
+ *   ws, ws_bytes    workspace of at least plan.ws_score_select bytes (the
+ *                   column sums of the softmax rows of each group of query
+ *                   blocks, written before they are read; no initial contents
+ *                   needed) */
+pbsa_status pbsa_score_select(const pbsa_config* cfg, const void* q, const float* kbar_local,
+                              const int32_t* ring_head, const float* persist_kbar, const int32_t* persist_len,
+                              int32_t* topk_idx, float* mass, void* ws, size_t ws_bytes, void* stream);
 
 /* Sparse attention forward.  Every query token of query block i attends all
  * valid rows of all persistent slots and every token of the K local blocks
@@ -229,9 +242,15 @@ pbsa_status pbsa_persist_update(const pbsa_config* cfg, const float* mass, const
 
 /* Write a new chunk's keys and values ([B,H,Nq,D] each) into the newest local
  * ring slot, physical slot (ring_head + R - 1) mod R, reading ring_head on the
- * device (so one captured graph serves every step of a rollout). */
+ * device (so one captured graph serves every step of a rollout), and pool the
+ * chunk's keys into kbar_local (the rows of that slot's NQ_blocks blocks).
+ * The per-chunk schedule of the paper's algorithm calls it once per pass:
+ * every denoising pass and the cache pass write their own keys and values
+ * into this slot before scoring, so the local window holds the current
+ * chunk. */
 pbsa_status pbsa_ring_append(const pbsa_config* cfg, const void* k_new, const void* v_new,
-                             const int32_t* ring_head, void* k_local, void* v_local, void* stream);
+                             const int32_t* ring_head, void* k_local, void* v_local, float* kbar_local,
+                             void* stream);
 
 /* Device status word: sticky error bits that kernels raise when they find
  * device-resident state out of range, without faulting.  The project page

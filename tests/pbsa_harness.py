@@ -52,10 +52,11 @@ class GpuStep:
         self.ws_update = pb.workspace(p, "persist_update")
         self.ws_fwd = pb.workspace(p, "fwd")
         pb.pbsa_pool_slots(p, self.k_p, self.plen, self.pkbar)
+        pb.pbsa_pool_local(p, self.k_l, self.kbar_l)   # the ring was written from outside the library
 
     def score_select(self):
-        pb.pbsa_score_select(self.p, self.q, self.k_l, self.ring_head, self.pkbar, self.plen, self.topk, self.mass,
-                             self.kbar_l, self.ws_score)
+        pb.pbsa_score_select(self.p, self.q, self.kbar_l, self.ring_head, self.pkbar, self.plen, self.topk, self.mass,
+                             self.ws_score)
 
     def fwd(self, topk=None):
         pb.pbsa_fwd(self.p, self.q, self.k_p, self.v_p, self.plen, self.k_l, self.v_l,

@@ -93,11 +93,11 @@ def test_pointer_checks_before_launch():
     assert _raw_fwd(cfg, o=0x8004) == _lib.PBSA_ERR_ALIGNMENT
     lib = pb.load_library()
     c = pb.make_config(cfg)
-    st = lib.pbsa_score_select(ctypes.byref(c), *(ctypes.c_void_p(0x1000 * (i + 1)) for i in range(8)),
+    st = lib.pbsa_score_select(ctypes.byref(c), *(ctypes.c_void_p(0x1000 * (i + 1)) for i in range(7)),
                                None, 0, None)
     assert st == _lib.PBSA_ERR_WORKSPACE
     p = pb.pbsa_plan(cfg)
-    st = lib.pbsa_score_select(ctypes.byref(c), *(ctypes.c_void_p(0x1000 * (i + 1)) for i in range(8)),
+    st = lib.pbsa_score_select(ctypes.byref(c), *(ctypes.c_void_p(0x1000 * (i + 1)) for i in range(7)),
                                ctypes.c_void_p(0x10000), p.ws_score_select - 1, None)
     assert st == _lib.PBSA_ERR_WORKSPACE
     st = lib.pbsa_persist_update(ctypes.byref(c), *(ctypes.c_void_p(0x1000 * (i + 1)) for i in range(5)),

@@ -291,9 +291,20 @@ def test_ring_append_and_empty_cache_fill():
     kn = torch.randn(st.q.shape, device="cuda").to(st.q.dtype)
     vn = torch.randn(st.q.shape, device="cuda").to(st.q.dtype)
     import block_sparse_attention_15_amd as pb
-    pb.pbsa_ring_append(st.p, kn, vn, st.ring_head, st.k_l, st.v_l)
+    kbar_before = st.kbar_l.clone()
+    pb.pbsa_ring_append(st.p, kn, vn, st.ring_head, st.k_l, st.v_l, st.kbar_l)
     torch.cuda.synchronize()
     slot = (1 + g.R - 1) % g.R
+    # the appended chunk's pooled keys, and only those, are rewritten
+    k_ref = x["k_l"].copy()
+    k_ref[:, :, slot * g.chunk_tokens:(slot + 1) * g.chunk_tokens] = host(kn)
+    want = oracle.pool_local_blocks(k_ref, g)
+    got = host(st.kbar_l)
+    rows = slice(slot * g.n_qblk, (slot + 1) * g.n_qblk)
+    np.testing.assert_allclose(got[:, :, rows], want[:, :, rows], rtol=1e-5, atol=1e-6)
+    keep = np.ones(g.n_lblk, bool)
+    keep[rows] = False
+    np.testing.assert_array_equal(got[:, :, keep], host(kbar_before)[:, :, keep])
     assert torch.equal(st.k_l[:, :, slot * g.chunk_tokens:(slot + 1) * g.chunk_tokens], kn)
     assert torch.equal(st.v_l[:, :, slot * g.chunk_tokens:(slot + 1) * g.chunk_tokens], vn)
     other = 1 - slot

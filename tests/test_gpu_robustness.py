@@ -35,7 +35,7 @@ def test_corrupt_ring_head_is_reduced_and_flagged(bad_head):
         st = GpuStep(cfg, x)
         st.ring_head.fill_(head)
         kn = torch.ones_like(st.q)
-        pb.pbsa_ring_append(st.p, kn, kn, st.ring_head, st.k_l, st.v_l)
+        pb.pbsa_ring_append(st.p, kn, kn, st.ring_head, st.k_l, st.v_l, st.kbar_l)
         st.score_select()
         st.update(2)
         torch.cuda.synchronize()
