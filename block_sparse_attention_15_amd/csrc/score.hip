@@ -25,6 +25,7 @@
 #include "common.h"
 
 namespace pbsa {
+
 namespace {
 
 constexpr int kThreads = 256;
@@ -89,25 +90,6 @@ __device__ __forceinline__ void pool_rows(const T* src, T* dst, int len, SrcFn s
   }
 }
 
-// Copy of a [*, D] row range without pooling (V of the appended chunk).
-template <int D, typename T, typename SrcFn, typename DstFn>
-__device__ __forceinline__ void copy_rows(const T* src, T* dst, int len, SrcFn src_row, DstFn dst_row) {
-  using R = Rows<D, T>;
-  const int c = threadIdx.x % R::CPR, rg = threadIdx.x / R::CPR;
-  uint4 v[R::RPT];
-#pragma unroll
-  for (int u = 0; u < R::RPT; ++u) {
-    const int i = rg + R::NRG * u;
-    v[u] = i < len ? *reinterpret_cast<const uint4*>(src + (size_t)src_row(i) * D + c * R::VEC)
-                   : make_uint4(0, 0, 0, 0);
-  }
-#pragma unroll
-  for (int u = 0; u < R::RPT; ++u) {
-    const int i = rg + R::NRG * u;
-    if (i < len) *reinterpret_cast<uint4*>(dst + (size_t)dst_row(i) * D + c * R::VEC) = v[u];
-  }
-}
-
 // grid (nq, H, B): write block j of a new chunk (k_new / v_new, [B,H,ct,D])
 // into the newest ring slot, (ring_head + R - 1) mod R, and its mean key into
 // kbar_local.  APPEND = false (pbsa_pool_local): grid (nl, H, B), only pool
@@ -127,11 +109,41 @@ __global__ __launch_bounds__(kThreads) void local_pool_kernel(Geo g, const T* __
   if (APPEND) {
     const int slot = (read_ring_head(ring_head, g.R, status) + g.R - 1) % g.R;
     const int off = slot * g.ct;
-    auto tok = [&](int i) { return block_token(g, e, i); };
-    auto dst = [&](int i) { return off + block_token(g, e, i); };
-    copy_rows<D, T>(v_new + bh * g.ct * D, vl + bh * (size_t)g.NL * D, e.len, tok, dst);
-    pool_rows<D, T, true>(k_new + bh * g.ct * D, kb, e.len, tok, dst, red,
-                          kbar_l + (bh * g.nl + slot * g.nq + j) * D);
+    // every K and V row load of the thread is issued before the first store
+    using R = Rows<D, T>;
+    const int c = threadIdx.x % R::CPR, rg = threadIdx.x / R::CPR;
+    const T* ks = k_new + bh * g.ct * D;
+    const T* vs = v_new + bh * g.ct * D;
+    T* vb = vl + bh * (size_t)g.NL * D;
+    int tk[R::RPT];
+    uint4 kv[R::RPT], vv[R::RPT];
+#pragma unroll
+    for (int u = 0; u < R::RPT; ++u) {
+      const int i = rg + R::NRG * u;
+      tk[u] = i < e.len ? block_token(g, e, i) : -1;
+      kv[u] = tk[u] >= 0 ? *reinterpret_cast<const uint4*>(ks + (size_t)tk[u] * D + c * R::VEC) : make_uint4(0, 0, 0, 0);
+      vv[u] = tk[u] >= 0 ? *reinterpret_cast<const uint4*>(vs + (size_t)tk[u] * D + c * R::VEC) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < R::RPT; ++u) {
+      if (tk[u] >= 0) {
+        const size_t d = (size_t)(off + tk[u]) * D + c * R::VEC;
+        *reinterpret_cast<uint4*>(kb + d) = kv[u];
+        *reinterpret_cast<uint4*>(vb + d) = vv[u];
+      }
+    }
+    float acc[R::VEC] = {};
+#pragma unroll
+    for (int u = 0; u < R::RPT; ++u) add_chunk(acc, kv[u], T{});  // rows past the block were loaded as zero
+#pragma unroll
+    for (int k = 0; k < R::VEC; ++k) red[rg * D + c * R::VEC + k] = acc[k];
+    __syncthreads();
+    float* out = kbar_l + (bh * g.nl + slot * g.nq + j) * D;
+    for (int d = threadIdx.x; d < D; d += kThreads) {
+      float sum = 0.f;
+      for (int k = 0; k < R::NRG; ++k) sum += red[k * D + d];
+      out[d] = e.len > 0 ? sum / (float)e.len : 0.f;
+    }
   } else {
     const int off = (j / g.nq) * g.ct;
     pool_rows<D, T, false>(kb, (T*)nullptr, e.len, [&](int i) { return off + block_token(g, e, i); },
@@ -254,6 +266,19 @@ __global__ __launch_bounds__(kScoreThreads) void score_topk_kernel(Geo g, const 
   float* red = (float*)(flag + QPW * g.nl); // [QPW][NRG][D] pooling partial sums
   const int i0 = grp * QPW;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  // the first candidate's pooled key (and slot length) is loaded together
+  // with the query rows: one round of loads
+  const int c0 = threadIdx.x;
+  float4 kr0[D / 4];
+  int len0 = 1;
+  if (c0 < W) {
+    const bool loc = c0 < g.nl;
+    const float4* kv = reinterpret_cast<const float4*>(loc ? kbar_l + (bh * g.nl + c0) * D
+                                                           : kbar_p + (bh * g.S + (c0 - g.nl)) * D);
+#pragma unroll
+    for (int d4 = 0; d4 < D / 4; ++d4) kr0[d4] = kv[d4];
+    if (!loc) len0 = plen[bh * g.S + (c0 - g.nl)];
+  }
   // pool the query blocks: every row load of the thread in flight together
   {
     const int blk = threadIdx.x / P::TPB, t = threadIdx.x % P::TPB;
@@ -285,18 +310,11 @@ __global__ __launch_bounds__(kScoreThreads) void score_topk_kernel(Geo g, const 
   }
   const int rh = read_ring_head(ring_head, g.R, status);
   __syncthreads();
-  for (int c = threadIdx.x; c < W; c += kScoreThreads) {
-    const bool loc = c < g.nl;
-    const int idx = loc ? c : c - g.nl;
-    if (!loc && plen[bh * g.S + idx] <= 0) {
+  auto score_one = [&](int c, const float4 (&kr)[D / 4], int len) {
+    if (c >= g.nl && len <= 0) {
       for (int k = 0; k < QPW; ++k) sc[k * W + c] = -INFINITY;
-      continue;
+      return;
     }
-    const float4* kv = reinterpret_cast<const float4*>(loc ? kbar_l + (bh * g.nl + idx) * D
-                                                           : kbar_p + (bh * g.S + idx) * D);
-    float4 kr[D / 4];  // the candidate's pooled key, all loads in flight together
-#pragma unroll
-    for (int d4 = 0; d4 < D / 4; ++d4) kr[d4] = kv[d4];
     float acc[QPW] = {};
 #pragma unroll
     for (int d4 = 0; d4 < D / 4; ++d4) {
@@ -312,6 +330,17 @@ __global__ __launch_bounds__(kScoreThreads) void score_topk_kernel(Geo g, const 
     }
 #pragma unroll
     for (int k = 0; k < QPW; ++k) sc[k * W + c] = acc[k] * g.scale;
+  };
+  if (c0 < W) score_one(c0, kr0, len0);
+  for (int c = c0 + kScoreThreads; c < W; c += kScoreThreads) {
+    const bool loc = c < g.nl;
+    const int idx = loc ? c : c - g.nl;
+    float4 kr[D / 4];  // the candidate's pooled key, all loads in flight together
+    const float4* kv = reinterpret_cast<const float4*>(loc ? kbar_l + (bh * g.nl + idx) * D
+                                                           : kbar_p + (bh * g.S + idx) * D);
+#pragma unroll
+    for (int d4 = 0; d4 < D / 4; ++d4) kr[d4] = kv[d4];
+    score_one(c, kr, loc ? 1 : plen[bh * g.S + idx]);
   }
   __syncthreads();
   const int i = i0 + w;

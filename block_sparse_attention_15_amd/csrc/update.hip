@@ -176,49 +176,51 @@ __global__ __launch_bounds__(kThreads) void update_move_kernel(Geo g, const floa
     for (int s = s_lo + lane; s < min(s_hi, g.Z); s += 64) s_plan[s - s_lo] = lall[s] > 0 ? -2 : s;
   }
   __syncthreads();
-  // metadata and rows of this group's slots
+  // metadata and rows of this group's slots: every load (pooled keys, K and V
+  // rows of each filled slot) issued before the first store
   constexpr int kVec = 16 / sizeof(T);
   constexpr int kCopyIt = 64 * (128 / kVec) / kThreads;  // 16-byte chunks per thread of a 64-row, d<=128 slot
   const int cpr = g.D / kVec;
+  uint4 kv[kSlotsPerWg][kCopyIt], vv[kSlotsPerWg][kCopyIt];
+  float kb[kSlotsPerWg];
+#pragma unroll
+  for (int k = 0; k < kSlotsPerWg; ++k) {
+    const int s = grp * kSlotsPerWg + k;
+    const int e = s < g.S ? s_plan[k] : -2;
+    const BlockExt be = block_ext(g, e >= 0 ? e : 0);
+    const int len = e >= 0 ? be.len : 0;
+    kb[k] = e >= 0 && (int)threadIdx.x < g.D ? kbar_l[(bh * g.nl + old * g.nq + e) * g.D + threadIdx.x] : 0.f;
+#pragma unroll
+    for (int u = 0; u < kCopyIt; ++u) {
+      const int c = threadIdx.x + kThreads * u, r = c / cpr, q = c - r * cpr;
+      kv[k][u] = make_uint4(0, 0, 0, 0);
+      vv[k][u] = make_uint4(0, 0, 0, 0);
+      if (r < len) {
+        const size_t src = (bh * g.NL + (size_t)old * g.ct + block_token(g, be, r)) * (size_t)g.D + q * kVec;
+        kv[k][u] = *reinterpret_cast<const uint4*>(kl + src);
+        vv[k][u] = *reinterpret_cast<const uint4*>(vl + src);
+      }
+    }
+  }
+#pragma unroll
   for (int k = 0; k < kSlotsPerWg; ++k) {
     const int s = grp * kSlotsPerWg + k;
     if (s >= g.S) break;
     const int e = s_plan[k];
     if (e == -2) continue;
     const size_t bs = bh * g.S + s;
-    BlockExt be;
-    int len = 0, off = 0;
-    if (e >= 0) {
-      be = block_ext(g, e);
-      len = be.len;
-      off = old * g.ct;
-    }
     if (threadIdx.x == 0) {
-      nlen[bs] = len;
+      nlen[bs] = e >= 0 ? block_ext(g, e).len : 0;
       nsrc[bs] = e >= 0 ? step_id * g.nq + e : kEmptySrc;
     }
-    for (int d = threadIdx.x; d < g.D; d += kThreads)
-      pkbar[bs * g.D + d] = e >= 0 ? kbar_l[(bh * g.nl + old * g.nq + e) * g.D + d] : 0.f;
-    // the slot's C rows: every load of the slot issued before the first store
+    if ((int)threadIdx.x < g.D) pkbar[bs * g.D + threadIdx.x] = kb[k];
     const size_t dst = bs * (size_t)g.C * g.D;
-    uint4 kv[kCopyIt], vv[kCopyIt];
-#pragma unroll
-    for (int u = 0; u < kCopyIt; ++u) {
-      const int c = threadIdx.x + kThreads * u, r = c / cpr, q = c - r * cpr;
-      kv[u] = make_uint4(0, 0, 0, 0);
-      vv[u] = make_uint4(0, 0, 0, 0);
-      if (r < len) {
-        const size_t src = (bh * g.NL + off + block_token(g, be, r)) * (size_t)g.D + q * kVec;
-        kv[u] = *reinterpret_cast<const uint4*>(kl + src);
-        vv[u] = *reinterpret_cast<const uint4*>(vl + src);
-      }
-    }
 #pragma unroll
     for (int u = 0; u < kCopyIt; ++u) {
       const int c = threadIdx.x + kThreads * u, r = c / cpr, q = c - r * cpr;
       if (c < g.C * cpr) {
-        *reinterpret_cast<uint4*>(kp + dst + (size_t)r * g.D + q * kVec) = kv[u];
-        *reinterpret_cast<uint4*>(vp + dst + (size_t)r * g.D + q * kVec) = vv[u];
+        *reinterpret_cast<uint4*>(kp + dst + (size_t)r * g.D + q * kVec) = kv[k][u];
+        *reinterpret_cast<uint4*>(vp + dst + (size_t)r * g.D + q * kVec) = vv[k][u];
       }
     }
   }
