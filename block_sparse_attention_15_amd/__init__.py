@@ -13,6 +13,7 @@ from .api import (  # noqa: F401
     pbsa_pool_slots,
     pbsa_pool_local,
     pbsa_score_select,
+    pbsa_score_select_noalloc,
     pbsa_fwd,
     pbsa_fwd_mass,
     pbsa_bwd,

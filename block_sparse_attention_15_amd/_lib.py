@@ -55,6 +55,7 @@ SIGNATURES = {
     "pbsa_pool_slots": [_CFG, _P, _P, _P, _P],
     "pbsa_pool_local": [_CFG, _P, _P, _P],
     "pbsa_score_select": [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "pbsa_score_select_noalloc": [_CFG, _P, _P, _P, _P, _P, _P, _P, _P],
     "pbsa_fwd": [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "pbsa_fwd_mass": [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "pbsa_bwd": [_CFG] + [_P] * 15 + [_P, ctypes.c_size_t, _P],

@@ -163,6 +163,19 @@ def pbsa_score_select(p: Plan, q, kbar_local, ring_head, persist_kbar, persist_l
           _ptr(mass, s["mass"], torch.float32, "mass"), w, nb, _stream(stream))
 
 
+def pbsa_score_select_noalloc(p: Plan, q, kbar_local, ring_head, persist_kbar, persist_len, topk_idx, mass,
+                              stream=None):
+    """pbsa_score_select with the library's static scratch instead of a workspace (allocates nothing)."""
+    s = shapes(p)
+    _call("pbsa_score_select_noalloc", ctypes.byref(p.cfg), _ptr(q, s["q"], p.torch_dtype, "q"),
+          _ptr(kbar_local, s["kbar_local"], torch.float32, "kbar_local"),
+          _ptr(ring_head, s["ring_head"], torch.int32, "ring_head"),
+          _ptr(persist_kbar, s["persist_kbar"], torch.float32, "persist_kbar"),
+          _ptr(persist_len, s["persist_len"], torch.int32, "persist_len"),
+          _ptr(topk_idx, s["topk_idx"], torch.int32, "topk_idx"),
+          _ptr(mass, s["mass"], torch.float32, "mass"), _stream(stream))
+
+
 def pbsa_fwd(p: Plan, q, k_pers, v_pers, persist_len, k_local, v_local, topk_idx, o, lse, ws=None, stream=None):
     s = shapes(p)
     dt = p.torch_dtype

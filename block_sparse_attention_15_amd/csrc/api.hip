@@ -271,6 +271,25 @@ pbsa_status pbsa_score_select(const pbsa_config* cfg, const void* q, const float
   return hip_status(e, "pbsa_score_select");
 }
 
+pbsa_status pbsa_score_select_noalloc(const pbsa_config* cfg, const void* q, const float* kbar_local,
+                                      const int32_t* ring_head, const float* persist_kbar,
+                                      const int32_t* persist_len, int32_t* topk_idx, float* mass, void* stream) {
+  Plan p;
+  pbsa_status st = make_plan(cfg, &p);
+  if (st != PBSA_OK) return st;
+  void* ws = nullptr;
+  size_t cap = 0;
+  hipError_t e = score_static_scratch(&ws, &cap);
+  if (e != hipSuccess) return hip_status(e, "pbsa_score_select_noalloc: static scratch");
+  if (p.info.ws_score_select > cap)
+    return fail(PBSA_ERR_WORKSPACE,
+                "pbsa_score_select_noalloc: this configuration needs %zu bytes of scratch, the static array holds %zu "
+                "(use pbsa_score_select with a workspace)",
+                p.info.ws_score_select, cap);
+  return pbsa_score_select(cfg, q, kbar_local, ring_head, persist_kbar, persist_len, topk_idx, mass, ws,
+                           p.info.ws_score_select, stream);
+}
+
 pbsa_status pbsa_fwd(const pbsa_config* cfg, const void* q, const void* k_pers, const void* v_pers,
                      const int32_t* persist_len, const void* k_local, const void* v_local,
                      const int32_t* topk_idx, void* o, float* lse, void* ws, size_t ws_bytes,

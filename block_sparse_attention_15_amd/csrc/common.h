@@ -187,6 +187,9 @@ struct WsScore {
   float* part;  // [B,H,groups,S+nl]  column sums of each score workgroup's softmax rows
 };
 size_t score_workspace(const Geo& g);
+// Device address and size of the static scratch array of the allocation-free
+// scoring entry point on the current device (looked up once per device).
+hipError_t score_static_scratch(void** out, size_t* bytes);
 hipError_t launch_pool_slots(const Geo& g, const void* k_p, const int32_t* plen, float* kbar, hipStream_t s);
 // Pooled keys of every physical local block of the ring.
 hipError_t launch_pool_local(const Geo& g, const void* k_l, float* kbar_l, hipStream_t s);

@@ -22,9 +22,36 @@
 //     one softmax row, and the column sums of those rows (ascending rows);
 //  2. the masses: per (head, candidate) the sum of the workgroups' column
 //     sums in ascending workgroup order -- deterministic.
+#include <mutex>
+
 #include "common.h"
 
 namespace pbsa {
+
+// Scratch of pbsa_score_select_noalloc: one array per device, held by the
+// library until the process ends.  Host code never uses this name as an
+// address (it is a host-side stand-in there); it takes the device address
+// from hipGetSymbolAddress, once per device, in score_static_scratch().
+constexpr size_t kStaticScratchBytes = size_t(8) << 20;
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+hipError_t score_static_scratch(void** out, size_t* bytes) {
+  static std::mutex mu;
+  static void* addr[PerDeviceOnce::kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= PerDeviceOnce::kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* ptr = nullptr;
+    if ((e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch))) != hipSuccess) return e;
+    addr[dev] = ptr;
+  }
+  *out = addr[dev];
+  *bytes = kStaticScratchBytes;
+  return hipSuccess;
+}
 
 namespace {
 

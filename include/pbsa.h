@@ -163,6 +163,21 @@ pbsa_status pbsa_score_select(const pbsa_config* cfg, const void* q, const float
                               const int32_t* ring_head, const float* persist_kbar, const int32_t* persist_len,
                               int32_t* topk_idx, float* mass, void* ws, size_t ws_bytes, void* stream);
 
+/* pbsa_score_select without a workspace, for callers that cannot allocate
+ * device memory (code under stream capture, tight serving loops, harnesses
+ * that forbid allocation).  Same arguments and results as pbsa_score_select
+ * minus ws / ws_bytes.  Its scratch is a static array of the library, 8 MiB
+ * per device, held until the process ends; a configuration whose
+ * plan.ws_score_select exceeds it is rejected with PBSA_ERR_WORKSPACE and
+ * nothing is launched.  The call allocates nothing.  Every call on a device
+ * shares that device's array, so calls that overlap on one device (on
+ * different streams, or concurrent graphs) race; calls on one stream are
+ * ordered and safe.  The scratch is fully written before it is read, so no
+ * call depends on what an earlier call left in it. */
+pbsa_status pbsa_score_select_noalloc(const pbsa_config* cfg, const void* q, const float* kbar_local,
+                                      const int32_t* ring_head, const float* persist_kbar,
+                                      const int32_t* persist_len, int32_t* topk_idx, float* mass, void* stream);
+
 /* Sparse attention forward.  Every query token of query block i attends all
  * valid rows of all persistent slots and every token of the K local blocks
  * topk_idx[b,h,i,:], with one softmax over that union.  Writes o (dtype) and
