@@ -501,6 +501,170 @@ __global__ __launch_bounds__(kPersThreads, 1) void fwd_pers_kernel(FwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Kernel 1 for the plain forward: the persistent part with the slots' valid
+// rows packed into dense 64-key steps.
+//
+// The valid rows of all slots are numbered consecutively through a row table
+// built in LDS at the start (prefix sums of the slot lengths), so every step
+// is 64 keys -- only the last is partial -- with no per-slot padding (slots of
+// 24 or 48 rows no longer take a whole 32-key tile each) and one barrier per
+// 64 keys instead of one per slot.  Same wave layout as fwd_pers_kernel (8
+// waves x 32 queries, 2 waves per SIMD, 256 contiguous queries per
+// workgroup), same per-tile product and softmax (tile()), rows reaching LDS by
+// LDS-bound loads two steps ahead (three buffers).  (Two 32-query tiles per
+// wave at one wave per SIMD halves the LDS operand reads per MFMA but measured
+// slower: nothing hides a single wave's latencies, and its O-rescale path
+// needs more than the 512 registers.)
+// ---------------------------------------------------------------------------
+constexpr int kP2Waves = 8;
+constexpr int kP2Threads = 64 * kP2Waves;
+constexpr int kP2Rows = 32 * kP2Waves;  // queries per workgroup
+
+template <int D> struct P2 {
+  using Sh = Shape<D>;
+  static constexpr int KEYS = 64;                     // keys per step
+  static constexpr int BUF = 2 * KEYS * Sh::ROWB;     // K rows, then V rows (swizzled)
+  static constexpr int RPK = 1024 / Sh::ROWB;         // rows per 1 KB unit
+  static constexpr int UPT = KEYS * Sh::ROWB / 1024;  // units per tensor per step
+  static constexpr int NU = 2 * UPT / kP2Waves;       // units per wave per step
+  static_assert(NU * kP2Waves == 2 * UPT, "whole units per wave");
+};
+
+// LDS the packed kernel needs besides its step buffers: the row table and
+// the slot prefix sums.
+size_t p2_table_bytes(const Geo& g) { return ((size_t)g.S * g.C + g.S + 1) * 4; }
+
+// LDS-bound loads of packed step t (rows 64t .. 64t+63 of the head's valid
+// rows) into buf; rows past the last valid one repeat it (finite; masked).
+template <int D>
+__device__ __forceinline__ void p2_issue(const FwdArgs& a, size_t bh, int t, int nvalid, const int* rowtab,
+                                         char* buf) {
+  using Sh = Shape<D>;
+  using Q = P2<D>;
+  const Geo& g = a.g;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int rr = lane / Sh::CPR, pos = lane % Sh::CPR;
+  const size_t base = bh * (size_t)g.S * g.C;
+#pragma unroll
+  for (int i = 0; i < Q::NU; ++i) {
+    const int u = wave * Q::NU + i, tsel = u / Q::UPT, tu = u % Q::UPT;  // tsel: 0 K, 1 V
+    const int r = Q::RPK * tu + rr;                                       // row of the step, 0-63
+    const int grow = rowtab[min(Q::KEYS * t + r, nvalid - 1)];
+    const int c = tsel ? swz_v(r, pos, Sh::CPR) : swz_k(r, pos, Sh::CPR);
+    const bf16_t* src = (tsel ? a.vp : a.kp) + (base + grow) * D + c * 8;
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(buf + tsel * Q::KEYS * Sh::ROWB + tu * 1024),
+                                     16, 0, 0);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kP2Threads, 1) void fwd_pers2_kernel(FwdArgs a) {
+  constexpr int NT = 1;
+  using Sh = Shape<D>;
+  using Q = P2<D>;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  __shared__ __attribute__((aligned(1024))) char pb0[Q::BUF];
+  __shared__ __attribute__((aligned(1024))) char pb1[Q::BUF];
+  __shared__ __attribute__((aligned(1024))) char pb2[Q::BUF];
+  const Geo& g = a.g;
+  const int total = g.B * g.H * a.ntiles;
+  const int lin = xcd_remap(total);
+  if (lin >= total) return;
+  const int qt = lin % a.ntiles;
+  const size_t bh = lin / a.ntiles;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, h = lane >> 5, l32 = lane & 31;
+  const int row_w = qt * kP2Rows + 32 * NT * wave;  // first query row of this wave
+  const int ntq = max(0, min(NT, (g.ct - row_w + 31) / 32));
+
+  WaveState<D, NT> st;
+  init_state(st);
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    const int r = row_w + 32 * n + l32;
+    load_q(a.q + (bh * g.ct + min(r, g.ct - 1)) * D, r < g.ct, n, st);
+  }
+  const float c2 = g.scale * 1.4426950408889634f;
+
+  // row table: packed row -> slot * C + row, from prefix sums of the lengths
+  int* rowtab = reinterpret_cast<int*>(smem);  // [S*C]
+  int* pre = rowtab + g.S * g.C;               // [S+1]
+  for (int x = threadIdx.x; x < g.S; x += kP2Threads) pre[x] = min(max(a.plen[bh * g.S + x], 0), g.C);
+  __syncthreads();
+  if (wave == 0) {
+    int run = 0;
+    for (int s0 = 0; s0 < g.S; s0 += 64) {
+      const int sl = s0 + lane;
+      const int n = sl < g.S ? pre[sl] : 0;
+      int x = n;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+      }
+      __builtin_amdgcn_wave_barrier();
+      if (sl < g.S) pre[sl] = run + x - n;
+      run += __shfl(x, 63, 64);
+    }
+    if (lane == 0) pre[g.S] = run;
+  }
+  __syncthreads();
+  const int nvalid = pre[g.S];
+  for (int x = threadIdx.x; x < g.S * g.C; x += kP2Threads) {
+    const int sl = x / g.C, r = x - sl * g.C;
+    const int b0 = pre[sl];
+    if (r < pre[sl + 1] - b0) rowtab[b0 + r] = x;
+  }
+  __syncthreads();
+
+  const int nsteps = (nvalid + Q::KEYS - 1) / Q::KEYS;
+  if (nsteps > 0) {
+    const int last = nsteps - 1;
+    p2_issue<D>(a, bh, 0, nvalid, rowtab, pb0);
+    p2_issue<D>(a, bh, min(1, last), nvalid, rowtab, pb1);
+    vm_barrier<Q::NU>();
+    auto step = [&](int t, char* cur, char* nx2) {
+      p2_issue<D>(a, bh, min(t + 2, last), nvalid, rowtab, nx2);
+      if (t <= last) {
+        // two 32-key halves; each K / V^T operand read feeds both query tiles
+        const int nk = min(Q::KEYS, nvalid - Q::KEYS * t);
+        tile<D, NT, false, true>(cur, cur + Q::KEYS * Sh::ROWB, 0, min(nk, 32), NT, c2, st);
+        if (nk > 32) tile<D, NT, false, true>(cur, cur + Q::KEYS * Sh::ROWB, 32, nk - 32, NT, c2, st);
+      }
+      vm_barrier<Q::NU>();
+    };
+    for (int t = 0; t < nsteps; t += 3) {
+      step(t, pb0, pb2);
+      step(t + 1, pb1, pb0);
+      step(t + 2, pb2, pb1);
+    }
+    __builtin_amdgcn_s_waitcnt(0xF70);  // the last loads land before the workgroup can end
+  }
+
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    if (n < ntq) {
+      const int r = row_w + 32 * n + l32;
+      const float lt = half_sum(st.l[n]);
+      if (r < g.ct) {
+        float* orow = a.o_part + (bh * g.ct + r) * D;
+        const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+#pragma unroll
+        for (int dt = 0; dt < Sh::DT; ++dt) {
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) {
+            const int d0 = 32 * dt + 8 * i4 + 4 * h;
+            *reinterpret_cast<float4*>(orow + d0) =
+                make_float4(st.o[n][dt][4 * i4] * inv, st.o[n][dt][4 * i4 + 1] * inv, st.o[n][dt][4 * i4 + 2] * inv,
+                            st.o[n][dt][4 * i4 + 3] * inv);
+          }
+        }
+        if (h == 0) a.lse_part[bh * g.ct + r] = lt > 0.f ? st.m[n] * kLn2 + logf(lt) : -INFINITY;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Kernel 2: each query block against its K selected local blocks, merged with
 // the persistent partial by log-sum-exp.  8 waves = 4 query blocks x 2 query
 // tiles; per step the workgroup stages 32 rows of each block's current
@@ -699,6 +863,10 @@ hipError_t set_lds(K kernel, size_t bytes) {
   return hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
+// Dynamic LDS of the packed persistent kernel (row table and prefix sums); its
+// three 64-key step buffers are static (96 KB at head_dim 128).
+constexpr int kP2TableMax = 60 * 1024;
+
 template <int D, bool MASS>
 hipError_t launch_d(const FwdArgs& base, hipStream_t s) {
   static PerDeviceOnce attr;
@@ -719,11 +887,22 @@ hipError_t launch_d(const FwdArgs& base, hipStream_t s) {
   }
   const Geo& g = base.g;
   FwdArgs a = base;
-  a.ntiles = (g.ct + kPersRows - 1) / kPersRows;
-  int total = g.B * g.H * a.ntiles;
-  fwd_pers_kernel<D, MASS><<<((total + 7) / 8) * 8, kPersThreads, shm, s>>>(a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
+  int total = 0;
+  const size_t tab2 = p2_table_bytes(g);
+  if (!MASS && g.S > 0 && tab2 <= (size_t)kP2TableMax) {
+    static PerDeviceOnce attr2;
+    e = attr2.run([] { return set_lds(fwd_pers2_kernel<D>, kP2TableMax); });
+    if (e != hipSuccess) return e;
+    a.ntiles = (g.ct + kP2Rows - 1) / kP2Rows;
+    total = g.B * g.H * a.ntiles;
+    fwd_pers2_kernel<D><<<((total + 7) / 8) * 8, kP2Threads, tab2, s>>>(a);
+  } else {
+    a.ntiles = (g.ct + kPersRows - 1) / kPersRows;
+    total = g.B * g.H * a.ntiles;
+    fwd_pers_kernel<D, MASS><<<((total + 7) / 8) * 8, kPersThreads, shm, s>>>(a);
+  }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   a.ntiles = (g.nq + kLocBlocks - 1) / kLocBlocks;
   total = g.B * g.H * a.ntiles;
   if (tab)

@@ -197,7 +197,9 @@ pbsa_status pbsa_fwd(const pbsa_config* cfg, const void* q, const void* k_pers, 
  * softmax probability that t's attention puts on the rows of block j (slot s
  * at index s, physical local block p at S+p).  Every entry is written: empty
  * slots and local blocks that no query block selected get 0, and the entries
- * of a head sum to Nq.  o and lse are as from pbsa_fwd.  Deterministic (fixed
+ * of a head sum to Nq.  o and lse are those of pbsa_fwd up to rounding (this
+ * call adds the persistent keys slot by slot, pbsa_fwd in packed 64-key
+ * steps).  Deterministic (fixed
  * summation order, no atomics).  ws: at least plan.ws_fwd_mass bytes
  * (per-query log-sum-exps over every slot and selected block, about
  * 4*B*H*(S+K)*Nq bytes, plus 4*B*H*NQ_blocks*NL_blocks). */

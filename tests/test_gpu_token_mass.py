@@ -5,7 +5,8 @@ Masses: the GPU sums fp32 exponentials of fp32 scores of the same
 bf16-rounded inputs the oracle takes in float64, so they agree to rounding:
 |gpu - oracle| <= 1e-4 * (1 + |oracle|).  Empty slots and unselected local
 blocks are exactly 0 on both sides.  The forward outputs of pbsa_fwd_mass are
-bitwise those of pbsa_fwd.  Update decisions are exact except counted near
+those of pbsa_fwd up to rounding (the summation order over the persistent
+keys differs).  Update decisions are exact except counted near
 ties of the oracle's masses; the moved state is bit-exact given the decisions.
 """
 import numpy as np
@@ -15,7 +16,7 @@ import torch
 import block_sparse_attention_15_amd as pb
 import oracle
 import synth
-from pbsa_harness import GpuStep, compare_update_decisions, decisions_from_state, dev, host
+from pbsa_harness import GpuStep, compare_update_decisions, decisions_from_state, dev, host, rel_l2
 from test_gpu_parity import SMALL, oracle_select
 
 pytestmark = pytest.mark.gpu
@@ -55,7 +56,11 @@ def test_fwd_mass_small(name):
     o1, l1 = st.o.clone(), st.lse.clone()
     st.fwd_mass(idx)
     torch.cuda.synchronize()
-    assert torch.equal(o1, st.o) and torch.equal(l1, st.lse)
+    # the same attention; the plain forward adds the persistent keys in packed
+    # 64-key steps, this one slot by slot, so they agree to rounding
+    o_a, o_b = host(o1), host(st.o)
+    assert np.abs(o_a - o_b).max() <= 2e-3 and rel_l2(o_b, o_a) <= 1e-3, name
+    np.testing.assert_allclose(host(st.lse), host(l1), rtol=0, atol=1e-4)
     check_mass(host(st.mass), ref, g, sel["topk_idx"], x["persist_len"], name)
 
 
