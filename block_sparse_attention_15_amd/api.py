@@ -68,6 +68,7 @@ def make_config(d: dict) -> _lib.PbsaConfig:
     for k in _CONFIG_KEYS:
         setattr(c, k, d[k])
     c.sink_slots = int(d.get("sink_slots", 0))
+    c.bwd_ds_max_mb = int(d.get("bwd_ds_max_mb", 0))
     dt = d.get("dtype", "bf16")
     c.dtype = {"bf16": _lib.PBSA_BF16, "fp32": _lib.PBSA_FP32}[dt] if isinstance(dt, str) else int(dt)
     return c

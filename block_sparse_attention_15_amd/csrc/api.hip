@@ -141,15 +141,15 @@ pbsa_status make_plan(const pbsa_config* c, Plan* p) {
                 c->sink_slots, g.S, g.nq);
   g.Z = c->sink_slots;
   // The backward stores dS of every (query, persistent key) pair in its
-  // workspace when that takes at most PBSA_BWD_DS_MAX_MB megabytes (default
-  // 8192); above it the dK pass recomputes dS instead (slower, no such
-  // workspace).
+  // workspace when that takes at most bwd_ds_max_mb MiB (0: 8192; -1: never);
+  // above it the dK pass recomputes dS instead (slower, no such workspace).
+  if (c->bwd_ds_max_mb < -1)
+    return fail(PBSA_ERR_INVALID_ARG, "bwd_ds_max_mb (%d) must be -1, 0 or positive", c->bwd_ds_max_mb);
   {
-    double cap_mb = 8192.0;
-    if (const char* env = getenv("PBSA_BWD_DS_MAX_MB")) cap_mb = atof(env);
+    const double cap_mb = c->bwd_ds_max_mb == 0 ? 8192.0 : (double)c->bwd_ds_max_mb;
     g.ds = 0;
     const size_t need = bwd_ds_tile_bytes(g);
-    g.ds = need > 0 && (double)need <= cap_mb * 1048576.0 ? 1 : 0;
+    g.ds = need > 0 && c->bwd_ds_max_mb >= 0 && (double)need <= cap_mb * 1048576.0 ? 1 : 0;
   }
 
   pbsa_plan_info& in = p->info;

@@ -33,8 +33,6 @@
 // natural 16-byte reads (rows of one chunk column) and the transposed
 // ds_read_b64_tr_b16 reads (4 rows x 4 chunks per 16 lanes) avoid bank
 // conflicts.
-#include <mutex>
-
 #include "common.h"
 
 namespace pbsa {
@@ -1123,52 +1121,19 @@ __global__ __launch_bounds__(kKvlThreads, 2) void dkv_local_kernel(BwdArgs a) {
     kvl_pass<D, false>(a, bh, p, kt, sel, slen, steps, nsteps, kv0, kv1);
 }
 
-// The dK/dV kernels run on a second stream of the device, forked from and
-// joined back into the caller's stream by events, so that they fill the CUs
-// the dQ kernels leave idle (the persistent dQ kernel has fewer workgroups
-// than CUs) and each chain's tail.  One side stream and its events per
-// device, default priority; the enqueue is serialised per device because
-// the events are shared.
-struct SideStream {
-  hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, prep = nullptr, dsready = nullptr, join = nullptr;
-  std::mutex mu;
-};
-constexpr int kMaxDevices = 64;
-
-hipError_t side_stream(SideStream** out) {
-  static SideStream per_dev[kMaxDevices];
-  static std::mutex init_mu;
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-  SideStream& ss = per_dev[dev];
-  std::lock_guard<std::mutex> lock(init_mu);
-  if (!ss.s) {
-    if ((e = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking)) != hipSuccess) return e;
-    if ((e = hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming)) != hipSuccess) return e;
-    if ((e = hipEventCreateWithFlags(&ss.prep, hipEventDisableTiming)) != hipSuccess) return e;
-    if ((e = hipEventCreateWithFlags(&ss.dsready, hipEventDisableTiming)) != hipSuccess) return e;
-    if ((e = hipEventCreateWithFlags(&ss.join, hipEventDisableTiming)) != hipSuccess) return e;
-  }
-  *out = &ss;
-  return hipSuccess;
-}
-
 template <typename K>
 hipError_t set_lds(K kernel, size_t bytes) {
   return hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
-// The MFMA kernels: dK/dV on the side stream s2, dQ on the caller's stream s
-// (both already past the preparation).  With g.ds, dq_pers writes the
-// persistent dS tiles that dk_ds reads: the side stream waits for it (event
-// dsready, recorded before the wait is issued) after its dK/dV of the local
-// blocks and its dV of the slots.  Without, the side stream's recomputing dK
-// pass needs nothing from the caller's stream.
+// The MFMA kernels, in order on the caller's stream: dK and dV of the local
+// blocks, dV (and without stored dS tiles, dK) of the persistent slots, dQ
+// of the persistent slots (with g.ds it also writes the dS tiles), dK of the
+// slots from those tiles, then dQ of the local blocks.  (Running the dK/dV
+// kernels on a second stream beside the dQ kernels measured within 1% of this
+// order at the decode shape, so the library keeps to the caller's stream.)
 template <int D>
-hipError_t launch_d(const BwdArgs& base, hipStream_t s, hipStream_t s2, hipEvent_t dsready) {
+hipError_t launch_d(const BwdArgs& base, hipStream_t s) {
   const Geo& g = base.g;
   const size_t shm_dq = 2 * 4 * Sh<D>::TILEB + g.S * 4;      // persistent: 2 x (K,K,V,V), slot lengths
   const size_t tabb = (size_t)kLocBlocks * g.K * 64 * 4;
@@ -1186,23 +1151,23 @@ hipError_t launch_d(const BwdArgs& base, hipStream_t s, hipStream_t s2, hipEvent
   if (e != hipSuccess) return e;
   BwdArgs a = base;
   const bool ds = g.ds && g.S > 0;
-  // side stream: dK, dV of the local blocks, then dV (and without dS tiles,
-  // dK) of the persistent slots
+  // dK, dV of the local blocks, then dV (and without dS tiles, dK) of the
+  // persistent slots
   int total = g.B * g.H * g.nl;
-  dkv_local_kernel<D><<<((total + 7) / 8) * 8, kKvlThreads, shm_kvl, s2>>>(a);
+  dkv_local_kernel<D><<<((total + 7) / 8) * 8, kKvlThreads, shm_kvl, s>>>(a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int kv_tiles = (g.S + kKvSlots - 1) / kKvSlots;
   if (g.S > 0) {
     a.ntiles = kv_tiles;
     total = g.B * g.H * a.ntiles;
-    dkv_pers_kernel<D, true><<<((total + 7) / 8) * 8, kKvThreads, 0, s2>>>(a);
+    dkv_pers_kernel<D, true><<<((total + 7) / 8) * 8, kKvThreads, 0, s>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (!ds) {
-      dkv_pers_kernel<D, false><<<((total + 7) / 8) * 8, kKvThreads, 0, s2>>>(a);
+      dkv_pers_kernel<D, false><<<((total + 7) / 8) * 8, kKvThreads, 0, s>>>(a);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
   }
-  // caller's stream: dq of the persistent slots (writes dq, and the dS tiles)
+  // dq of the persistent slots (writes dq, and the dS tiles)
   a.ntiles = (g.ct + kDqRows - 1) / kDqRows;
   total = g.B * g.H * a.ntiles;
   if (ds)
@@ -1211,15 +1176,13 @@ hipError_t launch_d(const BwdArgs& base, hipStream_t s, hipStream_t s2, hipEvent
     dq_pers_kernel<D, false><<<((total + 7) / 8) * 8, kDqThreads, shm_dq, s>>>(a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ds) {
-    // side stream: dK of the persistent slots from the dS tiles
-    if ((e = hipEventRecord(dsready, s)) != hipSuccess) return e;
-    if ((e = hipStreamWaitEvent(s2, dsready, 0)) != hipSuccess) return e;
+    // dK of the persistent slots from the dS tiles
     a.ntiles = kv_tiles;
     total = g.B * g.H * a.ntiles;
-    dk_ds_kernel<D><<<((total + 7) / 8) * 8, kKvThreads, 0, s2>>>(a);
+    dk_ds_kernel<D><<<((total + 7) / 8) * 8, kKvThreads, 0, s>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  // caller's stream: dq of the local blocks (adds)
+  // dq of the local blocks (adds)
   a.ntiles = (g.nq + kLocBlocks - 1) / kLocBlocks;
   total = g.B * g.H * a.ntiles;
   if (tab)
@@ -1240,35 +1203,21 @@ size_t bwd_ds_tile_bytes(const Geo& g) {
 
 size_t bwd_ds_bytes(const Geo& g) { return g.ds ? bwd_ds_tile_bytes(g) : 0; }
 
-// Fork onto the side stream first: the key-block index and its launch order
-// (read only by the key-outer local kernel) are built there while D, lse2
-// and the geometry table are computed on the caller's stream; the side
-// stream waits for those before its kernels, and the caller's stream waits
-// for the side stream at the end.
+// Preparation (key-block index and its launch order, D and lse*log2(e), the
+// geometry table), then the MFMA kernels, all on the caller's stream.
 hipError_t launch_bwd_mfma(const Geo& g, const void* q, const void* k_p, const void* v_p, const int32_t* plen,
                            const void* k_l, const void* v_l, const int32_t* topk, const void* o, const float* lse,
                            const void* dout, float* dq, float* dk_p, float* dv_p, float* dk_l, float* dv_l,
                            WsBwd ws, hipStream_t s) {
-  SideStream* ss = nullptr;
-  hipError_t e = side_stream(&ss);
-  if (e != hipSuccess) return e;
-  std::lock_guard<std::mutex> lock(ss->mu);
-  const hipStream_t s2 = ss->s;
-  if ((e = hipEventRecord(ss->fork, s)) != hipSuccess) return e;
-  if ((e = hipStreamWaitEvent(s2, ss->fork, 0)) != hipSuccess) return e;
-  if ((e = launch_bwd_index(g, topk, ws, s2)) != hipSuccess) return e;
+  hipError_t e = hipSuccess;
+  if ((e = launch_bwd_index(g, topk, ws, s)) != hipSuccess) return e;
   if ((e = launch_bwd_delta(g, o, dout, lse, ws, s)) != hipSuccess) return e;
   GeoTab tab;
   if ((e = launch_geo_table(g, ws.geo, &tab, s)) != hipSuccess) return e;
-  if ((e = hipEventRecord(ss->prep, s)) != hipSuccess) return e;
-  if ((e = hipStreamWaitEvent(s2, ss->prep, 0)) != hipSuccess) return e;
   BwdArgs a{g, (const bf16_t*)q, (const bf16_t*)k_p, (const bf16_t*)v_p, plen, (const bf16_t*)k_l,
             (const bf16_t*)v_l, topk, lse, ws.delta, ws.lse2, (const bf16_t*)dout, ws.tcount, ws.tlist,
             ws.korder, (const bf16_t*)ws.zrow, (bf16_t*)ws.dsb, dq, dk_p, dv_p, dk_l, dv_l, tab, 0};
-  if ((e = g.D == 128 ? launch_d<128>(a, s, s2, ss->dsready) : launch_d<64>(a, s, s2, ss->dsready)) != hipSuccess)
-    return e;
-  if ((e = hipEventRecord(ss->join, s2)) != hipSuccess) return e;
-  return hipStreamWaitEvent(s, ss->join, 0);
+  return g.D == 128 ? launch_d<128>(a, s) : launch_d<64>(a, s);
 }
 
 }  // namespace pbsa

@@ -23,13 +23,8 @@
  *    synchronizes.  Host pointers (the config, the plan) are read during the
  *    call only.
  *  - Streams: every kernel is enqueued on `stream` (a hipStream_t; NULL means
- *    the default stream), except that pbsa_bwd forks part of its kernels onto
- *    a second stream of the device (created by the library on first use,
- *    default priority) after an event recorded on `stream`, and makes
- *    `stream` wait for them with an event before it returns, so work enqueued
- *    on `stream` afterwards sees all of its results.  No entry point reads
- *    device data back to the host, so each call is asynchronous and may be
- *    captured into a hipGraph (the fork and join become graph dependencies).
+ *    the default stream).  No entry point reads device data back to the host,
+ *    so each call is asynchronous and may be captured into a hipGraph.
  *  - Errors: arguments are checked on the host before any launch.  On failure
  *    nothing is launched, a non-zero pbsa_status is returned and
  *    pbsa_last_error() describes the problem.  A failed kernel launch returns
@@ -99,6 +94,9 @@ typedef struct {
   int32_t sink_slots;                  /* "sink" pattern: the first sink_slots persistent slots
                                           are pinned (see pbsa_persist_update); 0 = none;
                                           at most min(S, NQ_blocks) */
+  int32_t bwd_ds_max_mb;               /* pbsa_bwd stores dS of the persistent keys in its
+                                          workspace while that takes at most this many MiB
+                                          (0 = 8192; -1 = never, the dK pass recomputes dS) */
 } pbsa_config;
 
 /* Derived sizes and workspace requirements (bytes). */
@@ -216,13 +214,10 @@ pbsa_status pbsa_fwd_mass(const pbsa_config* cfg, const void* q, const void* k_p
  * plan.ws_bwd bytes: for bf16 inputs it holds dS of every (query, persistent
  * key) pair as bf16 (about 2*B*H*2S*ceil(Nq/32)*1024 bytes: 1.2 GB at the
  * 30x52 decode shape), which the dq kernel writes and the dk kernel reads
- * instead of recomputing it, when that size is at most PBSA_BWD_DS_MAX_MB
- * megabytes (environment, read by every call; default 8192); above it the dk
- * kernel recomputes dS and the workspace is smaller.  Plan and call with the
- * same setting (a call that finds ws_bytes below its plan's ws_bwd fails with
- * PBSA_ERR_WORKSPACE).  The dk / dv kernels run on the library's second stream
- * of the device (see Streams above); calls on one device are serialised
- * while they are enqueued. */
+ * instead of recomputing it, when that size is at most cfg->bwd_ds_max_mb
+ * MiB (0: 8192; -1: never); otherwise the dk kernel recomputes dS and the
+ * workspace is smaller.  The setting is part of the configuration, so the
+ * plan that sizes the workspace and the call agree. */
 pbsa_status pbsa_bwd(const pbsa_config* cfg, const void* q, const void* k_pers, const void* v_pers,
                      const int32_t* persist_len, const void* k_local, const void* v_local,
                      const int32_t* topk_idx, const void* o, const float* lse, const void* dout,

@@ -66,6 +66,7 @@ def test_plan_footprint_c1():
     (dict(dtype=7), _lib.PBSA_ERR_INVALID_ARG),
     (dict(sink_slots=-1), _lib.PBSA_ERR_INVALID_ARG),
     (dict(sink_slots=85), _lib.PBSA_ERR_INVALID_ARG),     # more than the 84 blocks per chunk
+    (dict(bwd_ds_max_mb=-2), _lib.PBSA_ERR_INVALID_ARG),
 ])
 def test_plan_rejects(bad, status):
     cfg = dict(synth.workload("decode_c1"), **bad)
@@ -124,3 +125,15 @@ def test_ring_head_reduction_cpu_build(tmp_path):
     assert r.returncode == 0, r.stderr[-2000:]
     out = subprocess.run([exe], capture_output=True, text=True)
     assert out.returncode == 0 and out.stdout.strip() == "ok", out.stdout
+
+
+def test_plan_bwd_ds_cap_is_part_of_the_config():
+    """The backward's stored-dS workspace follows the config's cap: default
+    and generous caps store it, -1 or a cap below the tiles' size does not."""
+    base = synth.workload("decode_c1")
+    stored = pb.pbsa_plan(base).ws_bwd
+    assert stored > 10 ** 9
+    assert pb.pbsa_plan(dict(base, bwd_ds_max_mb=100000)).ws_bwd == stored
+    small = pb.pbsa_plan(dict(base, bwd_ds_max_mb=-1)).ws_bwd
+    assert small < 10 ** 8
+    assert pb.pbsa_plan(dict(base, bwd_ds_max_mb=1)).ws_bwd == small

@@ -1,8 +1,8 @@
 """The backward captured into a HIP graph and replayed.
 
-`pbsa_bwd` forks its dK/dV kernels onto a second stream of the device and
-joins them back with events; under stream capture that fork/join becomes
-graph dependencies.  The captured graph is replayed three times, with the
+`pbsa_bwd` enqueues its preparation and five MFMA kernels on the caller's
+stream, which stream capture records in order.  The captured graph is
+replayed three times, with the
 outputs refilled with NaN (eager work) and a synchronisation between
 replays, and every replay must equal the eager call bit for bit (the
 backward is deterministic: one owner per output element, fixed order).

@@ -162,13 +162,12 @@ def test_fwd_bwd_empty_slots(name):
 
 
 @pytest.mark.parametrize("name", ["ragged_bf16", "ragged_bf16_d64_b2", "block344_bf16", "tiny_bf16"])
-def test_bwd_recompute_path(name, monkeypatch):
-    """With the persistent dS tiles capped to 0 MB (PBSA_BWD_DS_MAX_MB) the
+def test_bwd_recompute_path(name):
+    """With the persistent dS tiles switched off (bwd_ds_max_mb = -1) the
     backward's dK pass recomputes dS instead of reading it from the
     workspace: the same gradients from a smaller workspace."""
-    cfg = SMALL[name]
-    stored = pb.pbsa_plan(cfg).ws_bwd
-    monkeypatch.setenv("PBSA_BWD_DS_MAX_MB", "0")
+    stored = pb.pbsa_plan(SMALL[name]).ws_bwd
+    cfg = dict(SMALL[name], bwd_ds_max_mb=-1)
     assert pb.pbsa_plan(cfg).ws_bwd < stored
     x = synth.make_step_inputs(cfg)
     x["persist_len"][..., 1] = 0
