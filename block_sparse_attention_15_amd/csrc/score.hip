@@ -17,11 +17,14 @@
 // synchronisation between workgroups:
 //  1. per workgroup QPW query blocks of one head (512 threads): pool them
 //     (16-byte row loads, fixed-order reduction), score them against every
-//     candidate (each candidate's pooled key read once for the QPW blocks),
-//     per query block (one wave) a two-phase radix select of the top K and
-//     one softmax row, and the column sums of those rows (ascending rows);
+//     candidate (the candidates' pooled keys loaded coalesced, all loads of
+//     the first chunks issued with the query rows, and staged through LDS a
+//     chunk at a time; one thread per (candidate, query block)), per query
+//     block (one wave) a two-phase radix select of the top K and one softmax
+//     row, and the column sums of those rows (ascending rows);
 //  2. the masses: per (head, candidate) the sum of the workgroups' column
 //     sums in ascending workgroup order -- deterministic.
+#include <algorithm>
 #include <mutex>
 
 #include "common.h"
@@ -254,6 +257,8 @@ __device__ __forceinline__ int xcd_remap(int total) {
 }
 
 constexpr int kScoreThreads = 512;
+constexpr int kScoreChunk = 128;      // candidate keys staged in LDS at a time
+constexpr int kScoreChunksHeld = 3;   // chunks whose loads are issued up front (registers)
 
 // Pooling of QPW query blocks by one workgroup: kScoreThreads / QPW threads
 // per block, each summing its row group's rows in order; row groups are then
@@ -287,25 +292,52 @@ __global__ __launch_bounds__(kScoreThreads) void score_topk_kernel(Geo g, const 
   if (lin >= total) return;
   const int grp = lin % ngrp;
   const size_t bh = lin / ngrp;
-  float* qb = smem;                         // [QPW][D]
-  float* sc = qb + QPW * D;                 // [QPW][W] scores, then softmax rows (-inf / 0 for empty slots)
+  constexpr int QST = D + 4;                // LDS row stride (floats) of pooled queries and keys:
+                                            // consecutive rows start in different banks
+  float* qb = smem;                         // [QPW][QST]
+  float* sc = qb + QPW * QST;               // [QPW][W] scores, then softmax rows (-inf / 0 for empty slots)
   int* flag = (int*)(sc + QPW * W);         // [QPW][nl] selected flags
-  float* red = (float*)(flag + QPW * g.nl); // [QPW][NRG][D] pooling partial sums
+  float* red = (float*)(flag + QPW * g.nl); // [QPW][NRG][D] pooling partial sums, then:
+  float* kch = red;                         // [kScoreChunk][QST] a chunk of the candidates' pooled keys
+  int* clen = (int*)(kch + kScoreChunk * QST);  // [kScoreChunk] their slot lengths (1: local block)
   const int i0 = grp * QPW;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  // the first candidate's pooled key (and slot length) is loaded together
-  // with the query rows: one round of loads
-  const int c0 = threadIdx.x;
-  float4 kr0[D / 4];
-  int len0 = 1;
-  if (c0 < W) {
-    const bool loc = c0 < g.nl;
-    const float4* kv = reinterpret_cast<const float4*>(loc ? kbar_l + (bh * g.nl + c0) * D
-                                                           : kbar_p + (bh * g.S + (c0 - g.nl)) * D);
+  // Candidates' pooled keys reach LDS kScoreChunk rows at a time, loaded
+  // coalesced (consecutive lanes read consecutive 16-byte pieces of a row).
+  // The loads of the first kScoreChunksHeld chunks are all issued up front,
+  // into registers, together with the query rows: one round of global loads
+  // for up to kScoreChunksHeld * kScoreChunk candidates; later chunks (larger
+  // local windows) are loaded when their turn comes.
+  constexpr int PPR = D / 4;                  // float4 pieces per row
+  constexpr int RPP = kScoreThreads / PPR;    // rows per pass
+  constexpr int NP = kScoreChunk / RPP;       // float4 loads per thread per chunk
+  static_assert(NP * RPP == kScoreChunk, "chunk layout");
+  const int pc = threadIdx.x % PPR, pr = threadIdx.x / PPR;
+  float4 kreg[kScoreChunksHeld][NP];
+  int lreg[kScoreChunksHeld];
+  auto load_chunk = [&](int cb, float4 (&kr)[NP], int& lr) {
 #pragma unroll
-    for (int d4 = 0; d4 < D / 4; ++d4) kr0[d4] = kv[d4];
-    if (!loc) len0 = plen[bh * g.S + (c0 - g.nl)];
-  }
+    for (int u = 0; u < NP; ++u) {
+      const int c = cb + pr + RPP * u;
+      kr[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (c < W) {
+        const float* src = c < g.nl ? kbar_l + (bh * g.nl + c) * D : kbar_p + (bh * g.S + (c - g.nl)) * D;
+        kr[u] = reinterpret_cast<const float4*>(src)[pc];
+      }
+    }
+    const int c = cb + (int)threadIdx.x;
+    lr = 0;
+    if (threadIdx.x < kScoreChunk) lr = c < g.nl ? 1 : (c < W ? plen[bh * g.S + (c - g.nl)] : 0);
+  };
+  auto store_chunk = [&](const float4 (&kr)[NP], int lr) {
+#pragma unroll
+    for (int u = 0; u < NP; ++u) reinterpret_cast<float4*>(kch + (pr + RPP * u) * QST)[pc] = kr[u];
+    if (threadIdx.x < kScoreChunk) clen[threadIdx.x] = lr;
+  };
+#pragma unroll
+  for (int h = 0; h < kScoreChunksHeld; ++h)
+    if (h * kScoreChunk < W) load_chunk(h * kScoreChunk, kreg[h], lreg[h]);
+  const int rh_raw = *ring_head;  // in flight with the other loads, checked after the pooling
   // pool the query blocks: every row load of the thread in flight together
   {
     const int blk = threadIdx.x / P::TPB, t = threadIdx.x % P::TPB;
@@ -332,42 +364,49 @@ __global__ __launch_bounds__(kScoreThreads) void score_topk_kernel(Geo g, const 
       float s = 0.f;
       for (int k = 0; k < P::NRG; ++k) s += red[(b2 * P::NRG + k) * D + d];
       const int l2 = i0 + b2 < g.nq ? block_ext(g, i0 + b2).len : 0;
-      qb[x] = l2 > 0 ? s / (float)l2 : 0.f;
+      qb[b2 * QST + d] = l2 > 0 ? s / (float)l2 : 0.f;
     }
   }
-  const int rh = read_ring_head(ring_head, g.R, status);
-  __syncthreads();
-  auto score_one = [&](int c, const float4 (&kr)[D / 4], int len) {
-    if (c >= g.nl && len <= 0) {
-      for (int k = 0; k < QPW; ++k) sc[k * W + c] = -INFINITY;
-      return;
-    }
-    float acc[QPW] = {};
+  if ((unsigned)rh_raw >= (unsigned)g.R) atomicOr(status, kStatusRingHead);
+  const int rh = ring_wrap(rh_raw, g.R);
+  __syncthreads();  // the pooling sums are read: their LDS takes the key chunks
+  // scores: one thread per (candidate, query block), d in ascending order
+  auto score_chunk = [&](int cb) {
+    for (int x = threadIdx.x; x < kScoreChunk * QPW; x += kScoreThreads) {
+      const int r = x / QPW, k = x - r * QPW, c = cb + r;
+      if (c >= W) break;
+      float sv = -INFINITY;  // empty slot
+      if (c < g.nl || clen[r] > 0) {
+        const float4* kr = reinterpret_cast<const float4*>(kch + r * QST);
+        const float4* qr = reinterpret_cast<const float4*>(qb + k * QST);
+        float acc = 0.f;
 #pragma unroll
-    for (int d4 = 0; d4 < D / 4; ++d4) {
-      const float4 k4 = kr[d4];
-#pragma unroll
-      for (int k = 0; k < QPW; ++k) {
-        const float4 q4 = reinterpret_cast<const float4*>(qb + k * D)[d4];
-        acc[k] = fmaf(q4.x, k4.x, acc[k]);
-        acc[k] = fmaf(q4.y, k4.y, acc[k]);
-        acc[k] = fmaf(q4.z, k4.z, acc[k]);
-        acc[k] = fmaf(q4.w, k4.w, acc[k]);
+        for (int d4 = 0; d4 < D / 4; ++d4) {
+          const float4 k4 = kr[d4], q4 = qr[d4];
+          acc = fmaf(q4.x, k4.x, acc);
+          acc = fmaf(q4.y, k4.y, acc);
+          acc = fmaf(q4.z, k4.z, acc);
+          acc = fmaf(q4.w, k4.w, acc);
+        }
+        sv = acc * g.scale;
       }
+      sc[k * W + c] = sv;
     }
-#pragma unroll
-    for (int k = 0; k < QPW; ++k) sc[k * W + c] = acc[k] * g.scale;
   };
-  if (c0 < W) score_one(c0, kr0, len0);
-  for (int c = c0 + kScoreThreads; c < W; c += kScoreThreads) {
-    const bool loc = c < g.nl;
-    const int idx = loc ? c : c - g.nl;
-    float4 kr[D / 4];  // the candidate's pooled key, all loads in flight together
-    const float4* kv = reinterpret_cast<const float4*>(loc ? kbar_l + (bh * g.nl + idx) * D
-                                                           : kbar_p + (bh * g.S + idx) * D);
 #pragma unroll
-    for (int d4 = 0; d4 < D / 4; ++d4) kr[d4] = kv[d4];
-    score_one(c, kr, loc ? 1 : plen[bh * g.S + idx]);
+  for (int h = 0; h < kScoreChunksHeld; ++h) {
+    if (h * kScoreChunk >= W) break;
+    if (h > 0) __syncthreads();  // the previous chunk is scored
+    store_chunk(kreg[h], lreg[h]);
+    __syncthreads();
+    score_chunk(h * kScoreChunk);
+  }
+  for (int cb = kScoreChunksHeld * kScoreChunk; cb < W; cb += kScoreChunk) {
+    load_chunk(cb, kreg[0], lreg[0]);
+    __syncthreads();
+    store_chunk(kreg[0], lreg[0]);
+    __syncthreads();
+    score_chunk(cb);
   }
   __syncthreads();
   const int i = i0 + w;
@@ -412,12 +451,13 @@ __global__ __launch_bounds__(kScoreThreads) void score_topk_kernel(Geo g, const 
     for (int c = lane; c < W; c += 64) mx = fmaxf(mx, row[c]);
     mx = wave_max(mx);
     float sum = 0.f;
-    for (int c = lane; c < W; c += 64) sum += row[c] == -INFINITY ? 0.f : expf(row[c] - mx);
-    sum = wave_sum(sum);
-    for (int c = lane; c < W; c += 64) {
-      const float x = row[c];
-      row[c] = x == -INFINITY ? 0.f : expf(x - mx) / sum;
+    for (int c = lane; c < W; c += 64) {  // each exponential once, kept in the row
+      const float x = row[c], e = x == -INFINITY ? 0.f : expf(x - mx);
+      row[c] = e;
+      sum += e;
     }
+    sum = wave_sum(sum);
+    for (int c = lane; c < W; c += 64) row[c] = row[c] / sum;
   }
   __syncthreads();
   // this workgroup's column sums (rows in ascending order), in the masses'
@@ -456,12 +496,15 @@ __global__ __launch_bounds__(kThreads) void mass_kernel(Geo g, int ngrp, const f
 
 constexpr int kScoreLdsMax = 159 * 1024;  // dynamic LDS
 
-// LDS of the score kernel at QPW query blocks per workgroup (pooling scratch
-// sized for the largest layout: fp32 rows, 512 / QPW threads per block).
+// LDS of the score kernel at QPW query blocks per workgroup: pooled queries,
+// scores, flags, then the larger of the pooling scratch (sized for the
+// largest layout: fp32 rows, 512 / QPW threads per block) and one chunk of
+// candidate keys with their lengths.
 size_t score_lds(const Geo& g, int qpw) {
   const int vec = g.dtype == PBSA_BF16 ? 8 : 4;
   const int nrg = (kScoreThreads / qpw) / (g.D / vec);
-  return ((size_t)qpw * (g.D + g.nl + g.S + g.nl) + (size_t)qpw * nrg * g.D) * 4;
+  const size_t pool = (size_t)qpw * nrg * g.D, chunk = (size_t)kScoreChunk * (g.D + 4 + 1);
+  return ((size_t)qpw * (g.D + 4 + g.nl + g.S + g.nl) + std::max(pool, chunk)) * 4;
 }
 
 int score_qpw(const Geo& g) {

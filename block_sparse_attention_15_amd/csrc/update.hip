@@ -15,10 +15,11 @@
 // Two launches:
 //  1. one workgroup per (batch, head, group of kSlotsPerWg slots).  Every
 //     workgroup decides its head's whole update from the masses (about 1 KB)
-//     -- a two-phase wavefront radix select of the (S - Z)-th largest
-//     candidate key, then ballot prefix counts that pair vacated slots with
-//     admitted blocks -- and then moves the rows of its own slots (16-byte
-//     coalesced copies, zero padding) and their pooled keys.  The new slot
+//     in one wavefront, from registers -- a two-phase radix select of the
+//     (S - Z)-th largest candidate key, then ballot prefix counts that pair
+//     vacated slots with admitted blocks -- and then moves the rows of its own
+//     slots (16-byte coalesced copies, zero padding; the ring token of each
+//     row computed once, into LDS) and their pooled keys.  The new slot
 //     lengths and source ids go to the workspace: every workgroup reads the
 //     old lengths to decide, so none may change them yet.
 //  2. one small workgroup commits lengths and source ids and advances the
@@ -98,8 +99,6 @@ __global__ __launch_bounds__(kThreads) void update_move_kernel(Geo g, const floa
   unsigned* lo = hi + NC;                 // [NC]
   int* alist = (int*)(lo + NC);           // [nq] admitted entrants, ascending
   __shared__ int s_plan[kSlotsPerWg];     // -2 keep, -1 empty, e >= 0 fill from evicted block e
-  __shared__ unsigned s_thr[2];
-  __shared__ int s_nadm;
   const int ngrp = (g.S + kSlotsPerWg - 1) / kSlotsPerWg;
   const int grp = blockIdx.x % ngrp;
   const size_t bh = blockIdx.x / ngrp;
@@ -125,7 +124,9 @@ __global__ __launch_bounds__(kThreads) void update_move_kernel(Geo g, const floa
   __syncthreads();
   const int lane = threadIdx.x & 63;
   const unsigned long long below = (1ull << lane) - 1;
+  __shared__ int s_tok[kSlotsPerWg][64];  // ring token of each row of each filled slot's block
   if (threadIdx.x < 64) {
+    // wave 0 decides from registers: candidate c = lane + 64 u
     unsigned hr[KPL], lr[KPL];
     int nvalid = 0;
 #pragma unroll
@@ -137,43 +138,53 @@ __global__ __launch_bounds__(kThreads) void update_move_kernel(Geo g, const floa
     }
     unsigned thr = 1u, thr2 = 0u;  // every candidate stays when they all fit
     if (nvalid > g.S - g.Z) radix_threshold<KPL>(hr, lr, g.S - g.Z, thr, thr2);
-    // admitted entrants (kept, and not a sink fill), ascending
-    int n_adm = 0, n_sink_fill = 0;
-    for (int e0 = 0; e0 < g.nq; e0 += 64) {
-      const int e = e0 + lane, c = g.S + e;
-      const bool on = e < g.nq && hi[c] != 0u && (hi[c] > thr || (hi[c] == thr && lo[c] >= thr2));
-      const unsigned long long m = __builtin_amdgcn_ballot_w64(on);
-      if (on) alist[n_adm + __builtin_popcountll(m & below)] = e;
-      n_adm += __builtin_popcountll(m);
+    // admitted entrants (kept, and not a sink fill) listed ascending; the
+    // rank of a vacated slot among the vacated slots (ascending) picks its
+    // entrant
+    const int s_lo = grp * kSlotsPerWg, s_hi = min(g.S, s_lo + kSlotsPerWg);
+    int n_adm = 0, nvac = 0, vrank[kSlotsPerWg];
+#pragma unroll
+    for (int k = 0; k < kSlotsPerWg; ++k) vrank[k] = -1;
+#pragma unroll
+    for (int u = 0; u < KPL; ++u) {
+      const int c = lane + 64 * u;
+      const bool kept = hr[u] != 0u && (hr[u] > thr || (hr[u] == thr && lr[u] >= thr2));
+      const bool adm = c >= g.S && c < NC && kept;
+      const bool vac = c >= g.Z && c < g.S && !kept;
+      const unsigned long long ma = __builtin_amdgcn_ballot_w64(adm), mv = __builtin_amdgcn_ballot_w64(vac);
+      if (adm) alist[n_adm + __builtin_popcountll(ma & below)] = c - g.S;
+      if (vac && c >= s_lo && c < s_hi) vrank[c - s_lo] = nvac + __builtin_popcountll(mv & below);
+      n_adm += __builtin_popcountll(ma);
+      nvac += __builtin_popcountll(mv);
     }
+    int n_sink_fill = 0;
     for (int s0 = 0; s0 < g.Z; s0 += 64) n_sink_fill += wave_count(s0 + lane < g.Z && lall[s0 + lane] == 0);
-    if (lane == 0) {
-      s_thr[0] = thr;
-      s_thr[1] = thr2;
-      s_nadm = n_adm;
-      if (grp == 0) n_rep[bh] = n_adm + n_sink_fill;
+    if (lane == 0 && grp == 0) n_rep[bh] = n_adm + n_sink_fill;
+    __builtin_amdgcn_wave_barrier();  // alist entries of every lane written before they are read
+#pragma unroll
+    for (int k = 0; k < kSlotsPerWg; ++k) {
+      const int s = s_lo + k;
+      // the lane holding slot s knows its vacated rank
+      const int holder = s & 63, vr = __shfl(vrank[k], holder, 64);
+      if (lane == 0 && s < s_hi) {
+        if (s < g.Z)  // sink slot: a valid one stays, an empty one takes the evicted block of its index
+          s_plan[k] = lall[s] > 0 ? -2 : s;
+        else
+          s_plan[k] = vr < 0 ? -2 : (vr < n_adm ? alist[vr] : -1);
+      }
     }
   }
   __syncthreads();
-  if (threadIdx.x < 64) {
-    // plan of this group's slots: rank of a vacated slot among the vacated
-    // slots (ascending) picks its entrant
-    const unsigned thr = s_thr[0], thr2 = s_thr[1];
-    const int s_lo = grp * kSlotsPerWg, s_hi = min(g.S, s_lo + kSlotsPerWg);
-    int nvac = 0;
-    for (int s0 = g.Z; s0 < s_hi; s0 += 64) {
-      const int s = s0 + lane;
-      const bool kept = s < g.S && hi[s] != 0u && (hi[s] > thr || (hi[s] == thr && lo[s] >= thr2));
-      const bool vac = s < s_hi && !kept;
-      const unsigned long long m = __builtin_amdgcn_ballot_w64(vac);
-      if (s >= s_lo && s < s_hi) {
-        const int j = nvac + __builtin_popcountll(m & below);
-        s_plan[s - s_lo] = !vac ? -2 : (j < s_nadm ? alist[j] : -1);
-      }
-      nvac += __builtin_popcountll(m);
+  // ring token of each row of each filled slot's block: one division per row
+  for (int x = threadIdx.x; x < kSlotsPerWg * 64; x += kThreads) {
+    const int k = x >> 6, r = x & 63, s = grp * kSlotsPerWg + k;
+    const int e = s < g.S ? s_plan[k] : -2;
+    int tok = -1;
+    if (e >= 0) {
+      const BlockExt be = block_ext(g, e);
+      if (r < be.len) tok = block_token(g, be, r);
     }
-    // sink slots: a valid one stays, an empty one takes the evicted block of its index
-    for (int s = s_lo + lane; s < min(s_hi, g.Z); s += 64) s_plan[s - s_lo] = lall[s] > 0 ? -2 : s;
+    s_tok[k][r] = tok;
   }
   __syncthreads();
   // metadata and rows of this group's slots: every load (pooled keys, K and V
@@ -183,22 +194,28 @@ __global__ __launch_bounds__(kThreads) void update_move_kernel(Geo g, const floa
   const int cpr = g.D / kVec;
   uint4 kv[kSlotsPerWg][kCopyIt], vv[kSlotsPerWg][kCopyIt];
   float kb[kSlotsPerWg];
+  const size_t ring0 = bh * g.NL + (size_t)old * g.ct;  // first token of the evicted chunk
 #pragma unroll
   for (int k = 0; k < kSlotsPerWg; ++k) {
     const int s = grp * kSlotsPerWg + k;
     const int e = s < g.S ? s_plan[k] : -2;
-    const BlockExt be = block_ext(g, e >= 0 ? e : 0);
-    const int len = e >= 0 ? be.len : 0;
-    kb[k] = e >= 0 && (int)threadIdx.x < g.D ? kbar_l[(bh * g.nl + old * g.nq + e) * g.D + threadIdx.x] : 0.f;
+    kb[k] = 0.f;
+#pragma unroll
+    for (int u = 0; u < kCopyIt; ++u) kv[k][u] = vv[k][u] = make_uint4(0, 0, 0, 0);
+    if (e < 0) continue;  // uniform: kept or emptied slots load nothing
+    if ((int)threadIdx.x < g.D) kb[k] = kbar_l[(bh * g.nl + old * g.nq + e) * g.D + threadIdx.x];
+    const int tok0 = s_tok[k][0];  // rows past the block's length load its first row (discarded)
 #pragma unroll
     for (int u = 0; u < kCopyIt; ++u) {
       const int c = threadIdx.x + kThreads * u, r = c / cpr, q = c - r * cpr;
-      kv[k][u] = make_uint4(0, 0, 0, 0);
-      vv[k][u] = make_uint4(0, 0, 0, 0);
-      if (r < len) {
-        const size_t src = (bh * g.NL + (size_t)old * g.ct + block_token(g, be, r)) * (size_t)g.D + q * kVec;
-        kv[k][u] = *reinterpret_cast<const uint4*>(kl + src);
-        vv[k][u] = *reinterpret_cast<const uint4*>(vl + src);
+      const int tok = r < 64 ? s_tok[k][r] : -1;
+      const bool on = tok >= 0;
+      const size_t src = (ring0 + (on ? tok : tok0)) * (size_t)g.D + q * kVec;
+      const uint4 kx = *reinterpret_cast<const uint4*>(kl + src);
+      const uint4 vx = *reinterpret_cast<const uint4*>(vl + src);
+      if (on) {
+        kv[k][u] = kx;
+        vv[k][u] = vx;
       }
     }
   }
