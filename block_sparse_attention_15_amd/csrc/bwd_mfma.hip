@@ -471,8 +471,12 @@ constexpr int kLocBlocks = 4;  // query blocks per workgroup (2 waves each)
 constexpr int kDqlThreads = 64 * 2 * kLocBlocks;
 
 // Row tokens of every step of this workgroup, built once in LDS (see the
-// forward's local kernel): rowtab[(w*K + t)*64 + r], lentab[w*K + t].
-constexpr int kRowTabMax = 24 * 1024;
+// forward's local kernel): rowtab[(w*K + t)*64 + r], lentab[w*K + t].  Used
+// when both fit in the LDS beside the two step buffers.
+template <int D>
+constexpr size_t dql_tab_room() {
+  return 160 * 1024 - 2 * (size_t)kLocBlocks * 2 * Sh<D>::TILEB;
+}
 
 __device__ __forceinline__ void build_rowtab(const BwdArgs& a, size_t bh, int qg, int nthreads, int* rowtab,
                                              int* lentab) {
@@ -1136,15 +1140,15 @@ template <int D>
 hipError_t launch_d(const BwdArgs& base, hipStream_t s) {
   const Geo& g = base.g;
   const size_t shm_dq = 2 * 4 * Sh<D>::TILEB + g.S * 4;      // persistent: 2 x (K,K,V,V), slot lengths
-  const size_t tabb = (size_t)kLocBlocks * g.K * 64 * 4;
-  const bool tab = tabb <= (size_t)kRowTabMax;
-  const size_t shm_dql = tab ? tabb + kLocBlocks * g.K * 4 : 0;  // local: row tables (step buffers are static)
+  const size_t tabb = (size_t)kLocBlocks * g.K * 64 * 4 + (size_t)kLocBlocks * g.K * 4;
+  const bool tab = tabb <= dql_tab_room<D>();
+  const size_t shm_dql = tab ? tabb : 0;  // local: row tables (step buffers are static)
   const size_t shm_kvl = kvl_lds(g.nq);
   static PerDeviceOnce attr;
   hipError_t e = attr.run([] {
     hipError_t r = set_lds(dq_pers_kernel<D, true>, 2 * 4 * Sh<D>::TILEB + 2048 * 4);
     if (r == hipSuccess) r = set_lds(dq_pers_kernel<D, false>, 2 * 4 * Sh<D>::TILEB + 2048 * 4);
-    if (r == hipSuccess) r = set_lds(dq_local_kernel<D, true>, kRowTabMax + 4096);
+    if (r == hipSuccess) r = set_lds(dq_local_kernel<D, true>, dql_tab_room<D>());
     if (r == hipSuccess) r = set_lds(dkv_local_kernel<D>, kvl_lds(2048));
     return r;
   });

@@ -676,8 +676,13 @@ constexpr int kLocThreads = 64 * kLocWaves;
 
 // Row tokens of every step of this workgroup, built once in LDS:
 // rowtab[(w*K + t)*64 + r] = ring row of row r of query block w's t-th
-// selected block, or -1.  Used when it fits (4*K*64 ints <= kRowTabMax).
-constexpr int kRowTabMax = 24 * 1024;
+// selected block, or -1; lentab[w*K + t] = that block's length.  Used when
+// both fit in the LDS beside the two step buffers (K <= 31 at d = 128, 94 at
+// d = 64); otherwise every gather looks its row tokens up in global memory.
+template <int D>
+constexpr size_t loc_tab_room() {
+  return 160 * 1024 - 2 * (size_t)kLocBlocks * 64 * Shape<D>::ROWB;
+}
 
 __device__ __forceinline__ void build_rowtab(const FwdArgs& a, size_t bh, int qg, int nthreads, int* rowtab,
                                              int* lentab) {
@@ -874,13 +879,13 @@ hipError_t launch_d(const FwdArgs& base, hipStream_t s) {
   // keeps only the slot lengths there (at most 2048 slots)
   const size_t shm = MASS ? 2 * kBufBytes : (size_t)base.g.S * 4;
   const Geo& g0 = base.g;
-  const size_t tabb = (size_t)kLocBlocks * g0.K * 64 * 4;
-  const bool tab = tabb <= (size_t)kRowTabMax;
-  const size_t shm_loc = tab ? tabb + kLocBlocks * g0.K * 4 : 0;  // row tables (step buffers are static)
+  const size_t tabb = (size_t)kLocBlocks * g0.K * 64 * 4 + (size_t)kLocBlocks * g0.K * 4;
+  const bool tab = tabb <= loc_tab_room<D>();
+  const size_t shm_loc = tab ? tabb : 0;  // row tables (step buffers are static)
   {
     const hipError_t e = attr.run([] {
       hipError_t r = set_lds(fwd_pers_kernel<D, MASS>, MASS ? 2 * kBufBytes : 2048 * 4);
-      if (r == hipSuccess) r = set_lds(fwd_local_kernel<D, MASS, true>, kRowTabMax + 4096);
+      if (r == hipSuccess) r = set_lds(fwd_local_kernel<D, MASS, true>, loc_tab_room<D>());
       return r;
     });
     if (e != hipSuccess) return e;
