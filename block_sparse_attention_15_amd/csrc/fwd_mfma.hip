@@ -243,9 +243,13 @@ __device__ __forceinline__ float tile(const char* kbase, const char* vbase, int 
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
     if (n < ntq) {
-      float tm = s[n][0];
+      // tree reductions (max, then the row sum below): short dependency chains
+      float m8[8];
 #pragma unroll
-      for (int j = 1; j < 16; ++j) tm = fmaxf(tm, s[n][j]);
+      for (int j = 0; j < 8; ++j) m8[j] = fmaxf(s[n][j], s[n][j + 8]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) m8[j] = fmaxf(m8[j], m8[j + 4]);
+      float tm = fmaxf(fmaxf(m8[0], m8[2]), fmaxf(m8[1], m8[3]));
       tm = half_max(tm) * c2;
       // raise the running max only when the tile exceeds it by more than 2^8
       if (__builtin_amdgcn_ballot_w64(tm > st.m[n] + 8.0f)) {
@@ -257,13 +261,17 @@ __device__ __forceinline__ float tile(const char* kbase, const char* vbase, int 
         st.m[n] = mn;
       }
       const float mneg = -st.m[n];
-      float ls = 0.f;
+      float p16[16];
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[n][j], c2, mneg));
-        ls += p;
-        pk[n][j >> 3][j & 7] = (__bf16)p;
+        p16[j] = __builtin_amdgcn_exp2f(fmaf(s[n][j], c2, mneg));
+        pk[n][j >> 3][j & 7] = (__bf16)p16[j];
       }
+#pragma unroll
+      for (int w2 = 8; w2 >= 1; w2 >>= 1)
+#pragma unroll
+        for (int j = 0; j < w2; ++j) p16[j] += p16[j + w2];
+      const float ls = p16[0];
       st.l[n] += ls;
       if (n == 0) ret = ls;
     }
