@@ -13,17 +13,16 @@
 // the other candidates compete for the remaining S - Z slots.
 //
 // Two launches:
-//  1. one workgroup per (batch, head, group of kSlotsPerWg slots).  Every
-//     workgroup decides its head's whole update from the masses (about 1 KB)
-//     in one wavefront, from registers -- a two-phase radix select of the
-//     (S - Z)-th largest candidate key, then ballot prefix counts that pair
-//     vacated slots with admitted blocks -- and then moves the rows of its own
-//     slots (16-byte coalesced copies, zero padding; the ring token of each
-//     row computed once, into LDS) and their pooled keys.  The new slot
-//     lengths and source ids go to the workspace: every workgroup reads the
-//     old lengths to decide, so none may change them yet.
-//  2. one small workgroup commits lengths and source ids and advances the
-//     ring head and the step counter.
+//  1. one workgroup per (batch, head) takes the head's decision once from the
+//     masses (about 1 KB): a two-phase wavefront radix select of the
+//     (S - Z)-th largest candidate key from registers, then ballot prefix
+//     counts that pair vacated slots with admitted blocks; it writes the plan
+//     of every slot to the workspace;
+//  2. one workgroup per (batch, head, group of kSlotsPerWg slots) carries out
+//     the plan of its slots (16-byte coalesced row copies, zero padding,
+//     pooled keys, new lengths and source ids), and workgroup 0 advances the
+//     ring head and the step counter.  Workgroups of the second launch read
+//     only the plan, never the lengths another one writes.
 #include <algorithm>
 #include <type_traits>
 
@@ -78,36 +77,39 @@ __device__ __forceinline__ void radix_threshold(const unsigned (&hi)[KPL], const
   }
 }
 
-// 1-D grid over (B, H, slot group).  nlen / nsrc: [B,H,S] new lengths and
-// source ids (workspace), committed by update_commit_kernel.
-template <typename T, int KPL>
-__global__ __launch_bounds__(kThreads) void update_move_kernel(Geo g, const float* __restrict__ mass,
-                                                               const int32_t* __restrict__ ring_head,
-                                                               const int32_t* __restrict__ step_counter,
-                                                               const int32_t* __restrict__ plen,
-                                                               const T* __restrict__ kl, const T* __restrict__ vl,
-                                                               const float* __restrict__ kbar_l,
-                                                               T* __restrict__ kp, T* __restrict__ vp,
-                                                               float* __restrict__ pkbar,
-                                                               int32_t* __restrict__ nlen,
-                                                               int32_t* __restrict__ nsrc,
-                                                               int32_t* __restrict__ n_rep,
-                                                               uint32_t* __restrict__ status) {
+// One workgroup per (batch, head): the head's whole decision, taken once.
+// Loads the head's masses, slot lengths, ring head and step counter in one
+// round, forms the candidate keys in LDS, and in one wavefront from
+// registers selects the (S - Z) largest, lists the admitted entrants
+// ascending, ranks the vacated slots ascending and writes the plan of every
+// slot: -2 keep, -1 empty, e >= 0 fill from evicted block e.  meta[0] and
+// meta[1] (written by head 0): the ring position of the evicted chunk and
+// the step id, for the copy kernel, which reads neither ring head nor step
+// counter.
+template <int KPL>
+__global__ __launch_bounds__(kThreads) void update_decide_kernel(Geo g, const float* __restrict__ mass,
+                                                                 const int32_t* __restrict__ ring_head,
+                                                                 const int32_t* __restrict__ step_counter,
+                                                                 const int32_t* __restrict__ plen,
+                                                                 int32_t* __restrict__ plan, int32_t* __restrict__ meta,
+                                                                 int32_t* __restrict__ n_rep,
+                                                                 uint32_t* __restrict__ status) {
   extern __shared__ unsigned sk[];
+  if (g.S == 0) {  // no persistent memory: nothing is admitted
+    if (threadIdx.x == 0) n_rep[blockIdx.x] = 0;
+    return;
+  }
   const int NC = g.S + g.nq;
   unsigned* hi = sk;                      // [NC] candidate keys (0: not a candidate)
   unsigned* lo = hi + NC;                 // [NC]
   int* alist = (int*)(lo + NC);           // [nq] admitted entrants, ascending
-  __shared__ int s_plan[kSlotsPerWg];     // -2 keep, -1 empty, e >= 0 fill from evicted block e
-  const int ngrp = (g.S + kSlotsPerWg - 1) / kSlotsPerWg;
-  const int grp = blockIdx.x % ngrp;
-  const size_t bh = blockIdx.x / ngrp;
+  float* mall = (float*)(alist + g.nq);   // [S + nl]
+  int* lall = (int*)(mall + g.S + g.nl);  // [S]
+  const size_t bh = blockIdx.x;
   const float* mrow = mass + bh * (g.S + g.nl);
   const int32_t* prow = plen + bh * g.S;
   // every mass and length of the head is loaded while the ring head is: the
   // evicted chunk's masses are picked from LDS once it is known
-  float* mall = (float*)(alist + g.nq);  // [S + nl]
-  int* lall = (int*)(mall + g.S + g.nl);  // [S]
   for (int c = threadIdx.x; c < g.S + g.nl; c += kThreads) mall[c] = mrow[c];
   for (int c = threadIdx.x; c < g.S; c += kThreads) lall[c] = prow[c];
   const int old = read_ring_head(ring_head, g.R, status);
@@ -122,63 +124,97 @@ __global__ __launch_bounds__(kThreads) void update_move_kernel(Geo g, const floa
     lo[c] = 0xffffffffu - (unsigned)c;  // ties: slots before entrants, lower index first
   }
   __syncthreads();
-  const int lane = threadIdx.x & 63;
+  if (threadIdx.x >= 64) return;
+  // one wavefront decides from registers: candidate c = lane + 64 u
+  const int lane = threadIdx.x;
   const unsigned long long below = (1ull << lane) - 1;
-  __shared__ int s_tok[kSlotsPerWg][64];  // ring token of each row of each filled slot's block
-  if (threadIdx.x < 64) {
-    // wave 0 decides from registers: candidate c = lane + 64 u
-    unsigned hr[KPL], lr[KPL];
-    int nvalid = 0;
+  unsigned hr[KPL], lr[KPL];
+  int nvalid = 0;
 #pragma unroll
-    for (int u = 0; u < KPL; ++u) {
-      const int c = lane + 64 * u;
-      hr[u] = c < NC ? hi[c] : 0u;
-      lr[u] = c < NC ? lo[c] : 0u;
-      nvalid += wave_count(hr[u] != 0u);
-    }
-    unsigned thr = 1u, thr2 = 0u;  // every candidate stays when they all fit
-    if (nvalid > g.S - g.Z) radix_threshold<KPL>(hr, lr, g.S - g.Z, thr, thr2);
-    // admitted entrants (kept, and not a sink fill) listed ascending; the
-    // rank of a vacated slot among the vacated slots (ascending) picks its
-    // entrant
-    const int s_lo = grp * kSlotsPerWg, s_hi = min(g.S, s_lo + kSlotsPerWg);
-    int n_adm = 0, nvac = 0, vrank[kSlotsPerWg];
+  for (int u = 0; u < KPL; ++u) {
+    const int c = lane + 64 * u;
+    hr[u] = c < NC ? hi[c] : 0u;
+    lr[u] = c < NC ? lo[c] : 0u;
+    nvalid += wave_count(hr[u] != 0u);
+  }
+  unsigned thr = 1u, thr2 = 0u;  // every candidate stays when they all fit
+  if (nvalid > g.S - g.Z) radix_threshold<KPL>(hr, lr, g.S - g.Z, thr, thr2);
+  // admitted entrants (kept, and not a sink fill) listed ascending; the rank
+  // of a vacated slot among the vacated slots (ascending) picks its entrant
+  int n_adm = 0, nvac = 0, vrank[KPL];
 #pragma unroll
-    for (int k = 0; k < kSlotsPerWg; ++k) vrank[k] = -1;
+  for (int u = 0; u < KPL; ++u) {
+    const int c = lane + 64 * u;
+    const bool kept = hr[u] != 0u && (hr[u] > thr || (hr[u] == thr && lr[u] >= thr2));
+    const bool adm = c >= g.S && c < NC && kept;
+    const bool vac = c >= g.Z && c < g.S && !kept;
+    const unsigned long long ma = __builtin_amdgcn_ballot_w64(adm), mv = __builtin_amdgcn_ballot_w64(vac);
+    if (adm) alist[n_adm + __builtin_popcountll(ma & below)] = c - g.S;
+    vrank[u] = vac ? nvac + __builtin_popcountll(mv & below) : -1;
+    n_adm += __builtin_popcountll(ma);
+    nvac += __builtin_popcountll(mv);
+  }
+  int n_sink_fill = 0;
+  for (int s0 = 0; s0 < g.Z; s0 += 64) n_sink_fill += wave_count(s0 + lane < g.Z && lall[s0 + lane] == 0);
+  __builtin_amdgcn_wave_barrier();  // alist entries of every lane written before they are read
+  int32_t* prow_plan = plan + bh * g.S;
 #pragma unroll
-    for (int u = 0; u < KPL; ++u) {
-      const int c = lane + 64 * u;
-      const bool kept = hr[u] != 0u && (hr[u] > thr || (hr[u] == thr && lr[u] >= thr2));
-      const bool adm = c >= g.S && c < NC && kept;
-      const bool vac = c >= g.Z && c < g.S && !kept;
-      const unsigned long long ma = __builtin_amdgcn_ballot_w64(adm), mv = __builtin_amdgcn_ballot_w64(vac);
-      if (adm) alist[n_adm + __builtin_popcountll(ma & below)] = c - g.S;
-      if (vac && c >= s_lo && c < s_hi) vrank[c - s_lo] = nvac + __builtin_popcountll(mv & below);
-      n_adm += __builtin_popcountll(ma);
-      nvac += __builtin_popcountll(mv);
-    }
-    int n_sink_fill = 0;
-    for (int s0 = 0; s0 < g.Z; s0 += 64) n_sink_fill += wave_count(s0 + lane < g.Z && lall[s0 + lane] == 0);
-    if (lane == 0 && grp == 0) n_rep[bh] = n_adm + n_sink_fill;
-    __builtin_amdgcn_wave_barrier();  // alist entries of every lane written before they are read
-#pragma unroll
-    for (int k = 0; k < kSlotsPerWg; ++k) {
-      const int s = s_lo + k;
-      // the lane holding slot s knows its vacated rank
-      const int holder = s & 63, vr = __shfl(vrank[k], holder, 64);
-      if (lane == 0 && s < s_hi) {
-        if (s < g.Z)  // sink slot: a valid one stays, an empty one takes the evicted block of its index
-          s_plan[k] = lall[s] > 0 ? -2 : s;
-        else
-          s_plan[k] = vr < 0 ? -2 : (vr < n_adm ? alist[vr] : -1);
-      }
+  for (int u = 0; u < KPL; ++u) {
+    const int c = lane + 64 * u;
+    if (c < g.S) {
+      int e;
+      if (c < g.Z)  // sink slot: a valid one stays, an empty one takes the evicted block of its index
+        e = lall[c] > 0 ? -2 : c;
+      else
+        e = vrank[u] < 0 ? -2 : (vrank[u] < n_adm ? alist[vrank[u]] : -1);
+      prow_plan[c] = e;
     }
   }
+  if (lane == 0) {
+    n_rep[bh] = n_adm + n_sink_fill;
+    if (bh == 0) {
+      meta[0] = old;
+      meta[1] = step_id;
+    }
+  }
+}
+
+// 1-D grid over (B, H, group of kSlotsPerWg slots): carries out the plan of
+// its slots -- rows of each filled slot copied from the evicted chunk (the
+// ring token of each row computed once, into LDS; every load issued before the
+// first store; zero padding), pooled keys copied, emptied slots zeroed, new
+// lengths and source ids written -- and workgroup 0 advances the ring head
+// and the step counter (no workgroup of this launch reads them: the evicted
+// chunk's position and the step id come from meta).
+template <typename T>
+__global__ __launch_bounds__(kThreads) void update_copy_kernel(Geo g, const int32_t* __restrict__ plan,
+                                                               const int32_t* __restrict__ meta,
+                                                               const T* __restrict__ kl, const T* __restrict__ vl,
+                                                               const float* __restrict__ kbar_l,
+                                                               T* __restrict__ kp, T* __restrict__ vp,
+                                                               float* __restrict__ pkbar, int32_t* __restrict__ plen,
+                                                               int32_t* __restrict__ psrc,
+                                                               int32_t* __restrict__ ring_head,
+                                                               int32_t* __restrict__ step_counter) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    *ring_head = (ring_wrap(*ring_head, g.R) + 1) % g.R;
+    *step_counter += 1;
+  }
+  if (g.S == 0) return;
+  __shared__ int s_plan[kSlotsPerWg];
+  __shared__ int s_tok[kSlotsPerWg][64];  // ring token of each row of each filled slot's block
+  const int ngrp = (g.S + kSlotsPerWg - 1) / kSlotsPerWg;
+  const int grp = blockIdx.x % ngrp;
+  const size_t bh = blockIdx.x / ngrp;
+  const int old = meta[0], step_id = meta[1];
+  if ((int)threadIdx.x < kSlotsPerWg) {
+    const int s = grp * kSlotsPerWg + threadIdx.x;
+    s_plan[threadIdx.x] = s < g.S ? plan[bh * g.S + s] : -2;
+  }
   __syncthreads();
-  // ring token of each row of each filled slot's block: one division per row
   for (int x = threadIdx.x; x < kSlotsPerWg * 64; x += kThreads) {
-    const int k = x >> 6, r = x & 63, s = grp * kSlotsPerWg + k;
-    const int e = s < g.S ? s_plan[k] : -2;
+    const int k = x >> 6, r = x & 63;
+    const int e = s_plan[k];
     int tok = -1;
     if (e >= 0) {
       const BlockExt be = block_ext(g, e);
@@ -187,8 +223,6 @@ __global__ __launch_bounds__(kThreads) void update_move_kernel(Geo g, const floa
     s_tok[k][r] = tok;
   }
   __syncthreads();
-  // metadata and rows of this group's slots: every load (pooled keys, K and V
-  // rows of each filled slot) issued before the first store
   constexpr int kVec = 16 / sizeof(T);
   constexpr int kCopyIt = 64 * (128 / kVec) / kThreads;  // 16-byte chunks per thread of a 64-row, d<=128 slot
   const int cpr = g.D / kVec;
@@ -197,8 +231,7 @@ __global__ __launch_bounds__(kThreads) void update_move_kernel(Geo g, const floa
   const size_t ring0 = bh * g.NL + (size_t)old * g.ct;  // first token of the evicted chunk
 #pragma unroll
   for (int k = 0; k < kSlotsPerWg; ++k) {
-    const int s = grp * kSlotsPerWg + k;
-    const int e = s < g.S ? s_plan[k] : -2;
+    const int e = s_plan[k];
     kb[k] = 0.f;
 #pragma unroll
     for (int u = 0; u < kCopyIt; ++u) kv[k][u] = vv[k][u] = make_uint4(0, 0, 0, 0);
@@ -227,8 +260,8 @@ __global__ __launch_bounds__(kThreads) void update_move_kernel(Geo g, const floa
     if (e == -2) continue;
     const size_t bs = bh * g.S + s;
     if (threadIdx.x == 0) {
-      nlen[bs] = e >= 0 ? block_ext(g, e).len : 0;
-      nsrc[bs] = e >= 0 ? step_id * g.nq + e : kEmptySrc;
+      plen[bs] = e >= 0 ? block_ext(g, e).len : 0;
+      psrc[bs] = e >= 0 ? step_id * g.nq + e : kEmptySrc;
     }
     if ((int)threadIdx.x < g.D) pkbar[bs * g.D + threadIdx.x] = kb[k];
     const size_t dst = bs * (size_t)g.C * g.D;
@@ -241,44 +274,13 @@ __global__ __launch_bounds__(kThreads) void update_move_kernel(Geo g, const floa
       }
     }
   }
-  // slots this launch leaves alone keep their metadata: mark them unchanged
-  if (threadIdx.x < kSlotsPerWg) {
-    const int s = grp * kSlotsPerWg + threadIdx.x;
-    if (s < g.S && s_plan[threadIdx.x] == -2) nlen[bh * g.S + s] = -1;
-  }
-}
-
-// Grid over (B, H, S): commit new lengths / source ids (-1 length:
-// unchanged); thread 0 advances the ring head and the step counter (no other
-// thread of this launch reads them).
-__global__ __launch_bounds__(kThreads) void update_commit_kernel(Geo g, const int32_t* __restrict__ nlen,
-                                                                 const int32_t* __restrict__ nsrc,
-                                                                 int32_t* __restrict__ plen,
-                                                                 int32_t* __restrict__ psrc,
-                                                                 int32_t* __restrict__ n_rep,
-                                                                 int32_t* __restrict__ ring_head,
-                                                                 int32_t* __restrict__ step_counter) {
-  const size_t n = (size_t)g.B * g.H * g.S;
-  const size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x;
-  if (g.S == 0 && i < (size_t)g.B * g.H) n_rep[i] = 0;  // no persistent memory: nothing is admitted
-  if (i < n) {
-    const int l = nlen[i];
-    if (l >= 0) {
-      plen[i] = l;
-      psrc[i] = nsrc[i];
-    }
-  }
-  if (i == 0) {
-    *ring_head = (ring_wrap(*ring_head, g.R) + 1) % g.R;
-    *step_counter += 1;
-  }
 }
 
 }  // namespace
 
 size_t update_workspace(const Geo& g) {
   const size_t n = (size_t)g.B * g.H * g.S * 4;
-  return 2 * ((n + 255) & ~size_t(255));
+  return ((n + 255) & ~size_t(255)) + 256;  // plan, then meta
 }
 
 hipError_t launch_persist_update(const Geo& g, const float* mass, const void* k_l, const void* v_l,
@@ -286,45 +288,35 @@ hipError_t launch_persist_update(const Geo& g, const float* mass, const void* k_
                                  void* v_p, int32_t* plen, int32_t* psrc, float* pkbar, int32_t* n_rep,
                                  void* ws, uint32_t* status, hipStream_t s) {
   const size_t n = (size_t)g.B * g.H * g.S * 4;
-  int32_t* nlen = (int32_t*)ws;
-  int32_t* nsrc = (int32_t*)((char*)ws + ((n + 255) & ~size_t(255)));
+  int32_t* plan = (int32_t*)ws;
+  int32_t* meta = (int32_t*)((char*)ws + ((n + 255) & ~size_t(255)));
   const int NC = g.S + g.nq;
-  if (g.S > 0) {
-    const size_t shm = (size_t)NC * 8 + (size_t)g.nq * 4 + (size_t)(g.S + g.nl) * 4 + (size_t)g.S * 4;
-    const int grid = g.B * g.H * ((g.S + kSlotsPerWg - 1) / kSlotsPerWg);
-    const bool bf = g.dtype == PBSA_BF16;
-    auto go = [&](auto kpl) {
-      constexpr int KPL = decltype(kpl)::value;
-      static PerDeviceOnce attr;
-      const hipError_t ea = attr.run([] {
-        hipError_t r = hipFuncSetAttribute((const void*)update_move_kernel<bf16_t, KPL>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
-        if (r == hipSuccess)
-          r = hipFuncSetAttribute((const void*)update_move_kernel<float, KPL>,
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
-        return r;
-      });
-      if (ea != hipSuccess) return ea;
-      if (bf)
-        update_move_kernel<bf16_t, KPL><<<grid, kThreads, shm, s>>>(g, mass, ring_head, step_counter, plen,
-                                                                   (const bf16_t*)k_l, (const bf16_t*)v_l, kbar_l,
-                                                                   (bf16_t*)k_p, (bf16_t*)v_p, pkbar, nlen, nsrc,
-                                                                   n_rep, status);
-      else
-        update_move_kernel<float, KPL><<<grid, kThreads, shm, s>>>(g, mass, ring_head, step_counter, plen,
-                                                                  (const float*)k_l, (const float*)v_l, kbar_l,
-                                                                  (float*)k_p, (float*)v_p, pkbar, nlen, nsrc,
-                                                                  n_rep, status);
-      return hipGetLastError();
-    };
-    const hipError_t e = NC <= 256    ? go(std::integral_constant<int, 4>{})
-                         : NC <= 1024 ? go(std::integral_constant<int, 16>{})
-                                      : go(std::integral_constant<int, 64>{});
-    if (e != hipSuccess) return e;
-  }
-  const size_t nc = std::max((size_t)g.B * g.H * g.S, (size_t)g.B * g.H);
-  update_commit_kernel<<<(unsigned)((nc + kThreads - 1) / kThreads), kThreads, 0, s>>>(g, nlen, nsrc, plen, psrc,
-                                                                                      n_rep, ring_head, step_counter);
+  const size_t shm = (size_t)NC * 8 + (size_t)g.nq * 4 + (size_t)(g.S + g.nl) * 4 + (size_t)g.S * 4;
+  auto go = [&](auto kpl) {
+    constexpr int KPL = decltype(kpl)::value;
+    static PerDeviceOnce attr;
+    const hipError_t ea = attr.run([] {
+      return hipFuncSetAttribute((const void*)update_decide_kernel<KPL>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 128 * 1024);
+    });
+    if (ea != hipSuccess) return ea;
+    update_decide_kernel<KPL><<<g.B * g.H, kThreads, shm, s>>>(g, mass, ring_head, step_counter, plen, plan, meta,
+                                                               n_rep, status);
+    return hipGetLastError();
+  };
+  hipError_t e = NC <= 256    ? go(std::integral_constant<int, 4>{})
+                 : NC <= 1024 ? go(std::integral_constant<int, 16>{})
+                              : go(std::integral_constant<int, 64>{});
+  if (e != hipSuccess) return e;
+  const int grid = std::max(1, g.B * g.H * ((g.S + kSlotsPerWg - 1) / kSlotsPerWg));
+  if (g.dtype == PBSA_BF16)
+    update_copy_kernel<bf16_t><<<grid, kThreads, 0, s>>>(g, plan, meta, (const bf16_t*)k_l, (const bf16_t*)v_l, kbar_l,
+                                                         (bf16_t*)k_p, (bf16_t*)v_p, pkbar, plen, psrc, ring_head,
+                                                         step_counter);
+  else
+    update_copy_kernel<float><<<grid, kThreads, 0, s>>>(g, plan, meta, (const float*)k_l, (const float*)v_l, kbar_l,
+                                                        (float*)k_p, (float*)v_p, pkbar, plen, psrc, ring_head,
+                                                        step_counter);
   return hipGetLastError();
 }
 
