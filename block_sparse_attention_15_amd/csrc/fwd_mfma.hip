@@ -11,8 +11,12 @@
 //    head, so the first kernel is a dense attention of all of a head's
 //    queries (contiguous 256-row tiles, 8 waves x 32 rows, two waves per
 //    SIMD so one wave's softmax overlaps the other's MFMAs) against the
-//    compact persistent memory, each slot staged once in LDS for the four
-//    waves; it writes a normalised fp32 partial output and its log-sum-exp.
+//    compact persistent memory: the valid rows of all slots are numbered
+//    through a row table in LDS and streamed as dense 64-key steps, each
+//    staged once in LDS for the eight waves (fwd_pers2_kernel; the
+//    token-mass variant, which needs per-slot sums, keeps one slot per step:
+//    fwd_pers_kernel).  It writes a normalised fp32 partial output and its
+//    log-sum-exp.
 //    The second kernel handles the selected local blocks, which differ per
 //    query block: 8 waves = 4 query blocks x 2 tiles of 32 queries, one LDS
 //    region per query block per step; it merges its result with the
@@ -28,11 +32,11 @@
 //    transposed with ds_read_b64_tr_b16 (two per 8-key operand).  Both LDS
 //    tiles are XOR-swizzled at 16-byte granularity to spread banks.
 //  * Rows reach LDS by LDS-bound loads (global_load_lds_dwordx4), with no
-//    staging registers.  The persistent kernel loads slots two steps ahead
-//    into three buffers and ends each step with a barrier that waits for all
-//    but the newest loads (its token-mass variant, which stores inside the
-//    loop, prefetches the next slot into registers instead); the local
-//    kernel gathers the next step's rows into two buffers.
+//    staging registers.  The persistent kernels load two steps ahead into
+//    three buffers and end each step with a barrier that waits for all but
+//    the newest loads (the token-mass variant, which stores inside the loop,
+//    prefetches the next slot into registers instead); the local kernel
+//    gathers the next step's rows into two buffers.
 //  * exp2 with softmax_scale*log2(e) folded into one FMA; the running max is
 //    only raised when a tile's max exceeds it by more than 2^8 (P values stay
 //    below 256, safe in bf16 and fp32), which makes O rescales rare.
