@@ -686,9 +686,11 @@ constexpr int kLocBlocks = 4;
 constexpr int kLocWaves = 2 * kLocBlocks;
 constexpr int kLocThreads = 64 * kLocWaves;
 
-// Row tokens of every step of this workgroup, built once in LDS:
-// rowtab[(w*K + t)*64 + r] = ring row of row r of query block w's t-th
-// selected block, or -1; lentab[w*K + t] = that block's length.  Used when
+// Rows of every step of this workgroup, built once in LDS:
+// rowtab[(w*K + t)*64 + r] = byte offset in the head's local K (or V) of row
+// r of query block w's t-th selected block; rows past the block's end repeat
+// its first row (finite; the tile masks them) and absent selections give 0
+// (no tile reads them); lentab[w*K + t] = that block's length (0 if absent).  Used when
 // both fit in the LDS beside the two step buffers (K <= 31 at d = 128, 94 at
 // d = 64); otherwise every gather looks its row tokens up in global memory.
 template <int D>
@@ -696,21 +698,22 @@ constexpr size_t loc_tab_room() {
   return 160 * 1024 - 2 * (size_t)kLocBlocks * 64 * Shape<D>::ROWB;
 }
 
+template <int D>
 __device__ __forceinline__ void build_rowtab(const FwdArgs& a, size_t bh, int qg, int nthreads, int* rowtab,
                                              int* lentab) {
   const Geo& g = a.g;
   for (int x = threadIdx.x; x < kLocBlocks * g.K * 64; x += nthreads) {
     const int w = x / (g.K * 64), t = (x / 64) % g.K, r = x & 63;
     const int qb = qg * kLocBlocks + w;
-    int tok = -1, len = 0;
+    int tok = 0, len = 0;
     if (qb < g.nq) {
       const int p = a.topk[(bh * g.nq + qb) * g.K + t];
       if ((unsigned)p < (unsigned)g.nl) {
         len = a.tab.blen[a.tab.pblk[p]];
-        if (r < len) tok = a.tab.pbase[p] + a.tab.btok[a.tab.pblk[p] * g.C + r];
+        tok = a.tab.pbase[p] + a.tab.btok[a.tab.pblk[p] * g.C + (r < len ? r : 0)];
       }
     }
-    rowtab[x] = tok;
+    rowtab[x] = tok * D * 2;
     if (r == 0) lentab[w * g.K + t] = len;
   }
 }
@@ -718,11 +721,12 @@ __device__ __forceinline__ void build_rowtab(const FwdArgs& a, size_t bh, int qg
 // One local step gathered straight into LDS (global_load_lds_dwordx4): no
 // staging registers and no LDS store instructions.  An instruction fills 1 KB
 // of the buffer (lane l at byte 16*l); lane l fetches the global chunk whose
-// swizzled position is l's, so K and V land in their swizzled layouts.  Rows
-// past a selected block's end (and absent selections) load row 0 of the
-// head's queries instead: finite values whose keys the tile masks.  TAB: row
-// tokens from the LDS row table (a compile-time choice: if the global-memory
-// address path shares the loop, the compiler joins the two with a full wait).
+// swizzled position is l's, so K and V land in their swizzled layouts.  TAB:
+// rows from the LDS row table as 32-bit byte offsets added to the head's base
+// (one add per load; a compile-time choice: if the global-memory lookup path
+// shares the loop, the compiler joins the two with a full wait).  Without the
+// table, rows past a selected block's end (and absent selections) load row 0
+// of the head's queries: finite values whose keys the tile masks.
 template <int D, bool TAB>
 __device__ __forceinline__ void loc_gather(const FwdArgs& a, size_t bh, int qg, int j, char* buf,
                                            const int* rowtab) {
@@ -732,7 +736,7 @@ __device__ __forceinline__ void loc_gather(const FwdArgs& a, size_t bh, int qg, 
   constexpr int PER_WAVE = kLocBlocks * 2 * UPT / kLocWaves;
   const Geo& g = a.g;
   const int t = j >> 1, half = j & 1;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int rr = lane / Sh::CPR, pos = lane % Sh::CPR;
   const bf16_t* kb = a.kl + bh * (size_t)g.NL * D;
   const bf16_t* vb = a.vl + bh * (size_t)g.NL * D;
@@ -743,10 +747,14 @@ __device__ __forceinline__ void loc_gather(const FwdArgs& a, size_t bh, int qg, 
     const int w = u / (2 * UPT), tensor = (u / UPT) & 1;
     const int r = RPK * (u % UPT) + rr;  // row in the 32-row tile
     const int c = tensor ? swz_v(r, pos, Sh::CPR) : swz_k(r, pos, Sh::CPR);
-    int tok = -1;
     if (TAB) {
-      tok = rowtab[(w * g.K + t) * 64 + 32 * half + r];
-    } else {
+      const uint32_t off = (uint32_t)rowtab[(w * g.K + t) * 64 + 32 * half + r] + (uint32_t)(c * 16);
+      const char* src = reinterpret_cast<const char*>(tensor ? vb : kb) + off;
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(buf + u * 1024), 16, 0, 0);
+      continue;
+    }
+    int tok = -1;
+    {
       const int qb = qg * kLocBlocks + w;
       if (qb < g.nq) {
         const int p = a.topk[(bh * g.nq + qb) * g.K + t];
@@ -794,7 +802,7 @@ __global__ __launch_bounds__(kLocThreads, 1) void fwd_local_kernel(FwdArgs a) {
   int* rowtab = reinterpret_cast<int*>(smem);
   int* lentab = rowtab + kLocBlocks * g.K * 64;
   if (TAB) {
-    build_rowtab(a, bh, qg, kLocThreads, rowtab, lentab);
+    build_rowtab<D>(a, bh, qg, kLocThreads, rowtab, lentab);
     __syncthreads();
   }
   loc_gather<D, TAB>(a, bh, qg, 0, kv0, rowtab);
@@ -892,7 +900,7 @@ hipError_t launch_d(const FwdArgs& base, hipStream_t s) {
   const size_t shm = MASS ? 2 * kBufBytes : (size_t)base.g.S * 4;
   const Geo& g0 = base.g;
   const size_t tabb = (size_t)kLocBlocks * g0.K * 64 * 4 + (size_t)kLocBlocks * g0.K * 4;
-  const bool tab = tabb <= loc_tab_room<D>();
+  const bool tab = tabb <= loc_tab_room<D>() && (size_t)g0.NL * D * 2 < ((size_t)1 << 31);  // 32-bit row offsets
   const size_t shm_loc = tab ? tabb : 0;  // row tables (step buffers are static)
   {
     const hipError_t e = attr.run([] {
