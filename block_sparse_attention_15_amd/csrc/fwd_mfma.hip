@@ -18,9 +18,10 @@
 //    fwd_pers_kernel).  It writes a normalised fp32 partial output and its
 //    log-sum-exp.
 //    The second kernel handles the selected local blocks, which differ per
-//    query block: 8 waves = 4 query blocks x 2 tiles of 32 queries, one LDS
-//    region per query block per step; it merges its result with the
-//    persistent partial by log-sum-exp and writes O (bf16) and LSE.
+//    query block: one query block per workgroup (2 waves = 2 tiles of 32
+//    queries, four workgroups per CU), so a step's barrier waits only for
+//    the two waves of one block; it merges its result with the persistent
+//    partial by log-sum-exp and writes O (bf16) and LSE.
 //  * The products are computed transposed with v_mfma_f32_32x32x16_bf16:
 //    S^T = K Q^T (keys x queries) and O^T += V^T P^T.  In the result layout a
 //    lane holds one query and 16 of the tile's 32 keys, so the online softmax
@@ -678,11 +679,14 @@ __global__ __launch_bounds__(kP2Threads, 1) void fwd_pers2_kernel(FwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // Kernel 2: each query block against its K selected local blocks, merged with
-// the persistent partial by log-sum-exp.  8 waves = 4 query blocks x 2 query
-// tiles; per step the workgroup stages 32 rows of each block's current
-// selected block (one LDS region per query block).
+// the persistent partial by log-sum-exp.  A workgroup is kLocBlocks query
+// blocks x 2 query tiles; per step it stages 32 rows of each block's current
+// selected block (one LDS region per query block).  One block per workgroup
+// measured 14% faster than four: the blocks' work differs (edge blocks of
+// 24-48 tokens, short selected blocks) and a shared barrier per step made
+// every block wait for the slowest.
 // ---------------------------------------------------------------------------
-constexpr int kLocBlocks = 4;
+constexpr int kLocBlocks = 1;
 constexpr int kLocWaves = 2 * kLocBlocks;
 constexpr int kLocThreads = 64 * kLocWaves;
 
@@ -690,9 +694,10 @@ constexpr int kLocThreads = 64 * kLocWaves;
 // rowtab[(w*K + t)*64 + r] = byte offset in the head's local K (or V) of row
 // r of query block w's t-th selected block; rows past the block's end repeat
 // its first row (finite; the tile masks them) and absent selections give 0
-// (no tile reads them); lentab[w*K + t] = that block's length (0 if absent).  Used when
-// both fit in the LDS beside the two step buffers (K <= 31 at d = 128, 94 at
-// d = 64); otherwise every gather looks its row tokens up in global memory.
+// (no tile reads them); lentab[w*K + t] = that block's length (0 if absent).
+// Used when both fit in the LDS beside the two step buffers (four workgroups
+// share a CU while the table stays under about 8 KB, K <= 31); otherwise
+// every gather looks its row tokens up in global memory.
 template <int D>
 constexpr size_t loc_tab_room() {
   return 160 * 1024 - 2 * (size_t)kLocBlocks * 64 * Shape<D>::ROWB;
@@ -770,7 +775,8 @@ __device__ __forceinline__ void loc_gather(const FwdArgs& a, size_t bh, int qg, 
 }
 
 template <int D, bool MASS, bool TAB>
-__global__ __launch_bounds__(kLocThreads, 1) void fwd_local_kernel(FwdArgs a) {
+// 2 waves per SIMD: the register budget of four such workgroups per CU
+__global__ __launch_bounds__(kLocThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_local_kernel(FwdArgs a) {
   using Sh = Shape<D>;
   extern __shared__ __attribute__((aligned(16))) char smem[];  // row tables
   constexpr int BUF = kLocBlocks * 64 * Sh::ROWB;            // per block: 32 K rows, 32 V rows
