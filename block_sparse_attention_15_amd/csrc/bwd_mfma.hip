@@ -27,7 +27,8 @@
 //   dk_ds     key-outer like dkv_pers: dK += dS^T Q from the stored dS tiles,
 //             one product where recomputing dS takes three.
 //   dkv_local key-outer over a local block (4 waves: dV and dK for 2 x 32
-//             keys), streaming only the query blocks that selected it (a
+//             keys; each dV wave passes P to its key tile's dK wave through
+//             LDS), streaming only the query blocks that selected it (a
 //             key-block -> query-block index built from the top-k lists),
 //             rows gathered straight into LDS.
 // LDS tiles hold 32 rows of 16-byte chunks XOR-swizzled so that both the
@@ -673,10 +674,16 @@ __device__ __forceinline__ void k_init(const bf16_t* krow, const bf16_t* vrow, b
 // tiles (see q_tile).  ASMTR: transposed reads in asm blocks that wait for
 // their own reads: all at once (rd_tr_all) in a dV role, per column tile
 // after the softmax (rd_tr_dt, fewer live registers) in a dK role, which
-// holds V as well.
-template <int D, bool DV, bool EARLY = false, bool XADDR = false, bool ASMTR = false, typename Mid = NoMid>
+// holds V as well.  PX (P exchange between the two waves of a key tile): 1,
+// a dV role, stores its P tile (fp32, 4 float4 per lane) in pex and calls
+// sync(); 2, a dK role, skips S = Q K^T and the exponentials, calls sync()
+// after its dP product and reads P from pex: the same values, one product
+// fewer per tile.
+template <int D, bool DV, bool EARLY = false, bool XADDR = false, bool ASMTR = false, typename Mid = NoMid,
+          int PX = 0, typename Sync = NoMid>
 __device__ __forceinline__ void k_tile(const char* tq, const char* td, const float* lse2, const float* dl, float c2,
-                                       KState<D, DV>& st, Mid mid = Mid{}, const char* arr = nullptr) {
+                                       KState<D, DV>& st, Mid mid = Mid{}, const char* arr = nullptr,
+                                       float4* pex = nullptr, Sync sync = Sync{}) {
   constexpr bool HOIST = !ASMTR || DV;
   static_assert(HOIST || !EARLY, "EARLY reads are hoisted reads");
   const int lane = threadIdx.x & 63, h = lane >> 5, l32 = lane & 31;
@@ -714,7 +721,7 @@ __device__ __forceinline__ void k_tile(const char* tq, const char* td, const flo
     const int bd = DV ? 0 : nat_base<D>((int)(td - arr), l32, h);
 #pragma unroll
     for (int ks = 0; ks < Sh<D>::KS; ++ks) {
-      s = mfma(rd_nat_at<D>(arr, bq, ks), st.kf[ks], s);
+      if (PX != 2) s = mfma(rd_nat_at<D>(arr, bq, ks), st.kf[ks], s);
       if (!DV) dp = mfma(rd_nat_at<D>(arr, bd, ks), st.vf[DV ? 0 : ks], dp);
     }
   } else {
@@ -726,15 +733,33 @@ __device__ __forceinline__ void k_tile(const char* tq, const char* td, const flo
   }
   if constexpr (HOIST && !EARLY) read_bt();
   f32x16_t x;
+  if constexpr (PX == 2) {
+    // P from the dV wave of this key tile
+    sync();
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float4 L = *reinterpret_cast<const float4*>(lse2 + 8 * i + 4 * h);
-    const float Ls[4] = {L.x, L.y, L.z, L.w};
+    for (int i = 0; i < 4; ++i) {
+      const float4 P = pex[i * 64 + lane];
+      x[4 * i] = P.x * dp[4 * i];
+      x[4 * i + 1] = P.y * dp[4 * i + 1];
+      x[4 * i + 2] = P.z * dp[4 * i + 2];
+      x[4 * i + 3] = P.w * dp[4 * i + 3];
+    }
+  } else {
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int j = 4 * i + jj;
-      const float p = __builtin_amdgcn_exp2f(fmaf(s[j], c2, -Ls[jj]));
-      x[j] = DV ? p : p * dp[j];  // P, or -dS = P (D - dP)
+    for (int i = 0; i < 4; ++i) {
+      const float4 L = *reinterpret_cast<const float4*>(lse2 + 8 * i + 4 * h);
+      const float Ls[4] = {L.x, L.y, L.z, L.w};
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int j = 4 * i + jj;
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[j], c2, -Ls[jj]));
+        x[j] = DV ? p : p * dp[j];  // P, or -dS = P (D - dP)
+      }
+    }
+    if constexpr (PX == 1) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pex[i * 64 + lane] = make_float4(x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]);
+      sync();
     }
   }
   const bf16x8_t x0 = pack8(x, 0), x1 = pack8(x, 1);
@@ -966,6 +991,10 @@ __global__ __launch_bounds__(kKvThreads, 1) void dk_ds_kernel(BwdArgs a) {
 // dkv_local: one local block (64 keys = 2 key tiles) per workgroup, 4 waves:
 // waves 0-1 accumulate dV and waves 2-3 dK of the two key tiles, over the
 // same gathered query tiles, which are staged into LDS once for both passes.
+// The dV wave of a key tile hands its probabilities to the dK wave through
+// LDS (a barrier in mid-step), so the dK wave computes dP and dK^T only: 16
+// products per wave and step in both roles instead of 16 and 24 (171 -> 157
+// us at the decode shape).
 // A step is one 32-row half of one query block that selected this local
 // block (key-block -> query-block lists from bwd_tindex_kernel, copied to LDS
 // with the step list).  Q and dO rows and their lse*log2(e) / D are
@@ -1039,7 +1068,8 @@ constexpr size_t kvl_lds(int nq) { return 4 * (size_t)nq * 4; }
 // every wave runs the same number of barriers and gathers whatever its role.
 template <int D, bool DV>
 __device__ __forceinline__ void kvl_pass(const BwdArgs& a, size_t bh, int p, int kt, const int* sel,
-                                         const int* slen, const int* steps, int nsteps, char* kv0, char* kv1) {
+                                         const int* slen, const int* steps, int nsteps, char* kv0, char* kv1,
+                                         float4* pex) {
   const Geo& g = a.g;
   const int l32 = threadIdx.x & 31;
   const BlockExt ke = block_ext(g, p % g.nq);
@@ -1066,11 +1096,20 @@ __device__ __forceinline__ void kvl_pass(const BwdArgs& a, size_t bh, int p, int
         if (i + 2 < nsteps) ga.tokens(a, sel, slen, steps[i + 2]);
       }
     };
+    // mid-step barrier: the dV wave of each key tile has written its P
+    auto sync = []() {
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); the LDS-bound loads stay in flight
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    };
     if (nk > 0) {
       const float* f = reinterpret_cast<const float*>(cur + 2 * Sh<D>::TILEB);
-      k_tile<D, DV, true, true>(cur, cur + Sh<D>::TILEB, f, f + 32, c2, st, mid, cur);
+      k_tile<D, DV, true, true, false, decltype(mid), DV ? 1 : 2, decltype(sync)>(cur, cur + Sh<D>::TILEB, f, f + 32,
+                                                                                 c2, st, mid, cur, pex, sync);
     } else {
       mid();
+      sync();
     }
     __syncthreads();
   };
@@ -1095,6 +1134,7 @@ __global__ __launch_bounds__(kKvlThreads, 2) void dkv_local_kernel(BwdArgs a) {
   // gather into one from the reads of the other
   __shared__ __attribute__((aligned(1024))) char kv0[KvlGather<D>::BUF];
   __shared__ __attribute__((aligned(1024))) char kv1[KvlGather<D>::BUF];
+  __shared__ float4 pex[2][4 * 64];  // P of each key tile's current step, from its dV wave
   const Geo& g = a.g;
   const int total = g.B * g.H * g.nl;
   const int slot = xcd_remap(total);
@@ -1125,9 +1165,9 @@ __global__ __launch_bounds__(kKvlThreads, 2) void dkv_local_kernel(BwdArgs a) {
   }
   __syncthreads();
   if (role == 0)
-    kvl_pass<D, true>(a, bh, p, kt, sel, slen, steps, nsteps, kv0, kv1);
+    kvl_pass<D, true>(a, bh, p, kt, sel, slen, steps, nsteps, kv0, kv1, pex[kt]);
   else
-    kvl_pass<D, false>(a, bh, p, kt, sel, slen, steps, nsteps, kv0, kv1);
+    kvl_pass<D, false>(a, bh, p, kt, sel, slen, steps, nsteps, kv0, kv1, pex[kt]);
 }
 
 template <typename K>
