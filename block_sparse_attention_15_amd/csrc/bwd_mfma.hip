@@ -259,6 +259,7 @@ struct BwdArgs {
   float* dvl;
   GeoTab tab;
   int ntiles;
+  int pk;  // dq_pers / dk_ds run on packed persistent rows (dkv_pers then zeroes dK past the slot lengths)
 };
 
 // Which tiles read their transposed operands ahead of the VALU work (only
@@ -380,18 +381,21 @@ template <int D> struct SlotPf {
   uint4 k[N], v[N];
 };
 
-template <int D>
-// Unconditional loads (rows clamped to the slot's last): the rows at or past
-// the slot's length are zeroed when staged, after the wait for the loads.
-__device__ __forceinline__ void slot_load(const BwdArgs& a, size_t bh, int s, SlotPf<D>& pf) {
+// Unconditional loads (rows clamped to the step's last): the rows at or
+// past the step's row count are zeroed when staged, after the wait for the
+// loads.  A step is one slot (its rows 0-63), or with a row table (PK) the
+// packed rows 64s .. 64s+63 of the head (nvalid of them in all).
+template <int D, bool PK>
+__device__ __forceinline__ void slot_load(const BwdArgs& a, size_t bh, int s, SlotPf<D>& pf, const int* rowtab,
+                                          int nvalid) {
   const Geo& g = a.g;
-  const bf16_t* kb = a.kp + (bh * g.S + s) * (size_t)g.C * D;
-  const bf16_t* vb = a.vp + (bh * g.S + s) * (size_t)g.C * D;
+  const size_t hb = PK ? bh * g.S * (size_t)g.C * D : (bh * g.S + s) * (size_t)g.C * D;
 #pragma unroll
   for (int u = 0; u < SlotPf<D>::N; ++u) {
-    const int id = threadIdx.x + kDqThreads * u, r = min(id / Sh<D>::CPR, g.C - 1), c = id % Sh<D>::CPR;
-    pf.k[u] = ld16(kb + (size_t)r * D + c * 8);
-    pf.v[u] = ld16(vb + (size_t)r * D + c * 8);
+    const int id = threadIdx.x + kDqThreads * u, c = id % Sh<D>::CPR;
+    const int r = PK ? rowtab[min(64 * s + id / Sh<D>::CPR, nvalid - 1)] : min(id / Sh<D>::CPR, g.C - 1);
+    pf.k[u] = ld16(a.kp + hb + (size_t)r * D + c * 8);
+    pf.v[u] = ld16(a.vp + hb + (size_t)r * D + c * 8);
   }
 }
 
@@ -408,9 +412,11 @@ __device__ __forceinline__ void slot_store(const SlotPf<D>& pf, char* buf, int n
   }
 }
 
-template <int D, bool DS>
+template <int D, bool DS, bool PK>
 __global__ __launch_bounds__(kDqThreads, 1) void dq_pers_kernel(BwdArgs a) {
-  // DS: also store every dS tile for dk_ds
+  // DS: also store every dS tile for dk_ds.  PK: the keys are the head's
+  // valid slot rows packed (a row table in LDS), 64 per step, so only the
+  // last step is partial; else one slot per step (its 64 rows, padded).
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int BUF = 4 * Sh<D>::TILEB;
   const Geo& g = a.g;
@@ -428,22 +434,32 @@ __global__ __launch_bounds__(kDqThreads, 1) void dq_pers_kernel(BwdArgs a) {
   const float c2 = g.scale * kLog2e;
   const int nqt = (g.ct + 31) / 32;  // query tiles of the head; this wave's is qt * kDqWaves + wave
   bf16_t* dsw = DS ? a.dsb + ((size_t)bh * 2 * g.S * nqt + qt * kDqWaves + wave) * 1024 : nullptr;
-  // Slot lengths go to LDS before the first dS store: a length read from
-  // global memory later would wait (vmcnt) for every store in flight.
-  int* plen_s = reinterpret_cast<int*>(smem + 2 * BUF);
-  for (int i = threadIdx.x; i < g.S; i += kDqThreads) plen_s[i] = min(a.plen[bh * g.S + i], g.C);
-  __syncthreads();
-  if (g.S > 0) {
-    SlotPf<D> pf;
-    slot_load<D>(a, bh, 0, pf);
-    slot_store<D>(pf, smem, plen_s[0]);
+  // Slot lengths (or the packed row table) go to LDS before the first dS
+  // store: a length read from global memory later would wait (vmcnt) for
+  // every store in flight.
+  int* plen_s = reinterpret_cast<int*>(smem + 2 * BUF);  // [S], or PK: prefix sums [S+1]
+  int* rowtab = plen_s + g.S + 1;                        // PK: [S*C]
+  int nsteps = g.S, nvalid = 0;
+  if (PK) {
+    nvalid = packed_rows(a.plen + bh * g.S, g.S, g.C, plen_s, rowtab, kDqThreads);
+    nsteps = (nvalid + 63) / 64;
+  } else {
+    for (int i = threadIdx.x; i < g.S; i += kDqThreads) plen_s[i] = min(a.plen[bh * g.S + i], g.C);
     __syncthreads();
-    for (int s = 0; s < g.S; ++s) {
-      if (s + 1 < g.S) slot_load<D>(a, bh, s + 1, pf);
+  }
+  // rows of step s
+  auto rows_of = [&](int s) { return PK ? min(nvalid - 64 * s, 64) : plen_s[s]; };
+  if (nsteps > 0) {
+    SlotPf<D> pf;
+    slot_load<D, PK>(a, bh, 0, pf, rowtab, nvalid);
+    slot_store<D>(pf, smem, rows_of(0));
+    __syncthreads();
+    for (int s = 0; s < nsteps; ++s) {
+      if (s + 1 < nsteps) slot_load<D, PK>(a, bh, s + 1, pf, rowtab, nvalid);
       if (active) {
-        // slot rows at or past n are staged as zeros: no key mask needed
-        // (see q_tile); dS goes to the tiles of key tiles 2s and 2s+1
-        const int n = plen_s[s], rb = (s & 1) * BUF;
+        // rows at or past n are staged as zeros: no key mask needed (see
+        // q_tile); dS goes to the tiles of key tiles 2s and 2s+1
+        const int n = rows_of(s), rb = (s & 1) * BUF;
         bf16_t* dso = DS ? dsw + (size_t)(2 * s) * nqt * 1024 : nullptr;
         if (n > 0)
           q_tile<D, kHoistDqPers, false, false, false, DS>(smem, rb, rb + 2 * Sh<D>::TILEB, 32, c2, st, NoMid{},
@@ -452,7 +468,7 @@ __global__ __launch_bounds__(kDqThreads, 1) void dq_pers_kernel(BwdArgs a) {
           q_tile<D, kHoistDqPers, false, false, false, DS>(smem, rb + Sh<D>::TILEB, rb + 3 * Sh<D>::TILEB, 32,
                                                            c2, st, NoMid{}, DS ? dso + (size_t)nqt * 1024 : nullptr);
       }
-      if (s + 1 < g.S) slot_store<D>(pf, smem + ((s + 1) & 1) * BUF, plen_s[s + 1]);
+      if (s + 1 < nsteps) slot_store<D>(pf, smem + ((s + 1) & 1) * BUF, rows_of(s + 1));
       __syncthreads();
     }
   }
@@ -887,6 +903,15 @@ __global__ __launch_bounds__(kKvThreads, 1) void dkv_pers_kernel(BwdArgs a) {
     dst = ob + (size_t)row * D;
     return true;
   });
+  if (DV && a.pk) {
+    // the packed dk_ds writes only the rows that exist: the slot's rows past
+    // its length get their zero dK here
+    float* zk = a.dkp + sbase;
+    for (int r = max(nk, 0); r < 32 && 32 * kh + r < g.C; ++r) {
+      typedef float nf2 __attribute__((ext_vector_type(2)));
+      __builtin_nontemporal_store(nf2{0.f, 0.f}, reinterpret_cast<nf2*>(zk + (size_t)(32 * kh + r) * D) + lane % (D / 2));
+    }
+  }
 }
 
 // dK of the persistent slots from the dS tiles that dq_pers stored:
@@ -932,25 +957,54 @@ template <int D> struct DsDma {
   }
 };
 
-template <int D>
+// PK: the key tiles are the head's packed valid rows (as dq_pers<PK> stored
+// their dS tiles).  The head's nkt tiles are split evenly over its
+// workgroups (sp takes tiles [sp*nkt/G, (sp+1)*nkt/G), one per wave, G =
+// ceil(S/4) workgroups per head), so that the compute units, two workgroups
+// each, carry nearly equal numbers of busy waves: the kernel's time follows
+// the most loaded unit.  Rows are written through the prefix sums of the
+// slot lengths; the rows past the slots' lengths, which no tile covers, get
+// their zeros from the dV pass of dkv_pers.
+template <int D, bool PK>
 __global__ __launch_bounds__(kKvThreads, 1) void dk_ds_kernel(BwdArgs a) {
   using Dm = DsDma<D>;
   __shared__ __attribute__((aligned(1024))) char db0[Dm::BUF];
   __shared__ __attribute__((aligned(1024))) char db1[Dm::BUF];
   __shared__ __attribute__((aligned(1024))) char db2[Dm::BUF];
+  __shared__ int dst32[PK ? kKvWaves : 1][32];  // PK: slot*C + row of each key of each wave's tile
+  extern __shared__ __attribute__((aligned(16))) int pre[];  // PK: [S+1] prefix sums of the slot lengths
   const Geo& g = a.g;
   const int total = g.B * g.H * a.ntiles;
   const int lin = xcd_remap(total);
   if (lin >= total) return;
-  const int sp = lin % a.ntiles;  // slot group
+  const int sp = lin % a.ntiles;  // slot group, or PK: group of packed key tiles
   const size_t bh = lin / a.ntiles;
-  const int wave = threadIdx.x >> 6;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int slot = kKvSlots * sp + (wave >> 1), kh = wave & 1;
-  const bool has_slot = slot < g.S;
-  const int n = has_slot ? min(a.plen[bh * g.S + slot], g.C) : 0;
-  const int nk = __builtin_amdgcn_readfirstlane(min(max(n - 32 * kh, 0), 32));  // valid keys of this wave's tile
   const int nqt = (g.ct + 31) / 32, last = nqt - 1;
-  const bf16_t* dsw = a.dsb + ((size_t)bh * 2 * g.S + (has_slot ? 2 * slot + kh : 0)) * nqt * 1024;
+  int nk, kt;  // valid keys of this wave's tile, its key tile (dS tile row)
+  if (PK) {
+    const int nvalid = packed_rows(a.plen + bh * g.S, g.S, g.C, pre, nullptr, kKvThreads);
+    const int nkt = (nvalid + 31) / 32;
+    const int t0 = sp * nkt / a.ntiles, t1 = (sp + 1) * nkt / a.ntiles;  // at most kKvWaves tiles
+    kt = t0 + wave;
+    nk = kt < t1 ? __builtin_amdgcn_readfirstlane(min(nvalid - 32 * kt, 32)) : 0;
+    if (nk > 0 && lane < 32) {
+      const int p = 32 * kt + lane;
+      if (p < nvalid) {
+        const int sl = packed_slot(pre, g.S, p);
+        dst32[PK ? wave : 0][lane] = sl * g.C + (p - pre[sl]);
+      }
+    }
+    if (t0 >= t1) return;  // no tile for this workgroup (uniform)
+    if (nk <= 0) kt = t0;  // loads of an existing tile, no product
+  } else {
+    const bool has_slot = slot < g.S;
+    const int n = has_slot ? min(a.plen[bh * g.S + slot], g.C) : 0;
+    nk = __builtin_amdgcn_readfirstlane(min(max(n - 32 * kh, 0), 32));
+    kt = has_slot ? 2 * slot + kh : 0;
+  }
+  const bf16_t* dsw = a.dsb + ((size_t)bh * 2 * g.S + kt) * nqt * 1024;
   KState<D, true> st;
 #pragma unroll
   for (int dt = 0; dt < Sh<D>::DT; ++dt) st.acc[dt] = f32x16_t{};
@@ -978,7 +1032,17 @@ __global__ __launch_bounds__(kKvThreads, 1) void dk_ds_kernel(BwdArgs a) {
     step(i + 2, db2, db1);
   }
   __builtin_amdgcn_s_waitcnt(0xF70);  // the last loads land before the workgroup can end
-  if (!has_slot || 32 * kh >= g.C) return;
+  if (PK) {
+    if (nk <= 0) return;
+    float* ob = a.dkp + bh * g.S * (size_t)g.C * D;
+    k_write<D, true>(st, nk, g.scale, [&](int r, float*& dst) {
+      if (r >= nk) return false;
+      dst = ob + (size_t)dst32[PK ? wave : 0][r] * D;
+      return true;
+    });
+    return;
+  }
+  if (slot >= g.S || 32 * kh >= g.C) return;
   float* ob = a.dkp + (bh * g.S + slot) * (size_t)g.C * D;
   k_write<D, true>(st, nk, g.scale, [&](int r, float*& dst) {
     const int row = 32 * kh + r;
@@ -1181,18 +1245,26 @@ hipError_t set_lds(K kernel, size_t bytes) {
 // slots from those tiles, then dQ of the local blocks.  (Running the dK/dV
 // kernels on a second stream beside the dQ kernels measured within 1% of this
 // order at the decode shape, so the library keeps to the caller's stream.)
+// Most LDS for the packed row table of dq_pers (beside its 2 x 4 tiles).
+constexpr size_t kDqTableMax = 60 * 1024;
+
 template <int D>
 hipError_t launch_d(const BwdArgs& base, hipStream_t s) {
   const Geo& g = base.g;
-  const size_t shm_dq = 2 * 4 * Sh<D>::TILEB + g.S * 4;      // persistent: 2 x (K,K,V,V), slot lengths
+  // persistent keys packed (valid rows numbered consecutively) where the row table fits
+  const size_t tab_dq = ((size_t)g.S * g.C + g.S + 1) * 4;
+  const bool pk = g.S > 0 && tab_dq <= kDqTableMax;
+  const size_t shm_dq = 2 * 4 * Sh<D>::TILEB + (pk ? tab_dq : g.S * 4);  // 2 x (K,K,V,V), row table or lengths
   const size_t tabb = (size_t)kLocBlocks * g.K * 64 * 4 + (size_t)kLocBlocks * g.K * 4;
   const bool tab = tabb <= dql_tab_room<D>();
   const size_t shm_dql = tab ? tabb : 0;  // local: row tables (step buffers are static)
   const size_t shm_kvl = kvl_lds(g.nq);
   static PerDeviceOnce attr;
   hipError_t e = attr.run([] {
-    hipError_t r = set_lds(dq_pers_kernel<D, true>, 2 * 4 * Sh<D>::TILEB + 2048 * 4);
-    if (r == hipSuccess) r = set_lds(dq_pers_kernel<D, false>, 2 * 4 * Sh<D>::TILEB + 2048 * 4);
+    hipError_t r = set_lds(dq_pers_kernel<D, true, false>, 2 * 4 * Sh<D>::TILEB + 2048 * 4);
+    if (r == hipSuccess) r = set_lds(dq_pers_kernel<D, false, false>, 2 * 4 * Sh<D>::TILEB + 2048 * 4);
+    if (r == hipSuccess) r = set_lds(dq_pers_kernel<D, true, true>, 2 * 4 * Sh<D>::TILEB + kDqTableMax);
+    if (r == hipSuccess) r = set_lds(dq_pers_kernel<D, false, true>, 2 * 4 * Sh<D>::TILEB + kDqTableMax);
     if (r == hipSuccess) r = set_lds(dq_local_kernel<D, true>, dql_tab_room<D>());
     if (r == hipSuccess) r = set_lds(dkv_local_kernel<D>, kvl_lds(2048));
     return r;
@@ -1200,6 +1272,7 @@ hipError_t launch_d(const BwdArgs& base, hipStream_t s) {
   if (e != hipSuccess) return e;
   BwdArgs a = base;
   const bool ds = g.ds && g.S > 0;
+  a.pk = ds && pk;
   // dK, dV of the local blocks, then dV (and without dS tiles, dK) of the
   // persistent slots
   int total = g.B * g.H * g.nl;
@@ -1219,16 +1292,24 @@ hipError_t launch_d(const BwdArgs& base, hipStream_t s) {
   // dq of the persistent slots (writes dq, and the dS tiles)
   a.ntiles = (g.ct + kDqRows - 1) / kDqRows;
   total = g.B * g.H * a.ntiles;
-  if (ds)
-    dq_pers_kernel<D, true><<<((total + 7) / 8) * 8, kDqThreads, shm_dq, s>>>(a);
+  const int grid_dq = ((total + 7) / 8) * 8;
+  if (ds && pk)
+    dq_pers_kernel<D, true, true><<<grid_dq, kDqThreads, shm_dq, s>>>(a);
+  else if (ds)
+    dq_pers_kernel<D, true, false><<<grid_dq, kDqThreads, shm_dq, s>>>(a);
+  else if (pk)
+    dq_pers_kernel<D, false, true><<<grid_dq, kDqThreads, shm_dq, s>>>(a);
   else
-    dq_pers_kernel<D, false><<<((total + 7) / 8) * 8, kDqThreads, shm_dq, s>>>(a);
+    dq_pers_kernel<D, false, false><<<grid_dq, kDqThreads, shm_dq, s>>>(a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ds) {
     // dK of the persistent slots from the dS tiles
     a.ntiles = kv_tiles;
     total = g.B * g.H * a.ntiles;
-    dk_ds_kernel<D><<<((total + 7) / 8) * 8, kKvThreads, 0, s>>>(a);
+    if (pk)  // the dS tiles are in packed key-tile order
+      dk_ds_kernel<D, true><<<((total + 7) / 8) * 8, kKvThreads, ((size_t)g.S + 1) * 4, s>>>(a);
+    else
+      dk_ds_kernel<D, false><<<((total + 7) / 8) * 8, kKvThreads, 0, s>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   // dq of the local blocks (adds)

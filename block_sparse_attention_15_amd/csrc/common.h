@@ -110,6 +110,56 @@ __device__ __forceinline__ void vm_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// The valid rows of a head's persistent slots numbered consecutively
+// ("packed" rows, slot order): pre[s] = first packed row of slot s (prefix
+// sums of the lengths clamped to [0, C]), pre[S] = the head's valid rows;
+// with rowtab, rowtab[p] = s*C + r for packed row p (row r of slot s).  Every
+// thread of the workgroup calls it (it has barriers); returns pre[S].
+__device__ inline int packed_rows(const int32_t* plen, int S, int C, int* pre, int* rowtab, int nthreads) {
+  const int lane = threadIdx.x & 63;
+  for (int x = threadIdx.x; x < S; x += nthreads) pre[x] = min(max(plen[x], 0), C);
+  __syncthreads();
+  if (threadIdx.x < 64) {  // wave 0: exclusive scan, 64 slots per round
+    int run = 0;
+    for (int s0 = 0; s0 < S; s0 += 64) {
+      const int sl = s0 + lane;
+      const int n = sl < S ? pre[sl] : 0;
+      int x = n;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+      }
+      __builtin_amdgcn_wave_barrier();
+      if (sl < S) pre[sl] = run + x - n;
+      run += __shfl(x, 63, 64);
+    }
+    if (lane == 0) pre[S] = run;
+  }
+  __syncthreads();
+  if (rowtab) {
+    for (int x = threadIdx.x; x < S * C; x += nthreads) {
+      const int sl = x / C, r = x - sl * C;
+      const int b0 = pre[sl];
+      if (r < pre[sl + 1] - b0) rowtab[b0 + r] = x;
+    }
+    __syncthreads();
+  }
+  return pre[S];
+}
+
+// Slot holding packed row p (0 <= p < pre[S]): the last s with pre[s] <= p
+// (slots without rows share their start with the next slot).
+__device__ inline int packed_slot(const int* pre, int S, int p) {
+  int lo = 0, hi = S;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (pre[mid] <= p) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
 // Runs a set-up step (kernel attributes) once per device: run(f) calls f
 // with the caller's device current the first time that device is seen and
 // returns its status; later calls on that device return hipSuccess.  A failed

@@ -601,33 +601,7 @@ __global__ __launch_bounds__(kP2Threads, 1) void fwd_pers2_kernel(FwdArgs a) {
   // row table: packed row -> slot * C + row, from prefix sums of the lengths
   int* rowtab = reinterpret_cast<int*>(smem);  // [S*C]
   int* pre = rowtab + g.S * g.C;               // [S+1]
-  for (int x = threadIdx.x; x < g.S; x += kP2Threads) pre[x] = min(max(a.plen[bh * g.S + x], 0), g.C);
-  __syncthreads();
-  if (wave == 0) {
-    int run = 0;
-    for (int s0 = 0; s0 < g.S; s0 += 64) {
-      const int sl = s0 + lane;
-      const int n = sl < g.S ? pre[sl] : 0;
-      int x = n;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(x, o, 64);
-        if (lane >= o) x += y;
-      }
-      __builtin_amdgcn_wave_barrier();
-      if (sl < g.S) pre[sl] = run + x - n;
-      run += __shfl(x, 63, 64);
-    }
-    if (lane == 0) pre[g.S] = run;
-  }
-  __syncthreads();
-  const int nvalid = pre[g.S];
-  for (int x = threadIdx.x; x < g.S * g.C; x += kP2Threads) {
-    const int sl = x / g.C, r = x - sl * g.C;
-    const int b0 = pre[sl];
-    if (r < pre[sl + 1] - b0) rowtab[b0 + r] = x;
-  }
-  __syncthreads();
+  const int nvalid = packed_rows(a.plen + bh * g.S, g.S, g.C, pre, rowtab, kP2Threads);
 
   const int nsteps = (nvalid + Q::KEYS - 1) / Q::KEYS;
   if (nsteps > 0) {
