@@ -509,8 +509,12 @@ __device__ __forceinline__ void build_rowtab(const BwdArgs& a, size_t bh, int qg
     if (qb < g.nq) {
       const int p = a.topk[(bh * g.nq + qb) * g.K + t];
       if ((unsigned)p < (unsigned)g.nl) {
-        len = a.tab.blen[a.tab.pblk[p]];
-        if (r < len) tok = a.tab.pbase[p] + a.tab.btok[a.tab.pblk[p] * g.C + r];
+        // ring chunk slot and block of p by arithmetic: one dependent load
+        // after the top-k entry instead of three
+        const int cp = p / g.nq, j = p - cp * g.nq;
+        len = a.tab.blen[j];
+        const int tr = r < g.C ? a.tab.btok[j * g.C + r] : -1;  // < 0: past the block's end
+        if (tr >= 0) tok = cp * g.ct + tr;
       }
     }
     rowtab[x] = tok;

@@ -688,8 +688,14 @@ __device__ __forceinline__ void build_rowtab(const FwdArgs& a, size_t bh, int qg
     if (qb < g.nq) {
       const int p = a.topk[(bh * g.nq + qb) * g.K + t];
       if ((unsigned)p < (unsigned)g.nl) {
-        len = a.tab.blen[a.tab.pblk[p]];
-        tok = a.tab.pbase[p] + a.tab.btok[a.tab.pblk[p] * g.C + (r < len ? r : 0)];
+        // ring chunk slot and block of p by arithmetic, and the row's token
+        // and the block's first token loaded together: one dependent load
+        // after the top-k entry instead of three
+        const int cp = p / g.nq, j = p - cp * g.nq;
+        const int32_t* bt = a.tab.btok + j * g.C;
+        len = a.tab.blen[j];
+        const int tr = r < g.C ? bt[r] : -1, t0 = bt[0];  // tr < 0: past the block's end
+        tok = cp * g.ct + (tr >= 0 ? tr : t0);
       }
     }
     rowtab[x] = tok * D * 2;
