@@ -50,6 +50,9 @@ SMALL = {
     # 16x16 grid, head_dim 64, 8 slots: a slot count that is not a multiple of the persistent
     # kernels' three-deep load rotation
     "tiny_bf16": {**synth.workload("tiny_fp32"), "dtype": "bf16", "seed": 61},
+    # 252 persistent slots: the row tables of the packed persistent kernels (forward and dQ/dK)
+    # would exceed their 60 KB of LDS, so the per-slot kernels run, with the stored dS tiles
+    "big_persistent_bf16": ragged(persistent_cache_size=42 * 308, total_cache_size=4 * 308 + 42 * 308, seed=28),
     # 8x8 grid, one block per frame: 64-query chunks (two query tiles), one persistent slot,
     # two local blocks, top-1 -- most of a workgroup's slots and steps are padding
     "micro_bf16": ragged(frame_h=8, frame_w=8, chunk_frames=1, total_cache_size=3 * 64, local_cache_size=2 * 64,
