@@ -37,10 +37,14 @@ SMALL = {
     "ragged_bf16_d64_b2": ragged(head_dim=64, batch=2, seed=22),
     "ragged_fp32": ragged(dtype="fp32", seed=23),
     "dense_local_bf16": ragged(use_local_block_sparse_attn=0, seed=24),
-    # dense local window of 36 blocks (K = 36): more selected blocks than the local kernels' LDS
-    # row tables hold at head_dim 128, so their gathers look the row tokens up in global memory
+    # dense local window of 36 blocks (K = 36): 9 KB row tables in the local kernels (three
+    # workgroups per CU instead of four)
     "dense_local_wide_bf16": ragged(use_local_block_sparse_attn=0, local_cache_size=6 * 308,
                                     total_cache_size=6 * 308 + 3 * 308, seed=26),
+    # dense local window of 516 blocks (K = 516): more selected blocks than the local kernels'
+    # LDS row tables hold at head_dim 128, so their gathers look the row tokens up in global memory
+    "dense_local_huge_bf16": ragged(use_local_block_sparse_attn=0, local_cache_size=86 * 308,
+                                    total_cache_size=86 * 308 + 3 * 308, seed=29),
     # [3,4,4] blocks on a 10x14 grid: 12 blocks per 3-frame group (48/24/24/12 tokens)
     "block344_bf16": ragged(frame_h=10, frame_w=14, block_t=3, block_h=4, block_w=4, chunk_frames=3,
                             total_cache_size=9 * 140, local_cache_size=6 * 140, persistent_cache_size=3 * 140,
