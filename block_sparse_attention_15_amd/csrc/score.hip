@@ -20,8 +20,9 @@
 //     candidate (the candidates' pooled keys loaded coalesced, all loads of
 //     the first chunks issued with the query rows, and staged through LDS a
 //     chunk at a time; one thread per (candidate, query block)), per query
-//     block (one wave) a two-phase radix select of the top K and one softmax
-//     row, and the column sums of those rows (ascending rows);
+//     block a two-phase radix select of the top K (one wave) and, beside it
+//     on another wave, one softmax row, and the column sums of those rows
+//     (ascending rows);
 //  2. the masses: per (head, candidate) the sum of the workgroups' column
 //     sums in ascending workgroup order -- deterministic.
 #include <algorithm>
@@ -409,11 +410,16 @@ __global__ __launch_bounds__(kScoreThreads) void score_topk_kernel(Geo g, const 
     score_chunk(cb);
   }
   __syncthreads();
+  // waves 0..QPW-1 select the top K of their query block's local scores,
+  // waves 4..4+QPW-1 turn the same rows into softmax rows: the selecting
+  // waves take their keys into registers first, then both run side by side
+  static_assert(QPW <= 4 && kScoreThreads == 512, "selecting and softmax waves");
   const int i = i0 + w;
   float* row = sc + w * W;
-  if (w < QPW && i < g.nq) {
-    // keys: descending score, then ascending logical index (oldest chunk first)
-    unsigned hi[KPL], lo[KPL];
+  const bool selects = w < QPW && i < g.nq;
+  // keys: descending score, then ascending logical index (oldest chunk first)
+  unsigned hi[KPL], lo[KPL];
+  if (selects) {
 #pragma unroll
     for (int u = 0; u < KPL; ++u) {
       const int p = lane + 64 * u;
@@ -425,6 +431,9 @@ __global__ __launch_bounds__(kScoreThreads) void score_topk_kernel(Geo g, const 
         lo[u] = 0xffffffffu - (unsigned)(ring_wrap(cp - rh, g.R) * g.nq + (p - cp * g.nq));
       }
     }
+  }
+  __syncthreads();  // the keys are in registers: the rows may be overwritten
+  if (selects) {
     bool on[KPL];
     select_top<KPL>(hi, lo, g.K, on);
     int* fl = flag + w * g.nl;
@@ -446,18 +455,22 @@ __global__ __launch_bounds__(kScoreThreads) void score_topk_kernel(Geo g, const 
       if (sp) out[running + __builtin_popcountll(m & ((1ull << lane) - 1))] = p;
       running += __builtin_popcountll(m);
     }
+  }
+  const int wsm = w - 4;  // softmax wave of query block i0 + wsm
+  if (wsm >= 0 && wsm < QPW && i0 + wsm < g.nq) {
     // pooled softmax over valid slots and all local blocks, in place of the scores
+    float* srow = sc + wsm * W;
     float mx = -INFINITY;
-    for (int c = lane; c < W; c += 64) mx = fmaxf(mx, row[c]);
+    for (int c = lane; c < W; c += 64) mx = fmaxf(mx, srow[c]);
     mx = wave_max(mx);
     float sum = 0.f;
     for (int c = lane; c < W; c += 64) {  // each exponential once, kept in the row
-      const float x = row[c], e = x == -INFINITY ? 0.f : expf(x - mx);
-      row[c] = e;
+      const float x = srow[c], e = x == -INFINITY ? 0.f : expf(x - mx);
+      srow[c] = e;
       sum += e;
     }
     sum = wave_sum(sum);
-    for (int c = lane; c < W; c += 64) row[c] = row[c] / sum;
+    for (int c = lane; c < W; c += 64) srow[c] = srow[c] / sum;
   }
   __syncthreads();
   // this workgroup's column sums (rows in ascending order), in the masses'
