@@ -60,6 +60,33 @@ __host__ __device__ inline int block_token(const Geo& g, const BlockExt& e, int 
   return (e.f0 + f) * g.ft + (e.r0 + r) * g.fw + e.c0 + c;
 }
 
+// floor(n / d) for 0 <= n < 2^20 and 1 <= d < 2^20 by one multiply with the
+// hardware reciprocal: (n + 1/2) / d lies at least 1 / (2d) from an integer,
+// and the product's relative error (reciprocal 1 ulp, product 1/2 ulp) keeps
+// it closer than that for n below 2^20.
+__device__ __forceinline__ int small_div(int n, int d) {
+  return (int)(((float)n + 0.5f) * __builtin_amdgcn_rcpf((float)d));
+}
+
+// Local block p of the ring (chunk slot p / nq, chunk block p mod nq): the
+// ring token of its first row, its length, and the extents that place row r.
+struct LocBlock {
+  int base, len, nw, hw;
+};
+
+__device__ __forceinline__ LocBlock loc_block(const Geo& g, int p) {
+  const int cp = p / g.nq, j = p - cp * g.nq;
+  const BlockExt e = block_ext(g, j);
+  return {cp * g.ct + e.f0 * g.ft + e.r0 * g.fw + e.c0, e.len, e.nw, e.nh * e.nw};
+}
+
+// Ring token of row r (0 <= r < b.len, r < 2^20) of a local block, raster order.
+__device__ __forceinline__ int loc_row(const Geo& g, const LocBlock& b, int r) {
+  const int f = small_div(r, b.hw), rem = r - f * b.hw;
+  const int y = small_div(rem, b.nw);
+  return b.base + f * g.ft + y * g.fw + (rem - y * b.nw);
+}
+
 // ---------------------------------------------------------------------------
 // Device-resident ring state
 // ---------------------------------------------------------------------------
@@ -212,7 +239,7 @@ constexpr int32_t kEmptySrc = INT32_MIN;
 // hipError_t of its launches.
 // ---------------------------------------------------------------------------
 // Geometry lookup tables (filled on the device by launch_geo_table at the
-// start of the attention entry points, in the caller's workspace): token
+// start of the backward entry point, in the caller's workspace): token
 // offset inside the chunk of row r of chunk block j (-1 past its length),
 // block lengths, and for every physical local block its chunk's first token
 // and its block index inside the chunk.

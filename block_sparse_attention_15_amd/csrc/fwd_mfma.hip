@@ -98,7 +98,6 @@ struct FwdArgs {
   float* lse_part;  // [B,H,ct]   its log-sum-exp (-inf when no slot is valid)
   float* blse_p;    // MASS: [B,H,S,ct] log2-sum-exp2 of each query's scaled scores (log2 units) over each slot's rows
   float* blse_l;    // MASS: [B,H,K,ct] ... over each of its selected local blocks
-  GeoTab tab;       // geometry lookup tables
   int ntiles;       // work items per (batch, head)
 };
 
@@ -668,38 +667,46 @@ constexpr int kLocThreads = 64 * kLocWaves;
 // rowtab[(w*K + t)*64 + r] = byte offset in the head's local K (or V) of row
 // r of query block w's t-th selected block; rows past the block's end repeat
 // its first row (finite; the tile masks them) and absent selections give 0
-// (no tile reads them); lentab[w*K + t] = that block's length (0 if absent).
-// Used when both fit in the LDS beside the two step buffers (four workgroups
-// share a CU while the table stays under about 8 KB, K <= 31); otherwise
-// every gather looks its row tokens up in global memory.
+// (no tile reads them); lentab[w*K + t] = that block's length (0 if absent);
+// binfo[w*K + t] = that block's first ring token and its length and extents
+// (8 bits each), from which the rows follow by arithmetic.  Used when the
+// tables fit in the LDS beside the two step buffers (four workgroups share a
+// CU while they stay under about 8 KB, K <= 30); otherwise every gather
+// places its rows itself.
 template <int D>
 constexpr size_t loc_tab_room() {
   return 160 * 1024 - 2 * (size_t)kLocBlocks * 64 * Shape<D>::ROWB;
 }
 
+constexpr size_t loc_tab_bytes(int K) { return (size_t)kLocBlocks * K * (64 * 4 + 8 + 4); }
+
 template <int D>
 __device__ __forceinline__ void build_rowtab(const FwdArgs& a, size_t bh, int qg, int nthreads, int* rowtab,
-                                             int* lentab) {
+                                             int2* binfo, int* lentab) {
   const Geo& g = a.g;
-  for (int x = threadIdx.x; x < kLocBlocks * g.K * 64; x += nthreads) {
-    const int w = x / (g.K * 64), t = (x / 64) % g.K, r = x & 63;
-    const int qb = qg * kLocBlocks + w;
-    int tok = 0, len = 0;
+  const int nb = kLocBlocks * g.K;
+  // one thread per selected block: where it sits in the ring (all top-k
+  // entries loaded at once, no table lookups behind them)
+  for (int x = threadIdx.x; x < nb; x += nthreads) {
+    const int w = x / g.K, qb = qg * kLocBlocks + w;
+    int2 bi = make_int2(0, 0);
     if (qb < g.nq) {
-      const int p = a.topk[(bh * g.nq + qb) * g.K + t];
+      const int p = a.topk[(bh * g.nq + qb) * g.K + (x - w * g.K)];
       if ((unsigned)p < (unsigned)g.nl) {
-        // ring chunk slot and block of p by arithmetic, and the row's token
-        // and the block's first token loaded together: one dependent load
-        // after the top-k entry instead of three
-        const int cp = p / g.nq, j = p - cp * g.nq;
-        const int32_t* bt = a.tab.btok + j * g.C;
-        len = a.tab.blen[j];
-        const int tr = r < g.C ? bt[r] : -1, t0 = bt[0];  // tr < 0: past the block's end
-        tok = cp * g.ct + (tr >= 0 ? tr : t0);
+        const LocBlock b = loc_block(g, p);  // len, nw, hw <= C <= 64
+        bi = make_int2(b.base, b.len | b.nw << 8 | b.hw << 16);
       }
     }
+    binfo[x] = bi;
+    lentab[x] = bi.y & 255;
+  }
+  __syncthreads();
+  for (int x = threadIdx.x; x < nb * 64; x += nthreads) {
+    const int r = x & 63;
+    const int2 bi = binfo[x >> 6];
+    const LocBlock b{bi.x, bi.y & 255, (bi.y >> 8) & 255, bi.y >> 16};
+    const int tok = r < b.len ? loc_row(g, b, r) : b.base;
     rowtab[x] = tok * D * 2;
-    if (r == 0) lentab[w * g.K + t] = len;
   }
 }
 
@@ -708,9 +715,9 @@ __device__ __forceinline__ void build_rowtab(const FwdArgs& a, size_t bh, int qg
 // of the buffer (lane l at byte 16*l); lane l fetches the global chunk whose
 // swizzled position is l's, so K and V land in their swizzled layouts.  TAB:
 // rows from the LDS row table as 32-bit byte offsets added to the head's base
-// (one add per load; a compile-time choice: if the global-memory lookup path
-// shares the loop, the compiler joins the two with a full wait).  Without the
-// table, rows past a selected block's end (and absent selections) load row 0
+// (one add per load; a compile-time choice: if the path that places rows per
+// load shares the loop, the compiler joins the two with a full wait).  Without
+// the table, rows past a selected block's end (and absent selections) load row 0
 // of the head's queries: finite values whose keys the tile masks.
 template <int D, bool TAB>
 __device__ __forceinline__ void loc_gather(const FwdArgs& a, size_t bh, int qg, int j, char* buf,
@@ -743,9 +750,9 @@ __device__ __forceinline__ void loc_gather(const FwdArgs& a, size_t bh, int qg, 
       const int qb = qg * kLocBlocks + w;
       if (qb < g.nq) {
         const int p = a.topk[(bh * g.nq + qb) * g.K + t];
-        if ((unsigned)p < (unsigned)g.nl && 32 * half + r < g.C) {
-          const int bt = a.tab.btok[a.tab.pblk[p] * g.C + 32 * half + r];
-          if (bt >= 0) tok = a.tab.pbase[p] + bt;
+        if ((unsigned)p < (unsigned)g.nl) {
+          const LocBlock b = loc_block(g, p);
+          if (32 * half + r < b.len) tok = loc_row(g, b, 32 * half + r);
         }
       }
     }
@@ -786,9 +793,10 @@ __global__ __launch_bounds__(kLocThreads) __attribute__((amdgpu_waves_per_eu(2, 
 
   const int nsteps = 2 * g.K;
   int* rowtab = reinterpret_cast<int*>(smem);
-  int* lentab = rowtab + kLocBlocks * g.K * 64;
+  int2* binfo = reinterpret_cast<int2*>(rowtab + kLocBlocks * g.K * 64);
+  int* lentab = reinterpret_cast<int*>(binfo + kLocBlocks * g.K);
   if (TAB) {
-    build_rowtab<D>(a, bh, qg, kLocThreads, rowtab, lentab);
+    build_rowtab<D>(a, bh, qg, kLocThreads, rowtab, binfo, lentab);
     __syncthreads();
   }
   loc_gather<D, TAB>(a, bh, qg, 0, kv0, rowtab);
@@ -803,7 +811,7 @@ __global__ __launch_bounds__(kLocThreads) __attribute__((amdgpu_waves_per_eu(2, 
         len = lentab[(wave >> 1) * g.K + (j >> 1)];
       } else {
         const int p = a.topk[(bh * g.nq + qb) * g.K + (j >> 1)];
-        if ((unsigned)p < (unsigned)g.nl) len = a.tab.blen[a.tab.pblk[p]];
+        if ((unsigned)p < (unsigned)g.nl) len = block_ext(g, p % g.nq).len;
       }
       nv = min(len - 32 * (j & 1), 32);
     }
@@ -885,7 +893,7 @@ hipError_t launch_d(const FwdArgs& base, hipStream_t s) {
   // keeps only the slot lengths there (at most 2048 slots)
   const size_t shm = MASS ? 2 * kBufBytes : (size_t)base.g.S * 4;
   const Geo& g0 = base.g;
-  const size_t tabb = (size_t)kLocBlocks * g0.K * 64 * 4 + (size_t)kLocBlocks * g0.K * 4;
+  const size_t tabb = loc_tab_bytes(g0.K);
   const bool tab = tabb <= loc_tab_room<D>() && (size_t)g0.NL * D * 2 < ((size_t)1 << 31);  // 32-bit row offsets
   const size_t shm_loc = tab ? tabb : 0;  // row tables (step buffers are static)
   {
@@ -930,20 +938,17 @@ bool fwd_mfma_supported(const Geo& g) {
 }
 
 size_t fwd_mfma_workspace(const Geo& g) {
-  return geo_table_bytes(g) + ((size_t)g.B * g.H * g.ct * g.D * 4 + 255) / 256 * 256 +
+  return ((size_t)g.B * g.H * g.ct * g.D * 4 + 255) / 256 * 256 +
          ((size_t)g.B * g.H * g.ct * 4 + 255) / 256 * 256;
 }
 
 hipError_t launch_fwd_mfma(const Geo& g, const void* q, const void* k_p, const void* v_p, const int32_t* plen,
                            const void* k_l, const void* v_l, const int32_t* topk, void* o, float* lse, void* ws,
                            float* blse_p, float* blse_l, hipStream_t s) {
-  GeoTab tab;
-  hipError_t e = launch_geo_table(g, ws, &tab, s);
-  if (e != hipSuccess) return e;
-  float* o_part = (float*)((char*)ws + geo_table_bytes(g));
+  float* o_part = (float*)ws;
   float* lse_part = (float*)((char*)o_part + ((size_t)g.B * g.H * g.ct * g.D * 4 + 255) / 256 * 256);
   FwdArgs a{g, (const bf16_t*)q, (const bf16_t*)k_p, (const bf16_t*)v_p, plen, (const bf16_t*)k_l,
-            (const bf16_t*)v_l, topk, (bf16_t*)o, lse, o_part, lse_part, blse_p, blse_l, tab, 0};
+            (const bf16_t*)v_l, topk, (bf16_t*)o, lse, o_part, lse_part, blse_p, blse_l, 0};
   if (blse_p) return g.D == 128 ? launch_d<128, true>(a, s) : launch_d<64, true>(a, s);
   return g.D == 128 ? launch_d<128, false>(a, s) : launch_d<64, false>(a, s);
 }

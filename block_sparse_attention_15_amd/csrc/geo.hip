@@ -1,10 +1,11 @@
-// Geometry lookup tables for the gather paths of the attention kernels.
+// Geometry lookup tables for the gather paths of the backward kernels.
 //
 // The tiling (block-row-major [block_t, block_h, block_w] blocks with smaller
 // edge blocks) needs integer divisions by runtime sizes to map (block, row)
 // to a token.  The matrix-core kernels gather 16-byte chunks of many rows per
 // step, so they read these precomputed tables instead: one small launch per
-// call fills them in the caller's workspace.
+// call fills them in the caller's workspace.  (The forward places its rows
+// by arithmetic once per workgroup and launches no table kernel.)
 #include "common.h"
 
 namespace pbsa {
