@@ -168,7 +168,7 @@ pbsa_status make_plan(const pbsa_config* c, Plan* p) {
   in.ws_score_select = score_workspace(g);
   in.ws_fwd = fwd_workspace(g);
   in.ws_bwd = align256(zrow_offset(BH * g.ct) * 4 + 256) + align256(BH * g.ct * 4 + 4) + 2 * align256(BH * g.nl * 4) +
-              align256(BH * g.nl * g.nq * 4) + align256(bwd_ds_bytes(g)) + geo_table_bytes(g);
+              align256(BH * g.nl * g.nq * 4) + align256(bwd_ds_bytes(g));
   in.ws_persist_update = update_workspace(g);
   in.ws_fwd_mass = align256(in.ws_fwd) + align256(BH * g.S * g.ct * 4) + align256(BH * g.K * g.ct * 4) +
                    align256(BH * g.nq * g.nl * 4);
@@ -392,8 +392,6 @@ pbsa_status pbsa_bwd(const pbsa_config* cfg, const void* q, const void* k_pers, 
   w.korder = (int32_t*)base;
   base += align256(BH * p.g.nl * 4);
   w.dsb = base;
-  base += align256(bwd_ds_bytes(p.g));
-  w.geo = base;
   return hip_status(launch_bwd(p.g, q, k_pers, v_pers, persist_len, k_local, v_local, topk_idx, o, lse, dout, dq,
                                dk_pers, dv_pers, dk_local, dv_local, w, (hipStream_t)stream),
                     "pbsa_bwd");

@@ -257,7 +257,6 @@ struct BwdArgs {
   float* dvp;
   float* dkl;
   float* dvl;
-  GeoTab tab;
   int ntiles;
   int pk;  // dq_pers / dk_ds run on packed persistent rows (dkv_pers then zeroes dK past the slot lengths)
 };
@@ -492,33 +491,39 @@ constexpr int kLocBlocks = 1;  // query blocks per workgroup (2 waves each)
 constexpr int kDqlThreads = 64 * 2 * kLocBlocks;
 
 // Row tokens of every step of this workgroup, built once in LDS (see the
-// forward's local kernel): rowtab[(w*K + t)*64 + r], lentab[w*K + t].  Used
-// when both fit in the LDS beside the two step buffers.
+// forward's local kernel): rowtab[(w*K + t)*64 + r] (-1 past the block's
+// end), binfo[w*K + t], lentab[w*K + t].  Used when they fit in the LDS
+// beside the two step buffers; otherwise every gather places its rows.
 template <int D>
 constexpr size_t dql_tab_room() {
   return 160 * 1024 - 2 * (size_t)kLocBlocks * 2 * Sh<D>::TILEB;
 }
 
 __device__ __forceinline__ void build_rowtab(const BwdArgs& a, size_t bh, int qg, int nthreads, int* rowtab,
-                                             int* lentab) {
+                                             int2* binfo, int* lentab) {
   const Geo& g = a.g;
-  for (int x = threadIdx.x; x < kLocBlocks * g.K * 64; x += nthreads) {
-    const int w = x / (g.K * 64), t = (x / 64) % g.K, r = x & 63;
-    const int qb = qg * kLocBlocks + w;
-    int tok = -1, len = 0;
+  const int nb = kLocBlocks * g.K;
+  // one thread per selected block: where it sits in the ring (binfo: first
+  // ring token; length and extents, 8 bits each)
+  for (int x = threadIdx.x; x < nb; x += nthreads) {
+    const int w = x / g.K, qb = qg * kLocBlocks + w;
+    int2 bi = make_int2(0, 0);
     if (qb < g.nq) {
-      const int p = a.topk[(bh * g.nq + qb) * g.K + t];
+      const int p = a.topk[(bh * g.nq + qb) * g.K + (x - w * g.K)];
       if ((unsigned)p < (unsigned)g.nl) {
-        // ring chunk slot and block of p by arithmetic: one dependent load
-        // after the top-k entry instead of three
-        const int cp = p / g.nq, j = p - cp * g.nq;
-        len = a.tab.blen[j];
-        const int tr = r < g.C ? a.tab.btok[j * g.C + r] : -1;  // < 0: past the block's end
-        if (tr >= 0) tok = cp * g.ct + tr;
+        const LocBlock b = loc_block(g, p);  // len, nw, hw <= C <= 64
+        bi = make_int2(b.base, b.len | b.nw << 8 | b.hw << 16);
       }
     }
-    rowtab[x] = tok;
-    if (r == 0) lentab[w * g.K + t] = len;
+    binfo[x] = bi;
+    lentab[x] = bi.y & 255;
+  }
+  __syncthreads();
+  for (int x = threadIdx.x; x < nb * 64; x += nthreads) {
+    const int r = x & 63;
+    const int2 bi = binfo[x >> 6];
+    const LocBlock b{bi.x, bi.y & 255, (bi.y >> 8) & 255, bi.y >> 16};
+    rowtab[x] = r < b.len ? loc_row(g, b, r) : -1;  // -1: past the block's end
   }
 }
 
@@ -555,9 +560,9 @@ __device__ __forceinline__ void loc_gather(const BwdArgs& a, size_t bh, int qg, 
       const int qb = qg * kLocBlocks + w;
       if (qb < g.nq) {
         const int p = a.topk[(bh * g.nq + qb) * g.K + t];
-        if ((unsigned)p < (unsigned)g.nl && 32 * half + r < g.C) {
-          const int bt = a.tab.btok[a.tab.pblk[p] * g.C + 32 * half + r];
-          if (bt >= 0) tok = a.tab.pbase[p] + bt;
+        if ((unsigned)p < (unsigned)g.nl) {
+          const LocBlock b = loc_block(g, p);
+          if (32 * half + r < b.len) tok = loc_row(g, b, 32 * half + r);
         }
       }
     }
@@ -594,9 +599,10 @@ __global__ __launch_bounds__(kDqlThreads) __attribute__((amdgpu_waves_per_eu(2, 
   const float c2 = g.scale * kLog2e;
   const int nsteps = 2 * g.K;
   int* rowtab = reinterpret_cast<int*>(smem);
-  int* lentab = rowtab + kLocBlocks * g.K * 64;
+  int2* binfo = reinterpret_cast<int2*>(rowtab + kLocBlocks * g.K * 64);
+  int* lentab = reinterpret_cast<int*>(binfo + kLocBlocks * g.K);
   if (TAB) {
-    build_rowtab(a, bh, qg, kDqlThreads, rowtab, lentab);
+    build_rowtab(a, bh, qg, kDqlThreads, rowtab, binfo, lentab);
     __syncthreads();
   }
   loc_gather<D, TAB>(a, bh, qg, 0, kv0, rowtab);
@@ -610,7 +616,7 @@ __global__ __launch_bounds__(kDqlThreads) __attribute__((amdgpu_waves_per_eu(2, 
         len = lentab[(wave >> 1) * g.K + (j >> 1)];
       } else {
         const int p = a.topk[(bh * g.nq + qb) * g.K + (j >> 1)];
-        if ((unsigned)p < (unsigned)g.nl) len = a.tab.blen[a.tab.pblk[p]];
+        if ((unsigned)p < (unsigned)g.nl) len = block_ext(g, p % g.nq).len;
       }
       nv = min(len - 32 * (j & 1), 32);
     }
@@ -1080,23 +1086,29 @@ template <int D> struct KvlGather {
   static constexpr int UPT = Sh<D>::TILEB / 1024;  // KB units per 32-row tile
   static constexpr int UPW = UPT / kKvlWaves;      // units of each tensor per wave
   static constexpr int BUF = 2 * Sh<D>::TILEB + 256;  // Q tile, dO tile, lse2[32], D[32]
-  int tok[UPW];  // row tokens of this lane's units in the next step (-1: no row)
-  int tokl;      // row token of row lane%32 (lse2 / D, gathered by wave 0)
+  // The next step's rows, read from LDS by tokens() and put together by
+  // gather() a step later (so nothing waits for the reads in between): the
+  // block's first token and length, the step's half, and the in-block
+  // offsets of this lane's rows (units, and row lane%32 for lse2 / D).
+  int tbase, tlen, thalf;
+  int toff[UPW];
+  int toffl;
 
-  // step = (selecting-list index << 1) | half
-  __device__ __forceinline__ void tokens(const BwdArgs& a, const int* sel, const int* slen, int step) {
-    const Geo& g = a.g;
+  // step = (selecting-list index << 3) | (shape class << 1) | half;
+  // sbase[i], slen[i] = first token and length of selecting block i;
+  // shape_off[c*64 + r] = offset of row r from the first token in class c.
+  // (Plain int reads: reads of a vector type made the compiler wait for the
+  // gather in flight.)
+  __device__ __forceinline__ void tokens(const int* sbase, const int* slen, const int* shape_off, int step) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int sidx = step >> 1, half = step & 1;
-    const int len = slen[sidx];
-    const int32_t* rows = a.tab.btok + sel[sidx] * g.C;
+    const int sidx = step >> 3, half = step & 1;
+    const int* off = shape_off + ((step >> 1) & 3) * 64;
+    tbase = sbase[sidx];
+    tlen = slen[sidx];
+    thalf = half;
 #pragma unroll
-    for (int i = 0; i < UPW; ++i) {
-      const int r = 32 * half + RPK * (wave * UPW + i) + lane / Sh<D>::CPR;
-      tok[i] = r < len ? rows[r] : -1;
-    }
-    const int rl = 32 * half + (threadIdx.x & 31);
-    tokl = rl < len ? rows[rl] : -1;
+    for (int i = 0; i < UPW; ++i) toff[i] = off[32 * half + RPK * (wave * UPW + i) + lane / Sh<D>::CPR];
+    toffl = off[32 * half + (threadIdx.x & 31)];
   }
   // Issue the gather of the step whose tokens are held into buf: Q and dO
   // rows, and (wave 0) the rows' lse2 and D, lanes 0-31 and 32-63.  Rows
@@ -1112,7 +1124,8 @@ template <int D> struct KvlGather {
     for (int i = 0; i < UPW; ++i) {
       const int u = wave * UPW + i;
       const int r = RPK * u + rr;
-      const int off = max(tok[i], 0) * D + swz(r, pos, Sh<D>::CPR) * 8;
+      const int tok = 32 * thalf + r < tlen ? tbase + toff[i] : 0;
+      const int off = tok * D + swz(r, pos, Sh<D>::CPR) * 8;
       __builtin_amdgcn_global_load_lds(qb + off, (__attribute__((address_space(3))) void*)(buf + u * 1024), 16, 0,
                                        0);
       __builtin_amdgcn_global_load_lds(db + off,
@@ -1122,22 +1135,24 @@ template <int D> struct KvlGather {
     if (wave == 0) {
       // rows without a token read the sentinel after the last head: lse2 = +inf
       // (probability 0, so their dV and dS terms vanish) and D = 0
-      const size_t ro = tokl >= 0 ? bh * g.ct + tokl : (size_t)g.B * g.H * g.ct;
+      const size_t ro = 32 * thalf + (lane & 31) < tlen ? bh * g.ct + tbase + toffl : (size_t)g.B * g.H * g.ct;
       __builtin_amdgcn_global_load_lds(lane < 32 ? a.lse2 + ro : a.delta + ro,
                                        (__attribute__((address_space(3))) void*)(buf + 2 * Sh<D>::TILEB), 4, 0, 0);
     }
   }
 };
 
-// LDS beyond the two static step buffers: the selecting list, lengths and steps.
-constexpr size_t kvl_lds(int nq) { return 4 * (size_t)nq * 4; }
+// LDS beyond the static arrays: the row offsets of the four block shapes,
+// the selecting blocks' first tokens and their lengths and shape classes,
+// and the steps (up to two per block).
+constexpr size_t kvl_lds(int nq) { return 4 * 64 * 4 + (size_t)nq * (4 + 4 + 2 * 4); }
 
 // The key-outer pass of one role (dV or dK) over the workgroup's step list;
 // every wave runs the same number of barriers and gathers whatever its role.
 template <int D, bool DV>
-__device__ __forceinline__ void kvl_pass(const BwdArgs& a, size_t bh, int p, int kt, const int* sel,
-                                         const int* slen, const int* steps, int nsteps, char* kv0, char* kv1,
-                                         float4* pex) {
+__device__ __forceinline__ void kvl_pass(const BwdArgs& a, size_t bh, int p, int kt, const int* sbase,
+                                         const int* slen, const int* shape_off, const int* steps, int nsteps,
+                                         char* kv0, char* kv1, float4* pex) {
   const Geo& g = a.g;
   const int l32 = threadIdx.x & 31;
   const BlockExt ke = block_ext(g, p % g.nq);
@@ -1151,9 +1166,9 @@ __device__ __forceinline__ void kvl_pass(const BwdArgs& a, size_t bh, int p, int
   const float c2 = g.scale * kLog2e;
   KvlGather<D> ga;
   if (nsteps > 0) {
-    ga.tokens(a, sel, slen, steps[0]);
+    ga.tokens(sbase, slen, shape_off, steps[0]);
     ga.gather(a, bh, kv0);
-    if (nsteps > 1) ga.tokens(a, sel, slen, steps[1]);
+    if (nsteps > 1) ga.tokens(sbase, slen, shape_off, steps[1]);
   }
   __syncthreads();  // its fence waits for the gather
   // unrolled by two so that each step's buffers are compile-time arrays
@@ -1161,7 +1176,7 @@ __device__ __forceinline__ void kvl_pass(const BwdArgs& a, size_t bh, int p, int
     auto mid = [&]() {
       if (i + 1 < nsteps) {
         ga.gather(a, bh, nxt);
-        if (i + 2 < nsteps) ga.tokens(a, sel, slen, steps[i + 2]);
+        if (i + 2 < nsteps) ga.tokens(sbase, slen, shape_off, steps[i + 2]);
       }
     };
     // mid-step barrier: the dV wave of each key tile has written its P
@@ -1213,29 +1228,46 @@ __global__ __launch_bounds__(kKvlThreads, 2) void dkv_local_kernel(BwdArgs a) {
   const int wave = threadIdx.x >> 6;
   const int kt = wave & 1, role = wave >> 1;  // role 0: dV, role 1: dK
 
-  // selecting query blocks (ascending), their lengths and the step list, in LDS
+  // Row offsets inside a block by shape class (bit 1: a last block row of
+  // fewer than block_h rows, bit 0: a last block column narrower than
+  // block_w), one thread per (class, row).  Every block of a class places
+  // its rows alike, so a row's token is one LDS read and an add.
+  static_assert(kKvlThreads == 4 * 64, "one thread per shape class and row");
+  int* shape_off = reinterpret_cast<int*>(smem);
+  {
+    const int c = threadIdx.x >> 6, r = threadIdx.x & 63;
+    const int nh = (c & 2) ? g.fh - (g.nbr - 1) * g.bh : g.bh;
+    const int nw = (c & 1) ? g.fw - (g.nbc - 1) * g.bw : g.bw;
+    const int f = r / (nh * nw), rem = r - f * nh * nw, y = rem / nw;
+    shape_off[threadIdx.x] = f * g.ft + y * g.fw + (rem - y * nw);
+  }
+  // selecting query blocks (ascending): each one's first token in the chunk
+  // and its length and shape class, and the step list, in LDS
   const int ncount = a.tcount[bh * g.nl + p];
   const int32_t* lst = a.tlist + (bh * g.nl + p) * g.nq;
-  int* sel = reinterpret_cast<int*>(smem);
-  int* slen = sel + g.nq;
+  int* sbase = shape_off + 4 * 64;
+  int* slen = sbase + g.nq;
   int* steps = slen + g.nq;
   for (int x = threadIdx.x; x < ncount; x += kKvlThreads) {
-    const int blk = lst[x];
-    sel[x] = blk;
-    slen[x] = a.tab.blen[blk];
+    const BlockExt e = block_ext(g, lst[x]);
+    const int cls = (e.nh != g.bh ? 2 : 0) | (e.nw != g.bw ? 1 : 0);
+    sbase[x] = e.f0 * g.ft + e.r0 * g.fw + e.c0;
+    slen[x] = e.len | cls << 8;  // the class moves into the steps below
   }
   __syncthreads();
   int nsteps = 0;
   for (int x = 0; x < ncount; ++x) {
-    const int nh = (slen[x] + 31) / 32;
-    if ((int)threadIdx.x < nh) steps[nsteps + threadIdx.x] = (x << 1) | threadIdx.x;
+    const int lc = slen[x], nh = ((lc & 255) + 31) / 32;
+    if ((int)threadIdx.x < nh) steps[nsteps + threadIdx.x] = (x << 3) | (lc >> 8) << 1 | threadIdx.x;
     nsteps += nh;
   }
   __syncthreads();
+  for (int x = threadIdx.x; x < ncount; x += kKvlThreads) slen[x] &= 255;
+  __syncthreads();
   if (role == 0)
-    kvl_pass<D, true>(a, bh, p, kt, sel, slen, steps, nsteps, kv0, kv1, pex[kt]);
+    kvl_pass<D, true>(a, bh, p, kt, sbase, slen, shape_off, steps, nsteps, kv0, kv1, pex[kt]);
   else
-    kvl_pass<D, false>(a, bh, p, kt, sel, slen, steps, nsteps, kv0, kv1, pex[kt]);
+    kvl_pass<D, false>(a, bh, p, kt, sbase, slen, shape_off, steps, nsteps, kv0, kv1, pex[kt]);
 }
 
 template <typename K>
@@ -1259,7 +1291,7 @@ hipError_t launch_d(const BwdArgs& base, hipStream_t s) {
   const size_t tab_dq = ((size_t)g.S * g.C + g.S + 1) * 4;
   const bool pk = g.S > 0 && tab_dq <= kDqTableMax;
   const size_t shm_dq = 2 * 4 * Sh<D>::TILEB + (pk ? tab_dq : g.S * 4);  // 2 x (K,K,V,V), row table or lengths
-  const size_t tabb = (size_t)kLocBlocks * g.K * 64 * 4 + (size_t)kLocBlocks * g.K * 4;
+  const size_t tabb = (size_t)kLocBlocks * g.K * (64 * 4 + 8 + 4);
   const bool tab = tabb <= dql_tab_room<D>();
   const size_t shm_dql = tab ? tabb : 0;  // local: row tables (step buffers are static)
   const size_t shm_kvl = kvl_lds(g.nq);
@@ -1337,8 +1369,8 @@ size_t bwd_ds_tile_bytes(const Geo& g) {
 
 size_t bwd_ds_bytes(const Geo& g) { return g.ds ? bwd_ds_tile_bytes(g) : 0; }
 
-// Preparation (key-block index and its launch order, D and lse*log2(e), the
-// geometry table), then the MFMA kernels, all on the caller's stream.
+// Preparation (key-block index and its launch order, D and lse*log2(e)),
+// then the MFMA kernels, all on the caller's stream.
 hipError_t launch_bwd_mfma(const Geo& g, const void* q, const void* k_p, const void* v_p, const int32_t* plen,
                            const void* k_l, const void* v_l, const int32_t* topk, const void* o, const float* lse,
                            const void* dout, float* dq, float* dk_p, float* dv_p, float* dk_l, float* dv_l,
@@ -1346,11 +1378,9 @@ hipError_t launch_bwd_mfma(const Geo& g, const void* q, const void* k_p, const v
   hipError_t e = hipSuccess;
   if ((e = launch_bwd_index(g, topk, ws, s)) != hipSuccess) return e;
   if ((e = launch_bwd_delta(g, o, dout, lse, ws, s)) != hipSuccess) return e;
-  GeoTab tab;
-  if ((e = launch_geo_table(g, ws.geo, &tab, s)) != hipSuccess) return e;
   BwdArgs a{g, (const bf16_t*)q, (const bf16_t*)k_p, (const bf16_t*)v_p, plen, (const bf16_t*)k_l,
             (const bf16_t*)v_l, topk, lse, ws.delta, ws.lse2, (const bf16_t*)dout, ws.tcount, ws.tlist,
-            ws.korder, (const bf16_t*)ws.zrow, (bf16_t*)ws.dsb, dq, dk_p, dv_p, dk_l, dv_l, tab, 0};
+            ws.korder, (const bf16_t*)ws.zrow, (bf16_t*)ws.dsb, dq, dk_p, dv_p, dk_l, dv_l, 0};
   return g.D == 128 ? launch_d<128>(a, s) : launch_d<64>(a, s);
 }
 

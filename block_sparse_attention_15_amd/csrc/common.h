@@ -238,25 +238,12 @@ constexpr int32_t kEmptySrc = INT32_MIN;
 // Launchers implemented in the kernel translation units.  Each returns the
 // hipError_t of its launches.
 // ---------------------------------------------------------------------------
-// Geometry lookup tables (filled on the device by launch_geo_table at the
-// start of the backward entry point, in the caller's workspace): token
-// offset inside the chunk of row r of chunk block j (-1 past its length),
-// block lengths, and for every physical local block its chunk's first token
-// and its block index inside the chunk.
-struct GeoTab {
-  const int32_t* btok;   // [nq][C]
-  const int32_t* blen;   // [nq]
-  const int32_t* pbase;  // [nl]
-  const int32_t* pblk;   // [nl]
-};
-size_t geo_table_bytes(const Geo& g);
 // Bytes of the persistent dS tiles that the MFMA backward passes from its dQ
 // kernel to its dK kernel, whether or not g.ds selects that path.
 size_t bwd_ds_tile_bytes(const Geo& g);
 // The same where g.ds is set, else 0.
 size_t bwd_ds_bytes(const Geo& g);
 bool bwd_mfma_supported(const Geo& g);
-hipError_t launch_geo_table(const Geo& g, void* ws, GeoTab* tab, hipStream_t s);
 
 // Query blocks per score workgroup at a geometry (4, 2 or 1: the largest whose LDS fits).
 int score_qpw(const Geo& g);
@@ -295,7 +282,6 @@ struct WsBwd {
   int32_t* tlist;   // [B,H,nl,nq]   their ids, ascending
   int32_t* korder;  // [B,H,nl]      local blocks in key-outer launch order (see bwd_korder_kernel)
   void* dsb;        // bwd_ds_bytes: dS of the persistent slots as bf16 32x32 tiles (MFMA path)
-  void* geo;        // geometry tables (geo_table_bytes)
 };
 // Backward preparation: D = rowsum(dO * O) and lse * log2(e) (with the
 // sentinel entries), and the key-block -> query-block index with its launch
