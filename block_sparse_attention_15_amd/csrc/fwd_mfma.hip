@@ -223,6 +223,14 @@ __device__ __forceinline__ float tile(const char* kbase, const char* vbase, int 
       for (int n = 0; n < NT; ++n)
         if (n < ntq) s[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], st.qf[n][ks], s[n], 0, 0, 0);
     }
+    if constexpr (EARLY) {
+      // the local kernel: every K read issued before the first product, then
+      // one partial wait per product (the scheduler would interleave them a
+      // pair at a time with full waits; 68 -> 66 us).  The persistent kernels
+      // measured slower with it: their eight waves read the same tile.
+      __builtin_amdgcn_sched_group_barrier(0x100, Sh::KS, 0);    // DS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, Sh::KS * NT, 0);  // MFMAs
+    }
   }
   // V^T operands read now if not yet: they do not depend on P, so their
   // latency is covered by the softmax below
