@@ -255,16 +255,17 @@ __device__ __forceinline__ float tile(const char* kbase, const char* vbase, int 
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
     if (n < ntq) {
-      // tree reductions (max, then the row sum below): short dependency chains
-      float m8[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) m8[j] = fmaxf(s[n][j], s[n][j + 8]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) m8[j] = fmaxf(m8[j], m8[j + 4]);
-      float tm = fmaxf(fmaxf(m8[0], m8[2]), fmaxf(m8[1], m8[3]));
-      tm = half_max(tm) * c2;
-      // raise the running max only when the tile exceeds it by more than 2^8
-      if (__builtin_amdgcn_ballot_w64(tm > st.m[n] + 8.0f)) {
+      // tree reductions (max, then the row sum below): short dependency
+      // chains; the max of this lane's 16 scores in eight 3-input maxes
+      auto mx3 = [](float x, float y, float z) { return fmaxf(fmaxf(x, y), z); };
+      const float* sv = reinterpret_cast<const float*>(&s[n]);
+      const float tl = fmaxf(mx3(mx3(sv[0], sv[1], sv[2]), mx3(sv[3], sv[4], sv[5]), mx3(sv[6], sv[7], sv[8])),
+                             mx3(mx3(sv[9], sv[10], sv[11]), mx3(sv[12], sv[13], sv[14]), sv[15]));
+      // raise the running max only when the tile exceeds it by more than 2^8:
+      // a row does exactly when one of its two lanes does, so the lanes test
+      // their own maxima and the row max is formed only then
+      if (__builtin_amdgcn_ballot_w64(tl * c2 > st.m[n] + 8.0f)) {
+        const float tm = half_max(tl) * c2;
         const float mn = fmaxf(st.m[n], tm);
         const float f = __builtin_amdgcn_exp2f(st.m[n] - mn);
         st.l[n] *= f;
