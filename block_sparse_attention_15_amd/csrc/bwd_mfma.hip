@@ -567,7 +567,7 @@ __device__ __forceinline__ void loc_gather(const BwdArgs& a, size_t bh, int qg, 
       }
     }
     const bf16_t* src = (tok >= 0 ? (tensor ? vb : kb) + (size_t)tok * D : a.zrow) + c * 8;
-    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(buf + u * 1024), 16, 0, 0);
+    PBSA_LDS_LOAD(src, (__attribute__((address_space(3))) void*)(buf + u * 1024), 16, 0, 0);
   }
 }
 
@@ -843,12 +843,12 @@ template <int D> struct PersDma {
       const int u = wave * NU + i, t = u / UPT, uu = u % UPT;  // t: 0 Q, 1 dO
       const int r = RPK * uu + rr;
       const bf16_t* src = (t ? a.dout : a.q) + (hb + min(row0 + r, g.ct - 1)) * D + swz(r, pos, Sh<D>::CPR) * 8;
-      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(buf + t * Sh<D>::TILEB + uu * 1024),
+      PBSA_LDS_LOAD(src, (__attribute__((address_space(3))) void*)(buf + t * Sh<D>::TILEB + uu * 1024),
                                        16, 0, 0);
     }
     const int rl = row0 + (lane & 31);
     const size_t ro = rl < g.ct ? hb + rl : (size_t)g.B * g.H * g.ct;
-    __builtin_amdgcn_global_load_lds(lane < 32 ? a.lse2 + ro : a.delta + ro,
+    PBSA_LDS_LOAD(lane < 32 ? a.lse2 + ro : a.delta + ro,
                                      (__attribute__((address_space(3))) void*)(buf + 2 * Sh<D>::TILEB), 4, 0, 0);
   }
 };
@@ -953,7 +953,7 @@ template <int D> struct DsDma {
     for (int i = 0; i < NQ; ++i) {
       const int u = (wave * NQ + i) % UPT, r = RPK * u + rr;
       const bf16_t* src = a.q + (bh * g.ct + min(row0 + r, g.ct - 1)) * D + swz(r, pos, Sh<D>::CPR) * 8;
-      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(buf + u * 1024), 16, 0, 0);
+      PBSA_LDS_LOAD(src, (__attribute__((address_space(3))) void*)(buf + u * 1024), 16, 0, 0);
     }
     // the dS tile, read once: a streaming (nt) load, so that the 2 KB tiles
     // of the whole pass do not evict what the caches hold for later kernels
@@ -961,7 +961,7 @@ template <int D> struct DsDma {
     constexpr int kNt = 2;  // cache-policy operand: nt
 #pragma unroll
     for (int u = 0; u < 2; ++u)
-      __builtin_amdgcn_global_load_lds(ds + u * 512,
+      PBSA_LDS_LOAD(ds + u * 512,
                                        (__attribute__((address_space(3))) void*)(buf + QB + wave * 2048 + u * 1024),
                                        16, 0, kNt);
   }
@@ -1126,9 +1126,9 @@ template <int D> struct KvlGather {
       const int r = RPK * u + rr;
       const int tok = 32 * thalf + r < tlen ? tbase + toff[i] : 0;
       const int off = tok * D + swz(r, pos, Sh<D>::CPR) * 8;
-      __builtin_amdgcn_global_load_lds(qb + off, (__attribute__((address_space(3))) void*)(buf + u * 1024), 16, 0,
+      PBSA_LDS_LOAD(qb + off, (__attribute__((address_space(3))) void*)(buf + u * 1024), 16, 0,
                                        0);
-      __builtin_amdgcn_global_load_lds(db + off,
+      PBSA_LDS_LOAD(db + off,
                                        (__attribute__((address_space(3))) void*)(buf + Sh<D>::TILEB + u * 1024),
                                        16, 0, 0);
     }
@@ -1136,7 +1136,7 @@ template <int D> struct KvlGather {
       // rows without a token read the sentinel after the last head: lse2 = +inf
       // (probability 0, so their dV and dS terms vanish) and D = 0
       const size_t ro = 32 * thalf + (lane & 31) < tlen ? bh * g.ct + tbase + toffl : (size_t)g.B * g.H * g.ct;
-      __builtin_amdgcn_global_load_lds(lane < 32 ? a.lse2 + ro : a.delta + ro,
+      PBSA_LDS_LOAD(lane < 32 ? a.lse2 + ro : a.delta + ro,
                                        (__attribute__((address_space(3))) void*)(buf + 2 * Sh<D>::TILEB), 4, 0, 0);
     }
   }

@@ -132,10 +132,31 @@ template <int N>
 __device__ __forceinline__ void vm_barrier() {
   static_assert(N >= 0 && N < 16, "vmcnt");
   asm volatile("" ::: "memory");
+#if PBSA_LDS_RACE_CHECK
+  __builtin_amdgcn_s_waitcnt(0);  // check build: every load and LDS access done first
+#else
   __builtin_amdgcn_s_waitcnt(0x070 | N);  // vmcnt(N), lgkmcnt(0), expcnt not waited for
+#endif
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
+
+// One LDS-bound load (global_load_lds).  The LDS-race check build
+// (PBSA_LDS_RACE_CHECK, a second library built beside the product one) waits
+// for each at once, so its bytes land as early as its issue allows, and every
+// step barrier drains all loads in flight: a kernel whose waves read a buffer
+// before its rows land, or issue rows into a buffer that another wave still
+// reads, then gives different results from the product build, which keeps
+// the loads in flight across the barriers.  The two builds must agree bitwise.
+#if PBSA_LDS_RACE_CHECK
+#define PBSA_LDS_LOAD(src, dst, size, off, aux)                \
+  do {                                                         \
+    __builtin_amdgcn_global_load_lds(src, dst, size, off, aux); \
+    __builtin_amdgcn_s_waitcnt(0x0F70); /* vmcnt(0) */          \
+  } while (0)
+#else
+#define PBSA_LDS_LOAD(src, dst, size, off, aux) __builtin_amdgcn_global_load_lds(src, dst, size, off, aux)
+#endif
 
 // The valid rows of a head's persistent slots numbered consecutively
 // ("packed" rows, slot order): pre[s] = first packed row of slot s (prefix

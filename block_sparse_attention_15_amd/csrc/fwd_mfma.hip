@@ -396,7 +396,7 @@ template <int D> struct PersSlotDma {
       const int r = RPK * tu + rr;                             // slot row 0-63
       const int c = t ? swz_v(r, pos, Sh::CPR) : swz_k(r, pos, Sh::CPR);
       const bf16_t* src = (t ? a.vp : a.kp) + sb + (size_t)min(r, nl) * D + c * 8;
-      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(buf + t * 64 * Sh::ROWB + tu * 1024),
+      PBSA_LDS_LOAD(src, (__attribute__((address_space(3))) void*)(buf + t * 64 * Sh::ROWB + tu * 1024),
                                        16, 0, 0);
     }
   }
@@ -573,7 +573,7 @@ __device__ __forceinline__ void p2_issue(const FwdArgs& a, size_t bh, int t, int
     const int grow = rowtab[min(Q::KEYS * t + r, nvalid - 1)];
     const int c = tsel ? swz_v(r, pos, Sh::CPR) : swz_k(r, pos, Sh::CPR);
     const bf16_t* src = (tsel ? a.vp : a.kp) + (base + grow) * D + c * 8;
-    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(buf + tsel * Q::KEYS * Sh::ROWB + tu * 1024),
+    PBSA_LDS_LOAD(src, (__attribute__((address_space(3))) void*)(buf + tsel * Q::KEYS * Sh::ROWB + tu * 1024),
                                      16, 0, 0);
   }
 }
@@ -751,7 +751,7 @@ __device__ __forceinline__ void loc_gather(const FwdArgs& a, size_t bh, int qg, 
     if (TAB) {
       const uint32_t off = (uint32_t)rowtab[(w * g.K + t) * 64 + 32 * half + r] + (uint32_t)(c * 16);
       const char* src = reinterpret_cast<const char*>(tensor ? vb : kb) + off;
-      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(buf + u * 1024), 16, 0, 0);
+      PBSA_LDS_LOAD(src, (__attribute__((address_space(3))) void*)(buf + u * 1024), 16, 0, 0);
       continue;
     }
     int tok = -1;
@@ -766,7 +766,7 @@ __device__ __forceinline__ void loc_gather(const FwdArgs& a, size_t bh, int qg, 
       }
     }
     const bf16_t* src = (tok >= 0 ? (tensor ? vb : kb) + (size_t)tok * D : fill) + c * 8;
-    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(buf + u * 1024), 16, 0, 0);
+    PBSA_LDS_LOAD(src, (__attribute__((address_space(3))) void*)(buf + u * 1024), 16, 0, 0);
   }
 }
 
