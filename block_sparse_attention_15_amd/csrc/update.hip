@@ -304,7 +304,9 @@ hipError_t launch_persist_update(const Geo& g, const float* mass, const void* k_
                                                                n_rep, status);
     return hipGetLastError();
   };
+  // candidates per lane: each radix round of the decision costs one ballot per key a lane holds
   hipError_t e = NC <= 256    ? go(std::integral_constant<int, 4>{})
+                 : NC <= 512  ? go(std::integral_constant<int, 8>{})
                  : NC <= 1024 ? go(std::integral_constant<int, 16>{})
                               : go(std::integral_constant<int, 64>{});
   if (e != hipSuccess) return e;
