@@ -244,10 +244,18 @@ def test_bwd_very_negative_scores(name):
         assert err <= t["g_abs"] * scale and r <= t["g_rel"], k
 
 
-@pytest.mark.parametrize("name", list(SMALL))
+# shapes for the update only: 600 persistent slots and 12 entrants, 612
+# candidates, the decision's 16-keys-per-lane tier (SMALL and the decode
+# shapes take the 4- and 8-key tiers, the size-limit test the 64-key one)
+UPDATE_EXTRA = {
+    "huge_persistent_bf16": ragged(persistent_cache_size=100 * 308, total_cache_size=4 * 308 + 100 * 308, seed=31),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL) + list(UPDATE_EXTRA))
 @pytest.mark.parametrize("ring_head", [0, 1])
 def test_update(name, ring_head):
-    cfg = SMALL[name]
+    cfg = SMALL[name] if name in SMALL else UPDATE_EXTRA[name]
     x = synth.make_step_inputs(cfg)
     x["ring_head"][:] = ring_head
     if name == "ragged_bf16":
