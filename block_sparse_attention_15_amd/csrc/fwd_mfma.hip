@@ -687,9 +687,9 @@ constexpr size_t loc_tab_room() {
   return 160 * 1024 - 2 * (size_t)kLocBlocks * 64 * Shape<D>::ROWB;
 }
 
-constexpr size_t loc_tab_bytes(int K) { return (size_t)kLocBlocks * K * (64 * 4 + 8 + 4); }
+constexpr size_t loc_tab_bytes(int K) { return (size_t)kLocBlocks * K * (64 * 4 + 8 + 4) + 4; }
 
-template <int D>
+template <int D, bool PACK>
 __device__ __forceinline__ void build_rowtab(const FwdArgs& a, size_t bh, int qg, int nthreads, int* rowtab,
                                              int2* binfo, int* lentab) {
   const Geo& g = a.g;
@@ -710,6 +710,43 @@ __device__ __forceinline__ void build_rowtab(const FwdArgs& a, size_t bh, int qg
     lentab[x] = bi.y & 255;
   }
   __syncthreads();
+  if (PACK) {
+    // packed: the selected blocks' rows numbered consecutively (lentab[t]
+    // becomes block t's first packed row, lentab[nb] the total), so only
+    // the last 32-row step is partial
+    static_assert(kLocBlocks == 1, "one query block per workgroup");
+    if (threadIdx.x < 64) {
+      const int lane = threadIdx.x;
+      int run = 0;
+      for (int t0 = 0; t0 < nb; t0 += 64) {
+        const int t = t0 + lane;
+        const int n = t < nb ? lentab[t] : 0;
+        int x = n;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int y = __shfl_up(x, o, 64);
+          if (lane >= o) x += y;
+        }
+        __builtin_amdgcn_wave_barrier();
+        if (t < nb) lentab[t] = run + x - n;
+        run += __shfl(x, 63, 64);
+      }
+      if (lane == 0) lentab[nb] = run;
+    }
+    __syncthreads();
+    const int total = lentab[nb];
+    for (int x = threadIdx.x; x < nb * 64; x += nthreads) {
+      const int r = x & 63, t = x >> 6;
+      const int2 bi = binfo[t];
+      const LocBlock b{bi.x, bi.y & 255, (bi.y >> 8) & 255, bi.y >> 16};
+      if (r < b.len) rowtab[lentab[t] + r] = loc_row(g, b, r) * D * 2;
+    }
+    // rows past the total up to the step boundary, and the whole first step
+    // when no block is selected (the first gather is issued regardless): row
+    // 0 of the head (finite; the tile masks them or no tile runs)
+    for (int x = total + threadIdx.x; x < max(32, (total + 31) & ~31); x += nthreads) rowtab[x] = 0;
+    return;
+  }
   for (int x = threadIdx.x; x < nb * 64; x += nthreads) {
     const int r = x & 63;
     const int2 bi = binfo[x >> 6];
@@ -800,13 +837,21 @@ __global__ __launch_bounds__(kLocThreads) __attribute__((amdgpu_waves_per_eu(2, 
   load_q(a.q + (bh * g.ct + tok) * D, row_ok, 0, st);
   const float c2 = g.scale * 1.4426950408889634f;
 
-  const int nsteps = 2 * g.K;
+  // PACK: the selected blocks' rows packed into consecutive 32-row steps
+  // (the token-mass variant keeps one block per two steps: it sums per block)
+  constexpr bool PACK = TAB && !MASS;
+  int nsteps = 2 * g.K;
   int* rowtab = reinterpret_cast<int*>(smem);
   int2* binfo = reinterpret_cast<int2*>(rowtab + kLocBlocks * g.K * 64);
   int* lentab = reinterpret_cast<int*>(binfo + kLocBlocks * g.K);
+  int nrows = 0;  // PACK: packed rows of all selected blocks
   if (TAB) {
-    build_rowtab<D>(a, bh, qg, kLocThreads, rowtab, binfo, lentab);
+    build_rowtab<D, PACK>(a, bh, qg, kLocThreads, rowtab, binfo, lentab);
     __syncthreads();
+    if (PACK) {
+      nrows = lentab[kLocBlocks * g.K];
+      nsteps = (nrows + 31) / 32;
+    }
   }
   loc_gather<D, TAB>(a, bh, qg, 0, kv0, rowtab);
   __syncthreads();  // its fence waits for the gather
@@ -814,7 +859,9 @@ __global__ __launch_bounds__(kLocThreads) __attribute__((amdgpu_waves_per_eu(2, 
   // unrolled by two so that each step's buffers are compile-time arrays
   auto step = [&](int j, char* cur, char* nxt) {
     int nv = 0;
-    if (ntq) {
+    if (PACK) {
+      nv = ntq ? min(nrows - 32 * j, 32) : 0;
+    } else if (ntq) {
       int len = 0;
       if (TAB) {
         len = lentab[(wave >> 1) * g.K + (j >> 1)];
