@@ -491,9 +491,11 @@ constexpr int kLocBlocks = 1;  // query blocks per workgroup (2 waves each)
 constexpr int kDqlThreads = 64 * 2 * kLocBlocks;
 
 // Row tokens of every step of this workgroup, built once in LDS (see the
-// forward's local kernel): rowtab[(w*K + t)*64 + r] (-1 past the block's
-// end), binfo[w*K + t], lentab[w*K + t].  Used when they fit in the LDS
-// beside the two step buffers; otherwise every gather places its rows.
+// forward's local kernel): the selected blocks' rows packed into consecutive
+// 32-row steps, rowtab[32*step + r] (-1 past the last row, up to the step
+// boundary), binfo[t], and lentab[t] = block t's first packed row (lentab[K]
+// = the total).  Used when they fit in the LDS beside the two step buffers;
+// otherwise every gather places its rows, two steps per selected block.
 template <int D>
 constexpr size_t dql_tab_room() {
   return 160 * 1024 - 2 * (size_t)kLocBlocks * 2 * Sh<D>::TILEB;
@@ -501,6 +503,7 @@ constexpr size_t dql_tab_room() {
 
 __device__ __forceinline__ void build_rowtab(const BwdArgs& a, size_t bh, int qg, int nthreads, int* rowtab,
                                              int2* binfo, int* lentab) {
+  static_assert(kLocBlocks == 1, "one query block per workgroup");
   const Geo& g = a.g;
   const int nb = kLocBlocks * g.K;
   // one thread per selected block: where it sits in the ring (binfo: first
@@ -519,12 +522,35 @@ __device__ __forceinline__ void build_rowtab(const BwdArgs& a, size_t bh, int qg
     lentab[x] = bi.y & 255;
   }
   __syncthreads();
-  for (int x = threadIdx.x; x < nb * 64; x += nthreads) {
-    const int r = x & 63;
-    const int2 bi = binfo[x >> 6];
-    const LocBlock b{bi.x, bi.y & 255, (bi.y >> 8) & 255, bi.y >> 16};
-    rowtab[x] = r < b.len ? loc_row(g, b, r) : -1;  // -1: past the block's end
+  if (threadIdx.x < 64) {  // wave 0: exclusive scan of the lengths, 64 blocks per round
+    const int lane = threadIdx.x;
+    int run = 0;
+    for (int t0 = 0; t0 < nb; t0 += 64) {
+      const int t = t0 + lane;
+      const int n = t < nb ? lentab[t] : 0;
+      int x = n;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+      }
+      __builtin_amdgcn_wave_barrier();
+      if (t < nb) lentab[t] = run + x - n;
+      run += __shfl(x, 63, 64);
+    }
+    if (lane == 0) lentab[nb] = run;
   }
+  __syncthreads();
+  const int nrows = lentab[nb];
+  for (int x = threadIdx.x; x < nb * 64; x += nthreads) {
+    const int r = x & 63, t = x >> 6;
+    const int2 bi = binfo[t];
+    const LocBlock b{bi.x, bi.y & 255, (bi.y >> 8) & 255, bi.y >> 16};
+    if (r < b.len) rowtab[lentab[t] + r] = loc_row(g, b, r);
+  }
+  // past the last row up to the step boundary, and the whole first step when
+  // no block is selected (the first gather is issued regardless): the zero row
+  for (int x = nrows + threadIdx.x; x < max(32, (nrows + 31) & ~31); x += nthreads) rowtab[x] = -1;
 }
 
 // One local step gathered straight into LDS (global_load_lds_dwordx4): no
@@ -555,7 +581,7 @@ __device__ __forceinline__ void loc_gather(const BwdArgs& a, size_t bh, int qg, 
     const int c = swz(r, pos, Sh<D>::CPR);
     int tok = -1;
     if (TAB) {
-      tok = rowtab[(w * g.K + t) * 64 + 32 * half + r];
+      tok = rowtab[32 * j + r];  // packed rows (one query block per workgroup)
     } else {
       const int qb = qg * kLocBlocks + w;
       if (qb < g.nq) {
@@ -597,13 +623,18 @@ __global__ __launch_bounds__(kDqlThreads) __attribute__((amdgpu_waves_per_eu(2, 
   QState<D> st;
   q_init<D>(a, bh, tok, ok, st);
   const float c2 = g.scale * kLog2e;
-  const int nsteps = 2 * g.K;
+  // TAB: the selected blocks' rows packed into consecutive 32-row steps
+  // (only the last partial); otherwise two steps per selected block
+  int nsteps = 2 * g.K;
   int* rowtab = reinterpret_cast<int*>(smem);
   int2* binfo = reinterpret_cast<int2*>(rowtab + kLocBlocks * g.K * 64);
   int* lentab = reinterpret_cast<int*>(binfo + kLocBlocks * g.K);
+  int nrows = 0;
   if (TAB) {
     build_rowtab(a, bh, qg, kDqlThreads, rowtab, binfo, lentab);
     __syncthreads();
+    nrows = lentab[kLocBlocks * g.K];
+    nsteps = (nrows + 31) / 32;
   }
   loc_gather<D, TAB>(a, bh, qg, 0, kv0, rowtab);
   __syncthreads();  // its fence waits for the gather
@@ -611,14 +642,13 @@ __global__ __launch_bounds__(kDqlThreads) __attribute__((amdgpu_waves_per_eu(2, 
   auto step = [&](int j, char* cur, char* nxt) {
     int nv = 0;
     if (active) {
-      int len = 0;
       if (TAB) {
-        len = lentab[(wave >> 1) * g.K + (j >> 1)];
+        nv = min(nrows - 32 * j, 32);
       } else {
         const int p = a.topk[(bh * g.nq + qb) * g.K + (j >> 1)];
-        if ((unsigned)p < (unsigned)g.nl) len = block_ext(g, p % g.nq).len;
+        const int len = (unsigned)p < (unsigned)g.nl ? block_ext(g, p % g.nq).len : 0;
+        nv = min(len - 32 * (j & 1), 32);
       }
-      nv = min(len - 32 * (j & 1), 32);
     }
     nv = __builtin_amdgcn_readfirstlane(nv);  // uniform per wave: a scalar branch
     auto gather = [&]() {
@@ -1291,7 +1321,7 @@ hipError_t launch_d(const BwdArgs& base, hipStream_t s) {
   const size_t tab_dq = ((size_t)g.S * g.C + g.S + 1) * 4;
   const bool pk = g.S > 0 && tab_dq <= kDqTableMax;
   const size_t shm_dq = 2 * 4 * Sh<D>::TILEB + (pk ? tab_dq : g.S * 4);  // 2 x (K,K,V,V), row table or lengths
-  const size_t tabb = (size_t)kLocBlocks * g.K * (64 * 4 + 8 + 4);
+  const size_t tabb = (size_t)kLocBlocks * g.K * (64 * 4 + 8 + 4) + 4;
   const bool tab = tabb <= dql_tab_room<D>();
   const size_t shm_dql = tab ? tabb : 0;  // local: row tables (step buffers are static)
   const size_t shm_kvl = kvl_lds(g.nq);
