@@ -1111,7 +1111,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void dk_ds_kernel(BwdArgs a) {
 constexpr int kKvlThreads = 256;
 constexpr int kKvlWaves = kKvlThreads / 64;
 
-template <int D> struct KvlGather {
+template <int D, bool PACK> struct KvlGather {
   static constexpr int RPK = 1024 / Sh<D>::ROWB;   // rows per KB unit
   static constexpr int UPT = Sh<D>::TILEB / 1024;  // KB units per 32-row tile
   static constexpr int UPW = UPT / kKvlWaves;      // units of each tensor per wave
@@ -1140,6 +1140,14 @@ template <int D> struct KvlGather {
     for (int i = 0; i < UPW; ++i) toff[i] = off[32 * half + RPK * (wave * UPW + i) + lane / Sh<D>::CPR];
     toffl = off[32 * half + (threadIdx.x & 31)];
   }
+  // PACK: the selecting blocks' rows packed into consecutive 32-row steps,
+  // rtab[32*step + r] = the chunk token of row r of the step (-1: none)
+  __device__ __forceinline__ void tokens(const int* rtab, int step) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < UPW; ++i) toff[i] = rtab[32 * step + RPK * (wave * UPW + i) + lane / Sh<D>::CPR];
+    toffl = rtab[32 * step + (threadIdx.x & 31)];
+  }
   // Issue the gather of the step whose tokens are held into buf: Q and dO
   // rows, and (wave 0) the rows' lse2 and D, lanes 0-31 and 32-63.  Rows
   // without a token load Q / dO row 0 of the head (finite filler) and the
@@ -1154,7 +1162,7 @@ template <int D> struct KvlGather {
     for (int i = 0; i < UPW; ++i) {
       const int u = wave * UPW + i;
       const int r = RPK * u + rr;
-      const int tok = 32 * thalf + r < tlen ? tbase + toff[i] : 0;
+      const int tok = PACK ? max(toff[i], 0) : 32 * thalf + r < tlen ? tbase + toff[i] : 0;
       const int off = tok * D + swz(r, pos, Sh<D>::CPR) * 8;
       PBSA_LDS_LOAD(qb + off, (__attribute__((address_space(3))) void*)(buf + u * 1024), 16, 0,
                                        0);
@@ -1165,7 +1173,8 @@ template <int D> struct KvlGather {
     if (wave == 0) {
       // rows without a token read the sentinel after the last head: lse2 = +inf
       // (probability 0, so their dV and dS terms vanish) and D = 0
-      const size_t ro = 32 * thalf + (lane & 31) < tlen ? bh * g.ct + tbase + toffl : (size_t)g.B * g.H * g.ct;
+      const bool has = PACK ? toffl >= 0 : 32 * thalf + (lane & 31) < tlen;
+      const size_t ro = has ? bh * g.ct + (PACK ? toffl : tbase + toffl) : (size_t)g.B * g.H * g.ct;
       PBSA_LDS_LOAD(lane < 32 ? a.lse2 + ro : a.delta + ro,
                                        (__attribute__((address_space(3))) void*)(buf + 2 * Sh<D>::TILEB), 4, 0, 0);
     }
@@ -1176,10 +1185,19 @@ template <int D> struct KvlGather {
 // the selecting blocks' first tokens and their lengths and shape classes,
 // and the steps (up to two per block).
 constexpr size_t kvl_lds(int nq) { return 4 * 64 * 4 + (size_t)nq * (4 + 4 + 2 * 4); }
+// PACK: the same lists plus the selecting blocks' first packed rows and the
+// packed row table (up to 64 rows per selecting block, padded to a step)
+constexpr size_t kvl_lds_pack(int nq) { return 4 * 64 * 4 + (size_t)nq * (4 + 4 + 4) + 4 + ((size_t)nq * 64 + 32) * 4; }
+// dynamic LDS that keeps two workgroups per CU beside the static arrays (the
+// two step buffers, each 1 KB aligned, and the probability hand-over)
+template <int D>
+constexpr size_t kvl_pack_room() {
+  return 80 * 1024 - 2 * (((size_t)KvlGather<D, true>::BUF + 1023) & ~size_t(1023)) - 2 * 4 * 64 * 16;
+}
 
 // The key-outer pass of one role (dV or dK) over the workgroup's step list;
 // every wave runs the same number of barriers and gathers whatever its role.
-template <int D, bool DV>
+template <int D, bool DV, bool PACK>
 __device__ __forceinline__ void kvl_pass(const BwdArgs& a, size_t bh, int p, int kt, const int* sbase,
                                          const int* slen, const int* shape_off, const int* steps, int nsteps,
                                          char* kv0, char* kv1, float4* pex) {
@@ -1194,11 +1212,18 @@ __device__ __forceinline__ void kvl_pass(const BwdArgs& a, size_t bh, int p, int
   KState<D, DV> st;
   k_init<D, DV>(a.kl + krow, a.vl + krow, kok, st);
   const float c2 = g.scale * kLog2e;
-  KvlGather<D> ga;
+  KvlGather<D, PACK> ga;
+  // PACK: steps is the packed row table and the step index is the step
+  auto toks = [&](int i) {
+    if constexpr (PACK)
+      ga.tokens(steps, i);
+    else
+      ga.tokens(sbase, slen, shape_off, steps[i]);
+  };
   if (nsteps > 0) {
-    ga.tokens(sbase, slen, shape_off, steps[0]);
+    toks(0);
     ga.gather(a, bh, kv0);
-    if (nsteps > 1) ga.tokens(sbase, slen, shape_off, steps[1]);
+    if (nsteps > 1) toks(1);
   }
   __syncthreads();  // its fence waits for the gather
   // unrolled by two so that each step's buffers are compile-time arrays
@@ -1206,7 +1231,7 @@ __device__ __forceinline__ void kvl_pass(const BwdArgs& a, size_t bh, int p, int
     auto mid = [&]() {
       if (i + 1 < nsteps) {
         ga.gather(a, bh, nxt);
-        if (i + 2 < nsteps) ga.tokens(sbase, slen, shape_off, steps[i + 2]);
+        if (i + 2 < nsteps) toks(i + 2);
       }
     };
     // mid-step barrier: the dV wave of each key tile has written its P
@@ -1240,13 +1265,16 @@ __device__ __forceinline__ void kvl_pass(const BwdArgs& a, size_t bh, int p, int
   });
 }
 
-template <int D>
+// PACK: the selecting blocks' rows packed into consecutive 32-row steps (only
+// the last partial; used when the row table fits, see kvl_pack_room);
+// otherwise one or two steps per selecting block from the step list.
+template <int D, bool PACK>
 __global__ __launch_bounds__(kKvlThreads, 2) void dkv_local_kernel(BwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];  // step lists
   // the two step buffers are separate arrays so that the compiler can tell the
   // gather into one from the reads of the other
-  __shared__ __attribute__((aligned(1024))) char kv0[KvlGather<D>::BUF];
-  __shared__ __attribute__((aligned(1024))) char kv1[KvlGather<D>::BUF];
+  __shared__ __attribute__((aligned(1024))) char kv0[KvlGather<D, PACK>::BUF];
+  __shared__ __attribute__((aligned(1024))) char kv1[KvlGather<D, PACK>::BUF];
   __shared__ float4 pex[2][4 * 64];  // P of each key tile's current step, from its dV wave
   const Geo& g = a.g;
   const int total = g.B * g.H * g.nl;
@@ -1286,6 +1314,44 @@ __global__ __launch_bounds__(kKvlThreads, 2) void dkv_local_kernel(BwdArgs a) {
   }
   __syncthreads();
   int nsteps = 0;
+  if constexpr (PACK) {
+    // first packed row of every selecting block (wave 0: exclusive scan, 64
+    // blocks per round), then every row's chunk token, -1 past the last
+    int* pre = steps;             // [ncount + 1]
+    int* rtab = pre + g.nq + 1;   // [nq*64 + 32]
+    if (threadIdx.x < 64) {
+      const int lane = threadIdx.x;
+      int run = 0;
+      for (int x0 = 0; x0 < ncount; x0 += 64) {
+        const int x = x0 + lane;
+        const int n = x < ncount ? (slen[x] & 255) : 0;
+        int v = n;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int y = __shfl_up(v, o, 64);
+          if (lane >= o) v += y;
+        }
+        __builtin_amdgcn_wave_barrier();
+        if (x < ncount) pre[x] = run + v - n;
+        run += __shfl(v, 63, 64);
+      }
+      if (lane == 0) pre[ncount] = run;
+    }
+    __syncthreads();
+    const int nrows = pre[ncount];
+    for (int x = threadIdx.x; x < ncount * 64; x += kKvlThreads) {
+      const int r = x & 63, b = x >> 6, lc = slen[b];
+      if (r < (lc & 255)) rtab[pre[b] + r] = sbase[b] + shape_off[(lc >> 8) * 64 + r];
+    }
+    for (int x = nrows + threadIdx.x; x < max(32, (nrows + 31) & ~31); x += kKvlThreads) rtab[x] = -1;
+    __syncthreads();
+    nsteps = (nrows + 31) / 32;
+    if (role == 0)
+      kvl_pass<D, true, true>(a, bh, p, kt, sbase, slen, shape_off, rtab, nsteps, kv0, kv1, pex[kt]);
+    else
+      kvl_pass<D, false, true>(a, bh, p, kt, sbase, slen, shape_off, rtab, nsteps, kv0, kv1, pex[kt]);
+    return;
+  }
   for (int x = 0; x < ncount; ++x) {
     const int lc = slen[x], nh = ((lc & 255) + 31) / 32;
     if ((int)threadIdx.x < nh) steps[nsteps + threadIdx.x] = (x << 3) | (lc >> 8) << 1 | threadIdx.x;
@@ -1295,9 +1361,9 @@ __global__ __launch_bounds__(kKvlThreads, 2) void dkv_local_kernel(BwdArgs a) {
   for (int x = threadIdx.x; x < ncount; x += kKvlThreads) slen[x] &= 255;
   __syncthreads();
   if (role == 0)
-    kvl_pass<D, true>(a, bh, p, kt, sbase, slen, shape_off, steps, nsteps, kv0, kv1, pex[kt]);
+    kvl_pass<D, true, false>(a, bh, p, kt, sbase, slen, shape_off, steps, nsteps, kv0, kv1, pex[kt]);
   else
-    kvl_pass<D, false>(a, bh, p, kt, sbase, slen, shape_off, steps, nsteps, kv0, kv1, pex[kt]);
+    kvl_pass<D, false, false>(a, bh, p, kt, sbase, slen, shape_off, steps, nsteps, kv0, kv1, pex[kt]);
 }
 
 template <typename K>
@@ -1324,7 +1390,8 @@ hipError_t launch_d(const BwdArgs& base, hipStream_t s) {
   const size_t tabb = (size_t)kLocBlocks * g.K * (64 * 4 + 8 + 4) + 4;
   const bool tab = tabb <= dql_tab_room<D>();
   const size_t shm_dql = tab ? tabb : 0;  // local: row tables (step buffers are static)
-  const size_t shm_kvl = kvl_lds(g.nq);
+  const bool kvl_pack = kvl_lds_pack(g.nq) <= kvl_pack_room<D>();
+  const size_t shm_kvl = kvl_pack ? kvl_lds_pack(g.nq) : kvl_lds(g.nq);
   static PerDeviceOnce attr;
   hipError_t e = attr.run([] {
     hipError_t r = set_lds(dq_pers_kernel<D, true, false>, 2 * 4 * Sh<D>::TILEB + 2048 * 4);
@@ -1332,7 +1399,8 @@ hipError_t launch_d(const BwdArgs& base, hipStream_t s) {
     if (r == hipSuccess) r = set_lds(dq_pers_kernel<D, true, true>, 2 * 4 * Sh<D>::TILEB + kDqTableMax);
     if (r == hipSuccess) r = set_lds(dq_pers_kernel<D, false, true>, 2 * 4 * Sh<D>::TILEB + kDqTableMax);
     if (r == hipSuccess) r = set_lds(dq_local_kernel<D, true>, dql_tab_room<D>());
-    if (r == hipSuccess) r = set_lds(dkv_local_kernel<D>, kvl_lds(2048));
+    if (r == hipSuccess) r = set_lds(dkv_local_kernel<D, false>, kvl_lds(2048));
+    if (r == hipSuccess) r = set_lds(dkv_local_kernel<D, true>, kvl_pack_room<D>());
     return r;
   });
   if (e != hipSuccess) return e;
@@ -1342,7 +1410,10 @@ hipError_t launch_d(const BwdArgs& base, hipStream_t s) {
   // dK, dV of the local blocks, then dV (and without dS tiles, dK) of the
   // persistent slots
   int total = g.B * g.H * g.nl;
-  dkv_local_kernel<D><<<((total + 7) / 8) * 8, kKvlThreads, shm_kvl, s>>>(a);
+  if (kvl_pack)
+    dkv_local_kernel<D, true><<<((total + 7) / 8) * 8, kKvlThreads, shm_kvl, s>>>(a);
+  else
+    dkv_local_kernel<D, false><<<((total + 7) / 8) * 8, kKvlThreads, shm_kvl, s>>>(a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int kv_tiles = (g.S + kKvSlots - 1) / kKvSlots;
   if (g.S > 0) {
