@@ -873,13 +873,12 @@ template <int D> struct PersDma {
       const int u = wave * NU + i, t = u / UPT, uu = u % UPT;  // t: 0 Q, 1 dO
       const int r = RPK * uu + rr;
       const bf16_t* src = (t ? a.dout : a.q) + (hb + min(row0 + r, g.ct - 1)) * D + swz(r, pos, Sh<D>::CPR) * 8;
-      PBSA_LDS_LOAD(src, (__attribute__((address_space(3))) void*)(buf + t * Sh<D>::TILEB + uu * 1024),
-                                       16, 0, 0);
+      PBSA_LDS_LOAD(src, (__attribute__((address_space(3))) void*)(buf + t * Sh<D>::TILEB + uu * 1024), 16, 0, 0);
     }
     const int rl = row0 + (lane & 31);
     const size_t ro = rl < g.ct ? hb + rl : (size_t)g.B * g.H * g.ct;
     PBSA_LDS_LOAD(lane < 32 ? a.lse2 + ro : a.delta + ro,
-                                     (__attribute__((address_space(3))) void*)(buf + 2 * Sh<D>::TILEB), 4, 0, 0);
+                  (__attribute__((address_space(3))) void*)(buf + 2 * Sh<D>::TILEB), 4, 0, 0);
   }
 };
 
@@ -991,9 +990,8 @@ template <int D> struct DsDma {
     constexpr int kNt = 2;  // cache-policy operand: nt
 #pragma unroll
     for (int u = 0; u < 2; ++u)
-      PBSA_LDS_LOAD(ds + u * 512,
-                                       (__attribute__((address_space(3))) void*)(buf + QB + wave * 2048 + u * 1024),
-                                       16, 0, kNt);
+      PBSA_LDS_LOAD(ds + u * 512, (__attribute__((address_space(3))) void*)(buf + QB + wave * 2048 + u * 1024), 16, 0,
+                    kNt);
   }
 };
 
@@ -1164,11 +1162,8 @@ template <int D, bool PACK> struct KvlGather {
       const int r = RPK * u + rr;
       const int tok = PACK ? max(toff[i], 0) : 32 * thalf + r < tlen ? tbase + toff[i] : 0;
       const int off = tok * D + swz(r, pos, Sh<D>::CPR) * 8;
-      PBSA_LDS_LOAD(qb + off, (__attribute__((address_space(3))) void*)(buf + u * 1024), 16, 0,
-                                       0);
-      PBSA_LDS_LOAD(db + off,
-                                       (__attribute__((address_space(3))) void*)(buf + Sh<D>::TILEB + u * 1024),
-                                       16, 0, 0);
+      PBSA_LDS_LOAD(qb + off, (__attribute__((address_space(3))) void*)(buf + u * 1024), 16, 0, 0);
+      PBSA_LDS_LOAD(db + off, (__attribute__((address_space(3))) void*)(buf + Sh<D>::TILEB + u * 1024), 16, 0, 0);
     }
     if (wave == 0) {
       // rows without a token read the sentinel after the last head: lse2 = +inf
@@ -1176,7 +1171,7 @@ template <int D, bool PACK> struct KvlGather {
       const bool has = PACK ? toffl >= 0 : 32 * thalf + (lane & 31) < tlen;
       const size_t ro = has ? bh * g.ct + (PACK ? toffl : tbase + toffl) : (size_t)g.B * g.H * g.ct;
       PBSA_LDS_LOAD(lane < 32 ? a.lse2 + ro : a.delta + ro,
-                                       (__attribute__((address_space(3))) void*)(buf + 2 * Sh<D>::TILEB), 4, 0, 0);
+                    (__attribute__((address_space(3))) void*)(buf + 2 * Sh<D>::TILEB), 4, 0, 0);
     }
   }
 };

@@ -396,8 +396,7 @@ template <int D> struct PersSlotDma {
       const int r = RPK * tu + rr;                             // slot row 0-63
       const int c = t ? swz_v(r, pos, Sh::CPR) : swz_k(r, pos, Sh::CPR);
       const bf16_t* src = (t ? a.vp : a.kp) + sb + (size_t)min(r, nl) * D + c * 8;
-      PBSA_LDS_LOAD(src, (__attribute__((address_space(3))) void*)(buf + t * 64 * Sh::ROWB + tu * 1024),
-                                       16, 0, 0);
+      PBSA_LDS_LOAD(src, (__attribute__((address_space(3))) void*)(buf + t * 64 * Sh::ROWB + tu * 1024), 16, 0, 0);
     }
   }
 };
@@ -573,8 +572,8 @@ __device__ __forceinline__ void p2_issue(const FwdArgs& a, size_t bh, int t, int
     const int grow = rowtab[min(Q::KEYS * t + r, nvalid - 1)];
     const int c = tsel ? swz_v(r, pos, Sh::CPR) : swz_k(r, pos, Sh::CPR);
     const bf16_t* src = (tsel ? a.vp : a.kp) + (base + grow) * D + c * 8;
-    PBSA_LDS_LOAD(src, (__attribute__((address_space(3))) void*)(buf + tsel * Q::KEYS * Sh::ROWB + tu * 1024),
-                                     16, 0, 0);
+    PBSA_LDS_LOAD(src, (__attribute__((address_space(3))) void*)(buf + tsel * Q::KEYS * Sh::ROWB + tu * 1024), 16, 0,
+                  0);
   }
 }
 
@@ -662,8 +661,9 @@ __global__ __launch_bounds__(kP2Threads, 1) void fwd_pers2_kernel(FwdArgs a) {
 // ---------------------------------------------------------------------------
 // Kernel 2: each query block against its K selected local blocks, merged with
 // the persistent partial by log-sum-exp.  A workgroup is kLocBlocks query
-// blocks x 2 query tiles; per step it stages 32 rows of each block's current
-// selected block (one LDS region per query block).  One block per workgroup
+// blocks x 2 query tiles; per step it stages the next 32 rows of the query
+// block's selected blocks, packed back to back (one LDS region per query
+// block).  One block per workgroup
 // measured 14% faster than four: the blocks' work differs (edge blocks of
 // 24-48 tokens, short selected blocks) and a shared barrier per step made
 // every block wait for the slowest.
@@ -672,16 +672,20 @@ constexpr int kLocBlocks = 1;
 constexpr int kLocWaves = 2 * kLocBlocks;
 constexpr int kLocThreads = 64 * kLocWaves;
 
-// Rows of every step of this workgroup, built once in LDS:
-// rowtab[(w*K + t)*64 + r] = byte offset in the head's local K (or V) of row
-// r of query block w's t-th selected block; rows past the block's end repeat
-// its first row (finite; the tile masks them) and absent selections give 0
-// (no tile reads them); lentab[w*K + t] = that block's length (0 if absent);
-// binfo[w*K + t] = that block's first ring token and its length and extents
-// (8 bits each), from which the rows follow by arithmetic.  Used when the
-// tables fit in the LDS beside the two step buffers (four workgroups share a
-// CU while they stay under about 8 KB, K <= 30); otherwise every gather
-// places its rows itself.
+// Rows of every step of this workgroup, built once in LDS: rowtab[32*j + r]
+// = byte offset in the head's local K (or V) of row r of step j; binfo[t] =
+// the t-th selected block's first ring token and its length and extents (8
+// bits each), from which its rows follow by arithmetic.  Packed (the plain
+// forward): the selected blocks' rows numbered consecutively, lentab[t] =
+// block t's first packed row and lentab[K] the total, rows past the total up
+// to the step boundary (and the whole first step when there is none) give 0.
+// Otherwise (the token-mass forward, which sums per block): block t fills
+// steps 2t and 2t+1, lentab[t] = its length (0 if absent), rows past its end
+// repeat its first row (finite; the tile masks them), absent selections give
+// 0 (no tile reads them).  Used when the tables fit in the LDS beside the two
+// step buffers (four workgroups share a CU while they stay under about 8 KB,
+// K <= 30); otherwise every gather places its rows itself, two steps per
+// selected block.
 template <int D>
 constexpr size_t loc_tab_room() {
   return 160 * 1024 - 2 * (size_t)kLocBlocks * 64 * Shape<D>::ROWB;
