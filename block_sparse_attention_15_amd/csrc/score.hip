@@ -15,7 +15,7 @@
 // filled from outside is pooled once by pbsa_pool_local).  Scoring therefore
 // reads only the queries and the pooled keys.  Two launches, no
 // synchronisation between workgroups:
-//  1. per workgroup QPW query blocks of one head (512 threads): pool them
+//  1. per workgroup QPW query blocks of one head (512 threads; 1024 for eight): pool them
 //     (16-byte row loads, fixed-order reduction), score them against every
 //     candidate (the candidates' pooled keys loaded coalesced, all loads of
 //     the first chunks issued with the query rows, and staged through LDS a
@@ -257,17 +257,20 @@ __device__ __forceinline__ int xcd_remap(int total) {
   return (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
 }
 
-constexpr int kScoreThreads = 512;
+constexpr int kScoreThreads = 512;  // up to four query blocks per workgroup
+// Threads of a scoring workgroup: one selecting and one softmax wave per
+// query block, at least 512 (eight query blocks: 1024).
+constexpr int score_threads(int qpw) { return qpw > 4 ? 128 * qpw : kScoreThreads; }
 constexpr int kScoreChunk = 128;      // candidate keys staged in LDS at a time
 constexpr int kScoreChunksHeld = 3;   // chunks whose loads are issued up front (registers)
 
-// Pooling of QPW query blocks by one workgroup: kScoreThreads / QPW threads
+// Pooling of QPW query blocks by one workgroup: score_threads(QPW) / QPW threads
 // per block, each summing its row group's rows in order; row groups are then
 // added in order (fixed order, deterministic).
 template <int D, typename T, int QPW> struct QPool {
   static constexpr int VEC = 16 / sizeof(T);
   static constexpr int CPR = D / VEC;             // 16-byte chunks per row
-  static constexpr int TPB = kScoreThreads / QPW; // threads per query block
+  static constexpr int TPB = score_threads(QPW) / QPW; // threads per query block
   static constexpr int NRG = TPB / CPR;           // row groups per block
   static constexpr int RPT = (64 + NRG - 1) / NRG;
   static_assert(NRG >= 1 && TPB % CPR == 0, "pooling layout");
@@ -276,7 +279,7 @@ template <int D, typename T, int QPW> struct QPool {
 // 1-D grid over (B, H, group of QPW query blocks).  qbar is pooled here; the
 // scores, top-K ids, softmax rows and the workgroup's column sums follow.
 template <int D, typename T, int QPW, int KPL>
-__global__ __launch_bounds__(kScoreThreads) void score_topk_kernel(Geo g, const T* __restrict__ q,
+__global__ __launch_bounds__(score_threads(QPW)) void score_topk_kernel(Geo g, const T* __restrict__ q,
                                                                    const int32_t* __restrict__ ring_head,
                                                                    const float* __restrict__ kbar_l,
                                                                    const float* __restrict__ kbar_p,
@@ -310,7 +313,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_topk_kernel(Geo g, const 
   // for up to kScoreChunksHeld * kScoreChunk candidates; later chunks (larger
   // local windows) are loaded when their turn comes.
   constexpr int PPR = D / 4;                  // float4 pieces per row
-  constexpr int RPP = kScoreThreads / PPR;    // rows per pass
+  constexpr int TH = score_threads(QPW);
+  constexpr int RPP = TH / PPR;               // rows per pass
   constexpr int NP = kScoreChunk / RPP;       // float4 loads per thread per chunk
   static_assert(NP * RPP == kScoreChunk, "chunk layout");
   const int pc = threadIdx.x % PPR, pr = threadIdx.x / PPR;
@@ -360,7 +364,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_topk_kernel(Geo g, const 
 #pragma unroll
     for (int k = 0; k < P::VEC; ++k) red[(blk * P::NRG + rg) * D + c * P::VEC + k] = acc[k];
     __syncthreads();
-    for (int x = threadIdx.x; x < QPW * D; x += kScoreThreads) {
+    for (int x = threadIdx.x; x < QPW * D; x += TH) {
       const int b2 = x / D, d = x % D;
       float s = 0.f;
       for (int k = 0; k < P::NRG; ++k) s += red[(b2 * P::NRG + k) * D + d];
@@ -373,7 +377,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_topk_kernel(Geo g, const 
   __syncthreads();  // the pooling sums are read: their LDS takes the key chunks
   // scores: one thread per (candidate, query block), d in ascending order
   auto score_chunk = [&](int cb) {
-    for (int x = threadIdx.x; x < kScoreChunk * QPW; x += kScoreThreads) {
+    for (int x = threadIdx.x; x < kScoreChunk * QPW; x += TH) {
       const int r = x / QPW, k = x - r * QPW, c = cb + r;
       if (c >= W) break;
       float sv = -INFINITY;  // empty slot
@@ -411,9 +415,11 @@ __global__ __launch_bounds__(kScoreThreads) void score_topk_kernel(Geo g, const 
   }
   __syncthreads();
   // waves 0..QPW-1 select the top K of their query block's local scores,
-  // waves 4..4+QPW-1 turn the same rows into softmax rows: the selecting
+  // waves SW..SW+QPW-1 (SW = max(4, QPW)) turn the same rows into softmax
+  // rows: the selecting
   // waves take their keys into registers first, then both run side by side
-  static_assert(QPW <= 4 && kScoreThreads == 512, "selecting and softmax waves");
+  constexpr int SW = QPW > 4 ? QPW : 4;  // first softmax wave
+  static_assert(TH / 64 >= SW + QPW, "selecting and softmax waves");
   const int i = i0 + w;
   float* row = sc + w * W;
   const bool selects = w < QPW && i < g.nq;
@@ -456,7 +462,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_topk_kernel(Geo g, const 
       running += __builtin_popcountll(m);
     }
   }
-  const int wsm = w - 4;  // softmax wave of query block i0 + wsm
+  const int wsm = w - SW;  // softmax wave of query block i0 + wsm
   if (wsm >= 0 && wsm < QPW && i0 + wsm < g.nq) {
     // pooled softmax over valid slots and all local blocks, in place of the scores
     float* srow = sc + wsm * W;
@@ -477,7 +483,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_topk_kernel(Geo g, const 
   // layout (column c is local block c or slot c - nl)
   const int nrows = min(QPW, g.nq - i0);
   float* mypart = part + (bh * ngrp + grp) * (size_t)W;
-  for (int c = threadIdx.x; c < W; c += kScoreThreads) {
+  for (int c = threadIdx.x; c < W; c += TH) {
     float v = 0.f;
     for (int k = 0; k < nrows; ++k) v += sc[k * W + c];
     mypart[c < g.nl ? g.S + c : c - g.nl] = v;
@@ -511,16 +517,22 @@ constexpr int kScoreLdsMax = 159 * 1024;  // dynamic LDS
 
 // LDS of the score kernel at QPW query blocks per workgroup: pooled queries,
 // scores, flags, then the larger of the pooling scratch (sized for the
-// largest layout: fp32 rows, 512 / QPW threads per block) and one chunk of
+// largest layout: fp32 rows, score_threads(QPW) / QPW threads per block) and one chunk of
 // candidate keys with their lengths.
 size_t score_lds(const Geo& g, int qpw) {
   const int vec = g.dtype == PBSA_BF16 ? 8 : 4;
-  const int nrg = (kScoreThreads / qpw) / (g.D / vec);
+  const int nrg = (score_threads(qpw) / qpw) / (g.D / vec);
   const size_t pool = (size_t)qpw * nrg * g.D, chunk = (size_t)kScoreChunk * (g.D + 4 + 1);
   return ((size_t)qpw * (g.D + 4 + g.nl + g.S + g.nl) + std::max(pool, chunk)) * 4;
 }
 
 int score_qpw(const Geo& g) {
+  // eight query blocks per workgroup (1024 threads) when four would need
+  // more workgroups than the GPU has compute units: each workgroup loads every
+  // candidate's pooled key, so fewer, fuller workgroups cost less
+  const long long wg4 = (long long)g.B * g.H * ((g.nq + 3) / 4);
+  // (bf16 inputs: the fp32 rows need more registers than 1024 threads leave)
+  if (g.dtype == PBSA_BF16 && wg4 > 256 && score_lds(g, 8) <= (size_t)kScoreLdsMax) return 8;
   for (int q = 4; q > 1; q /= 2)
     if (score_lds(g, q) <= (size_t)kScoreLdsMax) return q;
   return 1;
@@ -586,7 +598,7 @@ hipError_t score_launch(const Geo& g, const void* q, const int32_t* ring_head, c
   if (e != hipSuccess) return e;
   const int ngrp = (g.nq + QPW - 1) / QPW;
   const int total = g.B * g.H * ngrp;
-  score_topk_kernel<D, T, QPW, KPL><<<(total + 7) / 8 * 8, kScoreThreads, score_lds(g, QPW), s>>>(
+  score_topk_kernel<D, T, QPW, KPL><<<(total + 7) / 8 * 8, score_threads(QPW), score_lds(g, QPW), s>>>(
       g, (const T*)q, ring_head, kbar_l, kbar_p, plen, topk, part, status);
   return hipGetLastError();
 }
@@ -596,6 +608,7 @@ hipError_t score_qpw_launch(const Geo& g, const void* q, const int32_t* ring_hea
                             const float* kbar_p, const int32_t* plen, int32_t* topk, float* part, uint32_t* status,
                             hipStream_t s) {
   switch (score_qpw(g)) {
+    case 8: return score_launch<D, T, 8, KPL>(g, q, ring_head, kbar_l, kbar_p, plen, topk, part, status, s);
     case 4: return score_launch<D, T, 4, KPL>(g, q, ring_head, kbar_l, kbar_p, plen, topk, part, status, s);
     case 2: return score_launch<D, T, 2, KPL>(g, q, ring_head, kbar_l, kbar_p, plen, topk, part, status, s);
     default: return score_launch<D, T, 1, KPL>(g, q, ring_head, kbar_l, kbar_p, plen, topk, part, status, s);

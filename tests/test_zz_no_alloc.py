@@ -41,7 +41,7 @@ def test_noalloc_equals_workspace_entry_twice():
 
 
 def test_noalloc_rejects_configs_beyond_its_scratch():
-    big = dict(synth.workload("decode_c1"), batch=32)
+    big = dict(synth.workload("decode_c1"), batch=64)  # 11.4 MB of column sums (eight query blocks per workgroup)
     p = pb.pbsa_plan(big)
     assert p.ws_score_select > 8 << 20
     lib = _lib.load()
