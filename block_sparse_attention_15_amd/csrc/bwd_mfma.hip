@@ -884,29 +884,57 @@ template <int D> struct PersDma {
 
 // dV (DV) or dK of the persistent slots; dK comes from dk_ds where the dS
 // tiles are stored.
-template <int D, bool DV>
+// PK (the dV pass beside the packed dk_ds): every wave takes 32 consecutive
+// valid rows of the head's slots (the rows numbered through the prefix sums
+// of the slot lengths, as dq_pers and dk_ds number them), so slots shorter
+// than 64 rows leave no half-empty key tiles and the head needs fewer
+// workgroups; each workgroup also writes the zero dV and dK of the rows past
+// the lengths of its share of the slots.
+template <int D, bool DV, bool PK>
 __global__ __launch_bounds__(kKvThreads, 1) void dkv_pers_kernel(BwdArgs a) {
+  static_assert(!PK || DV, "packed rows: the dV pass");
   using Dm = PersDma<D>;
   // three step buffers, separate arrays so that the compiler can tell the
   // loads into one from the reads of another
   __shared__ __attribute__((aligned(1024))) char kb0[Dm::BUF];
   __shared__ __attribute__((aligned(1024))) char kb1[Dm::BUF];
   __shared__ __attribute__((aligned(1024))) char kb2[Dm::BUF];
+  __shared__ int dst32[PK ? kKvWaves : 1][32];  // PK: slot*C + row of each key of each wave's tile
+  extern __shared__ __attribute__((aligned(16))) int pre[];  // PK: [S+1] prefix sums of the slot lengths
   const Geo& g = a.g;
   const int total = g.B * g.H * a.ntiles;
   const int lin = xcd_remap(total);
   if (lin >= total) return;
-  const int sp = lin % a.ntiles;  // slot group
+  const int sp = lin % a.ntiles;  // slot group, or PK: group of packed key tiles
   const size_t bh = lin / a.ntiles;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31;
   const int slot = kKvSlots * sp + (wave >> 1), kh = wave & 1;
   const bool has_slot = slot < g.S;
-  const int n = has_slot ? min(a.plen[bh * g.S + slot], g.C) : 0;
-  const int nk = __builtin_amdgcn_readfirstlane(min(max(n - 32 * kh, 0), 32));  // valid keys of this wave's tile
-  const size_t sbase = (bh * g.S + (has_slot ? slot : 0)) * (size_t)g.C * D;
-  const int kr = 32 * kh + l32;
+  int nk;  // valid keys of this wave's tile
+  size_t sbase = 0;
+  bool busy = true;  // PK: the workgroup has a tile
   KState<D, DV> st;
-  k_init<D, DV>(a.kp + sbase + (size_t)kr * D, a.vp + sbase + (size_t)kr * D, kr < n, st);
+  if constexpr (PK) {
+    const int nvalid = packed_rows(a.plen + bh * g.S, g.S, g.C, pre, nullptr, kKvThreads);
+    const int kt = kKvWaves * sp + wave;
+    nk = __builtin_amdgcn_readfirstlane(min(max(nvalid - 32 * kt, 0), 32));
+    busy = kKvWaves * sp * 32 < nvalid;
+    int off = 0;
+    const bool ok = l32 < nk;
+    if (ok) {
+      const int p = 32 * kt + l32, sl = packed_slot(pre, g.S, p);
+      off = sl * g.C + (p - pre[sl]);
+    }
+    if (lane < 32) dst32[wave][lane] = off;
+    const size_t hb = bh * (size_t)g.S * g.C * D;
+    k_init<D, DV>(a.kp + hb + (size_t)off * D, a.vp + hb + (size_t)off * D, ok, st);
+  } else {
+    const int n = has_slot ? min(a.plen[bh * g.S + slot], g.C) : 0;
+    nk = __builtin_amdgcn_readfirstlane(min(max(n - 32 * kh, 0), 32));
+    sbase = (bh * g.S + (has_slot ? slot : 0)) * (size_t)g.C * D;
+    const int kr = 32 * kh + l32;
+    k_init<D, DV>(a.kp + sbase + (size_t)kr * D, a.vp + sbase + (size_t)kr * D, kr < n, st);
+  }
   const float c2 = g.scale * kLog2e;
 
   // Every query tile of the head streams through LDS, loaded two steps
@@ -915,25 +943,52 @@ __global__ __launch_bounds__(kKvThreads, 1) void dkv_pers_kernel(BwdArgs a) {
   // issued; the transposed operands are read by asm that the compiler's own
   // waits do not cover, so they do not drain the loads in flight either.
   // Every step issues its loads (steps past the end repeat the last tile),
-  // so the counts hold on every path.
-  const int nsteps = (g.ct + 31) / 32, last = nsteps - 1;
-  Dm::issue(a, bh, 0, kb0);
-  Dm::issue(a, bh, 32 * min(1, last), kb1);
-  vm_barrier<Dm::NLD>();
-  auto step = [&](int i, char* cur, char* nx2) {
-    Dm::issue(a, bh, 32 * min(i + 2, last), nx2);
-    if (nk > 0 && i <= last) {
-      const float* f = reinterpret_cast<const float*>(cur + 2 * Sh<D>::TILEB);
-      k_tile<D, DV, false, false, true>(cur, cur + Sh<D>::TILEB, f, f + 32, c2, st);
-    }
+  // so the counts hold on every path.  (PK: a workgroup without a tile, the
+  // same for all its waves, skips the stream.)
+  if (busy) {
+    const int nsteps = (g.ct + 31) / 32, last = nsteps - 1;
+    Dm::issue(a, bh, 0, kb0);
+    Dm::issue(a, bh, 32 * min(1, last), kb1);
     vm_barrier<Dm::NLD>();
-  };
-  for (int i = 0; i < nsteps; i += 3) {
-    step(i, kb0, kb2);
-    step(i + 1, kb1, kb0);
-    step(i + 2, kb2, kb1);
+    auto step = [&](int i, char* cur, char* nx2) {
+      Dm::issue(a, bh, 32 * min(i + 2, last), nx2);
+      if (nk > 0 && i <= last) {
+        const float* f = reinterpret_cast<const float*>(cur + 2 * Sh<D>::TILEB);
+        k_tile<D, DV, false, false, true>(cur, cur + Sh<D>::TILEB, f, f + 32, c2, st);
+      }
+      vm_barrier<Dm::NLD>();
+    };
+    for (int i = 0; i < nsteps; i += 3) {
+      step(i, kb0, kb2);
+      step(i + 1, kb1, kb0);
+      step(i + 2, kb2, kb1);
+    }
+    __builtin_amdgcn_s_waitcnt(0xF70);  // the last loads land before the workgroup can end
   }
-  __builtin_amdgcn_s_waitcnt(0xF70);  // the last loads land before the workgroup can end
+  typedef float nf2 __attribute__((ext_vector_type(2)));
+  if constexpr (PK) {
+    const size_t hb = bh * (size_t)g.S * g.C * D;
+    if (nk > 0)
+      k_write<D, DV>(st, nk, 1.0f, [&](int r, float*& dst) {
+        if (r >= nk) return false;
+        dst = a.dvp + hb + (size_t)dst32[wave][r] * D;
+        return true;
+      });
+    // the rows past the slot lengths of this workgroup's share of the slots:
+    // zero dV here, zero dK for the packed dk_ds, which writes only the rows
+    // that exist
+    const int s0 = (int)((long long)sp * g.S / a.ntiles), s1 = (int)((long long)(sp + 1) * g.S / a.ntiles);
+    for (int sl = s0; sl < s1; ++sl) {
+      const int len = pre[sl + 1] - pre[sl];
+      const int n2 = (g.C - len) * (D / 2);
+      for (int x = threadIdx.x; x < n2; x += kKvThreads) {
+        const size_t e = hb + ((size_t)sl * g.C + len + x / (D / 2)) * D + 2 * (x % (D / 2));
+        __builtin_nontemporal_store(nf2{0.f, 0.f}, reinterpret_cast<nf2*>(a.dvp + e));
+        __builtin_nontemporal_store(nf2{0.f, 0.f}, reinterpret_cast<nf2*>(a.dkp + e));
+      }
+    }
+    return;
+  }
   if (!has_slot || 32 * kh >= g.C) return;
   float* ob = (DV ? a.dvp : a.dkp) + sbase;
   k_write<D, DV>(st, nk, DV ? 1.0f : -g.scale, [&](int r, float*& dst) {
@@ -946,10 +1001,8 @@ __global__ __launch_bounds__(kKvThreads, 1) void dkv_pers_kernel(BwdArgs a) {
     // the packed dk_ds writes only the rows that exist: the slot's rows past
     // its length get their zero dK here
     float* zk = a.dkp + sbase;
-    for (int r = max(nk, 0); r < 32 && 32 * kh + r < g.C; ++r) {
-      typedef float nf2 __attribute__((ext_vector_type(2)));
+    for (int r = max(nk, 0); r < 32 && 32 * kh + r < g.C; ++r)
       __builtin_nontemporal_store(nf2{0.f, 0.f}, reinterpret_cast<nf2*>(zk + (size_t)(32 * kh + r) * D) + lane % (D / 2));
-    }
   }
 }
 
@@ -1412,12 +1465,21 @@ hipError_t launch_d(const BwdArgs& base, hipStream_t s) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int kv_tiles = (g.S + kKvSlots - 1) / kKvSlots;
   if (g.S > 0) {
+    // slots shorter than 64 rows: the dV pass on packed key tiles (eight per
+    // workgroup), beside the packed dk_ds
+    const size_t shm_pk = ((size_t)g.S + 1) * 4;
+    const bool dv_pk = a.pk && g.C < 64 && 3 * PersDma<D>::BUF + 1024 + shm_pk <= 65536;
+    a.ntiles = dv_pk ? (int)(((long long)g.S * g.C + 32 * kKvWaves - 1) / (32 * kKvWaves)) : kv_tiles;
+    total = g.B * g.H * a.ntiles;
+    if (dv_pk)
+      dkv_pers_kernel<D, true, true><<<((total + 7) / 8) * 8, kKvThreads, shm_pk, s>>>(a);
+    else
+      dkv_pers_kernel<D, true, false><<<((total + 7) / 8) * 8, kKvThreads, 0, s>>>(a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     a.ntiles = kv_tiles;
     total = g.B * g.H * a.ntiles;
-    dkv_pers_kernel<D, true><<<((total + 7) / 8) * 8, kKvThreads, 0, s>>>(a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
     if (!ds) {
-      dkv_pers_kernel<D, false><<<((total + 7) / 8) * 8, kKvThreads, 0, s>>>(a);
+      dkv_pers_kernel<D, false, false><<<((total + 7) / 8) * 8, kKvThreads, 0, s>>>(a);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
   }
