@@ -1464,12 +1464,15 @@ hipError_t launch_d(const BwdArgs& base, hipStream_t s) {
     dkv_local_kernel<D, false><<<((total + 7) / 8) * 8, kKvlThreads, shm_kvl, s>>>(a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int kv_tiles = (g.S + kKvSlots - 1) / kKvSlots;
+  // workgroups of eight packed key tiles: as many as the slots' rows could
+  // fill (kv_tiles when the slots hold 64 rows)
+  const int pk_tiles = (int)(((long long)g.S * g.C + 32 * kKvWaves - 1) / (32 * kKvWaves));
   if (g.S > 0) {
     // slots shorter than 64 rows: the dV pass on packed key tiles (eight per
     // workgroup), beside the packed dk_ds
     const size_t shm_pk = ((size_t)g.S + 1) * 4;
     const bool dv_pk = a.pk && g.C < 64 && 3 * PersDma<D>::BUF + 1024 + shm_pk <= 65536;
-    a.ntiles = dv_pk ? (int)(((long long)g.S * g.C + 32 * kKvWaves - 1) / (32 * kKvWaves)) : kv_tiles;
+    a.ntiles = dv_pk ? pk_tiles : kv_tiles;
     total = g.B * g.H * a.ntiles;
     if (dv_pk)
       dkv_pers_kernel<D, true, true><<<((total + 7) / 8) * 8, kKvThreads, shm_pk, s>>>(a);
@@ -1498,7 +1501,7 @@ hipError_t launch_d(const BwdArgs& base, hipStream_t s) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ds) {
     // dK of the persistent slots from the dS tiles
-    a.ntiles = kv_tiles;
+    a.ntiles = pk ? pk_tiles : kv_tiles;
     total = g.B * g.H * a.ntiles;
     if (pk)  // the dS tiles are in packed key-tile order
       dk_ds_kernel<D, true><<<((total + 7) / 8) * 8, kKvThreads, ((size_t)g.S + 1) * 4, s>>>(a);
