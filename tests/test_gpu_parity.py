@@ -49,6 +49,11 @@ SMALL = {
     "block344_bf16": ragged(frame_h=10, frame_w=14, block_t=3, block_h=4, block_w=4, chunk_frames=3,
                             total_cache_size=9 * 140, local_cache_size=6 * 140, persistent_cache_size=3 * 140,
                             seed=25),
+    # the same [3,4,4] blocks at head_dim 64, two batch entries: 48-row slots on the packed
+    # persistent dV pass and the packed dK grid at the smaller head size
+    "block344_bf16_d64_b2": ragged(frame_h=10, frame_w=14, block_t=3, block_h=4, block_w=4, chunk_frames=3,
+                                   total_cache_size=9 * 140, local_cache_size=6 * 140,
+                                   persistent_cache_size=3 * 140, head_dim=64, batch=2, seed=27),
     # no persistent memory: plain local block-sparse attention; the update only advances the ring
     "no_persistent_bf16": ragged(persistent_cache_size=0, total_cache_size=4 * 308, seed=51),
     # 16x16 grid, head_dim 64, 8 slots: a slot count that is not a multiple of the persistent
